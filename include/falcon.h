@@ -1,0 +1,146 @@
+/*
+ * falcon.h -- C ABI of the Falcon fast-weight recurrence on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method ("Fast Weight Attention for Continual Learning", authors'
+ * abstract): a fixed-size state S (d_v x d_k per batch and head) is updated
+ * once per token as one step of an online learner on the prefix-aligned
+ * example (x_t, y_t) = (k_{t-1}, v_t), and read after the write,
+ * o_t = S_t q_t.  Each step first decays S by the positive gate alpha_t and
+ * then applies a normalized first-order write (the KLA abstract on the same
+ * listing gives the key-norm step eta_t / (||x_t||^2 + eps) and the
+ * decay-then-delta order):
+ *
+ *   FALCON_F1   scalar NLMS:        S = S' + (y - S'x) u^T, u = eta x / (||x||^2 + eps)
+ *   FALCON_F2   per-column NLMS:    same with u_j = eta x_j / (|x_j| ||x||_1 + eps)
+ *   FALCON_F3   window mini-batch:  S = S' + b sum_{w<W} (y_{t-w} - S'x_{t-w}) x_{t-w}^T,
+ *                                   b = eta / (sum_{w<W} ||x_{t-w}||^2 + eps)
+ *   FALCON_F1A / F2A / F3A          inner-product counterparts: the target y is
+ *                                   written instead of the residual.
+ *   (S' = alpha_t S_{t-1}; the Falcon-2 and Falcon-3 formulas are this
+ *   library's reading of "per-column extension" and "sliding-window
+ *   mini-batch update"; the authors' text gives them in words only.)
+ *
+ * The abstract states that each rule has a chunk-parallel form with
+ * positive-decay renormalization; falcon_chunk_fwd computes that form
+ * (cumulative decays kept as chunk-local log sums, every factor a ratio
+ * later/earlier <= 1).  falcon_decode_step advances the recurrence by one
+ * token for many independent heads.
+ *
+ * Conventions for every entry point
+ *   - Pointers are device memory owned by the caller, except where noted.
+ *     The library never allocates, frees or synchronizes, and keeps no
+ *     global mutable state (re-entrant; concurrent calls on different
+ *     streams are safe when their buffers do not overlap).
+ *   - Work is enqueued on `stream` (NULL = the default stream); the call
+ *     returns without waiting for it.
+ *   - Arguments are validated on the host before anything is launched; an
+ *     invalid argument returns its negative status and launches nothing.
+ *     A launch failure reported by HIP returns FALCON_ERR_HIP.  Faults that
+ *     happen later on the device surface at the caller's next
+ *     synchronization, as HIP errors.
+ *   - Layouts are contiguous and head-major: [B, H, T, d] for sequences,
+ *     S row-major as [.., d_v, d_k] so that o = S q.
+ *   - alpha must lie in (0, 1] and eta should be >= 0; values outside are
+ *     not checked on the device and give undefined results.
+ */
+#ifndef FALCON_H
+#define FALCON_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FALCON_OK = 0,
+    FALCON_ERR_NULL = -1,        /* a required pointer is NULL */
+    FALCON_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+    FALCON_ERR_UNSUPPORTED = -3, /* valid, but not in the support matrix below */
+    FALCON_ERR_WORKSPACE = -4,   /* workspace missing or too small */
+    FALCON_ERR_HIP = -5          /* HIP reported an error at launch */
+} falcon_status;
+
+typedef enum {
+    FALCON_F1 = 1,
+    FALCON_F2 = 2,
+    FALCON_F3 = 3,
+    FALCON_F1A = 11,
+    FALCON_F2A = 12,
+    FALCON_F3A = 13
+} falcon_variant;
+
+typedef enum { FALCON_FP32 = 0, FALCON_BF16 = 1 } falcon_dtype;
+
+/*
+ * Workspace bytes falcon_chunk_fwd needs for these arguments (0 when none).
+ * Returns 0 as well for arguments falcon_chunk_fwd would reject.
+ */
+size_t falcon_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, falcon_dtype dt,
+                                  falcon_variant var, int window, int chunk);
+
+/*
+ * Chunk-parallel forward pass over whole sequences.
+ *
+ *   q, k      [B,H,T,dk]  dtype dt
+ *   v         [B,H,T,dv]  dtype dt
+ *   alpha     [B,H,T]     fp32, decay gate in (0,1]
+ *   eta       [B,H,T]     fp32, step size (eta >= 0)
+ *   S0        [B,H,dv,dk] fp32 initial state, or NULL for S0 = 0
+ *   k_prev    [B,H,W,dk]  dtype dt: the W keys before the sequence,
+ *                         k_{-W} .. k_{-1} (oldest first), or NULL for zeros
+ *                         (then x_0 = 0 and step 0 writes nothing)
+ *   v_prev    [B,H,W-1,dv] dtype dt: v_{-(W-1)} .. v_{-1}, or NULL for zeros
+ *                         (ignored when W = 1)
+ *   o         [B,H,T,dv]  dtype dt output, o_t = S_t q_t (rounded to nearest even
+ *                         for bf16).  Must not alias any input.
+ *   S_final   [B,H,dv,dk] fp32 output state S_T, or NULL to skip it.  May
+ *                         alias S0 (read before written, per workgroup).
+ *   W = window: 1 for F1/F2/F1A/F2A, 1..8 for F3/F3A.
+ *   chunk: rows per tile of the chunk form, one of 16, 32, 64.  A tile holds
+ *          floor(chunk / W) time steps, each contributing W window examples.
+ *   eps > 0 is recommended (eps = 0 with a zero key divides 0 by 0).
+ *   workspace / workspace_bytes: at least falcon_chunk_fwd_workspace(...)
+ *          bytes of device memory (may be NULL when that is 0).
+ *
+ * Support matrix: dk = dv in {64, 128}; T >= 0 (T = 0 only copies S0 to
+ * S_final); B*H >= 1; dt fp32 or bf16.  Continuing a sequence: pass the
+ * previous call's S_final as S0 and its last W keys / W-1 values as
+ * k_prev / v_prev; the result equals one call over the concatenation.
+ */
+int falcon_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                     const float* eta, const float* S0, const void* k_prev, const void* v_prev,
+                     void* o, float* S_final, int B, int H, int T, int dk, int dv,
+                     falcon_dtype dt, falcon_variant var, int window, int chunk, float eps,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One decode step for N independent sequences x H heads (one token each):
+ * x = k_cache (the previous key), S' = alpha S, write as above, o = S q,
+ * then k_cache <- k.
+ *
+ *   S         [N,H,dv,dk] fp32, read and overwritten in place
+ *   k_cache   [N,H,W,dk]  dtype dt, holds k_{t-1}; overwritten with k_t
+ *   q, k      [N,H,dk]    dtype dt
+ *   v         [N,H,dv]    dtype dt
+ *   alpha,eta [N,H]       fp32
+ *   o         [N,H,dv]    dtype dt output (must not alias inputs)
+ *
+ * Support matrix: var in {F1, F2, F1A, F2A} with window = 1; dk = dv in
+ * {64, 128}; dt fp32 or bf16.
+ */
+int falcon_decode_step(float* S, void* k_cache, const void* q, const void* k, const void* v,
+                       const float* alpha, const float* eta, void* o, int N, int H, int dk,
+                       int dv, falcon_dtype dt, falcon_variant var, int window, float eps,
+                       hipStream_t stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* falcon_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FALCON_H */

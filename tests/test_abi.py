@@ -1,0 +1,118 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/falcon.h declares, and rejects invalid arguments on the host (before
+any HIP call) with the documented status codes."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "falcon.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from weight_recurrent_sequence_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from weight_recurrent_sequence_amd import _build
+        _build.build()
+    return binding.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(falcon_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(["falcon_chunk_fwd", "falcon_chunk_fwd_workspace",
+                                           "falcon_decode_step", "falcon_status_string"])
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    from weight_recurrent_sequence_amd import binding
+    for code in (0, -1, -2, -3, -4, -5, 42):
+        s = binding.status_string(code)
+        assert isinstance(s, str) and s
+    assert binding.status_string(99) == "unknown status"
+
+
+def test_workspace_is_zero_for_the_fused_kernel(L):
+    assert L.falcon_chunk_fwd_workspace(8, 16, 4096, 128, 128, 1, 1, 1, 64) == 0
+
+
+P = 1 << 20  # a fake, 16-byte-aligned "device" address: never dereferenced
+
+
+def chunk(L, **kw):
+    a = dict(q=P, k=P, v=P, alpha=P, eta=P, S0=None, k_prev=None, v_prev=None, o=P, S_final=P,
+             B=2, H=4, T=100, dk=128, dv=128, dt=1, var=1, window=1, chunk=64, eps=1e-6)
+    a.update(kw)
+    return L.falcon_chunk_fwd(a["q"], a["k"], a["v"], a["alpha"], a["eta"], a["S0"], a["k_prev"],
+                              a["v_prev"], a["o"], a["S_final"], a["B"], a["H"], a["T"], a["dk"],
+                              a["dv"], a["dt"], a["var"], a["window"], a["chunk"],
+                              ctypes.c_float(a["eps"]), None, 0, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(var=4), -3), (dict(var=0), -3), (dict(dt=2), -3),
+    (dict(B=0), -2), (dict(H=-1), -2), (dict(T=-1), -2), (dict(dk=0), -2),
+    (dict(window=0), -2), (dict(window=2), -2),                 # window only for Falcon-3
+    (dict(var=3, window=9), -3), (dict(chunk=48), -3), (dict(chunk=128), -3),
+    (dict(dk=96, dv=96), -3), (dict(dk=64, dv=128), -3),
+    (dict(dt=0, chunk=64), -3),                                  # fp32 d128 chunk64: LDS
+    (dict(eps=-1.0), -2), (dict(eps=float("nan")), -2),
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(alpha=None), -1),
+    (dict(eta=None), -1), (dict(o=None), -1),
+    (dict(q=P + 8), -3), (dict(S0=P + 4), -3), (dict(alpha=P + 2), -3),
+])
+def test_chunk_rejects(L, kw, code):
+    assert chunk(L, **kw) == code
+
+
+def decode(L, **kw):
+    a = dict(S=P, kc=P, q=P, k=P, v=P, alpha=P, eta=P, o=P, N=4, H=2, dk=128, dv=128, dt=1,
+             var=1, window=1, eps=1e-6)
+    a.update(kw)
+    return L.falcon_decode_step(a["S"], a["kc"], a["q"], a["k"], a["v"], a["alpha"], a["eta"],
+                                a["o"], a["N"], a["H"], a["dk"], a["dv"], a["dt"], a["var"],
+                                a["window"], ctypes.c_float(a["eps"]), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(var=3), -3), (dict(var=13), -3), (dict(var=5), -3), (dict(dt=7), -3),
+    (dict(N=0), -2), (dict(H=0), -2), (dict(window=0), -2), (dict(window=2), -3),
+    (dict(dk=32, dv=32), -3), (dict(dk=128, dv=64), -3), (dict(eps=-2.0), -2),
+    (dict(S=None), -1), (dict(kc=None), -1), (dict(o=None), -1), (dict(eta=None), -1),
+    (dict(S=P + 8), -3),
+])
+def test_decode_rejects(L, kw, code):
+    assert decode(L, **kw) == code
+
+
+def test_python_binding_checks_shapes():
+    torch = pytest.importorskip("torch")
+    import weight_recurrent_sequence_amd as fal
+    q = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(TypeError):
+        fal.chunk_fwd(q.double(), q.double(), q.double(), torch.zeros(1, 1, 4),
+                      torch.zeros(1, 1, 4), "F1")
+    with pytest.raises(ValueError):
+        fal.chunk_fwd(q, q, q[:, :, :3], torch.zeros(1, 1, 4), torch.zeros(1, 1, 4), "F1")
+
+
+def test_package_has_no_cpu_fallback():
+    """The binding only marshals arguments: it imports neither the oracle nor
+    any CPU implementation of the recurrence."""
+    pkg = os.path.join(ROOT, "weight_recurrent_sequence_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            src = open(os.path.join(pkg, fn)).read()
+            assert "import oracle" not in src and "from oracle" not in src, fn

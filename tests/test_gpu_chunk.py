@@ -1,0 +1,180 @@
+"""GPU parity of falcon_chunk_fwd against the fp64 oracle (recurrent form).
+
+Acceptance (per (batch, head) slice): max|gpu - oracle| / max|oracle| <= 1e-4
+for fp32 inputs, <= 2e-2 for bf16 inputs, for the outputs o and the final
+state; fp32 state in both cases.  Inputs are seeded and synthetic; the oracle
+consumes the very same stored bits.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import TOL, announce, ensure_built, slice_rel_err, to_np
+from weight_recurrent_sequence_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+ALL = ["F1", "F2", "F3", "F1A", "F2A", "F3A"]
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    ensure_built()
+    return torch.device("cuda:0")
+
+
+def supported(dtype, D, chunk):
+    return not (dtype == "fp32" and D == 128 and chunk == 64)
+
+
+def gpu_run(dev, inp, variant, W, chunk, eps=1e-6, label=""):
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    t = inp.to_torch(dev)
+    B, H, T, D = inp.k.shape
+    announce(f"chunk_fwd {variant} {inp.dtype} B{B} H{H} T{T} d{D} W{W} chunk{chunk} {label}")
+    o, S = fal.chunk_fwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], variant, window=W,
+                         chunk=chunk, eps=eps, S0=t["S0"], k_prev=t["k_prev"],
+                         v_prev=t["v_prev"])
+    torch.cuda.synchronize()
+    return o, S
+
+
+def oracle_run(inp, variant, W, eps=1e-6, sl=None):
+    d = inp.f64(sl)
+    return oracle.recurrent(variant, d["q"], d["k"], d["v"], d["alpha"], d["eta"], window=W,
+                            eps=eps, S0=d["S0"], k_prev=d["k_prev"], v_prev=d["v_prev"])
+
+
+def check(dev, inp, variant, W, chunk, label=""):
+    o, S = gpu_run(dev, inp, variant, W, chunk, label=label)
+    o_ref, S_ref = oracle_run(inp, variant, W)
+    e_o = slice_rel_err(to_np(o), o_ref, (2, 3))
+    e_S = slice_rel_err(to_np(S), S_ref, (2, 3))
+    tol = TOL[inp.dtype]
+    assert np.isfinite(to_np(o)).all()
+    assert e_o <= tol and e_S <= tol, (e_o, e_S)
+    return e_o, e_S
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("variant", ALL)
+def test_grid(dev, variant, dtype, D, chunk):
+    if not supported(dtype, D, chunk):
+        pytest.skip("fp32 with d=128 supports chunk <= 32 (LDS)")
+    W = 3 if variant in ("F3", "F3A") else 1
+    inp = I.make_chunk_inputs(2, 3, 150, D, D, dtype=dtype, seed=100 + D + chunk, window=W,
+                              halo=True, S0_sd=0.3)
+    check(dev, inp, variant, W, chunk)
+
+
+@pytest.mark.parametrize("T", [0, 1, 2, 15, 16, 17, 63, 64, 65, 129])
+@pytest.mark.parametrize("case", [("F1", "bf16", 128, 64, 1), ("F3", "bf16", 128, 64, 4),
+                                  ("F2", "fp32", 64, 32, 1), ("F1A", "bf16", 64, 16, 1)])
+def test_lengths(dev, case, T):
+    variant, dtype, D, chunk, W = case
+    inp = I.make_chunk_inputs(1, 2, T, D, D, dtype=dtype, seed=200 + T, window=W, S0_sd=0.2)
+    if T == 0:
+        o, S = gpu_run(dev, inp, variant, W, chunk, label="T=0")
+        np.testing.assert_array_equal(to_np(S), inp.S0.astype(np.float64))
+        return
+    check(dev, inp, variant, W, chunk)
+
+
+@pytest.mark.parametrize("chunk", [16, 64])
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("variant", ["F3", "F3A"])
+def test_windows(dev, variant, W, chunk):
+    inp = I.make_chunk_inputs(1, 3, 100, 64, 64, dtype="bf16", seed=300 + W, window=W,
+                              halo=True)
+    check(dev, inp, variant, W, chunk)
+
+
+@pytest.mark.parametrize("variant", ALL)
+def test_continuation(dev, variant):
+    """Two calls with carried state and halo equal one call (and the oracle)."""
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    W = 4 if variant in ("F3", "F3A") else 1
+    inp = I.make_chunk_inputs(2, 2, 300, 128, 128, dtype="bf16", seed=400, window=W)
+    t = inp.to_torch(dev)
+    T1 = 130
+    announce(f"chunk_fwd continuation {variant} T=300 split {T1}")
+    o1, S1 = fal.chunk_fwd(*(t[x][:, :, :T1].contiguous() for x in ("q", "k", "v", "alpha",
+                                                                        "eta")),
+                           variant, window=W, chunk=64)
+    kp = t["k"][:, :, T1 - W:T1].contiguous()
+    vp = t["v"][:, :, T1 - W + 1:T1].contiguous() if W > 1 else None
+    o2, S2 = fal.chunk_fwd(*(t[x][:, :, T1:].contiguous() for x in ("q", "k", "v", "alpha",
+                                                                       "eta")),
+                           variant, window=W, chunk=64, S0=S1, k_prev=kp, v_prev=vp)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_run(inp, variant, W)
+    o = torch.cat([o1, o2], dim=2)
+    assert slice_rel_err(to_np(o), o_ref, (2, 3)) <= TOL["bf16"]
+    assert slice_rel_err(to_np(S2), S_ref, (2, 3)) <= TOL["bf16"]
+
+
+def test_deterministic_and_state_alias(dev):
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    inp = I.make_chunk_inputs(2, 4, 257, 128, 128, dtype="bf16", seed=500, S0_sd=0.3)
+    t = inp.to_torch(dev)
+    announce("chunk_fwd determinism F2 B2 H4 T257")
+    runs = [fal.chunk_fwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], "F2", S0=t["S0"])
+            for _ in range(2)]
+    S_alias = t["S0"].clone()
+    o3, _ = fal.chunk_fwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], "F2", S0=S_alias,
+                          S_final=S_alias)
+    torch.cuda.synchronize()
+    assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
+    assert torch.equal(o3, runs[0][0]) and torch.equal(S_alias, runs[0][1])
+
+
+def test_fp32_large_chunk_rejected(dev):
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    x = torch.zeros(1, 1, 8, 128, device=dev)
+    a = torch.ones(1, 1, 8, device=dev)
+    with pytest.raises(fal.FalconError):
+        fal.chunk_fwd(x, x, x, a, a, "F1", chunk=64)
+
+
+# ---- the workloads at full size, in the launch configuration the benchmark
+# times; the oracle recomputes a sample of (batch, head) sequences in full ----
+FULL = [
+    ("falcon1_fp32_B1H1T256d64", "F1", None),
+    ("falcon1_bf16_B8H16T4096d128", "F1", [(0, 0), (3, 7), (7, 15)]),
+    ("falcon1_bf16_B8H16T4096d128", "F1A", [(1, 2), (6, 9)]),
+    ("falcon2_bf16_B4H32T8192d128", "F2", [(0, 0), (2, 17), (3, 31)]),
+    ("falcon2_bf16_B4H32T8192d128", "F2A", [(1, 5)]),
+    ("falcon3_w4_bf16_B2H16T32768d128", "F3", [(0, 3), (1, 12)]),
+    ("falcon3_w4_bf16_B2H16T32768d128", "F3A", [(1, 0)]),
+]
+
+
+@pytest.mark.parametrize("name,variant,sample", FULL, ids=[f"{n}-{v}" for n, v, _ in FULL])
+def test_full_workloads_sampled(dev, name, variant, sample):
+    w = I.WORKLOADS[name]
+    W = w.get("window", 1)
+    inp = I.workload_inputs(name)
+    o, S = gpu_run(dev, inp, variant, W, w["chunk"], label=name)
+    o_np, S_np = to_np(o), to_np(S)
+    assert np.isfinite(o_np).all() and np.isfinite(S_np).all()
+    tol = TOL[inp.dtype]
+    heads = sample if sample is not None else [(b, h) for b in range(w["B"])
+                                               for h in range(w["H"])]
+    bs = np.array([b for b, _ in heads])
+    hs = np.array([h for _, h in heads])
+    # oracle on the sampled sequences only, as a [1, n] batch
+    d = inp.f64((bs, hs))
+    o_ref, S_ref = oracle.recurrent(variant, *(d[x][None] for x in ("q", "k", "v", "alpha",
+                                                                      "eta")), window=W)
+    e_o = slice_rel_err(o_np[bs, hs][None], o_ref, (2, 3))
+    e_S = slice_rel_err(S_np[bs, hs][None], S_ref, (2, 3))
+    announce(f"{name} {variant}: max rel err o={e_o:.2e} S={e_S:.2e} over {len(heads)} heads")
+    assert e_o <= tol and e_S <= tol, (e_o, e_S)

@@ -1,0 +1,93 @@
+"""GPU parity of falcon_decode_step against the fp64 oracle's decode step.
+
+Every step's output and the final state and key cache are compared per head
+(max|gpu - oracle| / max|oracle|, 1e-4 for fp32 inputs, 2e-2 for bf16)."""
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import TOL, announce, ensure_built, slice_rel_err, to_np
+from weight_recurrent_sequence_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    ensure_built()
+    return torch.device("cuda:0")
+
+
+def tens(a, dtype, dev):
+    import torch
+    x = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype == "bf16" and a.dtype == np.uint16:
+        x = x.view(torch.bfloat16)
+    return x.to(dev)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("variant", ["F1", "F2", "F1A", "F2A"])
+def test_decode_grid(dev, variant, dtype, D):
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    N, H, steps = 3, 5, 12
+    di = I.make_decode_inputs(N, H, D, D, steps, dtype=dtype, seed=600 + D, S0_sd=0.1)
+    S = tens(di.S0, "fp32", dev)
+    kc = tens(di.k_cache0, dtype, dev)
+    S_o, kc_o = di.S0.astype(np.float64), di.widen(di.k_cache0)[:, :, 0]
+    tol = TOL[dtype]
+    for s in range(steps):
+        announce(f"decode_step {variant} {dtype} N{N} H{H} d{D} step {s}")
+        o = fal.decode_step(S, kc, tens(di.q[s], dtype, dev), tens(di.k[s], dtype, dev),
+                            tens(di.v[s], dtype, dev), tens(di.alpha[s], "fp32", dev),
+                            tens(di.eta[s], "fp32", dev), variant)
+        o_ref, S_o, kc_o = oracle.decode_step(variant, S_o, kc_o, di.widen(di.q[s]),
+                                              di.widen(di.k[s]), di.widen(di.v[s]),
+                                              di.alpha[s], di.eta[s])
+        torch.cuda.synchronize()
+        assert slice_rel_err(to_np(o), o_ref, (2,)) <= tol
+    assert slice_rel_err(to_np(S), S_o, (2, 3)) <= tol
+    np.testing.assert_array_equal(to_np(kc)[:, :, 0], kc_o)
+
+
+def test_decode_full_workload_sampled(dev):
+    """256 sequences x 32 heads, d = 128, 1024 consecutive steps from
+    N(0, 0.02^2) states, in the benchmark's launch configuration; the oracle
+    follows a sample of heads through all 1024 steps."""
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    w = I.WORKLOADS["decode_falcon1_N256H32d128_1024steps"]
+    N, H, D, steps = w["N"], w["H"], w["d"], w["steps"]
+    x = I.make_decode_inputs_torch(N, H, D, D, steps, device=dev, seed=w["seed"])
+    sample = [(0, 0), (17, 5), (128, 31), (255, 16)]
+    ns = torch.tensor([n for n, _ in sample], device=dev)
+    hs = torch.tensor([h for _, h in sample], device=dev)
+    S = x["S0"].clone()
+    kc = x["k_cache0"].clone()
+    outs = torch.empty(steps, len(sample), D, dtype=torch.bfloat16, device=dev)
+    announce("decode_step F1 bf16 N256 H32 d128, 1024 steps")
+    for s in range(steps):
+        o = fal.decode_step(S, kc, x["q"][s], x["k"][s], x["v"][s], x["alpha"][s], x["eta"][s],
+                            "F1")
+        outs[s] = o[ns, hs]
+    torch.cuda.synchronize()
+    assert torch.isfinite(S).all()
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    S_o = f64(x["S0"][ns, hs])[None]
+    kc_o = f64(x["k_cache0"][ns, hs, 0])[None]
+    o_ref = np.empty((steps, len(sample), D))
+    for s in range(steps):
+        o1, S_o, kc_o = oracle.decode_step("F1", S_o, kc_o, f64(x["q"][s][ns, hs])[None],
+                                           f64(x["k"][s][ns, hs])[None],
+                                           f64(x["v"][s][ns, hs])[None],
+                                           f64(x["alpha"][s][ns, hs])[None],
+                                           f64(x["eta"][s][ns, hs])[None])
+        o_ref[s] = o1[0]
+    e_o = slice_rel_err(np.moveaxis(to_np(outs), 0, 1), np.moveaxis(o_ref, 0, 1), (1, 2))
+    e_S = slice_rel_err(to_np(S[ns, hs]), S_o[0], (1, 2))
+    announce(f"decode full workload: max rel err o={e_o:.2e} S={e_S:.2e}")
+    assert e_o <= TOL["bf16"] and e_S <= TOL["bf16"], (e_o, e_S)

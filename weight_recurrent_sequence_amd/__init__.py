@@ -1,1 +1,8 @@
-"""Falcon fast-weight recurrence on MI355X (gfx950): C-ABI library + binding."""
+"""Falcon fast-weight recurrence on AMD Instinct MI355X (gfx950).
+
+The computation runs in libfalcon.so (hand-written HIP kernels behind the C
+ABI of include/falcon.h); this package is its Python binding plus the seeded
+input generators used by tests and benchmarks.
+"""
+from .binding import (BF16, F1, F1A, F2, F2A, F3, F3A, FP32, VARIANTS, FalconError,  # noqa: F401
+                      chunk_fwd, decode_step, lib, status_string, workspace_bytes)

@@ -1,0 +1,167 @@
+"""Thin ctypes binding of libfalcon.so (the C ABI in include/falcon.h).
+
+Argument marshalling only: shapes and dtypes are checked, raw device
+pointers and the current HIP stream are handed to the library, and every
+step of the computation runs in the library's kernels.  PyTorch provides
+device memory and streams.  There is no fallback: without the built
+library, or without a GPU, every entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfalcon.so")
+
+F1, F2, F3, F1A, F2A, F3A = 1, 2, 3, 11, 12, 13
+VARIANTS = {"F1": F1, "F2": F2, "F3": F3, "F1A": F1A, "F2A": F2A, "F3A": F3A}
+FP32, BF16 = 0, 1
+STATUS = {0: "FALCON_OK", -1: "FALCON_ERR_NULL", -2: "FALCON_ERR_SHAPE",
+          -3: "FALCON_ERR_UNSUPPORTED", -4: "FALCON_ERR_WORKSPACE", -5: "FALCON_ERR_HIP"}
+EXPORTS = ("falcon_chunk_fwd_workspace", "falcon_chunk_fwd", "falcon_decode_step",
+           "falcon_status_string")
+
+
+class FalconError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m weight_recurrent_sequence_amd._build`"
+                " (there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, ci, cf, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.falcon_chunk_fwd_workspace.restype = sz
+        L.falcon_chunk_fwd_workspace.argtypes = [ci] * 9
+        L.falcon_chunk_fwd.restype = ci
+        L.falcon_chunk_fwd.argtypes = [vp] * 10 + [ci] * 9 + [cf, vp, sz, vp]
+        L.falcon_decode_step.restype = ci
+        L.falcon_decode_step.argtypes = [vp] * 8 + [ci] * 7 + [cf, vp]
+        L.falcon_status_string.restype = ctypes.c_char_p
+        L.falcon_status_string.argtypes = [ci]
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().falcon_status_string(int(status)).decode()
+
+
+def _variant(v) -> int:
+    return VARIANTS[v] if isinstance(v, str) else int(v)
+
+
+def _dt(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return FP32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def workspace_bytes(B, H, T, dk, dv, dtype, variant, window=1, chunk=64) -> int:
+    return int(lib().falcon_chunk_fwd_workspace(B, H, T, dk, dv, dtype, _variant(variant),
+                                                window, chunk))
+
+
+def chunk_fwd(q, k, v, alpha, eta, variant, *, window=1, chunk=64, eps=1e-6, S0=None,
+              k_prev=None, v_prev=None, o=None, S_final=None, return_state=True, stream=None):
+    """Chunk-parallel forward.  q,k [B,H,T,dk]; v [B,H,T,dv] (bf16 or fp32);
+    alpha, eta [B,H,T] fp32; S0 [B,H,dv,dk] fp32 or None; k_prev [B,H,W,dk],
+    v_prev [B,H,W-1,dv] or None.  Returns (o, S_final) (S_final None if
+    return_state is False and none was given)."""
+    import torch
+    var = _variant(variant)
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    dev, dt = k.device, k.dtype
+    dtc = _dt(k)
+    _check(q, "q", (B, H, T, dk), dt, dev)
+    _check(k, "k", (B, H, T, dk), dt, dev)
+    _check(v, "v", (B, H, T, dv), dt, dev)
+    _check(alpha, "alpha", (B, H, T), torch.float32, dev)
+    _check(eta, "eta", (B, H, T), torch.float32, dev)
+    _check(S0, "S0", (B, H, dv, dk), torch.float32, dev)
+    _check(k_prev, "k_prev", (B, H, window, dk), dt, dev)
+    if window > 1:
+        _check(v_prev, "v_prev", (B, H, window - 1, dv), dt, dev)
+    else:
+        v_prev = None
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+    _check(o, "o", (B, H, T, dv), dt, dev)
+    if S_final is None and return_state:
+        S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    _check(S_final, "S_final", (B, H, dv, dk), torch.float32, dev)
+    ws_n = workspace_bytes(B, H, T, dk, dv, dtc, var, window, chunk)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n > 0 else None
+    st = lib().falcon_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(S0),
+                                _ptr(k_prev), _ptr(v_prev), _ptr(o), _ptr(S_final), B, H, T, dk,
+                                dv, dtc, var, window, chunk, float(eps), _ptr(ws), ws_n,
+                                _stream(stream))
+    if st != 0:
+        raise FalconError(st, "falcon_chunk_fwd")
+    return o, S_final
+
+
+def decode_step(S, k_cache, q, k, v, alpha, eta, variant, *, eps=1e-6, o=None, stream=None):
+    """One decode step.  S [N,H,dv,dk] fp32 and k_cache [N,H,1,dk] are
+    updated in place; q,k [N,H,dk], v [N,H,dv] (bf16 or fp32), alpha, eta
+    [N,H] fp32.  Returns o [N,H,dv]."""
+    import torch
+    var = _variant(variant)
+    N, H, dv, dk = S.shape
+    dev, dt = k.device, k.dtype
+    dtc = _dt(k)
+    _check(S, "S", (N, H, dv, dk), torch.float32, dev)
+    _check(k_cache, "k_cache", (N, H, 1, dk), dt, dev)
+    _check(q, "q", (N, H, dk), dt, dev)
+    _check(k, "k", (N, H, dk), dt, dev)
+    _check(v, "v", (N, H, dv), dt, dev)
+    _check(alpha, "alpha", (N, H), torch.float32, dev)
+    _check(eta, "eta", (N, H), torch.float32, dev)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=dt, device=dev)
+    _check(o, "o", (N, H, dv), dt, dev)
+    st = lib().falcon_decode_step(_ptr(S), _ptr(k_cache), _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(alpha), _ptr(eta), _ptr(o), N, H, dk, dv, dtc, var, 1,
+                                  float(eps), _stream(stream))
+    if st != 0:
+        raise FalconError(st, "falcon_decode_step")
+    return o

@@ -1,0 +1,142 @@
+// falcon_api.hip -- the C ABI declared in include/falcon.h: argument
+// validation on the host (before any HIP call), then dispatch to the
+// kernels on the caller's stream.  No allocation, no synchronization, no
+// global mutable state.
+#include <stdint.h>
+
+#include "../../include/falcon.h"
+#include "falcon_internal.h"
+
+namespace {
+
+bool is_variant(int v) {
+    return v == FALCON_F1 || v == FALCON_F2 || v == FALCON_F3 || v == FALCON_F1A ||
+           v == FALCON_F2A || v == FALCON_F3A;
+}
+
+int norm_of(int v) {
+    switch (v) {
+        case FALCON_F1:
+        case FALCON_F1A: return falcon::kNormScalar;
+        case FALCON_F2:
+        case FALCON_F2A: return falcon::kNormColumn;
+        default: return falcon::kNormWindow;
+    }
+}
+
+bool is_delta(int v) { return v == FALCON_F1 || v == FALCON_F2 || v == FALCON_F3; }
+
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int check_chunk(const void* q, const void* k, const void* v, const float* alpha,
+                const float* eta, const float* S0, const void* k_prev, const void* v_prev,
+                const void* o, const float* S_final, int B, int H, int T, int dk, int dv,
+                int dt, int var, int window, int chunk, float eps) {
+    if (!is_variant(var)) return FALCON_ERR_UNSUPPORTED;
+    if (dt != FALCON_FP32 && dt != FALCON_BF16) return FALCON_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1) return FALCON_ERR_SHAPE;
+    if ((long long)B * H > (1LL << 28) || (long long)T * dk > (1LL << 40)) return FALCON_ERR_SHAPE;
+    if (window < 1) return FALCON_ERR_SHAPE;
+    const bool win = (var == FALCON_F3 || var == FALCON_F3A);
+    if (!win && window != 1) return FALCON_ERR_SHAPE;
+    if (window > 8) return FALCON_ERR_UNSUPPORTED;
+    if (chunk != 16 && chunk != 32 && chunk != 64) return FALCON_ERR_UNSUPPORTED;
+    if (window > chunk) return FALCON_ERR_UNSUPPORTED;
+    if (dk != dv) return FALCON_ERR_UNSUPPORTED;
+    if (!falcon::chunk_supported(dt, dk, chunk)) return FALCON_ERR_UNSUPPORTED;
+    if (!(eps >= 0.0f)) return FALCON_ERR_SHAPE;  // also rejects NaN
+    if (T > 0 && (!q || !k || !v || !alpha || !eta || !o)) return FALCON_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(S0) ||
+        !aligned16(S_final) || !aligned16(k_prev) || !aligned16(v_prev) || !aligned4(alpha) ||
+        !aligned4(eta))
+        return FALCON_ERR_UNSUPPORTED;
+    return FALCON_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t falcon_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, falcon_dtype dt,
+                                  falcon_variant var, int window, int chunk) {
+    (void)B; (void)H; (void)T; (void)dk; (void)dv; (void)dt; (void)var; (void)window;
+    (void)chunk;
+    return 0;  // the fused kernel keeps everything in registers and LDS
+}
+
+int falcon_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                     const float* eta, const float* S0, const void* k_prev, const void* v_prev,
+                     void* o, float* S_final, int B, int H, int T, int dk, int dv,
+                     falcon_dtype dt, falcon_variant var, int window, int chunk, float eps,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int st = check_chunk(q, k, v, alpha, eta, S0, k_prev, v_prev, o, S_final, B, H, T, dk, dv,
+                         dt, var, window, chunk, eps);
+    if (st != FALCON_OK) return st;
+    const size_t need = falcon_chunk_fwd_workspace(B, H, T, dk, dv, dt, var, window, chunk);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FALCON_ERR_WORKSPACE;
+    if (T == 0 && S_final == nullptr) return FALCON_OK;
+    falcon::ChunkArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = alpha;
+    a.eta = eta;
+    a.S0 = S0;
+    a.k_prev = k_prev;
+    a.v_prev = v_prev;
+    a.o = o;
+    a.S_final = S_final;
+    a.BH = B * H;
+    a.T = T;
+    a.W = window;
+    a.norm = norm_of(var);
+    a.eps = eps;
+    hipError_t e = falcon::launch_chunk(a, (int)dt, dk, chunk, is_delta(var), stream);
+    return e == hipSuccess ? FALCON_OK : FALCON_ERR_HIP;
+}
+
+int falcon_decode_step(float* S, void* k_cache, const void* q, const void* k, const void* v,
+                       const float* alpha, const float* eta, void* o, int N, int H, int dk,
+                       int dv, falcon_dtype dt, falcon_variant var, int window, float eps,
+                       hipStream_t stream) {
+    if (!is_variant(var)) return FALCON_ERR_UNSUPPORTED;
+    if (var == FALCON_F3 || var == FALCON_F3A) return FALCON_ERR_UNSUPPORTED;
+    if (dt != FALCON_FP32 && dt != FALCON_BF16) return FALCON_ERR_UNSUPPORTED;
+    if (N < 1 || H < 1 || dk < 1 || dv < 1 || window < 1) return FALCON_ERR_SHAPE;
+    if ((long long)N * H > (1LL << 30)) return FALCON_ERR_SHAPE;
+    if (window != 1) return FALCON_ERR_UNSUPPORTED;
+    if (dk != dv || !falcon::decode_supported((int)dt, dk)) return FALCON_ERR_UNSUPPORTED;
+    if (!(eps >= 0.0f)) return FALCON_ERR_SHAPE;
+    if (!S || !k_cache || !q || !k || !v || !alpha || !eta || !o) return FALCON_ERR_NULL;
+    if (!aligned16(S) || !aligned4(alpha) || !aligned4(eta)) return FALCON_ERR_UNSUPPORTED;
+    falcon::DecodeArgs a;
+    a.S = S;
+    a.k_cache = k_cache;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = alpha;
+    a.eta = eta;
+    a.o = o;
+    a.NH = N * H;
+    a.norm = norm_of(var);
+    a.delta = is_delta(var) ? 1 : 0;
+    a.eps = eps;
+    hipError_t e = falcon::launch_decode(a, (int)dt, dk, stream);
+    return e == hipSuccess ? FALCON_OK : FALCON_ERR_HIP;
+}
+
+const char* falcon_status_string(int status) {
+    switch (status) {
+        case FALCON_OK: return "ok";
+        case FALCON_ERR_NULL: return "a required pointer is NULL";
+        case FALCON_ERR_SHAPE: return "a size is out of range or inconsistent";
+        case FALCON_ERR_UNSUPPORTED: return "arguments outside the supported set";
+        case FALCON_ERR_WORKSPACE: return "workspace missing or too small";
+        case FALCON_ERR_HIP: return "HIP reported an error at launch";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,140 @@
+// falcon_decode.hip -- one decode step of the Falcon recurrence for many
+// independent heads (gfx950).
+//
+// One step of the recurrence ("Fast Weight Attention for Continual Learning",
+// authors' abstract: prefix-aligned example (k_{t-1}, v_t), read after the
+// write; KLA abstract: normalized step, decay then delta write), for
+// Falcon-1/1A (u = eta x / (||x||^2 + eps)) and Falcon-2/2A (per-column
+// normalizer u_j = eta x_j / (|x_j| ||x||_1 + eps)):
+//     x = k_cache,  S' = alpha S,  r = v - S'x  (A forms: r = v)
+//     S = S' + r u^T,  o = S q = alpha S q + (u . q) r,  k_cache <- k
+// S is read once and written once: Sx and Sq come from the same pass over
+// the registers, and o is formed without a second read of S.
+//
+// Work decomposition: one 256-thread workgroup per head; the d_v x d_k fp32
+// state (64 KiB at d = 128) sits in registers, 64 floats per lane.  Lane
+// groups of d/16 consecutive lanes share a row, each lane holding 16 columns
+// as four 16-byte pieces spaced so that one load instruction of a wave
+// covers whole 128-byte row segments.  Row dot products and the norms of x
+// are reduced within the lane group with cross-lane shuffles.  The kernel
+// is bound by HBM: 2 * d_v * d_k * 4 bytes of state traffic per head-step.
+#include "falcon_device.h"
+#include "falcon_internal.h"
+
+namespace falcon {
+
+template <class E, int D>
+__global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
+    using T = typename E::T;
+    constexpr int LPR = D / 16;               // lanes per row
+    constexpr int ROWS_PER_PASS = 256 / LPR;
+    constexpr int RPT = D / ROWS_PER_PASS;    // rows per thread
+    const int tid = threadIdx.x;
+    const int seg = tid % LPR;
+    const int row0 = tid / LPR;
+    const size_t head = blockIdx.x;
+
+    float* S = a.S + head * D * D;
+    T* kc = static_cast<T*>(a.k_cache) + head * D;
+    const T* qh = static_cast<const T*>(a.q) + head * D;
+    const T* kh = static_cast<const T*>(a.k) + head * D;
+    const T* vh = static_cast<const T*>(a.v) + head * D;
+    T* oh = static_cast<T*>(a.o) + head * D;
+    const float al = a.alpha[head];
+    const float et = a.eta[head];
+
+    // columns of this lane: 4*seg + 4*LPR*j + e, j, e in 0..3
+    float x[16], qv[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int c = 4 * seg + 4 * LPR * j;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[4 * j + e] = E::to_f(kc[c + e]);
+            qv[4 * j + e] = E::to_f(qh[c + e]);
+        }
+    }
+    f32x4 s[RPT][4];
+#pragma unroll
+    for (int p = 0; p < RPT; ++p) {
+        const int row = row0 + ROWS_PER_PASS * p;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            s[p][j] = *reinterpret_cast<const f32x4*>(S + (size_t)row * D + 4 * seg + 4 * LPR * j);
+    }
+
+    float n2 = 0.f, n1 = 0.f, xq = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        n2 += x[c] * x[c];
+        n1 += fabsf(x[c]);
+        xq += x[c] * qv[c];
+    }
+    n2 = group_sum<LPR>(n2);
+    n1 = group_sum<LPR>(n1);
+    float u[16];
+    float uq = 0.f;
+    if (a.norm == kNormScalar) {
+        const float den = n2 + a.eps;
+        const float b = den > 0.f ? et / den : 0.f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) u[c] = b * x[c];
+        uq = b * group_sum<LPR>(xq);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const float den = fabsf(x[c]) * n1 + a.eps;
+            u[c] = den > 0.f ? et * x[c] / den : 0.f;
+            uq += u[c] * qv[c];
+        }
+        uq = group_sum<LPR>(uq);
+    }
+
+#pragma unroll
+    for (int p = 0; p < RPT; ++p) {
+        const int row = row0 + ROWS_PER_PASS * p;
+        float sx = 0.f, sq = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sx += s[p][j][e] * x[4 * j + e];
+                sq += s[p][j][e] * qv[4 * j + e];
+            }
+        sx = group_sum<LPR>(sx);
+        sq = group_sum<LPR>(sq);
+        const float vr = E::to_f(vh[row]);
+        const float r = a.delta ? vr - al * sx : vr;
+        if (seg == 0) oh[row] = E::from_f(al * sq + uq * r);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f32x4 nv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) nv[e] = al * s[p][j][e] + r * u[4 * j + e];
+            *reinterpret_cast<f32x4*>(S + (size_t)row * D + 4 * seg + 4 * LPR * j) = nv;
+        }
+    }
+    __syncthreads();  // every lane has read the previous key
+    if (tid < D) kc[tid] = kh[tid];
+}
+
+bool decode_supported(int dt, int D) { return (dt == 0 || dt == 1) && (D == 64 || D == 128); }
+
+template <class E, int D>
+static hipError_t launch_dec(const DecodeArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_step_kernel<E, D>), dim3(a.NH), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int dt, int D, hipStream_t stream) {
+    if (dt == 1) {
+        if (D == 64) return launch_dec<EBf16, 64>(a, stream);
+        if (D == 128) return launch_dec<EBf16, 128>(a, stream);
+    } else {
+        if (D == 64) return launch_dec<EFp32, 64>(a, stream);
+        if (D == 128) return launch_dec<EFp32, 128>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace falcon

@@ -1,0 +1,97 @@
+// falcon_device.h -- device-side building blocks for the gfx950 kernels:
+// element policies (bf16 / fp32), MFMA fragment conventions and small
+// wavefront utilities.
+//
+// Fragment conventions (wave64, lane l, group g = l / 16, lr = l % 16), for a
+// 16 x 16 x 16 step of a matrix product C += A * B:
+//   A fragment  lane holds A[m = lr][k = 4g + r],     r = 0..3
+//   B fragment  lane holds B[k = 4g + r][n = lr],     r = 0..3
+//   accumulator lane holds C[m = 4g + r][n = lr],     r = 0..3
+// These are the operand layouts of v_mfma_f32_16x16x16_bf16 and, applied
+// instruction by instruction, of four v_mfma_f32_16x16x4_f32.  Consequence
+// used throughout: an accumulator tile is, as it stands, the B fragment of a
+// product that contracts over the tile's row index.
+//
+// A K = 32 step concatenates two K = 16 fragments into the eight operand
+// slots of v_mfma_f32_16x16x32_bf16.  The instruction sums over all 32 slot
+// pairs and maps (lane group, slot) to the same K position for A and for B,
+// so any consistent assignment of logical k to slots gives the same sum; the
+// one used here is "slots 0..3 = first 16-block, slots 4..7 = second".
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace falcon {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+// round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+struct EBf16 {
+    using T = uint16_t;   // storage element in HBM and LDS
+    using Frag = s16x4;   // four operand values
+    static constexpr int kBytes = 2;
+    static __device__ __forceinline__ float to_f(T x) { return bf2f(x); }
+    static __device__ __forceinline__ T from_f(float x) { return f2bf(x); }
+    static __device__ __forceinline__ Frag pack(f32x4 v) {
+        Frag f;
+        f.x = (short)f2bf(v.x);
+        f.y = (short)f2bf(v.y);
+        f.z = (short)f2bf(v.z);
+        f.w = (short)f2bf(v.w);
+        return f;
+    }
+    // Four consecutive elements at p (8-byte aligned).
+    static __device__ __forceinline__ Frag load(const T* p) {
+        return *reinterpret_cast<const Frag*>(p);
+    }
+    static __device__ __forceinline__ f32x4 mma16(Frag a, Frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 mma32(Frag a0, Frag a1, Frag b0, Frag b1, f32x4 c) {
+        s16x8 a = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        s16x8 b = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0,
+                                                       0);
+    }
+};
+
+struct EFp32 {
+    using T = float;
+    using Frag = f32x4;
+    static constexpr int kBytes = 4;
+    static __device__ __forceinline__ float to_f(T x) { return x; }
+    static __device__ __forceinline__ T from_f(float x) { return x; }
+    static __device__ __forceinline__ Frag pack(f32x4 v) { return v; }
+    static __device__ __forceinline__ Frag load(const T* p) {
+        return *reinterpret_cast<const Frag*>(p);
+    }
+    static __device__ __forceinline__ f32x4 mma16(Frag a, Frag b, f32x4 c) {
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, c, 0, 0, 0);
+        return c;
+    }
+    static __device__ __forceinline__ f32x4 mma32(Frag a0, Frag a1, Frag b0, Frag b1, f32x4 c) {
+        return mma16(a1, b1, mma16(a0, b0, c));
+    }
+};
+
+// Sum over groups of `width` consecutive lanes (width a power of two <= 64).
+template <int width>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int m = 1; m < width; m <<= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+
+}  // namespace falcon

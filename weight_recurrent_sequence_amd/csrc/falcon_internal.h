@@ -1,0 +1,56 @@
+// falcon_internal.h -- argument blocks and launchers shared by the host
+// library's translation units (not part of the public ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace falcon {
+
+// How the write vector of a step is normalized.
+enum NormKind : int {
+    kNormScalar = 1,  // Falcon-1/1A: u = eta x / (||x||^2 + eps)
+    kNormColumn = 2,  // Falcon-2/2A: u_j = eta x_j / (|x_j| ||x||_1 + eps)
+    kNormWindow = 3   // Falcon-3/3A: b = eta / (sum_w ||x_{t-w}||^2 + eps), writes b x_{t-w}
+};
+
+struct ChunkArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* eta;
+    const float* S0;
+    const void* k_prev;
+    const void* v_prev;
+    void* o;
+    float* S_final;
+    int BH;      // batch * heads
+    int T;
+    int W;       // window (1 unless kNormWindow)
+    int norm;    // NormKind
+    float eps;
+};
+
+struct DecodeArgs {
+    float* S;
+    void* k_cache;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* eta;
+    void* o;
+    int NH;      // sequences * heads
+    int norm;    // kNormScalar or kNormColumn
+    int delta;   // 1: regression (residual write), 0: inner-product write
+    float eps;
+};
+
+// dt: 0 fp32, 1 bf16.  Return false when the combination is not built.
+bool chunk_supported(int dt, int D, int chunk);
+hipError_t launch_chunk(const ChunkArgs& a, int dt, int D, int chunk, bool delta,
+                        hipStream_t stream);
+bool decode_supported(int dt, int D);
+hipError_t launch_decode(const DecodeArgs& a, int dt, int D, hipStream_t stream);
+
+}  // namespace falcon
