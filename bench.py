@@ -1,0 +1,226 @@
+"""Benchmark of the Falcon recurrence on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--copy-calibration]
+
+A step is one falcon_chunk_fwd call (Falcon-1, the path's hot kernel: prologue,
+intra-chunk Grams and triangular blocks, state pass and epilogue fused) over
+the whole batch B=8, H=16, T=4096, d_k=d_v=128, bf16 q/k/v, fp32 state,
+chunk 64, with the inputs resident in HBM.  `value` is tokens (B*T) per
+second.  The same line reports Falcon-1A on the same batch and the decode
+step (256 sequences x 32 heads, d=128, 1024 consecutive steps), each with its
+roofline, and the fp64 CPU oracle timed on this host over a bounded sample of
+the Falcon-1 workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Falcon-1 chunk fwd tokens/s (B8 H16 T4096 d128) + decode tok/s; % roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+
+
+def chunk_bytes(B, H, T, D, elem=2, with_state_out=True):
+    """Algorithmic HBM bytes of one chunk-forward call: q, k, v and o once
+    (elem bytes each element), alpha and eta (fp32), final state (fp32)."""
+    per_token_head = 3 * D * elem + 2 * 4 + D * elem
+    return B * H * T * per_token_head + (B * H * D * D * 4 if with_state_out else 0)
+
+
+def chunk_flops(B, H, T, D, C, delta=True):
+    """Algorithmic flops of the chunk form per call, counted on full C x C
+    tiles: Grams, the triangular solve, the two C x d products per side of the
+    state, and the state update (delta family); A family without the solve."""
+    if delta:
+        per = 2 * C * C * (3 * D + 2 * D) + 6 * C * D * D + 2 * C ** 3 / 3
+    else:
+        per = 2 * C * C * (D + D) + 4 * C * D * D
+    return B * H * (T // C) * per
+
+
+def decode_bytes(N, H, D, elem=2):
+    """Per step: state read + write (fp32), q, k, v, the key cache read and
+    rewritten, alpha, eta, and o."""
+    return N * H * (2 * D * D * 4 + 3 * D * elem + 2 * D * elem + 2 * 4 + D * elem)
+
+
+def timed(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(steps):
+        fn()
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def cpu_baseline(inp, budget_s=12.0):
+    """fp64 oracle on this host's cores over a bounded sample of whole
+    sequences of the Falcon-1 workload."""
+    import numpy as np
+
+    import oracle
+    B, H, T, D = inp.k.shape
+    cores = oracle.num_cpus()
+    # calibrate on one sequence
+    d1 = inp.f64((np.array([0]), np.array([0])))
+    t0 = time.perf_counter()
+    oracle.recurrent("F1", *(d1[x][None] for x in ("q", "k", "v", "alpha", "eta")), nthreads=1)
+    t_one = time.perf_counter() - t0
+    n = int(max(1, min(B * H, budget_s * cores / max(t_one, 1e-6))))
+    n = max(min(n, B * H), 1)
+    idx = np.arange(n)
+    bs, hs = idx // H, idx % H
+    d = inp.f64((bs, hs))
+    t0 = time.perf_counter()
+    used = oracle.recurrent_threads_used(1, n)
+    oracle.recurrent("F1", *(d[x][None] for x in ("q", "k", "v", "alpha", "eta")))
+    wall = time.perf_counter() - t0
+    token_heads_per_s = n * T / wall
+    return {"value": token_heads_per_s / H, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"Falcon-1 fp64 recurrent oracle on {n} of {B * H} (batch, head) "
+                      f"sequences, full T={T}, d={D}; {wall:.1f} s wall; token-heads/s "
+                      f"divided by H={H} to give tokens/s of the full workload"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter scaling)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(each (batch, head) sequence is independent; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import weight_recurrent_sequence_amd as fal
+    from weight_recurrent_sequence_amd import inputs as I
+    if not os.path.exists(fal.binding.LIB_PATH):
+        from weight_recurrent_sequence_amd import _build
+        _build.build()
+    dev = torch.device("cuda:0")
+
+    name = "falcon1_bf16_B8H16T4096d128"
+    w = I.WORKLOADS[name]
+    B, H, T, D, C = w["B"], w["H"], w["T"], w["d"], w["chunk"]
+    inp = I.workload_inputs(name)
+    t = inp.to_torch(dev)
+    o = torch.empty_like(t["v"])
+    S_fin = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(fal.workspace_bytes(B, H, T, D, D, fal.BF16, "F1", 1, C), dtype=torch.uint8,
+                     device=dev)
+
+    def step_f1():
+        fal.chunk_fwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], "F1", chunk=C, o=o,
+                      S_final=S_fin, workspace=ws)
+
+    def step_f1a():
+        fal.chunk_fwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], "F1A", chunk=C, o=o,
+                      S_final=S_fin, workspace=ws)
+
+    print(f"[bench] chunk_fwd F1 {name}: warmup {args.warmup}, steps {args.steps}",
+          file=sys.stderr, flush=True)
+    ms, wall = timed(step_f1, args.steps, args.warmup)
+    tok_s = B * T / (ms / 1e3)
+    nbytes = chunk_bytes(B, H, T, D)
+    nflops = chunk_flops(B, H, T, D, C, delta=True)
+    gbs = nbytes / (ms / 1e3) / 1e9
+    tfs = nflops / (ms / 1e3) / 1e12
+    print(f"[bench] F1A", file=sys.stderr, flush=True)
+    ms_a, _ = timed(step_f1a, args.steps, args.warmup)
+    gbs_a = nbytes / (ms_a / 1e3) / 1e9
+
+    line = {
+        "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "variant": "F1", "B": B, "H": H, "T": T, "d_k": D,
+                   "d_v": D, "chunk": C, "global_batch": B, "seq_len": T, "state": "fp32",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "chunk_fwd_kernel<EBf16,128,64,true>",
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "mfma_tflops": tfs, "mfma_frac_bf16": tfs / BF16_PEAK_TFLOPS,
+                     "algorithmic_flops_per_launch": nflops},
+        "falcon1a": {"tokens_per_s": B * T / (ms_a / 1e3), "ms_per_step": ms_a,
+                     "hbm_gbs": gbs_a, "hbm_frac": gbs_a / HBM_PEAK_GBS},
+    }
+
+    if not args.no_decode:
+        wd = I.WORKLOADS["decode_falcon1_N256H32d128_1024steps"]
+        N, Hd, Dd, steps = wd["N"], wd["H"], wd["d"], args.decode_steps
+        x = I.make_decode_inputs_torch(N, Hd, Dd, Dd, steps, device=dev, seed=wd["seed"])
+        S = x["S0"].clone()
+        kc = x["k_cache0"].clone()
+        od = torch.empty((N, Hd, Dd), dtype=torch.bfloat16, device=dev)
+        counter = [0]
+
+        def dec():
+            s = counter[0] % steps
+            counter[0] += 1
+            fal.decode_step(S, kc, x["q"][s], x["k"][s], x["v"][s], x["alpha"][s],
+                            x["eta"][s], "F1", o=od)
+
+        print(f"[bench] decode {steps} steps", file=sys.stderr, flush=True)
+        best = None
+        for rep in range(3):
+            S.copy_(x["S0"])
+            kc.copy_(x["k_cache0"])
+            counter[0] = 0
+            torch.cuda.synchronize()
+            ms_d, _ = timed(dec, steps, 0)
+            best = ms_d if best is None else min(best, ms_d)
+        db = decode_bytes(N, Hd, Dd)
+        dgbs = db / (best / 1e3) / 1e9
+        line["decode"] = {"workload": "decode_falcon1_N256H32d128_1024steps",
+                          "tokens_per_s": N / (best / 1e3), "ms_per_step": best,
+                          "steps": steps, "roofline": {
+                              "bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS,
+                              "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
+                              "algorithmic_bytes_per_launch": db,
+                              "kernel": "decode_step_kernel<EBf16,128>"}}
+        del x
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = 1 << 30
+
+    if not args.no_cpu:
+        print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -44,8 +44,20 @@ def test_status_strings(L):
     assert binding.status_string(99) == "unknown status"
 
 
-def test_workspace_is_zero_for_the_fused_kernel(L):
-    assert L.falcon_chunk_fwd_workspace(8, 16, 4096, 128, 128, 1, 1, 1, 64) == 0
+def test_workspace_query(L):
+    # one record per (batch*head, tile); a tile holds chunk // window steps
+    n1 = L.falcon_chunk_fwd_workspace(8, 16, 4096, 128, 128, 1, 1, 1, 64)
+    assert n1 > 0 and n1 % (8 * 16 * 64) == 0
+    n3 = L.falcon_chunk_fwd_workspace(2, 16, 32768, 128, 128, 1, 3, 4, 64)
+    assert n3 > 0 and n3 % (2 * 16 * (32768 // 16)) == 0
+    assert L.falcon_chunk_fwd_workspace(8, 16, 0, 128, 128, 1, 1, 1, 64) == 0
+    assert L.falcon_chunk_fwd_workspace(8, 16, 100, 96, 96, 1, 1, 1, 64) == 0   # rejected args
+    # the inner-product family needs no triangular blocks: smaller records
+    assert L.falcon_chunk_fwd_workspace(8, 16, 4096, 128, 128, 1, 11, 1, 64) < n1
+
+
+def test_missing_workspace_is_rejected(L):
+    assert chunk(L) == -4
 
 
 P = 1 << 20  # a fake, 16-byte-aligned "device" address: never dereferenced

@@ -101,11 +101,14 @@ def workspace_bytes(B, H, T, dk, dv, dtype, variant, window=1, chunk=64) -> int:
 
 
 def chunk_fwd(q, k, v, alpha, eta, variant, *, window=1, chunk=64, eps=1e-6, S0=None,
-              k_prev=None, v_prev=None, o=None, S_final=None, return_state=True, stream=None):
+              k_prev=None, v_prev=None, o=None, S_final=None, return_state=True,
+              workspace=None, stream=None):
     """Chunk-parallel forward.  q,k [B,H,T,dk]; v [B,H,T,dv] (bf16 or fp32);
     alpha, eta [B,H,T] fp32; S0 [B,H,dv,dk] fp32 or None; k_prev [B,H,W,dk],
-    v_prev [B,H,W-1,dv] or None.  Returns (o, S_final) (S_final None if
-    return_state is False and none was given)."""
+    v_prev [B,H,W-1,dv] or None.  `workspace` (uint8 device tensor of at
+    least workspace_bytes(...) bytes) is allocated per call when omitted.
+    Returns (o, S_final) (S_final None if return_state is False and none was
+    given)."""
     import torch
     var = _variant(variant)
     B, H, T, dk = k.shape
@@ -130,7 +133,12 @@ def chunk_fwd(q, k, v, alpha, eta, variant, *, window=1, chunk=64, eps=1e-6, S0=
         S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     _check(S_final, "S_final", (B, H, dv, dk), torch.float32, dev)
     ws_n = workspace_bytes(B, H, T, dk, dv, dtc, var, window, chunk)
-    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n > 0 else None
+    if workspace is not None:
+        if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_n:
+            raise ValueError(f"workspace: need {ws_n} bytes on {dev}")
+        ws, ws_n = workspace, workspace.numel() * workspace.element_size()
+    else:
+        ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n > 0 else None
     st = lib().falcon_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(S0),
                                 _ptr(k_prev), _ptr(v_prev), _ptr(o), _ptr(S_final), B, H, T, dk,
                                 dv, dtc, var, window, chunk, float(eps), _ptr(ws), ws_n,

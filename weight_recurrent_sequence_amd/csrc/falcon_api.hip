@@ -60,9 +60,13 @@ extern "C" {
 
 size_t falcon_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, falcon_dtype dt,
                                   falcon_variant var, int window, int chunk) {
-    (void)B; (void)H; (void)T; (void)dk; (void)dv; (void)dt; (void)var; (void)window;
-    (void)chunk;
-    return 0;  // the fused kernel keeps everything in registers and LDS
+    // Sizes only: pointers are not needed to size the workspace.
+    const void* p = reinterpret_cast<const void*>(uintptr_t(256));
+    if (check_chunk(p, p, p, (const float*)p, (const float*)p, nullptr, nullptr, nullptr, p,
+                    nullptr, B, H, T, dk, dv, dt, var, window, chunk, 0.0f) != FALCON_OK)
+        return 0;
+    return falcon::chunk_workspace_bytes(B * H, T, (int)dt, chunk, window, norm_of(var),
+                                         is_delta(var));
 }
 
 int falcon_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
@@ -92,7 +96,7 @@ int falcon_chunk_fwd(const void* q, const void* k, const void* v, const float* a
     a.W = window;
     a.norm = norm_of(var);
     a.eps = eps;
-    hipError_t e = falcon::launch_chunk(a, (int)dt, dk, chunk, is_delta(var), stream);
+    hipError_t e = falcon::launch_chunk(a, (int)dt, dk, chunk, is_delta(var), workspace, stream);
     return e == hipSuccess ? FALCON_OK : FALCON_ERR_HIP;
 }
 

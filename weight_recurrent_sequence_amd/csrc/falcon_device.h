@@ -52,6 +52,15 @@ struct EBf16 {
     static __device__ __forceinline__ Frag load(const T* p) {
         return *reinterpret_cast<const Frag*>(p);
     }
+    // Four elements spaced `stride` apart (a column of a row-major tile).
+    static __device__ __forceinline__ Frag gather4(const T* p, int stride) {
+        Frag f;
+        f.x = (short)p[0];
+        f.y = (short)p[stride];
+        f.z = (short)p[2 * stride];
+        f.w = (short)p[3 * stride];
+        return f;
+    }
     static __device__ __forceinline__ f32x4 mma16(Frag a, Frag b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
     }
@@ -73,6 +82,9 @@ struct EFp32 {
     static __device__ __forceinline__ Frag pack(f32x4 v) { return v; }
     static __device__ __forceinline__ Frag load(const T* p) {
         return *reinterpret_cast<const Frag*>(p);
+    }
+    static __device__ __forceinline__ Frag gather4(const T* p, int stride) {
+        return Frag{p[0], p[stride], p[2 * stride], p[3 * stride]};
     }
     static __device__ __forceinline__ f32x4 mma16(Frag a, Frag b, f32x4 c) {
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, c, 0, 0, 0);

@@ -48,7 +48,10 @@ struct DecodeArgs {
 
 // dt: 0 fp32, 1 bf16.  Return false when the combination is not built.
 bool chunk_supported(int dt, int D, int chunk);
-hipError_t launch_chunk(const ChunkArgs& a, int dt, int D, int chunk, bool delta,
+// Bytes of the per-tile records the intra-chunk kernel hands to the
+// state-passing kernel.
+size_t chunk_workspace_bytes(int BH, int T, int dt, int chunk, int window, int norm, bool delta);
+hipError_t launch_chunk(const ChunkArgs& a, int dt, int D, int chunk, bool delta, void* ws,
                         hipStream_t stream);
 bool decode_supported(int dt, int D);
 hipError_t launch_decode(const DecodeArgs& a, int dt, int D, hipStream_t stream);
