@@ -21,12 +21,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace falcon {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// 16-byte staging vector (a native vector type: copies are loads and stores,
+// never memcpy, so arrays of it stay in registers)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
@@ -97,6 +102,20 @@ struct EFp32 {
         return mma16(a1, b1, mma16(a0, b0, c));
     }
 };
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0..N-1, so that
+// register arrays are only ever indexed by constants.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>());
+        static_for_impl<I + 1, N>(f);
+    }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl<0, N>(f);
+}
 
 // Sum over groups of `width` consecutive lanes (width a power of two <= 64).
 template <int width>
