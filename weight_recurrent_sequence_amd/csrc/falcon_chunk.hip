@@ -165,8 +165,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a, void* ws, 
                 }
             }
         }
-        n2 = group_sum<4>(n2);
-        n1 = group_sum<4>(n1);
+        n2 = group_sum_dpp<4>(n2);
+        n1 = group_sum_dpp<4>(n1);
         if (i < CV && part == 0) {
             sm.nrm[i] = n2;
             sm.l1[i] = n1;
@@ -501,9 +501,47 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs a, const void
         const float* hrow = gam + CV;
         const float* gq = gam + 2 * CV;
 
+        // column fragment of a row-major LDS tile: lane (lr, grp) gets
+        // M[row0 + 4 grp + r][col0 + lr], r = 0..3
+        auto colfrag = [&](const T* m, int ld, int row0, int col0) __attribute__((always_inline)) {
+            if constexpr (E::kBytes == 2)
+                return E::load_tr(m + (size_t)(row0 + 4 * grp + (lr >> 2)) * ld + col0 + 4 * (lr & 3));
+            else
+                return E::gather4(m + (size_t)(row0 + 4 * grp) * ld + col0 + lr, ld);
+        };
+        constexpr int LDY = 64 + Smem::PADE;
+
         Frag SB[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) SB[kb] = E::pack(Sacc[kb]);
+
+        // Z = X S0^T and Zq = Q S0^T: 2 NB independent accumulation chains
+        f32x4 Z[NB], Zq[NB];
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) {
+            Z[rb] = zero4();
+            Zq[rb] = zero4();
+        }
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m) {
+            Frag xf0[NB], xf1[NB], qf0[NB], qf1[NB];
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) {
+                const T* xr = &sm.X[16 * rb + lr][32 * m + 4 * grp];
+                const T* qr = &sm.Q[16 * rb + lr][32 * m + 4 * grp];
+                if (DELTA) {
+                    xf0[rb] = E::load(xr);
+                    xf1[rb] = E::load(xr + 16);
+                }
+                qf0[rb] = E::load(qr);
+                qf1[rb] = E::load(qr + 16);
+            }
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) {
+                if (DELTA) Z[rb] = E::mma32(xf0[rb], xf1[rb], SB[2 * m], SB[2 * m + 1], Z[rb]);
+                if (rb < NBQ) Zq[rb] = E::mma32(qf0[rb], qf1[rb], SB[2 * m], SB[2 * m + 1], Zq[rb]);
+            }
+        }
 
         f32x4 Dl[NB];
         Frag DB[NB];
@@ -512,35 +550,31 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs a, const void
             f32x4 Rr[NB];
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb) {
-                f32x4 acc = zero4();
-                const T* ar = &sm.X[16 * rb + lr][0];
-#pragma unroll
-                for (int m = 0; m < D / 32; ++m)
-                    acc = E::mma32(E::load(ar + 32 * m + 4 * grp), E::load(ar + 32 * m + 16 + 4 * grp),
-                                   SB[2 * m], SB[2 * m + 1], acc);
+                const Frag yf = colfrag(&sm.Y[0][0], LDY, 16 * rb, 16 * wave);
                 const f32x4 gm = *reinterpret_cast<const f32x4*>(gam + 16 * rb + 4 * grp);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    Rr[rb][r] = E::to_f(sm.Y[16 * rb + 4 * grp + r][16 * wave + lr]) - gm[r] * acc[r];
+                for (int r = 0; r < 4; ++r) Rr[rb][r] = E::to_f((T)yf[r]) - gm[r] * Z[rb][r];
             }
             // blocked forward substitution: Delta_b = Td_b (R_b - sum_{c<b} A_bc Delta_c)
+            Frag Af[Rec<E, CV, DELTA>::NBA > 0 ? Rec<E, CV, DELTA>::NBA : 1], Tf[NB];
+#pragma unroll
+            for (int q = 0; q < R::NBA; ++q) Af[q] = E::load(recT + R::kA + (size_t)q * 256 + lane * 4);
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) Tf[rb] = E::load(recT + R::kD + (size_t)rb * 256 + lane * 4);
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb) {
                 f32x4 acc = Rr[rb];
 #pragma unroll
-                for (int cb = 0; cb < rb; ++cb)
-                    acc = E::mma16(E::load(recT + R::kA + (size_t)R::ablk(rb, cb) * 256 + lane * 4),
-                                   DB[cb], acc);
-                Dl[rb] = E::mma16(E::load(recT + R::kD + (size_t)rb * 256 + lane * 4), E::pack(acc),
-                                  zero4());
+                for (int cb = 0; cb < rb; ++cb) acc = E::mma16(Af[R::ablk(rb, cb)], DB[cb], acc);
+                Dl[rb] = E::mma16(Tf[rb], E::pack(acc), zero4());
                 DB[rb] = E::pack(Dl[rb]);
             }
         } else {
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb) {
+                const Frag yf = colfrag(&sm.Y[0][0], LDY, 16 * rb, 16 * wave);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    Dl[rb][r] = E::to_f(sm.Y[16 * rb + 4 * grp + r][16 * wave + lr]);
+                for (int r = 0; r < 4; ++r) Dl[rb][r] = E::to_f((T)yf[r]);
                 DB[rb] = E::pack(Dl[rb]);
             }
         }
@@ -549,12 +583,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs a, const void
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb) {
             if (tb >= NBQ) continue;
-            f32x4 acc = zero4();
-            const T* ar = &sm.Q[16 * tb + lr][0];
-#pragma unroll
-            for (int m = 0; m < D / 32; ++m)
-                acc = E::mma32(E::load(ar + 32 * m + 4 * grp), E::load(ar + 32 * m + 16 + 4 * grp),
-                               SB[2 * m], SB[2 * m + 1], acc);
+            f32x4 acc = Zq[tb];
             const f32x4 gqv = *reinterpret_cast<const f32x4*>(gq + 16 * tb + 4 * grp);
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[r] *= gqv[r];
@@ -570,7 +599,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs a, const void
         }
 
         // state update S^T = exp(g_last) S0^T + Omega^T diag(hrow) Delta; the A
-        // operand Omega^T is read column-wise from the row-major tile
+        // operand Omega^T comes from the row-major tile by column fragments
         Frag HB[NB];
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) {
@@ -587,15 +616,14 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs a, const void
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             f32x4 acc = Sacc[kb] * glq;
-            const T* col = om + 16 * kb + lr;
             if constexpr (NB == 1) {
-                acc = E::mma16(E::gather4(col + (4 * grp) * LDX, LDX), HB[0], acc);
+                acc = E::mma16(colfrag(om, LDX, 0, 16 * kb), HB[0], acc);
             } else {
 #pragma unroll
                 for (int m = 0; m < NB / 2; ++m)
-                    acc = E::mma32(E::gather4(col + (32 * m + 4 * grp) * LDX, LDX),
-                                   E::gather4(col + (32 * m + 16 + 4 * grp) * LDX, LDX), HB[2 * m],
-                                   HB[2 * m + 1], acc);
+                    acc = E::mma32(colfrag(om, LDX, 32 * m, 16 * kb),
+                                   colfrag(om, LDX, 32 * m + 16, 16 * kb), HB[2 * m], HB[2 * m + 1],
+                                   acc);
             }
             Sacc[kb] = acc;
         }

@@ -16,7 +16,7 @@
 // groups of d/16 consecutive lanes share a row, each lane holding 16 columns
 // as four 16-byte pieces spaced so that one load instruction of a wave
 // covers whole 128-byte row segments.  Row dot products and the norms of x
-// are reduced within the lane group with cross-lane shuffles.  The kernel
+// are reduced within the lane group with DPP lane permutations.  The kernel
 // is bound by HBM: 2 * d_v * d_k * 4 bytes of state traffic per head-step.
 #include "falcon_device.h"
 #include "falcon_internal.h"
@@ -48,10 +48,11 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int c = 4 * seg + 4 * LPR * j;
+        const typename E::Frag xf = E::load(kc + c), qf = E::load(qh + c);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            x[4 * j + e] = E::to_f(kc[c + e]);
-            qv[4 * j + e] = E::to_f(qh[c + e]);
+            x[4 * j + e] = E::to_f((T)xf[e]);
+            qv[4 * j + e] = E::to_f((T)qf[e]);
         }
     }
     f32x4 s[RPT][4];
@@ -70,8 +71,13 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
         n1 += fabsf(x[c]);
         xq += x[c] * qv[c];
     }
-    n2 = group_sum<LPR>(n2);
-    n1 = group_sum<LPR>(n1);
+    n2 = group_sum_dpp<LPR>(n2);
+    n1 = group_sum_dpp<LPR>(n1);
+    // Every lane has now consumed the previous key (its x registers are
+    // loaded); after this barrier k_cache may be overwritten.  It comes before
+    // any global store, so it does not wait for the state write-back.
+    __syncthreads();
+    if (tid < D) kc[tid] = kh[tid];
     float u[16];
     float uq = 0.f;
     if (a.norm == kNormScalar) {
@@ -79,7 +85,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
         const float b = den > 0.f ? et / den : 0.f;
 #pragma unroll
         for (int c = 0; c < 16; ++c) u[c] = b * x[c];
-        uq = b * group_sum<LPR>(xq);
+        uq = b * group_sum_dpp<LPR>(xq);
     } else {
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
@@ -87,7 +93,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
             u[c] = den > 0.f ? et * x[c] / den : 0.f;
             uq += u[c] * qv[c];
         }
-        uq = group_sum<LPR>(uq);
+        uq = group_sum_dpp<LPR>(uq);
     }
 
 #pragma unroll
@@ -101,8 +107,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
                 sx += s[p][j][e] * x[4 * j + e];
                 sq += s[p][j][e] * qv[4 * j + e];
             }
-        sx = group_sum<LPR>(sx);
-        sq = group_sum<LPR>(sq);
+        sx = group_sum_dpp<LPR>(sx);
+        sq = group_sum_dpp<LPR>(sq);
         const float vr = E::to_f(vh[row]);
         const float r = a.delta ? vr - al * sx : vr;
         if (seg == 0) oh[row] = E::from_f(al * sq + uq * r);
@@ -114,8 +120,6 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
             *reinterpret_cast<f32x4*>(S + (size_t)row * D + 4 * seg + 4 * LPR * j) = nv;
         }
     }
-    __syncthreads();  // every lane has read the previous key
-    if (tid < D) kc[tid] = kh[tid];
 }
 
 bool decode_supported(int dt, int D) { return (dt == 0 || dt == 1) && (D == 64 || D == 128); }

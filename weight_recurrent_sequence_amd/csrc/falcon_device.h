@@ -66,6 +66,17 @@ struct EBf16 {
         f.w = (short)p[3 * stride];
         return f;
     }
+    // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16
+    // lanes, lane i receives in slot s the element (i % 4) of the 8 bytes that
+    // lane 4 s + i / 4 of the group addressed.  So if lane i of a group
+    // addresses  row0 + i / 4,  column col0 + 4 (i % 4)  of a row-major tile,
+    // lane i receives rows row0 .. row0 + 3 of column col0 + i: a column
+    // fragment (B-fragment order of the tile, A-fragment order of its
+    // transpose) in one instruction.
+    static __device__ __forceinline__ Frag load_tr(const T* p) {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(p));
+    }
     static __device__ __forceinline__ f32x4 mma16(Frag a, Frag b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
     }
@@ -115,6 +126,24 @@ __device__ __forceinline__ void static_for_impl(F&& f) {
 template <int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
     static_for_impl<0, N>(f);
+}
+
+// Sum over aligned groups of `width` consecutive lanes, width in {2,4,8,16},
+// with DPP lane permutations (VALU only, no LDS round trip): quad_perm swaps
+// within quads, then the half-row and row mirrors fold 8 and 16 lanes.
+template <int width>
+__device__ __forceinline__ float group_sum_dpp(float x) {
+    static_assert(width == 2 || width == 4 || width == 8 || width == 16, "dpp group width");
+    auto dpp = [](float v, auto ctrl) {
+        return __builtin_bit_cast(
+            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), decltype(ctrl)::value,
+                                               0xF, 0xF, false));
+    };
+    x += dpp(x, std::integral_constant<int, 0xB1>());      // quad_perm [1,0,3,2]
+    if constexpr (width >= 4) x += dpp(x, std::integral_constant<int, 0x4E>());   // [2,3,0,1]
+    if constexpr (width >= 8) x += dpp(x, std::integral_constant<int, 0x141>());  // row_half_mirror
+    if constexpr (width >= 16) x += dpp(x, std::integral_constant<int, 0x140>()); // row_mirror
+    return x;
 }
 
 // Sum over groups of `width` consecutive lanes (width a power of two <= 64).
