@@ -2,14 +2,20 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--copy-calibration]
 
-A step is one falcon_chunk_fwd call (Falcon-1, the path's hot kernel: prologue,
-intra-chunk Grams and triangular blocks, state pass and epilogue fused) over
-the whole batch B=8, H=16, T=4096, d_k=d_v=128, bf16 q/k/v, fp32 state,
-chunk 64, with the inputs resident in HBM.  `value` is tokens (B*T) per
-second.  The same line reports Falcon-1A on the same batch and the decode
-step (256 sequences x 32 heads, d=128, 1024 consecutive steps), each with its
-roofline, and the fp64 CPU oracle timed on this host over a bounded sample of
-the Falcon-1 workload.
+A step is one falcon_chunk_fwd call for Falcon-1 over the whole batch B=8,
+H=16, T=4096, d_k=d_v=128, bf16 q/k/v, fp32 state, chunk 64, with the inputs
+resident in HBM: the intra-chunk kernel (prologue, masked Gram blocks,
+diagonal-block inverses) and the state-passing kernel (residuals, blocked
+forward substitution, outputs, state update, epilogue).  `value` is tokens
+(B*T) per second.  The same line reports Falcon-1A on the same batch and the
+decode step (256 sequences x 32 heads, d=128, 1024 consecutive steps), each
+with its roofline, and the fp64 CPU oracle timed on this host over a bounded
+sample of the Falcon-1 workload.
+
+roofline.achieved is the algorithmic HBM bytes of one call (q, k, v, o once,
+alpha, eta, final state) over the call's HIP-event time on the launch
+stream; roofline.traffic is the HBM bytes the PMC counters measured for the
+same call (profiles/), or null when the kernel sources changed since.
 """
 from __future__ import annotations
 
@@ -49,6 +55,24 @@ def decode_bytes(N, H, D, elem=2):
     """Per step: state read + write (fp32), q, k, v, the key cache read and
     rewritten, alpha, eta, and o."""
     return N * H * (2 * D * D * 4 + 3 * D * elem + 2 * D * elem + 2 * 4 + D * elem)
+
+
+def measured_traffic(entry):
+    """HBM bytes per call from profiles/traffic.json, if the kernel sources
+    still hash to what the counters were taken on; else None."""
+    import hashlib
+    try:
+        t = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+        e = t["entries"][entry]
+        m = hashlib.sha256()
+        for f in e["sources"]:
+            m.update(open(os.path.join(ROOT, "weight_recurrent_sequence_amd", "csrc", f), "rb").read())
+        if m.hexdigest() != e["sources_sha256"]:
+            return None
+        return sum(k["fetch_kib"] * 1024 * t["fetch_scale"] + k["write_kib"] * 1024 * t["write_scale"]
+                   for k in e["kernels"].values())
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def timed(fn, steps, warmup):
@@ -111,8 +135,8 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(each (batch, head) sequence is independent; see the design notes)",
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(every (batch, head) sequence is independent; shard batch x head across GPUs)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -164,13 +188,15 @@ def main():
                    "d_v": D, "chunk": C, "global_batch": B, "seq_len": T, "state": "fp32",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "chunk_fwd_kernel<EBf16,128,64,true>",
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("chunk_fwd_F1_B8H16T4096d128_bf16_c64"),
+                     "kernel": "chunk_prep_kernel + chunk_scan_kernel (one falcon_chunk_fwd call)",
                      "algorithmic_bytes_per_launch": nbytes,
                      "mfma_tflops": tfs, "mfma_frac_bf16": tfs / BF16_PEAK_TFLOPS,
                      "algorithmic_flops_per_launch": nflops},
         "falcon1a": {"tokens_per_s": B * T / (ms_a / 1e3), "ms_per_step": ms_a,
-                     "hbm_gbs": gbs_a, "hbm_frac": gbs_a / HBM_PEAK_GBS},
+                     "hbm_gbs": gbs_a, "hbm_frac": gbs_a / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("chunk_fwd_F1A_B8H16T4096d128_bf16_c64")},
     }
 
     if not args.no_decode:
@@ -204,6 +230,7 @@ def main():
                           "steps": steps, "roofline": {
                               "bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS,
                               "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
+                              "traffic": measured_traffic("decode_F1_N256H32d128_bf16"),
                               "algorithmic_bytes_per_launch": db,
                               "kernel": "decode_step_kernel<EBf16,128>"}}
         del x

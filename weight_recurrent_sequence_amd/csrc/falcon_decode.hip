@@ -24,7 +24,7 @@
 namespace falcon {
 
 template <class E, int D>
-__global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 4) void decode_step_kernel(DecodeArgs a) {
     using T = typename E::T;
     constexpr int LPR = D / 16;               // lanes per row
     constexpr int ROWS_PER_PASS = 256 / LPR;
