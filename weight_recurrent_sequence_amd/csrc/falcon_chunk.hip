@@ -68,6 +68,7 @@ struct Rec {
 
 static inline int tiles_of(int T, int Ct) { return (T + Ct - 1) / Ct; }
 
+
 __device__ __forceinline__ u32x4 sel16(bool ok, u32x4 v) {
     return ok ? v : u32x4{0u, 0u, 0u, 0u};
 }
@@ -648,6 +649,754 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs a, const void
 }
 
 // ---------------------------------------------------------------------------
+// Kernel 2, bf16 form: the state pass split into a chain half and an output
+// half of one workgroup (8 waves, two per SIMD).
+//
+//   waves 0-3 (chain)  tile `it`: S0 -> bf16 copy in LDS, Z = X S0^T,
+//                      residuals, forward substitution -> Delta (bf16 copy in
+//                      LDS), state update.  Everything the next tile needs
+//                      is in registers or LDS; no global memory traffic.
+//   waves 4-7 (output) tile `it - 1`: O^T = diag(gq) (S0 Q^T) + Delta^T P^T
+//                      from the two LDS copies, stored straight from the
+//                      accumulators (each lane owns four adjacent columns of
+//                      one row); then stage tile it+1 from registers into LDS
+//                      and issue the global loads of tile it+2.
+// One barrier per tile, fencing LDS only, so the loads in flight stay in
+// flight.  Loads use buffer descriptors: out-of-range rows read as zero in
+// hardware, and a lane's offsets stay fixed from tile to tile.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRawBufferFlags = 0x00020000;  // descriptor word 3 of a raw gfx9 buffer
+constexpr uint32_t kOob = 0x80000000u;       // an offset beyond every record count used here
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int n = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFF0 ? 0x7FFFFFF0 : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kRawBufferFlags);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ s16x4 buf_load8(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(s16x4, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+
+// Workgroup barrier that orders LDS only: global loads and stores in flight
+// are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int D, int CV, bool DELTA, bool COL>
+struct PassSmem {
+    using R = Rec<EBf16, CV, DELTA>;
+    static constexpr int LDX = D + 8;
+    static constexpr int LDY = 64 + 8;
+    static constexpr int KB = D / 16, NB = CV / 16;
+    static constexpr int RECF = (R::NBA + R::NBD) * 512;   // -A and Td fragments (bytes)
+    static constexpr int RECB = RECF + R::NSC * CV * 4;     // then the row factors
+    uint16_t X[2][CV][LDX];     // keys x_i
+    uint16_t Y[2][CV][LDY];     // targets y_i of this slice's 64 value columns
+    uint16_t QU[2][CV][LDX];    // queries q_t; write vectors u_i for the per-column rule
+    s16x4 SB[2][4][KB][64];     // bf16 state at the tile start, fragment order per chain wave
+    s16x4 DB[2][4][NB][64];     // bf16 Delta, fragment order per chain wave
+    alignas(16) char rec[2][RECB];
+};
+
+template <int D, int CV, bool DELTA, bool COL, bool WIN>
+__global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void* ws, int ntiles) {
+    using E = EBf16;
+    using T = uint16_t;
+    using Frag = s16x4;
+    using R = Rec<E, CV, DELTA>;
+    using Smem = PassSmem<D, CV, DELTA, COL>;
+    constexpr int NB = CV / 16, KB = D / 16, CPR = D / 8, NVS = D / 64;
+    constexpr int LDX = Smem::LDX, LDY = Smem::LDY;
+    constexpr int NXL = (CV * CPR + 255) / 256;  // 16-byte pieces of a key tile per stager
+    constexpr int NYL = (CV * 8 + 255) / 256;    // of a target tile
+    constexpr int RCH = Smem::RECB / 16, RFC = Smem::RECF / 16;
+    constexpr int NRL = (RCH + 255) / 256;
+    constexpr bool QG = COL;  // queries as register fragments from global memory
+    __shared__ Smem sm;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4,
+              lr = lane & 15;
+    const bool chain = wave < 4;
+    const int cw = wave & 3;  // value-column block (16 columns) of this wave
+    const int blk = blockIdx.x;
+    const int xcd = blk & 7;
+    const int jj = blk >> 3;
+    const int bh = (jj / NVS) * 8 + xcd;
+    const int vs = jj % NVS;
+    if (bh >= a.BH) return;
+    const int v0 = vs * 64;
+
+    const int W = a.W;
+    const int Wv = WIN ? W : 1;
+    const int Ct = CV / Wv, NVR = Ct * Wv, NBQ = (Ct + 15) / 16;
+    const int T_ = a.T;
+    const float eps = a.eps;
+    const T* qg = static_cast<const T*>(a.q) + (size_t)bh * T_ * D;
+    const T* kg = static_cast<const T*>(a.k) + (size_t)bh * T_ * D;
+    const T* vg = static_cast<const T*>(a.v) + (size_t)bh * T_ * D + v0;
+    const T* kp = a.k_prev ? static_cast<const T*>(a.k_prev) + (size_t)bh * W * D : nullptr;
+    const T* vp = (a.v_prev && W > 1)
+                      ? static_cast<const T*>(a.v_prev) + (size_t)bh * (W - 1) * D + v0
+                      : nullptr;
+    const char* recg = static_cast<const char*>(ws) + (size_t)bh * ntiles * R::kBytes;
+    T* og = static_cast<T*>(a.o) + (size_t)bh * T_ * D + v0;
+    const int ntl = ntiles;
+
+    // ---- chain: state slice as accumulators of S^T (wave cw owns 16 value
+    // columns): Sacc[kb][r] = S[v][k], v = v0 + 16 cw + lr, k = 16 kb + 4 grp + r
+    const int vcol = v0 + 16 * cw + lr;
+    f32x4 Sacc[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+        Sacc[kb] = (chain && a.S0) ? *reinterpret_cast<const f32x4*>(
+                                         a.S0 + ((size_t)bh * D + vcol) * D + 16 * kb + 4 * grp)
+                                   : zero4();
+
+    // ---- output: staging geometry, fixed across tiles ----
+    const int otid = tid - 256;
+    uint32_t xvo[NXL], qvo[NXL], yvo[NYL];  // byte offsets for the descriptor loads
+#pragma unroll
+    for (int it = 0; it < NXL; ++it) {
+        const int c = otid + 256 * it;
+        const int i = c / CPR, col = (c % CPR) * 8;
+        const int s = WIN ? i / Wv : i, w = WIN ? i - s * Wv : 0;
+        const bool ok = c < CV * CPR;
+        xvo[it] = (ok && i < NVR) ? (uint32_t)(((s - w - 1 + W) * D + col) * 2) : kOob;
+        qvo[it] = (ok && i < Ct) ? (uint32_t)((i * D + col) * 2) : kOob;
+    }
+#pragma unroll
+    for (int it = 0; it < NYL; ++it) {
+        const int c = otid + 256 * it;
+        const int i = c / 8, col = (c % 8) * 8;
+        const int s = WIN ? i / Wv : i, w = WIN ? i - s * Wv : 0;
+        yvo[it] = (c < CV * 8 && i < NVR) ? (uint32_t)(((s - w + W - 1) * D + col) * 2) : kOob;
+    }
+
+    u32x4 px[NXL], pq[QG ? 1 : NXL], py[NYL], pr[NRL];
+    float pl1[COL ? NXL : 1], per[COL ? NXL : 1];
+    Frag pP[NB][NB];
+    float pgq[NB];
+    Frag pQf[QG ? NB : 1][QG ? KB : 1];
+
+    // keys, targets and the record of `tile` into registers
+    auto load_xyr = [&](int tile) __attribute__((always_inline)) {
+        const int t0 = tile * Ct;
+        if (t0 >= W) {
+            const rsrc_t rx = make_rsrc(kg + (size_t)(t0 - W) * D, (int64_t)(T_ - t0 + W) * D * 2);
+            const rsrc_t ry =
+                make_rsrc(vg + (size_t)(t0 - W + 1) * D, (int64_t)(T_ - t0 + W - 1) * D * 2);
+#pragma unroll
+            for (int it = 0; it < NXL; ++it) px[it] = buf_load16(rx, xvo[it]);
+#pragma unroll
+            for (int it = 0; it < NYL; ++it) py[it] = buf_load16(ry, yvo[it]);
+        } else {
+            // first tiles: rows before the sequence come from the halo (or are zero)
+#pragma unroll
+            for (int it = 0; it < NXL; ++it) {
+                const int c = otid + 256 * it;
+                const int i = c / CPR, col = (c % CPR) * 8;
+                const int s = WIN ? i / Wv : i, w = WIN ? i - s * Wv : 0;
+                const int tau = t0 + s - w - 1;
+                const bool ok = c < CV * CPR && i < NVR && t0 + s < T_ && (tau >= 0 || kp != nullptr);
+                const T* p = tau >= 0 ? kg + (size_t)tau * D : (kp ? kp + (size_t)(W + tau) * D : kg);
+                px[it] = sel16(ok, *reinterpret_cast<const u32x4*>((ok ? p : kg) + col));
+            }
+#pragma unroll
+            for (int it = 0; it < NYL; ++it) {
+                const int c = otid + 256 * it;
+                const int i = c / 8, col = (c % 8) * 8;
+                const int s = WIN ? i / Wv : i, w = WIN ? i - s * Wv : 0;
+                const int tv = t0 + s - w;
+                const bool ok = c < CV * 8 && i < NVR && t0 + s < T_ && (tv >= 0 || vp != nullptr);
+                const T* p = tv >= 0 ? vg + (size_t)tv * D : (vp ? vp + (size_t)(W - 1 + tv) * D : vg);
+                py[it] = sel16(ok, *reinterpret_cast<const u32x4*>((ok ? p : vg) + col));
+            }
+        }
+        const char* rt = recg + (size_t)tile * R::kBytes;
+#pragma unroll
+        for (int it = 0; it < NRL; ++it) {
+            const int rc = min(otid + 256 * it, RCH - 1);
+            pr[it] = *reinterpret_cast<const u32x4*>(
+                rt + (rc < RFC ? (size_t)rc * 16 : R::kScalBytes + (size_t)(rc - RFC) * 16));
+        }
+        if constexpr (COL) {
+            const float* sc = reinterpret_cast<const float*>(rt + R::kScalBytes);
+#pragma unroll
+            for (int it = 0; it < NXL; ++it) {
+                const int i = min((otid + 256 * it) / CPR, CV - 1);
+                pl1[it] = sc[3 * CV + i];
+                per[it] = sc[4 * CV + i];
+            }
+        }
+    };
+    // queries of `tile`: staged through LDS, or (QG) as register fragments
+    auto load_q = [&](int tile) __attribute__((always_inline)) {
+        const int t0 = tile * Ct;
+        const rsrc_t rq = make_rsrc(qg + (size_t)t0 * D, (int64_t)(T_ - t0) * D * 2);
+        if constexpr (QG) {
+#pragma unroll
+            for (int tb = 0; tb < NB; ++tb) {
+                const int t = 16 * tb + lr;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+                    pQf[tb][kb] = buf_load8(rq, t < Ct ? (uint32_t)((t * D + 16 * kb + 4 * grp) * 2) : kOob);
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < NXL; ++it) pq[it] = buf_load16(rq, qvo[it]);
+        }
+    };
+    auto p_used = [&](int tb, int cb) __attribute__((always_inline)) {
+        return WIN ? (tb < NBQ && (16 * cb) / Wv <= 16 * tb + 15) : (cb <= tb);
+    };
+    // output-side record pieces of `tile`: P fragments and the query decays
+    auto load_p = [&](int tile) __attribute__((always_inline)) {
+        const char* rt = recg + (size_t)tile * R::kBytes;
+        static_for<NB>([&](auto tbc) __attribute__((always_inline)) {
+            constexpr int tb = decltype(tbc)::value;
+            static_for<NB>([&](auto cbc) __attribute__((always_inline)) {
+                constexpr int cb = decltype(cbc)::value;
+                if (WIN || cb <= tb) {
+                    if (p_used(tb, cb))
+                        pP[tb][cb] = *reinterpret_cast<const Frag*>(
+                            rt + R::kP * 2 + (size_t)(tb * NB + cb) * 512 + lane * 8);
+                }
+            });
+            pgq[tb] = reinterpret_cast<const float*>(rt + R::kScalBytes)[2 * CV + 16 * tb + lr];
+        });
+    };
+    auto store_xyr = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+        for (int it = 0; it < NXL; ++it) {
+            const int c = otid + 256 * it;
+            if (c < CV * CPR) {
+                const int i = c / CPR, col = (c % CPR) * 8;
+                *reinterpret_cast<u32x4*>(&sm.X[b][i][col]) = px[it];
+                if constexpr (COL) {
+                    // u = eta x / (|x| ||x||_1 + eps), elementwise
+                    const T* e = reinterpret_cast<const T*>(&px[it]);
+                    u32x4 outv;
+                    T* out = reinterpret_cast<T*>(&outv);
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const float x = E::to_f(e[u]);
+                        const float den = fabsf(x) * pl1[it] + eps;
+                        out[u] = E::from_f(den > 0.f ? per[it] * x / den : 0.f);
+                    }
+                    *reinterpret_cast<u32x4*>(&sm.QU[b][i][col]) = outv;
+                }
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < NYL; ++it) {
+            const int c = otid + 256 * it;
+            if (c < CV * 8) *reinterpret_cast<u32x4*>(&sm.Y[b][c / 8][(c % 8) * 8]) = py[it];
+        }
+#pragma unroll
+        for (int it = 0; it < NRL; ++it) {
+            const int rc = otid + 256 * it;
+            if (rc < RCH) reinterpret_cast<u32x4*>(sm.rec[b])[rc] = pr[it];
+        }
+    };
+    auto store_q = [&](int b) __attribute__((always_inline)) {
+        if constexpr (!QG) {
+#pragma unroll
+            for (int it = 0; it < NXL; ++it) {
+                const int c = otid + 256 * it;
+                if (c < CV * CPR)
+                    *reinterpret_cast<u32x4*>(&sm.QU[b][c / CPR][(c % CPR) * 8]) = pq[it];
+            }
+        }
+    };
+
+    // column fragment of a row-major LDS tile: lane (lr, grp) gets
+    // M[row0 + 4 grp + r][col0 + lr], r = 0..3
+    auto colfrag = [&](const T* m, int ld, int row0, int col0) __attribute__((always_inline)) {
+        return E::load_tr(m + (size_t)(row0 + 4 * grp + (lr >> 2)) * ld + col0 + 4 * (lr & 3));
+    };
+
+    // ---- chain: one tile ----
+    auto chain_tile = [&](int it) __attribute__((always_inline)) {
+        const int b = it & 1;
+        const T* Xb = &sm.X[b][0][0];
+        const T* Yb = &sm.Y[b][0][0];
+        const T* recT = reinterpret_cast<const T*>(sm.rec[b]);
+        const float* gam = reinterpret_cast<const float*>(sm.rec[b] + Smem::RECF);
+        const float* hrow = gam + CV;
+        const float* gq = gam + 2 * CV;
+
+        Frag SB[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            SB[kb] = E::pack(Sacc[kb]);
+            sm.SB[b][cw][kb][lane] = SB[kb];
+        }
+
+        f32x4 Dl[NB];
+        Frag DB[NB];
+        if constexpr (DELTA) {
+            // Z = X S0^T
+            f32x4 Z[NB];
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) Z[rb] = zero4();
+#pragma unroll
+            for (int m = 0; m < D / 32; ++m) {
+                Frag xf0[NB], xf1[NB];
+#pragma unroll
+                for (int rb = 0; rb < NB; ++rb) {
+                    const T* xr = Xb + (16 * rb + lr) * LDX + 32 * m + 4 * grp;
+                    xf0[rb] = E::load(xr);
+                    xf1[rb] = E::load(xr + 16);
+                }
+#pragma unroll
+                for (int rb = 0; rb < NB; ++rb)
+                    Z[rb] = E::mma32(xf0[rb], xf1[rb], SB[2 * m], SB[2 * m + 1], Z[rb]);
+            }
+            // residuals R = Y - diag(gam) Z, then the blocked forward substitution
+            // Delta_b = Td_b (R_b - sum_{c<b} A_bc Delta_c)
+            f32x4 Rr[NB];
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) {
+                const Frag yf = colfrag(Yb, LDY, 16 * rb, 16 * cw);
+                const f32x4 gm = *reinterpret_cast<const f32x4*>(gam + 16 * rb + 4 * grp);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Rr[rb][r] = E::to_f((T)yf[r]) - gm[r] * Z[rb][r];
+            }
+            Frag Af[R::NBA > 0 ? R::NBA : 1], Tf[NB];
+#pragma unroll
+            for (int q = 0; q < R::NBA; ++q) Af[q] = E::load(recT + R::kA + (size_t)q * 256 + lane * 4);
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) Tf[rb] = E::load(recT + R::kD + (size_t)rb * 256 + lane * 4);
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) {
+                f32x4 acc = Rr[rb];
+#pragma unroll
+                for (int cb = 0; cb < rb; ++cb) acc = E::mma16(Af[R::ablk(rb, cb)], DB[cb], acc);
+                Dl[rb] = E::mma16(Tf[rb], E::pack(acc), zero4());
+                DB[rb] = E::pack(Dl[rb]);
+            }
+        } else {
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) {
+                const Frag yf = colfrag(Yb, LDY, 16 * rb, 16 * cw);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Dl[rb][r] = E::to_f((T)yf[r]);
+                DB[rb] = yf;
+            }
+        }
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) sm.DB[b][cw][rb][lane] = DB[rb];
+
+        // S^T = exp(g_last) S0^T + Omega^T diag(hrow) Delta
+        Frag HB[NB];
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) {
+            const f32x4 hv = *reinterpret_cast<const f32x4*>(hrow + 16 * cb + 4 * grp);
+            f32x4 h;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) h[r] = hv[r] * Dl[cb][r];
+            HB[cb] = E::pack(h);
+        }
+        const float glq = gq[Ct - 1];
+        const T* om = COL ? &sm.QU[b][0][0] : Xb;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            f32x4 acc = Sacc[kb] * glq;
+            if constexpr (NB == 1) {
+                acc = E::mma16(colfrag(om, LDX, 0, 16 * kb), HB[0], acc);
+            } else {
+#pragma unroll
+                for (int m = 0; m < NB / 2; ++m)
+                    acc = E::mma32(colfrag(om, LDX, 32 * m, 16 * kb),
+                                   colfrag(om, LDX, 32 * m + 16, 16 * kb), HB[2 * m], HB[2 * m + 1],
+                                   acc);
+            }
+            Sacc[kb] = acc;
+        }
+    };
+
+    // ---- output: one tile, O^T = diag(gq) S0 Q^T + Delta^T P^T ----
+    auto output_tile = [&](int p) __attribute__((always_inline)) {
+        const int pb = p & 1;
+        const int t0 = p * Ct;
+        Frag sb[KB], db[NB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) sb[kb] = sm.SB[pb][cw][kb][lane];
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) db[cb] = sm.DB[pb][cw][cb][lane];
+        static_for<NB>([&](auto tbc) __attribute__((always_inline)) {
+            constexpr int tb = decltype(tbc)::value;
+            if (tb < NBQ) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int m = 0; m < D / 32; ++m) {
+                    Frag q0, q1;
+                    if constexpr (QG) {
+                        q0 = pQf[tb][2 * m];
+                        q1 = pQf[tb][2 * m + 1];
+                    } else {
+                        const T* qr = &sm.QU[pb][16 * tb + lr][32 * m + 4 * grp];
+                        q0 = E::load(qr);
+                        q1 = E::load(qr + 16);
+                    }
+                    acc = E::mma32(sb[2 * m], sb[2 * m + 1], q0, q1, acc);
+                }
+                acc = acc * pgq[tb];
+                static_for<NB>([&](auto cbc) __attribute__((always_inline)) {
+                    constexpr int cb = decltype(cbc)::value;
+                    if (WIN || cb <= tb) {
+                        if (p_used(tb, cb)) acc = E::mma16(db[cb], pP[tb][cb], acc);
+                    }
+                });
+                // lane holds O[t = 16 tb + lr][v = 16 cw + 4 grp + r]
+                const int t = 16 * tb + lr;
+                if (t < Ct && t0 + t < T_)
+                    *reinterpret_cast<Frag*>(og + (size_t)(t0 + t) * D + 16 * cw + 4 * grp) =
+                        E::pack(acc);
+            }
+        });
+    };
+
+    // ---- pipeline ----
+    if (!chain && ntl > 0) {
+        load_xyr(0);
+        if constexpr (!QG) load_q(0);
+        store_xyr(0);
+        if (ntl > 1) load_xyr(1);
+    }
+    lds_barrier();
+    for (int it = 0; it <= ntl; ++it) {
+        if (chain) {
+            if (it < ntl) chain_tile(it);
+        } else {
+            if (it >= 1) output_tile(it - 1);
+            if (it + 1 < ntl) store_xyr((it + 1) & 1);
+            if (it < ntl) store_q(it & 1);
+            if (it + 2 < ntl) load_xyr(it + 2);
+            if constexpr (QG) {
+                if (it < ntl) load_q(it);
+            } else {
+                if (it + 1 < ntl) load_q(it + 1);
+            }
+            if (it < ntl) load_p(it);
+        }
+        lds_barrier();
+    }
+
+    if (chain && a.S_final) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            *reinterpret_cast<f32x4*>(a.S_final + ((size_t)bh * D + vcol) * D + 16 * kb + 4 * grp) =
+                Sacc[kb];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 1, bf16 form: persistent intra-chunk preparation.  Each workgroup
+// walks tiles (batch*head, tile) with a stride of the grid, holding the next
+// tile's keys, queries and gates in registers while it works on the current
+// one, so the loads of one tile overlap the arithmetic of the previous.
+// Per tile: norms, the log-decay scan, the Gram blocks (A: x_i . omega_j,
+// P: q_t . omega_j) shared round-robin over the four waves, masks and decays
+// from per-row and per-column factors, then the 16 x 16 diagonal inverses.
+// Blocks of P that the state pass never reads are not written.
+// ---------------------------------------------------------------------------
+template <int D, int CV, bool COL>
+struct Prep2Smem {
+    static constexpr int LDX = D + 8;
+    uint16_t X[CV][LDX];           // keys x_i (virtual rows)
+    uint16_t Q[CV][LDX];           // queries q_t
+    uint16_t Om[COL ? CV : 1][LDX];  // per-column write vectors u_i
+    float Adg[CV / 16][16][17];    // diagonal blocks of A (fp32), then their inverses
+    float al[CV], et[CV];          // gates of the tile's steps (padding: 1, 0)
+    float nrm[CV], l1[CV];         // ||x_i||^2, ||x_i||_1
+    alignas(16) float gv[CV];      // log2(e) * g of the step of virtual row i
+    alignas(16) float gs[CV];      // log2(e) * g_t per step t
+    alignas(16) float rs[CV];      // row scale r_i of the write vector
+    alignas(16) int step[CV];      // step of virtual row i
+};
+
+template <int D, int CV, bool DELTA, bool COL, bool WIN>
+__global__ __launch_bounds__(256, 2) void chunk_prep2_kernel(ChunkArgs a, void* ws, int ntiles,
+                                                             int njobs) {
+    using E = EBf16;
+    using T = uint16_t;
+    using Frag = s16x4;
+    using R = Rec<E, CV, DELTA>;
+    using Smem = Prep2Smem<D, CV, COL>;
+    constexpr int NB = CV / 16, CPR = D / 8;
+    constexpr int NXL = (CV * CPR + 255) / 256;
+    constexpr int LDX = Smem::LDX;
+    constexpr int NJA = DELTA ? NB * (NB + 1) / 2 : 0;  // A blocks on and below the diagonal
+    constexpr int NJP = WIN ? NB * NB : NB * (NB + 1) / 2;
+    constexpr float kLog2e = 1.4426950408889634f;
+    __shared__ Smem sm;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4,
+              lr = lane & 15;
+    const int W = a.W;
+    const int Wv = WIN ? W : 1;
+    const int Ct = CV / Wv, NVR = Ct * Wv, NBQ = (Ct + 15) / 16;
+    const int T_ = a.T;
+    const float eps = a.eps;
+
+    // staging geometry, fixed across tiles
+    uint32_t xvo[NXL], qvo[NXL];
+#pragma unroll
+    for (int it = 0; it < NXL; ++it) {
+        const int c = tid + 256 * it;
+        const int i = c / CPR, col = (c % CPR) * 8;
+        const int s = WIN ? i / Wv : i, w = WIN ? i - s * Wv : 0;
+        const bool ok = c < CV * CPR;
+        xvo[it] = (ok && i < NVR) ? (uint32_t)(((s - w - 1 + W) * D + col) * 2) : kOob;
+        qvo[it] = (ok && i < Ct) ? (uint32_t)((i * D + col) * 2) : kOob;
+    }
+    u32x4 px[NXL], pq[NXL];
+    float pal = 1.f, pet = 0.f;
+
+    auto load = [&](int job) __attribute__((always_inline)) {
+        const int bh = job / ntiles, tile = job - bh * ntiles;
+        const int t0 = tile * Ct;
+        const T* kg = static_cast<const T*>(a.k) + (size_t)bh * T_ * D;
+        const T* qg = static_cast<const T*>(a.q) + (size_t)bh * T_ * D;
+        if (t0 >= W) {
+            const rsrc_t rx = make_rsrc(kg + (size_t)(t0 - W) * D, (int64_t)(T_ - t0 + W) * D * 2);
+#pragma unroll
+            for (int it = 0; it < NXL; ++it) px[it] = buf_load16(rx, xvo[it]);
+        } else {
+            const T* kp = a.k_prev ? static_cast<const T*>(a.k_prev) + (size_t)bh * W * D : nullptr;
+#pragma unroll
+            for (int it = 0; it < NXL; ++it) {
+                const int c = tid + 256 * it;
+                const int i = c / CPR, col = (c % CPR) * 8;
+                const int s = WIN ? i / Wv : i, w = WIN ? i - s * Wv : 0;
+                const int tau = t0 + s - w - 1;
+                const bool ok = c < CV * CPR && i < NVR && t0 + s < T_ && (tau >= 0 || kp != nullptr);
+                const T* p = tau >= 0 ? kg + (size_t)tau * D : (kp ? kp + (size_t)(W + tau) * D : kg);
+                px[it] = sel16(ok, *reinterpret_cast<const u32x4*>((ok ? p : kg) + col));
+            }
+        }
+        const rsrc_t rq = make_rsrc(qg + (size_t)t0 * D, (int64_t)(T_ - t0) * D * 2);
+#pragma unroll
+        for (int it = 0; it < NXL; ++it) pq[it] = buf_load16(rq, qvo[it]);
+        if (tid < CV) {
+            const bool ok = tid < Ct && t0 + tid < T_;
+            pal = ok ? a.alpha[(size_t)bh * T_ + t0 + tid] : 1.f;  // padding steps: identity
+            pet = ok ? a.eta[(size_t)bh * T_ + t0 + tid] : 0.f;
+        }
+    };
+
+    int job = blockIdx.x;
+    if (job < njobs) load(job);
+    for (; job < njobs; job += gridDim.x) {
+        const int bh = job / ntiles, tile = job - bh * ntiles;
+        char* rec = static_cast<char*>(ws) + ((size_t)bh * ntiles + tile) * R::kBytes;
+        T* recT = reinterpret_cast<T*>(rec);
+        float* recS = reinterpret_cast<float*>(rec + R::kScalBytes);
+
+        // ---- stage the prefetched tile, then prefetch the next ----
+#pragma unroll
+        for (int it = 0; it < NXL; ++it) {
+            const int c = tid + 256 * it;
+            if (c < CV * CPR) {
+                *reinterpret_cast<u32x4*>(&sm.X[c / CPR][(c % CPR) * 8]) = px[it];
+                *reinterpret_cast<u32x4*>(&sm.Q[c / CPR][(c % CPR) * 8]) = pq[it];
+            }
+        }
+        if (tid < CV) {
+            sm.al[tid] = pal;
+            sm.et[tid] = pet;
+        }
+        lds_barrier();
+        if (job + (int)gridDim.x < njobs) load(job + gridDim.x);
+
+        // ---- norms: 4 threads per row ----
+        {
+            const int i = tid >> 2, part = tid & 3;
+            float n2 = 0.f, n1 = 0.f;
+            if (i < CV) {
+#pragma unroll
+                for (int c = 0; c < D / 4; c += 8) {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.X[i][part * (D / 4) + c]);
+                    const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const float x = E::to_f(e[u]);
+                        n2 += x * x;
+                        n1 += fabsf(x);
+                    }
+                }
+            }
+            n2 = group_sum_dpp<4>(n2);
+            n1 = group_sum_dpp<4>(n1);
+            if (i < CV && part == 0) {
+                sm.nrm[i] = n2;
+                sm.l1[i] = n1;
+            }
+        }
+        lds_barrier();
+
+        // ---- log-decay scan and row factors (wave 0) ----
+        if (wave == 0) {
+            const int j = lane;
+            float lg = (j < Ct) ? __logf(sm.al[j]) : 0.f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(lg, off, 64);
+                if (j >= off) lg += y;
+            }
+            const float glast = __shfl(lg, Ct - 1, 64);
+            float bwin = 0.f;  // window normalizer of step j
+            if (WIN && j < Ct) {
+                float tot = 0.f;
+                for (int w = 0; w < Wv; ++w) tot += sm.nrm[j * Wv + w];
+                const float den = tot + eps;
+                bwin = den > 0.f ? sm.et[j] / den : 0.f;
+            }
+            const int sj = WIN ? min(j / Wv, Ct - 1) : min(j, Ct - 1);
+            const float gsj = __shfl(lg, sj, 64);
+            const float bsj = __shfl(bwin, sj, 64);
+            const float esj = __shfl(sm.et[j < CV ? j : 0], sj, 64);
+            if (j < CV) {
+                float r = 0.f;
+                if (j < NVR) {
+                    if (WIN) {
+                        r = bsj;
+                    } else if (COL) {
+                        r = 1.f;
+                    } else {
+                        const float den = sm.nrm[j] + eps;
+                        r = den > 0.f ? esj / den : 0.f;
+                    }
+                }
+                sm.gv[j] = gsj * kLog2e;
+                sm.gs[j] = lg * kLog2e;
+                sm.rs[j] = r;
+                sm.step[j] = (j < NVR) ? sj : (1 << 20);  // padding rows: after every step
+                recS[0 * CV + j] = __expf(gsj);                  // gam
+                recS[1 * CV + j] = __expf(glast - gsj) * r;      // hrow
+                recS[2 * CV + j] = __expf(lg);                   // gq
+                recS[3 * CV + j] = sm.l1[j];                     // l1
+                recS[4 * CV + j] = (j < NVR) ? esj : 0.f;        // erow
+            }
+        }
+        if constexpr (COL) {
+            // u_j = eta x_j / (|x_j| ||x||_1 + eps)
+            for (int c = tid; c < CV * CPR; c += 256) {
+                const int i = c / CPR, col = (c % CPR) * 8;
+                const int s = WIN ? min(i / Wv, Ct - 1) : min(i, Ct - 1);
+                const float et = (i < NVR) ? sm.et[s] : 0.f, l1 = sm.l1[i];
+                const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.X[i][col]);
+                const T* e = reinterpret_cast<const T*>(&v);
+                u32x4 outv;
+                T* out = reinterpret_cast<T*>(&outv);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float x = E::to_f(e[u]);
+                    const float den = fabsf(x) * l1 + eps;
+                    out[u] = E::from_f(den > 0.f ? et * x / den : 0.f);
+                }
+                *reinterpret_cast<u32x4*>(&sm.Om[i][col]) = outv;
+            }
+        }
+        lds_barrier();
+
+        // ---- Gram blocks, round-robin over the waves.  Operands are swapped
+        // (rows of omega as the A operand) so lane (lr, grp) holds
+        // M[16 b + lr][16 c + 4 grp + r]: the fragment order the state pass reads.
+        const T* omb = COL ? &sm.Om[0][0] : &sm.X[0][0];
+        for (int q = wave; q < NJA + NJP; q += 4) {
+            const bool isA = q < NJA;
+            int b, c;
+            if (isA || !WIN) {
+                const int qq = isA ? q : q - NJA;
+                b = 0;
+                while ((b + 1) * (b + 2) / 2 <= qq) ++b;
+                c = qq - b * (b + 1) / 2;
+            } else {
+                b = (q - NJA) / NB;
+                c = (q - NJA) - b * NB;
+                if (!(b < NBQ && (16 * c) / Wv <= 16 * b + 15)) continue;  // never read
+            }
+            const T* ar = omb + (size_t)(16 * c + lr) * LDX + 4 * grp;
+            const T* br = (isA ? &sm.X[16 * b + lr][0] : &sm.Q[16 * b + lr][0]) + 4 * grp;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int m = 0; m < D / 32; ++m)
+                acc = E::mma32(E::load(ar + 32 * m), E::load(ar + 32 * m + 16), E::load(br + 32 * m),
+                               E::load(br + 32 * m + 16), acc);
+            const int j0 = 16 * c + 4 * grp;
+            const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.gv[j0]);
+            const f32x4 rj = *reinterpret_cast<const f32x4*>(&sm.rs[j0]);
+            const int4 sj = *reinterpret_cast<const int4*>(&sm.step[j0]);
+            const int i = 16 * b + lr;
+            f32x4 val;
+            if (isA) {
+                const int si = sm.step[i];
+                const float gi = sm.gv[i];
+                val[0] = (sj.x < si) ? exp2f(gi - gj[0]) * acc[0] * rj[0] : 0.f;
+                val[1] = (sj.y < si) ? exp2f(gi - gj[1]) * acc[1] * rj[1] : 0.f;
+                val[2] = (sj.z < si) ? exp2f(gi - gj[2]) * acc[2] * rj[2] : 0.f;
+                val[3] = (sj.w < si) ? exp2f(gi - gj[3]) * acc[3] * rj[3] : 0.f;
+                if (b == c) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sm.Adg[b][lr][4 * grp + r] = val[r];
+                } else {
+                    *reinterpret_cast<Frag*>(recT + R::kA + (size_t)R::ablk(b, c) * 256 + lane * 4) =
+                        E::pack(-val);
+                }
+            } else {
+                const bool tv = i < Ct;
+                const float gi = sm.gs[i];
+                val[0] = (tv && sj.x <= i) ? exp2f(gi - gj[0]) * acc[0] * rj[0] : 0.f;
+                val[1] = (tv && sj.y <= i) ? exp2f(gi - gj[1]) * acc[1] * rj[1] : 0.f;
+                val[2] = (tv && sj.z <= i) ? exp2f(gi - gj[2]) * acc[2] * rj[2] : 0.f;
+                val[3] = (tv && sj.w <= i) ? exp2f(gi - gj[3]) * acc[3] * rj[3] : 0.f;
+                *reinterpret_cast<Frag*>(recT + R::kP + (size_t)(b * NB + c) * 256 + lane * 4) =
+                    E::pack(val);
+            }
+        }
+        if constexpr (DELTA) {
+            lds_barrier();
+            // ---- (I + A_bb)^-1 by forward substitution, one column per lane;
+            // wave b owns block b from here on, so no further barrier ----
+            if (wave < NB) {
+                const int bb = wave;
+                if (lane < 16) {
+                    const int c = lane;
+                    float tcol[16];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        float acc = (i == c) ? 1.f : 0.f;
+#pragma unroll
+                        for (int j = 0; j < i; ++j) acc -= sm.Adg[bb][i][j] * tcol[j];
+                        tcol[i] = acc;
+                    }
+                    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sm.Adg[bb][i][c] = tcol[i];
+                }
+                __builtin_amdgcn_wave_barrier();
+                f32x4 tv;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) tv[r] = sm.Adg[bb][lr][4 * grp + r];
+                *reinterpret_cast<Frag*>(recT + R::kD + (size_t)bb * 256 + lane * 4) = E::pack(tv);
+            }
+        } else {
+            // the next tile's staging overwrites the keys and queries the Gram
+            // blocks above read
+            lds_barrier();
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 template <class E, int D, int CV, bool DELTA, bool COL, bool WIN>
@@ -655,15 +1404,35 @@ static hipError_t launch_one(const ChunkArgs& a, void* ws, hipStream_t stream) {
     const int Wv = WIN ? a.W : 1;
     const int ntiles = tiles_of(a.T, CV / Wv);
     if (ntiles > 0) {
-        hipLaunchKernelGGL((chunk_prep_kernel<E, D, CV, DELTA, COL, WIN>), dim3(a.BH * ntiles),
-                           dim3(256), 0, stream, a, ws, ntiles);
+        if constexpr (E::kBytes == 2) {
+            // persistent grid: as many workgroups as fit on the device at once
+            // (LDS allows floor(160 KiB / footprint) per compute unit, at most 3)
+            constexpr int per_cu_lds = (int)(163840 / sizeof(Prep2Smem<D, CV, COL>));
+            constexpr int per_cu = per_cu_lds < 1 ? 1 : (per_cu_lds > 3 ? 3 : per_cu_lds);
+            int dev = 0, cus = 0;
+            if (hipGetDevice(&dev) != hipSuccess ||
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+                cus < 1)
+                cus = 256;
+            const int njobs = a.BH * ntiles;
+            const int grid = njobs < cus * per_cu ? njobs : cus * per_cu;
+            hipLaunchKernelGGL((chunk_prep2_kernel<D, CV, DELTA, COL, WIN>), dim3(grid), dim3(256),
+                               0, stream, a, ws, ntiles, njobs);
+        } else {
+            hipLaunchKernelGGL((chunk_prep_kernel<E, D, CV, DELTA, COL, WIN>), dim3(a.BH * ntiles),
+                               dim3(256), 0, stream, a, ws, ntiles);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int nvs = D / 64;
     const int bh8 = (a.BH + 7) / 8 * 8;
-    hipLaunchKernelGGL((chunk_scan_kernel<E, D, CV, DELTA, COL, WIN>), dim3(bh8 * nvs), dim3(256),
-                       0, stream, a, (const void*)ws, ntiles);
+    if constexpr (E::kBytes == 2)
+        hipLaunchKernelGGL((chunk_pass_kernel<D, CV, DELTA, COL, WIN>), dim3(bh8 * nvs), dim3(512),
+                           0, stream, a, (const void*)ws, ntiles);
+    else
+        hipLaunchKernelGGL((chunk_scan_kernel<E, D, CV, DELTA, COL, WIN>), dim3(bh8 * nvs),
+                           dim3(256), 0, stream, a, (const void*)ws, ntiles);
     return hipGetLastError();
 }
 
