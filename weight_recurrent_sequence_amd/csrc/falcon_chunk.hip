@@ -64,6 +64,12 @@ struct Rec {
     static constexpr int NSC = 5;  // gam, hrow, gq, l1, erow (CV floats each)
     static constexpr size_t kBytes = (kScalBytes + NSC * CV * 4 + 255) / 256 * 256;
     static __host__ __device__ constexpr int ablk(int b, int c) { return b * (b - 1) / 2 + c; }
+    // P block (b, c): without a window the blocks on and below the diagonal in
+    // row order; with one (two query blocks at most) row-major over them.
+    static __host__ __device__ constexpr int pblk(int b, int c, bool win) {
+        return win ? b * NB + c : b * (b + 1) / 2 + c;
+    }
+    static constexpr int npblk(bool win) { return win ? 2 * NB : NB * (NB + 1) / 2; }
 };
 
 static inline int tiles_of(int T, int Ct) { return (T + Ct - 1) / Ct; }
@@ -256,11 +262,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a, void* ws, 
             b = (q - NJA) / NB;
             c = (q - NJA) % NB;
         }
-        if (!isA && !(b < NBQ && (16 * c) / Wv <= 16 * b + 15)) {
-            *reinterpret_cast<Frag*>(recT + R::kP + (size_t)(b * NB + c) * 256 + lane * 4) =
-                E::pack(zero4());
-            continue;
-        }
+        if (!isA && !(b < NBQ && (16 * c) / Wv <= 16 * b + 15)) continue;  // never read
         const T* ar = omb + (size_t)(16 * c + lr) * LDX;                       // omega_j rows
         const T* br = isA ? &sm.X[16 * b + lr][0] : &sm.Q[16 * b + lr][0];   // x_i / q_t rows
         f32x4 acc = zero4();
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a, void* ws, 
                 const int sj = sm.step[j];
                 val[r] = (sj <= i && i < Ct) ? __expf(gi - sm.g[sj]) * acc[r] * sm.rs[j] : 0.f;
             }
-            *reinterpret_cast<Frag*>(recT + R::kP + (size_t)(b * NB + c) * 256 + lane * 4) =
+            *reinterpret_cast<Frag*>(recT + R::kP + (size_t)R::pblk(b, c, WIN) * 256 + lane * 4) =
                 E::pack(val);
         }
     }
@@ -592,7 +594,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs a, const void
             for (int cb = 0; cb < NB; ++cb) {
                 if (WIN && (16 * cb) / Wv > 16 * tb + 15) continue;
                 if (!WIN && cb > tb) continue;
-                acc = E::mma16(E::load(recT + R::kP + (size_t)(tb * NB + cb) * 256 + lane * 4),
+                acc = E::mma16(E::load(recT + R::kP + (size_t)R::pblk(tb, cb, WIN) * 256 + lane * 4),
                                DB[cb], acc);
             }
 #pragma unroll
@@ -688,7 +690,7 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int D, int CV, bool DELTA, bool COL>
+template <int D, int CV, bool DELTA, bool COL, bool WIN>
 struct PassSmem {
     using R = Rec<EBf16, CV, DELTA>;
     static constexpr int LDX = D + 8;
@@ -696,12 +698,14 @@ struct PassSmem {
     static constexpr int KB = D / 16, NB = CV / 16;
     static constexpr int RECF = (R::NBA + R::NBD) * 512;   // -A and Td fragments (bytes)
     static constexpr int RECB = RECF + R::NSC * CV * 4;     // then the row factors
+    static constexpr int PGB = R::npblk(WIN) * 512 + CV * 4;  // P fragments, then gq
     uint16_t X[2][CV][LDX];     // keys x_i
     uint16_t Y[2][CV][LDY];     // targets y_i of this slice's 64 value columns
     uint16_t QU[2][CV][LDX];    // queries q_t; write vectors u_i for the per-column rule
     s16x4 SB[2][4][KB][64];     // bf16 state at the tile start, fragment order per chain wave
     s16x4 DB[2][4][NB][64];     // bf16 Delta, fragment order per chain wave
     alignas(16) char rec[2][RECB];
+    alignas(16) char pg[2][PGB];  // the output half's record pieces, staged one tile later
 };
 
 template <int D, int CV, bool DELTA, bool COL, bool WIN>
@@ -710,13 +714,15 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
     using T = uint16_t;
     using Frag = s16x4;
     using R = Rec<E, CV, DELTA>;
-    using Smem = PassSmem<D, CV, DELTA, COL>;
+    using Smem = PassSmem<D, CV, DELTA, COL, WIN>;
     constexpr int NB = CV / 16, KB = D / 16, CPR = D / 8, NVS = D / 64;
     constexpr int LDX = Smem::LDX, LDY = Smem::LDY;
     constexpr int NXL = (CV * CPR + 255) / 256;  // 16-byte pieces of a key tile per stager
     constexpr int NYL = (CV * 8 + 255) / 256;    // of a target tile
     constexpr int RCH = Smem::RECB / 16, RFC = Smem::RECF / 16;
     constexpr int NRL = (RCH + 255) / 256;
+    constexpr int PCH = Smem::PGB / 16, PFC = R::npblk(WIN) * 32;
+    constexpr int NPL = (PCH + 255) / 256;
     constexpr bool QG = COL;  // queries as register fragments from global memory
     __shared__ Smem sm;
 
@@ -780,8 +786,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
 
     u32x4 px[NXL], pq[QG ? 1 : NXL], py[NYL], pr[NRL];
     float pl1[COL ? NXL : 1], per[COL ? NXL : 1];
-    Frag pP[NB][NB];
-    float pgq[NB];
+    u32x4 ppg[NPL];
     Frag pQf[QG ? NB : 1][QG ? KB : 1];
 
     // keys, targets and the record of `tile` into registers
@@ -852,24 +857,23 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
             for (int it = 0; it < NXL; ++it) pq[it] = buf_load16(rq, qvo[it]);
         }
     };
-    auto p_used = [&](int tb, int cb) __attribute__((always_inline)) {
-        return WIN ? (tb < NBQ && (16 * cb) / Wv <= 16 * tb + 15) : (cb <= tb);
-    };
-    // output-side record pieces of `tile`: P fragments and the query decays
-    auto load_p = [&](int tile) __attribute__((always_inline)) {
+    // output-side record pieces of `tile` (P fragments, query decays)
+    auto load_pg = [&](int tile) __attribute__((always_inline)) {
         const char* rt = recg + (size_t)tile * R::kBytes;
-        static_for<NB>([&](auto tbc) __attribute__((always_inline)) {
-            constexpr int tb = decltype(tbc)::value;
-            static_for<NB>([&](auto cbc) __attribute__((always_inline)) {
-                constexpr int cb = decltype(cbc)::value;
-                if (WIN || cb <= tb) {
-                    if (p_used(tb, cb))
-                        pP[tb][cb] = *reinterpret_cast<const Frag*>(
-                            rt + R::kP * 2 + (size_t)(tb * NB + cb) * 512 + lane * 8);
-                }
-            });
-            pgq[tb] = reinterpret_cast<const float*>(rt + R::kScalBytes)[2 * CV + 16 * tb + lr];
-        });
+#pragma unroll
+        for (int it = 0; it < NPL; ++it) {
+            const int pc = min(otid + 256 * it, PCH - 1);
+            ppg[it] = *reinterpret_cast<const u32x4*>(
+                rt + (pc < PFC ? R::kP * 2 + (size_t)pc * 16
+                               : R::kScalBytes + 2 * CV * 4 + (size_t)(pc - PFC) * 16));
+        }
+    };
+    auto store_pg = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+        for (int it = 0; it < NPL; ++it) {
+            const int pc = otid + 256 * it;
+            if (pc < PCH) reinterpret_cast<u32x4*>(sm.pg[b])[pc] = ppg[it];
+        }
     };
     auto store_xyr = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
@@ -931,6 +935,23 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
         const float* hrow = gam + CV;
         const float* gq = gam + 2 * CV;
 
+        // reads that do not depend on the state go out first, so their latency
+        // overlaps X S0^T
+        Frag yf[NB], Af[R::NBA > 0 ? R::NBA : 1], Tf[NB];
+        f32x4 gm[NB], hv[NB];
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) {
+            yf[rb] = colfrag(Yb, LDY, 16 * rb, 16 * cw);
+            hv[rb] = *reinterpret_cast<const f32x4*>(hrow + 16 * rb + 4 * grp);
+            if constexpr (DELTA) {
+                gm[rb] = *reinterpret_cast<const f32x4*>(gam + 16 * rb + 4 * grp);
+                Tf[rb] = E::load(recT + R::kD + (size_t)rb * 256 + lane * 4);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < R::NBA; ++q) Af[q] = E::load(recT + R::kA + (size_t)q * 256 + lane * 4);
+        const float glq = gq[Ct - 1];
+
         Frag SB[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -960,22 +981,11 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
             }
             // residuals R = Y - diag(gam) Z, then the blocked forward substitution
             // Delta_b = Td_b (R_b - sum_{c<b} A_bc Delta_c)
-            f32x4 Rr[NB];
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb) {
-                const Frag yf = colfrag(Yb, LDY, 16 * rb, 16 * cw);
-                const f32x4 gm = *reinterpret_cast<const f32x4*>(gam + 16 * rb + 4 * grp);
+                f32x4 acc;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Rr[rb][r] = E::to_f((T)yf[r]) - gm[r] * Z[rb][r];
-            }
-            Frag Af[R::NBA > 0 ? R::NBA : 1], Tf[NB];
-#pragma unroll
-            for (int q = 0; q < R::NBA; ++q) Af[q] = E::load(recT + R::kA + (size_t)q * 256 + lane * 4);
-#pragma unroll
-            for (int rb = 0; rb < NB; ++rb) Tf[rb] = E::load(recT + R::kD + (size_t)rb * 256 + lane * 4);
-#pragma unroll
-            for (int rb = 0; rb < NB; ++rb) {
-                f32x4 acc = Rr[rb];
+                for (int r = 0; r < 4; ++r) acc[r] = E::to_f((T)yf[rb][r]) - gm[rb][r] * Z[rb][r];
 #pragma unroll
                 for (int cb = 0; cb < rb; ++cb) acc = E::mma16(Af[R::ablk(rb, cb)], DB[cb], acc);
                 Dl[rb] = E::mma16(Tf[rb], E::pack(acc), zero4());
@@ -984,10 +994,9 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
         } else {
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb) {
-                const Frag yf = colfrag(Yb, LDY, 16 * rb, 16 * cw);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Dl[rb][r] = E::to_f((T)yf[r]);
-                DB[rb] = yf;
+                for (int r = 0; r < 4; ++r) Dl[rb][r] = E::to_f((T)yf[rb][r]);
+                DB[rb] = yf[rb];
             }
         }
 #pragma unroll
@@ -997,13 +1006,11 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
         Frag HB[NB];
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) {
-            const f32x4 hv = *reinterpret_cast<const f32x4*>(hrow + 16 * cb + 4 * grp);
             f32x4 h;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) h[r] = hv[r] * Dl[cb][r];
+            for (int r = 0; r < 4; ++r) h[r] = hv[cb][r] * Dl[cb][r];
             HB[cb] = E::pack(h);
         }
-        const float glq = gq[Ct - 1];
         const T* om = COL ? &sm.QU[b][0][0] : Xb;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -1025,6 +1032,8 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
     auto output_tile = [&](int p) __attribute__((always_inline)) {
         const int pb = p & 1;
         const int t0 = p * Ct;
+        const T* Pf = reinterpret_cast<const T*>(sm.pg[pb]);
+        const float* gqt = reinterpret_cast<const float*>(sm.pg[pb] + R::npblk(WIN) * 512);
         Frag sb[KB], db[NB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) sb[kb] = sm.SB[pb][cw][kb][lane];
@@ -1047,11 +1056,14 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
                     }
                     acc = E::mma32(sb[2 * m], sb[2 * m + 1], q0, q1, acc);
                 }
-                acc = acc * pgq[tb];
+                acc = acc * gqt[16 * tb + lr];
                 static_for<NB>([&](auto cbc) __attribute__((always_inline)) {
                     constexpr int cb = decltype(cbc)::value;
                     if (WIN || cb <= tb) {
-                        if (p_used(tb, cb)) acc = E::mma16(db[cb], pP[tb][cb], acc);
+                        if (!WIN || (tb < 2 && (16 * cb) / Wv <= 16 * tb + 15))
+                            acc = E::mma16(db[cb],
+                                           E::load(Pf + (size_t)R::pblk(tb, cb, WIN) * 256 + lane * 4),
+                                           acc);
                     }
                 });
                 // lane holds O[t = 16 tb + lr][v = 16 cw + 4 grp + r]
@@ -1066,6 +1078,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
     // ---- pipeline ----
     if (!chain && ntl > 0) {
         load_xyr(0);
+        load_pg(0);
         if constexpr (!QG) load_q(0);
         store_xyr(0);
         if (ntl > 1) load_xyr(1);
@@ -1077,14 +1090,18 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
         } else {
             if (it >= 1) output_tile(it - 1);
             if (it + 1 < ntl) store_xyr((it + 1) & 1);
-            if (it < ntl) store_q(it & 1);
+            if (it < ntl) {
+                store_q(it & 1);
+                store_pg(it & 1);
+            }
             if (it + 2 < ntl) load_xyr(it + 2);
+            if (it + 1 < ntl) {
+                load_pg(it + 1);
+                if constexpr (!QG) load_q(it + 1);
+            }
             if constexpr (QG) {
                 if (it < ntl) load_q(it);
-            } else {
-                if (it + 1 < ntl) load_q(it + 1);
             }
-            if (it < ntl) load_p(it);
         }
         lds_barrier();
     }
@@ -1358,7 +1375,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep2_kernel(ChunkArgs a, void* 
                 val[1] = (tv && sj.y <= i) ? exp2f(gi - gj[1]) * acc[1] * rj[1] : 0.f;
                 val[2] = (tv && sj.z <= i) ? exp2f(gi - gj[2]) * acc[2] * rj[2] : 0.f;
                 val[3] = (tv && sj.w <= i) ? exp2f(gi - gj[3]) * acc[3] * rj[3] : 0.f;
-                *reinterpret_cast<Frag*>(recT + R::kP + (size_t)(b * NB + c) * 256 + lane * 4) =
+                *reinterpret_cast<Frag*>(recT + R::kP + (size_t)R::pblk(b, c, WIN) * 256 + lane * 4) =
                     E::pack(val);
             }
         }
@@ -1467,6 +1484,10 @@ static hipError_t launch_e(const ChunkArgs& a, int D, int chunk, bool delta, voi
             return delta ? launch_d<E, true, true, false>(a, D, chunk, ws, stream)
                          : launch_d<E, false, true, false>(a, D, chunk, ws, stream);
         case kNormWindow:
+            // a window of one example is the scalar rule
+            if (a.W == 1)
+                return delta ? launch_d<E, true, false, false>(a, D, chunk, ws, stream)
+                             : launch_d<E, false, false, false>(a, D, chunk, ws, stream);
             return delta ? launch_d<E, true, false, true>(a, D, chunk, ws, stream)
                          : launch_d<E, false, false, true>(a, D, chunk, ws, stream);
         default: return hipErrorInvalidValue;
