@@ -24,7 +24,7 @@
 namespace falcon {
 
 template <class E, int D>
-__global__ __launch_bounds__(256, 4) void decode_step_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 2) void decode_step_kernel(DecodeArgs a) {
     using T = typename E::T;
     constexpr int LPR = D / 16;               // lanes per row
     constexpr int ROWS_PER_PASS = 256 / LPR;
@@ -42,6 +42,12 @@ __global__ __launch_bounds__(256, 4) void decode_step_kernel(DecodeArgs a) {
     T* oh = static_cast<T*>(a.o) + head * D;
     const float al = a.alpha[head];
     const float et = a.eta[head];
+    // Everything this thread reads is requested up front (targets and the new
+    // key too), so no wait further down has a load queued behind a store.
+    const T knew = kh[tid < D ? tid : 0];
+    T vraw[RPT];  // converted where used, so the load stays in flight meanwhile
+#pragma unroll
+    for (int p = 0; p < RPT; ++p) vraw[p] = vh[row0 + ROWS_PER_PASS * p];
 
     // columns of this lane: 4*seg + 4*LPR*j + e, j, e in 0..3
     float x[16], qv[16];
@@ -61,7 +67,8 @@ __global__ __launch_bounds__(256, 4) void decode_step_kernel(DecodeArgs a) {
         const int row = row0 + ROWS_PER_PASS * p;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            s[p][j] = *reinterpret_cast<const f32x4*>(S + (size_t)row * D + 4 * seg + 4 * LPR * j);
+            s[p][j] = __builtin_nontemporal_load(
+                reinterpret_cast<const f32x4*>(S + (size_t)row * D + 4 * seg + 4 * LPR * j));
     }
 
     float n2 = 0.f, n1 = 0.f, xq = 0.f;
@@ -73,11 +80,11 @@ __global__ __launch_bounds__(256, 4) void decode_step_kernel(DecodeArgs a) {
     }
     n2 = group_sum_dpp<LPR>(n2);
     n1 = group_sum_dpp<LPR>(n1);
-    // Every lane has now consumed the previous key (its x registers are
-    // loaded); after this barrier k_cache may be overwritten.  It comes before
-    // any global store, so it does not wait for the state write-back.
-    __syncthreads();
-    if (tid < D) kc[tid] = kh[tid];
+    // Every lane has now consumed the previous key (its x values entered the
+    // norms); after this barrier k_cache may be overwritten.  The barrier
+    // orders no memory besides that, so it waits for no load in flight.
+    __builtin_amdgcn_s_barrier();
+    if (tid < D) kc[tid] = knew;
     float u[16];
     float uq = 0.f;
     if (a.norm == kNormScalar) {
@@ -109,7 +116,7 @@ __global__ __launch_bounds__(256, 4) void decode_step_kernel(DecodeArgs a) {
             }
         sx = group_sum_dpp<LPR>(sx);
         sq = group_sum_dpp<LPR>(sq);
-        const float vr = E::to_f(vh[row]);
+        const float vr = E::to_f(vraw[p]);
         const float r = a.delta ? vr - al * sx : vr;
         if (seg == 0) oh[row] = E::from_f(al * sq + uq * r);
 #pragma unroll
@@ -117,7 +124,7 @@ __global__ __launch_bounds__(256, 4) void decode_step_kernel(DecodeArgs a) {
             f32x4 nv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) nv[e] = al * s[p][j][e] + r * u[4 * j + e];
-            *reinterpret_cast<f32x4*>(S + (size_t)row * D + 4 * seg + 4 * LPR * j) = nv;
+            __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(S + (size_t)row * D + 4 * seg + 4 * LPR * j));
         }
     }
 }
