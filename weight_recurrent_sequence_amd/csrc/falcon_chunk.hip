@@ -682,6 +682,16 @@ __device__ __forceinline__ s16x4 buf_load8(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(s16x4, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane l writes
+// lds + 16 l (lds is wave-uniform); lanes whose exec bit is off write nothing,
+// out-of-range offsets write zeros.  Completion is counted by vmcnt.
+__device__ __forceinline__ void buf_load16_lds(rsrc_t r, void* lds, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                             off, 0, 0, 0);
+}
+// s_waitcnt vmcnt(0), leaving the other counters alone
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Workgroup barrier that orders LDS only: global loads and stores in flight
 // are not waited for.
 __device__ __forceinline__ void lds_barrier() {
@@ -766,25 +776,36 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
 
     // ---- output: staging geometry, fixed across tiles ----
     const int otid = tid - 256;
-    uint32_t xvo[NXL], qvo[NXL], yvo[NYL];  // byte offsets for the descriptor loads
+    // Each 16-byte piece a stager moves: its row relative to the tile start
+    // (key x_i = k_{t0 + s - w - 1}, target y_i = v_{t0 + s - w}), its byte
+    // column, and whether it exists.  Loads choose addresses, never data:
+    // rows outside the sequence read as zero (descriptor bounds), halo rows
+    // come from a second load that is merged when the piece is stored.
+    int xrel[NXL], yrel[NYL];
+    uint32_t xcb[NXL], ycb[NYL], qvo[NXL];
+    bool xok[NXL], yok[NYL];
 #pragma unroll
     for (int it = 0; it < NXL; ++it) {
         const int c = otid + 256 * it;
         const int i = c / CPR, col = (c % CPR) * 8;
         const int s = WIN ? i / Wv : i, w = WIN ? i - s * Wv : 0;
-        const bool ok = c < CV * CPR;
-        xvo[it] = (ok && i < NVR) ? (uint32_t)(((s - w - 1 + W) * D + col) * 2) : kOob;
-        qvo[it] = (ok && i < Ct) ? (uint32_t)((i * D + col) * 2) : kOob;
+        xok[it] = c < CV * CPR && i < NVR;
+        xrel[it] = s - w - 1;
+        xcb[it] = (uint32_t)col * 2;
+        qvo[it] = (c < CV * CPR && i < Ct) ? (uint32_t)((i * D + col) * 2) : kOob;
     }
 #pragma unroll
     for (int it = 0; it < NYL; ++it) {
         const int c = otid + 256 * it;
         const int i = c / 8, col = (c % 8) * 8;
         const int s = WIN ? i / Wv : i, w = WIN ? i - s * Wv : 0;
-        yvo[it] = (c < CV * 8 && i < NVR) ? (uint32_t)(((s - w + W - 1) * D + col) * 2) : kOob;
+        yok[it] = c < CV * 8 && i < NVR;
+        yrel[it] = s - w;
+        ycb[it] = (uint32_t)col * 2;
     }
 
     u32x4 px[NXL], pq[QG ? 1 : NXL], py[NYL], pr[NRL];
+    u32x4 pxh[NXL], pyh[NYL];  // halo rows of the first tiles
     float pl1[COL ? NXL : 1], per[COL ? NXL : 1];
     u32x4 ppg[NPL];
     Frag pQf[QG ? NB : 1][QG ? KB : 1];
@@ -792,35 +813,32 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
     // keys, targets and the record of `tile` into registers
     auto load_xyr = [&](int tile) __attribute__((always_inline)) {
         const int t0 = tile * Ct;
-        if (t0 >= W) {
-            const rsrc_t rx = make_rsrc(kg + (size_t)(t0 - W) * D, (int64_t)(T_ - t0 + W) * D * 2);
-            const rsrc_t ry =
-                make_rsrc(vg + (size_t)(t0 - W + 1) * D, (int64_t)(T_ - t0 + W - 1) * D * 2);
+        const int bx = max(t0 - W, 0), by = max(t0 - W + 1, 0);
+        const rsrc_t rx = make_rsrc(kg + (size_t)bx * D, (int64_t)(T_ - bx) * D * 2);
+        const rsrc_t ry = make_rsrc(vg + (size_t)by * D, (int64_t)(T_ - by) * D * 2);
 #pragma unroll
-            for (int it = 0; it < NXL; ++it) px[it] = buf_load16(rx, xvo[it]);
+        for (int it = 0; it < NXL; ++it) {
+            const int tau = t0 + xrel[it];
+            px[it] = buf_load16(rx, (xok[it] && tau >= 0) ? (uint32_t)((tau - bx) * D * 2) + xcb[it] : kOob);
+        }
 #pragma unroll
-            for (int it = 0; it < NYL; ++it) py[it] = buf_load16(ry, yvo[it]);
-        } else {
-            // first tiles: rows before the sequence come from the halo (or are zero)
+        for (int it = 0; it < NYL; ++it) {
+            const int tv = t0 + yrel[it];
+            py[it] = buf_load16(ry, (yok[it] && tv >= 0) ? (uint32_t)((tv - by) * D * 2) + ycb[it] : kOob);
+        }
+        if (t0 < W) {
+            // rows before the sequence: the halo, or zero without one
+            const rsrc_t hx = make_rsrc(kp ? kp : kg, kp ? (int64_t)W * D * 2 : 0);
 #pragma unroll
             for (int it = 0; it < NXL; ++it) {
-                const int c = otid + 256 * it;
-                const int i = c / CPR, col = (c % CPR) * 8;
-                const int s = WIN ? i / Wv : i, w = WIN ? i - s * Wv : 0;
-                const int tau = t0 + s - w - 1;
-                const bool ok = c < CV * CPR && i < NVR && t0 + s < T_ && (tau >= 0 || kp != nullptr);
-                const T* p = tau >= 0 ? kg + (size_t)tau * D : (kp ? kp + (size_t)(W + tau) * D : kg);
-                px[it] = sel16(ok, *reinterpret_cast<const u32x4*>((ok ? p : kg) + col));
+                const int tau = t0 + xrel[it];
+                pxh[it] = buf_load16(hx, (xok[it] && tau < 0) ? (uint32_t)((W + tau) * D * 2) + xcb[it] : kOob);
             }
+            const rsrc_t hy = make_rsrc(vp ? vp : vg, vp ? (int64_t)(W - 1) * D * 2 : 0);
 #pragma unroll
             for (int it = 0; it < NYL; ++it) {
-                const int c = otid + 256 * it;
-                const int i = c / 8, col = (c % 8) * 8;
-                const int s = WIN ? i / Wv : i, w = WIN ? i - s * Wv : 0;
-                const int tv = t0 + s - w;
-                const bool ok = c < CV * 8 && i < NVR && t0 + s < T_ && (tv >= 0 || vp != nullptr);
-                const T* p = tv >= 0 ? vg + (size_t)tv * D : (vp ? vp + (size_t)(W - 1 + tv) * D : vg);
-                py[it] = sel16(ok, *reinterpret_cast<const u32x4*>((ok ? p : vg) + col));
+                const int tv = t0 + yrel[it];
+                pyh[it] = buf_load16(hy, (yok[it] && tv < 0) ? (uint32_t)((W - 1 + tv) * D * 2) + ycb[it] : kOob);
             }
         }
         const char* rt = recg + (size_t)tile * R::kBytes;
@@ -875,7 +893,14 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
             if (pc < PCH) reinterpret_cast<u32x4*>(sm.pg[b])[pc] = ppg[it];
         }
     };
-    auto store_xyr = [&](int b) __attribute__((always_inline)) {
+    auto store_xyr = [&](int tile) __attribute__((always_inline)) {
+        const int b = tile & 1;
+        if (tile * Ct < W) {
+#pragma unroll
+            for (int it = 0; it < NXL; ++it) px[it] |= pxh[it];
+#pragma unroll
+            for (int it = 0; it < NYL; ++it) py[it] |= pyh[it];
+        }
 #pragma unroll
         for (int it = 0; it < NXL; ++it) {
             const int c = otid + 256 * it;
@@ -908,16 +933,6 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
             if (rc < RCH) reinterpret_cast<u32x4*>(sm.rec[b])[rc] = pr[it];
         }
     };
-    auto store_q = [&](int b) __attribute__((always_inline)) {
-        if constexpr (!QG) {
-#pragma unroll
-            for (int it = 0; it < NXL; ++it) {
-                const int c = otid + 256 * it;
-                if (c < CV * CPR)
-                    *reinterpret_cast<u32x4*>(&sm.QU[b][c / CPR][(c % CPR) * 8]) = pq[it];
-            }
-        }
-    };
 
     // column fragment of a row-major LDS tile: lane (lr, grp) gets
     // M[row0 + 4 grp + r][col0 + lr], r = 0..3
@@ -943,13 +958,16 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
         for (int rb = 0; rb < NB; ++rb) {
             yf[rb] = colfrag(Yb, LDY, 16 * rb, 16 * cw);
             hv[rb] = *reinterpret_cast<const f32x4*>(hrow + 16 * rb + 4 * grp);
-            if constexpr (DELTA) {
-                gm[rb] = *reinterpret_cast<const f32x4*>(gam + 16 * rb + 4 * grp);
-                Tf[rb] = E::load(recT + R::kD + (size_t)rb * 256 + lane * 4);
-            }
+            if constexpr (DELTA) gm[rb] = *reinterpret_cast<const f32x4*>(gam + 16 * rb + 4 * grp);
         }
+        // the system's blocks too, unless registers are short (per-column rule)
+        auto load_sys = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < R::NBA; ++q) Af[q] = E::load(recT + R::kA + (size_t)q * 256 + lane * 4);
+            for (int rb = 0; rb < NB; ++rb) Tf[rb] = E::load(recT + R::kD + (size_t)rb * 256 + lane * 4);
+#pragma unroll
+            for (int q = 0; q < R::NBA; ++q) Af[q] = E::load(recT + R::kA + (size_t)q * 256 + lane * 4);
+        };
+        if constexpr (DELTA && !COL) load_sys();
         const float glq = gq[Ct - 1];
 
         Frag SB[KB];
@@ -981,6 +999,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
             }
             // residuals R = Y - diag(gam) Z, then the blocked forward substitution
             // Delta_b = Td_b (R_b - sum_{c<b} A_bc Delta_c)
+            if constexpr (COL) load_sys();
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb) {
                 f32x4 acc;
@@ -1029,9 +1048,19 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
     };
 
     // ---- output: one tile, O^T = diag(gq) S0 Q^T + Delta^T P^T ----
+    Frag opk[NB];  // outputs of one tile, packed, until they are stored
+    auto store_o = [&](int p) __attribute__((always_inline)) {
+        const int t0 = p * Ct;
+        static_for<NB>([&](auto tbc) __attribute__((always_inline)) {
+            constexpr int tb = decltype(tbc)::value;
+            // lane holds O[t = 16 tb + lr][v = 16 cw + 4 grp + r]
+            const int t = 16 * tb + lr;
+            if (tb < NBQ && t < Ct && t0 + t < T_)
+                *reinterpret_cast<Frag*>(og + (size_t)(t0 + t) * D + 16 * cw + 4 * grp) = opk[tb];
+        });
+    };
     auto output_tile = [&](int p) __attribute__((always_inline)) {
         const int pb = p & 1;
-        const int t0 = p * Ct;
         const T* Pf = reinterpret_cast<const T*>(sm.pg[pb]);
         const float* gqt = reinterpret_cast<const float*>(sm.pg[pb] + R::npblk(WIN) * 512);
         Frag sb[KB], db[NB];
@@ -1066,44 +1095,169 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
                                            acc);
                     }
                 });
-                // lane holds O[t = 16 tb + lr][v = 16 cw + 4 grp + r]
-                const int t = 16 * tb + lr;
-                if (t < Ct && t0 + t < T_)
-                    *reinterpret_cast<Frag*>(og + (size_t)(t0 + t) * D + 16 * cw + 4 * grp) =
-                        E::pack(acc);
+                if constexpr (COL) {
+                    // stored at once (the per-column pipeline does not defer)
+                    const int t = 16 * tb + lr, t0 = p * Ct;
+                    if (t < Ct && t0 + t < T_)
+                        *reinterpret_cast<Frag*>(og + (size_t)(t0 + t) * D + 16 * cw + 4 * grp) =
+                            E::pack(acc);
+                } else {
+                    opk[tb] = E::pack(acc);
+                }
             }
         });
     };
 
-    // ---- pipeline ----
-    if (!chain && ntl > 0) {
-        load_xyr(0);
-        load_pg(0);
-        if constexpr (!QG) load_q(0);
-        store_xyr(0);
-        if (ntl > 1) load_xyr(1);
+    // ---- direct-to-LDS staging (all rules but the per-column one, whose
+    // write vectors are derived while staging): every 16-byte slot of an LDS
+    // tile is one lane of one buffer_load ... lds, issued by the output waves
+    // right after a barrier and waited for before the next one.  A slot's
+    // source is fixed relative to its tile, so the offsets are computed once;
+    // padding and missing rows read as zero.
+    constexpr int SPX = LDX / 8, SPY = LDY / 8;      // slots per key / target row
+    constexpr int NSX = CV * SPX, NSY = CV * SPY;    // slots per tile
+    constexpr int NIX = (NSX + 63) / 64, NIY = (NSY + 63) / 64;
+    constexpr int NIR = (RCH + 63) / 64, NIP = (PCH + 63) / 64;
+    constexpr int MIX = (NIX + 3) / 4, MIY = (NIY + 3) / 4, MIR = (NIR + 3) / 4, MIP = (NIP + 3) / 4;
+    uint32_t dx[MIX], dq[MIX], dy[MIY], dr[MIR], dp[MIP];
+    const int ow = cw;  // index of this wave within its half
+    if constexpr (!COL) {
+#pragma unroll
+        for (int m = 0; m < MIX; ++m) {
+            const int k = 64 * (ow + 4 * m) + lane;
+            const int row = k / SPX, wi = k - row * SPX;
+            const int s = WIN ? row / Wv : row, w = WIN ? row - s * Wv : 0;
+            const bool in = k < NSX && wi < D / 8;
+            dx[m] = (in && row < NVR) ? (uint32_t)(((s - w - 1 + W) * D + wi * 8) * 2) : kOob;
+            dq[m] = (in && row < Ct) ? (uint32_t)((row * D + wi * 8) * 2) : kOob;
+        }
+#pragma unroll
+        for (int m = 0; m < MIY; ++m) {
+            const int k = 64 * (ow + 4 * m) + lane;
+            const int row = k / SPY, wi = k - row * SPY;
+            const int s = WIN ? row / Wv : row, w = WIN ? row - s * Wv : 0;
+            dy[m] = (k < NSY && wi < 8 && row < NVR) ? (uint32_t)(((s - w + W - 1) * D + wi * 8) * 2)
+                                                      : kOob;
+        }
+#pragma unroll
+        for (int m = 0; m < MIR; ++m) {
+            const int k = 64 * (ow + 4 * m) + lane;
+            dr[m] = k < RCH ? (uint32_t)(k < RFC ? k * 16 : R::kScalBytes + (k - RFC) * 16) : kOob;
+        }
+#pragma unroll
+        for (int m = 0; m < MIP; ++m) {
+            const int k = 64 * (ow + 4 * m) + lane;
+            dp[m] = k < PCH ? (uint32_t)(k < PFC ? R::kP * 2 + k * 16 : R::kScalBytes + 2 * CV * 4 + (k - PFC) * 16)
+                            : kOob;
+        }
     }
-    lds_barrier();
-    for (int it = 0; it <= ntl; ++it) {
-        if (chain) {
-            if (it < ntl) chain_tile(it);
-        } else {
-            if (it >= 1) output_tile(it - 1);
-            if (it + 1 < ntl) store_xyr((it + 1) & 1);
-            if (it < ntl) {
-                store_q(it & 1);
-                store_pg(it & 1);
-            }
-            if (it + 2 < ntl) load_xyr(it + 2);
-            if (it + 1 < ntl) {
-                load_pg(it + 1);
-                if constexpr (!QG) load_q(it + 1);
-            }
-            if constexpr (QG) {
-                if (it < ntl) load_q(it);
-            }
+    // Fills of one tile, each spread over the four waves of the calling half.
+    // Keys and the chain's record pieces (output half) and targets (chain
+    // half) of a tile with t0 >= W go to buffer tile & 1, as do queries and
+    // the output half's record pieces (chain half).
+    auto dma_xr = [&](int tile) __attribute__((always_inline)) {
+        const int t0 = tile * Ct, b = tile & 1;
+        const rsrc_t rx = make_rsrc(kg + (size_t)(t0 - W) * D, (int64_t)(T_ - t0 + W) * D * 2);
+        const rsrc_t rr = make_rsrc(recg + (size_t)tile * R::kBytes, R::kBytes);
+        char* xb = reinterpret_cast<char*>(&sm.X[b][0][0]);
+#pragma unroll
+        for (int m = 0; m < MIX; ++m) {
+            const int i = ow + 4 * m;
+            if (i < NIX && 64 * i + lane < NSX) buf_load16_lds(rx, xb + 1024 * i, dx[m]);
+        }
+#pragma unroll
+        for (int m = 0; m < MIR; ++m) {
+            const int i = ow + 4 * m;
+            if (i < NIR && 64 * i + lane < RCH) buf_load16_lds(rr, sm.rec[b] + 1024 * i, dr[m]);
+        }
+    };
+    auto dma_y = [&](int tile) __attribute__((always_inline)) {
+        const int t0 = tile * Ct, b = tile & 1;
+        const rsrc_t ry = make_rsrc(vg + (size_t)(t0 - W + 1) * D, (int64_t)(T_ - t0 + W - 1) * D * 2);
+        char* yb = reinterpret_cast<char*>(&sm.Y[b][0][0]);
+#pragma unroll
+        for (int m = 0; m < MIY; ++m) {
+            const int i = ow + 4 * m;
+            if (i < NIY && 64 * i + lane < NSY) buf_load16_lds(ry, yb + 1024 * i, dy[m]);
+        }
+    };
+    auto dma_qp = [&](int tile) __attribute__((always_inline)) {
+        const int t0 = tile * Ct, b = tile & 1;
+        const rsrc_t rq = make_rsrc(qg + (size_t)t0 * D, (int64_t)(T_ - t0) * D * 2);
+        const rsrc_t rr = make_rsrc(recg + (size_t)tile * R::kBytes, R::kBytes);
+        char* qb = reinterpret_cast<char*>(&sm.QU[b][0][0]);
+#pragma unroll
+        for (int m = 0; m < MIX; ++m) {
+            const int i = ow + 4 * m;
+            if (i < NIX && 64 * i + lane < NSX) buf_load16_lds(rq, qb + 1024 * i, dq[m]);
+        }
+#pragma unroll
+        for (int m = 0; m < MIP; ++m) {
+            const int i = ow + 4 * m;
+            if (i < NIP && 64 * i + lane < PCH) buf_load16_lds(rr, sm.pg[b] + 1024 * i, dp[m]);
+        }
+    };
+
+    // ---- pipeline: the chain works on tile it while the output half
+    // finishes tile it-1 ----
+    if constexpr (COL) {
+        // staged through registers (u is derived from x on the way)
+        if (!chain && ntl > 0) {
+            load_xyr(0);
+            load_pg(0);
+            store_xyr(0);
+            if (ntl > 1) load_xyr(1);
         }
         lds_barrier();
+        for (int it = 0; it <= ntl; ++it) {
+            if (chain) {
+                if (it < ntl) chain_tile(it);
+            } else {
+                if (it >= 1) output_tile(it - 1);
+                if (it + 1 < ntl) store_xyr(it + 1);
+                if (it < ntl) store_pg(it & 1);
+                if (it + 2 < ntl) load_xyr(it + 2);
+                if (it + 1 < ntl) load_pg(it + 1);
+                if (it < ntl) load_q(it);
+            }
+            lds_barrier();
+        }
+    } else {
+        // Iteration it.  Output half: store the outputs of tile it-2, start
+        // the fills of tile it+1's keys and chain record, compute tile it-1.
+        // Chain half: tile it, then start the fills of tile it+1's targets
+        // and tile it's queries and output record (its wait at the barrier
+        // absorbs them).  Both halves wait for their fills before the
+        // barrier.  Tiles that still reach back before the sequence (t0 < W)
+        // are staged by the output half through registers, halo included.
+        if (!chain && ntl > 0) {
+            load_xyr(0);
+            store_xyr(0);
+        }
+        lds_barrier();
+        for (int it = 0; it <= ntl; ++it) {
+            const bool next_fast = it + 1 < ntl && (it + 1) * Ct >= W;
+            if (chain) {
+                if (it < ntl) {
+                    chain_tile(it);
+                    if (next_fast) dma_y(it + 1);
+                    dma_qp(it);
+                    wait_vm_all();
+                }
+            } else {
+                if (it >= 2) store_o(it - 2);
+                if (next_fast) {
+                    dma_xr(it + 1);
+                } else if (it + 1 < ntl) {
+                    load_xyr(it + 1);
+                    store_xyr(it + 1);
+                }
+                if (it >= 1) output_tile(it - 1);
+                wait_vm_all();
+            }
+            lds_barrier();
+        }
+        if (!chain && ntl >= 1) store_o(ntl - 1);
     }
 
     if (chain && a.S_final) {
@@ -1163,18 +1317,25 @@ __global__ __launch_bounds__(256, 2) void chunk_prep2_kernel(ChunkArgs a, void* 
     const int T_ = a.T;
     const float eps = a.eps;
 
-    // staging geometry, fixed across tiles
-    uint32_t xvo[NXL], qvo[NXL];
+    // staging geometry, fixed across tiles: each 16-byte piece's key row
+    // relative to the tile start (x_i = k_{t0 + s - w - 1}), byte column and
+    // existence.  Loads choose addresses, never data, so no load is waited
+    // for before the next tile is staged: rows outside the sequence read as
+    // zero (descriptor bounds) and halo rows come from a second load.
+    int xrel[NXL];
+    uint32_t xcb[NXL], qvo[NXL];
+    bool xok[NXL];
 #pragma unroll
     for (int it = 0; it < NXL; ++it) {
         const int c = tid + 256 * it;
         const int i = c / CPR, col = (c % CPR) * 8;
         const int s = WIN ? i / Wv : i, w = WIN ? i - s * Wv : 0;
-        const bool ok = c < CV * CPR;
-        xvo[it] = (ok && i < NVR) ? (uint32_t)(((s - w - 1 + W) * D + col) * 2) : kOob;
-        qvo[it] = (ok && i < Ct) ? (uint32_t)((i * D + col) * 2) : kOob;
+        xok[it] = c < CV * CPR && i < NVR;
+        xrel[it] = s - w - 1;
+        xcb[it] = (uint32_t)col * 2;
+        qvo[it] = (c < CV * CPR && i < Ct) ? (uint32_t)((i * D + col) * 2) : kOob;
     }
-    u32x4 px[NXL], pq[NXL];
+    u32x4 px[NXL], pxh[NXL], pq[NXL];
     float pal = 1.f, pet = 0.f;
 
     auto load = [&](int job) __attribute__((always_inline)) {
@@ -1182,30 +1343,30 @@ __global__ __launch_bounds__(256, 2) void chunk_prep2_kernel(ChunkArgs a, void* 
         const int t0 = tile * Ct;
         const T* kg = static_cast<const T*>(a.k) + (size_t)bh * T_ * D;
         const T* qg = static_cast<const T*>(a.q) + (size_t)bh * T_ * D;
-        if (t0 >= W) {
-            const rsrc_t rx = make_rsrc(kg + (size_t)(t0 - W) * D, (int64_t)(T_ - t0 + W) * D * 2);
+        const int bx = max(t0 - W, 0);
+        const rsrc_t rx = make_rsrc(kg + (size_t)bx * D, (int64_t)(T_ - bx) * D * 2);
 #pragma unroll
-            for (int it = 0; it < NXL; ++it) px[it] = buf_load16(rx, xvo[it]);
-        } else {
+        for (int it = 0; it < NXL; ++it) {
+            const int tau = t0 + xrel[it];
+            px[it] = buf_load16(rx, (xok[it] && tau >= 0) ? (uint32_t)((tau - bx) * D * 2) + xcb[it] : kOob);
+        }
+        if (t0 < W) {
             const T* kp = a.k_prev ? static_cast<const T*>(a.k_prev) + (size_t)bh * W * D : nullptr;
+            const rsrc_t hx = make_rsrc(kp ? kp : kg, kp ? (int64_t)W * D * 2 : 0);
 #pragma unroll
             for (int it = 0; it < NXL; ++it) {
-                const int c = tid + 256 * it;
-                const int i = c / CPR, col = (c % CPR) * 8;
-                const int s = WIN ? i / Wv : i, w = WIN ? i - s * Wv : 0;
-                const int tau = t0 + s - w - 1;
-                const bool ok = c < CV * CPR && i < NVR && t0 + s < T_ && (tau >= 0 || kp != nullptr);
-                const T* p = tau >= 0 ? kg + (size_t)tau * D : (kp ? kp + (size_t)(W + tau) * D : kg);
-                px[it] = sel16(ok, *reinterpret_cast<const u32x4*>((ok ? p : kg) + col));
+                const int tau = t0 + xrel[it];
+                pxh[it] = buf_load16(hx, (xok[it] && tau < 0) ? (uint32_t)((W + tau) * D * 2) + xcb[it] : kOob);
             }
         }
         const rsrc_t rq = make_rsrc(qg + (size_t)t0 * D, (int64_t)(T_ - t0) * D * 2);
 #pragma unroll
         for (int it = 0; it < NXL; ++it) pq[it] = buf_load16(rq, qvo[it]);
         if (tid < CV) {
-            const bool ok = tid < Ct && t0 + tid < T_;
-            pal = ok ? a.alpha[(size_t)bh * T_ + t0 + tid] : 1.f;  // padding steps: identity
-            pet = ok ? a.eta[(size_t)bh * T_ + t0 + tid] : 0.f;
+            // clamped index, selected when staged
+            const size_t g = (size_t)bh * T_ + min(t0 + tid, T_ - 1);
+            pal = a.alpha[g];
+            pet = a.eta[g];
         }
     };
 
@@ -1218,6 +1379,10 @@ __global__ __launch_bounds__(256, 2) void chunk_prep2_kernel(ChunkArgs a, void* 
         float* recS = reinterpret_cast<float*>(rec + R::kScalBytes);
 
         // ---- stage the prefetched tile, then prefetch the next ----
+        if (tile * Ct < W) {
+#pragma unroll
+            for (int it = 0; it < NXL; ++it) px[it] |= pxh[it];
+        }
 #pragma unroll
         for (int it = 0; it < NXL; ++it) {
             const int c = tid + 256 * it;
@@ -1227,8 +1392,9 @@ __global__ __launch_bounds__(256, 2) void chunk_prep2_kernel(ChunkArgs a, void* 
             }
         }
         if (tid < CV) {
-            sm.al[tid] = pal;
-            sm.et[tid] = pet;
+            const bool ok = tid < Ct && tile * Ct + tid < T_;  // padding steps: identity
+            sm.al[tid] = ok ? pal : 1.f;
+            sm.et[tid] = ok ? pet : 0.f;
         }
         lds_barrier();
         if (job + (int)gridDim.x < njobs) load(job + gridDim.x);
