@@ -4,9 +4,9 @@
 
 A step is one falcon_chunk_fwd call for Falcon-1 over the whole batch B=8,
 H=16, T=4096, d_k=d_v=128, bf16 q/k/v, fp32 state, chunk 64, with the inputs
-resident in HBM: the intra-chunk kernel (prologue, masked Gram blocks,
-diagonal-block inverses) and the state-passing kernel (residuals, blocked
-forward substitution, outputs, state update, epilogue).  `value` is tokens
+resident in HBM: the intra-chunk kernel (norms, decay scan, masked Gram
+blocks, diagonal-block inverses) and the state-passing kernel (residuals,
+blocked forward substitution, outputs, state update).  `value` is tokens
 (B*T) per second.  The same line reports Falcon-1A on the same batch and the
 decode step (256 sequences x 32 heads, d=128, 1024 consecutive steps), each
 with its roofline, and the fp64 CPU oracle timed on this host over a bounded
@@ -190,7 +190,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic("chunk_fwd_F1_B8H16T4096d128_bf16_c64"),
-                     "kernel": "chunk_prep_kernel + chunk_scan_kernel (one falcon_chunk_fwd call)",
+                     "kernel": "chunk_prep2_kernel + chunk_pass_kernel (one falcon_chunk_fwd call)",
                      "algorithmic_bytes_per_launch": nbytes,
                      "mfma_tflops": tfs, "mfma_frac_bf16": tfs / BF16_PEAK_TFLOPS,
                      "algorithmic_flops_per_launch": nflops},
