@@ -1284,8 +1284,10 @@ struct Prep2Smem {
     uint16_t X[CV][LDX];           // keys x_i (virtual rows)
     uint16_t Q[CV][LDX];           // queries q_t
     uint16_t Om[COL ? CV : 1][LDX];  // per-column write vectors u_i
-    float Adg[CV / 16][16][17];    // diagonal blocks of A (fp32), then their inverses
+    alignas(16) float Adg[CV / 16][16][20];  // diagonal blocks of A (fp32), then their inverses
     float al[CV], et[CV];          // gates of the tile's steps (padding: 1, 0)
+    alignas(16) float cf[CV];      // column factor exp(g_ref(c) - g_j) r_j, c = block of j
+    float gref[CV / 16];           // log2(e) * g at the last row of each block
     float nrm[CV], l1[CV];         // ||x_i||^2, ||x_i||_1
     alignas(16) float gv[CV];      // log2(e) * g of the step of virtual row i
     alignas(16) float gs[CV];      // log2(e) * g_t per step t
@@ -1294,7 +1296,7 @@ struct Prep2Smem {
 };
 
 template <int D, int CV, bool DELTA, bool COL, bool WIN>
-__global__ __launch_bounds__(256, 2) void chunk_prep2_kernel(ChunkArgs a, void* ws, int ntiles,
+__global__ __launch_bounds__(256, 3) void chunk_prep2_kernel(ChunkArgs a, void* ws, int ntiles,
                                                              int njobs) {
     using E = EBf16;
     using T = uint16_t;
@@ -1461,6 +1463,13 @@ __global__ __launch_bounds__(256, 2) void chunk_prep2_kernel(ChunkArgs a, void* 
                 sm.gv[j] = gsj * kLog2e;
                 sm.gs[j] = lg * kLog2e;
                 sm.rs[j] = r;
+                if constexpr (!WIN) {
+                    // decays off the diagonal split at the block's last row: both
+                    // factors are exp(later - earlier) <= 1
+                    const float gref = __shfl(gsj, (j & ~15) + 15, 64);
+                    sm.cf[j] = __expf(gref - gsj) * r;
+                    if ((j & 15) == 15) sm.gref[j >> 4] = gref * kLog2e;
+                }
                 sm.step[j] = (j < NVR) ? sj : (1 << 20);  // padding rows: after every step
                 recS[0 * CV + j] = __expf(gsj);                  // gam
                 recS[1 * CV + j] = __expf(glast - gsj) * r;      // hrow
@@ -1490,59 +1499,155 @@ __global__ __launch_bounds__(256, 2) void chunk_prep2_kernel(ChunkArgs a, void* 
         }
         lds_barrier();
 
-        // ---- Gram blocks, round-robin over the waves.  Operands are swapped
-        // (rows of omega as the A operand) so lane (lr, grp) holds
-        // M[16 b + lr][16 c + 4 grp + r]: the fragment order the state pass reads.
+        // ---- Gram blocks.  Operands are swapped (rows of omega as the A
+        // operand) so lane (lr, grp) holds M[16 b + lr][16 c + 4 grp + r]: the
+        // fragment order the state pass reads.
         const T* omb = COL ? &sm.Om[0][0] : &sm.X[0][0];
-        for (int q = wave; q < NJA + NJP; q += 4) {
-            const bool isA = q < NJA;
-            int b, c;
-            if (isA || !WIN) {
-                const int qq = isA ? q : q - NJA;
-                b = 0;
-                while ((b + 1) * (b + 2) / 2 <= qq) ++b;
-                c = qq - b * (b + 1) / 2;
-            } else {
-                b = (q - NJA) / NB;
-                c = (q - NJA) - b * NB;
-                if (!(b < NBQ && (16 * c) / Wv <= 16 * b + 15)) continue;  // never read
-            }
-            const T* ar = omb + (size_t)(16 * c + lr) * LDX + 4 * grp;
-            const T* br = (isA ? &sm.X[16 * b + lr][0] : &sm.Q[16 * b + lr][0]) + 4 * grp;
-            f32x4 acc = zero4();
+        if constexpr (!WIN) {
+            // Wave w owns A row block w and P row block NB-1-w (the A family:
+            // P row block w): its key and query rows are loaded once, and each
+            // column block's omega rows serve both products as two independent
+            // accumulation chains.
+            constexpr int KM = D / 32;
+            const int bA = wave, bP = DELTA ? NB - 1 - wave : wave;
+            if (wave < NB) {
+                Frag xa[KM][2], qp[KM][2];
 #pragma unroll
-            for (int m = 0; m < D / 32; ++m)
-                acc = E::mma32(E::load(ar + 32 * m), E::load(ar + 32 * m + 16), E::load(br + 32 * m),
-                               E::load(br + 32 * m + 16), acc);
-            const int j0 = 16 * c + 4 * grp;
-            const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.gv[j0]);
-            const f32x4 rj = *reinterpret_cast<const f32x4*>(&sm.rs[j0]);
-            const int4 sj = *reinterpret_cast<const int4*>(&sm.step[j0]);
-            const int i = 16 * b + lr;
-            f32x4 val;
-            if (isA) {
-                const int si = sm.step[i];
-                const float gi = sm.gv[i];
-                val[0] = (sj.x < si) ? exp2f(gi - gj[0]) * acc[0] * rj[0] : 0.f;
-                val[1] = (sj.y < si) ? exp2f(gi - gj[1]) * acc[1] * rj[1] : 0.f;
-                val[2] = (sj.z < si) ? exp2f(gi - gj[2]) * acc[2] * rj[2] : 0.f;
-                val[3] = (sj.w < si) ? exp2f(gi - gj[3]) * acc[3] * rj[3] : 0.f;
-                if (b == c) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) sm.Adg[b][lr][4 * grp + r] = val[r];
-                } else {
-                    *reinterpret_cast<Frag*>(recT + R::kA + (size_t)R::ablk(b, c) * 256 + lane * 4) =
-                        E::pack(-val);
+                for (int m = 0; m < KM; ++m) {
+                    const T* xr = &sm.X[16 * bA + lr][32 * m + 4 * grp];
+                    const T* qr = &sm.Q[16 * bP + lr][32 * m + 4 * grp];
+                    if constexpr (DELTA) {
+                        xa[m][0] = E::load(xr);
+                        xa[m][1] = E::load(xr + 16);
+                    }
+                    qp[m][0] = E::load(qr);
+                    qp[m][1] = E::load(qr + 16);
                 }
-            } else {
-                const bool tv = i < Ct;
-                const float gi = sm.gs[i];
-                val[0] = (tv && sj.x <= i) ? exp2f(gi - gj[0]) * acc[0] * rj[0] : 0.f;
-                val[1] = (tv && sj.y <= i) ? exp2f(gi - gj[1]) * acc[1] * rj[1] : 0.f;
-                val[2] = (tv && sj.z <= i) ? exp2f(gi - gj[2]) * acc[2] * rj[2] : 0.f;
-                val[3] = (tv && sj.w <= i) ? exp2f(gi - gj[3]) * acc[3] * rj[3] : 0.f;
-                *reinterpret_cast<Frag*>(recT + R::kP + (size_t)R::pblk(b, c, WIN) * 256 + lane * 4) =
-                    E::pack(val);
+                const int iA = 16 * bA + lr, iP = 16 * bP + lr;
+                const float giA = sm.gv[iA], giP = sm.gs[iP];
+                static_for<NB>([&](auto cc) __attribute__((always_inline)) {
+                    constexpr int c = decltype(cc)::value;
+                    const bool doA = DELTA && c <= bA, doP = c <= bP;
+                    if (doA || doP) {
+                        const T* ar = omb + (size_t)(16 * c + lr) * LDX + 4 * grp;
+                        f32x4 accA = zero4(), accP = zero4();
+#pragma unroll
+                        for (int m = 0; m < KM; ++m) {
+                            const Frag o0 = E::load(ar + 32 * m), o1 = E::load(ar + 32 * m + 16);
+                            if (doA) accA = E::mma32(o0, o1, xa[m][0], xa[m][1], accA);
+                            if (doP) accP = E::mma32(o0, o1, qp[m][0], qp[m][1], accP);
+                        }
+                        const int j0 = 16 * c + 4 * grp;
+                        if (doA) {
+                            f32x4 val;
+                            if (c < bA) {
+                                // fully unmasked: row factor times column factor
+                                const f32x4 cfj = *reinterpret_cast<const f32x4*>(&sm.cf[j0]);
+                                const float rf = exp2f(giA - sm.gref[c]);
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) val[r] = accA[r] * rf * cfj[r];
+                                *reinterpret_cast<Frag*>(recT + R::kA + (size_t)R::ablk(bA, c) * 256 +
+                                                         lane * 4) = E::pack(-val);
+                            } else {
+                                const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.gv[j0]);
+                                const f32x4 rj = *reinterpret_cast<const f32x4*>(&sm.rs[j0]);
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) {
+                                    const int j = j0 + r;
+                                    val[r] = (j < iA) ? exp2f(giA - gj[r]) * accA[r] * rj[r] : 0.f;
+                                    sm.Adg[bA][lr][4 * grp + r] = val[r];
+                                }
+                            }
+                        }
+                        if (doP) {
+                            f32x4 val;
+                            if (c < bP) {
+                                const f32x4 cfj = *reinterpret_cast<const f32x4*>(&sm.cf[j0]);
+                                const float rf = exp2f(giP - sm.gref[c]);
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) val[r] = accP[r] * rf * cfj[r];
+                            } else {
+                                const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.gv[j0]);
+                                const f32x4 rj = *reinterpret_cast<const f32x4*>(&sm.rs[j0]);
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) {
+                                    const int j = j0 + r;
+                                    val[r] = (j <= iP && iP < Ct) ? exp2f(giP - gj[r]) * accP[r] * rj[r]
+                                                                  : 0.f;
+                                }
+                            }
+                            *reinterpret_cast<Frag*>(recT + R::kP + (size_t)R::pblk(bP, c, WIN) * 256 +
+                                                     lane * 4) = E::pack(val);
+                        }
+                    }
+                });
+            }
+        } else {
+            // window: round-robin over the waves
+            for (int q = wave; q < NJA + NJP; q += 4) {
+                const bool isA = q < NJA;
+                int b, c;
+                if (isA || !WIN) {
+                    const int qq = isA ? q : q - NJA;
+                    b = 0;
+                    while ((b + 1) * (b + 2) / 2 <= qq) ++b;
+                    c = qq - b * (b + 1) / 2;
+                } else {
+                    b = (q - NJA) / NB;
+                    c = (q - NJA) - b * NB;
+                    if (!(b < NBQ && (16 * c) / Wv <= 16 * b + 15)) continue;  // never read
+                }
+                const T* ar = omb + (size_t)(16 * c + lr) * LDX + 4 * grp;
+                const T* br = (isA ? &sm.X[16 * b + lr][0] : &sm.Q[16 * b + lr][0]) + 4 * grp;
+                f32x4 acc = zero4();
+    #pragma unroll
+                for (int m = 0; m < D / 32; ++m)
+                    acc = E::mma32(E::load(ar + 32 * m), E::load(ar + 32 * m + 16), E::load(br + 32 * m),
+                                   E::load(br + 32 * m + 16), acc);
+                const int j0 = 16 * c + 4 * grp;
+                const int i = 16 * b + lr;
+                f32x4 val;
+                if (!WIN && c < b) {
+                    // fully unmasked block: row factor times column factor
+                    const f32x4 cfj = *reinterpret_cast<const f32x4*>(&sm.cf[j0]);
+                    const float rf = exp2f((isA ? sm.gv[i] : sm.gs[i]) - sm.gref[c]);
+    #pragma unroll
+                    for (int r = 0; r < 4; ++r) val[r] = acc[r] * rf * cfj[r];
+                    if (isA)
+                        *reinterpret_cast<Frag*>(recT + R::kA + (size_t)R::ablk(b, c) * 256 + lane * 4) =
+                            E::pack(-val);
+                    else
+                        *reinterpret_cast<Frag*>(recT + R::kP + (size_t)R::pblk(b, c, WIN) * 256 + lane * 4) =
+                            E::pack(val);
+                    continue;
+                }
+                const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.gv[j0]);
+                const f32x4 rj = *reinterpret_cast<const f32x4*>(&sm.rs[j0]);
+                const int4 sj = *reinterpret_cast<const int4*>(&sm.step[j0]);
+                if (isA) {
+                    const int si = sm.step[i];
+                    const float gi = sm.gv[i];
+                    val[0] = (sj.x < si) ? exp2f(gi - gj[0]) * acc[0] * rj[0] : 0.f;
+                    val[1] = (sj.y < si) ? exp2f(gi - gj[1]) * acc[1] * rj[1] : 0.f;
+                    val[2] = (sj.z < si) ? exp2f(gi - gj[2]) * acc[2] * rj[2] : 0.f;
+                    val[3] = (sj.w < si) ? exp2f(gi - gj[3]) * acc[3] * rj[3] : 0.f;
+                    if (b == c) {
+    #pragma unroll
+                        for (int r = 0; r < 4; ++r) sm.Adg[b][lr][4 * grp + r] = val[r];
+                    } else {
+                        *reinterpret_cast<Frag*>(recT + R::kA + (size_t)R::ablk(b, c) * 256 + lane * 4) =
+                            E::pack(-val);
+                    }
+                } else {
+                    const bool tv = i < Ct;
+                    const float gi = sm.gs[i];
+                    val[0] = (tv && sj.x <= i) ? exp2f(gi - gj[0]) * acc[0] * rj[0] : 0.f;
+                    val[1] = (tv && sj.y <= i) ? exp2f(gi - gj[1]) * acc[1] * rj[1] : 0.f;
+                    val[2] = (tv && sj.z <= i) ? exp2f(gi - gj[2]) * acc[2] * rj[2] : 0.f;
+                    val[3] = (tv && sj.w <= i) ? exp2f(gi - gj[3]) * acc[3] * rj[3] : 0.f;
+                    *reinterpret_cast<Frag*>(recT + R::kP + (size_t)R::pblk(b, c, WIN) * 256 + lane * 4) =
+                        E::pack(val);
+                }
             }
         }
         if constexpr (DELTA) {
@@ -1556,10 +1661,16 @@ __global__ __launch_bounds__(256, 2) void chunk_prep2_kernel(ChunkArgs a, void* 
                     float tcol[16];
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        float acc = (i == c) ? 1.f : 0.f;
+                        // t_i = delta_ic - sum_{j<i} A_ij t_j, as four independent chains
+                        float part[4] = {(i == c) ? 1.f : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int j = 0; j < i; ++j) acc -= sm.Adg[bb][i][j] * tcol[j];
-                        tcol[i] = acc;
+                        for (int j4 = 0; j4 < i; j4 += 4) {
+                            const f32x4 arow = *reinterpret_cast<const f32x4*>(&sm.Adg[bb][i][j4]);
+#pragma unroll
+                            for (int u = 0; u < 4; ++u)
+                                if (j4 + u < i) part[u] -= arow[u] * tcol[j4 + u];
+                        }
+                        tcol[i] = (part[0] + part[1]) + (part[2] + part[3]);
                     }
                     __builtin_amdgcn_wave_barrier();
 #pragma unroll
