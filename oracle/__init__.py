@@ -9,6 +9,7 @@ Contents
 recurrent(...)    the step-by-step form, in plain C (falcon_oracle.c), threads
                   over the independent (batch, head) sequences.
 decode_step(...)  one step of the same recurrence for N x H heads.
+decode_step_window(...)  the same for Falcon-3/3A, with key and value caches.
 forms             numpy fp64 masked-parallel and chunk-parallel forms, used only
                   to cross-check the recurrent form (the authors' abstract of
                   "Fast Weight Attention for Continual Learning" states that the
@@ -55,6 +56,8 @@ def _load():
         lib.oracle_recurrent.argtypes = [ctypes.c_int] * 7 + [ctypes.c_double] + [dp] * 10 + [ctypes.c_int]
         lib.oracle_decode_step.restype = ctypes.c_int
         lib.oracle_decode_step.argtypes = [ctypes.c_int] * 5 + [ctypes.c_double] + [dp] * 8
+        lib.oracle_decode_step_window.restype = ctypes.c_int
+        lib.oracle_decode_step_window.argtypes = [ctypes.c_int] * 6 + [ctypes.c_double] + [dp] * 9
         lib.oracle_num_cpus.restype = ctypes.c_int
         lib.oracle_num_cpus.argtypes = []
         _lib = lib
@@ -126,3 +129,27 @@ def decode_step(variant, S, k_cache, q, k, v, alpha, eta, *, eps=1e-6):
     if rc < 0:
         raise ValueError(f"oracle_decode_step rejected its arguments (code {rc})")
     return o, S, k_cache
+
+
+def decode_step_window(variant, S, k_cache, v_cache, q, k, v, alpha, eta, *, eps=1e-6):
+    """One Falcon-3 / Falcon-3A decode step with a window of W pairs.
+
+    S [N,H,dv,dk]; k_cache [N,H,W,dk] with k_cache[..., w, :] = k_{t-1-w};
+    v_cache [N,H,W-1,dv] with v_cache[..., w-1, :] = v_{t-w}.  Returns
+    (o, S_new, k_cache_new, v_cache_new), all float64 copies."""
+    variant = VARIANTS.get(variant, variant)
+    S = _f64(S).copy()
+    q, k, v, alpha, eta = map(_f64, (q, k, v, alpha, eta))
+    N, H, dv, dk = S.shape
+    k_cache = _f64(k_cache).reshape(N, H, -1, dk).copy()
+    W = k_cache.shape[2]
+    v_cache = (_f64(v_cache).reshape(N, H, W - 1, dv).copy() if W > 1
+               else np.zeros((N, H, 0, dv), np.float64))
+    o = np.zeros((N, H, dv), np.float64)
+    vbuf = v_cache if W > 1 else np.zeros((N, H, 1, dv), np.float64)
+    rc = _load().oracle_decode_step_window(variant, N, H, dk, dv, W, float(eps), _ptr(S),
+                                           _ptr(k_cache), _ptr(vbuf), _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(alpha), _ptr(eta), _ptr(o))
+    if rc < 0:
+        raise ValueError(f"oracle_decode_step_window rejected its arguments (code {rc})")
+    return o, S, k_cache, v_cache

@@ -276,3 +276,64 @@ int oracle_decode_step(int variant, int N, int H, int dk, int dv, double eps, do
     free(r);
     return 0;
 }
+
+/*
+ * One step of Falcon-3 / Falcon-3A for N x H heads, carrying the window in
+ * caches (newest first):
+ *   k_cache [N,H,W,dk]:  k_cache[w] = k_{t-1-w}, so x_{t-w} = k_cache[w];
+ *   v_cache [N,H,W-1,dv]: v_cache[w-1] = v_{t-w} for w >= 1 (y_t = v, the new
+ *                         value).
+ * The step is the same one the recurrent form takes at step t: S' = alpha S,
+ * b = eta / (sum_w ||x_{t-w}||^2 + eps), then S = S' + b sum_w R_w x_{t-w}^T
+ * with every residual R_w = y_{t-w} - S' x_{t-w} taken at S' (Falcon-3A:
+ * R_w = y_{t-w}), and o = S q.  Both caches then move one slot: the new key
+ * and value enter at slot 0 and the oldest leave.
+ */
+int oracle_decode_step_window(int variant, int N, int H, int dk, int dv, int W, double eps,
+                              double* S, double* k_cache, double* v_cache, const double* q,
+                              const double* k, const double* v, const double* alpha,
+                              const double* eta, double* o) {
+    if (variant != OR_F3 && variant != OR_F3A) return -3;
+    if (N < 1 || H < 1 || dk < 1 || dv < 1 || W < 1) return -2;
+    double* R = calloc((size_t)W * dv, sizeof(double));
+    const double** y = calloc((size_t)W, sizeof(double*));
+    for (size_t n = 0; n < (size_t)N * H; ++n) {
+        double* Sh = S + n * dv * dk;
+        double* kc = k_cache + n * W * dk;
+        double* vc = v_cache + n * (W - 1) * dv;
+        const double *qh = q + n * dk, *kh = k + n * dk, *vh = v + n * dv;
+        const double a = alpha[n], e = eta[n];
+        for (int w = 0; w < W; ++w) y[w] = (w == 0) ? vh : vc + (size_t)(w - 1) * dv;
+        for (size_t m = 0; m < (size_t)dv * dk; ++m) Sh[m] *= a;
+        double nrm = 0.0;
+        for (int w = 0; w < W; ++w)
+            for (int c = 0; c < dk; ++c) nrm += kc[(size_t)w * dk + c] * kc[(size_t)w * dk + c];
+        const double b = e / (nrm + eps);
+        for (int w = 0; w < W; ++w) {
+            const double* x = kc + (size_t)w * dk;
+            for (int i = 0; i < dv; ++i) {
+                double s = 0.0;
+                if (variant == OR_F3)
+                    for (int c = 0; c < dk; ++c) s += Sh[(size_t)i * dk + c] * x[c];
+                R[(size_t)w * dv + i] = y[w][i] - s;
+            }
+        }
+        for (int w = 0; w < W; ++w) {
+            const double* x = kc + (size_t)w * dk;
+            for (int i = 0; i < dv; ++i)
+                for (int c = 0; c < dk; ++c) Sh[(size_t)i * dk + c] += b * R[(size_t)w * dv + i] * x[c];
+        }
+        for (int i = 0; i < dv; ++i) {
+            double s = 0.0;
+            for (int c = 0; c < dk; ++c) s += Sh[(size_t)i * dk + c] * qh[c];
+            o[n * dv + i] = s;
+        }
+        for (int w = W - 1; w >= 1; --w) memcpy(kc + (size_t)w * dk, kc + (size_t)(w - 1) * dk, sizeof(double) * dk);
+        memcpy(kc, kh, sizeof(double) * dk);
+        for (int w = W - 2; w >= 1; --w) memcpy(vc + (size_t)w * dv, vc + (size_t)(w - 1) * dv, sizeof(double) * dv);
+        if (W > 1) memcpy(vc, vh, sizeof(double) * dv);
+    }
+    free(R);
+    free(y);
+    return 0;
+}

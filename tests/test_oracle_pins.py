@@ -504,6 +504,68 @@ def test_decode_step_is_one_recurrent_step(variant):
     np.testing.assert_allclose(S_run, S_rec, rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("variant", ["F3", "F3A"])
+@pytest.mark.parametrize("W", [1, 2, 4])
+def test_decode_step_window_is_one_recurrent_step(variant, W):
+    """Windowed decode (caches newest first) over T steps equals the recurrent
+    form with the same halo (k_prev / v_prev oldest first); the caches end as
+    the last W keys and W-1 values."""
+    r = np.random.default_rng(31 + W)
+    N, H, dk, dv, steps = 2, 2, 5, 4, 11
+    S = r.standard_normal((N, H, dv, dk)) * 0.1
+    k_prev = r.standard_normal((N, H, W, dk))
+    v_prev = r.standard_normal((N, H, W - 1, dv))
+    kc = k_prev[:, :, ::-1, :].copy()          # kc[w] = k_{-1-w}
+    vc = v_prev[:, :, ::-1, :].copy()          # vc[w-1] = v_{-w}
+    q, k = r.standard_normal((steps, N, H, dk)), r.standard_normal((steps, N, H, dk))
+    v = r.standard_normal((steps, N, H, dv))
+    al, et = r.uniform(0.5, 1, (steps, N, H)), r.uniform(0, 1, (steps, N, H))
+    S_run, kc_run, vc_run, outs = S, kc, vc, []
+    for s in range(steps):
+        o, S_run, kc_run, vc_run = oracle.decode_step_window(variant, S_run, kc_run, vc_run, q[s],
+                                                             k[s], v[s], al[s], et[s])
+        outs.append(o)
+    tr = lambda a: np.moveaxis(a, 0, 2)  # noqa: E731
+    o_rec, S_rec = oracle.recurrent(variant, tr(q), tr(k), tr(v), tr(al), tr(et), window=W,
+                                    S0=S, k_prev=k_prev, v_prev=v_prev if W > 1 else None)
+    np.testing.assert_allclose(tr(np.array(outs)), o_rec, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(S_run, S_rec, rtol=1e-12, atol=1e-13)
+    for w in range(W):
+        np.testing.assert_array_equal(kc_run[:, :, w], k[steps - 1 - w])
+    for w in range(W - 1):
+        np.testing.assert_array_equal(vc_run[:, :, w], v[steps - 1 - w])
+
+
+@pytest.mark.parametrize("variant,base", [("F3", "F1"), ("F3A", "F1A")])
+def test_decode_step_window_of_one_is_the_scalar_rule(variant, base):
+    """Reduction: a window of one pair is Falcon-1 (Falcon-1A) exactly."""
+    r = np.random.default_rng(37)
+    N, H, dk, dv = 3, 2, 6, 5
+    S = r.standard_normal((N, H, dv, dk)) * 0.2
+    kc = r.standard_normal((N, H, dk))
+    q, k, v = r.standard_normal((N, H, dk)), r.standard_normal((N, H, dk)), r.standard_normal((N, H, dv))
+    al, et = r.uniform(0.5, 1, (N, H)), r.uniform(0, 1, (N, H))
+    o1, S1, _ = oracle.decode_step(base, S, kc, q, k, v, al, et)
+    o3, S3, _, _ = oracle.decode_step_window(variant, S, kc[:, :, None, :], None, q, k, v, al, et)
+    np.testing.assert_allclose(o3, o1, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(S3, S1, rtol=1e-13, atol=1e-14)
+
+
+def test_decode_step_window_interpolates_its_window():
+    """P2 on the decode path: alpha = 1, eta = 1, eps = 0 and a window whose
+    only nonzero key is x_{t-1} (slot 1) makes S x_{t-1} = y_{t-1} exactly."""
+    r = np.random.default_rng(41)
+    N, H, dk, dv, W = 1, 1, 4, 3, 3
+    S = r.standard_normal((N, H, dv, dk))
+    kc = np.zeros((N, H, W, dk))
+    kc[:, :, 1] = r.standard_normal(dk)
+    vc = r.standard_normal((N, H, W - 1, dv))
+    q, k, v = r.standard_normal((N, H, dk)), r.standard_normal((N, H, dk)), r.standard_normal((N, H, dv))
+    one = np.ones((N, H))
+    _, S_new, _, _ = oracle.decode_step_window("F3", S, kc, vc, q, k, v, one, one, eps=0.0)
+    np.testing.assert_allclose(S_new[0, 0] @ kc[0, 0, 1], vc[0, 0, 0], rtol=1e-12, atol=1e-12)
+
+
 def test_oracle_rejects_bad_arguments():
     d = rnd(27)
     with pytest.raises(ValueError):
