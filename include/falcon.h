@@ -24,8 +24,9 @@
  * The abstract states that each rule has a chunk-parallel form with
  * positive-decay renormalization; falcon_chunk_fwd computes that form
  * (cumulative decays kept as chunk-local log sums, every factor a ratio
- * later/earlier <= 1).  falcon_decode_step advances the recurrence by one
- * token for many independent heads.
+ * later/earlier <= 1).  falcon_decode_step (and falcon_decode_step_window for
+ * the window rules) advances the recurrence by one token for many
+ * independent heads.
  *
  * Conventions for every entry point
  *   - Pointers are device memory owned by the caller, except where noted.
@@ -135,6 +136,38 @@ int falcon_decode_step(float* S, void* k_cache, const void* q, const void* k, co
                        const float* alpha, const float* eta, void* o, int N, int H, int dk,
                        int dv, falcon_dtype dt, falcon_variant var, int window, float eps,
                        hipStream_t stream);
+
+/*
+ * One decode step of Falcon-3 / Falcon-3A (the sliding-window mini-batch
+ * rule, "Fast Weight Attention for Continual Learning", authors' abstract)
+ * for N sequences x H heads.  The window of the W most recent prefix-aligned
+ * pairs is carried in two caches, newest first:
+ *
+ *   S         [N,H,dv,dk]  fp32, read and overwritten in place
+ *   k_cache   [N,H,W,dk]   dtype dt, slot w holds k_{t-1-w} (x_{t-w});
+ *                          on return slot 0 holds k_t and the rest moved one slot
+ *   v_cache   [N,H,W-1,dv] dtype dt, slot w-1 holds v_{t-w} (y_{t-w}, w >= 1);
+ *                          on return slot 0 holds v_t; may be NULL when W = 1
+ *   q, k      [N,H,dk]     dtype dt
+ *   v         [N,H,dv]     dtype dt (y_t)
+ *   alpha,eta [N,H]        fp32
+ *   o         [N,H,dv]     dtype dt output, o = S q after the write (must not
+ *                          alias inputs)
+ *
+ * The step: S' = alpha S, b = eta / (sum_w ||x_{t-w}||^2 + eps), then
+ * S = S' + b sum_w (y_{t-w} - S' x_{t-w}) x_{t-w}^T (Falcon-3A writes
+ * y_{t-w} instead of the residual), o = S q: the step falcon_chunk_fwd takes
+ * at time t.  Caches filled from a chunk call's halo: k_cache[w] = k_prev[W-1-w],
+ * v_cache[w-1] = v_prev[W-1-w].
+ *
+ * Support matrix: var in {F3, F3A}; window W in 1..8; dk = dv in {64, 128};
+ * dt fp32 or bf16.
+ */
+int falcon_decode_step_window(float* S, void* k_cache, void* v_cache, const void* q,
+                              const void* k, const void* v, const float* alpha,
+                              const float* eta, void* o, int N, int H, int dk, int dv,
+                              falcon_dtype dt, falcon_variant var, int window, float eps,
+                              hipStream_t stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* falcon_status_string(int status);

@@ -28,7 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["falcon_chunk_fwd", "falcon_chunk_fwd_workspace",
-                                           "falcon_decode_step", "falcon_status_string"])
+                                           "falcon_decode_step", "falcon_decode_step_window",
+                                           "falcon_status_string"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -107,6 +108,27 @@ def decode(L, **kw):
 ])
 def test_decode_rejects(L, kw, code):
     assert decode(L, **kw) == code
+
+
+def decode_window(L, **kw):
+    a = dict(S=P, kc=P, vc=P, q=P, k=P, v=P, alpha=P, eta=P, o=P, N=4, H=2, dk=128, dv=128, dt=1,
+             var=3, window=4, eps=1e-6)
+    a.update(kw)
+    return L.falcon_decode_step_window(a["S"], a["kc"], a["vc"], a["q"], a["k"], a["v"],
+                                       a["alpha"], a["eta"], a["o"], a["N"], a["H"], a["dk"],
+                                       a["dv"], a["dt"], a["var"], a["window"],
+                                       ctypes.c_float(a["eps"]), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(var=1), -3), (dict(var=11), -3), (dict(var=2), -3), (dict(dt=5), -3),
+    (dict(N=0), -2), (dict(H=0), -2), (dict(window=0), -2), (dict(window=9), -3),
+    (dict(dk=32, dv=32), -3), (dict(dk=128, dv=64), -3), (dict(eps=-1.0), -2),
+    (dict(S=None), -1), (dict(kc=None), -1), (dict(vc=None), -1), (dict(o=None), -1),
+    (dict(alpha=None), -1), (dict(S=P + 4), -3), (dict(eta=P + 2), -3),
+])
+def test_decode_window_rejects(L, kw, code):
+    assert decode_window(L, **kw) == code
 
 
 def test_python_binding_checks_shapes():

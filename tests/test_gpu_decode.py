@@ -1,4 +1,5 @@
-"""GPU parity of falcon_decode_step against the fp64 oracle's decode step.
+"""GPU parity of falcon_decode_step and falcon_decode_step_window against the
+fp64 oracle's decode steps.
 
 Every step's output and the final state and key cache are compared per head
 (max|gpu - oracle| / max|oracle|, 1e-4 for fp32 inputs, 2e-2 for bf16)."""
@@ -91,3 +92,64 @@ def test_decode_full_workload_sampled(dev):
     e_S = slice_rel_err(to_np(S[ns, hs]), S_o[0], (1, 2))
     announce(f"decode full workload: max rel err o={e_o:.2e} S={e_S:.2e}")
     assert e_o <= TOL["bf16"] and e_S <= TOL["bf16"], (e_o, e_S)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("W", [1, 2, 4, 8])
+@pytest.mark.parametrize("variant", ["F3", "F3A"])
+def test_decode_window_grid(dev, variant, W, dtype, D):
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    N, H, steps = 3, 4, 10
+    di = I.make_decode_inputs(N, H, D, D, steps, dtype=dtype, seed=700 + 10 * W + D, S0_sd=0.1,
+                              window=W)
+    S = tens(di.S0, "fp32", dev)
+    kc = tens(di.k_cache0, dtype, dev)
+    vc = tens(di.v_cache0, dtype, dev) if W > 1 else None
+    S_o, kc_o, vc_o = di.S0.astype(np.float64), di.widen(di.k_cache0), di.widen(di.v_cache0)
+    tol = TOL[dtype]
+    for s in range(steps):
+        announce(f"decode_step_window {variant} W{W} {dtype} N{N} H{H} d{D} step {s}")
+        o = fal.decode_step_window(S, kc, vc, tens(di.q[s], dtype, dev), tens(di.k[s], dtype, dev),
+                                   tens(di.v[s], dtype, dev), tens(di.alpha[s], "fp32", dev),
+                                   tens(di.eta[s], "fp32", dev), variant)
+        o_ref, S_o, kc_o, vc_o = oracle.decode_step_window(
+            variant, S_o, kc_o, vc_o, di.widen(di.q[s]), di.widen(di.k[s]), di.widen(di.v[s]),
+            di.alpha[s], di.eta[s])
+        torch.cuda.synchronize()
+        assert slice_rel_err(to_np(o), o_ref, (2,)) <= tol
+    assert slice_rel_err(to_np(S), S_o, (2, 3)) <= tol
+    # the caches only move values: bit-exact
+    np.testing.assert_array_equal(to_np(kc), kc_o)
+    if W > 1:
+        np.testing.assert_array_equal(to_np(vc), vc_o)
+
+
+def test_decode_window_continues_a_chunk_call(dev):
+    """A Falcon-3 chunk call over T tokens followed by decode steps equals one
+    chunk call over all tokens: the caches are the chunk call's halo reversed
+    (newest first)."""
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    B, H, T, D, W, extra = 1, 3, 40, 64, 4, 6
+    inp = I.make_chunk_inputs(B, H, T + extra, D, D, dtype="fp32", seed=77, window=W)
+    t = inp.to_torch(dev)
+    sl = lambda a, lo, hi: a[:, :, lo:hi].contiguous()  # noqa: E731
+    announce("decode_step_window continues chunk_fwd F3 W4 fp32")
+    o_all, S_all = fal.chunk_fwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], "F3", window=W,
+                                 chunk=16, return_state=True)
+    _, S_T = fal.chunk_fwd(sl(t["q"], 0, T), sl(t["k"], 0, T), sl(t["v"], 0, T),
+                           sl(t["alpha"], 0, T), sl(t["eta"], 0, T), "F3", window=W, chunk=16,
+                           return_state=True)
+    kc = t["k"][:, :, T - W:T].flip(2).contiguous()          # k_{T-1} .. k_{T-W}
+    vc = t["v"][:, :, T - W + 1:T].flip(2).contiguous()      # v_{T-1} .. v_{T-W+1}
+    S = S_T.contiguous()
+    for s in range(T, T + extra):
+        o = fal.decode_step_window(S, kc, vc, t["q"][:, :, s].contiguous(),
+                                   t["k"][:, :, s].contiguous(), t["v"][:, :, s].contiguous(),
+                                   t["alpha"][:, :, s].contiguous(), t["eta"][:, :, s].contiguous(),
+                                   "F3")
+        torch.cuda.synchronize()
+        assert slice_rel_err(to_np(o), to_np(o_all[:, :, s]), (2,)) <= 1e-4
+    assert slice_rel_err(to_np(S), to_np(S_all), (2, 3)) <= 1e-4

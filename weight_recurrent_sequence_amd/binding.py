@@ -20,7 +20,7 @@ FP32, BF16 = 0, 1
 STATUS = {0: "FALCON_OK", -1: "FALCON_ERR_NULL", -2: "FALCON_ERR_SHAPE",
           -3: "FALCON_ERR_UNSUPPORTED", -4: "FALCON_ERR_WORKSPACE", -5: "FALCON_ERR_HIP"}
 EXPORTS = ("falcon_chunk_fwd_workspace", "falcon_chunk_fwd", "falcon_decode_step",
-           "falcon_status_string")
+           "falcon_decode_step_window", "falcon_status_string")
 
 
 class FalconError(RuntimeError):
@@ -48,6 +48,8 @@ def lib():
         L.falcon_chunk_fwd.argtypes = [vp] * 10 + [ci] * 9 + [cf, vp, sz, vp]
         L.falcon_decode_step.restype = ci
         L.falcon_decode_step.argtypes = [vp] * 8 + [ci] * 7 + [cf, vp]
+        L.falcon_decode_step_window.restype = ci
+        L.falcon_decode_step_window.argtypes = [vp] * 9 + [ci] * 7 + [cf, vp]
         L.falcon_status_string.restype = ctypes.c_char_p
         L.falcon_status_string.argtypes = [ci]
         _lib = L
@@ -172,4 +174,36 @@ def decode_step(S, k_cache, q, k, v, alpha, eta, variant, *, eps=1e-6, o=None, s
                                   float(eps), _stream(stream))
     if st != 0:
         raise FalconError(st, "falcon_decode_step")
+    return o
+
+
+def decode_step_window(S, k_cache, v_cache, q, k, v, alpha, eta, variant, *, eps=1e-6, o=None,
+                       stream=None):
+    """One Falcon-3 / Falcon-3A decode step.  S [N,H,dv,dk] fp32, k_cache
+    [N,H,W,dk] (slot w = k_{t-1-w}) and v_cache [N,H,W-1,dv] (slot w-1 =
+    v_{t-w}; None when W = 1) are updated in place; q,k [N,H,dk], v [N,H,dv]
+    (bf16 or fp32), alpha, eta [N,H] fp32.  Returns o [N,H,dv]."""
+    import torch
+    var = _variant(variant)
+    N, H, dv, dk = S.shape
+    dev, dt = k.device, k.dtype
+    dtc = _dt(k)
+    W = k_cache.shape[2] if k_cache.dim() == 4 else -1
+    _check(S, "S", (N, H, dv, dk), torch.float32, dev)
+    _check(k_cache, "k_cache", (N, H, W, dk), dt, dev)
+    if W > 1 or v_cache is not None:
+        _check(v_cache, "v_cache", (N, H, W - 1, dv), dt, dev)
+    _check(q, "q", (N, H, dk), dt, dev)
+    _check(k, "k", (N, H, dk), dt, dev)
+    _check(v, "v", (N, H, dv), dt, dev)
+    _check(alpha, "alpha", (N, H), torch.float32, dev)
+    _check(eta, "eta", (N, H), torch.float32, dev)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=dt, device=dev)
+    _check(o, "o", (N, H, dv), dt, dev)
+    st = lib().falcon_decode_step_window(_ptr(S), _ptr(k_cache), _ptr(v_cache) if W > 1 else None,
+                                         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(o),
+                                         N, H, dk, dv, dtc, var, W, float(eps), _stream(stream))
+    if st != 0:
+        raise FalconError(st, "falcon_decode_step_window")
     return o

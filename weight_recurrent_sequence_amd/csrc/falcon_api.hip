@@ -105,6 +105,7 @@ int falcon_decode_step(float* S, void* k_cache, const void* q, const void* k, co
                        int dv, falcon_dtype dt, falcon_variant var, int window, float eps,
                        hipStream_t stream) {
     if (!is_variant(var)) return FALCON_ERR_UNSUPPORTED;
+    // the window rules have their own entry point, falcon_decode_step_window
     if (var == FALCON_F3 || var == FALCON_F3A) return FALCON_ERR_UNSUPPORTED;
     if (dt != FALCON_FP32 && dt != FALCON_BF16) return FALCON_ERR_UNSUPPORTED;
     if (N < 1 || H < 1 || dk < 1 || dv < 1 || window < 1) return FALCON_ERR_SHAPE;
@@ -128,6 +129,39 @@ int falcon_decode_step(float* S, void* k_cache, const void* q, const void* k, co
     a.delta = is_delta(var) ? 1 : 0;
     a.eps = eps;
     hipError_t e = falcon::launch_decode(a, (int)dt, dk, stream);
+    return e == hipSuccess ? FALCON_OK : FALCON_ERR_HIP;
+}
+
+int falcon_decode_step_window(float* S, void* k_cache, void* v_cache, const void* q,
+                              const void* k, const void* v, const float* alpha,
+                              const float* eta, void* o, int N, int H, int dk, int dv,
+                              falcon_dtype dt, falcon_variant var, int window, float eps,
+                              hipStream_t stream) {
+    if (var != FALCON_F3 && var != FALCON_F3A) return FALCON_ERR_UNSUPPORTED;
+    if (dt != FALCON_FP32 && dt != FALCON_BF16) return FALCON_ERR_UNSUPPORTED;
+    if (N < 1 || H < 1 || dk < 1 || dv < 1 || window < 1) return FALCON_ERR_SHAPE;
+    if ((long long)N * H > (1LL << 30)) return FALCON_ERR_SHAPE;
+    if (window > 8) return FALCON_ERR_UNSUPPORTED;
+    if (dk != dv || !falcon::decode_supported((int)dt, dk)) return FALCON_ERR_UNSUPPORTED;
+    if (!(eps >= 0.0f)) return FALCON_ERR_SHAPE;
+    if (!S || !k_cache || !q || !k || !v || !alpha || !eta || !o) return FALCON_ERR_NULL;
+    if (window > 1 && !v_cache) return FALCON_ERR_NULL;
+    if (!aligned16(S) || !aligned4(alpha) || !aligned4(eta)) return FALCON_ERR_UNSUPPORTED;
+    falcon::DecodeWinArgs a;
+    a.S = S;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = alpha;
+    a.eta = eta;
+    a.o = o;
+    a.NH = N * H;
+    a.W = window;
+    a.delta = var == FALCON_F3 ? 1 : 0;
+    a.eps = eps;
+    hipError_t e = falcon::launch_decode_window(a, (int)dt, dk, stream);
     return e == hipSuccess ? FALCON_OK : FALCON_ERR_HIP;
 }
 

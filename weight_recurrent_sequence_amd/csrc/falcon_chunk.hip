@@ -692,13 +692,6 @@ __device__ __forceinline__ void buf_load16_lds(rsrc_t r, void* lds, uint32_t off
 // s_waitcnt vmcnt(0), leaving the other counters alone
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Workgroup barrier that orders LDS only: global loads and stores in flight
-// are not waited for.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 template <int D, int CV, bool DELTA, bool COL, bool WIN>
 struct PassSmem {

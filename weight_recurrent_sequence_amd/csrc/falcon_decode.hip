@@ -149,3 +149,183 @@ hipError_t launch_decode(const DecodeArgs& a, int dt, int D, hipStream_t stream)
 }
 
 }  // namespace falcon
+
+namespace falcon {
+
+// ---------------------------------------------------------------------------
+// Falcon-3 / Falcon-3A decode step: a window of W prefix-aligned pairs
+// ("Fast Weight Attention for Continual Learning", authors' abstract: the
+// sliding-window mini-batch variant).  With x_w = k_{t-1-w} (k_cache slot w)
+// and y_w = v_{t-w} (y_0 = v, y_w = v_cache slot w-1):
+//     S' = alpha S,  b = eta / (sum_w ||x_w||^2 + eps)
+//     S  = S' + b sum_w r_w x_w^T,  r_w = y_w - S' x_w  (3A: r_w = y_w)
+//     o  = S q = alpha S q + b sum_w r_w (x_w . q)
+// then both caches move one slot (the new key and value enter at slot 0).
+// One workgroup per head, as in the single-pair step: the state rows and the
+// W keys' column slices sit in registers, S is read and written once.  Every
+// thread shifts only its own column of the caches, so no thread overwrites
+// a cache element another thread still has to read.
+// ---------------------------------------------------------------------------
+template <class E, int D, int W>
+__global__ __launch_bounds__(256, 2) void decode_window_kernel(DecodeWinArgs a) {
+    using T = typename E::T;
+    constexpr int LPR = D / 16;
+    constexpr int ROWS_PER_PASS = 256 / LPR;
+    constexpr int RPT = D / ROWS_PER_PASS;
+    __shared__ float ys[W][D];  // targets y_w of every row
+    const int tid = threadIdx.x;
+    const int seg = tid % LPR;
+    const int row0 = tid / LPR;
+    const size_t head = blockIdx.x;
+
+    float* S = a.S + head * D * D;
+    T* kc = static_cast<T*>(a.k_cache) + head * W * D;
+    T* vc = W > 1 ? static_cast<T*>(a.v_cache) + head * (W - 1) * D : nullptr;
+    const T* qh = static_cast<const T*>(a.q) + head * D;
+    const T* kh = static_cast<const T*>(a.k) + head * D;
+    const T* vh = static_cast<const T*>(a.v) + head * D;
+    T* oh = static_cast<T*>(a.o) + head * D;
+    const float al = a.alpha[head];
+    const float et = a.eta[head];
+
+    // ---- every read is requested first ----
+    // this thread's column of both caches and of the new key and value
+    const int col = tid < D ? tid : 0;
+    T kcol[W], vcol[W];  // kcol[w] = k_cache[w][col]; vcol[0] = v[col], vcol[w] = v_cache[w-1][col]
+#pragma unroll
+    for (int w = 0; w < W; ++w) kcol[w] = kc[(size_t)w * D + col];
+    vcol[0] = vh[col];
+#pragma unroll
+    for (int w = 1; w < W; ++w) vcol[w] = vc[(size_t)(w - 1) * D + col];
+    const T knew = kh[col];
+    // columns of this lane: 4*seg + 4*LPR*j + e, j, e in 0..3
+    float x[W][16], qv[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int c = 4 * seg + 4 * LPR * j;
+        const typename E::Frag qf = E::load(qh + c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qv[4 * j + e] = E::to_f((T)qf[e]);
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const typename E::Frag xf = E::load(kc + (size_t)w * D + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[w][4 * j + e] = E::to_f((T)xf[e]);
+        }
+    }
+    f32x4 s[RPT][4];
+#pragma unroll
+    for (int p = 0; p < RPT; ++p) {
+        const int row = row0 + ROWS_PER_PASS * p;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            s[p][j] = __builtin_nontemporal_load(
+                reinterpret_cast<const f32x4*>(S + (size_t)row * D + 4 * seg + 4 * LPR * j));
+    }
+
+    // ---- targets to LDS; window norm and x_w . q ----
+    if (tid < D) {
+#pragma unroll
+        for (int w = 0; w < W; ++w) ys[w][tid] = E::to_f(vcol[w]);
+    }
+    float n2 = 0.f, xq[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        float d = 0.f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            n2 += x[w][c] * x[w][c];
+            d += x[w][c] * qv[c];
+        }
+        xq[w] = group_sum_dpp<LPR>(d);
+    }
+    n2 = group_sum_dpp<LPR>(n2);
+    const float den = n2 + a.eps;
+    const float bw = den > 0.f ? et / den : 0.f;
+    // Every lane has consumed its cache reads (they entered the sums above)
+    // and the targets are in LDS: the caches may now move.  The barrier
+    // orders LDS only, so no load in flight is waited for.
+    lds_barrier();
+    if (tid < D) {
+#pragma unroll
+        for (int w = W - 1; w >= 1; --w) kc[(size_t)w * D + tid] = kcol[w - 1];
+        kc[tid] = knew;
+#pragma unroll
+        for (int w = W - 1; w >= 2; --w) vc[(size_t)(w - 1) * D + tid] = vcol[w - 1];
+        if (W > 1) vc[tid] = vcol[0];
+    }
+
+#pragma unroll
+    for (int p = 0; p < RPT; ++p) {
+        const int row = row0 + ROWS_PER_PASS * p;
+        float sq = 0.f, sx[W];
+#pragma unroll
+        for (int w = 0; w < W; ++w) sx[w] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float sv = s[p][j][e];
+                sq += sv * qv[4 * j + e];
+                if (a.delta) {
+#pragma unroll
+                    for (int w = 0; w < W; ++w) sx[w] += sv * x[w][4 * j + e];
+                }
+            }
+        sq = group_sum_dpp<LPR>(sq);
+        float r[W], orow = al * sq;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const float y = ys[w][row];
+            r[w] = bw * (a.delta ? y - al * group_sum_dpp<LPR>(sx[w]) : y);  // b r_w
+            orow += r[w] * xq[w];
+        }
+        if (seg == 0) oh[row] = E::from_f(orow);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f32x4 nv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float acc = al * s[p][j][e];
+#pragma unroll
+                for (int w = 0; w < W; ++w) acc += r[w] * x[w][4 * j + e];
+                nv[e] = acc;
+            }
+            __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(S + (size_t)row * D + 4 * seg + 4 * LPR * j));
+        }
+    }
+}
+
+template <class E, int D, int W>
+static hipError_t launch_decw(const DecodeWinArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_window_kernel<E, D, W>), dim3(a.NH), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <class E, int D>
+static hipError_t launch_decw_w(const DecodeWinArgs& a, hipStream_t stream) {
+    switch (a.W) {
+        case 1: return launch_decw<E, D, 1>(a, stream);
+        case 2: return launch_decw<E, D, 2>(a, stream);
+        case 3: return launch_decw<E, D, 3>(a, stream);
+        case 4: return launch_decw<E, D, 4>(a, stream);
+        case 5: return launch_decw<E, D, 5>(a, stream);
+        case 6: return launch_decw<E, D, 6>(a, stream);
+        case 7: return launch_decw<E, D, 7>(a, stream);
+        case 8: return launch_decw<E, D, 8>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode_window(const DecodeWinArgs& a, int dt, int D, hipStream_t stream) {
+    if (dt == 1) {
+        if (D == 64) return launch_decw_w<EBf16, 64>(a, stream);
+        if (D == 128) return launch_decw_w<EBf16, 128>(a, stream);
+    } else {
+        if (D == 64) return launch_decw_w<EFp32, 64>(a, stream);
+        if (D == 128) return launch_decw_w<EFp32, 128>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace falcon

@@ -114,6 +114,14 @@ struct EFp32 {
     }
 };
 
+// Workgroup barrier that orders LDS only: global loads and stores in flight
+// are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Compile-time loop: f(std::integral_constant<int, i>) for i = 0..N-1, so that
 // register arrays are only ever indexed by constants.
 template <int I, int N, class F>

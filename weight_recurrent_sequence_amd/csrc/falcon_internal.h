@@ -46,6 +46,22 @@ struct DecodeArgs {
     float eps;
 };
 
+struct DecodeWinArgs {
+    float* S;
+    void* k_cache;       // [NH, W, d]: slot w holds k_{t-1-w}
+    void* v_cache;       // [NH, W-1, d]: slot w-1 holds v_{t-w} (unused when W = 1)
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* eta;
+    void* o;
+    int NH;
+    int W;
+    int delta;   // 1: Falcon-3 (residual writes), 0: Falcon-3A
+    float eps;
+};
+
 // dt: 0 fp32, 1 bf16.  Return false when the combination is not built.
 bool chunk_supported(int dt, int D, int chunk);
 // Bytes of the per-tile records the intra-chunk kernel hands to the
@@ -55,5 +71,6 @@ hipError_t launch_chunk(const ChunkArgs& a, int dt, int D, int chunk, bool delta
                         hipStream_t stream);
 bool decode_supported(int dt, int D);
 hipError_t launch_decode(const DecodeArgs& a, int dt, int D, hipStream_t stream);
+hipError_t launch_decode_window(const DecodeWinArgs& a, int dt, int D, hipStream_t stream);
 
 }  // namespace falcon

@@ -169,8 +169,9 @@ def workload_inputs(name: str, **override) -> ChunkInputs:
 
 @dataclass
 class DecodeInputs:
-    """Decode inputs: S0 [N,H,dv,dk] float32, k_cache0 [N,H,1,dk] and per-step
-    q,k [steps,N,H,dk], v [steps,N,H,dv] (storage type), alpha, eta
+    """Decode inputs: S0 [N,H,dv,dk] float32, k_cache0 [N,H,W,dk] (newest key
+    first), v_cache0 [N,H,W-1,dv] (newest value first; empty for W = 1) and
+    per-step q,k [steps,N,H,dk], v [steps,N,H,dv] (storage type), alpha, eta
     [steps,N,H] float32."""
     dtype: str
     S0: np.ndarray
@@ -180,6 +181,7 @@ class DecodeInputs:
     v: np.ndarray
     alpha: np.ndarray
     eta: np.ndarray
+    v_cache0: np.ndarray = None
 
     def widen(self, a):
         if self.dtype == "bf16" and a.dtype == np.uint16:
@@ -188,7 +190,7 @@ class DecodeInputs:
 
 
 def make_decode_inputs(N, H, dk, dv, steps, *, dtype="bf16", seed=1005, alpha_mu=3.0,
-                       alpha_sd=1.0, S0_sd=0.02) -> DecodeInputs:
+                       alpha_sd=1.0, S0_sd=0.02, window=1) -> DecodeInputs:
     ss = np.random.SeedSequence(seed)
     cq, ck, cv, ca, ce, cs, csp, cS, ckp, cvp = ss.spawn(10)
     g = lambda c: np.random.Generator(np.random.PCG64(c))  # noqa: E731
@@ -198,9 +200,10 @@ def make_decode_inputs(N, H, dk, dv, steps, *, dtype="bf16", seed=1005, alpha_mu
     alpha = sigmoid32(g(ca).normal(alpha_mu, alpha_sd, (steps, N, H)).astype(np.float32))
     eta = sigmoid32(g(ce).normal(0.0, 1.0, (steps, N, H)).astype(np.float32))
     S0 = (g(cS).standard_normal((N, H, dv, dk), dtype=np.float32) * np.float32(S0_sd))
-    kc = g(ckp).standard_normal((N, H, 1, dk), dtype=np.float32)
+    kc = g(ckp).standard_normal((N, H, window, dk), dtype=np.float32)
+    vc = g(cvp).standard_normal((N, H, window - 1, dv), dtype=np.float32)
     return DecodeInputs(dtype, S0.astype(np.float32), _store(kc, dtype), _store(q, dtype),
-                        _store(k, dtype), _store(v, dtype), alpha, eta)
+                        _store(k, dtype), _store(v, dtype), alpha, eta, _store(vc, dtype))
 
 
 def make_decode_inputs_torch(N, H, dk, dv, steps, *, device, seed=1005, alpha_mu=3.0,
