@@ -8,9 +8,10 @@ resident in HBM: the intra-chunk kernel (norms, decay scan, masked Gram
 blocks, diagonal-block inverses) and the state-passing kernel (residuals,
 blocked forward substitution, outputs, state update).  `value` is tokens
 (B*T) per second.  The same line reports Falcon-1A on the same batch and the
-decode step (256 sequences x 32 heads, d=128, 1024 consecutive steps), each
-with its roofline, and the fp64 CPU oracle timed on this host over a bounded
-sample of the Falcon-1 workload.
+decode step (256 sequences x 32 heads, d=128, 1024 consecutive steps) and the
+Falcon-3 decode step at the same shape with a window of four, each with its
+roofline, and the fp64 CPU oracle timed on this host over a bounded sample of
+the Falcon-1 workload.
 
 roofline.achieved is the algorithmic HBM bytes of one call (q, k, v, o once,
 alpha, eta, final state) over the call's HIP-event time on the launch
@@ -55,6 +56,14 @@ def decode_bytes(N, H, D, elem=2):
     """Per step: state read + write (fp32), q, k, v, the key cache read and
     rewritten, alpha, eta, and o."""
     return N * H * (2 * D * D * 4 + 3 * D * elem + 2 * D * elem + 2 * 4 + D * elem)
+
+
+def decode_window_bytes(N, H, D, W, elem=2):
+    """Per Falcon-3 step: state read + write (fp32), q, k, v, o, the key cache
+    (W slots) and the value cache (W - 1 slots) each read and rewritten,
+    alpha, eta."""
+    return N * H * (2 * D * D * 4 + 4 * D * elem + 2 * W * D * elem + 2 * (W - 1) * D * elem
+                    + 2 * 4)
 
 
 def measured_traffic(entry):
@@ -233,6 +242,42 @@ def main():
                               "traffic": measured_traffic("decode_F1_N256H32d128_bf16"),
                               "algorithmic_bytes_per_launch": db,
                               "kernel": "decode_step_kernel<EBf16,128>"}}
+        del x
+
+        wn = "decode_falcon3_w4_N256H32d128_1024steps"
+        w3 = I.WORKLOADS[wn]
+        N, Hd, Dd, Wd = w3["N"], w3["H"], w3["d"], w3["window"]
+        x = I.make_decode_inputs_torch(N, Hd, Dd, Dd, steps, device=dev, seed=w3["seed"],
+                                       window=Wd)
+        S = x["S0"].clone()
+        kc = x["k_cache0"].clone()
+        vc = x["v_cache0"].clone()
+
+        def dec3():
+            s = counter[0] % steps
+            counter[0] += 1
+            fal.decode_step_window(S, kc, vc, x["q"][s], x["k"][s], x["v"][s], x["alpha"][s],
+                                   x["eta"][s], "F3", o=od)
+
+        print(f"[bench] decode F3 window {Wd}, {steps} steps", file=sys.stderr, flush=True)
+        best = None
+        for rep in range(3):
+            S.copy_(x["S0"])
+            kc.copy_(x["k_cache0"])
+            vc.copy_(x["v_cache0"])
+            counter[0] = 0
+            torch.cuda.synchronize()
+            ms_d, _ = timed(dec3, steps, 0)
+            best = ms_d if best is None else min(best, ms_d)
+        db = decode_window_bytes(N, Hd, Dd, Wd)
+        dgbs = db / (best / 1e3) / 1e9
+        line["decode_falcon3"] = {"workload": wn, "tokens_per_s": N / (best / 1e3),
+                                  "ms_per_step": best, "steps": steps, "roofline": {
+                                      "bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS,
+                                      "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
+                                      "traffic": measured_traffic("decode_F3W4_N256H32d128_bf16"),
+                                      "algorithmic_bytes_per_launch": db,
+                                      "kernel": "decode_window_kernel<EBf16,128,4>"}}
         del x
 
     if args.copy_calibration:

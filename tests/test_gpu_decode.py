@@ -153,3 +153,44 @@ def test_decode_window_continues_a_chunk_call(dev):
         torch.cuda.synchronize()
         assert slice_rel_err(to_np(o), to_np(o_all[:, :, s]), (2,)) <= 1e-4
     assert slice_rel_err(to_np(S), to_np(S_all), (2, 3)) <= 1e-4
+
+
+@pytest.mark.parametrize("variant", ["F3", "F3A"])
+def test_decode_window_full_workload_sampled(dev, variant):
+    """256 sequences x 32 heads, d = 128, window 4, 1024 consecutive steps in
+    the benchmark's launch configuration; the oracle follows a sample of heads
+    through every step, caches included."""
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    w = I.WORKLOADS["decode_falcon3_w4_N256H32d128_1024steps"]
+    N, H, D, W, steps = w["N"], w["H"], w["d"], w["window"], w["steps"]
+    x = I.make_decode_inputs_torch(N, H, D, D, steps, device=dev, seed=w["seed"], window=W)
+    sample = [(0, 0), (77, 9), (200, 31), (255, 30)]
+    ns = torch.tensor([n for n, _ in sample], device=dev)
+    hs = torch.tensor([h for _, h in sample], device=dev)
+    S, kc, vc = x["S0"].clone(), x["k_cache0"].clone(), x["v_cache0"].clone()
+    outs = torch.empty(steps, len(sample), D, dtype=torch.bfloat16, device=dev)
+    announce(f"decode_step_window {variant} W{W} bf16 N{N} H{H} d{D}, {steps} steps")
+    for s in range(steps):
+        o = fal.decode_step_window(S, kc, vc, x["q"][s], x["k"][s], x["v"][s], x["alpha"][s],
+                                   x["eta"][s], variant)
+        outs[s] = o[ns, hs]
+    torch.cuda.synchronize()
+    assert torch.isfinite(S).all()
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    S_o = f64(x["S0"][ns, hs])[None]
+    kc_o = f64(x["k_cache0"][ns, hs])[None]
+    vc_o = f64(x["v_cache0"][ns, hs])[None]
+    o_ref = np.empty((steps, len(sample), D))
+    for s in range(steps):
+        o1, S_o, kc_o, vc_o = oracle.decode_step_window(
+            variant, S_o, kc_o, vc_o, f64(x["q"][s][ns, hs])[None], f64(x["k"][s][ns, hs])[None],
+            f64(x["v"][s][ns, hs])[None], f64(x["alpha"][s][ns, hs])[None],
+            f64(x["eta"][s][ns, hs])[None])
+        o_ref[s] = o1[0]
+    e_o = slice_rel_err(np.moveaxis(to_np(outs), 0, 1), np.moveaxis(o_ref, 0, 1), (1, 2))
+    e_S = slice_rel_err(to_np(S[ns, hs]), S_o[0], (1, 2))
+    announce(f"decode window full workload {variant}: max rel err o={e_o:.2e} S={e_S:.2e}")
+    assert e_o <= TOL["bf16"] and e_S <= TOL["bf16"], (e_o, e_S)
+    np.testing.assert_array_equal(f64(kc[ns, hs]), kc_o[0])
+    np.testing.assert_array_equal(f64(vc[ns, hs]), vc_o[0])

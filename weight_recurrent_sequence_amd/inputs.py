@@ -138,7 +138,8 @@ def make_chunk_inputs(B, H, T, dk, dv, *, dtype="bf16", seed=0, alpha_mu=3.0, al
                        window, S0, k_prev, v_prev, meta)
 
 
-# The five workloads, by what they are.  `seed` is SeedSequence(1000 + i).
+# The workloads, by what they are.  `seed` is SeedSequence(1000 + i); the last is the
+# windowed (Falcon-3) decode step at the same serving shape as the Falcon-1 one.
 WORKLOADS = {
     "falcon1_fp32_B1H1T256d64": dict(variant="F1", B=1, H=1, T=256, d=64, dtype="fp32",
                                      chunk=32, alpha_mu=2.0, alpha_sd=0.5, seed=1001),
@@ -153,6 +154,11 @@ WORKLOADS = {
     "decode_falcon1_N256H32d128_1024steps": dict(variant="F1", N=256, H=32, d=128, steps=1024,
                                                  dtype="bf16", alpha_mu=3.0, alpha_sd=1.0,
                                                  S0_sd=0.02, seed=1005),
+    # the Falcon-3 decode step at the same serving shape, window of four
+    "decode_falcon3_w4_N256H32d128_1024steps": dict(variant="F3", N=256, H=32, d=128,
+                                                    steps=1024, window=4, dtype="bf16",
+                                                    alpha_mu=3.0, alpha_sd=1.0, S0_sd=0.02,
+                                                    seed=1006),
 }
 
 
@@ -207,10 +213,12 @@ def make_decode_inputs(N, H, dk, dv, steps, *, dtype="bf16", seed=1005, alpha_mu
 
 
 def make_decode_inputs_torch(N, H, dk, dv, steps, *, device, seed=1005, alpha_mu=3.0,
-                             alpha_sd=1.0, S0_sd=0.02):
+                             alpha_sd=1.0, S0_sd=0.02, window=1):
     """Same distributions drawn on the device with torch's seeded generator,
     for workloads too large to draw on the host (the oracle then receives
-    host copies of the sampled heads).  Returns a dict of bf16/fp32 tensors."""
+    host copies of the sampled heads).  Returns a dict of bf16/fp32 tensors;
+    the value cache (window - 1 slots) is drawn last, so a window of one
+    draws exactly what it did before windows existed."""
     import torch
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
@@ -219,10 +227,11 @@ def make_decode_inputs_torch(N, H, dk, dv, steps, *, device, seed=1005, alpha_mu
         return torch.randn(*shape, generator=gen, device=device, dtype=torch.float32)
     out = {}
     out["S0"] = n(N, H, dv, dk) * S0_sd
-    out["k_cache0"] = n(N, H, 1, dk).to(torch.bfloat16)
+    out["k_cache0"] = n(N, H, window, dk).to(torch.bfloat16)
     out["q"] = n(steps, N, H, dk).to(torch.bfloat16)
     out["k"] = n(steps, N, H, dk).to(torch.bfloat16)
     out["v"] = n(steps, N, H, dv).to(torch.bfloat16)
     out["alpha"] = torch.sigmoid(n(steps, N, H) * alpha_sd + alpha_mu)
     out["eta"] = torch.sigmoid(n(steps, N, H))
+    out["v_cache0"] = n(N, H, window - 1, dv).to(torch.bfloat16)
     return out
