@@ -651,21 +651,28 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs a, const void
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 2, bf16 form: the state pass split into a chain half and an output
-// half of one workgroup (8 waves, two per SIMD).
+// Kernel 2, bf16 form: the state pass, one workgroup per (batch*head, 64-wide
+// value slice), its waves in three roles.
 //
-//   waves 0-3 (chain)  tile `it`: S0 -> bf16 copy in LDS, Z = X S0^T,
-//                      residuals, forward substitution -> Delta (bf16 copy in
-//                      LDS), state update.  Everything the next tile needs
-//                      is in registers or LDS; no global memory traffic.
-//   waves 4-7 (output) tile `it - 1`: O^T = diag(gq) (S0 Q^T) + Delta^T P^T
-//                      from the two LDS copies, stored straight from the
-//                      accumulators (each lane owns four adjacent columns of
-//                      one row); then stage tile it+1 from registers into LDS
-//                      and issue the global loads of tile it+2.
-// One barrier per tile, fencing LDS only, so the loads in flight stay in
-// flight.  Loads use buffer descriptors: out-of-range rows read as zero in
-// hardware, and a lane's offsets stay fixed from tile to tile.
+//   waves 0-3  (chain)  tile `it`: S0 -> bf16 copy in LDS, Z = X S0^T,
+//                       residuals, forward substitution -> Delta (bf16 copy
+//                       in LDS), state update.  No global memory traffic.
+//   waves 4-7  (output) tile `it - 1`: O^T = diag(gq) (S0 Q^T) + Delta^T P^T
+//                       from the two LDS copies, stored straight from the
+//                       accumulators (each lane owns four adjacent columns of
+//                       one row).
+//   waves 8-11 (fill)   the fills of tile it+1's keys, targets and chain
+//                       record and tile it's queries and output record:
+//                       direct to LDS for the delta family, through registers
+//                       one iteration ahead for the A family.  A wave that
+//                       issues a tile's worth of fills stalls on a full
+//                       memory queue for thousands of cycles; here no
+//                       computing wave does.
+// The per-column rule stages through registers instead (its write vectors
+// are derived on the way) and runs without fill waves.  One barrier per
+// tile, fencing LDS only.  Loads use buffer descriptors: out-of-range rows
+// read as zero in hardware, and a lane's offsets stay fixed from tile to
+// tile.
 // ---------------------------------------------------------------------------
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRawBufferFlags = 0x00020000;  // descriptor word 3 of a raw gfx9 buffer
@@ -682,12 +689,35 @@ __device__ __forceinline__ s16x4 buf_load8(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(s16x4, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
 }
 
+// Descriptor words of a raw buffer (base, stride 0, size in bytes, flags),
+// wave-uniform, for the direct-to-LDS fill below.
+__device__ __forceinline__ u32x4 make_desc(const void* base, int64_t bytes) {
+    const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0x7FFFFFF0 ? 0x7FFFFFF0u : (uint32_t)bytes);
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    u32x4 d;
+    d[0] = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    d[1] = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xFFFFu);
+    d[2] = __builtin_amdgcn_readfirstlane(n);
+    d[3] = (uint32_t)kRawBufferFlags;
+    return d;
+}
 // 16 bytes per lane from a buffer straight into LDS: lane l writes
 // lds + 16 l (lds is wave-uniform); lanes whose exec bit is off write nothing,
-// out-of-range offsets write zeros.  Completion is counted by vmcnt.
-__device__ __forceinline__ void buf_load16_lds(rsrc_t r, void* lds, uint32_t off) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
-                                             off, 0, 0, 0);
+// out-of-range offsets write zeros.  Completion is counted by vmcnt and the
+// caller waits for it (wait_vm_all) before the barrier that publishes the
+// tile.  The instruction is issued from inline assembly on purpose: the
+// compiler cannot tell which LDS bytes such a fill writes, and for the
+// builtin form it waits for every fill in flight before the wave's next LDS
+// read, which would serialize each fill's latency with the arithmetic it is
+// meant to overlap.  The asm has no outputs; the fills' targets are read only
+// after the explicit wait and a barrier.
+// `lds` is the wave's LDS byte address (it goes to M0).
+__device__ __forceinline__ void buf_load16_lds(u32x4 d, uint32_t lds, uint32_t off) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(off), "s"(d), "{m0}"(m0)
+                 : "memory");
 }
 // s_waitcnt vmcnt(0), leaving the other counters alone
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -712,7 +742,8 @@ struct PassSmem {
 };
 
 template <int D, int CV, bool DELTA, bool COL, bool WIN>
-__global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void* ws, int ntiles) {
+__global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a, const void* ws,
+                                                                     int ntiles) {
     using E = EBf16;
     using T = uint16_t;
     using Frag = s16x4;
@@ -732,6 +763,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4,
               lr = lane & 15;
     const bool chain = wave < 4;
+    const bool filler = !COL && wave >= 8;
     const int cw = wave & 3;  // value-column block (16 columns) of this wave
     const int blk = blockIdx.x;
     const int xcd = blk & 7;
@@ -768,7 +800,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
                                    : zero4();
 
     // ---- output: staging geometry, fixed across tiles ----
-    const int otid = tid - 256;
+    const int otid = tid & 255;  // index within the output or fill role
     // Each 16-byte piece a stager moves: its row relative to the tile start
     // (key x_i = k_{t0 + s - w - 1}, target y_i = v_{t0 + s - w}), its byte
     // column, and whether it exists.  Loads choose addresses, never data:
@@ -877,6 +909,13 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
             ppg[it] = *reinterpret_cast<const u32x4*>(
                 rt + (pc < PFC ? R::kP * 2 + (size_t)pc * 16
                                : R::kScalBytes + 2 * CV * 4 + (size_t)(pc - PFC) * 16));
+        }
+    };
+    auto store_q = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+        for (int it = 0; it < NXL; ++it) {
+            const int c = otid + 256 * it;
+            if (c < CV * CPR) *reinterpret_cast<u32x4*>(&sm.QU[b][c / CPR][(c % CPR) * 8]) = pq[it];
         }
     };
     auto store_pg = [&](int b) __attribute__((always_inline)) {
@@ -1113,7 +1152,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
     constexpr int NIR = (RCH + 63) / 64, NIP = (PCH + 63) / 64;
     constexpr int MIX = (NIX + 3) / 4, MIY = (NIY + 3) / 4, MIR = (NIR + 3) / 4, MIP = (NIP + 3) / 4;
     uint32_t dx[MIX], dq[MIX], dy[MIY], dr[MIR], dp[MIP];
-    const int ow = cw;  // index of this wave within its half
+    const int ow = cw;  // index of this wave within its role
     if constexpr (!COL) {
 #pragma unroll
         for (int m = 0; m < MIX; ++m) {
@@ -1144,15 +1183,21 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
                             : kOob;
         }
     }
-    // Fills of one tile, each spread over the four waves of the calling half.
-    // Keys and the chain's record pieces (output half) and targets (chain
-    // half) of a tile with t0 >= W go to buffer tile & 1, as do queries and
-    // the output half's record pieces (chain half).
+    // Fills of one tile, each spread over the four fill waves: keys, targets
+    // and the chain's record pieces of a tile with t0 >= W go to buffer
+    // tile & 1, as do its queries and the output waves' record pieces.
+    // LDS byte addresses of the filled buffers (the workgroup's one LDS
+    // object starts at sm_lds)
+    const uint32_t sm_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) Smem*)&sm;
+    auto lds_of = [&](size_t field, size_t bytes_per_buffer, int b) __attribute__((always_inline)) {
+        return sm_lds + (uint32_t)(field + bytes_per_buffer * b);
+    };
     auto dma_xr = [&](int tile) __attribute__((always_inline)) {
         const int t0 = tile * Ct, b = tile & 1;
-        const rsrc_t rx = make_rsrc(kg + (size_t)(t0 - W) * D, (int64_t)(T_ - t0 + W) * D * 2);
-        const rsrc_t rr = make_rsrc(recg + (size_t)tile * R::kBytes, R::kBytes);
-        char* xb = reinterpret_cast<char*>(&sm.X[b][0][0]);
+        const u32x4 rx = make_desc(kg + (size_t)(t0 - W) * D, (int64_t)(T_ - t0 + W) * D * 2);
+        const u32x4 rr = make_desc(recg + (size_t)tile * R::kBytes, R::kBytes);
+        const uint32_t xb = lds_of(offsetof(Smem, X), sizeof(sm.X[0]), b);
+        const uint32_t rb = lds_of(offsetof(Smem, rec), sizeof(sm.rec[0]), b);
 #pragma unroll
         for (int m = 0; m < MIX; ++m) {
             const int i = ow + 4 * m;
@@ -1161,13 +1206,13 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
 #pragma unroll
         for (int m = 0; m < MIR; ++m) {
             const int i = ow + 4 * m;
-            if (i < NIR && 64 * i + lane < RCH) buf_load16_lds(rr, sm.rec[b] + 1024 * i, dr[m]);
+            if (i < NIR && 64 * i + lane < RCH) buf_load16_lds(rr, rb + 1024 * i, dr[m]);
         }
     };
     auto dma_y = [&](int tile) __attribute__((always_inline)) {
         const int t0 = tile * Ct, b = tile & 1;
-        const rsrc_t ry = make_rsrc(vg + (size_t)(t0 - W + 1) * D, (int64_t)(T_ - t0 + W - 1) * D * 2);
-        char* yb = reinterpret_cast<char*>(&sm.Y[b][0][0]);
+        const u32x4 ry = make_desc(vg + (size_t)(t0 - W + 1) * D, (int64_t)(T_ - t0 + W - 1) * D * 2);
+        const uint32_t yb = lds_of(offsetof(Smem, Y), sizeof(sm.Y[0]), b);
 #pragma unroll
         for (int m = 0; m < MIY; ++m) {
             const int i = ow + 4 * m;
@@ -1176,9 +1221,10 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
     };
     auto dma_qp = [&](int tile) __attribute__((always_inline)) {
         const int t0 = tile * Ct, b = tile & 1;
-        const rsrc_t rq = make_rsrc(qg + (size_t)t0 * D, (int64_t)(T_ - t0) * D * 2);
-        const rsrc_t rr = make_rsrc(recg + (size_t)tile * R::kBytes, R::kBytes);
-        char* qb = reinterpret_cast<char*>(&sm.QU[b][0][0]);
+        const u32x4 rq = make_desc(qg + (size_t)t0 * D, (int64_t)(T_ - t0) * D * 2);
+        const u32x4 rr = make_desc(recg + (size_t)tile * R::kBytes, R::kBytes);
+        const uint32_t qb = lds_of(offsetof(Smem, QU), sizeof(sm.QU[0]), b);
+        const uint32_t pb = lds_of(offsetof(Smem, pg), sizeof(sm.pg[0]), b);
 #pragma unroll
         for (int m = 0; m < MIX; ++m) {
             const int i = ow + 4 * m;
@@ -1187,7 +1233,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
 #pragma unroll
         for (int m = 0; m < MIP; ++m) {
             const int i = ow + 4 * m;
-            if (i < NIP && 64 * i + lane < PCH) buf_load16_lds(rr, sm.pg[b] + 1024 * i, dp[m]);
+            if (i < NIP && 64 * i + lane < PCH) buf_load16_lds(rr, pb + 1024 * i, dp[m]);
         }
     };
 
@@ -1218,39 +1264,83 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(ChunkArgs a, const void
     } else {
         // Iteration it.  Output half: store the outputs of tile it-2, start
         // the fills of tile it+1's keys and chain record, compute tile it-1.
-        // Chain half: tile it, then start the fills of tile it+1's targets
-        // and tile it's queries and output record (its wait at the barrier
-        // absorbs them).  Both halves wait for their fills before the
-        // barrier.  Tiles that still reach back before the sequence (t0 < W)
+        // Chain half: start the fills of tile it+1's targets and tile it's
+        // queries and output record, then compute tile it.  Both halves wait
+        // for their fills before the barrier, so the fills' latency overlaps
+        // the arithmetic.  Tiles that still reach back before the sequence (t0 < W)
         // are staged by the output half through registers, halo included.
-        if (!chain && ntl > 0) {
+        // Each role runs its own loop with the same number of barriers, so
+        // the compiler's wait bookkeeping for one role's memory operations
+        // never reaches another role's code.  Iteration it: the chain works on
+        // tile it, the output waves store tile it-2 and compute tile it-1, the
+        // fill waves bring in tile it+1's keys, targets and chain record and
+        // tile it's queries and output record.  Every buffer a fill writes
+        // was last read in the previous iteration.  Tiles that still reach
+        // back before the sequence (t0 < W) are staged by the output waves
+        // through registers, halo included.
+        const bool out = !chain && !filler;
+        if (out && ntl > 0) {
             load_xyr(0);
             store_xyr(0);
         }
+        // the state's initial loads (chain) are complete before the loops, so
+        // no wait inside them is owed to a load issued out here
+        if (!filler) wait_vm_all();
         lds_barrier();
-        for (int it = 0; it <= ntl; ++it) {
-            const bool next_fast = it + 1 < ntl && (it + 1) * Ct >= W;
-            if (chain) {
-                if (it < ntl) {
-                    chain_tile(it);
-                    if (next_fast) dma_y(it + 1);
-                    dma_qp(it);
-                    wait_vm_all();
-                }
-            } else {
-                if (it >= 2) store_o(it - 2);
-                if (next_fast) {
+        if (chain) {
+            for (int it = 0; it <= ntl; ++it) {
+                if (it < ntl) chain_tile(it);
+                lds_barrier();
+            }
+        } else if (filler && DELTA) {
+            // Delta family: direct-to-LDS fills, issued after the barrier and
+            // waited for before the next one.  Its chain and output waves keep
+            // LDS busy, and these fills cost no LDS instruction of their own.
+            for (int it = 0; it <= ntl; ++it) {
+                if (it + 1 < ntl && (it + 1) * Ct >= W) {
                     dma_xr(it + 1);
-                } else if (it + 1 < ntl) {
+                    dma_y(it + 1);
+                }
+                if (it < ntl) dma_qp(it);
+                wait_vm_all();
+                lds_barrier();
+            }
+        } else if (filler) {
+            // A family (lighter on LDS): loads run one iteration ahead of their
+            // LDS stores through registers, so each has a whole iteration to
+            // arrive: the registers hold tile it+1's keys, targets and chain
+            // record and tile it's queries and output record while iteration
+            // it-1 runs.
+            if (1 < ntl && Ct >= W) load_xyr(1);
+            if (ntl > 0) {
+                load_q(0);
+                load_pg(0);
+            }
+            for (int it = 0; it <= ntl; ++it) {
+                if (it + 1 < ntl && (it + 1) * Ct >= W) store_xyr(it + 1);
+                if (it < ntl) {
+                    store_q(it & 1);
+                    store_pg(it & 1);
+                }
+                if (it + 2 < ntl && (it + 2) * Ct >= W) load_xyr(it + 2);
+                if (it + 1 < ntl) {
+                    load_q(it + 1);
+                    load_pg(it + 1);
+                }
+                lds_barrier();
+            }
+        } else {
+            for (int it = 0; it <= ntl; ++it) {
+                if (it >= 2) store_o(it - 2);
+                if (it + 1 < ntl && (it + 1) * Ct < W) {
                     load_xyr(it + 1);
                     store_xyr(it + 1);
                 }
                 if (it >= 1) output_tile(it - 1);
-                wait_vm_all();
+                lds_barrier();
             }
-            lds_barrier();
+            if (ntl >= 1) store_o(ntl - 1);
         }
-        if (!chain && ntl >= 1) store_o(ntl - 1);
     }
 
     if (chain && a.S_final) {
@@ -1715,7 +1805,7 @@ static hipError_t launch_one(const ChunkArgs& a, void* ws, hipStream_t stream) {
     const int nvs = D / 64;
     const int bh8 = (a.BH + 7) / 8 * 8;
     if constexpr (E::kBytes == 2)
-        hipLaunchKernelGGL((chunk_pass_kernel<D, CV, DELTA, COL, WIN>), dim3(bh8 * nvs), dim3(512),
+        hipLaunchKernelGGL((chunk_pass_kernel<D, CV, DELTA, COL, WIN>), dim3(bh8 * nvs), dim3(COL ? 512 : 768),
                            0, stream, a, (const void*)ws, ntiles);
     else
         hipLaunchKernelGGL((chunk_scan_kernel<E, D, CV, DELTA, COL, WIN>), dim3(bh8 * nvs),
