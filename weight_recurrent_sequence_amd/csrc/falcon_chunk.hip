@@ -1357,8 +1357,10 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
 // tile's keys, queries and gates in registers while it works on the current
 // one, so the loads of one tile overlap the arithmetic of the previous.
 // Per tile: norms, the log-decay scan, the Gram blocks (A: x_i . omega_j,
-// P: q_t . omega_j) shared round-robin over the four waves, masks and decays
-// from per-row and per-column factors, then the 16 x 16 diagonal inverses.
+// P: q_t . omega_j; without a window each wave owns one row block of each and
+// reads each column block's operand once for both, with a window the blocks
+// go round-robin over the waves), masks and decays from per-row and
+// per-column factors, then the 16 x 16 diagonal inverses.
 // Blocks of P that the state pass never reads are not written.
 // ---------------------------------------------------------------------------
 template <int D, int CV, bool COL>
@@ -1378,8 +1380,14 @@ struct Prep2Smem {
     alignas(16) int step[CV];      // step of virtual row i
 };
 
+// Occupancy: three workgroups per compute unit for the A family; two for the
+// delta family, whose Gram rows, inverse and prefetch registers would spill
+// at three.
+template <bool DELTA>
+constexpr int kPrepPerCu = DELTA ? 2 : 3;
+
 template <int D, int CV, bool DELTA, bool COL, bool WIN>
-__global__ __launch_bounds__(256, 3) void chunk_prep2_kernel(ChunkArgs a, void* ws, int ntiles,
+__global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(ChunkArgs a, void* ws, int ntiles,
                                                              int njobs) {
     using E = EBf16;
     using T = uint16_t;
@@ -1735,30 +1743,46 @@ __global__ __launch_bounds__(256, 3) void chunk_prep2_kernel(ChunkArgs a, void* 
         }
         if constexpr (DELTA) {
             lds_barrier();
-            // ---- (I + A_bb)^-1 by forward substitution, one column per lane;
-            // wave b owns block b from here on, so no further barrier ----
+            // ---- (I + A_bb)^-1 by forward substitution, t_i = delta_ic -
+            // sum_{j<i} A_ij t_j for each column c.  Lane 4c + p works on column c
+            // and the terms 4p <= j < 4p + 4 of every row's sum; the four partial
+            // sums of a row meet in one DPP reduction within the lane quad.  The
+            // masked block holds zeros on and above its diagonal, so every lane
+            // runs the same unmasked loop.  Wave b owns block b from here on, so
+            // no further barrier ----
             if (wave < NB) {
                 const int bb = wave;
-                if (lane < 16) {
-                    const int c = lane;
-                    float tcol[16];
+                const int c = lane >> 2, p = lane & 3;
+                float tp[4] = {0.f, 0.f, 0.f, 0.f};  // tp[u] = t_{4p+u} of column c
+                // rows four at a time, the next four read while these are used
+                f32x4 cur[4], nxt[4];
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        // t_i = delta_ic - sum_{j<i} A_ij t_j, as four independent chains
-                        float part[4] = {(i == c) ? 1.f : 0.f, 0.f, 0.f, 0.f};
+                for (int r = 0; r < 4; ++r) cur[r] = *reinterpret_cast<const f32x4*>(&sm.Adg[bb][r][4 * p]);
 #pragma unroll
-                        for (int j4 = 0; j4 < i; j4 += 4) {
-                            const f32x4 arow = *reinterpret_cast<const f32x4*>(&sm.Adg[bb][i][j4]);
+                for (int q = 0; q < 4; ++q) {
+                    if (q < 3) {
 #pragma unroll
-                            for (int u = 0; u < 4; ++u)
-                                if (j4 + u < i) part[u] -= arow[u] * tcol[j4 + u];
-                        }
-                        tcol[i] = (part[0] + part[1]) + (part[2] + part[3]);
+                        for (int r = 0; r < 4; ++r)
+                            nxt[r] = *reinterpret_cast<const f32x4*>(&sm.Adg[bb][4 * q + 4 + r][4 * p]);
                     }
-                    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) sm.Adg[bb][i][c] = tcol[i];
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 4 * q + r;
+                        float s = 0.f;
+                        if (i > 0) {
+                            const f32x4 a = cur[r];
+                            s = (a[0] * tp[0] + a[1] * tp[1]) + (a[2] * tp[2] + a[3] * tp[3]);
+                            s = group_sum_dpp<4>(s);
+                        }
+                        const float ti = ((i == c) ? 1.f : 0.f) - s;
+                        if (p == q) tp[r] = ti;
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) cur[r] = nxt[r];
                 }
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int u = 0; u < 4; ++u) sm.Adg[bb][4 * p + u][c] = tp[u];
                 __builtin_amdgcn_wave_barrier();
                 f32x4 tv;
 #pragma unroll
@@ -1783,9 +1807,11 @@ static hipError_t launch_one(const ChunkArgs& a, void* ws, hipStream_t stream) {
     if (ntiles > 0) {
         if constexpr (E::kBytes == 2) {
             // persistent grid: as many workgroups as fit on the device at once
-            // (LDS allows floor(160 KiB / footprint) per compute unit, at most 3)
+            // (LDS allows floor(160 KiB / footprint) per compute unit, at most
+            // the kernel's occupancy target)
             constexpr int per_cu_lds = (int)(163840 / sizeof(Prep2Smem<D, CV, COL>));
-            constexpr int per_cu = per_cu_lds < 1 ? 1 : (per_cu_lds > 3 ? 3 : per_cu_lds);
+            constexpr int per_cu = per_cu_lds < 1 ? 1
+                                                  : (per_cu_lds > kPrepPerCu<DELTA> ? kPrepPerCu<DELTA> : per_cu_lds);
             int dev = 0, cus = 0;
             if (hipGetDevice(&dev) != hipSuccess ||
                 hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
