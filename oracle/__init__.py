@@ -10,6 +10,9 @@ recurrent(...)    the step-by-step form, in plain C (falcon_oracle.c), threads
                   over the independent (batch, head) sequences.
 decode_step(...)  one step of the same recurrence for N x H heads.
 decode_step_window(...)  the same for Falcon-3/3A, with key and value caches.
+Every entry takes align="prefix" (the pair of step t is (k_{t-1}, v_t), the
+authors' alignment) or align="same" (k_t, v_t: the same-step alignment of the
+KLA/GDN recurrences the pages contrast it with).
 forms             numpy fp64 masked-parallel and chunk-parallel forms, used only
                   to cross-check the recurrent form (the authors' abstract of
                   "Fast Weight Attention for Continual Learning" states that the
@@ -31,6 +34,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 F1, F2, F3, F1A, F2A, F3A = 1, 2, 3, 11, 12, 13
 VARIANTS = {"F1": F1, "F2": F2, "F3": F3, "F1A": F1A, "F2A": F2A, "F3A": F3A}
+ALIGN_LAG = {"prefix": 1, "same": 0}
 
 _lib = None
 
@@ -52,12 +56,12 @@ def _load():
         build()
         lib = ctypes.CDLL(LIB)
         dp = ctypes.POINTER(ctypes.c_double)
-        lib.oracle_recurrent.restype = ctypes.c_int
-        lib.oracle_recurrent.argtypes = [ctypes.c_int] * 7 + [ctypes.c_double] + [dp] * 10 + [ctypes.c_int]
-        lib.oracle_decode_step.restype = ctypes.c_int
-        lib.oracle_decode_step.argtypes = [ctypes.c_int] * 5 + [ctypes.c_double] + [dp] * 8
-        lib.oracle_decode_step_window.restype = ctypes.c_int
-        lib.oracle_decode_step_window.argtypes = [ctypes.c_int] * 6 + [ctypes.c_double] + [dp] * 9
+        lib.oracle_recurrent_lag.restype = ctypes.c_int
+        lib.oracle_recurrent_lag.argtypes = [ctypes.c_int] * 8 + [ctypes.c_double] + [dp] * 10 + [ctypes.c_int]
+        lib.oracle_decode_step_lag.restype = ctypes.c_int
+        lib.oracle_decode_step_lag.argtypes = [ctypes.c_int] * 6 + [ctypes.c_double] + [dp] * 8
+        lib.oracle_decode_step_window_lag.restype = ctypes.c_int
+        lib.oracle_decode_step_window_lag.argtypes = [ctypes.c_int] * 7 + [ctypes.c_double] + [dp] * 9
         lib.oracle_num_cpus.restype = ctypes.c_int
         lib.oracle_num_cpus.argtypes = []
         _lib = lib
@@ -81,12 +85,15 @@ def _ptr(a):
 
 
 def recurrent(variant, q, k, v, alpha, eta, *, window=1, eps=1e-6, S0=None, k_prev=None,
-              v_prev=None, nthreads=0):
-    """Run the recurrence.  q, k: [B,H,T,dk]; v: [B,H,T,dv]; alpha, eta: [B,H,T].
+              v_prev=None, nthreads=0, align="prefix"):
+    """Run the recurrence.  q, k: [B,H,T,dk]; v: [B,H,T,dv]; alpha, eta: [B,H,T];
+    k_prev holds the W keys before the sequence (oldest first) in either
+    alignment.
 
     Returns (o [B,H,T,dv], S_T [B,H,dv,dk]) in float64.
     """
     variant = VARIANTS.get(variant, variant)
+    lag = ALIGN_LAG[align]
     q, k, v, alpha, eta = map(_f64, (q, k, v, alpha, eta))
     S0, k_prev, v_prev = map(_f64, (S0, k_prev, v_prev))
     B, H, T, dk = k.shape
@@ -101,9 +108,9 @@ def recurrent(variant, q, k, v, alpha, eta, *, window=1, eps=1e-6, S0=None, k_pr
         assert v_prev.shape == (B, H, window - 1, dv)
     o = np.zeros((B, H, T, dv), np.float64)
     S = np.zeros((B, H, dv, dk), np.float64)
-    rc = _load().oracle_recurrent(variant, B, H, T, dk, dv, window, float(eps), _ptr(q), _ptr(k),
-                                  _ptr(v), _ptr(alpha), _ptr(eta), _ptr(S0), _ptr(k_prev),
-                                  _ptr(v_prev), _ptr(o), _ptr(S), int(nthreads))
+    rc = _load().oracle_recurrent_lag(variant, B, H, T, dk, dv, window, lag, float(eps), _ptr(q),
+                                      _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(S0),
+                                      _ptr(k_prev), _ptr(v_prev), _ptr(o), _ptr(S), int(nthreads))
     if rc < 0:
         raise ValueError(f"oracle_recurrent rejected its arguments (code {rc})")
     return o, S
@@ -114,30 +121,34 @@ def recurrent_threads_used(B, H, nthreads=0):
     return min(n, B * H)
 
 
-def decode_step(variant, S, k_cache, q, k, v, alpha, eta, *, eps=1e-6):
+def decode_step(variant, S, k_cache, q, k, v, alpha, eta, *, eps=1e-6, align="prefix"):
     """One decode step.  S [N,H,dv,dk] and k_cache [N,H,dk] are copied, updated
     and returned together with o [N,H,dv]: (o, S_new, k_cache_new)."""
     variant = VARIANTS.get(variant, variant)
+    lag = ALIGN_LAG[align]
     S = _f64(S).copy()
     k_cache = _f64(k_cache).copy()
     q, k, v, alpha, eta = map(_f64, (q, k, v, alpha, eta))
     N, H, dv, dk = S.shape
     k_cache = k_cache.reshape(N, H, dk).copy()
     o = np.zeros((N, H, dv), np.float64)
-    rc = _load().oracle_decode_step(variant, N, H, dk, dv, float(eps), _ptr(S), _ptr(k_cache),
-                                    _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(o))
+    rc = _load().oracle_decode_step_lag(variant, N, H, dk, dv, lag, float(eps), _ptr(S),
+                                        _ptr(k_cache), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                        _ptr(eta), _ptr(o))
     if rc < 0:
         raise ValueError(f"oracle_decode_step rejected its arguments (code {rc})")
     return o, S, k_cache
 
 
-def decode_step_window(variant, S, k_cache, v_cache, q, k, v, alpha, eta, *, eps=1e-6):
+def decode_step_window(variant, S, k_cache, v_cache, q, k, v, alpha, eta, *, eps=1e-6,
+                       align="prefix"):
     """One Falcon-3 / Falcon-3A decode step with a window of W pairs.
 
     S [N,H,dv,dk]; k_cache [N,H,W,dk] with k_cache[..., w, :] = k_{t-1-w};
     v_cache [N,H,W-1,dv] with v_cache[..., w-1, :] = v_{t-w}.  Returns
     (o, S_new, k_cache_new, v_cache_new), all float64 copies."""
     variant = VARIANTS.get(variant, variant)
+    lag = ALIGN_LAG[align]
     S = _f64(S).copy()
     q, k, v, alpha, eta = map(_f64, (q, k, v, alpha, eta))
     N, H, dv, dk = S.shape
@@ -147,7 +158,7 @@ def decode_step_window(variant, S, k_cache, v_cache, q, k, v, alpha, eta, *, eps
                else np.zeros((N, H, 0, dv), np.float64))
     o = np.zeros((N, H, dv), np.float64)
     vbuf = v_cache if W > 1 else np.zeros((N, H, 1, dv), np.float64)
-    rc = _load().oracle_decode_step_window(variant, N, H, dk, dv, W, float(eps), _ptr(S),
+    rc = _load().oracle_decode_step_window_lag(variant, N, H, dk, dv, W, lag, float(eps), _ptr(S),
                                            _ptr(k_cache), _ptr(vbuf), _ptr(q), _ptr(k), _ptr(v),
                                            _ptr(alpha), _ptr(eta), _ptr(o))
     if rc < 0:

@@ -21,9 +21,11 @@ def _dot(a, b):
 
 
 def recurrent_seq(variant, q, k, v, alpha, eta, *, window=1, eps=Fr(0), S0=None, k_prev=None,
-                  v_prev=None):
+                  v_prev=None, lag=1):
     """One sequence.  q, k: T lists of dk Fractions; v: T lists of dv; alpha,
-    eta: T Fractions.  Returns (o as T lists of dv, S as dv lists of dk)."""
+    eta: T Fractions; the key of step t's pair w is k_{t-w-lag} (lag 1:
+    prefix alignment, 0: same-step).  Returns (o as T lists of dv, S as dv
+    lists of dk)."""
     variant = _NAMES.get(variant, variant)
     T = len(k)
     dk = len(k[0]) if T else len(S0[0])
@@ -47,7 +49,7 @@ def recurrent_seq(variant, q, k, v, alpha, eta, *, window=1, eps=Fr(0), S0=None,
         a, e = Fr(alpha[t]), Fr(eta[t])
         S = [[a * s for s in row] for row in S]
         if variant in (F3, F3A):
-            pairs = [(key(t - w - 1), val(t - w)) for w in range(W)]
+            pairs = [(key(t - w - lag), val(t - w)) for w in range(W)]
             b = e / (sum(_dot(x, x) for x, _ in pairs) + eps)
             if variant == F3:
                 coef = [[b * (y[i] - _dot(S[i], x)) for i in range(dv)] for x, y in pairs]
@@ -58,7 +60,7 @@ def recurrent_seq(variant, q, k, v, alpha, eta, *, window=1, eps=Fr(0), S0=None,
                     for j in range(dk):
                         S[i][j] += c[i] * x[j]
         else:
-            x, y = key(t - 1), v[t]
+            x, y = key(t - lag), v[t]
             if variant in (F1, F1A):
                 n = _dot(x, x) + eps
                 u = [e * xj / n for xj in x]

@@ -19,6 +19,9 @@
  *     (authors' abstract: read-after-write autoregressive semantics);
  *   - the example revealed at step t is the prefix-aligned pair
  *     x_t = phi(k_{t-1}), y_t = v_t (authors' abstract; phi = identity here);
+ *     the same-step pair x_t = k_t, y_t = v_t (the alignment of the KLA/GDN
+ *     recurrences the pages contrast it with) is an option: `lag` = 1 is the
+ *     prefix alignment, lag = 0 the same-step one;
  *   - the updates are normalized first-order steps on a squared-error
  *     regression loss (Falcon-1/2/3) or a negative inner-product loss
  *     (Falcon-1A/2A/3A) (authors' abstract, the variant list);
@@ -50,7 +53,7 @@
 enum { OR_F1 = 1, OR_F2 = 2, OR_F3 = 3, OR_F1A = 11, OR_F2A = 12, OR_F3A = 13 };
 
 typedef struct {
-    int variant, B, H, T, dk, dv, W;
+    int variant, B, H, T, dk, dv, W, lag;
     double eps;
     const double *q, *k, *v, *alpha, *eta, *S0, *k_prev, *v_prev;
     double *o, *S_out;
@@ -63,7 +66,8 @@ static int is_known_variant(int var) {
 }
 
 /* Key k_tau of one (b,h) sequence for tau in [-W, T-1]; tau < 0 reads the
- * carried halo k_prev[W + tau] (oldest first) or 0 when there is none. */
+ * carried halo k_prev[W + tau] (oldest first) or 0 when there is none.  The
+ * key of step t's pair w is k_{t-w-lag}. */
 static const double* key_at(const seq_job* j, const double* kseq, const double* kprev, int tau,
                             const double* zeros) {
     if (tau >= 0) return kseq + (size_t)tau * j->dk;
@@ -103,7 +107,7 @@ static void run_sequence(const seq_job* j, int bh) {
         for (size_t n = 0; n < (size_t)dv * dk; ++n) S[n] *= a;
 
         if (var == OR_F1 || var == OR_F1A || var == OR_F2 || var == OR_F2A) {
-            const double* x = key_at(j, k, kprev, t - 1, zeros); /* x_t = k_{t-1} */
+            const double* x = key_at(j, k, kprev, t - j->lag, zeros); /* x_t = k_{t-lag} */
             const double* y = v + (size_t)t * dv;                /* y_t = v_t */
             if (var == OR_F1 || var == OR_F1A) {
                 double nrm = 0.0;
@@ -128,17 +132,17 @@ static void run_sequence(const seq_job* j, int bh) {
                 for (int i = 0; i < dv; ++i)
                     for (int c = 0; c < dk; ++c) S[(size_t)i * dk + c] += y[i] * u[c];
             }
-        } else { /* Falcon-3 / 3A: the W most recent pairs (x_{t-w}, y_{t-w}), w = 0..W-1 */
+        } else { /* Falcon-3 / 3A: the W most recent pairs (k_{t-w-lag}, v_{t-w}), w = 0..W-1 */
             double nrm = 0.0;
             for (int w = 0; w < W; ++w) {
-                const double* x = key_at(j, k, kprev, t - w - 1, zeros);
+                const double* x = key_at(j, k, kprev, t - w - j->lag, zeros);
                 for (int c = 0; c < dk; ++c) nrm += x[c] * x[c];
             }
             const double bstep = e / (nrm + j->eps);
             if (var == OR_F3) {
                 /* every residual is taken at the same decayed state S' */
                 for (int w = 0; w < W; ++w) {
-                    const double* x = key_at(j, k, kprev, t - w - 1, zeros);
+                    const double* x = key_at(j, k, kprev, t - w - j->lag, zeros);
                     const double* y = val_at(j, v, vprev, t - w, zeros);
                     for (int i = 0; i < dv; ++i) {
                         double s = 0.0;
@@ -147,7 +151,7 @@ static void run_sequence(const seq_job* j, int bh) {
                     }
                 }
                 for (int w = 0; w < W; ++w) {
-                    const double* x = key_at(j, k, kprev, t - w - 1, zeros);
+                    const double* x = key_at(j, k, kprev, t - w - j->lag, zeros);
                     for (int i = 0; i < dv; ++i) {
                         const double r = bstep * pred[(size_t)w * dv + i];
                         for (int c = 0; c < dk; ++c) S[(size_t)i * dk + c] += r * x[c];
@@ -155,7 +159,7 @@ static void run_sequence(const seq_job* j, int bh) {
                 }
             } else {
                 for (int w = 0; w < W; ++w) {
-                    const double* x = key_at(j, k, kprev, t - w - 1, zeros);
+                    const double* x = key_at(j, k, kprev, t - w - j->lag, zeros);
                     const double* y = val_at(j, v, vprev, t - w, zeros);
                     for (int i = 0; i < dv; ++i) {
                         const double r = bstep * y[i];
@@ -199,14 +203,17 @@ int oracle_num_cpus(void) {
 /* Recurrent form over [B,H,T,*] inputs.  Shapes: q,k [B,H,T,dk]; v [B,H,T,dv];
  * alpha, eta [B,H,T]; S0 [B,H,dv,dk] or NULL; k_prev [B,H,W,dk] or NULL;
  * v_prev [B,H,W-1,dv] or NULL.  Outputs o [B,H,T,dv], S_out [B,H,dv,dk] (or
- * NULL).  W must be 1 unless the variant is Falcon-3/3A.  Returns the number
- * of threads used, or a negative value for an invalid argument. */
-int oracle_recurrent(int variant, int B, int H, int T, int dk, int dv, int W, double eps,
-                     const double* q, const double* k, const double* v, const double* alpha,
-                     const double* eta, const double* S0, const double* k_prev,
-                     const double* v_prev, double* o, double* S_out, int nthreads) {
+ * NULL).  W must be 1 unless the variant is Falcon-3/3A; lag is 1 (prefix
+ * alignment) or 0 (same-step).  Returns the number of threads used, or a
+ * negative value for an invalid argument. */
+int oracle_recurrent_lag(int variant, int B, int H, int T, int dk, int dv, int W, int lag,
+                         double eps, const double* q, const double* k, const double* v,
+                         const double* alpha, const double* eta, const double* S0,
+                         const double* k_prev, const double* v_prev, double* o, double* S_out,
+                         int nthreads) {
     if (!is_known_variant(variant)) return -3;
     if (B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1 || W < 1) return -2;
+    if (lag != 0 && lag != 1) return -2;
     if (W != 1 && variant != OR_F3 && variant != OR_F3A) return -2;
     if (!q || !k || !v || !alpha || !eta || !o) return -1;
     int n = B * H;
@@ -215,8 +222,8 @@ int oracle_recurrent(int variant, int B, int H, int T, int dk, int dv, int W, do
     seq_job* jobs = calloc((size_t)nthreads, sizeof(seq_job));
     pthread_t* th = calloc((size_t)nthreads, sizeof(pthread_t));
     for (int i = 0; i < nthreads; ++i) {
-        seq_job jb = {variant, B, H, T, dk, dv, W, eps, q, k, v, alpha, eta, S0, k_prev, v_prev,
-                      o, S_out, nthreads, i};
+        seq_job jb = {variant, B, H, T, dk, dv, W, lag, eps, q, k, v, alpha, eta, S0, k_prev,
+                      v_prev, o, S_out, nthreads, i};
         jobs[i] = jb;
     }
     for (int i = 1; i < nthreads; ++i) pthread_create(&th[i], NULL, seq_worker, &jobs[i]);
@@ -227,22 +234,32 @@ int oracle_recurrent(int variant, int B, int H, int T, int dk, int dv, int W, do
     return nthreads;
 }
 
+/* The prefix-aligned form (lag 1). */
+int oracle_recurrent(int variant, int B, int H, int T, int dk, int dv, int W, double eps,
+                     const double* q, const double* k, const double* v, const double* alpha,
+                     const double* eta, const double* S0, const double* k_prev,
+                     const double* v_prev, double* o, double* S_out, int nthreads) {
+    return oracle_recurrent_lag(variant, B, H, T, dk, dv, W, 1, eps, q, k, v, alpha, eta, S0,
+                                k_prev, v_prev, o, S_out, nthreads);
+}
+
 /* One decode step for N*H independent heads (Falcon-1/1A/2/2A, window 1):
- * x = k_cache (the previous key), then decay, write and read exactly as one
- * iteration of the recurrence; afterwards k_cache holds the new key.
- * S [N,H,dv,dk] and k_cache [N,H,dk] are updated in place; q, k [N,H,dk];
- * v [N,H,dv]; alpha, eta [N,H]; o [N,H,dv]. */
-int oracle_decode_step(int variant, int N, int H, int dk, int dv, double eps, double* S,
-                       double* k_cache, const double* q, const double* k, const double* v,
-                       const double* alpha, const double* eta, double* o) {
+ * x = k_cache (the previous key; lag 0: the new key k), then decay, write and
+ * read exactly as one iteration of the recurrence; afterwards k_cache holds
+ * the new key.  S [N,H,dv,dk] and k_cache [N,H,dk] are updated in place;
+ * q, k [N,H,dk]; v [N,H,dv]; alpha, eta [N,H]; o [N,H,dv]. */
+int oracle_decode_step_lag(int variant, int N, int H, int dk, int dv, int lag, double eps,
+                           double* S, double* k_cache, const double* q, const double* k,
+                           const double* v, const double* alpha, const double* eta, double* o) {
     if (variant != OR_F1 && variant != OR_F2 && variant != OR_F1A && variant != OR_F2A) return -3;
-    if (N < 1 || H < 1 || dk < 1 || dv < 1) return -2;
+    if (N < 1 || H < 1 || dk < 1 || dv < 1 || (lag != 0 && lag != 1)) return -2;
     double* u = calloc((size_t)dk, sizeof(double));
     double* r = calloc((size_t)dv, sizeof(double));
     for (size_t n = 0; n < (size_t)N * H; ++n) {
         double* Sh = S + n * dv * dk;
-        double* x = k_cache + n * dk;
+        double* kc = k_cache + n * dk;
         const double *qh = q + n * dk, *kh = k + n * dk, *vh = v + n * dv;
+        const double* x = lag ? kc : kh;
         const double a = alpha[n], e = eta[n];
         for (size_t m = 0; m < (size_t)dv * dk; ++m) Sh[m] *= a;
         if (variant == OR_F1 || variant == OR_F1A) {
@@ -270,11 +287,18 @@ int oracle_decode_step(int variant, int N, int H, int dk, int dv, double eps, do
             for (int c = 0; c < dk; ++c) s += Sh[(size_t)i * dk + c] * qh[c];
             o[n * dv + i] = s;
         }
-        memcpy(x, kh, sizeof(double) * dk);
+        memcpy(kc, kh, sizeof(double) * dk);
     }
     free(u);
     free(r);
     return 0;
+}
+
+int oracle_decode_step(int variant, int N, int H, int dk, int dv, double eps, double* S,
+                       double* k_cache, const double* q, const double* k, const double* v,
+                       const double* alpha, const double* eta, double* o) {
+    return oracle_decode_step_lag(variant, N, H, dk, dv, 1, eps, S, k_cache, q, k, v, alpha, eta,
+                                  o);
 }
 
 /*
@@ -287,30 +311,35 @@ int oracle_decode_step(int variant, int N, int H, int dk, int dv, double eps, do
  * b = eta / (sum_w ||x_{t-w}||^2 + eps), then S = S' + b sum_w R_w x_{t-w}^T
  * with every residual R_w = y_{t-w} - S' x_{t-w} taken at S' (Falcon-3A:
  * R_w = y_{t-w}), and o = S q.  Both caches then move one slot: the new key
- * and value enter at slot 0 and the oldest leave.
+ * and value enter at slot 0 and the oldest leave.  With lag 0 (same-step
+ * pairs) pair w's key is k_{t-w}: the new key for w = 0, k_cache[w-1] after.
  */
-int oracle_decode_step_window(int variant, int N, int H, int dk, int dv, int W, double eps,
-                              double* S, double* k_cache, double* v_cache, const double* q,
-                              const double* k, const double* v, const double* alpha,
-                              const double* eta, double* o) {
+int oracle_decode_step_window_lag(int variant, int N, int H, int dk, int dv, int W, int lag,
+                                  double eps, double* S, double* k_cache, double* v_cache,
+                                  const double* q, const double* k, const double* v,
+                                  const double* alpha, const double* eta, double* o) {
     if (variant != OR_F3 && variant != OR_F3A) return -3;
-    if (N < 1 || H < 1 || dk < 1 || dv < 1 || W < 1) return -2;
+    if (N < 1 || H < 1 || dk < 1 || dv < 1 || W < 1 || (lag != 0 && lag != 1)) return -2;
     double* R = calloc((size_t)W * dv, sizeof(double));
     const double** y = calloc((size_t)W, sizeof(double*));
+    const double** xs = calloc((size_t)W, sizeof(double*));
     for (size_t n = 0; n < (size_t)N * H; ++n) {
         double* Sh = S + n * dv * dk;
         double* kc = k_cache + n * W * dk;
         double* vc = v_cache + n * (W - 1) * dv;
         const double *qh = q + n * dk, *kh = k + n * dk, *vh = v + n * dv;
         const double a = alpha[n], e = eta[n];
-        for (int w = 0; w < W; ++w) y[w] = (w == 0) ? vh : vc + (size_t)(w - 1) * dv;
+        for (int w = 0; w < W; ++w) {
+            y[w] = (w == 0) ? vh : vc + (size_t)(w - 1) * dv;
+            xs[w] = (w + lag == 0) ? kh : kc + (size_t)(w + lag - 1) * dk;
+        }
         for (size_t m = 0; m < (size_t)dv * dk; ++m) Sh[m] *= a;
         double nrm = 0.0;
         for (int w = 0; w < W; ++w)
-            for (int c = 0; c < dk; ++c) nrm += kc[(size_t)w * dk + c] * kc[(size_t)w * dk + c];
+            for (int c = 0; c < dk; ++c) nrm += xs[w][c] * xs[w][c];
         const double b = e / (nrm + eps);
         for (int w = 0; w < W; ++w) {
-            const double* x = kc + (size_t)w * dk;
+            const double* x = xs[w];
             for (int i = 0; i < dv; ++i) {
                 double s = 0.0;
                 if (variant == OR_F3)
@@ -319,7 +348,7 @@ int oracle_decode_step_window(int variant, int N, int H, int dk, int dv, int W, 
             }
         }
         for (int w = 0; w < W; ++w) {
-            const double* x = kc + (size_t)w * dk;
+            const double* x = xs[w];
             for (int i = 0; i < dv; ++i)
                 for (int c = 0; c < dk; ++c) Sh[(size_t)i * dk + c] += b * R[(size_t)w * dv + i] * x[c];
         }
@@ -335,5 +364,14 @@ int oracle_decode_step_window(int variant, int N, int H, int dk, int dv, int W, 
     }
     free(R);
     free(y);
+    free(xs);
     return 0;
+}
+
+int oracle_decode_step_window(int variant, int N, int H, int dk, int dv, int W, double eps,
+                              double* S, double* k_cache, double* v_cache, const double* q,
+                              const double* k, const double* v, const double* alpha,
+                              const double* eta, double* o) {
+    return oracle_decode_step_window_lag(variant, N, H, dk, dv, W, 1, eps, S, k_cache, v_cache, q,
+                                         k, v, alpha, eta, o);
 }

@@ -11,7 +11,8 @@ Algebra used (one (batch, head) sequence, a segment of L steps that starts
 from the state S0):
 
 * Each step s contributes "virtual examples" (s, w), w = 0..Wv-1 (Wv = W for
-  Falcon-3/3A, 1 otherwise) with key x_{s-w}, target y_{s-w} and write vector
+  Falcon-3/3A, 1 otherwise) with key x_{s-w} = k_{s-w-lag} (lag 1: prefix
+  alignment, 0: same-step), target y_{s-w} and write vector
   omega_(s,w): u_s for Falcon-1/2 (and the A forms), b_s x_{s-w} for Falcon-3.
 * g_s is the cumulative log-decay from the segment start and
   D(t, s) = exp(g_t - g_s) <= 1 for s <= t: every decay factor is a ratio of a
@@ -53,7 +54,7 @@ def _halo_vals(v, v_prev, W):
     return np.concatenate([pre, v], axis=0)
 
 
-def _segment(variant, S0, q, kh, vh, alpha, eta, t0, L, W, eps):
+def _segment(variant, S0, q, kh, vh, alpha, eta, t0, L, W, eps, lag):
     """Masked form of one segment [t0, t0+L) of one sequence."""
     regression = variant in (F1, F2, F3)
     Wv = W if variant in (F3, F3A) else 1
@@ -61,7 +62,7 @@ def _segment(variant, S0, q, kh, vh, alpha, eta, t0, L, W, eps):
     rows_x, rows_y, rows_w, step = [], [], [], []
     for s in range(L):
         t = t0 + s
-        xs = [kh[t - w - 1 + W] for w in range(Wv)]   # x_{t-w} = k_{t-w-1}
+        xs = [kh[t - w - lag + W] for w in range(Wv)]   # x_{t-w} = k_{t-w-lag}
         ys = [vh[t - w + W - 1] for w in range(Wv)]   # y_{t-w} = v_{t-w}
         if variant in (F1, F1A):
             x = xs[0]
@@ -106,7 +107,7 @@ def _segment(variant, S0, q, kh, vh, alpha, eta, t0, L, W, eps):
 
 
 def chunked(variant, q, k, v, alpha, eta, *, chunk, window=1, eps=1e-6, S0=None, k_prev=None,
-            v_prev=None):
+            v_prev=None, lag=1):
     """Chunk-parallel form with chunks of `chunk` steps (chunk >= T gives the
     masked-parallel form).  Same argument shapes as the recurrent oracle."""
     variant = _NAMES.get(variant, variant)
@@ -124,7 +125,7 @@ def chunked(variant, q, k, v, alpha, eta, *, chunk, window=1, eps=1e-6, S0=None,
             for t0 in range(0, T, chunk):
                 L = min(chunk, T - t0)
                 O, S = _segment(variant, S, q[b, h], kh, vh, alpha[b, h], eta[b, h], t0, L, W,
-                                eps)
+                                eps, lag)
                 o[b, h, t0:t0 + L] = O
             S_out[b, h] = S
     return o, S_out

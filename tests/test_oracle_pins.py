@@ -572,3 +572,144 @@ def test_oracle_rejects_bad_arguments():
         oracle.recurrent(7, d["q"], d["k"], d["v"], d["alpha"], d["eta"])
     with pytest.raises(ValueError):
         oracle.recurrent("F1", d["q"], d["k"], d["v"], d["alpha"], d["eta"], window=2)
+
+
+# ------------------------------------------------- same-step alignment ------
+# The pages contrast the prefix-aligned pair (k_{t-1}, v_t) with the same-step
+# pair (k_t, v_t) of the KLA / gated-delta-rule recurrences.  align="same"
+# gives the latter; these pin it.
+def run_same(variant, d, W=1, eps=1e-6):
+    return run(variant, d, W=W, eps=eps, align="same")
+
+
+def test_same_step_falcon1_is_kla_product_form():
+    """Falcon-1 with same-step pairs is KLA exactly: the gated delta rule in its
+    product form S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+    with beta_t = eta_t / (||k_t||^2 + eps), on the unshifted keys."""
+    d = rnd(51, B=1, H=2, T=14, dk=5, dv=4)
+    eps = 1e-3
+    o, S = run_same("F1", d, eps=eps)
+    for h in range(2):
+        St = d["S0"][0, h].copy()
+        for t in range(14):
+            kk = d["k"][0, h, t]
+            beta = d["eta"][0, h, t] / (kk @ kk + eps)
+            St = d["alpha"][0, h, t] * St @ (np.eye(5) - beta * np.outer(kk, kk)) \
+                + beta * np.outer(d["v"][0, h, t], kk)
+            np.testing.assert_allclose(o[0, h, t], St @ d["q"][0, h, t], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(S[0, h], St, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("variant", ALL)
+def test_same_step_is_prefix_alignment_on_keys_moved_one_step(variant):
+    """Same-step pairs on keys k equal prefix-aligned pairs on k' with
+    k'_tau = k_{tau+1}: the halo moves with them (k'_{-W..-1} = k_{-W+1..0}),
+    and k'_{T-1} is never read."""
+    for W in ([1, 2, 4] if variant in ("F3", "F3A") else [1]):
+        d = rnd(52 + W, B=1, H=2, T=13, dk=5, dv=4, W=W)
+        o, S = run_same(variant, d, W=W)
+        kh = np.concatenate([d["k_prev"], d["k"]], axis=2)          # k_tau, tau = -W..T-1
+        d2 = dict(d)
+        d2["k_prev"] = kh[:, :, 1:W + 1].copy()                      # k_{-W+1} .. k_0
+        d2["k"] = np.concatenate([kh[:, :, W + 1:], np.full_like(kh[:, :, :1], 7.0)], axis=2)
+        o2, S2 = run(variant, d2, W=W)
+        np.testing.assert_allclose(o, o2, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(S, S2, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("variant", ["F1", "F2"])
+def test_same_step_interpolation(variant):
+    """alpha = eta = 1, eps = 0: the same-step write makes S_t k_t = v_t, so a
+    read with q_t = k_t returns v_t."""
+    d = rnd(57, T=9, dk=6, dv=3)
+    d["alpha"][:] = 1.0
+    d["eta"][:] = 1.0
+    d["q"] = d["k"].copy()
+    o, _ = run_same(variant, d, eps=0.0)
+    np.testing.assert_allclose(o, d["v"], rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("variant", ALL)
+def test_same_step_exact_rational_matches_fp64(variant):
+    r = np.random.default_rng(58)
+    for W in wins(variant):
+        T, dk, dv = 5, 3, 2
+        ri = lambda *s: r.integers(-4, 5, s)  # noqa: E731
+        q, k, v = ri(T, dk), ri(T, dk), ri(T, dv)
+        kp, vp, S0 = ri(W, dk), ri(W - 1, dv), ri(dv, dk)
+        al = [Fr(int(a), 8) for a in r.integers(1, 9, T)]
+        et = [Fr(int(a), 4) for a in r.integers(0, 5, T)]
+        eps = Fr(1, 16)
+        F = lambda a: [[Fr(int(x)) for x in row] for row in a]  # noqa: E731
+        oe, Se = exact.recurrent_seq(variant, F(q), F(k), F(v), al, et, window=W, eps=eps,
+                                     S0=F(S0), k_prev=F(kp), v_prev=F(vp) if W > 1 else None,
+                                     lag=0)
+        o, S = oracle.recurrent(variant, q[None, None], k[None, None], v[None, None],
+                                np.array([float(a) for a in al])[None, None],
+                                np.array([float(a) for a in et])[None, None], window=W,
+                                eps=float(eps), S0=S0[None, None], k_prev=kp[None, None],
+                                v_prev=vp[None, None] if W > 1 else None, align="same")
+        oe = np.array([[float(x) for x in row] for row in oe])
+        Se = np.array([[float(x) for x in row] for row in Se])
+        assert np.abs(o[0, 0] - oe).max() <= 1e-13 * max(1.0, np.abs(oe).max())
+        assert np.abs(S[0, 0] - Se).max() <= 1e-13 * max(1.0, np.abs(Se).max())
+
+
+@pytest.mark.parametrize("variant", ALL)
+def test_same_step_recurrent_masked_chunk_agree(variant):
+    for W in ([1, 3] if variant in ("F3", "F3A") else [1]):
+        d = rnd(60 + W, B=1, H=2, T=20, dk=5, dv=4, W=W)
+        o, S = run_same(variant, d, W=W)
+        kw = dict(window=W, eps=1e-6, S0=d["S0"], k_prev=d["k_prev"], v_prev=d["v_prev"], lag=0)
+        for C in (1, 3, 8, 20):
+            oc, Sc = forms.chunked(variant, d["q"], d["k"], d["v"], d["alpha"], d["eta"],
+                                   chunk=C, **kw)
+            np.testing.assert_allclose(oc, o, rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(Sc, S, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("variant", ["F1", "F2", "F1A", "F2A"])
+def test_same_step_decode_is_one_recurrent_step(variant):
+    r = np.random.default_rng(63)
+    N, H, dk, dv, steps = 2, 2, 5, 4, 8
+    S = r.standard_normal((N, H, dv, dk)) * 0.1
+    kc = r.standard_normal((N, H, dk))
+    q, k = r.standard_normal((steps, N, H, dk)), r.standard_normal((steps, N, H, dk))
+    v = r.standard_normal((steps, N, H, dv))
+    al, et = r.uniform(0.5, 1, (steps, N, H)), r.uniform(0, 1, (steps, N, H))
+    S_run, kc_run, outs = S, kc, []
+    for s in range(steps):
+        o, S_run, kc_run = oracle.decode_step(variant, S_run, kc_run, q[s], k[s], v[s], al[s],
+                                              et[s], align="same")
+        outs.append(o)
+    tr = lambda a: np.moveaxis(a, 0, 2)  # noqa: E731
+    o_rec, S_rec = oracle.recurrent(variant, tr(q), tr(k), tr(v), tr(al), tr(et), S0=S,
+                                    k_prev=kc[:, :, None, :], align="same")
+    np.testing.assert_allclose(tr(np.array(outs)), o_rec, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(S_run, S_rec, rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(kc_run, k[steps - 1])
+
+
+@pytest.mark.parametrize("variant", ["F3", "F3A"])
+@pytest.mark.parametrize("W", [1, 2, 4])
+def test_same_step_decode_window_is_one_recurrent_step(variant, W):
+    r = np.random.default_rng(65 + W)
+    N, H, dk, dv, steps = 2, 2, 5, 4, 9
+    S = r.standard_normal((N, H, dv, dk)) * 0.1
+    k_prev = r.standard_normal((N, H, W, dk))
+    v_prev = r.standard_normal((N, H, W - 1, dv))
+    kc, vc = k_prev[:, :, ::-1, :].copy(), v_prev[:, :, ::-1, :].copy()
+    q, k = r.standard_normal((steps, N, H, dk)), r.standard_normal((steps, N, H, dk))
+    v = r.standard_normal((steps, N, H, dv))
+    al, et = r.uniform(0.5, 1, (steps, N, H)), r.uniform(0, 1, (steps, N, H))
+    S_run, kc_run, vc_run, outs = S, kc, vc, []
+    for s in range(steps):
+        o, S_run, kc_run, vc_run = oracle.decode_step_window(
+            variant, S_run, kc_run, vc_run, q[s], k[s], v[s], al[s], et[s], align="same")
+        outs.append(o)
+    tr = lambda a: np.moveaxis(a, 0, 2)  # noqa: E731
+    o_rec, S_rec = oracle.recurrent(variant, tr(q), tr(k), tr(v), tr(al), tr(et), window=W,
+                                    S0=S, k_prev=k_prev, v_prev=v_prev if W > 1 else None,
+                                    align="same")
+    np.testing.assert_allclose(tr(np.array(outs)), o_rec, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(S_run, S_rec, rtol=1e-12, atol=1e-13)
