@@ -21,6 +21,14 @@
  *   library's reading of "per-column extension" and "sliding-window
  *   mini-batch update"; the authors' text gives them in words only.)
  *
+ * Alignment.  By default step t learns the prefix-aligned pair
+ * (k_{t-1}, v_t).  OR-ing FALCON_SAME_STEP into the variant selects the
+ * same-step pair (k_t, v_t), the alignment of the KLA / gated-delta-rule
+ * recurrences the pages contrast the method with (with it, FALCON_F1 is KLA
+ * with beta_t = eta_t / (||k_t||^2 + eps)).  Every entry point accepts the
+ * flag; halos and caches keep their meaning (the last W keys, the last W-1
+ * values), a same-step pair w simply takes k_{t-w} instead of k_{t-1-w}.
+ *
  * The abstract states that each rule has a chunk-parallel form with
  * positive-decay renormalization; falcon_chunk_fwd computes that form
  * (cumulative decays kept as chunk-local log sums, every factor a ratio
@@ -70,7 +78,8 @@ typedef enum {
     FALCON_F3 = 3,
     FALCON_F1A = 11,
     FALCON_F2A = 12,
-    FALCON_F3A = 13
+    FALCON_F3A = 13,
+    FALCON_SAME_STEP = 0x100 /* flag OR-ed into a variant: same-step pairs (k_t, v_t) */
 } falcon_variant;
 
 typedef enum { FALCON_FP32 = 0, FALCON_BF16 = 1 } falcon_dtype;
@@ -119,8 +128,8 @@ int falcon_chunk_fwd(const void* q, const void* k, const void* v, const float* a
 
 /*
  * One decode step for N independent sequences x H heads (one token each):
- * x = k_cache (the previous key), S' = alpha S, write as above, o = S q,
- * then k_cache <- k.
+ * x = k_cache (the previous key; with FALCON_SAME_STEP the new key k),
+ * S' = alpha S, write as above, o = S q, then k_cache <- k.
  *
  *   S         [N,H,dv,dk] fp32, read and overwritten in place
  *   k_cache   [N,H,W,dk]  dtype dt, holds k_{t-1}; overwritten with k_t
@@ -157,7 +166,8 @@ int falcon_decode_step(float* S, void* k_cache, const void* q, const void* k, co
  * The step: S' = alpha S, b = eta / (sum_w ||x_{t-w}||^2 + eps), then
  * S = S' + b sum_w (y_{t-w} - S' x_{t-w}) x_{t-w}^T (Falcon-3A writes
  * y_{t-w} instead of the residual), o = S q: the step falcon_chunk_fwd takes
- * at time t.  Caches filled from a chunk call's halo: k_cache[w] = k_prev[W-1-w],
+ * at time t.  With FALCON_SAME_STEP pair w's key is k_{t-w}: the new key k
+ * for w = 0 and k_cache slot w-1 after (the last slot is then only carried).  Caches filled from a chunk call's halo: k_cache[w] = k_prev[W-1-w],
  * v_cache[w-1] = v_prev[W-1-w].
  *
  * Support matrix: var in {F3, F3A}; window W in 1..8; dk = dv in {64, 128};

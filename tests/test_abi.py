@@ -85,6 +85,8 @@ def chunk(L, **kw):
     (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(alpha=None), -1),
     (dict(eta=None), -1), (dict(o=None), -1),
     (dict(q=P + 8), -3), (dict(S0=P + 4), -3), (dict(alpha=P + 2), -3),
+    (dict(var=1 | 0x200), -3), (dict(var=0x100), -3), (dict(var=4 | 0x100), -3),  # flag bits
+    (dict(var=1 | 0x100, window=2), -2),
 ])
 def test_chunk_rejects(L, kw, code):
     assert chunk(L, **kw) == code
@@ -105,6 +107,7 @@ def decode(L, **kw):
     (dict(dk=32, dv=32), -3), (dict(dk=128, dv=64), -3), (dict(eps=-2.0), -2),
     (dict(S=None), -1), (dict(kc=None), -1), (dict(o=None), -1), (dict(eta=None), -1),
     (dict(S=P + 8), -3),
+    (dict(var=3 | 0x100), -3), (dict(var=1 | 0x800), -3), (dict(var=0x100), -3),
 ])
 def test_decode_rejects(L, kw, code):
     assert decode(L, **kw) == code
@@ -126,6 +129,7 @@ def decode_window(L, **kw):
     (dict(dk=32, dv=32), -3), (dict(dk=128, dv=64), -3), (dict(eps=-1.0), -2),
     (dict(S=None), -1), (dict(kc=None), -1), (dict(vc=None), -1), (dict(o=None), -1),
     (dict(alpha=None), -1), (dict(S=P + 4), -3), (dict(eta=P + 2), -3),
+    (dict(var=1 | 0x100), -3), (dict(var=3 | 0x400), -3),
 ])
 def test_decode_window_rejects(L, kw, code):
     assert decode_window(L, **kw) == code
@@ -150,3 +154,12 @@ def test_package_has_no_cpu_fallback():
         if fn.endswith(".py"):
             src = open(os.path.join(pkg, fn)).read()
             assert "import oracle" not in src and "from oracle" not in src, fn
+
+
+def test_same_step_flag_keeps_the_workspace_size(L):
+    """The alignment flag changes which key each pair reads, not the records."""
+    for var in (1, 2, 3, 11, 12, 13):
+        W = 4 if var in (3, 13) else 1
+        a = L.falcon_chunk_fwd_workspace(2, 3, 1000, 128, 128, 1, var, W, 64)
+        b = L.falcon_chunk_fwd_workspace(2, 3, 1000, 128, 128, 1, var | 0x100, W, 64)
+        assert a == b and a > 0

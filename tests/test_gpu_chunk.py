@@ -29,28 +29,30 @@ def supported(dtype, D, chunk):
     return not (dtype == "fp32" and D == 128 and chunk == 64)
 
 
-def gpu_run(dev, inp, variant, W, chunk, eps=1e-6, label=""):
+def gpu_run(dev, inp, variant, W, chunk, eps=1e-6, label="", align="prefix"):
     import torch
     import weight_recurrent_sequence_amd as fal
     t = inp.to_torch(dev)
     B, H, T, D = inp.k.shape
-    announce(f"chunk_fwd {variant} {inp.dtype} B{B} H{H} T{T} d{D} W{W} chunk{chunk} {label}")
+    announce(f"chunk_fwd {variant} {inp.dtype} B{B} H{H} T{T} d{D} W{W} chunk{chunk} "
+             f"align={align} {label}")
     o, S = fal.chunk_fwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], variant, window=W,
                          chunk=chunk, eps=eps, S0=t["S0"], k_prev=t["k_prev"],
-                         v_prev=t["v_prev"])
+                         v_prev=t["v_prev"], align=align)
     torch.cuda.synchronize()
     return o, S
 
 
-def oracle_run(inp, variant, W, eps=1e-6, sl=None):
+def oracle_run(inp, variant, W, eps=1e-6, sl=None, align="prefix"):
     d = inp.f64(sl)
     return oracle.recurrent(variant, d["q"], d["k"], d["v"], d["alpha"], d["eta"], window=W,
-                            eps=eps, S0=d["S0"], k_prev=d["k_prev"], v_prev=d["v_prev"])
+                            eps=eps, S0=d["S0"], k_prev=d["k_prev"], v_prev=d["v_prev"],
+                            align=align)
 
 
-def check(dev, inp, variant, W, chunk, label=""):
-    o, S = gpu_run(dev, inp, variant, W, chunk, label=label)
-    o_ref, S_ref = oracle_run(inp, variant, W)
+def check(dev, inp, variant, W, chunk, label="", align="prefix"):
+    o, S = gpu_run(dev, inp, variant, W, chunk, label=label, align=align)
+    o_ref, S_ref = oracle_run(inp, variant, W, align=align)
     e_o = slice_rel_err(to_np(o), o_ref, (2, 3))
     e_S = slice_rel_err(to_np(S), S_ref, (2, 3))
     tol = TOL[inp.dtype]
@@ -92,6 +94,38 @@ def test_windows(dev, variant, W, chunk):
     inp = I.make_chunk_inputs(1, 3, 100, 64, 64, dtype="bf16", seed=300 + W, window=W,
                               halo=True)
     check(dev, inp, variant, W, chunk)
+
+
+# ---- same-step pairs (k_t, v_t), the KLA / gated-delta-rule alignment ----
+@pytest.mark.parametrize("chunk", [16, 64])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("variant", ALL)
+def test_same_step_grid(dev, variant, dtype, D, chunk):
+    if not supported(dtype, D, chunk):
+        pytest.skip("fp32 with d=128 supports chunk <= 32 (LDS)")
+    W = 3 if variant in ("F3", "F3A") else 1
+    inp = I.make_chunk_inputs(2, 3, 150, D, D, dtype=dtype, seed=600 + D + chunk, window=W,
+                              halo=True, S0_sd=0.3)
+    check(dev, inp, variant, W, chunk, align="same")
+
+
+@pytest.mark.parametrize("T", [1, 2, 17, 64, 65, 130])
+@pytest.mark.parametrize("case", [("F1", "bf16", 128, 64, 1), ("F3", "bf16", 128, 64, 4),
+                                  ("F3A", "bf16", 64, 16, 8), ("F2", "fp32", 64, 32, 1)])
+def test_same_step_lengths(dev, case, T):
+    variant, dtype, D, chunk, W = case
+    inp = I.make_chunk_inputs(1, 2, T, D, D, dtype=dtype, seed=700 + T, window=W, halo=True,
+                              S0_sd=0.2)
+    check(dev, inp, variant, W, chunk, align="same")
+
+
+def test_same_step_differs_from_prefix(dev):
+    """The flag reaches the kernels: the two alignments give different outputs."""
+    inp = I.make_chunk_inputs(1, 2, 100, 64, 64, dtype="fp32", seed=710)
+    o1, _ = gpu_run(dev, inp, "F1", 1, 32)
+    o2, _ = gpu_run(dev, inp, "F1", 1, 32, align="same")
+    assert np.abs(to_np(o1) - to_np(o2)).max() > 1e-2
 
 
 @pytest.mark.parametrize("variant", ALL)
@@ -154,15 +188,19 @@ FULL = [
     ("falcon2_bf16_B4H32T8192d128", "F2A", [(1, 5)]),
     ("falcon3_w4_bf16_B2H16T32768d128", "F3", [(0, 3), (1, 12)]),
     ("falcon3_w4_bf16_B2H16T32768d128", "F3A", [(1, 0)]),
+    ("falcon1_bf16_B8H16T4096d128", "F1@same", [(2, 4), (5, 11)]),
+    ("falcon3_w4_bf16_B2H16T32768d128", "F3@same", [(0, 9)]),
 ]
 
 
 @pytest.mark.parametrize("name,variant,sample", FULL, ids=[f"{n}-{v}" for n, v, _ in FULL])
 def test_full_workloads_sampled(dev, name, variant, sample):
+    variant, _, align = variant.partition("@")
+    align = align or "prefix"
     w = I.WORKLOADS[name]
     W = w.get("window", 1)
     inp = I.workload_inputs(name)
-    o, S = gpu_run(dev, inp, variant, W, w["chunk"], label=name)
+    o, S = gpu_run(dev, inp, variant, W, w["chunk"], label=name, align=align)
     o_np, S_np = to_np(o), to_np(S)
     assert np.isfinite(o_np).all() and np.isfinite(S_np).all()
     tol = TOL[inp.dtype]
@@ -173,7 +211,8 @@ def test_full_workloads_sampled(dev, name, variant, sample):
     # oracle on the sampled sequences only, as a [1, n] batch
     d = inp.f64((bs, hs))
     o_ref, S_ref = oracle.recurrent(variant, *(d[x][None] for x in ("q", "k", "v", "alpha",
-                                                                      "eta")), window=W)
+                                                                      "eta")), window=W,
+                                    align=align)
     e_o = slice_rel_err(o_np[bs, hs][None], o_ref, (2, 3))
     e_S = slice_rel_err(S_np[bs, hs][None], S_ref, (2, 3))
     announce(f"{name} {variant}: max rel err o={e_o:.2e} S={e_S:.2e} over {len(heads)} heads")

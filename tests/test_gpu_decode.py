@@ -194,3 +194,56 @@ def test_decode_window_full_workload_sampled(dev, variant):
     assert e_o <= TOL["bf16"] and e_S <= TOL["bf16"], (e_o, e_S)
     np.testing.assert_array_equal(f64(kc[ns, hs]), kc_o[0])
     np.testing.assert_array_equal(f64(vc[ns, hs]), vc_o[0])
+
+
+
+# ---- same-step pairs: x = k_t (the new key), caches as in the prefix form ----
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("variant", ["F1", "F2", "F1A", "F2A"])
+def test_same_step_decode(dev, variant, dtype):
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    N, H, D, steps = 3, 4, 128, 8
+    di = I.make_decode_inputs(N, H, D, D, steps, dtype=dtype, seed=800, S0_sd=0.1)
+    S, kc = tens(di.S0, "fp32", dev), tens(di.k_cache0, dtype, dev)
+    S_o, kc_o = di.S0.astype(np.float64), di.widen(di.k_cache0)[:, :, 0]
+    for s in range(steps):
+        announce(f"decode_step same-step {variant} {dtype} step {s}")
+        o = fal.decode_step(S, kc, tens(di.q[s], dtype, dev), tens(di.k[s], dtype, dev),
+                            tens(di.v[s], dtype, dev), tens(di.alpha[s], "fp32", dev),
+                            tens(di.eta[s], "fp32", dev), variant, align="same")
+        o_ref, S_o, kc_o = oracle.decode_step(variant, S_o, kc_o, di.widen(di.q[s]),
+                                              di.widen(di.k[s]), di.widen(di.v[s]),
+                                              di.alpha[s], di.eta[s], align="same")
+        torch.cuda.synchronize()
+        assert slice_rel_err(to_np(o), o_ref, (2,)) <= TOL[dtype]
+    assert slice_rel_err(to_np(S), S_o, (2, 3)) <= TOL[dtype]
+    np.testing.assert_array_equal(to_np(kc)[:, :, 0], kc_o)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("W", [1, 2, 4, 8])
+@pytest.mark.parametrize("variant", ["F3", "F3A"])
+def test_same_step_decode_window(dev, variant, W, D):
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    N, H, steps, dtype = 3, 4, 8, "bf16"
+    di = I.make_decode_inputs(N, H, D, D, steps, dtype=dtype, seed=810 + W + D, S0_sd=0.1,
+                              window=W)
+    S, kc = tens(di.S0, "fp32", dev), tens(di.k_cache0, dtype, dev)
+    vc = tens(di.v_cache0, dtype, dev) if W > 1 else None
+    S_o, kc_o, vc_o = di.S0.astype(np.float64), di.widen(di.k_cache0), di.widen(di.v_cache0)
+    for s in range(steps):
+        announce(f"decode_step_window same-step {variant} W{W} d{D} step {s}")
+        o = fal.decode_step_window(S, kc, vc, tens(di.q[s], dtype, dev), tens(di.k[s], dtype, dev),
+                                   tens(di.v[s], dtype, dev), tens(di.alpha[s], "fp32", dev),
+                                   tens(di.eta[s], "fp32", dev), variant, align="same")
+        o_ref, S_o, kc_o, vc_o = oracle.decode_step_window(
+            variant, S_o, kc_o, vc_o, di.widen(di.q[s]), di.widen(di.k[s]), di.widen(di.v[s]),
+            di.alpha[s], di.eta[s], align="same")
+        torch.cuda.synchronize()
+        assert slice_rel_err(to_np(o), o_ref, (2,)) <= TOL[dtype]
+    assert slice_rel_err(to_np(S), S_o, (2, 3)) <= TOL[dtype]
+    np.testing.assert_array_equal(to_np(kc), kc_o)
+    if W > 1:
+        np.testing.assert_array_equal(to_np(vc), vc_o)

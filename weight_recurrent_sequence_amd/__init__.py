@@ -4,6 +4,6 @@ The computation runs in libfalcon.so (hand-written HIP kernels behind the C
 ABI of include/falcon.h); this package is its Python binding plus the seeded
 input generators used by tests and benchmarks.
 """
-from .binding import (BF16, F1, F1A, F2, F2A, F3, F3A, FP32, VARIANTS, FalconError,  # noqa: F401
+from .binding import (BF16, F1, F1A, F2, F2A, F3, F3A, FP32, SAME_STEP, VARIANTS, FalconError,  # noqa: F401
                       chunk_fwd, decode_step, decode_step_window, lib, status_string,
                       workspace_bytes)

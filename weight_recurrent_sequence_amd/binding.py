@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(PKG, "libfalcon.so")
 
 F1, F2, F3, F1A, F2A, F3A = 1, 2, 3, 11, 12, 13
 VARIANTS = {"F1": F1, "F2": F2, "F3": F3, "F1A": F1A, "F2A": F2A, "F3A": F3A}
+SAME_STEP = 0x100  # flag OR-ed into a variant: same-step pairs (k_t, v_t)
+ALIGN = {"prefix": 0, "same": SAME_STEP}
 FP32, BF16 = 0, 1
 STATUS = {0: "FALCON_OK", -1: "FALCON_ERR_NULL", -2: "FALCON_ERR_SHAPE",
           -3: "FALCON_ERR_UNSUPPORTED", -4: "FALCON_ERR_WORKSPACE", -5: "FALCON_ERR_HIP"}
@@ -60,8 +62,10 @@ def status_string(status: int) -> str:
     return lib().falcon_status_string(int(status)).decode()
 
 
-def _variant(v) -> int:
-    return VARIANTS[v] if isinstance(v, str) else int(v)
+def _variant(v, align="prefix") -> int:
+    """Variant code with the alignment flag: align="prefix" pairs (k_{t-1}, v_t),
+    align="same" pairs (k_t, v_t)."""
+    return (VARIANTS[v] if isinstance(v, str) else int(v)) | ALIGN[align]
 
 
 def _dt(t) -> int:
@@ -104,7 +108,7 @@ def workspace_bytes(B, H, T, dk, dv, dtype, variant, window=1, chunk=64) -> int:
 
 def chunk_fwd(q, k, v, alpha, eta, variant, *, window=1, chunk=64, eps=1e-6, S0=None,
               k_prev=None, v_prev=None, o=None, S_final=None, return_state=True,
-              workspace=None, stream=None):
+              workspace=None, stream=None, align="prefix"):
     """Chunk-parallel forward.  q,k [B,H,T,dk]; v [B,H,T,dv] (bf16 or fp32);
     alpha, eta [B,H,T] fp32; S0 [B,H,dv,dk] fp32 or None; k_prev [B,H,W,dk],
     v_prev [B,H,W-1,dv] or None.  `workspace` (uint8 device tensor of at
@@ -112,7 +116,7 @@ def chunk_fwd(q, k, v, alpha, eta, variant, *, window=1, chunk=64, eps=1e-6, S0=
     Returns (o, S_final) (S_final None if return_state is False and none was
     given)."""
     import torch
-    var = _variant(variant)
+    var = _variant(variant, align)
     B, H, T, dk = k.shape
     dv = v.shape[-1]
     dev, dt = k.device, k.dtype
@@ -150,12 +154,13 @@ def chunk_fwd(q, k, v, alpha, eta, variant, *, window=1, chunk=64, eps=1e-6, S0=
     return o, S_final
 
 
-def decode_step(S, k_cache, q, k, v, alpha, eta, variant, *, eps=1e-6, o=None, stream=None):
+def decode_step(S, k_cache, q, k, v, alpha, eta, variant, *, eps=1e-6, o=None, stream=None,
+                align="prefix"):
     """One decode step.  S [N,H,dv,dk] fp32 and k_cache [N,H,1,dk] are
     updated in place; q,k [N,H,dk], v [N,H,dv] (bf16 or fp32), alpha, eta
     [N,H] fp32.  Returns o [N,H,dv]."""
     import torch
-    var = _variant(variant)
+    var = _variant(variant, align)
     N, H, dv, dk = S.shape
     dev, dt = k.device, k.dtype
     dtc = _dt(k)
@@ -178,13 +183,13 @@ def decode_step(S, k_cache, q, k, v, alpha, eta, variant, *, eps=1e-6, o=None, s
 
 
 def decode_step_window(S, k_cache, v_cache, q, k, v, alpha, eta, variant, *, eps=1e-6, o=None,
-                       stream=None):
+                       stream=None, align="prefix"):
     """One Falcon-3 / Falcon-3A decode step.  S [N,H,dv,dk] fp32, k_cache
     [N,H,W,dk] (slot w = k_{t-1-w}) and v_cache [N,H,W-1,dv] (slot w-1 =
     v_{t-w}; None when W = 1) are updated in place; q,k [N,H,dk], v [N,H,dv]
     (bf16 or fp32), alpha, eta [N,H] fp32.  Returns o [N,H,dv]."""
     import torch
-    var = _variant(variant)
+    var = _variant(variant, align)
     N, H, dv, dk = S.shape
     dev, dt = k.device, k.dtype
     dtc = _dt(k)

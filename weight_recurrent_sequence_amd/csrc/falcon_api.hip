@@ -26,14 +26,25 @@ int norm_of(int v) {
 
 bool is_delta(int v) { return v == FALCON_F1 || v == FALCON_F2 || v == FALCON_F3; }
 
+// The variant argument: a variant code, optionally OR-ed with FALCON_SAME_STEP.
+// Splits it into the code and the key lag (1: pair (k_{t-1}, v_t), 0: (k_t, v_t));
+// returns false for unknown flag bits.
+bool split_variant(int var, int* base, int* lag) {
+    if (var & ~(0xFF | FALCON_SAME_STEP)) return false;
+    *base = var & 0xFF;
+    *lag = (var & FALCON_SAME_STEP) ? 0 : 1;
+    return true;
+}
+
 bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 int check_chunk(const void* q, const void* k, const void* v, const float* alpha,
                 const float* eta, const float* S0, const void* k_prev, const void* v_prev,
                 const void* o, const float* S_final, int B, int H, int T, int dk, int dv,
-                int dt, int var, int window, int chunk, float eps) {
-    if (!is_variant(var)) return FALCON_ERR_UNSUPPORTED;
+                int dt, int var_arg, int window, int chunk, float eps) {
+    int var = 0, lag = 1;
+    if (!split_variant(var_arg, &var, &lag) || !is_variant(var)) return FALCON_ERR_UNSUPPORTED;
     if (dt != FALCON_FP32 && dt != FALCON_BF16) return FALCON_ERR_UNSUPPORTED;
     if (B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1) return FALCON_ERR_SHAPE;
     if ((long long)B * H > (1LL << 28) || (long long)T * dk > (1LL << 40)) return FALCON_ERR_SHAPE;
@@ -65,8 +76,10 @@ size_t falcon_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, falcon_dt
     if (check_chunk(p, p, p, (const float*)p, (const float*)p, nullptr, nullptr, nullptr, p,
                     nullptr, B, H, T, dk, dv, dt, var, window, chunk, 0.0f) != FALCON_OK)
         return 0;
-    return falcon::chunk_workspace_bytes(B * H, T, (int)dt, chunk, window, norm_of(var),
-                                         is_delta(var));
+    int base = 0, lag = 1;
+    split_variant(var, &base, &lag);
+    return falcon::chunk_workspace_bytes(B * H, T, (int)dt, chunk, window, norm_of(base),
+                                         is_delta(base));
 }
 
 int falcon_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
@@ -80,6 +93,8 @@ int falcon_chunk_fwd(const void* q, const void* k, const void* v, const float* a
     const size_t need = falcon_chunk_fwd_workspace(B, H, T, dk, dv, dt, var, window, chunk);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FALCON_ERR_WORKSPACE;
     if (T == 0 && S_final == nullptr) return FALCON_OK;
+    int base = 0, lag = 1;
+    split_variant(var, &base, &lag);
     falcon::ChunkArgs a;
     a.q = q;
     a.k = k;
@@ -94,17 +109,19 @@ int falcon_chunk_fwd(const void* q, const void* k, const void* v, const float* a
     a.BH = B * H;
     a.T = T;
     a.W = window;
-    a.norm = norm_of(var);
+    a.lag = lag;
+    a.norm = norm_of(base);
     a.eps = eps;
-    hipError_t e = falcon::launch_chunk(a, (int)dt, dk, chunk, is_delta(var), workspace, stream);
+    hipError_t e = falcon::launch_chunk(a, (int)dt, dk, chunk, is_delta(base), workspace, stream);
     return e == hipSuccess ? FALCON_OK : FALCON_ERR_HIP;
 }
 
 int falcon_decode_step(float* S, void* k_cache, const void* q, const void* k, const void* v,
                        const float* alpha, const float* eta, void* o, int N, int H, int dk,
-                       int dv, falcon_dtype dt, falcon_variant var, int window, float eps,
+                       int dv, falcon_dtype dt, falcon_variant var_arg, int window, float eps,
                        hipStream_t stream) {
-    if (!is_variant(var)) return FALCON_ERR_UNSUPPORTED;
+    int var = 0, lag = 1;
+    if (!split_variant(var_arg, &var, &lag) || !is_variant(var)) return FALCON_ERR_UNSUPPORTED;
     // the window rules have their own entry point, falcon_decode_step_window
     if (var == FALCON_F3 || var == FALCON_F3A) return FALCON_ERR_UNSUPPORTED;
     if (dt != FALCON_FP32 && dt != FALCON_BF16) return FALCON_ERR_UNSUPPORTED;
@@ -127,6 +144,7 @@ int falcon_decode_step(float* S, void* k_cache, const void* q, const void* k, co
     a.NH = N * H;
     a.norm = norm_of(var);
     a.delta = is_delta(var) ? 1 : 0;
+    a.lag = lag;
     a.eps = eps;
     hipError_t e = falcon::launch_decode(a, (int)dt, dk, stream);
     return e == hipSuccess ? FALCON_OK : FALCON_ERR_HIP;
@@ -135,8 +153,10 @@ int falcon_decode_step(float* S, void* k_cache, const void* q, const void* k, co
 int falcon_decode_step_window(float* S, void* k_cache, void* v_cache, const void* q,
                               const void* k, const void* v, const float* alpha,
                               const float* eta, void* o, int N, int H, int dk, int dv,
-                              falcon_dtype dt, falcon_variant var, int window, float eps,
+                              falcon_dtype dt, falcon_variant var_arg, int window, float eps,
                               hipStream_t stream) {
+    int var = 0, lag = 1;
+    if (!split_variant(var_arg, &var, &lag)) return FALCON_ERR_UNSUPPORTED;
     if (var != FALCON_F3 && var != FALCON_F3A) return FALCON_ERR_UNSUPPORTED;
     if (dt != FALCON_FP32 && dt != FALCON_BF16) return FALCON_ERR_UNSUPPORTED;
     if (N < 1 || H < 1 || dk < 1 || dv < 1 || window < 1) return FALCON_ERR_SHAPE;
@@ -160,6 +180,7 @@ int falcon_decode_step_window(float* S, void* k_cache, void* v_cache, const void
     a.NH = N * H;
     a.W = window;
     a.delta = var == FALCON_F3 ? 1 : 0;
+    a.lag = lag;
     a.eps = eps;
     hipError_t e = falcon::launch_decode_window(a, (int)dt, dk, stream);
     return e == hipSuccess ? FALCON_OK : FALCON_ERR_HIP;

@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a, void* ws, 
         if (c < CV * CPR) {
             const int i = c / CPR, col = (c % CPR) * EPC;
             const int s = WIN ? i / Wv : i, w = WIN ? i - s * Wv : 0;
-            const int t = t0 + s, tau = t - w - 1;  // x_i = k_{t-w-1}
+            const int t = t0 + s, tau = t - w - a.lag;  // x_i = k_{t-w-lag}
             const bool okx = i < NVR && t < T_ && (tau >= 0 || kp != nullptr);
             const T* px = tau >= 0 ? kg + (size_t)tau * D + col
                                    : (kp ? kp + (size_t)(W + tau) * D + col : kg + col);
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs a, const void
         xcol[it] = (c % CPR) * EPC;
         const int s = WIN ? xi[it] / Wv : xi[it];
         xs[it] = (tid + 256 * it < CV * CPR && xi[it] < NVR) ? s : (1 << 28);  // never valid
-        xoff[it] = s - (WIN ? xi[it] - s * Wv : 0) - 1;  // key index - t0
+        xoff[it] = s - (WIN ? xi[it] - s * Wv : 0) - a.lag;  // key index - t0
     }
 #pragma unroll
     for (int it = 0; it < NYL; ++it) {
@@ -802,7 +802,7 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
     // ---- output: staging geometry, fixed across tiles ----
     const int otid = tid & 255;  // index within the output or fill role
     // Each 16-byte piece a stager moves: its row relative to the tile start
-    // (key x_i = k_{t0 + s - w - 1}, target y_i = v_{t0 + s - w}), its byte
+    // (key x_i = k_{t0 + s - w - lag}, target y_i = v_{t0 + s - w}), its byte
     // column, and whether it exists.  Loads choose addresses, never data:
     // rows outside the sequence read as zero (descriptor bounds), halo rows
     // come from a second load that is merged when the piece is stored.
@@ -815,7 +815,7 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
         const int i = c / CPR, col = (c % CPR) * 8;
         const int s = WIN ? i / Wv : i, w = WIN ? i - s * Wv : 0;
         xok[it] = c < CV * CPR && i < NVR;
-        xrel[it] = s - w - 1;
+        xrel[it] = s - w - a.lag;
         xcb[it] = (uint32_t)col * 2;
         qvo[it] = (c < CV * CPR && i < Ct) ? (uint32_t)((i * D + col) * 2) : kOob;
     }
@@ -1160,7 +1160,7 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
             const int row = k / SPX, wi = k - row * SPX;
             const int s = WIN ? row / Wv : row, w = WIN ? row - s * Wv : 0;
             const bool in = k < NSX && wi < D / 8;
-            dx[m] = (in && row < NVR) ? (uint32_t)(((s - w - 1 + W) * D + wi * 8) * 2) : kOob;
+            dx[m] = (in && row < NVR) ? (uint32_t)(((s - w - a.lag + W) * D + wi * 8) * 2) : kOob;
             dq[m] = (in && row < Ct) ? (uint32_t)((row * D + wi * 8) * 2) : kOob;
         }
 #pragma unroll
@@ -1411,7 +1411,7 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
     const float eps = a.eps;
 
     // staging geometry, fixed across tiles: each 16-byte piece's key row
-    // relative to the tile start (x_i = k_{t0 + s - w - 1}), byte column and
+    // relative to the tile start (x_i = k_{t0 + s - w - lag}), byte column and
     // existence.  Loads choose addresses, never data, so no load is waited
     // for before the next tile is staged: rows outside the sequence read as
     // zero (descriptor bounds) and halo rows come from a second load.
@@ -1424,7 +1424,7 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
         const int i = c / CPR, col = (c % CPR) * 8;
         const int s = WIN ? i / Wv : i, w = WIN ? i - s * Wv : 0;
         xok[it] = c < CV * CPR && i < NVR;
-        xrel[it] = s - w - 1;
+        xrel[it] = s - w - a.lag;
         xcb[it] = (uint32_t)col * 2;
         qvo[it] = (c < CV * CPR && i < Ct) ? (uint32_t)((i * D + col) * 2) : kOob;
     }

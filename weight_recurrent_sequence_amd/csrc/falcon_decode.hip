@@ -6,7 +6,7 @@
 // write; KLA abstract: normalized step, decay then delta write), for
 // Falcon-1/1A (u = eta x / (||x||^2 + eps)) and Falcon-2/2A (per-column
 // normalizer u_j = eta x_j / (|x_j| ||x||_1 + eps)):
-//     x = k_cache,  S' = alpha S,  r = v - S'x  (A forms: r = v)
+//     x = k_cache (same-step pairs: x = k),  S' = alpha S,  r = v - S'x  (A forms: r = v)
 //     S = S' + r u^T,  o = S q = alpha S q + (u . q) r,  k_cache <- k
 // S is read once and written once: Sx and Sq come from the same pass over
 // the registers, and o is formed without a second read of S.
@@ -50,11 +50,12 @@ __global__ __launch_bounds__(256, 2) void decode_step_kernel(DecodeArgs a) {
     for (int p = 0; p < RPT; ++p) vraw[p] = vh[row0 + ROWS_PER_PASS * p];
 
     // columns of this lane: 4*seg + 4*LPR*j + e, j, e in 0..3
+    const T* xh = a.lag ? kc : kh;
     float x[16], qv[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int c = 4 * seg + 4 * LPR * j;
-        const typename E::Frag xf = E::load(kc + c), qf = E::load(qh + c);
+        const typename E::Frag xf = E::load(xh + c), qf = E::load(qh + c);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             x[4 * j + e] = E::to_f((T)xf[e]);
@@ -155,7 +156,8 @@ namespace falcon {
 // ---------------------------------------------------------------------------
 // Falcon-3 / Falcon-3A decode step: a window of W prefix-aligned pairs
 // ("Fast Weight Attention for Continual Learning", authors' abstract: the
-// sliding-window mini-batch variant).  With x_w = k_{t-1-w} (k_cache slot w)
+// sliding-window mini-batch variant).  With x_w = k_{t-1-w} (k_cache slot w;
+// same-step pairs: x_w = k_{t-w}, the new key for w = 0 and slot w-1 after)
 // and y_w = v_{t-w} (y_0 = v, y_w = v_cache slot w-1):
 //     S' = alpha S,  b = eta / (sum_w ||x_w||^2 + eps)
 //     S  = S' + b sum_w r_w x_w^T,  r_w = y_w - S' x_w  (3A: r_w = y_w)
@@ -208,7 +210,8 @@ __global__ __launch_bounds__(256, 2) void decode_window_kernel(DecodeWinArgs a) 
         for (int e = 0; e < 4; ++e) qv[4 * j + e] = E::to_f((T)qf[e]);
 #pragma unroll
         for (int w = 0; w < W; ++w) {
-            const typename E::Frag xf = E::load(kc + (size_t)w * D + c);
+            const T* xw = (w + a.lag == 0) ? kh : kc + (size_t)(w + a.lag - 1) * D;
+            const typename E::Frag xf = E::load(xw + c);
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[w][4 * j + e] = E::to_f((T)xf[e]);
         }

@@ -27,6 +27,7 @@ struct ChunkArgs {
     int BH;      // batch * heads
     int T;
     int W;       // window (1 unless kNormWindow)
+    int lag;     // key of step t's pair w is k_{t-w-lag}: 1 prefix-aligned, 0 same-step
     int norm;    // NormKind
     float eps;
 };
@@ -43,6 +44,7 @@ struct DecodeArgs {
     int NH;      // sequences * heads
     int norm;    // kNormScalar or kNormColumn
     int delta;   // 1: regression (residual write), 0: inner-product write
+    int lag;     // 1: x = k_cache (prefix-aligned), 0: x = k (same-step)
     float eps;
 };
 
@@ -59,6 +61,7 @@ struct DecodeWinArgs {
     int NH;
     int W;
     int delta;   // 1: Falcon-3 (residual writes), 0: Falcon-3A
+    int lag;     // pair w's key is k_{t-w-lag}: slot w+lag-1 of k_cache, or k when w+lag = 0
     float eps;
 };
 
