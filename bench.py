@@ -7,8 +7,9 @@ H=16, T=4096, d_k=d_v=128, bf16 q/k/v, fp32 state, chunk 64, with the inputs
 resident in HBM: the intra-chunk kernel (norms, decay scan, masked Gram
 blocks, diagonal-block inverses) and the state-passing kernel (residuals,
 blocked forward substitution, outputs, state update).  `value` is tokens
-(B*T) per second.  The same line reports Falcon-1A on the same batch and the
-decode step (256 sequences x 32 heads, d=128, 1024 consecutive steps) and the
+(B*T) per second.  The same line reports Falcon-1A on the same batch,
+Falcon-1 with same-step pairs (k_t, v_t), the decode step (256 sequences x
+32 heads, d=128, 1024 consecutive steps) and the
 Falcon-3 decode step at the same shape with a window of four, each with its
 roofline, and the fp64 CPU oracle timed on this host over a bounded sample of
 the Falcon-1 workload.
@@ -188,6 +189,14 @@ def main():
     ms_a, _ = timed(step_f1a, args.steps, args.warmup)
     gbs_a = nbytes / (ms_a / 1e3) / 1e9
 
+    def step_f1_same():
+        fal.chunk_fwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], "F1", chunk=C, o=o,
+                      S_final=S_fin, workspace=ws, align="same")
+
+    print(f"[bench] F1 same-step pairs", file=sys.stderr, flush=True)
+    ms_s, _ = timed(step_f1_same, args.steps, args.warmup)
+    gbs_s = nbytes / (ms_s / 1e3) / 1e9
+
     line = {
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -206,6 +215,9 @@ def main():
         "falcon1a": {"tokens_per_s": B * T / (ms_a / 1e3), "ms_per_step": ms_a,
                      "hbm_gbs": gbs_a, "hbm_frac": gbs_a / HBM_PEAK_GBS,
                      "traffic": measured_traffic("chunk_fwd_F1A_B8H16T4096d128_bf16_c64")},
+        "falcon1_same_step": {"tokens_per_s": B * T / (ms_s / 1e3), "ms_per_step": ms_s,
+                              "hbm_gbs": gbs_s, "hbm_frac": gbs_s / HBM_PEAK_GBS,
+                              "pairs": "(k_t, v_t), FALCON_SAME_STEP"},
     }
 
     if not args.no_decode:
