@@ -14,6 +14,11 @@ Falcon-3 decode step at the same shape with a window of four, each with its
 roofline, and the fp64 CPU oracle timed on this host over a bounded sample of
 the Falcon-1 workload.
 
+Before the first timed region, untimed Falcon-1 calls run for 0.3 s so the
+device's clocks reach their sustained state (a fresh process otherwise times
+its first ~100 calls up to 10% slow); every region then does its own
+--warmup steps.
+
 roofline.achieved is the algorithmic HBM bytes of one call (q, k, v, o once,
 alpha, eta, final state) over the call's HIP-event time on the launch
 stream; roofline.traffic is the HBM bytes the PMC counters measured for the
@@ -32,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "Falcon-1 chunk fwd tokens/s (B8 H16 T4096 d128) + decode tok/s; % roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+SETTLE_S = 0.3               # untimed calls before the first timed region
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 
 
@@ -177,8 +183,19 @@ def main():
         fal.chunk_fwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], "F1A", chunk=C, o=o,
                       S_final=S_fin, workspace=ws)
 
-    print(f"[bench] chunk_fwd F1 {name}: warmup {args.warmup}, steps {args.steps}",
-          file=sys.stderr, flush=True)
+    # Clocks settle: in a fresh process the first ~100 calls run up to 10%
+    # slower while the device ramps to its sustained state, so untimed calls
+    # run for at least SETTLE_S before the first warm-up of the first timed
+    # region (each region then does its own `--warmup` steps).
+    t_end = time.perf_counter() + SETTLE_S
+    n_settle = 0
+    while time.perf_counter() < t_end or n_settle < 20:
+        for _ in range(10):
+            step_f1()
+        torch.cuda.synchronize()
+        n_settle += 10
+    print(f"[bench] chunk_fwd F1 {name}: settle {n_settle} calls, warmup {args.warmup}, "
+          f"steps {args.steps}", file=sys.stderr, flush=True)
     ms, wall = timed(step_f1, args.steps, args.warmup)
     tok_s = B * T / (ms / 1e3)
     nbytes = chunk_bytes(B, H, T, D)
