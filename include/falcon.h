@@ -127,6 +127,41 @@ int falcon_chunk_fwd(const void* q, const void* k, const void* v, const float* a
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Chunk-parallel forward over N packed sequences of different lengths.  Each
+ * head's plane holds the sequences back to back; the recurrence restarts at
+ * every boundary, so the result equals one falcon_chunk_fwd call per
+ * sequence.
+ *
+ *   q, k        [H,total_T,dk]  dtype dt
+ *   v           [H,total_T,dv]  dtype dt
+ *   alpha, eta  [H,total_T]     fp32
+ *   cu_seqlens  [N+1] int32, device memory: sequence n covers rows
+ *               cu_seqlens[n] .. cu_seqlens[n+1]-1 of every head's plane
+ *               (non-decreasing, cu_seqlens[N] <= total_T, every length
+ *               <= max_seqlen).  The device clamps offsets outside this
+ *               contract so that no access leaves the buffers; the results
+ *               for such offsets are unspecified.
+ *   S0, S_final [N,H,dv,dk]  fp32 or NULL, per sequence (as in falcon_chunk_fwd)
+ *   k_prev      [N,H,W,dk], v_prev [N,H,W-1,dv], or NULL: per-sequence halos
+ *   o           [H,total_T,dv] dtype dt; rows outside every sequence are not
+ *               written
+ *   workspace   falcon_chunk_fwd_varlen_workspace(...) bytes (it grows with
+ *               N * H * max_seqlen)
+ *
+ * Everything else (variants, FALCON_SAME_STEP, window, chunk, eps, support
+ * matrix, errors) is as for falcon_chunk_fwd.
+ */
+size_t falcon_chunk_fwd_varlen_workspace(int N, int H, int max_seqlen, int dk, int dv,
+                                         falcon_dtype dt, falcon_variant var, int window,
+                                         int chunk);
+int falcon_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* alpha,
+                            const float* eta, const float* S0, const void* k_prev,
+                            const void* v_prev, void* o, float* S_final, const int* cu_seqlens,
+                            int N, int H, int total_T, int max_seqlen, int dk, int dv,
+                            falcon_dtype dt, falcon_variant var, int window, int chunk, float eps,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * One decode step for N independent sequences x H heads (one token each):
  * x = k_cache (the previous key; with FALCON_SAME_STEP the new key k),
  * S' = alpha S, write as above, o = S q, then k_cache <- k.

@@ -28,6 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["falcon_chunk_fwd", "falcon_chunk_fwd_workspace",
+                                           "falcon_chunk_fwd_varlen",
+                                           "falcon_chunk_fwd_varlen_workspace",
                                            "falcon_decode_step", "falcon_decode_step_window",
                                            "falcon_status_string"])
 
@@ -163,3 +165,32 @@ def test_same_step_flag_keeps_the_workspace_size(L):
         a = L.falcon_chunk_fwd_workspace(2, 3, 1000, 128, 128, 1, var, W, 64)
         b = L.falcon_chunk_fwd_workspace(2, 3, 1000, 128, 128, 1, var | 0x100, W, 64)
         assert a == b and a > 0
+
+
+def varlen(L, **kw):
+    a = dict(q=P, k=P, v=P, alpha=P, eta=P, S0=None, k_prev=None, v_prev=None, o=P, S_final=P,
+             cu=P, N=3, H=4, Ttot=300, maxT=150, dk=128, dv=128, dt=1, var=1, window=1,
+             chunk=64, eps=1e-6)
+    a.update(kw)
+    return L.falcon_chunk_fwd_varlen(a["q"], a["k"], a["v"], a["alpha"], a["eta"], a["S0"],
+                                     a["k_prev"], a["v_prev"], a["o"], a["S_final"], a["cu"],
+                                     a["N"], a["H"], a["Ttot"], a["maxT"], a["dk"], a["dv"],
+                                     a["dt"], a["var"], a["window"], a["chunk"],
+                                     ctypes.c_float(a["eps"]), None, 0, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=None), -1), (dict(cu=P + 2), -3), (dict(N=0), -2), (dict(H=0), -2),
+    (dict(Ttot=-1), -2), (dict(maxT=-1), -2), (dict(var=4), -3), (dict(window=2), -2),
+    (dict(dk=96, dv=96), -3), (dict(q=None), -1), (dict(o=None), -1), (dict(eps=-1.0), -2),
+    (dict(), -4),                                                   # no workspace given
+])
+def test_varlen_rejects(L, kw, code):
+    assert varlen(L, **kw) == code
+
+
+def test_varlen_workspace_matches_batched_layout(L):
+    """Records are per (sequence, head) with the longest sequence's tile count."""
+    a = L.falcon_chunk_fwd_varlen_workspace(3, 4, 150, 128, 128, 1, 1, 1, 64)
+    b = L.falcon_chunk_fwd_workspace(3, 4, 150, 128, 128, 1, 1, 1, 64)
+    assert a == b > 0

@@ -21,7 +21,8 @@ ALIGN = {"prefix": 0, "same": SAME_STEP}
 FP32, BF16 = 0, 1
 STATUS = {0: "FALCON_OK", -1: "FALCON_ERR_NULL", -2: "FALCON_ERR_SHAPE",
           -3: "FALCON_ERR_UNSUPPORTED", -4: "FALCON_ERR_WORKSPACE", -5: "FALCON_ERR_HIP"}
-EXPORTS = ("falcon_chunk_fwd_workspace", "falcon_chunk_fwd", "falcon_decode_step",
+EXPORTS = ("falcon_chunk_fwd_workspace", "falcon_chunk_fwd", "falcon_chunk_fwd_varlen_workspace",
+           "falcon_chunk_fwd_varlen", "falcon_decode_step",
            "falcon_decode_step_window", "falcon_status_string")
 
 
@@ -48,6 +49,10 @@ def lib():
         L.falcon_chunk_fwd_workspace.argtypes = [ci] * 9
         L.falcon_chunk_fwd.restype = ci
         L.falcon_chunk_fwd.argtypes = [vp] * 10 + [ci] * 9 + [cf, vp, sz, vp]
+        L.falcon_chunk_fwd_varlen_workspace.restype = sz
+        L.falcon_chunk_fwd_varlen_workspace.argtypes = [ci] * 9
+        L.falcon_chunk_fwd_varlen.restype = ci
+        L.falcon_chunk_fwd_varlen.argtypes = [vp] * 11 + [ci] * 10 + [cf, vp, sz, vp]
         L.falcon_decode_step.restype = ci
         L.falcon_decode_step.argtypes = [vp] * 8 + [ci] * 7 + [cf, vp]
         L.falcon_decode_step_window.restype = ci
@@ -151,6 +156,69 @@ def chunk_fwd(q, k, v, alpha, eta, variant, *, window=1, chunk=64, eps=1e-6, S0=
                                 _stream(stream))
     if st != 0:
         raise FalconError(st, "falcon_chunk_fwd")
+    return o, S_final
+
+
+def varlen_workspace_bytes(N, H, max_seqlen, dk, dv, dtype, variant, window=1, chunk=64) -> int:
+    return int(lib().falcon_chunk_fwd_varlen_workspace(N, H, max_seqlen, dk, dv, dtype,
+                                                       _variant(variant), window, chunk))
+
+
+def chunk_fwd_varlen(q, k, v, alpha, eta, cu_seqlens, variant, *, max_seqlen=None, window=1,
+                     chunk=64, eps=1e-6, S0=None, k_prev=None, v_prev=None, o=None,
+                     S_final=None, return_state=True, workspace=None, stream=None,
+                     align="prefix"):
+    """Chunk-parallel forward over N packed sequences.  q, k [H,total_T,dk];
+    v [H,total_T,dv]; alpha, eta [H,total_T] fp32; cu_seqlens int32 [N+1] on
+    the device (sequence n = rows cu_seqlens[n] .. cu_seqlens[n+1]-1 of every
+    head); S0 [N,H,dv,dk]; k_prev [N,H,W,dk]; v_prev [N,H,W-1,dv].
+    max_seqlen bounds every sequence's length; when None it is read from
+    cu_seqlens (a device-to-host copy, which synchronizes).  Returns
+    (o [H,total_T,dv], S_final [N,H,dv,dk] or None)."""
+    import torch
+    var = _variant(variant, align)
+    H, Ttot, dk = k.shape
+    dv = v.shape[-1]
+    dev, dt = k.device, k.dtype
+    dtc = _dt(k)
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != dev \
+            or not cu_seqlens.is_contiguous() or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens: int32 [N+1] contiguous tensor on the inputs' device")
+    N = cu_seqlens.numel() - 1
+    if max_seqlen is None:
+        c = cu_seqlens.cpu()
+        max_seqlen = int((c[1:] - c[:-1]).max().item()) if N > 0 else 0
+    _check(q, "q", (H, Ttot, dk), dt, dev)
+    _check(k, "k", (H, Ttot, dk), dt, dev)
+    _check(v, "v", (H, Ttot, dv), dt, dev)
+    _check(alpha, "alpha", (H, Ttot), torch.float32, dev)
+    _check(eta, "eta", (H, Ttot), torch.float32, dev)
+    _check(S0, "S0", (N, H, dv, dk), torch.float32, dev)
+    _check(k_prev, "k_prev", (N, H, window, dk), dt, dev)
+    if window > 1:
+        _check(v_prev, "v_prev", (N, H, window - 1, dv), dt, dev)
+    else:
+        v_prev = None
+    if o is None:
+        o = torch.empty((H, Ttot, dv), dtype=dt, device=dev)
+    _check(o, "o", (H, Ttot, dv), dt, dev)
+    if S_final is None and return_state:
+        S_final = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
+    _check(S_final, "S_final", (N, H, dv, dk), torch.float32, dev)
+    ws_n = varlen_workspace_bytes(N, H, max_seqlen, dk, dv, dtc, var, window, chunk)
+    if workspace is not None:
+        if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_n:
+            raise ValueError(f"workspace: need {ws_n} bytes on {dev}")
+        ws, ws_n = workspace, workspace.numel() * workspace.element_size()
+    else:
+        ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n > 0 else None
+    st = lib().falcon_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta),
+                                       _ptr(S0), _ptr(k_prev), _ptr(v_prev), _ptr(o),
+                                       _ptr(S_final), _ptr(cu_seqlens), N, H, Ttot, max_seqlen,
+                                       dk, dv, dtc, var, window, chunk, float(eps), _ptr(ws),
+                                       ws_n, _stream(stream))
+    if st != 0:
+        raise FalconError(st, "falcon_chunk_fwd_varlen")
     return o, S_final
 
 

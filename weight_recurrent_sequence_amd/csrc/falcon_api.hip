@@ -108,6 +108,61 @@ int falcon_chunk_fwd(const void* q, const void* k, const void* v, const float* a
     a.S_final = S_final;
     a.BH = B * H;
     a.T = T;
+    a.cu = nullptr;
+    a.H = H;
+    a.Ttot = T;
+    a.W = window;
+    a.lag = lag;
+    a.norm = norm_of(base);
+    a.eps = eps;
+    hipError_t e = falcon::launch_chunk(a, (int)dt, dk, chunk, is_delta(base), workspace, stream);
+    return e == hipSuccess ? FALCON_OK : FALCON_ERR_HIP;
+}
+
+size_t falcon_chunk_fwd_varlen_workspace(int N, int H, int max_seqlen, int dk, int dv,
+                                         falcon_dtype dt, falcon_variant var, int window,
+                                         int chunk) {
+    // the records are laid out per (sequence, head) with the longest sequence's tile count
+    return falcon_chunk_fwd_workspace(N, H, max_seqlen, dk, dv, dt, var, window, chunk);
+}
+
+int falcon_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* alpha,
+                            const float* eta, const float* S0, const void* k_prev,
+                            const void* v_prev, void* o, float* S_final, const int* cu_seqlens,
+                            int N, int H, int total_T, int max_seqlen, int dk, int dv,
+                            falcon_dtype dt, falcon_variant var, int window, int chunk, float eps,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    // per-sequence checks as for N sequences of max_seqlen steps
+    int st = check_chunk(q, k, v, alpha, eta, S0, k_prev, v_prev, o, S_final, N, H, max_seqlen,
+                         dk, dv, dt, var, window, chunk, eps);
+    if (st != FALCON_OK) return st;
+    if (total_T < 0 || (long long)H * total_T > (1LL << 40) / (dk > 0 ? dk : 1))
+        return FALCON_ERR_SHAPE;
+    if (!cu_seqlens || !aligned4(cu_seqlens)) return cu_seqlens ? FALCON_ERR_UNSUPPORTED : FALCON_ERR_NULL;
+    if (total_T > 0 && max_seqlen > 0 && (!q || !k || !v || !alpha || !eta || !o))
+        return FALCON_ERR_NULL;
+    const size_t need = falcon_chunk_fwd_varlen_workspace(N, H, max_seqlen, dk, dv, dt, var,
+                                                          window, chunk);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FALCON_ERR_WORKSPACE;
+    if ((max_seqlen == 0 || total_T == 0) && S_final == nullptr) return FALCON_OK;
+    int base = 0, lag = 1;
+    split_variant(var, &base, &lag);
+    falcon::ChunkArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = alpha;
+    a.eta = eta;
+    a.S0 = S0;
+    a.k_prev = k_prev;
+    a.v_prev = v_prev;
+    a.o = o;
+    a.S_final = S_final;
+    a.BH = N * H;
+    a.T = total_T == 0 ? 0 : max_seqlen;
+    a.cu = cu_seqlens;
+    a.H = H;
+    a.Ttot = total_T;
     a.W = window;
     a.lag = lag;
     a.norm = norm_of(base);

@@ -72,7 +72,23 @@ struct Rec {
     static constexpr int npblk(bool win) { return win ? 2 * NB : NB * (NB + 1) / 2; }
 };
 
-static inline int tiles_of(int T, int Ct) { return (T + Ct - 1) / Ct; }
+__host__ __device__ inline int tiles_of(int T, int Ct) { return (T + Ct - 1) / Ct; }
+
+// Rows of sequence bh in the [rows, d] planes: [row0, row0 + T).  Batched
+// calls: row0 = bh * T.  Packed calls: the bounds come from cu, clamped to the
+// plane and to the longest sequence allowed, so offsets outside the contract
+// cannot move any access out of the buffers.
+struct SeqRows {
+    size_t row0;
+    int T;
+};
+__device__ __forceinline__ SeqRows seq_rows(const ChunkArgs& a, int bh) {
+    if (!a.cu) return {(size_t)bh * a.T, a.T};
+    const int n = bh / a.H, h = bh - n * a.H;
+    const int s0 = min(max(a.cu[n], 0), a.Ttot);
+    const int s1 = min(min(max(a.cu[n + 1], s0), a.Ttot), s0 + a.T);
+    return {(size_t)h * a.Ttot + s0, s1 - s0};
+}
 
 
 __device__ __forceinline__ u32x4 sel16(bool ok, u32x4 v) {
@@ -118,11 +134,12 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a, void* ws, 
     const int W = a.W;
     const int Wv = WIN ? W : 1;
     const int Ct = CV / Wv, NVR = Ct * Wv, NBQ = (Ct + 15) / 16;
-    const int T_ = a.T;
+    const SeqRows sr = seq_rows(a, bh);
+    const int T_ = sr.T;
     const int t0 = tile * Ct;
     const float eps = a.eps;
-    const T* qg = static_cast<const T*>(a.q) + (size_t)bh * T_ * D;
-    const T* kg = static_cast<const T*>(a.k) + (size_t)bh * T_ * D;
+    const T* qg = static_cast<const T*>(a.q) + sr.row0 * D;
+    const T* kg = static_cast<const T*>(a.k) + sr.row0 * D;
     const T* kp = a.k_prev ? static_cast<const T*>(a.k_prev) + (size_t)bh * W * D : nullptr;
     char* rec = static_cast<char*>(ws) + ((size_t)bh * ntiles + tile) * R::kBytes;
     T* recT = reinterpret_cast<T*>(rec);
@@ -150,8 +167,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a, void* ws, 
     if (tid < CV) {
         const int t = t0 + tid;
         const bool ok = tid < Ct && t < T_;
-        sm.alpha[tid] = ok ? a.alpha[(size_t)bh * T_ + t] : 1.f;  // padding steps: identity
-        sm.eta[tid] = ok ? a.eta[(size_t)bh * T_ + t] : 0.f;
+        sm.alpha[tid] = ok ? a.alpha[sr.row0 + t] : 1.f;  // padding steps: identity
+        sm.eta[tid] = ok ? a.eta[sr.row0 + t] : 0.f;
     }
     __syncthreads();
 
@@ -379,17 +396,18 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs a, const void
     const int W = a.W;
     const int Wv = WIN ? W : 1;
     const int Ct = CV / Wv, NVR = Ct * Wv, NBQ = (Ct + 15) / 16;
-    const int T_ = a.T;
+    const SeqRows sr = seq_rows(a, bh);
+    const int T_ = sr.T;
     const float eps = a.eps;
-    const T* qg = static_cast<const T*>(a.q) + (size_t)bh * T_ * D;
-    const T* kg = static_cast<const T*>(a.k) + (size_t)bh * T_ * D;
-    const T* vg = static_cast<const T*>(a.v) + (size_t)bh * T_ * D + v0;
+    const T* qg = static_cast<const T*>(a.q) + sr.row0 * D;
+    const T* kg = static_cast<const T*>(a.k) + sr.row0 * D;
+    const T* vg = static_cast<const T*>(a.v) + sr.row0 * D + v0;
     const T* kp = a.k_prev ? static_cast<const T*>(a.k_prev) + (size_t)bh * W * D : nullptr;
     const T* vp = (a.v_prev && W > 1)
                       ? static_cast<const T*>(a.v_prev) + (size_t)bh * (W - 1) * D + v0
                       : nullptr;
     const char* recg = static_cast<const char*>(ws) + (size_t)bh * ntiles * R::kBytes;
-    T* og = static_cast<T*>(a.o) + (size_t)bh * T_ * D + v0;
+    T* og = static_cast<T*>(a.o) + sr.row0 * D + v0;
 
     // State slice as accumulators of S^T: Sacc[kb][r] = S[v][k],
     // v = v0 + 16*wave + lr, k = 16*kb + 4*grp + r.
@@ -489,7 +507,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs a, const void
         });
     };
 
-    const int ntl = ntiles;
+    const int ntl = tiles_of(T_, Ct);  // this sequence's tiles (ntiles: the record stride)
     if (ntl > 0) load_tile(0);
     for (int tile = 0; tile < ntl; ++tile) {
         const int t0 = tile * Ct;
@@ -776,18 +794,19 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
     const int W = a.W;
     const int Wv = WIN ? W : 1;
     const int Ct = CV / Wv, NVR = Ct * Wv, NBQ = (Ct + 15) / 16;
-    const int T_ = a.T;
+    const SeqRows sr = seq_rows(a, bh);
+    const int T_ = sr.T;
     const float eps = a.eps;
-    const T* qg = static_cast<const T*>(a.q) + (size_t)bh * T_ * D;
-    const T* kg = static_cast<const T*>(a.k) + (size_t)bh * T_ * D;
-    const T* vg = static_cast<const T*>(a.v) + (size_t)bh * T_ * D + v0;
+    const T* qg = static_cast<const T*>(a.q) + sr.row0 * D;
+    const T* kg = static_cast<const T*>(a.k) + sr.row0 * D;
+    const T* vg = static_cast<const T*>(a.v) + sr.row0 * D + v0;
     const T* kp = a.k_prev ? static_cast<const T*>(a.k_prev) + (size_t)bh * W * D : nullptr;
     const T* vp = (a.v_prev && W > 1)
                       ? static_cast<const T*>(a.v_prev) + (size_t)bh * (W - 1) * D + v0
                       : nullptr;
     const char* recg = static_cast<const char*>(ws) + (size_t)bh * ntiles * R::kBytes;
-    T* og = static_cast<T*>(a.o) + (size_t)bh * T_ * D + v0;
-    const int ntl = ntiles;
+    T* og = static_cast<T*>(a.o) + sr.row0 * D + v0;
+    const int ntl = tiles_of(T_, Ct);  // this sequence's tiles (ntiles: the record stride)
 
     // ---- chain: state slice as accumulators of S^T (wave cw owns 16 value
     // columns): Sacc[kb][r] = S[v][k], v = v0 + 16 cw + lr, k = 16 kb + 4 grp + r
@@ -1407,7 +1426,6 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
     const int W = a.W;
     const int Wv = WIN ? W : 1;
     const int Ct = CV / Wv, NVR = Ct * Wv, NBQ = (Ct + 15) / 16;
-    const int T_ = a.T;
     const float eps = a.eps;
 
     // staging geometry, fixed across tiles: each 16-byte piece's key row
@@ -1434,8 +1452,10 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
     auto load = [&](int job) __attribute__((always_inline)) {
         const int bh = job / ntiles, tile = job - bh * ntiles;
         const int t0 = tile * Ct;
-        const T* kg = static_cast<const T*>(a.k) + (size_t)bh * T_ * D;
-        const T* qg = static_cast<const T*>(a.q) + (size_t)bh * T_ * D;
+        const SeqRows sr = seq_rows(a, bh);
+        const int T_ = sr.T;
+        const T* kg = static_cast<const T*>(a.k) + sr.row0 * D;
+        const T* qg = static_cast<const T*>(a.q) + sr.row0 * D;
         const int bx = max(t0 - W, 0);
         const rsrc_t rx = make_rsrc(kg + (size_t)bx * D, (int64_t)(T_ - bx) * D * 2);
 #pragma unroll
@@ -1456,8 +1476,8 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
 #pragma unroll
         for (int it = 0; it < NXL; ++it) pq[it] = buf_load16(rq, qvo[it]);
         if (tid < CV) {
-            // clamped index, selected when staged
-            const size_t g = (size_t)bh * T_ + min(t0 + tid, T_ - 1);
+            // an index inside the gates whatever the tile, selected when staged
+            const size_t g = (t0 + tid < T_) ? sr.row0 + t0 + tid : 0;
             pal = a.alpha[g];
             pet = a.eta[g];
         }
@@ -1467,6 +1487,7 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
     if (job < njobs) load(job);
     for (; job < njobs; job += gridDim.x) {
         const int bh = job / ntiles, tile = job - bh * ntiles;
+        const int T_ = seq_rows(a, bh).T;  // tiles beyond it are identity padding, never read
         char* rec = static_cast<char*>(ws) + ((size_t)bh * ntiles + tile) * R::kBytes;
         T* recT = reinterpret_cast<T*>(rec);
         float* recS = reinterpret_cast<float*>(rec + R::kScalBytes);

@@ -24,8 +24,15 @@ struct ChunkArgs {
     const void* v_prev;
     void* o;
     float* S_final;
-    int BH;      // batch * heads
-    int T;
+    int BH;      // batch * heads (packed: sequences * heads)
+    int T;       // steps per sequence (packed: the longest sequence allowed)
+    // Packed sequences: q, k, v, o are [H, Ttot, d] and alpha, eta [H, Ttot];
+    // sequence n of head h covers rows cu[n] .. cu[n+1] of head h's plane and
+    // is "batch row" n * H + h for S0, S_final, k_prev, v_prev.  cu is NULL
+    // for the batched layout [B, H, T, d].
+    const int* cu;
+    int H;
+    int Ttot;
     int W;       // window (1 unless kNormWindow)
     int lag;     // key of step t's pair w is k_{t-w-lag}: 1 prefix-aligned, 0 same-step
     int norm;    // NormKind

@@ -195,6 +195,63 @@ class DecodeInputs:
         return np.asarray(a, dtype=np.float64)
 
 
+@dataclass
+class VarlenInputs:
+    """Packed sequences: q, k [H,Ttot,dk], v [H,Ttot,dv] (storage type), alpha,
+    eta [H,Ttot] float32, cu [N+1] int32 offsets, S0 [N,H,dv,dk] float32 or
+    None, k_prev [N,H,W,dk] / v_prev [N,H,W-1,dv] (storage type) or None."""
+    dtype: str
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    alpha: np.ndarray
+    eta: np.ndarray
+    cu: np.ndarray
+    window: int = 1
+    S0: np.ndarray | None = None
+    k_prev: np.ndarray | None = None
+    v_prev: np.ndarray | None = None
+
+    def sequence(self, n) -> ChunkInputs:
+        """Sequence n as a one-batch ChunkInputs (a view into the packed arrays)."""
+        a, b = int(self.cu[n]), int(self.cu[n + 1])
+        pick = lambda x: None if x is None else x[n:n + 1]  # noqa: E731
+        return ChunkInputs(self.dtype, self.q[None, :, a:b], self.k[None, :, a:b],
+                           self.v[None, :, a:b], self.alpha[None, :, a:b],
+                           self.eta[None, :, a:b], self.window, pick(self.S0),
+                           pick(self.k_prev), pick(self.v_prev))
+
+
+def make_varlen_inputs(lengths, H, dk, dv, *, dtype="bf16", seed=0, window=1, alpha_mu=3.0,
+                       alpha_sd=1.0, S0_sd=0.0, halo=False, tail=0) -> VarlenInputs:
+    """N sequences of the given lengths packed back to back in every head's
+    plane ([H, sum(lengths) + tail, d]; `tail` rows after the last sequence
+    belong to none).  Same distributions as make_chunk_inputs; children
+    spawned in the order q, k, v, alpha-logit, eta-logit, S0, k_prev, v_prev."""
+    lengths = [int(x) for x in lengths]
+    N, Ttot = len(lengths), sum(lengths) + tail
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    cq, ck, cv, ca, ce, cS, ckp, cvp = np.random.SeedSequence(seed).spawn(8)
+    g = lambda c: np.random.Generator(np.random.PCG64(c))  # noqa: E731
+    q = g(cq).standard_normal((H, Ttot, dk), dtype=np.float32)
+    k = g(ck).standard_normal((H, Ttot, dk), dtype=np.float32)
+    v = g(cv).standard_normal((H, Ttot, dv), dtype=np.float32)
+    alpha = sigmoid32(g(ca).normal(alpha_mu, alpha_sd, (H, Ttot)).astype(np.float32))
+    eta = sigmoid32(g(ce).normal(0.0, 1.0, (H, Ttot)).astype(np.float32))
+    S0 = None
+    if S0_sd > 0:
+        S0 = (g(cS).standard_normal((N, H, dv, dk), dtype=np.float32) * np.float32(S0_sd))
+        S0 = S0.astype(np.float32)
+    k_prev = v_prev = None
+    if halo:
+        k_prev = _store(g(ckp).standard_normal((N, H, window, dk), dtype=np.float32), dtype)
+        if window > 1:
+            v_prev = _store(g(cvp).standard_normal((N, H, window - 1, dv), dtype=np.float32),
+                            dtype)
+    return VarlenInputs(dtype, _store(q, dtype), _store(k, dtype), _store(v, dtype), alpha, eta,
+                        cu, window, S0, k_prev, v_prev)
+
+
 def make_decode_inputs(N, H, dk, dv, steps, *, dtype="bf16", seed=1005, alpha_mu=3.0,
                        alpha_sd=1.0, S0_sd=0.02, window=1) -> DecodeInputs:
     ss = np.random.SeedSequence(seed)
