@@ -8,7 +8,8 @@ resident in HBM: the intra-chunk kernel (norms, decay scan, masked Gram
 blocks, diagonal-block inverses) and the state-passing kernel (residuals,
 blocked forward substitution, outputs, state update).  `value` is tokens
 (B*T) per second.  The same line reports Falcon-1A on the same batch,
-Falcon-1 with same-step pairs (k_t, v_t), the decode step (256 sequences x
+Falcon-1 with same-step pairs (k_t, v_t), Falcon-1 over 16 packed sequences
+of mixed lengths with the same token count, the decode step (256 sequences x
 32 heads, d=128, 1024 consecutive steps) and the
 Falcon-3 decode step at the same shape with a window of four, each with its
 roofline, and the fp64 CPU oracle timed on this host over a bounded sample of
@@ -214,6 +215,30 @@ def main():
     ms_s, _ = timed(step_f1_same, args.steps, args.warmup)
     gbs_s = nbytes / (ms_s / 1e3) / 1e9
 
+    # Falcon-1 over a packed batch of 16 sequences of mixed lengths with the
+    # same 32768 tokens per head (falcon_chunk_fwd_varlen)
+    rl = __import__("numpy").random.default_rng(5)
+    lengths = rl.integers(256, 3840, 15).tolist()
+    lengths.append(B * T - sum(lengths))
+    vi = I.make_varlen_inputs(lengths, H, D, D, dtype="bf16", seed=980)
+    tv = {n: torch.from_numpy(getattr(vi, n)).view(torch.bfloat16).to(dev) for n in ("q", "k", "v")}
+    av, ev = torch.from_numpy(vi.alpha).to(dev), torch.from_numpy(vi.eta).to(dev)
+    cu = torch.from_numpy(vi.cu).to(dev)
+    maxT = max(lengths)
+    ov = torch.empty_like(tv["v"])
+    Sv = torch.empty((len(lengths), H, D, D), dtype=torch.float32, device=dev)
+    wsv = torch.empty(fal.varlen_workspace_bytes(len(lengths), H, maxT, D, D, fal.BF16, "F1", 1, C),
+                      dtype=torch.uint8, device=dev)
+
+    def step_varlen():
+        fal.chunk_fwd_varlen(tv["q"], tv["k"], tv["v"], av, ev, cu, "F1", max_seqlen=maxT, chunk=C,
+                             o=ov, S_final=Sv, workspace=wsv)
+
+    print(f"[bench] F1 packed varlen ({len(lengths)} sequences)", file=sys.stderr, flush=True)
+    ms_v, _ = timed(step_varlen, args.steps, args.warmup)
+    gbs_v = nbytes / (ms_v / 1e3) / 1e9
+    del tv, ov, wsv
+
     line = {
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -235,6 +260,10 @@ def main():
         "falcon1_same_step": {"tokens_per_s": B * T / (ms_s / 1e3), "ms_per_step": ms_s,
                               "hbm_gbs": gbs_s, "hbm_frac": gbs_s / HBM_PEAK_GBS,
                               "pairs": "(k_t, v_t), FALCON_SAME_STEP"},
+        "falcon1_varlen": {"tokens_per_s": B * T / (ms_v / 1e3), "ms_per_step": ms_v,
+                           "hbm_gbs": gbs_v, "hbm_frac": gbs_v / HBM_PEAK_GBS,
+                           "batch": f"{len(lengths)} packed sequences, lengths {min(lengths)}.."
+                                    f"{maxT}, {B * T} tokens per head, H={H}"},
     }
 
     if not args.no_decode:

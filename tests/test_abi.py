@@ -190,7 +190,11 @@ def test_varlen_rejects(L, kw, code):
 
 
 def test_varlen_workspace_matches_batched_layout(L):
-    """Records are per (sequence, head) with the longest sequence's tile count."""
+    """Records are per (sequence, head) with the longest sequence's tile count,
+    followed by 256-byte-aligned room for 2N+1 ints (the schedule) and a job
+    table of 16 bytes per record slot."""
     a = L.falcon_chunk_fwd_varlen_workspace(3, 4, 150, 128, 128, 1, 1, 1, 64)
     b = L.falcon_chunk_fwd_workspace(3, 4, 150, 128, 128, 1, 1, 1, 64)
-    assert a == b > 0
+    assert b > 0 and a == b + 256 + 3 * 4 * 3 * 16
+    assert L.falcon_chunk_fwd_varlen_workspace(1000, 4, 150, 128, 128, 1, 1, 1, 64) == \
+        L.falcon_chunk_fwd_workspace(1000, 4, 150, 128, 128, 1, 1, 1, 64) + 8192 + 1000 * 4 * 3 * 16

@@ -111,6 +111,10 @@ int falcon_chunk_fwd(const void* q, const void* k, const void* v, const float* a
     a.cu = nullptr;
     a.H = H;
     a.Ttot = T;
+    a.order_ws = nullptr;
+    a.order = nullptr;
+    a.toff = nullptr;
+    a.jobs = nullptr;
     a.W = window;
     a.lag = lag;
     a.norm = norm_of(base);
@@ -122,8 +126,15 @@ int falcon_chunk_fwd(const void* q, const void* k, const void* v, const float* a
 size_t falcon_chunk_fwd_varlen_workspace(int N, int H, int max_seqlen, int dk, int dv,
                                          falcon_dtype dt, falcon_variant var, int window,
                                          int chunk) {
-    // the records are laid out per (sequence, head) with the longest sequence's tile count
-    return falcon_chunk_fwd_workspace(N, H, max_seqlen, dk, dv, dt, var, window, chunk);
+    // the records, laid out per (sequence, head) with the longest sequence's
+    // tile count, then the schedule: 2N+1 ints (the sequences' order, the
+    // prefix sums of their tile counts) and, 256-byte aligned, a job table of
+    // 4 ints per record slot
+    const size_t rec = falcon_chunk_fwd_workspace(N, H, max_seqlen, dk, dv, dt, var, window, chunk);
+    if (rec == 0) return 0;
+    const int Wv = (var & 0xFF) == FALCON_F3 || (var & 0xFF) == FALCON_F3A ? window : 1;
+    const size_t slots = (size_t)N * H * ((max_seqlen + chunk / Wv - 1) / (chunk / Wv));
+    return rec + ((2 * (size_t)N + 1) * sizeof(int) + 255) / 256 * 256 + slots * 4 * sizeof(int);
 }
 
 int falcon_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* alpha,
@@ -163,6 +174,12 @@ int falcon_chunk_fwd_varlen(const void* q, const void* k, const void* v, const f
     a.cu = cu_seqlens;
     a.H = H;
     a.Ttot = total_T;
+    const size_t rec = falcon_chunk_fwd_workspace(N, H, max_seqlen, dk, dv, dt, var, window, chunk);
+    a.order_ws = (need > 0 && workspace) ? reinterpret_cast<int*>(static_cast<char*>(workspace) + rec)
+                                         : nullptr;
+    a.order = nullptr;
+    a.toff = nullptr;
+    a.jobs = nullptr;
     a.W = window;
     a.lag = lag;
     a.norm = norm_of(base);

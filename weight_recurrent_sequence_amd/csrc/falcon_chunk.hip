@@ -82,12 +82,130 @@ struct SeqRows {
     size_t row0;
     int T;
 };
+__device__ __forceinline__ SeqRows rows_of(const ChunkArgs& a, int h, int c0, int c1) {
+    const int s0 = min(max(c0, 0), a.Ttot);
+    const int s1 = min(min(max(c1, s0), a.Ttot), s0 + a.T);
+    return {(size_t)h * a.Ttot + s0, s1 - s0};
+}
 __device__ __forceinline__ SeqRows seq_rows(const ChunkArgs& a, int bh) {
     if (!a.cu) return {(size_t)bh * a.T, a.T};
-    const int n = bh / a.H, h = bh - n * a.H;
-    const int s0 = min(max(a.cu[n], 0), a.Ttot);
-    const int s1 = min(min(max(a.cu[n + 1], s0), a.Ttot), s0 + a.T);
-    return {(size_t)h * a.Ttot + s0, s1 - s0};
+    const int n = bh / a.H;
+    return rows_of(a, bh - n * a.H, a.cu[n], a.cu[n + 1]);
+}
+
+// The (batch*head) row of state-pass workgroup rank r: the natural order, or
+// for packed calls the sequences longest first (`order`), so the longest
+// sequences are dispatched first and none is left to run alone at the end.
+__device__ __forceinline__ int pass_bh(const ChunkArgs& a, int r) {
+    if (!a.order) return r;
+    const int i = r / a.H;
+    return a.order[i] * a.H + (r - i * a.H);
+}
+
+constexpr int kCuLds = 4096;  // offsets the schedule kernel copies to LDS
+
+// Packed calls, before the kernels: in one workgroup,
+//  * order[i]: sequence indices by tile count, longest first (a counting sort
+//    in LDS bins; the order within a bin is immaterial, since no sequence's
+//    result depends on when it runs), for the state pass;
+//  * toff[n]: exclusive prefix sums of the tile counts in sequence order
+//    (toff[N] = all tiles), so the intra-chunk kernel schedules only the
+//    tiles that exist.
+__global__ __launch_bounds__(1024) void packed_schedule_kernel(ChunkArgs a, int Ct, int nbins,
+                                                               int* order, int* toff, int* jobs) {
+    // LDS: nbins bins, one partial sum per thread, the total, then (up to
+    // kCuLds entries) a copy of the offsets
+    extern __shared__ int bins[];
+    int* part = bins + nbins;
+    int* cul = part + blockDim.x + 1;
+    const int N = a.BH / a.H, tid = threadIdx.x, nt = blockDim.x;
+    const bool in_lds = N + 1 <= kCuLds;
+    for (int b = tid; b < nbins; b += nt) bins[b] = 0;
+    if (in_lds)
+        for (int i = tid; i <= N; i += nt) cul[i] = a.cu[i];
+    __syncthreads();
+    // sequence n's rows in head 0's plane (its start is the same in every plane)
+    auto seq_rows = [&](const ChunkArgs&, int bh) {
+        const int n = bh / a.H;
+        return in_lds ? rows_of(a, 0, cul[n], cul[n + 1]) : rows_of(a, 0, a.cu[n], a.cu[n + 1]);
+    };
+    for (int n = tid; n < N; n += nt)
+        atomicAdd(&bins[min(tiles_of(seq_rows(a, n * a.H).T, Ct), nbins - 1)], 1);
+    // prefix sums of tile counts: thread t owns sequences [t*per, (t+1)*per)
+    const int per = (N + nt - 1) / nt;
+    const int n0 = min(tid * per, N), n1 = min(n0 + per, N);
+    int sum = 0;
+    for (int n = n0; n < n1; ++n) sum += tiles_of(seq_rows(a, n * a.H).T, Ct);
+    part[tid] = sum;
+    __syncthreads();
+    if (tid == 0) {
+        int acc = 0;
+        for (int b = nbins - 1; b >= 0; --b) {
+            const int c = bins[b];
+            bins[b] = acc;
+            acc += c;
+        }
+        acc = 0;
+        const int nparts = per > 0 ? (N + per - 1) / per : 0;  // threads that own sequences
+        for (int t = 0; t < nparts; ++t) {
+            const int c = part[t];
+            part[t] = acc;
+            acc += c;
+        }
+        part[nt] = acc;  // all tiles
+        toff[N] = acc;
+    }
+    __syncthreads();
+    for (int n = tid; n < N; n += nt)
+        order[atomicAdd(&bins[min(tiles_of(seq_rows(a, n * a.H).T, Ct), nbins - 1)], 1)] = n;
+    // the job table, j = h * G + g: (row, tile, sequence start, length); head
+    // 0's row0 is the sequence's start in every plane
+    const int Gall = part[nt];
+    auto put = [&](int n, const SeqRows& sr, int g0, int h, int tile) {
+        int* e = jobs + 4 * ((size_t)h * Gall + g0 + tile);
+        e[0] = n * a.H + h;
+        e[1] = tile;
+        e[2] = (int)sr.row0;
+        e[3] = sr.T;
+    };
+    int acc = part[tid];
+    for (int n = n0; n < n1; ++n) {
+        toff[n] = acc;
+        const SeqRows sr = seq_rows(a, n * a.H);
+        const int ntl = tiles_of(sr.T, Ct);
+        if (N >= nt)  // enough sequences: each thread fills its own
+            for (int h = 0; h < a.H; ++h)
+                for (int tile = 0; tile < ntl; ++tile) put(n, sr, acc, h, tile);
+        acc += ntl;
+    }
+    if (N < nt) {  // few sequences: all threads fill each one
+        int g0 = 0;
+        for (int n = 0; n < N; ++n) {
+            const SeqRows sr = seq_rows(a, n * a.H);
+            const int ntl = tiles_of(sr.T, Ct);
+            for (int e = tid; e < a.H * ntl; e += nt) put(n, sr, g0, e / ntl, e - (e / ntl) * ntl);
+            g0 += ntl;
+        }
+    }
+}
+
+// The (batch*head row, tile) of intra-chunk job j.  Batched calls: row-major
+// over (row, tile).  Packed calls: only existing tiles, j = h * G + g with G
+// the tile count of all sequences and g a tile index in sequence order (so
+// consecutive jobs walk one head's plane in address order), the sequence of
+// g found in toff by binary search.
+struct Job {
+    int bh, tile;
+    SeqRows sr;
+};
+__device__ __forceinline__ Job job_of(const ChunkArgs& a, int j, int ntiles) {
+    if (!a.jobs) {
+        const int bh = j / ntiles;
+        return {bh, j - bh * ntiles, seq_rows(a, bh)};
+    }
+    const int4 e = reinterpret_cast<const int4*>(a.jobs)[j];
+    const int h = e.x - (e.x / a.H) * a.H;
+    return {e.x, e.y, {(size_t)h * a.Ttot + e.z, e.w}};
 }
 
 
@@ -136,6 +254,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a, void* ws, 
     const int Ct = CV / Wv, NVR = Ct * Wv, NBQ = (Ct + 15) / 16;
     const SeqRows sr = seq_rows(a, bh);
     const int T_ = sr.T;
+    if (tile >= tiles_of(T_, Ct)) return;  // a shorter packed sequence: never read
     const int t0 = tile * Ct;
     const float eps = a.eps;
     const T* qg = static_cast<const T*>(a.q) + sr.row0 * D;
@@ -388,9 +507,10 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs a, const void
     const int blk = blockIdx.x;
     const int xcd = blk & 7;
     const int jj = blk >> 3;
-    const int bh = (jj / NVS) * 8 + xcd;
+    const int r = (jj / NVS) * 8 + xcd;
     const int vs = jj % NVS;
-    if (bh >= a.BH) return;
+    if (r >= a.BH) return;
+    const int bh = pass_bh(a, r);
     const int v0 = vs * 64;
 
     const int W = a.W;
@@ -786,9 +906,10 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
     const int blk = blockIdx.x;
     const int xcd = blk & 7;
     const int jj = blk >> 3;
-    const int bh = (jj / NVS) * 8 + xcd;
+    const int r = (jj / NVS) * 8 + xcd;
     const int vs = jj % NVS;
-    if (bh >= a.BH) return;
+    if (r >= a.BH) return;
+    const int bh = pass_bh(a, r);
     const int v0 = vs * 64;
 
     const int W = a.W;
@@ -1449,10 +1570,10 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
     u32x4 px[NXL], pxh[NXL], pq[NXL];
     float pal = 1.f, pet = 0.f;
 
-    auto load = [&](int job) __attribute__((always_inline)) {
-        const int bh = job / ntiles, tile = job - bh * ntiles;
+    auto load = [&](const Job& jb) __attribute__((always_inline)) {
+        const int bh = jb.bh, tile = jb.tile;
         const int t0 = tile * Ct;
-        const SeqRows sr = seq_rows(a, bh);
+        const SeqRows sr = jb.sr;
         const int T_ = sr.T;
         const T* kg = static_cast<const T*>(a.k) + sr.row0 * D;
         const T* qg = static_cast<const T*>(a.q) + sr.row0 * D;
@@ -1483,11 +1604,30 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
         }
     };
 
+    // Packed calls read each job's entry from the table one job ahead, with a
+    // vector load (counted by vmcnt, so no LDS wait ever waits for it; a scalar
+    // load would share lgkmcnt with LDS and stall the next LDS read).
+    if (a.toff) njobs = a.H * a.toff[a.BH / a.H];  // packed: the tiles that exist
+    const rsrc_t rjobs = make_rsrc(a.jobs, a.jobs ? (int64_t)njobs * 16 : 0);
+    auto fetch = [&](int j) __attribute__((always_inline)) {
+        return buf_load16(rjobs, (a.jobs && j < njobs) ? (uint32_t)j * 16u : kOob);
+    };
+    auto decode = [&](int j, u32x4 e) __attribute__((always_inline)) {
+        if (!a.jobs) return job_of(a, j, ntiles);
+        const int bh = (int)__builtin_amdgcn_readfirstlane(e[0]);
+        const int h = bh - (bh / a.H) * a.H;
+        return Job{bh, (int)__builtin_amdgcn_readfirstlane(e[1]),
+                   {(size_t)h * a.Ttot + (int)__builtin_amdgcn_readfirstlane(e[2]),
+                    (int)__builtin_amdgcn_readfirstlane(e[3])}};
+    };
     int job = blockIdx.x;
-    if (job < njobs) load(job);
+    u32x4 e_cur = fetch(job), e_nxt = fetch(job + gridDim.x);
+    Job jcur = decode(job, e_cur);
+    if (job < njobs) load(jcur);
     for (; job < njobs; job += gridDim.x) {
-        const int bh = job / ntiles, tile = job - bh * ntiles;
-        const int T_ = seq_rows(a, bh).T;  // tiles beyond it are identity padding, never read
+        const Job jb = jcur;
+        const int bh = jb.bh, tile = jb.tile;
+        const int T_ = jb.sr.T;  // tiles beyond it are identity padding, never read
         char* rec = static_cast<char*>(ws) + ((size_t)bh * ntiles + tile) * R::kBytes;
         T* recT = reinterpret_cast<T*>(rec);
         float* recS = reinterpret_cast<float*>(rec + R::kScalBytes);
@@ -1511,7 +1651,14 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
             sm.et[tid] = ok ? pet : 0.f;
         }
         lds_barrier();
-        if (job + (int)gridDim.x < njobs) load(job + gridDim.x);
+        if (job + (int)gridDim.x < njobs) {
+            jcur = decode(job + gridDim.x, e_nxt);
+            load(jcur);
+        }
+        e_nxt = fetch(job + 2 * gridDim.x);
+        // a packed sequence shorter than the longest leaves tiles that the
+        // state pass never reads: stage them (the prefetch chain) and move on
+        if (tile >= tiles_of(T_, Ct)) continue;
 
         // ---- norms: 4 threads per row ----
         {
@@ -1825,6 +1972,26 @@ template <class E, int D, int CV, bool DELTA, bool COL, bool WIN>
 static hipError_t launch_one(const ChunkArgs& a, void* ws, hipStream_t stream) {
     const int Wv = WIN ? a.W : 1;
     const int ntiles = tiles_of(a.T, CV / Wv);
+    ChunkArgs b = a;
+    b.order = nullptr;
+    b.toff = nullptr;
+    b.jobs = nullptr;
+    const int nbins = ntiles + 1;
+    if (a.cu && a.order_ws && ntiles > 0 && nbins <= 8192) {
+        // schedule layout: order [N], toff [N+1], then (256-byte aligned) the
+        // job table, 4 ints for each of at most BH * ntiles jobs
+        const int N = a.BH / a.H;
+        int* jobs = a.order_ws + ((2 * (size_t)N + 1 + 63) / 64) * 64;
+        const int cul = N + 1 <= kCuLds ? N + 1 : 0;
+        hipLaunchKernelGGL(packed_schedule_kernel, dim3(1), dim3(1024),
+                           (nbins + 1025 + cul) * sizeof(int),
+                           stream, a, CV / Wv, nbins, a.order_ws, a.order_ws + N, jobs);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        b.order = a.order_ws;
+        b.toff = a.order_ws + N;
+        b.jobs = jobs;
+    }
     if (ntiles > 0) {
         if constexpr (E::kBytes == 2) {
             // persistent grid: as many workgroups as fit on the device at once
@@ -1841,22 +2008,22 @@ static hipError_t launch_one(const ChunkArgs& a, void* ws, hipStream_t stream) {
             const int njobs = a.BH * ntiles;
             const int grid = njobs < cus * per_cu ? njobs : cus * per_cu;
             hipLaunchKernelGGL((chunk_prep2_kernel<D, CV, DELTA, COL, WIN>), dim3(grid), dim3(256),
-                               0, stream, a, ws, ntiles, njobs);
+                               0, stream, b, ws, ntiles, njobs);
         } else {
             hipLaunchKernelGGL((chunk_prep_kernel<E, D, CV, DELTA, COL, WIN>), dim3(a.BH * ntiles),
-                               dim3(256), 0, stream, a, ws, ntiles);
+                               dim3(256), 0, stream, b, ws, ntiles);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int nvs = D / 64;
-    const int bh8 = (a.BH + 7) / 8 * 8;
+    const int bh8 = (b.BH + 7) / 8 * 8;
     if constexpr (E::kBytes == 2)
         hipLaunchKernelGGL((chunk_pass_kernel<D, CV, DELTA, COL, WIN>), dim3(bh8 * nvs), dim3(COL ? 512 : 768),
-                           0, stream, a, (const void*)ws, ntiles);
+                           0, stream, b, (const void*)ws, ntiles);
     else
         hipLaunchKernelGGL((chunk_scan_kernel<E, D, CV, DELTA, COL, WIN>), dim3(bh8 * nvs),
-                           dim3(256), 0, stream, a, (const void*)ws, ntiles);
+                           dim3(256), 0, stream, b, (const void*)ws, ntiles);
     return hipGetLastError();
 }
 

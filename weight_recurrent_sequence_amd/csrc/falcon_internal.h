@@ -33,6 +33,17 @@ struct ChunkArgs {
     const int* cu;
     int H;
     int Ttot;
+    // Packed calls: workspace room for the schedule (N + N+1 ints): the
+    // sequences longest first (`order`) and the prefix sums of their tile
+    // counts (`toff`), both written on the device before the kernels run and
+    // set by the launcher (NULL: natural order, every (row, tile) job).
+    int* order_ws;
+    const int* order;
+    const int* toff;
+    // Packed calls: the intra-chunk jobs, 4 ints each (row, tile, first row of
+    // the sequence in its head's plane, its length), written with the
+    // schedule; NULL: jobs are decoded from their index.
+    const int* jobs;
     int W;       // window (1 unless kNormWindow)
     int lag;     // key of step t's pair w is k_{t-w-lag}: 1 prefix-aligned, 0 same-step
     int norm;    // NormKind
