@@ -12,7 +12,9 @@ decode_step(...)  one step of the same recurrence for N x H heads.
 decode_step_window(...)  the same for Falcon-3/3A, with key and value caches.
 Every entry takes align="prefix" (the pair of step t is (k_{t-1}, v_t), the
 authors' alignment) or align="same" (k_t, v_t: the same-step alignment of the
-KLA/GDN recurrences the pages contrast it with).
+KLA/GDN recurrences the pages contrast it with), and phi="identity" (the
+default), "l2" (x / ||x||, 0 for x = 0) or "silu" (x / (1 + exp(-x))): a
+feature map applied to every key and query.
 forms             numpy fp64 masked-parallel and chunk-parallel forms, used only
                   to cross-check the recurrent form (the authors' abstract of
                   "Fast Weight Attention for Continual Learning" states that the
@@ -35,6 +37,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 F1, F2, F3, F1A, F2A, F3A = 1, 2, 3, 11, 12, 13
 VARIANTS = {"F1": F1, "F2": F2, "F3": F3, "F1A": F1A, "F2A": F2A, "F3A": F3A}
 ALIGN_LAG = {"prefix": 1, "same": 0}
+PHI = {"identity": 0, "l2": 1, "silu": 2}
 
 _lib = None
 
@@ -56,12 +59,12 @@ def _load():
         build()
         lib = ctypes.CDLL(LIB)
         dp = ctypes.POINTER(ctypes.c_double)
-        lib.oracle_recurrent_lag.restype = ctypes.c_int
-        lib.oracle_recurrent_lag.argtypes = [ctypes.c_int] * 8 + [ctypes.c_double] + [dp] * 10 + [ctypes.c_int]
-        lib.oracle_decode_step_lag.restype = ctypes.c_int
-        lib.oracle_decode_step_lag.argtypes = [ctypes.c_int] * 6 + [ctypes.c_double] + [dp] * 8
-        lib.oracle_decode_step_window_lag.restype = ctypes.c_int
-        lib.oracle_decode_step_window_lag.argtypes = [ctypes.c_int] * 7 + [ctypes.c_double] + [dp] * 9
+        lib.oracle_recurrent_ex.restype = ctypes.c_int
+        lib.oracle_recurrent_ex.argtypes = [ctypes.c_int] * 9 + [ctypes.c_double] + [dp] * 10 + [ctypes.c_int]
+        lib.oracle_decode_step_ex.restype = ctypes.c_int
+        lib.oracle_decode_step_ex.argtypes = [ctypes.c_int] * 7 + [ctypes.c_double] + [dp] * 8
+        lib.oracle_decode_step_window_ex.restype = ctypes.c_int
+        lib.oracle_decode_step_window_ex.argtypes = [ctypes.c_int] * 8 + [ctypes.c_double] + [dp] * 9
         lib.oracle_num_cpus.restype = ctypes.c_int
         lib.oracle_num_cpus.argtypes = []
         _lib = lib
@@ -85,7 +88,7 @@ def _ptr(a):
 
 
 def recurrent(variant, q, k, v, alpha, eta, *, window=1, eps=1e-6, S0=None, k_prev=None,
-              v_prev=None, nthreads=0, align="prefix"):
+              v_prev=None, nthreads=0, align="prefix", phi="identity"):
     """Run the recurrence.  q, k: [B,H,T,dk]; v: [B,H,T,dv]; alpha, eta: [B,H,T];
     k_prev holds the W keys before the sequence (oldest first) in either
     alignment.
@@ -108,7 +111,7 @@ def recurrent(variant, q, k, v, alpha, eta, *, window=1, eps=1e-6, S0=None, k_pr
         assert v_prev.shape == (B, H, window - 1, dv)
     o = np.zeros((B, H, T, dv), np.float64)
     S = np.zeros((B, H, dv, dk), np.float64)
-    rc = _load().oracle_recurrent_lag(variant, B, H, T, dk, dv, window, lag, float(eps), _ptr(q),
+    rc = _load().oracle_recurrent_ex(variant, B, H, T, dk, dv, window, lag, PHI[phi], float(eps), _ptr(q),
                                       _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(S0),
                                       _ptr(k_prev), _ptr(v_prev), _ptr(o), _ptr(S), int(nthreads))
     if rc < 0:
@@ -121,7 +124,8 @@ def recurrent_threads_used(B, H, nthreads=0):
     return min(n, B * H)
 
 
-def decode_step(variant, S, k_cache, q, k, v, alpha, eta, *, eps=1e-6, align="prefix"):
+def decode_step(variant, S, k_cache, q, k, v, alpha, eta, *, eps=1e-6, align="prefix",
+                phi="identity"):
     """One decode step.  S [N,H,dv,dk] and k_cache [N,H,dk] are copied, updated
     and returned together with o [N,H,dv]: (o, S_new, k_cache_new)."""
     variant = VARIANTS.get(variant, variant)
@@ -132,7 +136,7 @@ def decode_step(variant, S, k_cache, q, k, v, alpha, eta, *, eps=1e-6, align="pr
     N, H, dv, dk = S.shape
     k_cache = k_cache.reshape(N, H, dk).copy()
     o = np.zeros((N, H, dv), np.float64)
-    rc = _load().oracle_decode_step_lag(variant, N, H, dk, dv, lag, float(eps), _ptr(S),
+    rc = _load().oracle_decode_step_ex(variant, N, H, dk, dv, lag, PHI[phi], float(eps), _ptr(S),
                                         _ptr(k_cache), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                         _ptr(eta), _ptr(o))
     if rc < 0:
@@ -141,7 +145,7 @@ def decode_step(variant, S, k_cache, q, k, v, alpha, eta, *, eps=1e-6, align="pr
 
 
 def decode_step_window(variant, S, k_cache, v_cache, q, k, v, alpha, eta, *, eps=1e-6,
-                       align="prefix"):
+                       align="prefix", phi="identity"):
     """One Falcon-3 / Falcon-3A decode step with a window of W pairs.
 
     S [N,H,dv,dk]; k_cache [N,H,W,dk] with k_cache[..., w, :] = k_{t-1-w};
@@ -158,7 +162,7 @@ def decode_step_window(variant, S, k_cache, v_cache, q, k, v, alpha, eta, *, eps
                else np.zeros((N, H, 0, dv), np.float64))
     o = np.zeros((N, H, dv), np.float64)
     vbuf = v_cache if W > 1 else np.zeros((N, H, 1, dv), np.float64)
-    rc = _load().oracle_decode_step_window_lag(variant, N, H, dk, dv, W, lag, float(eps), _ptr(S),
+    rc = _load().oracle_decode_step_window_ex(variant, N, H, dk, dv, W, lag, PHI[phi], float(eps), _ptr(S),
                                            _ptr(k_cache), _ptr(vbuf), _ptr(q), _ptr(k), _ptr(v),
                                            _ptr(alpha), _ptr(eta), _ptr(o))
     if rc < 0:

@@ -22,6 +22,10 @@
  *     the same-step pair x_t = k_t, y_t = v_t (the alignment of the KLA/GDN
  *     recurrences the pages contrast it with) is an option: `lag` = 1 is the
  *     prefix alignment, lag = 0 the same-step one;
+ *   - phi is left open by the pages; identity is the default, and a feature
+ *     map applied to every key and every query (halo keys included) is an
+ *     option: `phi` = 1 is L2 normalization x / ||x|| (0 for x = 0), 2 is
+ *     SiLU x / (1 + exp(-x)), elementwise;
  *   - the updates are normalized first-order steps on a squared-error
  *     regression loss (Falcon-1/2/3) or a negative inner-product loss
  *     (Falcon-1A/2A/3A) (authors' abstract, the variant list);
@@ -53,7 +57,7 @@
 enum { OR_F1 = 1, OR_F2 = 2, OR_F3 = 3, OR_F1A = 11, OR_F2A = 12, OR_F3A = 13 };
 
 typedef struct {
-    int variant, B, H, T, dk, dv, W, lag;
+    int variant, B, H, T, dk, dv, W, lag, phi;
     double eps;
     const double *q, *k, *v, *alpha, *eta, *S0, *k_prev, *v_prev;
     double *o, *S_out;
@@ -83,15 +87,42 @@ static const double* val_at(const seq_job* j, const double* vseq, const double* 
     return zeros;
 }
 
+/* The feature map phi applied to one vector of n entries, into out. */
+static void apply_phi(int phi, const double* x, double* out, int n) {
+    if (phi == 1) {
+        double nrm = 0.0;
+        for (int c = 0; c < n; ++c) nrm += x[c] * x[c];
+        const double s = nrm > 0.0 ? 1.0 / sqrt(nrm) : 0.0;
+        for (int c = 0; c < n; ++c) out[c] = x[c] * s;
+    } else if (phi == 2) {
+        for (int c = 0; c < n; ++c) out[c] = x[c] / (1.0 + exp(-x[c]));
+    } else {
+        for (int c = 0; c < n; ++c) out[c] = x[c];
+    }
+}
+
+/* A copy of `rows` vectors of length n with phi applied to each (NULL in,
+ * NULL out). */
+static double* phi_copy(int phi, const double* x, int rows, int n) {
+    if (!x) return NULL;
+    double* out = malloc(sizeof(double) * (size_t)(rows > 0 ? rows : 1) * n);
+    for (int r = 0; r < rows; ++r) apply_phi(phi, x + (size_t)r * n, out + (size_t)r * n, n);
+    return out;
+}
+
 /* One (b,h) sequence, t = 0..T-1, in the order the recurrence defines. */
 static void run_sequence(const seq_job* j, int bh) {
     const int T = j->T, dk = j->dk, dv = j->dv, W = j->W, var = j->variant;
-    const double* q = j->q + (size_t)bh * T * dk;
-    const double* k = j->k + (size_t)bh * T * dk;
+    /* the feature map on the keys (halo included) and queries, up front */
+    double* qphi = phi_copy(j->phi, j->q + (size_t)bh * T * dk, T, dk);
+    double* kphi = phi_copy(j->phi, j->k + (size_t)bh * T * dk, T, dk);
+    double* kpphi = phi_copy(j->phi, j->k_prev ? j->k_prev + (size_t)bh * W * dk : NULL, W, dk);
+    const double* q = qphi;
+    const double* k = kphi;
     const double* v = j->v + (size_t)bh * T * dv;
     const double* al = j->alpha + (size_t)bh * T;
     const double* et = j->eta + (size_t)bh * T;
-    const double* kprev = j->k_prev ? j->k_prev + (size_t)bh * W * dk : NULL;
+    const double* kprev = kpphi;
     const double* vprev = (j->v_prev && W > 1) ? j->v_prev + (size_t)bh * (W - 1) * dv : NULL;
     double* o = j->o + (size_t)bh * T * dv;
 
@@ -177,6 +208,9 @@ static void run_sequence(const seq_job* j, int bh) {
         }
     }
     if (j->S_out) memcpy(j->S_out + (size_t)bh * dv * dk, S, sizeof(double) * dv * dk);
+    free(qphi);
+    free(kphi);
+    free(kpphi);
     free(S);
     free(u);
     free(pred);
@@ -206,14 +240,15 @@ int oracle_num_cpus(void) {
  * NULL).  W must be 1 unless the variant is Falcon-3/3A; lag is 1 (prefix
  * alignment) or 0 (same-step).  Returns the number of threads used, or a
  * negative value for an invalid argument. */
-int oracle_recurrent_lag(int variant, int B, int H, int T, int dk, int dv, int W, int lag,
-                         double eps, const double* q, const double* k, const double* v,
-                         const double* alpha, const double* eta, const double* S0,
-                         const double* k_prev, const double* v_prev, double* o, double* S_out,
-                         int nthreads) {
+int oracle_recurrent_ex(int variant, int B, int H, int T, int dk, int dv, int W, int lag,
+                        int phi, double eps, const double* q, const double* k, const double* v,
+                        const double* alpha, const double* eta, const double* S0,
+                        const double* k_prev, const double* v_prev, double* o, double* S_out,
+                        int nthreads) {
     if (!is_known_variant(variant)) return -3;
     if (B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1 || W < 1) return -2;
     if (lag != 0 && lag != 1) return -2;
+    if (phi < 0 || phi > 2) return -2;
     if (W != 1 && variant != OR_F3 && variant != OR_F3A) return -2;
     if (!q || !k || !v || !alpha || !eta || !o) return -1;
     int n = B * H;
@@ -222,8 +257,8 @@ int oracle_recurrent_lag(int variant, int B, int H, int T, int dk, int dv, int W
     seq_job* jobs = calloc((size_t)nthreads, sizeof(seq_job));
     pthread_t* th = calloc((size_t)nthreads, sizeof(pthread_t));
     for (int i = 0; i < nthreads; ++i) {
-        seq_job jb = {variant, B, H, T, dk, dv, W, lag, eps, q, k, v, alpha, eta, S0, k_prev,
-                      v_prev, o, S_out, nthreads, i};
+        seq_job jb = {variant, B, H, T, dk, dv, W, lag, phi, eps, q, k, v, alpha, eta, S0,
+                      k_prev, v_prev, o, S_out, nthreads, i};
         jobs[i] = jb;
     }
     for (int i = 1; i < nthreads; ++i) pthread_create(&th[i], NULL, seq_worker, &jobs[i]);
@@ -234,7 +269,17 @@ int oracle_recurrent_lag(int variant, int B, int H, int T, int dk, int dv, int W
     return nthreads;
 }
 
-/* The prefix-aligned form (lag 1). */
+/* The identity feature map. */
+int oracle_recurrent_lag(int variant, int B, int H, int T, int dk, int dv, int W, int lag,
+                         double eps, const double* q, const double* k, const double* v,
+                         const double* alpha, const double* eta, const double* S0,
+                         const double* k_prev, const double* v_prev, double* o, double* S_out,
+                         int nthreads) {
+    return oracle_recurrent_ex(variant, B, H, T, dk, dv, W, lag, 0, eps, q, k, v, alpha, eta, S0,
+                               k_prev, v_prev, o, S_out, nthreads);
+}
+
+/* The prefix-aligned form (lag 1), identity feature map. */
 int oracle_recurrent(int variant, int B, int H, int T, int dk, int dv, int W, double eps,
                      const double* q, const double* k, const double* v, const double* alpha,
                      const double* eta, const double* S0, const double* k_prev,
@@ -248,18 +293,25 @@ int oracle_recurrent(int variant, int B, int H, int T, int dk, int dv, int W, do
  * read exactly as one iteration of the recurrence; afterwards k_cache holds
  * the new key.  S [N,H,dv,dk] and k_cache [N,H,dk] are updated in place;
  * q, k [N,H,dk]; v [N,H,dv]; alpha, eta [N,H]; o [N,H,dv]. */
-int oracle_decode_step_lag(int variant, int N, int H, int dk, int dv, int lag, double eps,
-                           double* S, double* k_cache, const double* q, const double* k,
-                           const double* v, const double* alpha, const double* eta, double* o) {
+int oracle_decode_step_ex(int variant, int N, int H, int dk, int dv, int lag, int phi,
+                          double eps, double* S, double* k_cache, const double* q,
+                          const double* k, const double* v, const double* alpha,
+                          const double* eta, double* o) {
     if (variant != OR_F1 && variant != OR_F2 && variant != OR_F1A && variant != OR_F2A) return -3;
     if (N < 1 || H < 1 || dk < 1 || dv < 1 || (lag != 0 && lag != 1)) return -2;
+    if (phi < 0 || phi > 2) return -2;
     double* u = calloc((size_t)dk, sizeof(double));
     double* r = calloc((size_t)dv, sizeof(double));
+    double* xb = calloc((size_t)dk, sizeof(double));
+    double* qb = calloc((size_t)dk, sizeof(double));
     for (size_t n = 0; n < (size_t)N * H; ++n) {
         double* Sh = S + n * dv * dk;
         double* kc = k_cache + n * dk;
-        const double *qh = q + n * dk, *kh = k + n * dk, *vh = v + n * dv;
-        const double* x = lag ? kc : kh;
+        const double *kh = k + n * dk, *vh = v + n * dv;
+        apply_phi(phi, lag ? kc : kh, xb, dk);  /* the caches keep the raw keys */
+        apply_phi(phi, q + n * dk, qb, dk);
+        const double* x = xb;
+        const double* qh = qb;
         const double a = alpha[n], e = eta[n];
         for (size_t m = 0; m < (size_t)dv * dk; ++m) Sh[m] *= a;
         if (variant == OR_F1 || variant == OR_F1A) {
@@ -291,7 +343,16 @@ int oracle_decode_step_lag(int variant, int N, int H, int dk, int dv, int lag, d
     }
     free(u);
     free(r);
+    free(xb);
+    free(qb);
     return 0;
+}
+
+int oracle_decode_step_lag(int variant, int N, int H, int dk, int dv, int lag, double eps,
+                           double* S, double* k_cache, const double* q, const double* k,
+                           const double* v, const double* alpha, const double* eta, double* o) {
+    return oracle_decode_step_ex(variant, N, H, dk, dv, lag, 0, eps, S, k_cache, q, k, v, alpha,
+                                 eta, o);
 }
 
 int oracle_decode_step(int variant, int N, int H, int dk, int dv, double eps, double* S,
@@ -314,24 +375,33 @@ int oracle_decode_step(int variant, int N, int H, int dk, int dv, double eps, do
  * and value enter at slot 0 and the oldest leave.  With lag 0 (same-step
  * pairs) pair w's key is k_{t-w}: the new key for w = 0, k_cache[w-1] after.
  */
-int oracle_decode_step_window_lag(int variant, int N, int H, int dk, int dv, int W, int lag,
-                                  double eps, double* S, double* k_cache, double* v_cache,
-                                  const double* q, const double* k, const double* v,
-                                  const double* alpha, const double* eta, double* o) {
+int oracle_decode_step_window_ex(int variant, int N, int H, int dk, int dv, int W, int lag,
+                                 int phi, double eps, double* S, double* k_cache,
+                                 double* v_cache, const double* q, const double* k,
+                                 const double* v, const double* alpha, const double* eta,
+                                 double* o) {
     if (variant != OR_F3 && variant != OR_F3A) return -3;
     if (N < 1 || H < 1 || dk < 1 || dv < 1 || W < 1 || (lag != 0 && lag != 1)) return -2;
+    if (phi < 0 || phi > 2) return -2;
     double* R = calloc((size_t)W * dv, sizeof(double));
     const double** y = calloc((size_t)W, sizeof(double*));
     const double** xs = calloc((size_t)W, sizeof(double*));
+    double* xb = calloc((size_t)W * dk, sizeof(double));
+    double* qb = calloc((size_t)dk, sizeof(double));
     for (size_t n = 0; n < (size_t)N * H; ++n) {
         double* Sh = S + n * dv * dk;
         double* kc = k_cache + n * W * dk;
         double* vc = v_cache + n * (W - 1) * dv;
-        const double *qh = q + n * dk, *kh = k + n * dk, *vh = v + n * dv;
+        const double *kh = k + n * dk, *vh = v + n * dv;
+        apply_phi(phi, q + n * dk, qb, dk);
+        const double* qh = qb;
         const double a = alpha[n], e = eta[n];
         for (int w = 0; w < W; ++w) {
             y[w] = (w == 0) ? vh : vc + (size_t)(w - 1) * dv;
-            xs[w] = (w + lag == 0) ? kh : kc + (size_t)(w + lag - 1) * dk;
+            /* the caches keep the raw keys; phi is applied to each pair's key */
+            apply_phi(phi, (w + lag == 0) ? kh : kc + (size_t)(w + lag - 1) * dk,
+                      xb + (size_t)w * dk, dk);
+            xs[w] = xb + (size_t)w * dk;
         }
         for (size_t m = 0; m < (size_t)dv * dk; ++m) Sh[m] *= a;
         double nrm = 0.0;
@@ -365,7 +435,17 @@ int oracle_decode_step_window_lag(int variant, int N, int H, int dk, int dv, int
     free(R);
     free(y);
     free(xs);
+    free(xb);
+    free(qb);
     return 0;
+}
+
+int oracle_decode_step_window_lag(int variant, int N, int H, int dk, int dv, int W, int lag,
+                                  double eps, double* S, double* k_cache, double* v_cache,
+                                  const double* q, const double* k, const double* v,
+                                  const double* alpha, const double* eta, double* o) {
+    return oracle_decode_step_window_ex(variant, N, H, dk, dv, W, lag, 0, eps, S, k_cache,
+                                        v_cache, q, k, v, alpha, eta, o);
 }
 
 int oracle_decode_step_window(int variant, int N, int H, int dk, int dv, int W, double eps,

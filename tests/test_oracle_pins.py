@@ -713,3 +713,86 @@ def test_same_step_decode_window_is_one_recurrent_step(variant, W):
                                     align="same")
     np.testing.assert_allclose(tr(np.array(outs)), o_rec, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(S_run, S_rec, rtol=1e-12, atol=1e-13)
+
+
+# ----------------------------------------------------- feature maps phi ------
+# phi is left open by the pages; the oracle offers phi on every key and query.
+def np_phi(name, x):
+    x = np.asarray(x, np.float64)
+    if name == "l2":
+        n = np.sqrt((x * x).sum(-1, keepdims=True))
+        return np.where(n > 0, x / np.where(n > 0, n, 1.0), 0.0)
+    if name == "silu":
+        return x * (1.0 / (1.0 + np.exp(-x)))
+    return x
+
+
+@pytest.mark.parametrize("align", ["prefix", "same"])
+@pytest.mark.parametrize("phi", ["l2", "silu"])
+@pytest.mark.parametrize("variant", ALL)
+def test_phi_is_the_identity_form_on_mapped_inputs(variant, phi, align):
+    """The feature-map option equals the identity form run on keys, halo keys
+    and queries mapped by numpy's own L2 normalization / SiLU (values and
+    targets untouched), with a zero key in the mix."""
+    for W in ([1, 3] if variant in ("F3", "F3A") else [1]):
+        d = rnd(70 + W, B=1, H=2, T=11, dk=5, dv=4, W=W)
+        d["k"][0, 1, 4] = 0.0
+        o, S = run(variant, d, W=W, align=align, phi=phi)
+        d2 = dict(d, q=np_phi(phi, d["q"]), k=np_phi(phi, d["k"]), k_prev=np_phi(phi, d["k_prev"]))
+        o2, S2 = run(variant, d2, W=W, align=align)
+        np.testing.assert_allclose(o, o2, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(S, S2, rtol=1e-12, atol=1e-13)
+
+
+def test_phi_l2_falcon1_gain():
+    """L2-normalized keys have unit norm: Falcon-1 at alpha = 1, eps = 0 then
+    writes exactly eta of the residual along x (S_t x = (1-eta) S' x + eta y)."""
+    d = rnd(74, B=1, H=1, T=6, dk=4, dv=3)
+    d["alpha"][:] = 1.0
+    eta = d["eta"][0, 0]
+    St = [d["S0"][0, 0]]
+    for t in range(6):
+        dt_ = {kk: (vv[:, :, :t + 1] if (vv is not None and vv.ndim == 4 and kk in ("q", "k", "v"))
+                    else vv) for kk, vv in d.items()}
+        dt_["alpha"], dt_["eta"] = d["alpha"][:, :, :t + 1], d["eta"][:, :, :t + 1]
+        _, S = run("F1", dt_, eps=0.0, phi="l2")
+        St.append(S[0, 0])
+    kh = np.concatenate([d["k_prev"][0, 0], d["k"][0, 0]])
+    for t in range(6):
+        x = np_phi("l2", kh[t])                        # x_t = phi(k_{t-1})
+        lhs = St[t + 1] @ x
+        rhs = (1 - eta[t]) * (St[t] @ x) + eta[t] * d["v"][0, 0, t]
+        np.testing.assert_allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("phi", ["l2", "silu"])
+def test_phi_decode_steps_are_recurrent_steps(phi):
+    r = np.random.default_rng(77)
+    N, H, dk, dv, steps, W = 2, 2, 5, 4, 7, 3
+    S = r.standard_normal((N, H, dv, dk)) * 0.1
+    k_prev, v_prev = r.standard_normal((N, H, W, dk)), r.standard_normal((N, H, W - 1, dv))
+    q, k = r.standard_normal((steps, N, H, dk)), r.standard_normal((steps, N, H, dk))
+    v = r.standard_normal((steps, N, H, dv))
+    al, et = r.uniform(0.5, 1, (steps, N, H)), r.uniform(0, 1, (steps, N, H))
+    tr = lambda a: np.moveaxis(a, 0, 2)  # noqa: E731
+    for align in ("prefix", "same"):
+        # windowed rule (caches hold raw keys, newest first)
+        S_run, kc, vc, outs = S, k_prev[:, :, ::-1].copy(), v_prev[:, :, ::-1].copy(), []
+        for s in range(steps):
+            o, S_run, kc, vc = oracle.decode_step_window("F3", S_run, kc, vc, q[s], k[s], v[s],
+                                                         al[s], et[s], align=align, phi=phi)
+            outs.append(o)
+        o_rec, S_rec = oracle.recurrent("F3", tr(q), tr(k), tr(v), tr(al), tr(et), window=W, S0=S,
+                                        k_prev=k_prev, v_prev=v_prev, align=align, phi=phi)
+        np.testing.assert_allclose(tr(np.array(outs)), o_rec, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(S_run, S_rec, rtol=1e-12, atol=1e-13)
+        # single-key rule
+        S_run, kc1, outs = S, k_prev[:, :, -1].copy(), []
+        for s in range(steps):
+            o, S_run, kc1 = oracle.decode_step("F2", S_run, kc1, q[s], k[s], v[s], al[s], et[s],
+                                               align=align, phi=phi)
+            outs.append(o)
+        o_rec, S_rec = oracle.recurrent("F2", tr(q), tr(k), tr(v), tr(al), tr(et), S0=S,
+                                        k_prev=k_prev[:, :, -1:], align=align, phi=phi)
+        np.testing.assert_allclose(tr(np.array(outs)), o_rec, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(S_run, S_rec, rtol=1e-12, atol=1e-13)
