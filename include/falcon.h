@@ -29,6 +29,14 @@
  * flag; halos and caches keep their meaning (the last W keys, the last W-1
  * values), a same-step pair w simply takes k_{t-w} instead of k_{t-1-w}.
  *
+ * Feature map.  The pages leave phi open and the default is the identity.
+ * OR-ing FALCON_PHI_L2 (x / ||x||, 0 for a zero vector) or FALCON_PHI_SILU
+ * (x / (1 + e^-x), elementwise) into the variant applies that map to every key
+ * (halo and cache keys included) and every query before the step: x = phi(k),
+ * o = S phi(q).  Halos and caches keep the raw keys.  For falcon_chunk_fwd the
+ * mapped keys and queries go through the workspace (the size queries include
+ * them when the flag is set).
+ *
  * The abstract states that each rule has a chunk-parallel form with
  * positive-decay renormalization; falcon_chunk_fwd computes that form
  * (cumulative decays kept as chunk-local log sums, every factor a ratio
@@ -79,7 +87,9 @@ typedef enum {
     FALCON_F1A = 11,
     FALCON_F2A = 12,
     FALCON_F3A = 13,
-    FALCON_SAME_STEP = 0x100 /* flag OR-ed into a variant: same-step pairs (k_t, v_t) */
+    FALCON_SAME_STEP = 0x100, /* flag OR-ed into a variant: same-step pairs (k_t, v_t) */
+    FALCON_PHI_L2 = 0x200,    /* flag: feature map x / ||x|| (0 for x = 0) on keys and queries */
+    FALCON_PHI_SILU = 0x400   /* flag: feature map x / (1 + exp(-x)) on keys and queries */
 } falcon_variant;
 
 typedef enum { FALCON_FP32 = 0, FALCON_BF16 = 1 } falcon_dtype;

@@ -87,8 +87,10 @@ def chunk(L, **kw):
     (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(alpha=None), -1),
     (dict(eta=None), -1), (dict(o=None), -1),
     (dict(q=P + 8), -3), (dict(S0=P + 4), -3), (dict(alpha=P + 2), -3),
-    (dict(var=1 | 0x200), -3), (dict(var=0x100), -3), (dict(var=4 | 0x100), -3),  # flag bits
+    (dict(var=1 | 0x800), -3), (dict(var=0x100), -3), (dict(var=4 | 0x100), -3),  # flag bits
     (dict(var=1 | 0x100, window=2), -2),
+    (dict(var=1 | 0x200 | 0x400), -3),                           # two feature maps
+    (dict(var=1 | 0x200), -4), (dict(var=2 | 0x400 | 0x100), -4),  # valid flags, no workspace
 ])
 def test_chunk_rejects(L, kw, code):
     assert chunk(L, **kw) == code
@@ -110,6 +112,7 @@ def decode(L, **kw):
     (dict(S=None), -1), (dict(kc=None), -1), (dict(o=None), -1), (dict(eta=None), -1),
     (dict(S=P + 8), -3),
     (dict(var=3 | 0x100), -3), (dict(var=1 | 0x800), -3), (dict(var=0x100), -3),
+    (dict(var=1 | 0x600), -3),
 ])
 def test_decode_rejects(L, kw, code):
     assert decode(L, **kw) == code
@@ -131,7 +134,7 @@ def decode_window(L, **kw):
     (dict(dk=32, dv=32), -3), (dict(dk=128, dv=64), -3), (dict(eps=-1.0), -2),
     (dict(S=None), -1), (dict(kc=None), -1), (dict(vc=None), -1), (dict(o=None), -1),
     (dict(alpha=None), -1), (dict(S=P + 4), -3), (dict(eta=P + 2), -3),
-    (dict(var=1 | 0x100), -3), (dict(var=3 | 0x400), -3),
+    (dict(var=1 | 0x100), -3), (dict(var=3 | 0x1000), -3), (dict(var=3 | 0x600), -3),
 ])
 def test_decode_window_rejects(L, kw, code):
     assert decode_window(L, **kw) == code
@@ -198,3 +201,15 @@ def test_varlen_workspace_matches_batched_layout(L):
     assert b > 0 and a == b + 256 + 3 * 4 * 3 * 16
     assert L.falcon_chunk_fwd_varlen_workspace(1000, 4, 150, 128, 128, 1, 1, 1, 64) == \
         L.falcon_chunk_fwd_workspace(1000, 4, 150, 128, 128, 1, 1, 1, 64) + 8192 + 1000 * 4 * 3 * 16
+
+
+def test_feature_map_workspace_holds_the_mapped_inputs(L):
+    """With a feature map the workspace also holds the mapped keys and queries
+    (B*H*T*dk entries each, 256-byte aligned) and the mapped halo keys."""
+    B, H, T, d, W = 2, 3, 1000, 128, 4
+    base = L.falcon_chunk_fwd_workspace(B, H, T, d, d, 1, 3, W, 64)
+    es = 2
+    al = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    for flag in (0x200, 0x400, 0x200 | 0x100):
+        got = L.falcon_chunk_fwd_workspace(B, H, T, d, d, 1, 3 | flag, W, 64)
+        assert got == al(base) + 2 * al(B * H * T * d * es) + al(B * H * W * d * es)

@@ -18,6 +18,8 @@ F1, F2, F3, F1A, F2A, F3A = 1, 2, 3, 11, 12, 13
 VARIANTS = {"F1": F1, "F2": F2, "F3": F3, "F1A": F1A, "F2A": F2A, "F3A": F3A}
 SAME_STEP = 0x100  # flag OR-ed into a variant: same-step pairs (k_t, v_t)
 ALIGN = {"prefix": 0, "same": SAME_STEP}
+PHI_L2, PHI_SILU = 0x200, 0x400  # flags: feature map on keys and queries
+PHI = {"identity": 0, "l2": PHI_L2, "silu": PHI_SILU}
 FP32, BF16 = 0, 1
 STATUS = {0: "FALCON_OK", -1: "FALCON_ERR_NULL", -2: "FALCON_ERR_SHAPE",
           -3: "FALCON_ERR_UNSUPPORTED", -4: "FALCON_ERR_WORKSPACE", -5: "FALCON_ERR_HIP"}
@@ -67,10 +69,11 @@ def status_string(status: int) -> str:
     return lib().falcon_status_string(int(status)).decode()
 
 
-def _variant(v, align="prefix") -> int:
-    """Variant code with the alignment flag: align="prefix" pairs (k_{t-1}, v_t),
-    align="same" pairs (k_t, v_t)."""
-    return (VARIANTS[v] if isinstance(v, str) else int(v)) | ALIGN[align]
+def _variant(v, align="prefix", phi="identity") -> int:
+    """Variant code with the flags: align="prefix" pairs (k_{t-1}, v_t),
+    align="same" pairs (k_t, v_t); phi="identity", "l2" or "silu" maps keys
+    and queries."""
+    return (VARIANTS[v] if isinstance(v, str) else int(v)) | ALIGN[align] | PHI[phi]
 
 
 def _dt(t) -> int:
@@ -106,14 +109,14 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def workspace_bytes(B, H, T, dk, dv, dtype, variant, window=1, chunk=64) -> int:
-    return int(lib().falcon_chunk_fwd_workspace(B, H, T, dk, dv, dtype, _variant(variant),
+def workspace_bytes(B, H, T, dk, dv, dtype, variant, window=1, chunk=64, phi="identity") -> int:
+    return int(lib().falcon_chunk_fwd_workspace(B, H, T, dk, dv, dtype, _variant(variant, phi=phi),
                                                 window, chunk))
 
 
 def chunk_fwd(q, k, v, alpha, eta, variant, *, window=1, chunk=64, eps=1e-6, S0=None,
               k_prev=None, v_prev=None, o=None, S_final=None, return_state=True,
-              workspace=None, stream=None, align="prefix"):
+              workspace=None, stream=None, align="prefix", phi="identity"):
     """Chunk-parallel forward.  q,k [B,H,T,dk]; v [B,H,T,dv] (bf16 or fp32);
     alpha, eta [B,H,T] fp32; S0 [B,H,dv,dk] fp32 or None; k_prev [B,H,W,dk],
     v_prev [B,H,W-1,dv] or None.  `workspace` (uint8 device tensor of at
@@ -121,7 +124,7 @@ def chunk_fwd(q, k, v, alpha, eta, variant, *, window=1, chunk=64, eps=1e-6, S0=
     Returns (o, S_final) (S_final None if return_state is False and none was
     given)."""
     import torch
-    var = _variant(variant, align)
+    var = _variant(variant, align, phi)
     B, H, T, dk = k.shape
     dv = v.shape[-1]
     dev, dt = k.device, k.dtype
@@ -143,7 +146,7 @@ def chunk_fwd(q, k, v, alpha, eta, variant, *, window=1, chunk=64, eps=1e-6, S0=
     if S_final is None and return_state:
         S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     _check(S_final, "S_final", (B, H, dv, dk), torch.float32, dev)
-    ws_n = workspace_bytes(B, H, T, dk, dv, dtc, var, window, chunk)
+    ws_n = int(lib().falcon_chunk_fwd_workspace(B, H, T, dk, dv, dtc, var, window, chunk))
     if workspace is not None:
         if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_n:
             raise ValueError(f"workspace: need {ws_n} bytes on {dev}")
@@ -159,15 +162,16 @@ def chunk_fwd(q, k, v, alpha, eta, variant, *, window=1, chunk=64, eps=1e-6, S0=
     return o, S_final
 
 
-def varlen_workspace_bytes(N, H, max_seqlen, dk, dv, dtype, variant, window=1, chunk=64) -> int:
+def varlen_workspace_bytes(N, H, max_seqlen, dk, dv, dtype, variant, window=1, chunk=64,
+                           phi="identity") -> int:
     return int(lib().falcon_chunk_fwd_varlen_workspace(N, H, max_seqlen, dk, dv, dtype,
-                                                       _variant(variant), window, chunk))
+                                                       _variant(variant, phi=phi), window, chunk))
 
 
 def chunk_fwd_varlen(q, k, v, alpha, eta, cu_seqlens, variant, *, max_seqlen=None, window=1,
                      chunk=64, eps=1e-6, S0=None, k_prev=None, v_prev=None, o=None,
                      S_final=None, return_state=True, workspace=None, stream=None,
-                     align="prefix"):
+                     align="prefix", phi="identity"):
     """Chunk-parallel forward over N packed sequences.  q, k [H,total_T,dk];
     v [H,total_T,dv]; alpha, eta [H,total_T] fp32; cu_seqlens int32 [N+1] on
     the device (sequence n = rows cu_seqlens[n] .. cu_seqlens[n+1]-1 of every
@@ -176,7 +180,7 @@ def chunk_fwd_varlen(q, k, v, alpha, eta, cu_seqlens, variant, *, max_seqlen=Non
     cu_seqlens (a device-to-host copy, which synchronizes).  Returns
     (o [H,total_T,dv], S_final [N,H,dv,dk] or None)."""
     import torch
-    var = _variant(variant, align)
+    var = _variant(variant, align, phi)
     H, Ttot, dk = k.shape
     dv = v.shape[-1]
     dev, dt = k.device, k.dtype
@@ -205,7 +209,8 @@ def chunk_fwd_varlen(q, k, v, alpha, eta, cu_seqlens, variant, *, max_seqlen=Non
     if S_final is None and return_state:
         S_final = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
     _check(S_final, "S_final", (N, H, dv, dk), torch.float32, dev)
-    ws_n = varlen_workspace_bytes(N, H, max_seqlen, dk, dv, dtc, var, window, chunk)
+    ws_n = int(lib().falcon_chunk_fwd_varlen_workspace(N, H, max_seqlen, dk, dv, dtc, var,
+                                                        window, chunk))
     if workspace is not None:
         if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_n:
             raise ValueError(f"workspace: need {ws_n} bytes on {dev}")
@@ -223,12 +228,12 @@ def chunk_fwd_varlen(q, k, v, alpha, eta, cu_seqlens, variant, *, max_seqlen=Non
 
 
 def decode_step(S, k_cache, q, k, v, alpha, eta, variant, *, eps=1e-6, o=None, stream=None,
-                align="prefix"):
+                align="prefix", phi="identity"):
     """One decode step.  S [N,H,dv,dk] fp32 and k_cache [N,H,1,dk] are
     updated in place; q,k [N,H,dk], v [N,H,dv] (bf16 or fp32), alpha, eta
     [N,H] fp32.  Returns o [N,H,dv]."""
     import torch
-    var = _variant(variant, align)
+    var = _variant(variant, align, phi)
     N, H, dv, dk = S.shape
     dev, dt = k.device, k.dtype
     dtc = _dt(k)
@@ -251,13 +256,13 @@ def decode_step(S, k_cache, q, k, v, alpha, eta, variant, *, eps=1e-6, o=None, s
 
 
 def decode_step_window(S, k_cache, v_cache, q, k, v, alpha, eta, variant, *, eps=1e-6, o=None,
-                       stream=None, align="prefix"):
+                       stream=None, align="prefix", phi="identity"):
     """One Falcon-3 / Falcon-3A decode step.  S [N,H,dv,dk] fp32, k_cache
     [N,H,W,dk] (slot w = k_{t-1-w}) and v_cache [N,H,W-1,dv] (slot w-1 =
     v_{t-w}; None when W = 1) are updated in place; q,k [N,H,dk], v [N,H,dv]
     (bf16 or fp32), alpha, eta [N,H] fp32.  Returns o [N,H,dv]."""
     import torch
-    var = _variant(variant, align)
+    var = _variant(variant, align, phi)
     N, H, dv, dk = S.shape
     dev, dt = k.device, k.dtype
     dtc = _dt(k)

@@ -26,14 +26,26 @@ int norm_of(int v) {
 
 bool is_delta(int v) { return v == FALCON_F1 || v == FALCON_F2 || v == FALCON_F3; }
 
-// The variant argument: a variant code, optionally OR-ed with FALCON_SAME_STEP.
-// Splits it into the code and the key lag (1: pair (k_{t-1}, v_t), 0: (k_t, v_t));
-// returns false for unknown flag bits.
-bool split_variant(int var, int* base, int* lag) {
-    if (var & ~(0xFF | FALCON_SAME_STEP)) return false;
+// The variant argument: a variant code, optionally OR-ed with FALCON_SAME_STEP
+// and with one of FALCON_PHI_L2 / FALCON_PHI_SILU.  Splits it into the code,
+// the key lag (1: pair (k_{t-1}, v_t), 0: (k_t, v_t)) and the feature map
+// (0 identity, 1 L2, 2 SiLU); returns false for unknown or conflicting flags.
+bool split_variant(int var, int* base, int* lag, int* phi = nullptr) {
+    if (var & ~(0xFF | FALCON_SAME_STEP | FALCON_PHI_L2 | FALCON_PHI_SILU)) return false;
+    if ((var & FALCON_PHI_L2) && (var & FALCON_PHI_SILU)) return false;
     *base = var & 0xFF;
     *lag = (var & FALCON_SAME_STEP) ? 0 : 1;
+    if (phi) *phi = (var & FALCON_PHI_L2) ? 1 : ((var & FALCON_PHI_SILU) ? 2 : 0);
     return true;
+}
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Workspace of the mapped keys, queries and halo keys (a feature map is
+// selected): `rows` rows of dk entries twice, then BH * W halo rows.
+size_t phi_bytes(size_t rows, size_t BH, int W, int dk, int dt) {
+    const size_t es = dt == FALCON_BF16 ? 2 : 4;
+    return 2 * align256(rows * dk * es) + align256(BH * W * dk * es);
 }
 
 bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -76,10 +88,24 @@ size_t falcon_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, falcon_dt
     if (check_chunk(p, p, p, (const float*)p, (const float*)p, nullptr, nullptr, nullptr, p,
                     nullptr, B, H, T, dk, dv, dt, var, window, chunk, 0.0f) != FALCON_OK)
         return 0;
-    int base = 0, lag = 1;
-    split_variant(var, &base, &lag);
-    return falcon::chunk_workspace_bytes(B * H, T, (int)dt, chunk, window, norm_of(base),
-                                         is_delta(base));
+    int base = 0, lag = 1, phi = 0;
+    split_variant(var, &base, &lag, &phi);
+    const size_t rec = align256(falcon::chunk_workspace_bytes(B * H, T, (int)dt, chunk, window,
+                                                              norm_of(base), is_delta(base)));
+    if (rec == 0 || phi == 0) return rec;
+    return rec + phi_bytes((size_t)B * H * T, (size_t)B * H, window, dk, dt);
+}
+
+// Where the mapped keys, queries and halo keys go (after the records).
+void set_phi_buffers(falcon::ChunkArgs& a, void* ws, size_t rows, int BH, int W, int dk, int dt,
+                     size_t rec) {
+    const size_t es = dt == FALCON_BF16 ? 2 : 4;
+    char* p = static_cast<char*>(ws) + rec;
+    a.kphi = p;
+    a.qphi = p + align256(rows * dk * es);
+    a.kpphi = p + 2 * align256(rows * dk * es);
+    (void)BH;
+    (void)W;
 }
 
 int falcon_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
@@ -93,9 +119,15 @@ int falcon_chunk_fwd(const void* q, const void* k, const void* v, const float* a
     const size_t need = falcon_chunk_fwd_workspace(B, H, T, dk, dv, dt, var, window, chunk);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FALCON_ERR_WORKSPACE;
     if (T == 0 && S_final == nullptr) return FALCON_OK;
-    int base = 0, lag = 1;
-    split_variant(var, &base, &lag);
+    int base = 0, lag = 1, phi = 0;
+    split_variant(var, &base, &lag, &phi);
     falcon::ChunkArgs a;
+    a.phi = phi;
+    a.kphi = a.qphi = a.kpphi = nullptr;
+    if (phi && need > 0)
+        set_phi_buffers(a, workspace, (size_t)B * H * T, B * H, window, dk, dt,
+                        align256(falcon::chunk_workspace_bytes(B * H, T, (int)dt, chunk, window,
+                                                               norm_of(base), is_delta(base))));
     a.q = q;
     a.k = k;
     a.v = v;
@@ -156,9 +188,16 @@ int falcon_chunk_fwd_varlen(const void* q, const void* k, const void* v, const f
                                                           window, chunk);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FALCON_ERR_WORKSPACE;
     if ((max_seqlen == 0 || total_T == 0) && S_final == nullptr) return FALCON_OK;
-    int base = 0, lag = 1;
-    split_variant(var, &base, &lag);
+    int base = 0, lag = 1, phi = 0;
+    split_variant(var, &base, &lag, &phi);
     falcon::ChunkArgs a;
+    a.phi = phi;
+    a.kphi = a.qphi = a.kpphi = nullptr;
+    if (phi && need > 0)  // room for N * max_seqlen >= total_T rows per head
+        set_phi_buffers(a, workspace, (size_t)N * H * max_seqlen, N * H, window, dk, dt,
+                        align256(falcon::chunk_workspace_bytes(N * H, max_seqlen, (int)dt, chunk,
+                                                               window, norm_of(base),
+                                                               is_delta(base))));
     a.q = q;
     a.k = k;
     a.v = v;
@@ -192,8 +231,8 @@ int falcon_decode_step(float* S, void* k_cache, const void* q, const void* k, co
                        const float* alpha, const float* eta, void* o, int N, int H, int dk,
                        int dv, falcon_dtype dt, falcon_variant var_arg, int window, float eps,
                        hipStream_t stream) {
-    int var = 0, lag = 1;
-    if (!split_variant(var_arg, &var, &lag) || !is_variant(var)) return FALCON_ERR_UNSUPPORTED;
+    int var = 0, lag = 1, phi = 0;
+    if (!split_variant(var_arg, &var, &lag, &phi) || !is_variant(var)) return FALCON_ERR_UNSUPPORTED;
     // the window rules have their own entry point, falcon_decode_step_window
     if (var == FALCON_F3 || var == FALCON_F3A) return FALCON_ERR_UNSUPPORTED;
     if (dt != FALCON_FP32 && dt != FALCON_BF16) return FALCON_ERR_UNSUPPORTED;
@@ -217,6 +256,7 @@ int falcon_decode_step(float* S, void* k_cache, const void* q, const void* k, co
     a.norm = norm_of(var);
     a.delta = is_delta(var) ? 1 : 0;
     a.lag = lag;
+    a.phi = phi;
     a.eps = eps;
     hipError_t e = falcon::launch_decode(a, (int)dt, dk, stream);
     return e == hipSuccess ? FALCON_OK : FALCON_ERR_HIP;
@@ -227,8 +267,8 @@ int falcon_decode_step_window(float* S, void* k_cache, void* v_cache, const void
                               const float* eta, void* o, int N, int H, int dk, int dv,
                               falcon_dtype dt, falcon_variant var_arg, int window, float eps,
                               hipStream_t stream) {
-    int var = 0, lag = 1;
-    if (!split_variant(var_arg, &var, &lag)) return FALCON_ERR_UNSUPPORTED;
+    int var = 0, lag = 1, phi = 0;
+    if (!split_variant(var_arg, &var, &lag, &phi)) return FALCON_ERR_UNSUPPORTED;
     if (var != FALCON_F3 && var != FALCON_F3A) return FALCON_ERR_UNSUPPORTED;
     if (dt != FALCON_FP32 && dt != FALCON_BF16) return FALCON_ERR_UNSUPPORTED;
     if (N < 1 || H < 1 || dk < 1 || dv < 1 || window < 1) return FALCON_ERR_SHAPE;
@@ -253,6 +293,7 @@ int falcon_decode_step_window(float* S, void* k_cache, void* v_cache, const void
     a.W = window;
     a.delta = var == FALCON_F3 ? 1 : 0;
     a.lag = lag;
+    a.phi = phi;
     a.eps = eps;
     hipError_t e = falcon::launch_decode_window(a, (int)dt, dk, stream);
     return e == hipSuccess ? FALCON_OK : FALCON_ERR_HIP;

@@ -264,23 +264,35 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a, void* ws, 
     T* recT = reinterpret_cast<T*>(rec);
     float* recS = reinterpret_cast<float*>(rec + R::kScalBytes);
 
-    // ---- stage keys (virtual rows) and queries ----
+    // ---- stage keys (virtual rows) and queries, with the feature map; with a
+    // map, also write the mapped keys, halo keys and queries for the state pass
+    T* kq = a.phi ? static_cast<T*>(a.kphi) + sr.row0 * D : nullptr;
+    T* qq = a.phi ? static_cast<T*>(a.qphi) + sr.row0 * D : nullptr;
+    T* kpq = (a.phi && a.kpphi) ? static_cast<T*>(a.kpphi) + (size_t)bh * W * D : nullptr;
 #pragma unroll
     for (int it = 0; it < NXL; ++it) {
         const int c = tid + 256 * it;
-        if (c < CV * CPR) {
-            const int i = c / CPR, col = (c % CPR) * EPC;
-            const int s = WIN ? i / Wv : i, w = WIN ? i - s * Wv : 0;
-            const int t = t0 + s, tau = t - w - a.lag;  // x_i = k_{t-w-lag}
-            const bool okx = i < NVR && t < T_ && (tau >= 0 || kp != nullptr);
-            const T* px = tau >= 0 ? kg + (size_t)tau * D + col
-                                   : (kp ? kp + (size_t)(W + tau) * D + col : kg + col);
-            const bool okq = i < Ct && t0 + i < T_;
-            const T* pq = okq ? qg + (size_t)(t0 + i) * D + col : qg + col;
-            const u32x4 xv = sel16(okx, *reinterpret_cast<const u32x4*>(okx ? px : kg + col));
-            const u32x4 qv = sel16(okq, *reinterpret_cast<const u32x4*>(pq));
+        const bool in = c < CV * CPR;
+        const int i = (in ? c : 0) / CPR, col = ((in ? c : 0) % CPR) * EPC;
+        const int s = WIN ? i / Wv : i, w = WIN ? i - s * Wv : 0;
+        const int t = t0 + s, tau = t - w - a.lag;  // x_i = k_{t-w-lag}
+        const bool okx = in && i < NVR && t < T_ && (tau >= 0 || kp != nullptr);
+        const T* px = tau >= 0 ? kg + (size_t)tau * D + col
+                               : (kp ? kp + (size_t)(W + tau) * D + col : kg + col);
+        const bool okq = in && i < Ct && t0 + i < T_;
+        const T* pq = okq ? qg + (size_t)(t0 + i) * D + col : qg + col;
+        u32x4 xv = sel16(okx, *reinterpret_cast<const u32x4*>(okx ? px : kg + col));
+        u32x4 qv = sel16(okq, *reinterpret_cast<const u32x4*>(pq));
+        xv = phi_piece<E, CPR>(a.phi, xv);  // every lane: the row norm is a group sum
+        qv = phi_piece<E, CPR>(a.phi, qv);
+        if (in) {
             *reinterpret_cast<u32x4*>(&sm.X[i][col]) = xv;
             *reinterpret_cast<u32x4*>(&sm.Q[i][col]) = qv;
+        }
+        if (a.phi) {
+            if (okx && tau >= 0) *reinterpret_cast<u32x4*>(kq + (size_t)tau * D + col) = xv;
+            else if (okx && kpq) *reinterpret_cast<u32x4*>(kpq + (size_t)(W + tau) * D + col) = xv;
+            if (okq) *reinterpret_cast<u32x4*>(qq + (size_t)(t0 + i) * D + col) = qv;
         }
     }
     if (tid < CV) {
@@ -1637,6 +1649,29 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
 #pragma unroll
             for (int it = 0; it < NXL; ++it) px[it] |= pxh[it];
         }
+        if (a.phi) {
+            // the feature map, and the mapped keys, halo keys and queries for
+            // the state pass (a key appearing in several virtual rows is
+            // written with the same value by each)
+            const int t0 = tile * Ct;
+            T* kq = static_cast<T*>(a.kphi) + jb.sr.row0 * D;
+            T* qq = static_cast<T*>(a.qphi) + jb.sr.row0 * D;
+            T* kpq = a.kpphi ? static_cast<T*>(a.kpphi) + (size_t)bh * W * D : nullptr;
+#pragma unroll
+            for (int it = 0; it < NXL; ++it) {
+                px[it] = phi_piece<E, CPR>(a.phi, px[it]);
+                pq[it] = phi_piece<E, CPR>(a.phi, pq[it]);
+                const int c = tid + 256 * it;
+                const int i = c / CPR, col = (c % CPR) * 8;
+                const int tau = t0 + xrel[it];
+                if (xok[it] && tau >= 0 && tau < T_)
+                    *reinterpret_cast<u32x4*>(kq + (size_t)tau * D + col) = px[it];
+                else if (xok[it] && tau < 0 && kpq)
+                    *reinterpret_cast<u32x4*>(kpq + (size_t)(W + tau) * D + col) = px[it];
+                if (qvo[it] != kOob && t0 + i < T_)
+                    *reinterpret_cast<u32x4*>(qq + (size_t)(t0 + i) * D + col) = pq[it];
+            }
+        }
 #pragma unroll
         for (int it = 0; it < NXL; ++it) {
             const int c = tid + 256 * it;
@@ -2015,6 +2050,12 @@ static hipError_t launch_one(const ChunkArgs& a, void* ws, hipStream_t stream) {
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+    }
+    if (a.phi) {
+        // the state pass reads the mapped keys, halo keys and queries
+        b.k = a.kphi;
+        b.q = a.qphi;
+        b.k_prev = a.k_prev ? a.kpphi : nullptr;
     }
     const int nvs = D / 64;
     const int bh8 = (b.BH + 7) / 8 * 8;

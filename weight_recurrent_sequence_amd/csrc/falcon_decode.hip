@@ -23,6 +23,25 @@
 
 namespace falcon {
 
+// Feature map on one row held as 16 entries per lane by a group of G lanes:
+// L2 normalization (the row norm a DPP sum over the group; 0 for a zero row)
+// or SiLU elementwise.  phi 0 leaves the row as it is.
+template <int G>
+__device__ __forceinline__ void phi_row(int phi, float (&x)[16]) {
+    if (phi == 1) {
+        float n2 = 0.f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) n2 += x[c] * x[c];
+        n2 = group_sum_dpp<G>(n2);
+        const float sc = n2 > 0.f ? rsqrtf(n2) : 0.f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) x[c] *= sc;
+    } else if (phi == 2) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) x[c] = x[c] / (1.f + __expf(-x[c]));
+    }
+}
+
 template <class E, int D>
 __global__ __launch_bounds__(256, 2) void decode_step_kernel(DecodeArgs a) {
     using T = typename E::T;
@@ -71,6 +90,8 @@ __global__ __launch_bounds__(256, 2) void decode_step_kernel(DecodeArgs a) {
             s[p][j] = __builtin_nontemporal_load(
                 reinterpret_cast<const f32x4*>(S + (size_t)row * D + 4 * seg + 4 * LPR * j));
     }
+    phi_row<LPR>(a.phi, x);
+    phi_row<LPR>(a.phi, qv);
 
     float n2 = 0.f, n1 = 0.f, xq = 0.f;
 #pragma unroll
@@ -225,6 +246,10 @@ __global__ __launch_bounds__(256, 2) void decode_window_kernel(DecodeWinArgs a) 
             s[p][j] = __builtin_nontemporal_load(
                 reinterpret_cast<const f32x4*>(S + (size_t)row * D + 4 * seg + 4 * LPR * j));
     }
+
+    phi_row<LPR>(a.phi, qv);
+#pragma unroll
+    for (int w = 0; w < W; ++w) phi_row<LPR>(a.phi, x[w]);
 
     // ---- targets to LDS; window norm and x_w . q ----
     if (tid < D) {

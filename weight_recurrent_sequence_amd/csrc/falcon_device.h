@@ -162,4 +162,38 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Feature maps on keys and queries (0 identity, 1 L2 normalization x/||x||
+// with 0 for x = 0, 2 SiLU x / (1 + e^-x)) applied to one 16-byte piece of a
+// row held by G consecutive lanes, one piece each (the row norm is a sum over
+// the lane group).  Every lane of the wave must call it.  The identity
+// returns the piece unchanged (no rounding).
+template <class E, int G>
+__device__ __forceinline__ u32x4 phi_piece(int phi, u32x4 v) {
+    using T = typename E::T;
+    constexpr int EPP = 16 / E::kBytes;
+    if (phi == 0) return v;
+    const T* e = reinterpret_cast<const T*>(&v);
+    float f[EPP];
+#pragma unroll
+    for (int u = 0; u < EPP; ++u) f[u] = E::to_f(e[u]);
+    if (phi == 1) {
+        float n2 = 0.f;
+#pragma unroll
+        for (int u = 0; u < EPP; ++u) n2 += f[u] * f[u];
+        if constexpr (G <= 16) n2 = group_sum_dpp<G>(n2);
+        else n2 = group_sum<G>(n2);
+        const float sc = n2 > 0.f ? rsqrtf(n2) : 0.f;
+#pragma unroll
+        for (int u = 0; u < EPP; ++u) f[u] *= sc;
+    } else {
+#pragma unroll
+        for (int u = 0; u < EPP; ++u) f[u] = f[u] / (1.f + __expf(-f[u]));
+    }
+    u32x4 out;
+    T* o = reinterpret_cast<T*>(&out);
+#pragma unroll
+    for (int u = 0; u < EPP; ++u) o[u] = E::from_f(f[u]);
+    return out;
+}
+
 }  // namespace falcon

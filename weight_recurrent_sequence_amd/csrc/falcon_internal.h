@@ -48,6 +48,14 @@ struct ChunkArgs {
     int lag;     // key of step t's pair w is k_{t-w-lag}: 1 prefix-aligned, 0 same-step
     int norm;    // NormKind
     float eps;
+    // Feature map on keys and queries (0 identity, 1 L2, 2 SiLU).  With a map,
+    // the intra-chunk kernel writes the mapped keys, queries and halo keys to
+    // kphi, qphi (layout of k, q) and kpphi (layout of k_prev), and the state
+    // pass reads those instead.
+    int phi;
+    void* kphi;
+    void* qphi;
+    void* kpphi;
 };
 
 struct DecodeArgs {
@@ -63,6 +71,7 @@ struct DecodeArgs {
     int norm;    // kNormScalar or kNormColumn
     int delta;   // 1: regression (residual write), 0: inner-product write
     int lag;     // 1: x = k_cache (prefix-aligned), 0: x = k (same-step)
+    int phi;     // feature map on x and q (0 identity, 1 L2, 2 SiLU); caches stay raw
     float eps;
 };
 
@@ -80,6 +89,7 @@ struct DecodeWinArgs {
     int W;
     int delta;   // 1: Falcon-3 (residual writes), 0: Falcon-3A
     int lag;     // pair w's key is k_{t-w-lag}: slot w+lag-1 of k_cache, or k when w+lag = 0
+    int phi;     // feature map on the keys and q (0 identity, 1 L2, 2 SiLU); caches stay raw
     float eps;
 };
 
