@@ -8,7 +8,8 @@ resident in HBM: the intra-chunk kernel (norms, decay scan, masked Gram
 blocks, diagonal-block inverses) and the state-passing kernel (residuals,
 blocked forward substitution, outputs, state update).  `value` is tokens
 (B*T) per second.  The same line reports Falcon-1A on the same batch,
-Falcon-1 with same-step pairs (k_t, v_t), Falcon-1 over 16 packed sequences
+Falcon-1 with same-step pairs (k_t, v_t), Falcon-1 with L2-normalized keys
+and queries, Falcon-1 over 16 packed sequences
 of mixed lengths with the same token count, the decode step (256 sequences x
 32 heads, d=128, 1024 consecutive steps) and the
 Falcon-3 decode step at the same shape with a window of four, each with its
@@ -215,6 +216,18 @@ def main():
     ms_s, _ = timed(step_f1_same, args.steps, args.warmup)
     gbs_s = nbytes / (ms_s / 1e3) / 1e9
 
+    ws_phi = torch.empty(fal.workspace_bytes(B, H, T, D, D, fal.BF16, "F1", 1, C, phi="l2"),
+                         dtype=torch.uint8, device=dev)
+
+    def step_f1_l2():
+        fal.chunk_fwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], "F1", chunk=C, o=o,
+                      S_final=S_fin, workspace=ws_phi, phi="l2")
+
+    print(f"[bench] F1 with L2-normalized keys and queries", file=sys.stderr, flush=True)
+    ms_p, _ = timed(step_f1_l2, args.steps, args.warmup)
+    gbs_p = nbytes / (ms_p / 1e3) / 1e9
+    del ws_phi
+
     # Falcon-1 over a packed batch of 16 sequences of mixed lengths with the
     # same 32768 tokens per head (falcon_chunk_fwd_varlen)
     rl = __import__("numpy").random.default_rng(5)
@@ -260,6 +273,9 @@ def main():
         "falcon1_same_step": {"tokens_per_s": B * T / (ms_s / 1e3), "ms_per_step": ms_s,
                               "hbm_gbs": gbs_s, "hbm_frac": gbs_s / HBM_PEAK_GBS,
                               "pairs": "(k_t, v_t), FALCON_SAME_STEP"},
+        "falcon1_phi_l2": {"tokens_per_s": B * T / (ms_p / 1e3), "ms_per_step": ms_p,
+                           "hbm_gbs": gbs_p, "hbm_frac": gbs_p / HBM_PEAK_GBS,
+                           "phi": "L2 normalization of keys and queries, FALCON_PHI_L2"},
         "falcon1_varlen": {"tokens_per_s": B * T / (ms_v / 1e3), "ms_per_step": ms_v,
                            "hbm_gbs": gbs_v, "hbm_frac": gbs_v / HBM_PEAK_GBS,
                            "batch": f"{len(lengths)} packed sequences, lengths {min(lengths)}.."

@@ -1633,8 +1633,9 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
                     (int)__builtin_amdgcn_readfirstlane(e[3])}};
     };
     int job = blockIdx.x;
-    u32x4 e_cur = fetch(job), e_nxt = fetch(job + gridDim.x);
-    Job jcur = decode(job, e_cur);
+    const u32x4 zero16 = {0u, 0u, 0u, 0u};
+    u32x4 e_nxt = a.jobs ? fetch(job + gridDim.x) : zero16;
+    Job jcur = decode(job, a.jobs ? fetch(job) : zero16);
     if (job < njobs) load(jcur);
     for (; job < njobs; job += gridDim.x) {
         const Job jb = jcur;
@@ -1690,7 +1691,7 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
             jcur = decode(job + gridDim.x, e_nxt);
             load(jcur);
         }
-        e_nxt = fetch(job + 2 * gridDim.x);
+        if (a.jobs) e_nxt = fetch(job + 2 * gridDim.x);
         // a packed sequence shorter than the longest leaves tiles that the
         // state pass never reads: stage them (the prefetch chain) and move on
         if (tile >= tiles_of(T_, Ct)) continue;
