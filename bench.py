@@ -50,6 +50,14 @@ def chunk_bytes(B, H, T, D, elem=2, with_state_out=True):
     return B * H * T * per_token_head + (B * H * D * D * 4 if with_state_out else 0)
 
 
+def bwd_bytes(B, H, T, D, elem=2):
+    """Algorithmic HBM bytes of one backward call: q, k, v, d_o read and dq,
+    dk, dv written once (elem bytes each), alpha and eta read and their
+    gradients written (fp32), dS_final read and dS0 written (fp32)."""
+    per_token_head = 7 * D * elem + 4 * 4
+    return B * H * T * per_token_head + 2 * B * H * D * D * 4
+
+
 def chunk_flops(B, H, T, D, C, delta=True):
     """Algorithmic flops of the chunk form per call, counted on full C x C
     tiles: Grams, the triangular solve, the two C x d products per side of the
@@ -252,6 +260,26 @@ def main():
     gbs_v = nbytes / (ms_v / 1e3) / 1e9
     del tv, ov, wsv
 
+    # Backward (falcon_chunk_bwd) of Falcon-1 and Falcon-1A on the same batch:
+    # forward recompute with checkpoints, reverse tile scan, per-tile gradients
+    d_o_np, dS_np = I.make_cotangents(B, H, T, D, D, seed=w["seed"])
+    d_o = torch.from_numpy(d_o_np).view(torch.bfloat16).to(dev)
+    dS_fin = torch.from_numpy(dS_np).to(dev)
+    del d_o_np, dS_np
+    ws_b = torch.empty(fal.bwd_workspace_bytes(B, H, T, D, D, fal.BF16, "F1", 1, C),
+                       dtype=torch.uint8, device=dev)
+
+    def step_bwd(variant):
+        return lambda: fal.chunk_bwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], d_o, variant,
+                                     dS_final=dS_fin, chunk=C, workspace=ws_b)
+
+    print(f"[bench] F1 backward", file=sys.stderr, flush=True)
+    ms_b, _ = timed(step_bwd("F1"), args.steps, args.warmup)
+    print(f"[bench] F1A backward", file=sys.stderr, flush=True)
+    ms_ba, _ = timed(step_bwd("F1A"), args.steps, args.warmup)
+    nbytes_b = bwd_bytes(B, H, T, D)
+    del ws_b, d_o, dS_fin
+
     line = {
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -276,6 +304,15 @@ def main():
         "falcon1_phi_l2": {"tokens_per_s": B * T / (ms_p / 1e3), "ms_per_step": ms_p,
                            "hbm_gbs": gbs_p, "hbm_frac": gbs_p / HBM_PEAK_GBS,
                            "phi": "L2 normalization of keys and queries, FALCON_PHI_L2"},
+        "falcon1_bwd": {"tokens_per_s": B * T / (ms_b / 1e3), "ms_per_step": ms_b,
+                        "hbm_gbs": nbytes_b / (ms_b / 1e3) / 1e9,
+                        "hbm_frac": nbytes_b / (ms_b / 1e3) / 1e9 / HBM_PEAK_GBS,
+                        "algorithmic_bytes_per_call": nbytes_b,
+                        "call": "falcon_chunk_bwd: dq, dk, dv, dalpha, deta, dS0 from d_o and "
+                                "dS_final (forward recomputed inside)"},
+        "falcon1a_bwd": {"tokens_per_s": B * T / (ms_ba / 1e3), "ms_per_step": ms_ba,
+                         "hbm_gbs": nbytes_b / (ms_ba / 1e3) / 1e9,
+                         "hbm_frac": nbytes_b / (ms_ba / 1e3) / 1e9 / HBM_PEAK_GBS},
         "falcon1_varlen": {"tokens_per_s": B * T / (ms_v / 1e3), "ms_per_step": ms_v,
                            "hbm_gbs": gbs_v, "hbm_frac": gbs_v / HBM_PEAK_GBS,
                            "batch": f"{len(lengths)} packed sequences, lengths {min(lengths)}.."

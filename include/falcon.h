@@ -172,6 +172,47 @@ int falcon_chunk_fwd_varlen(const void* q, const void* k, const void* v, const f
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Backward pass of falcon_chunk_fwd (the gradients of a loss through o and
+ * S_T; "Fast Weight Attention for Continual Learning", authors' abstract: the
+ * rules have a chunk-parallel form, whose derivative this computes).  Given
+ * the forward's inputs and the cotangents d_o = dL/do and dS_final =
+ * dL/dS_T, writes dL/d(q, k, v, alpha, eta, S0, k_prev).  The forward is
+ * recomputed inside the call (its checkpoints live in the workspace).
+ *
+ *   q, k, v, alpha, eta, S0, k_prev, v_prev
+ *               as for falcon_chunk_fwd (inputs of the forward)
+ *   d_o         [B,H,T,dv]  dtype dt
+ *   dS_final    [B,H,dv,dk] fp32, or NULL for zero
+ *   dq, dk, dv  [B,H,T,d]   dtype dt outputs (rounded to nearest even)
+ *   dalpha, deta [B,H,T]    fp32 outputs
+ *   dS0         [B,H,dv,dk] fp32 output, or NULL (not wanted)
+ *   dk_prev     [B,H,W,dk]  dtype dt output, or NULL (not wanted); zero where
+ *               no pair reads the halo key (or k_prev is NULL)
+ *   dv_prev     unused (a window of one reads no value before the sequence)
+ *   workspace   falcon_chunk_bwd_workspace(...) bytes: the forward's
+ *               records, then the bf16 state at every tile start, the state
+ *               gradient at every tile end and Delta of every
+ *               tile, all bf16: about B*H*ceil(T/chunk)*dk*(4 dk + 2 chunk)
+ *               bytes
+ * Outputs must not alias inputs or each other.
+ *
+ * Support matrix: dt bf16, dk = dv in {64, 128}, chunk 64, var F1 or F1A
+ * (or F3 / F3A with window 1, the same rule), with FALCON_SAME_STEP and the
+ * feature-map flags.  Other arguments that falcon_chunk_fwd accepts return
+ * FALCON_ERR_UNSUPPORTED; errors otherwise as for falcon_chunk_fwd.
+ * falcon_chunk_bwd_workspace returns 0 for unsupported arguments and T = 0.
+ */
+size_t falcon_chunk_bwd_workspace(int B, int H, int T, int dk, int dv, falcon_dtype dt,
+                                  falcon_variant var, int window, int chunk);
+int falcon_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
+                     const float* eta, const float* S0, const void* k_prev, const void* v_prev,
+                     const void* d_o, const float* dS_final, void* dq, void* dk, void* dv,
+                     float* dalpha, float* deta, float* dS0, void* dk_prev, void* dv_prev,
+                     int B, int H, int T, int dk_dim, int dv_dim, falcon_dtype dt,
+                     falcon_variant var, int window, int chunk, float eps, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/*
  * One decode step for N independent sequences x H heads (one token each):
  * x = k_cache (the previous key; with FALCON_SAME_STEP the new key k),
  * S' = alpha S, write as above, o = S q, then k_cache <- k.

@@ -28,6 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["falcon_chunk_fwd", "falcon_chunk_fwd_workspace",
+                                           "falcon_chunk_bwd", "falcon_chunk_bwd_workspace",
                                            "falcon_chunk_fwd_varlen",
                                            "falcon_chunk_fwd_varlen_workspace",
                                            "falcon_decode_step", "falcon_decode_step_window",
@@ -213,3 +214,45 @@ def test_feature_map_workspace_holds_the_mapped_inputs(L):
     for flag in (0x200, 0x400, 0x200 | 0x100):
         got = L.falcon_chunk_fwd_workspace(B, H, T, d, d, 1, 3 | flag, W, 64)
         assert got == al(base) + 2 * al(B * H * T * d * es) + al(B * H * W * d * es)
+
+
+def bwd(L, **kw):
+    a = dict(q=P, k=P, v=P, alpha=P, eta=P, S0=None, k_prev=None, v_prev=None, do=P, dS=None,
+             dq=P, dk=P, dv=P, dal=P, det=P, dS0=None, dkp=None, dvp=None, B=2, H=4, T=100,
+             dk_=128, dv_=128, dt=1, var=1, window=1, chunk=64, eps=1e-6, ws=None, wsn=0)
+    a.update(kw)
+    return L.falcon_chunk_bwd(a["q"], a["k"], a["v"], a["alpha"], a["eta"], a["S0"], a["k_prev"],
+                              a["v_prev"], a["do"], a["dS"], a["dq"], a["dk"], a["dv"], a["dal"],
+                              a["det"], a["dS0"], a["dkp"], a["dvp"], a["B"], a["H"], a["T"],
+                              a["dk_"], a["dv_"], a["dt"], a["var"], a["window"], a["chunk"],
+                              ctypes.c_float(a["eps"]), a["ws"], a["wsn"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(var=4), -3), (dict(dt=0), -3), (dict(chunk=32), -3), (dict(var=2), -3),
+    (dict(var=12), -3), (dict(var=3, window=2), -3), (dict(dk_=96, dv_=96), -3),
+    (dict(B=0), -2), (dict(T=-1), -2), (dict(eps=-1.0), -2),
+    (dict(q=None), -1), (dict(do=None), -1), (dict(dq=None), -1), (dict(dk=None), -1),
+    (dict(dv=None), -1), (dict(dal=None), -1), (dict(det=None), -1),
+    (dict(dq=P + 8), -3), (dict(dal=P + 2), -3), (dict(dS0=P + 4), -3),
+    (dict(var=1 | 0x800), -3), (dict(var=1 | 0x600), -3),
+    (dict(), -4), (dict(var=11 | 0x100 | 0x200), -4), (dict(var=3, window=1), -4),
+])
+def test_bwd_rejects(L, kw, code):
+    assert bwd(L, **kw) == code
+
+
+def test_bwd_workspace_sizes(L):
+    """The forward's workspace, then the state at every tile start and the
+    state gradient at every tile end (bf16, d x d each) and Delta (bf16,
+    d x chunk), each 256-byte aligned."""
+    al = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    for var in (1, 11, 1 | 0x100, 11 | 0x200):
+        B, H, T, d = 2, 3, 1000, 128
+        fwd = L.falcon_chunk_fwd_workspace(B, H, T, d, d, 1, var, 1, 64)
+        nt = (T + 63) // 64
+        want = al(fwd) + 2 * al(B * H * nt * d * d * 2) + al(B * H * nt * d * 64 * 2)
+        assert L.falcon_chunk_bwd_workspace(B, H, T, d, d, 1, var, 1, 64) == want
+    assert L.falcon_chunk_bwd_workspace(2, 3, 1000, 128, 128, 1, 2, 1, 64) == 0   # unsupported
+    assert L.falcon_chunk_bwd_workspace(2, 3, 1000, 128, 128, 0, 1, 1, 32) == 0
+    assert L.falcon_chunk_bwd_workspace(2, 3, 0, 128, 128, 1, 1, 1, 64) == 0

@@ -1,0 +1,199 @@
+"""GPU parity of the backward pass (falcon_chunk_bwd) against the fp64
+gradient oracle (oracle/grad.py: autograd over the recurrence, itself pinned
+by finite differences of the C oracle).
+
+The acceptance metric is the forward's: per (batch, head) slice, max|got -
+ref| / max|ref| for every gradient, at the bf16 bar (2e-2)."""
+import numpy as np
+import pytest
+
+from oracle import grad as G
+from tests.gpu_util import TOL, announce, ensure_built, slice_rel_err, to_np
+from weight_recurrent_sequence_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+AX = {"dq": (2, 3), "dk": (2, 3), "dv": (2, 3), "dalpha": (2,), "deta": (2,), "dS0": (2, 3),
+      "dk_prev": (2, 3)}
+NAME = {"dq": "q", "dk": "k", "dv": "v", "dalpha": "alpha", "deta": "eta", "dS0": "S0",
+        "dk_prev": "k_prev"}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    ensure_built()
+    return torch.device("cuda:0")
+
+
+def run_bwd(dev, inp, variant, *, d_o, dS, align="prefix", phi="identity", sl=None):
+    """GPU gradients and oracle gradients (optionally of one (b, h) slice)."""
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    t = inp.to_torch(dev)
+    B, H, T, D = inp.k.shape
+    do_t = torch.from_numpy(np.ascontiguousarray(d_o)).view(torch.bfloat16).to(dev)
+    dS_t = torch.from_numpy(dS).to(dev) if dS is not None else None
+    announce(f"chunk_bwd {variant} B{B} H{H} T{T} d{D} align={align} phi={phi} "
+             f"S0={inp.S0 is not None} halo={inp.k_prev is not None} dS={dS is not None}")
+    g = fal.chunk_bwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], do_t, variant, dS_final=dS_t,
+                      S0=t["S0"], k_prev=t["k_prev"], align=align, phi=phi,
+                      want_dk_prev=True)
+    torch.cuda.synchronize()
+    d = inp.f64(sl)
+    dof = inp.widen(d_o if sl is None else d_o[sl])
+    dSf = None if dS is None else np.asarray(dS if sl is None else dS[sl], np.float64)
+    if sl is not None:
+        d = {k: (None if v is None else v[None, None]) for k, v in d.items()}
+        dof = dof[None, None]
+        dSf = None if dSf is None else dSf[None, None]
+    ref = G.gradients(variant, d["q"], d["k"], d["v"], d["alpha"], d["eta"], dof, dSf,
+                      S0=d["S0"], k_prev=d["k_prev"], align=align, phi=phi)
+    got = {k: (None if v is None else to_np(v)) for k, v in g.items()}
+    if sl is not None:
+        got = {k: (None if v is None else v[sl][None, None]) for k, v in got.items()}
+    return got, ref
+
+
+def check(got, ref, tol, keys=("dq", "dk", "dv", "dalpha", "deta", "dS0", "dk_prev")):
+    """Per-slice errors at the bar.  The gate gradients of a step are dot
+    products (dO_t . Delta, x_t . dOmega_t, ...) that can cancel, and the bf16
+    forward forms Delta from a bf16 right-hand side: at a step whose dot
+    cancels by a factor c the relative error is about c * 2^-9.  A slice of
+    many steps is normalized by its largest gradient, which absorbs this; a
+    slice of fewer than 16 steps has no scale of its own, so there the gate
+    gradients are normalized over all slices of the call."""
+    errs = {}
+    for k in keys:
+        r = ref.get(NAME[k])
+        if r is None or got.get(k) is None:
+            continue
+        assert np.isfinite(got[k]).all(), k
+        ax = AX[k]
+        if k in ("dalpha", "deta") and r.shape[2] < 16:
+            ax = (0, 1, 2)
+        errs[k] = slice_rel_err(got[k], r, ax)
+    bad = {k: e for k, e in errs.items() if e > tol}
+    assert not bad, errs
+    return errs
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T", [150, 64, 1, 65, 128])
+@pytest.mark.parametrize("variant", ["F1", "F1A"])
+def test_bwd_grid(dev, variant, T, D):
+    inp = I.make_chunk_inputs(2, 3, T, D, D, dtype="bf16", seed=1300 + T + D, halo=True,
+                              S0_sd=0.3)
+    d_o, dS = I.make_cotangents(2, 3, T, D, D, seed=1300 + T + D)
+    got, ref = run_bwd(dev, inp, variant, d_o=d_o, dS=dS)
+    check(got, ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("variant", ["F1", "F1A"])
+def test_bwd_without_optional_inputs(dev, variant):
+    """No S0, no halo, no dS_final: the halo key is the constant 0 (its
+    gradient is reported as 0)."""
+    inp = I.make_chunk_inputs(1, 2, 130, 128, 128, dtype="bf16", seed=1320)
+    d_o, _ = I.make_cotangents(1, 2, 130, 128, 128, seed=1320, dS_sd=0)
+    got, ref = run_bwd(dev, inp, variant, d_o=d_o, dS=None)
+    check(got, ref, TOL["bf16"], keys=("dq", "dk", "dv", "dalpha", "deta", "dS0"))
+    assert not np.any(got["dk_prev"])
+
+
+@pytest.mark.parametrize("T", [150, 64])
+@pytest.mark.parametrize("variant", ["F1", "F1A"])
+def test_bwd_same_step(dev, variant, T):
+    inp = I.make_chunk_inputs(2, 2, T, 128, 128, dtype="bf16", seed=1330 + T, halo=True,
+                              S0_sd=0.3)
+    d_o, dS = I.make_cotangents(2, 2, T, 128, 128, seed=1330 + T)
+    got, ref = run_bwd(dev, inp, variant, d_o=d_o, dS=dS, align="same")
+    check(got, ref, TOL["bf16"])
+    assert not np.any(got["dk_prev"])  # same-step pairs never read the halo
+
+
+@pytest.mark.parametrize("phi", ["l2", "silu"])
+@pytest.mark.parametrize("variant", ["F1", "F1A"])
+def test_bwd_feature_maps(dev, variant, phi):
+    inp = I.make_chunk_inputs(2, 2, 150, 128, 128, dtype="bf16", seed=1340, halo=True,
+                              S0_sd=0.3)
+    d_o, dS = I.make_cotangents(2, 2, 150, 128, 128, seed=1340)
+    got, ref = run_bwd(dev, inp, variant, d_o=d_o, dS=dS, phi=phi)
+    check(got, ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("pair", [("F3", "F1"), ("F3A", "F1A")])
+def test_bwd_window_of_one_is_the_scalar_rule(dev, pair):
+    """Falcon-3 with a window of one runs the scalar rule's kernels: bitwise
+    the same gradients."""
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    inp = I.make_chunk_inputs(1, 2, 100, 64, 64, dtype="bf16", seed=1350, halo=True, S0_sd=0.2)
+    d_o, dS = I.make_cotangents(1, 2, 100, 64, 64, seed=1350)
+    t = inp.to_torch(dev)
+    do_t = torch.from_numpy(d_o).view(torch.bfloat16).to(dev)
+    dS_t = torch.from_numpy(dS).to(dev)
+    announce(f"chunk_bwd {pair} window 1")
+    a = fal.chunk_bwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], do_t, pair[0], window=1,
+                      dS_final=dS_t, S0=t["S0"], k_prev=t["k_prev"])
+    b = fal.chunk_bwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], do_t, pair[1],
+                      dS_final=dS_t, S0=t["S0"], k_prev=t["k_prev"])
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_bwd_empty_sequence(dev):
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    inp = I.make_chunk_inputs(2, 2, 0, 64, 64, dtype="bf16", seed=1360, halo=True, S0_sd=0.2)
+    _, dS = I.make_cotangents(2, 2, 0, 64, 64, seed=1360)
+    t = inp.to_torch(dev)
+    do_t = torch.zeros(2, 2, 0, 64, dtype=torch.bfloat16, device=dev)
+    announce("chunk_bwd T=0")
+    g = fal.chunk_bwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], do_t, "F1",
+                      dS_final=torch.from_numpy(dS).to(dev), S0=t["S0"], k_prev=t["k_prev"])
+    torch.cuda.synchronize()
+    assert torch.equal(g["dS0"].cpu(), torch.from_numpy(dS))
+    assert not torch.any(g["dk_prev"].float())
+
+
+def test_bwd_is_deterministic(dev):
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    inp = I.make_chunk_inputs(2, 2, 200, 128, 128, dtype="bf16", seed=1370, halo=True, S0_sd=0.2)
+    d_o, dS = I.make_cotangents(2, 2, 200, 128, 128, seed=1370)
+    t = inp.to_torch(dev)
+    do_t = torch.from_numpy(d_o).view(torch.bfloat16).to(dev)
+    announce("chunk_bwd determinism")
+    a = fal.chunk_bwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], do_t, "F1",
+                      S0=t["S0"], k_prev=t["k_prev"])
+    b = fal.chunk_bwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], do_t, "F1",
+                      S0=t["S0"], k_prev=t["k_prev"])
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("variant", ["F1", "F1A"])
+def test_bwd_full_size_sampled(dev, variant):
+    """B=8, H=16, T=4096, d=128 (the headline forward's shape) in one call;
+    two (b, h) slices are checked against the oracle run on those slices."""
+    w = dict(I.WORKLOADS["falcon1_bf16_B8H16T4096d128"])
+    inp = I.workload_inputs("falcon1_bf16_B8H16T4096d128")
+    d_o, dS = I.make_cotangents(8, 16, 4096, 128, 128, seed=w["seed"])
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    t = inp.to_torch(dev)
+    do_t = torch.from_numpy(d_o).view(torch.bfloat16).to(dev)
+    dS_t = torch.from_numpy(dS).to(dev)
+    announce(f"chunk_bwd {variant} full size B8 H16 T4096 d128")
+    g = fal.chunk_bwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], do_t, variant,
+                      dS_final=dS_t)
+    torch.cuda.synchronize()
+    for sl in [(0, 0), (7, 13)]:
+        d = inp.f64(sl)
+        ref = G.gradients(variant, *(d[n][None, None] for n in ("q", "k", "v", "alpha", "eta")),
+                          inp.widen(d_o[sl])[None, None], np.asarray(dS[sl], np.float64)[None, None])
+        got = {k: (None if v is None else to_np(v[sl])[None, None]) for k, v in g.items()}
+        check(got, ref, TOL["bf16"], keys=("dq", "dk", "dv", "dalpha", "deta", "dS0"))

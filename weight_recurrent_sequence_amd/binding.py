@@ -55,6 +55,10 @@ def lib():
         L.falcon_chunk_fwd_varlen_workspace.argtypes = [ci] * 9
         L.falcon_chunk_fwd_varlen.restype = ci
         L.falcon_chunk_fwd_varlen.argtypes = [vp] * 11 + [ci] * 10 + [cf, vp, sz, vp]
+        L.falcon_chunk_bwd_workspace.restype = sz
+        L.falcon_chunk_bwd_workspace.argtypes = [ci] * 9
+        L.falcon_chunk_bwd.restype = ci
+        L.falcon_chunk_bwd.argtypes = [vp] * 18 + [ci] * 9 + [cf, vp, sz, vp]
         L.falcon_decode_step.restype = ci
         L.falcon_decode_step.argtypes = [vp] * 8 + [ci] * 7 + [cf, vp]
         L.falcon_decode_step_window.restype = ci
@@ -160,6 +164,62 @@ def chunk_fwd(q, k, v, alpha, eta, variant, *, window=1, chunk=64, eps=1e-6, S0=
     if st != 0:
         raise FalconError(st, "falcon_chunk_fwd")
     return o, S_final
+
+
+def bwd_workspace_bytes(B, H, T, dk, dv, dtype, variant, window=1, chunk=64, align="prefix",
+                        phi="identity") -> int:
+    return int(lib().falcon_chunk_bwd_workspace(B, H, T, dk, dv, dtype,
+                                                _variant(variant, align, phi), window, chunk))
+
+
+def chunk_bwd(q, k, v, alpha, eta, d_o, variant, *, dS_final=None, window=1, chunk=64,
+              eps=1e-6, S0=None, k_prev=None, v_prev=None, want_dS0=True, want_dk_prev=None,
+              workspace=None, stream=None, align="prefix", phi="identity"):
+    """Gradients of the chunk forward.  Inputs as for chunk_fwd, plus d_o
+    [B,H,T,dv] (input dtype) and dS_final [B,H,dv,dk] fp32 or None.  Returns a
+    dict with dq, dk, dv (input dtype), dalpha, deta (fp32), dS0 (fp32, or
+    None) and dk_prev (input dtype, when k_prev is given or want_dk_prev)."""
+    import torch
+    var = _variant(variant, align, phi)
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    dev, dt = k.device, k.dtype
+    dtc = _dt(k)
+    _check(q, "q", (B, H, T, dk), dt, dev)
+    _check(k, "k", (B, H, T, dk), dt, dev)
+    _check(v, "v", (B, H, T, dv), dt, dev)
+    _check(d_o, "d_o", (B, H, T, dv), dt, dev)
+    _check(alpha, "alpha", (B, H, T), torch.float32, dev)
+    _check(eta, "eta", (B, H, T), torch.float32, dev)
+    _check(S0, "S0", (B, H, dv, dk), torch.float32, dev)
+    _check(dS_final, "dS_final", (B, H, dv, dk), torch.float32, dev)
+    _check(k_prev, "k_prev", (B, H, window, dk), dt, dev)
+    if window > 1:
+        _check(v_prev, "v_prev", (B, H, window - 1, dv), dt, dev)
+    else:
+        v_prev = None
+    g = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+             dalpha=torch.empty_like(alpha), deta=torch.empty_like(eta),
+             dS0=torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev) if want_dS0 else None)
+    if want_dk_prev is None:
+        want_dk_prev = k_prev is not None
+    g["dk_prev"] = torch.empty((B, H, window, dk), dtype=dt, device=dev) if want_dk_prev else None
+    ws_n = int(lib().falcon_chunk_bwd_workspace(B, H, T, dk, dv, dtc, var, window, chunk))
+    if workspace is not None:
+        if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_n:
+            raise ValueError(f"workspace: need {ws_n} bytes on {dev}")
+        ws, ws_n = workspace, workspace.numel() * workspace.element_size()
+    else:
+        ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n > 0 else None
+    st = lib().falcon_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(S0),
+                                _ptr(k_prev), _ptr(v_prev), _ptr(d_o), _ptr(dS_final),
+                                _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dalpha"]),
+                                _ptr(g["deta"]), _ptr(g["dS0"]), _ptr(g["dk_prev"]), None,
+                                B, H, T, dk, dv, dtc, var, window, chunk, float(eps), _ptr(ws),
+                                ws_n, _stream(stream))
+    if st != 0:
+        raise FalconError(st, "falcon_chunk_bwd")
+    return g
 
 
 def varlen_workspace_bytes(N, H, max_seqlen, dk, dv, dtype, variant, window=1, chunk=64,

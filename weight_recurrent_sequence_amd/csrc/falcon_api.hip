@@ -299,6 +299,120 @@ int falcon_decode_step_window(float* S, void* k_cache, void* v_cache, const void
     return e == hipSuccess ? FALCON_OK : FALCON_ERR_HIP;
 }
 
+size_t falcon_chunk_bwd_workspace(int B, int H, int T, int dk, int dv, falcon_dtype dt,
+                                  falcon_variant var, int window, int chunk) {
+    const size_t fwd = falcon_chunk_fwd_workspace(B, H, T, dk, dv, dt, var, window, chunk);
+    if (fwd == 0) return 0;
+    int base = 0, lag = 1, phi = 0;
+    split_variant(var, &base, &lag, &phi);
+    if (!falcon::chunk_bwd_supported((int)dt, dk, chunk, norm_of(base), window)) return 0;
+    const size_t ntiles = (size_t)((T + chunk - 1) / chunk);
+    const size_t ck = (size_t)B * H * ntiles * dk * dk * 2;
+    const size_t cd = (size_t)B * H * ntiles * dk * chunk * 2;
+    return align256(fwd) + 2 * align256(ck) + align256(cd);
+}
+
+int falcon_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
+                     const float* eta, const float* S0, const void* k_prev, const void* v_prev,
+                     const void* d_o, const float* dS_final, void* dq, void* dk, void* dv,
+                     float* dalpha, float* deta, float* dS0, void* dk_prev, void* dv_prev,
+                     int B, int H, int T, int dk_, int dv_, falcon_dtype dt, falcon_variant var,
+                     int window, int chunk, float eps, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+    int st = check_chunk(q, k, v, alpha, eta, S0, k_prev, v_prev, d_o, dS_final, B, H, T, dk_,
+                         dv_, dt, var, window, chunk, eps);
+    if (st != FALCON_OK) return st;
+    int base = 0, lag = 1, phi = 0;
+    split_variant(var, &base, &lag, &phi);
+    if (!falcon::chunk_bwd_supported((int)dt, dk_, chunk, norm_of(base), window))
+        return FALCON_ERR_UNSUPPORTED;
+    if (T > 0 && (!dq || !dk || !dv || !dalpha || !deta)) return FALCON_ERR_NULL;
+    if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dS0) ||
+        !aligned16(dk_prev) || !aligned16(dv_prev) || !aligned4(dalpha) || !aligned4(deta))
+        return FALCON_ERR_UNSUPPORTED;
+    const size_t need = falcon_chunk_bwd_workspace(B, H, T, dk_, dv_, dt, var, window, chunk);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FALCON_ERR_WORKSPACE;
+    if (T == 0 && dS0 == nullptr && dk_prev == nullptr) return FALCON_OK;
+    (void)dv_prev;  // a window of one reads no value before the sequence
+
+    const int BH = B * H;
+    const int ntiles = (T + chunk - 1) / chunk;
+    const size_t fwd = falcon_chunk_fwd_workspace(B, H, T, dk_, dv_, dt, var, window, chunk);
+    const size_t rec = align256(falcon::chunk_workspace_bytes(BH, T, (int)dt, chunk, window,
+                                                              norm_of(base), is_delta(base)));
+    char* ws = static_cast<char*>(workspace);
+    const size_t ck = align256((size_t)BH * ntiles * dk_ * dk_ * 2);
+    char* ck_s = ws + align256(fwd);
+    char* ck_ds = ck_s + ck;
+    char* ck_d = ck_ds + ck;
+
+    falcon::ChunkArgs a;
+    a.phi = phi;
+    a.kphi = a.qphi = a.kpphi = nullptr;
+    if (phi && T > 0) set_phi_buffers(a, workspace, (size_t)BH * T, BH, window, dk_, dt, rec);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = alpha;
+    a.eta = eta;
+    a.S0 = S0;
+    a.k_prev = k_prev;
+    a.v_prev = v_prev;
+    a.o = nullptr;
+    a.S_final = nullptr;
+    a.BH = BH;
+    a.T = T;
+    a.cu = nullptr;
+    a.H = H;
+    a.Ttot = T;
+    a.order_ws = nullptr;
+    a.order = nullptr;
+    a.toff = nullptr;
+    a.jobs = nullptr;
+    a.W = window;
+    a.lag = lag;
+    a.norm = norm_of(base);
+    a.eps = eps;
+    a.ck_s = ck_s;
+    a.ck_d = ck_d;
+    if (T > 0) {
+        hipError_t e = falcon::launch_chunk(a, (int)dt, dk_, chunk, is_delta(base), workspace, stream);
+        if (e != hipSuccess) return FALCON_ERR_HIP;
+    }
+
+    falcon::BwdArgs b;
+    b.q = phi ? a.qphi : q;
+    b.k = phi ? a.kphi : k;
+    b.k_prev = k_prev ? (phi ? a.kpphi : k_prev) : nullptr;
+    b.q_raw = q;
+    b.k_raw = k;
+    b.kp_raw = k_prev;
+    b.alpha = alpha;
+    b.eta = eta;
+    b.d_o = d_o;
+    b.dS_final = dS_final;
+    b.dq = dq;
+    b.dk = dk;
+    b.dv = dv;
+    b.dalpha = dalpha;
+    b.deta = deta;
+    b.dS0 = dS0;
+    b.dk_prev = dk_prev;
+    b.rec = workspace;
+    b.ck_s = ck_s;
+    b.ck_d = ck_d;
+    b.ck_ds = ck_ds;
+    b.BH = BH;
+    b.T = T;
+    b.ntiles = ntiles;
+    b.W = window;
+    b.lag = lag;
+    b.phi = phi;
+    b.eps = eps;
+    hipError_t e = falcon::launch_chunk_bwd(b, dk_, chunk, is_delta(base), stream);
+    return e == hipSuccess ? FALCON_OK : FALCON_ERR_HIP;
+}
+
 const char* falcon_status_string(int status) {
     switch (status) {
         case FALCON_OK: return "ok";

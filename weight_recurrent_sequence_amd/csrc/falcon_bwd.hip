@@ -1,0 +1,746 @@
+// falcon_bwd.hip -- backward pass of the chunk-parallel form on gfx950.
+//
+// Method ("Fast Weight Attention for Continual Learning", authors' abstract:
+// the rules have a chunk-parallel form; this file differentiates it).  Per
+// tile of CV rows, with S0 the state at the tile start, g the tile-local
+// cumulative log decay, omega_j = r_j x_j the write vectors, the forward is
+//   (I + A) Delta = Y - diag(exp g) X S0^T        (A family: Delta = Y)
+//   O     = diag(exp g) Q S0^T + P Delta
+//   S_end = exp(g_L) S0 + Delta^T diag(exp(g_L - g)) Omega
+// with A[i][j] = [j < i] exp(g_i - g_j) x_i.omega_j and
+// P[t][j] = [j <= t] exp(g_t - g_j) q_t.omega_j.  Given dO and dS_end:
+//   dDelta = P^T dO + diag(hrow) X dS_end^T            hrow_j = exp(g_L-g_j) r_j
+//   dR     = (I + A)^-T dDelta                         (A family: dR = dDelta)
+//   dS0    = exp(g_L) dS_end + dO^T diag(exp g) Q - dR^T diag(exp g) X
+// (the last term only for the delta family), which is a reverse scan over
+// the tiles (kernel 1 below), and then, per tile and independently (kernel 2),
+//   DP[t][j] = [j <= t] exp(g_t - g_j) dO_t.Delta_j
+//   DA[i][j] = -[j < i] exp(g_i - g_j) dR_i.Delta_j
+//   dQ     = diag(exp g) dO S0 + DP Omega
+//   dX     = -diag(exp g) dR S0 + DA Omega
+//   dOmega = DP^T Q + DA^T X + diag(exp(g_L - g)) Delta dS_end
+//   dY     = dR
+// then the write scale (r = eta / (||x||^2 + eps): dx += r dOmega -
+// 2 (r / n) (x.dOmega) x, deta = x.dOmega / n) and the decays: every factor
+// exp(later - earlier) moves with g, so dg_s collects x_i.dX_i - omega_i.dOmega_i
+// of its rows, q_s.dQ_s, and at the tile's last step exp(g_L) <dS_end, S0> +
+// sum_j omega_j.dOmega3_j (dOmega3 the S_end term); dlog(alpha_s) is the sum of
+// dg over the tile's steps from s on.
+//
+// The state at each tile start and Delta come from the forward state pass
+// (bf16 checkpoints: the forward itself forms Delta from a bf16 right-hand
+// side, so a wider copy would carry no more information), the A / P blocks and diagonal inverses from its
+// intra-chunk records: kernel 1 reads them transposed out of LDS
+// (ds_read_b64_tr_b16 on the record's fragment order).
+#include "falcon_device.h"
+#include "falcon_internal.h"
+#include "falcon_records.h"
+
+namespace falcon {
+
+namespace {
+
+typedef uint16_t bf;
+
+__device__ __forceinline__ u32x4 zero_u4() { return u32x4{0u, 0u, 0u, 0u}; }
+
+// Key row of virtual row i of the tile starting at t0 (window 1): k_{t0+i-lag},
+// the halo before the sequence, zero outside.
+__device__ __forceinline__ u32x4 key_piece(const bf* kg, const bf* kp, int W, int T, int tau,
+                                           int col, int D) {
+    if (tau >= 0 && tau < T) return *reinterpret_cast<const u32x4*>(kg + (size_t)tau * D + col);
+    if (tau < 0 && kp && tau >= -W) return *reinterpret_cast<const u32x4*>(kp + (size_t)(W + tau) * D + col);
+    return zero_u4();
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Kernel 1: reverse scan over the tiles of one (batch*head, 64-wide value
+// slice); 4 waves, wave cw owns value columns v0 + 16 cw .. + 15.  The state
+// gradient slice lives in registers as accumulators of dS^T (lane (lr, grp),
+// block kb: dS[v = v0 + 16 cw + lr][k = 16 kb + 4 grp + r]), the operand
+// layout of X dS^T as it stands.  Per tile: checkpoint dS (the gradient at
+// the tile end), dDelta, the transposed blocked substitution, dv (= dR for a
+// window of one) through LDS as row stores, then dS at the tile start.  The
+// next tile's operands are loaded into registers while the current tile
+// computes.
+// ---------------------------------------------------------------------------
+template <int D, int CV, bool DELTA>
+struct BScanSmem {
+    using R = Rec<EBf16, CV, DELTA>;
+    static constexpr int LDX = D + 8, LDY = 64 + 8;
+    bf X[CV][LDX];
+    bf Q[CV][LDX];
+    bf dO[CV][LDY];
+    bf dR[CV][LDY];
+    alignas(16) char rec[R::kBytes];
+};
+
+template <int D, int CV, bool DELTA>
+__global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
+    using E = EBf16;
+    using Frag = s16x4;
+    using R = Rec<E, CV, DELTA>;
+    using Smem = BScanSmem<D, CV, DELTA>;
+    constexpr int NB = CV / 16, KB = D / 16, CPR = D / 8, NVS = D / 64;
+    constexpr int LDX = Smem::LDX, LDY = Smem::LDY;
+    constexpr int NXL = (CV * CPR + 255) / 256;
+    constexpr int NYL = (CV * 8 + 255) / 256;
+    constexpr int RPC = (int)(R::kBytes / 16);
+    constexpr int NRL = (RPC + 255) / 256;
+    static_assert(NB % 2 == 0, "pairs of 16-row blocks");
+    __shared__ Smem sm;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4,
+              lr = lane & 15;
+    const int cw = wave;
+    // slices of one sequence on one XCD (consecutive workgroups go round the 8)
+    const int blk = blockIdx.x, xcd = blk & 7, jj = blk >> 3;
+    const int bh = (jj / NVS) * 8 + xcd, vs = jj % NVS;
+    if (bh >= a.BH) return;
+    const int v0 = vs * 64;
+    const int T_ = a.T, ntiles = a.ntiles, ntl = tiles_of(T_, CV), W = a.W, lag = a.lag;
+    const bf* kg = static_cast<const bf*>(a.k) + (size_t)bh * T_ * D;
+    const bf* qg = static_cast<const bf*>(a.q) + (size_t)bh * T_ * D;
+    const bf* dog = static_cast<const bf*>(a.d_o) + (size_t)bh * T_ * D + v0;
+    const bf* kp = a.k_prev ? static_cast<const bf*>(a.k_prev) + (size_t)bh * W * D : nullptr;
+    const char* recg = static_cast<const char*>(a.rec) + (size_t)bh * ntiles * R::kBytes;
+    bf* dvg = static_cast<bf*>(a.dv) + (size_t)bh * T_ * D + v0;
+    const int vcol = v0 + 16 * cw + lr;
+
+    f32x4 dS[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+        dS[kb] = a.dS_final ? *reinterpret_cast<const f32x4*>(a.dS_final + ((size_t)bh * D + vcol) * D +
+                                                              16 * kb + 4 * grp)
+                            : zero4();
+
+    u32x4 px[NXL], pq[NXL], py[NYL], pr[NRL];
+    auto load = [&](int tile) __attribute__((always_inline)) {
+        const int t0 = tile * CV;
+#pragma unroll
+        for (int it = 0; it < NXL; ++it) {
+            const int c = tid + 256 * it, i = c / CPR, col = (c % CPR) * 8;
+            const bool ok = c < CV * CPR;
+            px[it] = ok ? key_piece(kg, kp, W, T_, t0 + i - lag, col, D) : zero_u4();
+            pq[it] = (ok && t0 + i < T_) ? *reinterpret_cast<const u32x4*>(qg + (size_t)(t0 + i) * D + col)
+                                         : zero_u4();
+        }
+#pragma unroll
+        for (int it = 0; it < NYL; ++it) {
+            const int c = tid + 256 * it, i = c / 8, col = (c % 8) * 8;
+            py[it] = (c < CV * 8 && t0 + i < T_)
+                         ? *reinterpret_cast<const u32x4*>(dog + (size_t)(t0 + i) * D + col)
+                         : zero_u4();
+        }
+        const char* rg = recg + (size_t)tile * R::kBytes;
+#pragma unroll
+        for (int it = 0; it < NRL; ++it) {
+            const int c = tid + 256 * it;
+            pr[it] = c < RPC ? *reinterpret_cast<const u32x4*>(rg + 16 * (size_t)c) : zero_u4();
+        }
+    };
+    auto store = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int it = 0; it < NXL; ++it) {
+            const int c = tid + 256 * it, i = c / CPR, col = (c % CPR) * 8;
+            if (c < CV * CPR) {
+                *reinterpret_cast<u32x4*>(&sm.X[i][col]) = px[it];
+                *reinterpret_cast<u32x4*>(&sm.Q[i][col]) = pq[it];
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < NYL; ++it) {
+            const int c = tid + 256 * it, i = c / 8, col = (c % 8) * 8;
+            if (c < CV * 8) *reinterpret_cast<u32x4*>(&sm.dO[i][col]) = py[it];
+        }
+#pragma unroll
+        for (int it = 0; it < NRL; ++it) {
+            const int c = tid + 256 * it;
+            if (c < RPC) *reinterpret_cast<u32x4*>(sm.rec + 16 * c) = pr[it];
+        }
+    };
+    // column fragment of a row-major LDS tile: lane (lr, grp) gets
+    // M[row0 + 4 grp + r][col0 + lr]
+    auto colfrag = [&](const bf* m, int ld, int row0, int col0) __attribute__((always_inline)) {
+        return E::load_tr(m + (size_t)(row0 + 4 * grp + (lr >> 2)) * ld + col0 + 4 * (lr & 3));
+    };
+    // transposed record block (element offset `off`): lane (lr, grp) gets
+    // M[4 grp + r][lr] of a block stored with M[lr][4 grp + r] at lane (lr, grp)
+    auto rec_tr = [&](size_t off) __attribute__((always_inline)) {
+        const bf* b = reinterpret_cast<const bf*>(sm.rec) + off;
+        return E::load_tr(b + (size_t)((lr & 3) * 16 + 4 * grp + (lr >> 2)) * 4);
+    };
+
+    if (ntl > 0) load(ntl - 1);
+    for (int it = ntl - 1; it >= 0; --it) {
+        store();
+        lds_barrier();
+        if (it > 0) load(it - 1);
+        const float* gam = reinterpret_cast<const float*>(sm.rec + R::kScalBytes);
+        const float* hrow = gam + CV;
+        const float* gq = gam + 2 * CV;
+
+        Frag dSB[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) dSB[kb] = E::pack(dS[kb]);
+        {
+            bf* cs = static_cast<bf*>(a.ck_ds) + (((size_t)bh * ntiles + it) * D + vcol) * D + 4 * grp;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) *reinterpret_cast<Frag*>(cs + 16 * kb) = dSB[kb];
+        }
+
+        // dDelta = diag(hrow) X dS^T + P^T dO   (rows j, columns v)
+        f32x4 dd[NB];
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) dd[rb] = zero4();
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m) {
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) {
+                const bf* xr = &sm.X[16 * rb + lr][32 * m + 4 * grp];
+                dd[rb] = E::mma32(E::load(xr), E::load(xr + 16), dSB[2 * m], dSB[2 * m + 1], dd[rb]);
+            }
+        }
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) {
+            const f32x4 h = *reinterpret_cast<const f32x4*>(hrow + 16 * rb + 4 * grp);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dd[rb][r] *= h[r];
+        }
+        Frag dOc[NB];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) dOc[tb] = colfrag(&sm.dO[0][0], LDY, 16 * tb, 16 * cw);
+        static_for<NB>([&](auto rbc) __attribute__((always_inline)) {
+            constexpr int rb = decltype(rbc)::value;
+            static_for<NB>([&](auto tbc) __attribute__((always_inline)) {
+                constexpr int tb = decltype(tbc)::value;
+                if constexpr (tb >= rb)
+                    dd[rb] = E::mma16(rec_tr(R::kP + (size_t)R::pblk(tb, rb, false) * 256), dOc[tb], dd[rb]);
+            });
+        });
+
+        // dR = (I + A)^-T dDelta, by blocks from the last:
+        // dR_b = Td_b^T (dDelta_b + sum_{c>b} (-A)_cb^T dR_c)
+        f32x4 dr[NB];
+        Frag drb[NB];
+        if constexpr (DELTA) {
+            static_for<NB>([&](auto qc) __attribute__((always_inline)) {
+                constexpr int rb = NB - 1 - decltype(qc)::value;
+                f32x4 acc = dd[rb];
+                static_for<NB>([&](auto cbc) __attribute__((always_inline)) {
+                    constexpr int cb = decltype(cbc)::value;
+                    if constexpr (cb > rb)
+                        acc = E::mma16(rec_tr(R::kA + (size_t)R::ablk(cb, rb) * 256), drb[cb], acc);
+                });
+                dr[rb] = E::mma16(rec_tr(R::kD + (size_t)rb * 256), E::pack(acc), zero4());
+                drb[rb] = E::pack(dr[rb]);
+            });
+        } else {
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) dr[rb] = dd[rb];
+        }
+        // dv rows leave through LDS
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm.dR[16 * rb + 4 * grp + r][16 * cw + lr] = f2bf(dr[rb][r]);
+
+        // dS at the tile start: exp(g_L) dS + (Q^T diag(gq) dO - X^T diag(gam) dR)^T
+        const float gl = gq[CV - 1];
+        Frag bq[NB], bx[NB];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) {
+            const f32x4 g = *reinterpret_cast<const f32x4*>(gq + 16 * tb + 4 * grp);
+            f32x4 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = bf2f((bf)dOc[tb][r]) * g[r];
+            bq[tb] = E::pack(v);
+        }
+        if constexpr (DELTA) {
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) {
+                const f32x4 g = *reinterpret_cast<const f32x4*>(gam + 16 * jb + 4 * grp);
+                f32x4 v;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = -g[r] * dr[jb][r];
+                bx[jb] = E::pack(v);
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            f32x4 acc = dS[kb] * gl;
+#pragma unroll
+            for (int m = 0; m < NB / 2; ++m)
+                acc = E::mma32(colfrag(&sm.Q[0][0], LDX, 32 * m, 16 * kb),
+                               colfrag(&sm.Q[0][0], LDX, 32 * m + 16, 16 * kb), bq[2 * m], bq[2 * m + 1], acc);
+            // the residuals' S0 term (delta family only: the inner-product
+            // family writes its targets, which do not depend on S0)
+            if constexpr (DELTA) {
+#pragma unroll
+                for (int m = 0; m < NB / 2; ++m)
+                    acc = E::mma32(colfrag(&sm.X[0][0], LDX, 32 * m, 16 * kb),
+                                   colfrag(&sm.X[0][0], LDX, 32 * m + 16, 16 * kb), bx[2 * m], bx[2 * m + 1],
+                                   acc);
+            }
+            dS[kb] = acc;
+        }
+        lds_barrier();
+        {
+            const int t0 = it * CV;
+#pragma unroll
+            for (int q = 0; q < NYL; ++q) {
+                const int c = tid + 256 * q, i = c / 8, col = (c % 8) * 8;
+                if (c < CV * 8 && t0 + i < T_)
+                    *reinterpret_cast<u32x4*>(dvg + (size_t)(t0 + i) * D + col) =
+                        *reinterpret_cast<const u32x4*>(&sm.dR[i][col]);
+            }
+        }
+    }
+    if (a.dS0) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            *reinterpret_cast<f32x4*>(a.dS0 + ((size_t)bh * D + vcol) * D + 16 * kb + 4 * grp) = dS[kb];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 2: one workgroup of 8 waves per (batch*head, tile).  The value
+// dimension is contracted in halves of 64 (state, state gradient, Delta, dR
+// and dO of one half in LDS at a time); then the masked, decayed DP and DA go
+// to LDS and the second products run; the three gradient tiles leave the
+// accumulators through LDS in fp32 for a row-wise epilogue (8 lanes per row):
+// the write-scale and feature-map derivatives, the decay gradients and the
+// stores.
+// ---------------------------------------------------------------------------
+template <int D, int CV>
+struct BGradSmem {
+    static constexpr int LDX = D + 8, LDH = 64 + 8, LDC = CV + 8, LDF = D + 4;
+    bf X[CV][LDX];
+    bf Q[CV][LDX];
+    struct Half {
+        bf S0h[64][LDX];  // state at the tile start, 64 value rows ([v][k])
+        bf dSh[64][LDX];  // state gradient at the tile end
+        bf Dh[64][LDC];   // Delta ([v][i])
+        bf dRh[CV][LDH];  // dR rows of the half ([i][v])
+        bf dOh[CV][LDH];  // dO rows of the half ([t][v])
+        bf DP[CV][LDC];   // DP^T [j][t]
+        bf DA[CV][LDC];   // DA^T [j][i]
+        bf DPr[CV][LDC];  // r_j DP^T
+        bf DAr[CV][LDC];  // r_j DA^T
+    };
+    struct Rows {
+        float dX[CV][LDF];
+        float dQ[CV][LDF];
+        float dW[CV][LDF];
+    };
+    union {
+        Half h;
+        Rows w;
+    } u;
+    alignas(16) float gs[CV];  // log2(e) * g (tile-local cumulative log decay)
+    alignas(16) float rr[CV];  // write scale r_i
+    alignas(16) float nn[CV];  // ||x_i||^2 + eps
+    float al[CV], et[CV], dg[CV];
+    float red[8][2];
+};
+
+template <int D, int CV, bool DELTA>
+__global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
+    using E = EBf16;
+    using Frag = s16x4;
+    using Smem = BGradSmem<D, CV>;
+    constexpr int NB = CV / 16, KB = D / 16, CPR = D / 8, NH = D / 64;
+    constexpr int WPK = 8 / KB;    // waves per 16-row block of k
+    constexpr int NCB = NB / WPK;  // column blocks per wave
+    constexpr int LDX = Smem::LDX, LDH = Smem::LDH, LDC = Smem::LDC;
+    constexpr int EPT = D / 8;     // row elements per epilogue lane
+    constexpr float kLog2e = 1.4426950408889634f;
+    static_assert(NB == 4, "one 64-row tile");
+    __shared__ Smem sm;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4,
+              lr = lane & 15;
+    const int ntiles = a.ntiles;
+    const int bh = blockIdx.x / ntiles, tile = blockIdx.x - bh * ntiles;
+    const int T_ = a.T, W = a.W, lag = a.lag;
+    const int t0 = tile * CV;
+    if (bh >= a.BH || t0 >= T_) return;
+    const bf* kg = static_cast<const bf*>(a.k) + (size_t)bh * T_ * D;
+    const bf* qg = static_cast<const bf*>(a.q) + (size_t)bh * T_ * D;
+    const bf* kp = a.k_prev ? static_cast<const bf*>(a.k_prev) + (size_t)bh * W * D : nullptr;
+    const size_t tix = (size_t)bh * ntiles + tile;
+
+    // ---- keys, queries, gates ----
+    for (int c = tid; c < CV * CPR; c += 512) {
+        const int i = c / CPR, col = (c % CPR) * 8;
+        *reinterpret_cast<u32x4*>(&sm.X[i][col]) = key_piece(kg, kp, W, T_, t0 + i - lag, col, D);
+        *reinterpret_cast<u32x4*>(&sm.Q[i][col]) =
+            t0 + i < T_ ? *reinterpret_cast<const u32x4*>(qg + (size_t)(t0 + i) * D + col) : zero_u4();
+    }
+    if (tid < CV) {
+        const bool in = t0 + tid < T_;
+        sm.al[tid] = in ? a.alpha[(size_t)bh * T_ + t0 + tid] : 1.f;
+        sm.et[tid] = in ? a.eta[(size_t)bh * T_ + t0 + tid] : 0.f;
+    }
+    lds_barrier();
+    {
+        // norms and write scales (8 lanes per row), the log-decay scan (wave 0)
+        const int row = tid >> 3, part = tid & 7;
+        float n2 = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const float x = bf2f(sm.X[row][part * EPT + e]);
+            n2 += x * x;
+        }
+        n2 = group_sum_dpp<8>(n2);
+        if (part == 0) {
+            const float den = n2 + a.eps;
+            sm.nn[row] = den;
+            sm.rr[row] = den > 0.f ? sm.et[row] / den : 0.f;
+        }
+        if (wave == 0) {
+            float lg = __logf(sm.al[lane]);
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(lg, off, 64);
+                if (lane >= off) lg += y;
+            }
+            sm.gs[lane] = lg * kLog2e;
+        }
+    }
+
+    auto colfrag = [&](const bf* m, int ld, int row0, int col0) __attribute__((always_inline)) {
+        return E::load_tr(m + (size_t)(row0 + 4 * grp + (lr >> 2)) * ld + col0 + 4 * (lr & 3));
+    };
+
+    const int kb = wave / WPK, cb0 = (wave % WPK) * NCB;
+    const int jbw = wave >> 1, tbw0 = (wave & 1) * 2;
+    f32x4 aQ[NCB], aX[NCB], aW[NCB], aP[2], aA[2];
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) aQ[c] = aX[c] = aW[c] = zero4();
+    aP[0] = aP[1] = aA[0] = aA[1] = zero4();
+    float sdot = 0.f;  // <dS_end, S0>, this lane's share
+
+    const bf* cks = static_cast<const bf*>(a.ck_s) + tix * D * D;
+    const bf* ckds = static_cast<const bf*>(a.ck_ds) + tix * D * D;
+    const bf* ckd = static_cast<const bf*>(a.ck_d) + tix * D * CV;
+    const bf* dvg = static_cast<const bf*>(a.dv) + ((size_t)bh * T_ + t0) * D;
+    const bf* dog = static_cast<const bf*>(a.d_o) + ((size_t)bh * T_ + t0) * D;
+    for (int h = 0; h < NH; ++h) {
+        lds_barrier();  // the previous half's operands are consumed
+        for (int c = tid; c < 64 * CPR; c += 512) {
+            const int v = c / CPR, col = (c % CPR) * 8;
+            const u32x4 s = *reinterpret_cast<const u32x4*>(cks + (size_t)(64 * h + v) * D + col);
+            const u32x4 g = *reinterpret_cast<const u32x4*>(ckds + (size_t)(64 * h + v) * D + col);
+            *reinterpret_cast<u32x4*>(&sm.u.h.S0h[v][col]) = s;
+            *reinterpret_cast<u32x4*>(&sm.u.h.dSh[v][col]) = g;
+            const bf* se = reinterpret_cast<const bf*>(&s);
+            const bf* ge = reinterpret_cast<const bf*>(&g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sdot += bf2f(se[e]) * bf2f(ge[e]);
+        }
+        for (int c = tid; c < 64 * (CV / 8); c += 512) {
+            const int v = c / (CV / 8), col = (c % (CV / 8)) * 8;
+            *reinterpret_cast<u32x4*>(&sm.u.h.Dh[v][col]) =
+                *reinterpret_cast<const u32x4*>(ckd + (size_t)(64 * h + v) * CV + col);
+        }
+        for (int c = tid; c < CV * 8; c += 512) {
+            const int i = c / 8, col = (c % 8) * 8;
+            const bool in = t0 + i < T_;
+            *reinterpret_cast<u32x4*>(&sm.u.h.dRh[i][col]) =
+                in ? *reinterpret_cast<const u32x4*>(dvg + (size_t)i * D + 64 * h + col) : zero_u4();
+            *reinterpret_cast<u32x4*>(&sm.u.h.dOh[i][col]) =
+                in ? *reinterpret_cast<const u32x4*>(dog + (size_t)i * D + 64 * h + col) : zero_u4();
+        }
+        lds_barrier();
+        const bf* Dh = &sm.u.h.Dh[0][0];
+        const bf* S0h = &sm.u.h.S0h[0][0];
+        const bf* dSh = &sm.u.h.dSh[0][0];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const Frag dj0 = colfrag(Dh, LDC, 32 * m, 16 * jbw), dj1 = colfrag(Dh, LDC, 32 * m + 16, 16 * jbw);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int tb = tbw0 + u;
+                if (tb >= jbw) {
+                    const bf* orow = &sm.u.h.dOh[16 * tb + lr][32 * m + 4 * grp];
+                    const Frag o0 = E::load(orow), o1 = E::load(orow + 16);
+                    aP[u] = E::mma32(dj0, dj1, o0, o1, aP[u]);
+                    if constexpr (DELTA) {
+                        const bf* rrow = &sm.u.h.dRh[16 * tb + lr][32 * m + 4 * grp];
+                        aA[u] = E::mma32(dj0, dj1, E::load(rrow), E::load(rrow + 16), aA[u]);
+                    }
+                }
+            }
+            const Frag s0 = colfrag(S0h, LDX, 32 * m, 16 * kb), s1 = colfrag(S0h, LDX, 32 * m + 16, 16 * kb);
+            const Frag g0 = colfrag(dSh, LDX, 32 * m, 16 * kb), g1 = colfrag(dSh, LDX, 32 * m + 16, 16 * kb);
+#pragma unroll
+            for (int c = 0; c < NCB; ++c) {
+                const int cb = cb0 + c;
+                const bf* orow = &sm.u.h.dOh[16 * cb + lr][32 * m + 4 * grp];
+                aQ[c] = E::mma32(s0, s1, E::load(orow), E::load(orow + 16), aQ[c]);
+                if constexpr (DELTA) {
+                    const bf* rrow = &sm.u.h.dRh[16 * cb + lr][32 * m + 4 * grp];
+                    aX[c] = E::mma32(s0, s1, E::load(rrow), E::load(rrow + 16), aX[c]);
+                }
+                aW[c] = E::mma32(g0, g1, colfrag(Dh, LDC, 32 * m, 16 * cb),
+                                 colfrag(Dh, LDC, 32 * m + 16, 16 * cb), aW[c]);
+            }
+        }
+    }
+
+    // ---- decays, masks; DP and DA to LDS ----
+    const float gL = sm.gs[CV - 1];
+    float s3 = 0.f;  // sum_j omega_j . dOmega3_j, this lane's share
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+        const int col = 16 * (cb0 + c) + lr;
+        const float gc = sm.gs[col];
+        const float eq = exp2f(gc);
+        aQ[c] = aQ[c] * eq;
+        aX[c] = aX[c] * (-eq);
+        aW[c] = aW[c] * exp2f(gL - gc);
+        const Frag xk = E::load(&sm.X[col][16 * kb + 4 * grp]);
+        float p = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p += bf2f((bf)xk[r]) * aW[c][r];
+        s3 += sm.rr[col] * p;
+    }
+    s3 = group_sum<64>(s3);
+    sdot = group_sum<64>(sdot);
+    if (lane == 0) {
+        sm.red[wave][0] = s3;
+        sm.red[wave][1] = sdot;
+    }
+    lds_barrier();  // the last half's operands are consumed before DP / DA overwrite nothing of
+                    // theirs, and the partial sums are visible
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int tb = tbw0 + u;
+        const int t = 16 * tb + lr;
+        const float gt = sm.gs[t];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = 16 * jbw + 4 * grp + r;
+            const float gj = sm.gs[j], rj = sm.rr[j];
+            const float vp = (j <= t) ? aP[u][r] * exp2f(gt - gj) : 0.f;
+            const float va = (DELTA && j < t) ? -aA[u][r] * exp2f(gt - gj) : 0.f;
+            sm.u.h.DP[j][t] = f2bf(vp);
+            sm.u.h.DPr[j][t] = f2bf(vp * rj);
+            sm.u.h.DA[j][t] = f2bf(va);
+            sm.u.h.DAr[j][t] = f2bf(va * rj);
+        }
+    }
+    lds_barrier();
+
+    // ---- second products ----
+    {
+        const bf* Xs = &sm.X[0][0];
+        const bf* Qs = &sm.Q[0][0];
+        const bf* DP = &sm.u.h.DP[0][0];
+        const bf* DA = &sm.u.h.DA[0][0];
+        const bf* DPr = &sm.u.h.DPr[0][0];
+        const bf* DAr = &sm.u.h.DAr[0][0];
+#pragma unroll
+        for (int c = 0; c < NCB; ++c) {
+            const int cb = cb0 + c;
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) {
+                if (jb <= cb) {
+                    const Frag xj = colfrag(Xs, LDX, 16 * jb, 16 * kb);
+                    aQ[c] = E::mma16(xj, colfrag(DPr, LDC, 16 * jb, 16 * cb), aQ[c]);
+                    if constexpr (DELTA) aX[c] = E::mma16(xj, colfrag(DAr, LDC, 16 * jb, 16 * cb), aX[c]);
+                }
+                if (jb >= cb) {
+                    aW[c] = E::mma16(colfrag(Qs, LDX, 16 * jb, 16 * kb),
+                                     E::load(DP + (size_t)(16 * cb + lr) * LDC + 16 * jb + 4 * grp), aW[c]);
+                    if constexpr (DELTA)
+                        aW[c] = E::mma16(colfrag(Xs, LDX, 16 * jb, 16 * kb),
+                                         E::load(DA + (size_t)(16 * cb + lr) * LDC + 16 * jb + 4 * grp), aW[c]);
+                }
+            }
+        }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+        const int row = 16 * (cb0 + c) + lr;
+        *reinterpret_cast<f32x4*>(&sm.u.w.dQ[row][16 * kb + 4 * grp]) = aQ[c];
+        *reinterpret_cast<f32x4*>(&sm.u.w.dX[row][16 * kb + 4 * grp]) = aX[c];
+        *reinterpret_cast<f32x4*>(&sm.u.w.dW[row][16 * kb + 4 * grp]) = aW[c];
+    }
+    lds_barrier();
+
+    // ---- row epilogue: 8 lanes per row ----
+    {
+        const int row = tid >> 3, part = tid & 7, k0 = part * EPT;
+        const int t = t0 + row;
+        float x[EPT], dx[EPT], dw[EPT], qv[EPT], dq[EPT];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            x[e] = bf2f(sm.X[row][k0 + e]);
+            qv[e] = bf2f(sm.Q[row][k0 + e]);
+            dx[e] = sm.u.w.dX[row][k0 + e];
+            dw[e] = sm.u.w.dW[row][k0 + e];
+            dq[e] = sm.u.w.dQ[row][k0 + e];
+        }
+        float sX = 0.f, sO = 0.f, sQ = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            sX += x[e] * dx[e];
+            sO += x[e] * dw[e];
+            sQ += qv[e] * dq[e];
+        }
+        sX = group_sum_dpp<8>(sX);
+        sO = group_sum_dpp<8>(sO);
+        sQ = group_sum_dpp<8>(sQ);
+        const float r = sm.rr[row], n = sm.nn[row];
+        const float cn = n > 0.f ? 2.f * r * sO / n : 0.f;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) dx[e] = dx[e] + r * dw[e] - cn * x[e];
+        if (part == 0) {
+            sm.dg[row] = sX - r * sO + sQ;
+            if (t < T_) a.deta[(size_t)bh * T_ + t] = n > 0.f ? sO / n : 0.f;
+        }
+
+        // the feature map's derivative, on the caller's raw rows
+        auto phi_back = [&](float (&g)[EPT], const bf* raw) __attribute__((always_inline)) {
+            if (a.phi == 0) return;
+            float kr[EPT];
+            const u32x4* p = reinterpret_cast<const u32x4*>(raw + k0);
+#pragma unroll
+            for (int c = 0; c < EPT / 8; ++c) {
+                const u32x4 v = p[c];
+                const bf* e8 = reinterpret_cast<const bf*>(&v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kr[8 * c + e] = bf2f(e8[e]);
+            }
+            if (a.phi == 1) {
+                float n2 = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) n2 += kr[e] * kr[e];
+                n2 = group_sum_dpp<8>(n2);
+                const float inv = n2 > 0.f ? rsqrtf(n2) : 0.f;
+                float pd = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) pd += kr[e] * inv * g[e];
+                pd = group_sum_dpp<8>(pd);
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) g[e] = (g[e] - kr[e] * inv * pd) * inv;
+            } else {
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) {
+                    const float s = 1.f / (1.f + __expf(-kr[e]));
+                    g[e] = g[e] * s * (1.f + kr[e] * (1.f - s));
+                }
+            }
+        };
+        auto store_row = [&](bf* dst, const float (&g)[EPT]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int c = 0; c < EPT / 8; ++c) {
+                u32x4 o;
+                bf* oe = reinterpret_cast<bf*>(&o);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) oe[e] = f2bf(g[8 * c + e]);
+                *reinterpret_cast<u32x4*>(dst + k0 + 8 * c) = o;
+            }
+        };
+
+        // key row tau = t - lag: its only use (window of one) is as x of step t;
+        // a padded step (t >= T) computes dx = 0, which is the gradient of the
+        // key no step reads (k_{T-1} under prefix alignment)
+        const int tau = t - lag;
+        const bool key_row = (t < T_ + lag) && tau < T_ && (tau >= 0 || (a.dk_prev && a.kp_raw));
+        if (key_row) {  // uniform over the row's 8 lanes
+            const bf* raw = tau >= 0 ? static_cast<const bf*>(a.k_raw) + ((size_t)bh * T_ + tau) * D
+                                     : static_cast<const bf*>(a.kp_raw) + ((size_t)bh * W + W + tau) * D;
+            phi_back(dx, raw);
+            bf* dst = tau >= 0 ? static_cast<bf*>(a.dk) + ((size_t)bh * T_ + tau) * D
+                               : static_cast<bf*>(a.dk_prev) + ((size_t)bh * W + W + tau) * D;
+            store_row(dst, dx);
+        }
+        if (t < T_) {
+            phi_back(dq, static_cast<const bf*>(a.q_raw) + ((size_t)bh * T_ + t) * D);
+            store_row(static_cast<bf*>(a.dq) + ((size_t)bh * T_ + t) * D, dq);
+        }
+        // keys no row of any tile reaches: k_{T-1} (prefix alignment, T a
+        // multiple of the tile) and the halo rows same-step pairs never read
+        const bool last = t0 + CV >= T_;
+        if (last && lag == 1 && T_ - t0 == CV && row == 0) {
+            float z[EPT];
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) z[e] = 0.f;
+            store_row(static_cast<bf*>(a.dk) + ((size_t)bh * T_ + T_ - 1) * D, z);
+        }
+        if (tile == 0 && a.dk_prev && row < W && (lag == 0 || !a.kp_raw || row < W - 1)) {
+            float z[EPT];
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) z[e] = 0.f;
+            store_row(static_cast<bf*>(a.dk_prev) + ((size_t)bh * W + row) * D, z);
+        }
+    }
+    lds_barrier();
+    // ---- decay gradients: dlog alpha_s = sum over the tile's steps s' >= s of dg ----
+    if (wave == 0) {
+        float g = sm.dg[lane];
+        if (lane == CV - 1) {
+            float s3t = 0.f, sdt = 0.f;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                s3t += sm.red[w][0];
+                sdt += sm.red[w][1];
+            }
+            g += exp2f(gL) * sdt + s3t;
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_down(g, off, 64);
+            if (lane + off < 64) g += y;
+        }
+        if (t0 + lane < T_) a.dalpha[(size_t)bh * T_ + t0 + lane] = g / sm.al[lane];
+    }
+}
+
+__global__ void bwd_zero_kernel(bf* p, size_t n) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+bool chunk_bwd_supported(int dt, int D, int chunk, int norm, int window) {
+    return dt == 1 && (D == 64 || D == 128) && chunk == 64 &&
+           (norm == kNormScalar || (norm == kNormWindow && window == 1));
+}
+
+template <int D, bool DELTA>
+static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
+    constexpr int CV = 64;
+    const int nvs = D / 64;
+    const int bh8 = (a.BH + 7) / 8 * 8;
+    hipLaunchKernelGGL((bwd_scan_kernel<D, CV, DELTA>), dim3(bh8 * nvs), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.T > 0) {
+        hipLaunchKernelGGL((bwd_grad_kernel<D, CV, DELTA>), dim3(a.BH * a.ntiles), dim3(512), 0, stream, a);
+        e = hipGetLastError();
+    } else if (a.dk_prev) {
+        const size_t n = (size_t)a.BH * a.W * D;
+        hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                           static_cast<bf*>(a.dk_prev), n);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+hipError_t launch_chunk_bwd(const BwdArgs& a, int D, int chunk, bool delta, hipStream_t stream) {
+    if (chunk != 64) return hipErrorInvalidValue;
+    if (D == 64) return delta ? launch_bwd_d<64, true>(a, stream) : launch_bwd_d<64, false>(a, stream);
+    if (D == 128) return delta ? launch_bwd_d<128, true>(a, stream) : launch_bwd_d<128, false>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace falcon

@@ -45,34 +45,10 @@
 // second slice's key and query reads hit that XCD's L2.
 #include "falcon_device.h"
 #include "falcon_internal.h"
+#include "falcon_records.h"
 
 namespace falcon {
 
-// ---------------------------------------------------------------------------
-// workspace record of one (batch*head, tile)
-// ---------------------------------------------------------------------------
-template <class E, int CV, bool DELTA>
-struct Rec {
-    static constexpr int NB = CV / 16;
-    static constexpr int NBA = DELTA ? NB * (NB - 1) / 2 : 0;  // strictly lower blocks of -A
-    static constexpr int NBD = DELTA ? NB : 0;                 // (I + A_bb)^-1
-    static constexpr int NBP = NB * NB;                        // blocks of P
-    static constexpr size_t kA = 0;                            // element offsets
-    static constexpr size_t kD = (size_t)NBA * 256;
-    static constexpr size_t kP = (size_t)(NBA + NBD) * 256;
-    static constexpr size_t kScalBytes = (size_t)(NBA + NBD + NBP) * 256 * E::kBytes;
-    static constexpr int NSC = 5;  // gam, hrow, gq, l1, erow (CV floats each)
-    static constexpr size_t kBytes = (kScalBytes + NSC * CV * 4 + 255) / 256 * 256;
-    static __host__ __device__ constexpr int ablk(int b, int c) { return b * (b - 1) / 2 + c; }
-    // P block (b, c): without a window the blocks on and below the diagonal in
-    // row order; with one (two query blocks at most) row-major over them.
-    static __host__ __device__ constexpr int pblk(int b, int c, bool win) {
-        return win ? b * NB + c : b * (b + 1) / 2 + c;
-    }
-    static constexpr int npblk(bool win) { return win ? 2 * NB : NB * (NB + 1) / 2; }
-};
-
-__host__ __device__ inline int tiles_of(int T, int Ct) { return (T + Ct - 1) / Ct; }
 
 // Rows of sequence bh in the [rows, d] planes: [row0, row0 + T).  Batched
 // calls: row0 = bh * T.  Packed calls: the bounds come from cu, clamped to the
@@ -1239,7 +1215,7 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
             constexpr int tb = decltype(tbc)::value;
             // lane holds O[t = 16 tb + lr][v = 16 cw + 4 grp + r]
             const int t = 16 * tb + lr;
-            if (tb < NBQ && t < Ct && t0 + t < T_)
+            if (tb < NBQ && t < Ct && t0 + t < T_ && a.o)
                 *reinterpret_cast<Frag*>(og + (size_t)(t0 + t) * D + 16 * cw + 4 * grp) = opk[tb];
         });
     };
@@ -1252,6 +1228,17 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
         for (int kb = 0; kb < KB; ++kb) sb[kb] = sm.SB[pb][cw][kb][lane];
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) db[cb] = sm.DB[pb][cw][cb][lane];
+        if (a.ck_s) {
+            // checkpoints for the backward pass: lane holds S[v][16 kb + 4 grp + r]
+            // and Delta[16 cb + 4 grp + r][v] of value row v = vcol
+            const size_t tb = (size_t)bh * ntiles + p;
+            T* cs = static_cast<T*>(a.ck_s) + (tb * D + vcol) * D + 4 * grp;
+            T* cd = static_cast<T*>(a.ck_d) + (tb * D + vcol) * CV + 4 * grp;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) *reinterpret_cast<Frag*>(cs + 16 * kb) = sb[kb];
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) *reinterpret_cast<Frag*>(cd + 16 * cb) = db[cb];
+        }
         static_for<NB>([&](auto tbc) __attribute__((always_inline)) {
             constexpr int tb = decltype(tbc)::value;
             if (tb < NBQ) {
@@ -1282,7 +1269,7 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
                 if constexpr (COL) {
                     // stored at once (the per-column pipeline does not defer)
                     const int t = 16 * tb + lr, t0 = p * Ct;
-                    if (t < Ct && t0 + t < T_)
+                    if (t < Ct && t0 + t < T_ && a.o)
                         *reinterpret_cast<Frag*>(og + (size_t)(t0 + t) * D + 16 * cw + 4 * grp) =
                             E::pack(acc);
                 } else {

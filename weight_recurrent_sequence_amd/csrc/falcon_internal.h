@@ -56,6 +56,14 @@ struct ChunkArgs {
     void* kphi;
     void* qphi;
     void* kpphi;
+    // Checkpoints for the backward pass (bf16 state pass, batched layout):
+    // when ck_s is set, the state pass also writes, for every (row, tile), the
+    // state at the tile start rounded to bf16 ([d_v][d_k], row-major) to
+    // ck_s and the tile's Delta (the residuals at the decayed state; the
+    // targets for the inner-product family) as [d_v][CV] to ck_d.  o may then
+    // be NULL (not written).
+    void* ck_s = nullptr;
+    void* ck_d = nullptr;
 };
 
 struct DecodeArgs {
@@ -92,6 +100,39 @@ struct DecodeWinArgs {
     int phi;     // feature map on the keys and q (0 identity, 1 L2, 2 SiLU); caches stay raw
     float eps;
 };
+
+// Backward pass of the chunk form (bf16, batched layout).  The forward is
+// re-run first with checkpoints (ChunkArgs::ck_s / ck_d); then a reverse scan
+// over the tiles carries the state gradient and writes dv and the state
+// gradient at every tile end (ck_ds); then one workgroup per tile forms dq,
+// dk, dalpha and deta.
+struct BwdArgs {
+    const void* q;        // queries and keys the kernels contract with (the
+    const void* k;        // mapped copies when a feature map is on)
+    const void* k_prev;   // halo keys (mapped copy likewise), or NULL
+    const void* q_raw;    // the caller's queries, keys and halo keys, for the
+    const void* k_raw;    // feature map's own derivative
+    const void* kp_raw;
+    const float* alpha;
+    const float* eta;
+    const void* d_o;      // [BH, T, d]
+    const float* dS_final;  // [BH, d, d] or NULL (zero)
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dalpha;
+    float* deta;
+    float* dS0;           // or NULL
+    void* dk_prev;        // or NULL
+    const void* rec;      // records of the intra-chunk kernel
+    const void* ck_s;     // bf16 state at each tile start, [BH][ntiles][d][d]
+    const void* ck_d;     // bf16 Delta of each tile, [BH][ntiles][d][CV]
+    void* ck_ds;          // bf16 state gradient at each tile end, [BH][ntiles][d][d]
+    int BH, T, ntiles, W, lag, phi;
+    float eps;
+};
+bool chunk_bwd_supported(int dt, int D, int chunk, int norm, int window);
+hipError_t launch_chunk_bwd(const BwdArgs& a, int D, int chunk, bool delta, hipStream_t stream);
 
 // dt: 0 fp32, 1 bf16.  Return false when the combination is not built.
 bool chunk_supported(int dt, int D, int chunk);

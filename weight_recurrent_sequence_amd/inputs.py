@@ -138,6 +138,22 @@ def make_chunk_inputs(B, H, T, dk, dv, *, dtype="bf16", seed=0, alpha_mu=3.0, al
                        window, S0, k_prev, v_prev, meta)
 
 
+def make_cotangents(B, H, T, dk, dv, *, dtype="bf16", seed=0, dS_sd=0.1):
+    """Seeded cotangents for a backward call: d_o [B,H,T,dv] in the input
+    storage (standard normal, rounded like the inputs) and dS_final
+    [B,H,dv,dk] fp32 (normal, sd dS_sd; None when dS_sd is 0).  Widened to
+    float64 they are the oracle's cotangents bit for bit."""
+    ss = np.random.SeedSequence([seed, 7])
+    co, cs = ss.spawn(2)
+    g = lambda c: np.random.Generator(np.random.PCG64(c))  # noqa: E731
+    d_o = _store(g(co).standard_normal((B, H, T, dv), dtype=np.float32), dtype)
+    dS = None
+    if dS_sd > 0:
+        dS = (g(cs).standard_normal((B, H, dv, dk), dtype=np.float32) * np.float32(dS_sd))
+        dS = dS.astype(np.float32)
+    return d_o, dS
+
+
 # The workloads, by what they are.  `seed` is SeedSequence(1000 + i); the last is the
 # windowed (Falcon-3) decode step at the same serving shape as the Falcon-1 one.
 WORKLOADS = {
