@@ -306,58 +306,57 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 2: one workgroup of 8 waves per (batch*head, tile).  The value
-// dimension is contracted in halves of 64 (state, state gradient, Delta, dR
-// and dO of one half in LDS at a time); then the masked, decayed DP and DA go
-// to LDS and the second products run; the three gradient tiles leave the
-// accumulators through LDS in fp32 for a row-wise epilogue (8 lanes per row):
-// the write-scale and feature-map derivatives, the decay gradients and the
-// stores.
+// Kernel 2: one workgroup of 4 waves per (batch*head, tile), two workgroups
+// per compute unit (LDS under 80 KB), so that one workgroup's loads overlap
+// the other's arithmetic.  The value dimension is contracted in quarters of
+// 32 (state, state gradient, Delta, dR and dO of one quarter in LDS at a
+// time); the masked, decayed DP and DA then take the staging room for the
+// second products.  The gradients leave from the accumulators: the row dot
+// products that the write-scale, decay and feature-map derivatives need are
+// reduced across the waves through a small LDS table, and each lane stores
+// four adjacent entries of a row.
 // ---------------------------------------------------------------------------
 template <int D, int CV>
 struct BGradSmem {
-    static constexpr int LDX = D + 8, LDH = 64 + 8, LDC = CV + 8, LDF = D + 4;
+    static constexpr int LDX = D + 8, LDQ = 32 + 8, LDC = CV + 8;
     bf X[CV][LDX];
     bf Q[CV][LDX];
-    struct Half {
-        bf S0h[64][LDX];  // state at the tile start, 64 value rows ([v][k])
-        bf dSh[64][LDX];  // state gradient at the tile end
-        bf Dh[64][LDC];   // Delta ([v][i])
-        bf dRh[CV][LDH];  // dR rows of the half ([i][v])
-        bf dOh[CV][LDH];  // dO rows of the half ([t][v])
+    struct Quarter {
+        bf S0q[32][LDX];  // state at the tile start, 32 value rows ([v][k])
+        bf dSq[32][LDX];  // state gradient at the tile end
+        bf Dq[32][LDC];   // Delta ([v][i])
+        bf dRq[CV][LDQ];  // dR rows ([i][v of the quarter])
+        bf dOq[CV][LDQ];  // dO rows ([t][v of the quarter])
+    };
+    struct Mats {
         bf DP[CV][LDC];   // DP^T [j][t]
         bf DA[CV][LDC];   // DA^T [j][i]
         bf DPr[CV][LDC];  // r_j DP^T
         bf DAr[CV][LDC];  // r_j DA^T
     };
-    struct Rows {
-        float dX[CV][LDF];
-        float dQ[CV][LDF];
-        float dW[CV][LDF];
-    };
     union {
-        Half h;
-        Rows w;
+        Quarter q;
+        Mats m;
     } u;
+    float part[4][4][CV];  // per-wave partial row sums
     alignas(16) float gs[CV];  // log2(e) * g (tile-local cumulative log decay)
     alignas(16) float rr[CV];  // write scale r_i
     alignas(16) float nn[CV];  // ||x_i||^2 + eps
-    float al[CV], et[CV], dg[CV];
-    float red[8][2];
+    float al[CV], et[CV], dg[CV], cn[CV];
+    float rowk[2][CV], rowq[2][CV];  // feature map: 1/||raw||, phi . g
+    float red[4][2];
 };
 
 template <int D, int CV, bool DELTA>
-__global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
     using E = EBf16;
     using Frag = s16x4;
     using Smem = BGradSmem<D, CV>;
-    constexpr int NB = CV / 16, KB = D / 16, CPR = D / 8, NH = D / 64;
-    constexpr int WPK = 8 / KB;    // waves per 16-row block of k
-    constexpr int NCB = NB / WPK;  // column blocks per wave
-    constexpr int LDX = Smem::LDX, LDH = Smem::LDH, LDC = Smem::LDC;
-    constexpr int EPT = D / 8;     // row elements per epilogue lane
+    constexpr int NB = CV / 16, KB = D / 16, CPR = D / 8, NQ = D / 32;
+    constexpr int KPW = KB / 4;    // 16-row blocks of k per wave
+    constexpr int LDX = Smem::LDX, LDQ = Smem::LDQ, LDC = Smem::LDC;
     constexpr float kLog2e = 1.4426950408889634f;
-    static_assert(NB == 4, "one 64-row tile");
+    static_assert(NB == 4 && KB % 4 == 0, "one 64-row tile, d a multiple of 64");
     __shared__ Smem sm;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4,
@@ -367,34 +366,45 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
     const int T_ = a.T, W = a.W, lag = a.lag;
     const int t0 = tile * CV;
     if (bh >= a.BH || t0 >= T_) return;
-    const bf* kg = static_cast<const bf*>(a.k) + (size_t)bh * T_ * D;
-    const bf* qg = static_cast<const bf*>(a.q) + (size_t)bh * T_ * D;
-    const bf* kp = a.k_prev ? static_cast<const bf*>(a.k_prev) + (size_t)bh * W * D : nullptr;
     const size_t tix = (size_t)bh * ntiles + tile;
 
     // ---- keys, queries, gates ----
-    for (int c = tid; c < CV * CPR; c += 512) {
-        const int i = c / CPR, col = (c % CPR) * 8;
-        *reinterpret_cast<u32x4*>(&sm.X[i][col]) = key_piece(kg, kp, W, T_, t0 + i - lag, col, D);
-        *reinterpret_cast<u32x4*>(&sm.Q[i][col]) =
-            t0 + i < T_ ? *reinterpret_cast<const u32x4*>(qg + (size_t)(t0 + i) * D + col) : zero_u4();
-    }
-    if (tid < CV) {
-        const bool in = t0 + tid < T_;
-        sm.al[tid] = in ? a.alpha[(size_t)bh * T_ + t0 + tid] : 1.f;
-        sm.et[tid] = in ? a.eta[(size_t)bh * T_ + t0 + tid] : 0.f;
+    {
+        const bf* kg = static_cast<const bf*>(a.k) + (size_t)bh * T_ * D;
+        const bf* qg = static_cast<const bf*>(a.q) + (size_t)bh * T_ * D;
+        const bf* kp = a.k_prev ? static_cast<const bf*>(a.k_prev) + (size_t)bh * W * D : nullptr;
+        constexpr int NXP = CV * CPR / 256;
+        u32x4 px[NXP], pq[NXP];
+#pragma unroll
+        for (int it = 0; it < NXP; ++it) {
+            const int c = tid + 256 * it, i = c / CPR, col = (c % CPR) * 8;
+            px[it] = key_piece(kg, kp, W, T_, t0 + i - lag, col, D);
+            pq[it] = t0 + i < T_ ? *reinterpret_cast<const u32x4*>(qg + (size_t)(t0 + i) * D + col) : zero_u4();
+        }
+        if (tid < CV) {
+            const bool in = t0 + tid < T_;
+            sm.al[tid] = in ? a.alpha[(size_t)bh * T_ + t0 + tid] : 1.f;
+            sm.et[tid] = in ? a.eta[(size_t)bh * T_ + t0 + tid] : 0.f;
+        }
+#pragma unroll
+        for (int it = 0; it < NXP; ++it) {
+            const int c = tid + 256 * it, i = c / CPR, col = (c % CPR) * 8;
+            *reinterpret_cast<u32x4*>(&sm.X[i][col]) = px[it];
+            *reinterpret_cast<u32x4*>(&sm.Q[i][col]) = pq[it];
+        }
     }
     lds_barrier();
     {
-        // norms and write scales (8 lanes per row), the log-decay scan (wave 0)
-        const int row = tid >> 3, part = tid & 7;
+        // norms and write scales (4 lanes per row), the log-decay scan (wave 0)
+        const int row = tid >> 2, part = tid & 3;
+        constexpr int EP = D / 4;
         float n2 = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            const float x = bf2f(sm.X[row][part * EPT + e]);
+        for (int e = 0; e < EP; ++e) {
+            const float x = bf2f(sm.X[row][part * EP + e]);
             n2 += x * x;
         }
-        n2 = group_sum_dpp<8>(n2);
+        n2 = group_sum_dpp<4>(n2);
         if (part == 0) {
             const float den = n2 + a.eps;
             sm.nn[row] = den;
@@ -415,12 +425,16 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
         return E::load_tr(m + (size_t)(row0 + 4 * grp + (lr >> 2)) * ld + col0 + 4 * (lr & 3));
     };
 
-    const int kb = wave / WPK, cb0 = (wave % WPK) * NCB;
-    const int jbw = wave >> 1, tbw0 = (wave & 1) * 2;
-    f32x4 aQ[NCB], aX[NCB], aW[NCB], aP[2], aA[2];
+    // wave w: k blocks KPW w .. KPW w + KPW - 1 of the three gradient tiles
+    // (all four column blocks), and row block w of DP^T and DA^T
+    const int jbw = wave;
+    f32x4 aQ[KPW][NB], aX[KPW][NB], aW[KPW][NB], aP[NB], aA[NB];
 #pragma unroll
-    for (int c = 0; c < NCB; ++c) aQ[c] = aX[c] = aW[c] = zero4();
-    aP[0] = aP[1] = aA[0] = aA[1] = zero4();
+    for (int kk = 0; kk < KPW; ++kk)
+#pragma unroll
+        for (int c = 0; c < NB; ++c) aQ[kk][c] = aX[kk][c] = aW[kk][c] = zero4();
+#pragma unroll
+    for (int c = 0; c < NB; ++c) aP[c] = aA[c] = zero4();
     float sdot = 0.f;  // <dS_end, S0>, this lane's share
 
     const bf* cks = static_cast<const bf*>(a.ck_s) + tix * D * D;
@@ -428,85 +442,109 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
     const bf* ckd = static_cast<const bf*>(a.ck_d) + tix * D * CV;
     const bf* dvg = static_cast<const bf*>(a.dv) + ((size_t)bh * T_ + t0) * D;
     const bf* dog = static_cast<const bf*>(a.d_o) + ((size_t)bh * T_ + t0) * D;
-    for (int h = 0; h < NH; ++h) {
-        lds_barrier();  // the previous half's operands are consumed
-        for (int c = tid; c < 64 * CPR; c += 512) {
-            const int v = c / CPR, col = (c % CPR) * 8;
-            const u32x4 s = *reinterpret_cast<const u32x4*>(cks + (size_t)(64 * h + v) * D + col);
-            const u32x4 g = *reinterpret_cast<const u32x4*>(ckds + (size_t)(64 * h + v) * D + col);
-            *reinterpret_cast<u32x4*>(&sm.u.h.S0h[v][col]) = s;
-            *reinterpret_cast<u32x4*>(&sm.u.h.dSh[v][col]) = g;
-            const bf* se = reinterpret_cast<const bf*>(&s);
-            const bf* ge = reinterpret_cast<const bf*>(&g);
+    constexpr int NSP = 32 * CPR / 256, NDP = 32 * (CV / 8) / 256, NRP = CV * 4 / 256;
+    // not unrolled: an unrolled loop would hoist every quarter's loads to the
+    // top (the barriers order LDS only) and run out of registers
+#pragma unroll 1
+    for (int qv = 0; qv < NQ; ++qv) {
+        u32x4 pS[NSP], pG[NSP], pD[NDP], pR[NRP], pO[NRP];
+#pragma unroll
+        for (int it = 0; it < NSP; ++it) {
+            const int c = tid + 256 * it, v = c / CPR, col = (c % CPR) * 8;
+            pS[it] = *reinterpret_cast<const u32x4*>(cks + (size_t)(32 * qv + v) * D + col);
+            pG[it] = *reinterpret_cast<const u32x4*>(ckds + (size_t)(32 * qv + v) * D + col);
+        }
+#pragma unroll
+        for (int it = 0; it < NDP; ++it) {
+            const int c = tid + 256 * it, v = c / (CV / 8), col = (c % (CV / 8)) * 8;
+            pD[it] = *reinterpret_cast<const u32x4*>(ckd + (size_t)(32 * qv + v) * CV + col);
+        }
+#pragma unroll
+        for (int it = 0; it < NRP; ++it) {
+            const int c = tid + 256 * it, i = c / 4, col = (c % 4) * 8;
+            const bool in = t0 + i < T_;
+            pR[it] = in ? *reinterpret_cast<const u32x4*>(dvg + (size_t)i * D + 32 * qv + col) : zero_u4();
+            pO[it] = in ? *reinterpret_cast<const u32x4*>(dog + (size_t)i * D + 32 * qv + col) : zero_u4();
+        }
+        lds_barrier();  // the previous quarter's operands are consumed
+#pragma unroll
+        for (int it = 0; it < NSP; ++it) {
+            const int c = tid + 256 * it, v = c / CPR, col = (c % CPR) * 8;
+            *reinterpret_cast<u32x4*>(&sm.u.q.S0q[v][col]) = pS[it];
+            *reinterpret_cast<u32x4*>(&sm.u.q.dSq[v][col]) = pG[it];
+            const bf* se = reinterpret_cast<const bf*>(&pS[it]);
+            const bf* ge = reinterpret_cast<const bf*>(&pG[it]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) sdot += bf2f(se[e]) * bf2f(ge[e]);
         }
-        for (int c = tid; c < 64 * (CV / 8); c += 512) {
-            const int v = c / (CV / 8), col = (c % (CV / 8)) * 8;
-            *reinterpret_cast<u32x4*>(&sm.u.h.Dh[v][col]) =
-                *reinterpret_cast<const u32x4*>(ckd + (size_t)(64 * h + v) * CV + col);
+#pragma unroll
+        for (int it = 0; it < NDP; ++it) {
+            const int c = tid + 256 * it, v = c / (CV / 8), col = (c % (CV / 8)) * 8;
+            *reinterpret_cast<u32x4*>(&sm.u.q.Dq[v][col]) = pD[it];
         }
-        for (int c = tid; c < CV * 8; c += 512) {
-            const int i = c / 8, col = (c % 8) * 8;
-            const bool in = t0 + i < T_;
-            *reinterpret_cast<u32x4*>(&sm.u.h.dRh[i][col]) =
-                in ? *reinterpret_cast<const u32x4*>(dvg + (size_t)i * D + 64 * h + col) : zero_u4();
-            *reinterpret_cast<u32x4*>(&sm.u.h.dOh[i][col]) =
-                in ? *reinterpret_cast<const u32x4*>(dog + (size_t)i * D + 64 * h + col) : zero_u4();
+#pragma unroll
+        for (int it = 0; it < NRP; ++it) {
+            const int c = tid + 256 * it, i = c / 4, col = (c % 4) * 8;
+            *reinterpret_cast<u32x4*>(&sm.u.q.dRq[i][col]) = pR[it];
+            *reinterpret_cast<u32x4*>(&sm.u.q.dOq[i][col]) = pO[it];
         }
         lds_barrier();
-        const bf* Dh = &sm.u.h.Dh[0][0];
-        const bf* S0h = &sm.u.h.S0h[0][0];
-        const bf* dSh = &sm.u.h.dSh[0][0];
+        const bf* Dq = &sm.u.q.Dq[0][0];
+        {
+            const Frag dj0 = colfrag(Dq, LDC, 0, 16 * jbw), dj1 = colfrag(Dq, LDC, 16, 16 * jbw);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const Frag dj0 = colfrag(Dh, LDC, 32 * m, 16 * jbw), dj1 = colfrag(Dh, LDC, 32 * m + 16, 16 * jbw);
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int tb = tbw0 + u;
+            for (int tb = 0; tb < NB; ++tb) {
                 if (tb >= jbw) {
-                    const bf* orow = &sm.u.h.dOh[16 * tb + lr][32 * m + 4 * grp];
-                    const Frag o0 = E::load(orow), o1 = E::load(orow + 16);
-                    aP[u] = E::mma32(dj0, dj1, o0, o1, aP[u]);
+                    const bf* orow = &sm.u.q.dOq[16 * tb + lr][4 * grp];
+                    aP[tb] = E::mma32(dj0, dj1, E::load(orow), E::load(orow + 16), aP[tb]);
                     if constexpr (DELTA) {
-                        const bf* rrow = &sm.u.h.dRh[16 * tb + lr][32 * m + 4 * grp];
-                        aA[u] = E::mma32(dj0, dj1, E::load(rrow), E::load(rrow + 16), aA[u]);
+                        const bf* rrow = &sm.u.q.dRq[16 * tb + lr][4 * grp];
+                        aA[tb] = E::mma32(dj0, dj1, E::load(rrow), E::load(rrow + 16), aA[tb]);
                     }
                 }
             }
-            const Frag s0 = colfrag(S0h, LDX, 32 * m, 16 * kb), s1 = colfrag(S0h, LDX, 32 * m + 16, 16 * kb);
-            const Frag g0 = colfrag(dSh, LDX, 32 * m, 16 * kb), g1 = colfrag(dSh, LDX, 32 * m + 16, 16 * kb);
+        }
 #pragma unroll
-            for (int c = 0; c < NCB; ++c) {
-                const int cb = cb0 + c;
-                const bf* orow = &sm.u.h.dOh[16 * cb + lr][32 * m + 4 * grp];
-                aQ[c] = E::mma32(s0, s1, E::load(orow), E::load(orow + 16), aQ[c]);
+        for (int kk = 0; kk < KPW; ++kk) {
+            const int kb = KPW * wave + kk;
+            const Frag s0 = colfrag(&sm.u.q.S0q[0][0], LDX, 0, 16 * kb);
+            const Frag s1 = colfrag(&sm.u.q.S0q[0][0], LDX, 16, 16 * kb);
+            const Frag g0 = colfrag(&sm.u.q.dSq[0][0], LDX, 0, 16 * kb);
+            const Frag g1 = colfrag(&sm.u.q.dSq[0][0], LDX, 16, 16 * kb);
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) {
+                const bf* orow = &sm.u.q.dOq[16 * cb + lr][4 * grp];
+                aQ[kk][cb] = E::mma32(s0, s1, E::load(orow), E::load(orow + 16), aQ[kk][cb]);
                 if constexpr (DELTA) {
-                    const bf* rrow = &sm.u.h.dRh[16 * cb + lr][32 * m + 4 * grp];
-                    aX[c] = E::mma32(s0, s1, E::load(rrow), E::load(rrow + 16), aX[c]);
+                    const bf* rrow = &sm.u.q.dRq[16 * cb + lr][4 * grp];
+                    aX[kk][cb] = E::mma32(s0, s1, E::load(rrow), E::load(rrow + 16), aX[kk][cb]);
                 }
-                aW[c] = E::mma32(g0, g1, colfrag(Dh, LDC, 32 * m, 16 * cb),
-                                 colfrag(Dh, LDC, 32 * m + 16, 16 * cb), aW[c]);
+                aW[kk][cb] = E::mma32(g0, g1, colfrag(Dq, LDC, 0, 16 * cb), colfrag(Dq, LDC, 16, 16 * cb),
+                                      aW[kk][cb]);
             }
         }
     }
 
-    // ---- decays, masks; DP and DA to LDS ----
+    // ---- decays; sum_j omega_j . dOmega3_j; DP and DA to LDS ----
     const float gL = sm.gs[CV - 1];
-    float s3 = 0.f;  // sum_j omega_j . dOmega3_j, this lane's share
+    float s3 = 0.f;
 #pragma unroll
-    for (int c = 0; c < NCB; ++c) {
-        const int col = 16 * (cb0 + c) + lr;
+    for (int cb = 0; cb < NB; ++cb) {
+        const int col = 16 * cb + lr;
         const float gc = sm.gs[col];
-        const float eq = exp2f(gc);
-        aQ[c] = aQ[c] * eq;
-        aX[c] = aX[c] * (-eq);
-        aW[c] = aW[c] * exp2f(gL - gc);
-        const Frag xk = E::load(&sm.X[col][16 * kb + 4 * grp]);
-        float p = 0.f;
+        const float eq = exp2f(gc), ew = exp2f(gL - gc), rc = sm.rr[col];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p += bf2f((bf)xk[r]) * aW[c][r];
-        s3 += sm.rr[col] * p;
+        for (int kk = 0; kk < KPW; ++kk) {
+            const int kb = KPW * wave + kk;
+            aQ[kk][cb] = aQ[kk][cb] * eq;
+            aX[kk][cb] = aX[kk][cb] * (-eq);
+            aW[kk][cb] = aW[kk][cb] * ew;
+            const Frag xk = E::load(&sm.X[col][16 * kb + 4 * grp]);
+            float p = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p += bf2f((bf)xk[r]) * aW[kk][cb][r];
+            s3 += rc * p;
+        }
     }
     s3 = group_sum<64>(s3);
     sdot = group_sum<64>(sdot);
@@ -514,23 +552,22 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
         sm.red[wave][0] = s3;
         sm.red[wave][1] = sdot;
     }
-    lds_barrier();  // the last half's operands are consumed before DP / DA overwrite nothing of
-                    // theirs, and the partial sums are visible
+    lds_barrier();  // the staging room is free for DP and DA
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int tb = tbw0 + u;
+    for (int tb = 0; tb < NB; ++tb) {
         const int t = 16 * tb + lr;
         const float gt = sm.gs[t];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int j = 16 * jbw + 4 * grp + r;
             const float gj = sm.gs[j], rj = sm.rr[j];
-            const float vp = (j <= t) ? aP[u][r] * exp2f(gt - gj) : 0.f;
-            const float va = (DELTA && j < t) ? -aA[u][r] * exp2f(gt - gj) : 0.f;
-            sm.u.h.DP[j][t] = f2bf(vp);
-            sm.u.h.DPr[j][t] = f2bf(vp * rj);
-            sm.u.h.DA[j][t] = f2bf(va);
-            sm.u.h.DAr[j][t] = f2bf(va * rj);
+            const float dec = (j <= t) ? exp2f(gt - gj) : 0.f;
+            const float vp = aP[tb][r] * dec;
+            const float va = (DELTA && j < t) ? -aA[tb][r] * dec : 0.f;
+            sm.u.m.DP[j][t] = f2bf(vp);
+            sm.u.m.DPr[j][t] = f2bf(vp * rj);
+            sm.u.m.DA[j][t] = f2bf(va);
+            sm.u.m.DAr[j][t] = f2bf(va * rj);
         }
     }
     lds_barrier();
@@ -539,156 +576,248 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
     {
         const bf* Xs = &sm.X[0][0];
         const bf* Qs = &sm.Q[0][0];
-        const bf* DP = &sm.u.h.DP[0][0];
-        const bf* DA = &sm.u.h.DA[0][0];
-        const bf* DPr = &sm.u.h.DPr[0][0];
-        const bf* DAr = &sm.u.h.DAr[0][0];
+        const bf* DP = &sm.u.m.DP[0][0];
+        const bf* DA = &sm.u.m.DA[0][0];
+        const bf* DPr = &sm.u.m.DPr[0][0];
+        const bf* DAr = &sm.u.m.DAr[0][0];
 #pragma unroll
-        for (int c = 0; c < NCB; ++c) {
-            const int cb = cb0 + c;
+        for (int kk = 0; kk < KPW; ++kk) {
+            const int kb = KPW * wave + kk;
 #pragma unroll
             for (int jb = 0; jb < NB; ++jb) {
-                if (jb <= cb) {
-                    const Frag xj = colfrag(Xs, LDX, 16 * jb, 16 * kb);
-                    aQ[c] = E::mma16(xj, colfrag(DPr, LDC, 16 * jb, 16 * cb), aQ[c]);
-                    if constexpr (DELTA) aX[c] = E::mma16(xj, colfrag(DAr, LDC, 16 * jb, 16 * cb), aX[c]);
-                }
-                if (jb >= cb) {
-                    aW[c] = E::mma16(colfrag(Qs, LDX, 16 * jb, 16 * kb),
-                                     E::load(DP + (size_t)(16 * cb + lr) * LDC + 16 * jb + 4 * grp), aW[c]);
-                    if constexpr (DELTA)
-                        aW[c] = E::mma16(colfrag(Xs, LDX, 16 * jb, 16 * kb),
-                                         E::load(DA + (size_t)(16 * cb + lr) * LDC + 16 * jb + 4 * grp), aW[c]);
+                const Frag xj = colfrag(Xs, LDX, 16 * jb, 16 * kb);
+                const Frag qj = colfrag(Qs, LDX, 16 * jb, 16 * kb);
+#pragma unroll
+                for (int cb = 0; cb < NB; ++cb) {
+                    if (jb <= cb) {
+                        aQ[kk][cb] = E::mma16(xj, colfrag(DPr, LDC, 16 * jb, 16 * cb), aQ[kk][cb]);
+                        if constexpr (DELTA)
+                            aX[kk][cb] = E::mma16(xj, colfrag(DAr, LDC, 16 * jb, 16 * cb), aX[kk][cb]);
+                    }
+                    if (jb >= cb) {
+                        aW[kk][cb] = E::mma16(qj, E::load(DP + (size_t)(16 * cb + lr) * LDC + 16 * jb + 4 * grp),
+                                              aW[kk][cb]);
+                        if constexpr (DELTA)
+                            aW[kk][cb] = E::mma16(xj, E::load(DA + (size_t)(16 * cb + lr) * LDC + 16 * jb + 4 * grp),
+                                                  aW[kk][cb]);
+                    }
                 }
             }
         }
     }
-    lds_barrier();
+
+    // ---- row sums across the waves: x_j.dX_j, x_j.dOmega_j, q_t.dQ_t ----
+    // lane (lr, grp) holds, for column block cb, row 16 cb + lr and entries
+    // k = 16 kb + 4 grp + r of each of its k blocks
+    auto row_sum = [&](float v) __attribute__((always_inline)) {
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        return v;
+    };
 #pragma unroll
-    for (int c = 0; c < NCB; ++c) {
-        const int row = 16 * (cb0 + c) + lr;
-        *reinterpret_cast<f32x4*>(&sm.u.w.dQ[row][16 * kb + 4 * grp]) = aQ[c];
-        *reinterpret_cast<f32x4*>(&sm.u.w.dX[row][16 * kb + 4 * grp]) = aX[c];
-        *reinterpret_cast<f32x4*>(&sm.u.w.dW[row][16 * kb + 4 * grp]) = aW[c];
+    for (int cb = 0; cb < NB; ++cb) {
+        const int row = 16 * cb + lr;
+        float pX = 0.f, pO = 0.f, pQ = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KPW; ++kk) {
+            const int kb = KPW * wave + kk;
+            const Frag xk = E::load(&sm.X[row][16 * kb + 4 * grp]);
+            const Frag qk = E::load(&sm.Q[row][16 * kb + 4 * grp]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x = bf2f((bf)xk[r]);
+                pX += x * aX[kk][cb][r];
+                pO += x * aW[kk][cb][r];
+                pQ += bf2f((bf)qk[r]) * aQ[kk][cb][r];
+            }
+        }
+        pX = row_sum(pX);
+        pO = row_sum(pO);
+        pQ = row_sum(pQ);
+        if (grp == 0) {
+            sm.part[wave][0][row] = pX;
+            sm.part[wave][1][row] = pO;
+            sm.part[wave][2][row] = pQ;
+        }
     }
     lds_barrier();
-
-    // ---- row epilogue: 8 lanes per row ----
-    {
-        const int row = tid >> 3, part = tid & 7, k0 = part * EPT;
-        const int t = t0 + row;
-        float x[EPT], dx[EPT], dw[EPT], qv[EPT], dq[EPT];
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            x[e] = bf2f(sm.X[row][k0 + e]);
-            qv[e] = bf2f(sm.Q[row][k0 + e]);
-            dx[e] = sm.u.w.dX[row][k0 + e];
-            dw[e] = sm.u.w.dW[row][k0 + e];
-            dq[e] = sm.u.w.dQ[row][k0 + e];
-        }
+    if (tid < CV) {
+        const int row = tid, t = t0 + row;
         float sX = 0.f, sO = 0.f, sQ = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            sX += x[e] * dx[e];
-            sO += x[e] * dw[e];
-            sQ += qv[e] * dq[e];
+        for (int w = 0; w < 4; ++w) {
+            sX += sm.part[w][0][row];
+            sO += sm.part[w][1][row];
+            sQ += sm.part[w][2][row];
         }
-        sX = group_sum_dpp<8>(sX);
-        sO = group_sum_dpp<8>(sO);
-        sQ = group_sum_dpp<8>(sQ);
         const float r = sm.rr[row], n = sm.nn[row];
-        const float cn = n > 0.f ? 2.f * r * sO / n : 0.f;
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) dx[e] = dx[e] + r * dw[e] - cn * x[e];
-        if (part == 0) {
-            sm.dg[row] = sX - r * sO + sQ;
-            if (t < T_) a.deta[(size_t)bh * T_ + t] = n > 0.f ? sO / n : 0.f;
-        }
-
-        // the feature map's derivative, on the caller's raw rows
-        auto phi_back = [&](float (&g)[EPT], const bf* raw) __attribute__((always_inline)) {
-            if (a.phi == 0) return;
-            float kr[EPT];
-            const u32x4* p = reinterpret_cast<const u32x4*>(raw + k0);
-#pragma unroll
-            for (int c = 0; c < EPT / 8; ++c) {
-                const u32x4 v = p[c];
-                const bf* e8 = reinterpret_cast<const bf*>(&v);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) kr[8 * c + e] = bf2f(e8[e]);
-            }
-            if (a.phi == 1) {
-                float n2 = 0.f;
-#pragma unroll
-                for (int e = 0; e < EPT; ++e) n2 += kr[e] * kr[e];
-                n2 = group_sum_dpp<8>(n2);
-                const float inv = n2 > 0.f ? rsqrtf(n2) : 0.f;
-                float pd = 0.f;
-#pragma unroll
-                for (int e = 0; e < EPT; ++e) pd += kr[e] * inv * g[e];
-                pd = group_sum_dpp<8>(pd);
-#pragma unroll
-                for (int e = 0; e < EPT; ++e) g[e] = (g[e] - kr[e] * inv * pd) * inv;
-            } else {
-#pragma unroll
-                for (int e = 0; e < EPT; ++e) {
-                    const float s = 1.f / (1.f + __expf(-kr[e]));
-                    g[e] = g[e] * s * (1.f + kr[e] * (1.f - s));
-                }
-            }
-        };
-        auto store_row = [&](bf* dst, const float (&g)[EPT]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int c = 0; c < EPT / 8; ++c) {
-                u32x4 o;
-                bf* oe = reinterpret_cast<bf*>(&o);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) oe[e] = f2bf(g[8 * c + e]);
-                *reinterpret_cast<u32x4*>(dst + k0 + 8 * c) = o;
-            }
-        };
-
-        // key row tau = t - lag: its only use (window of one) is as x of step t;
-        // a padded step (t >= T) computes dx = 0, which is the gradient of the
-        // key no step reads (k_{T-1} under prefix alignment)
-        const int tau = t - lag;
-        const bool key_row = (t < T_ + lag) && tau < T_ && (tau >= 0 || (a.dk_prev && a.kp_raw));
-        if (key_row) {  // uniform over the row's 8 lanes
-            const bf* raw = tau >= 0 ? static_cast<const bf*>(a.k_raw) + ((size_t)bh * T_ + tau) * D
-                                     : static_cast<const bf*>(a.kp_raw) + ((size_t)bh * W + W + tau) * D;
-            phi_back(dx, raw);
-            bf* dst = tau >= 0 ? static_cast<bf*>(a.dk) + ((size_t)bh * T_ + tau) * D
-                               : static_cast<bf*>(a.dk_prev) + ((size_t)bh * W + W + tau) * D;
-            store_row(dst, dx);
-        }
-        if (t < T_) {
-            phi_back(dq, static_cast<const bf*>(a.q_raw) + ((size_t)bh * T_ + t) * D);
-            store_row(static_cast<bf*>(a.dq) + ((size_t)bh * T_ + t) * D, dq);
-        }
-        // keys no row of any tile reaches: k_{T-1} (prefix alignment, T a
-        // multiple of the tile) and the halo rows same-step pairs never read
-        const bool last = t0 + CV >= T_;
-        if (last && lag == 1 && T_ - t0 == CV && row == 0) {
-            float z[EPT];
-#pragma unroll
-            for (int e = 0; e < EPT; ++e) z[e] = 0.f;
-            store_row(static_cast<bf*>(a.dk) + ((size_t)bh * T_ + T_ - 1) * D, z);
-        }
-        if (tile == 0 && a.dk_prev && row < W && (lag == 0 || !a.kp_raw || row < W - 1)) {
-            float z[EPT];
-#pragma unroll
-            for (int e = 0; e < EPT; ++e) z[e] = 0.f;
-            store_row(static_cast<bf*>(a.dk_prev) + ((size_t)bh * W + row) * D, z);
-        }
+        sm.cn[row] = n > 0.f ? 2.f * r * sO / n : 0.f;
+        sm.dg[row] = sX - r * sO + sQ;
+        if (t < T_) a.deta[(size_t)bh * T_ + t] = n > 0.f ? sO / n : 0.f;
     }
     lds_barrier();
+
+    // ---- key and query gradients: dx = dX + r dOmega - cn x, dq = dQ ----
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+        const int row = 16 * cb + lr;
+        const float r = sm.rr[row], c = sm.cn[row];
+#pragma unroll
+        for (int kk = 0; kk < KPW; ++kk) {
+            const int kb = KPW * wave + kk;
+            const Frag xk = E::load(&sm.X[row][16 * kb + 4 * grp]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                aX[kk][cb][e] = aX[kk][cb][e] + r * aW[kk][cb][e] - c * bf2f((bf)xk[e]);
+        }
+    }
+    // rows: key row tau = t - lag (its only use, window of one, is as x of step
+    // t; a padded step t >= T computes dx = 0, the gradient of the key no step
+    // reads), query row t
+    auto key_ok = [&](int row) __attribute__((always_inline)) {
+        const int t = t0 + row, tau = t - lag;
+        return (t < T_ + lag) && tau < T_ && (tau >= 0 || (a.dk_prev && a.kp_raw));
+    };
+    auto key_raw = [&](int row) __attribute__((always_inline)) {
+        const int tau = t0 + row - lag;
+        return tau >= 0 ? static_cast<const bf*>(a.k_raw) + ((size_t)bh * T_ + tau) * D
+                        : static_cast<const bf*>(a.kp_raw) + ((size_t)bh * W + W + tau) * D;
+    };
+    auto raw4 = [&](const bf* raw, int kb, float (&kr)[4]) __attribute__((always_inline)) {
+        const Frag f = *reinterpret_cast<const Frag*>(raw + 16 * kb + 4 * grp);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kr[e] = bf2f((bf)f[e]);
+    };
+    if (a.phi == 1) {
+        // L2 map: g_raw = (g - phi (phi . g)) / ||raw||, phi = raw / ||raw||
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) {
+            const int row = 16 * cb + lr;
+            const bool kok = key_ok(row), qok = t0 + row < T_;
+            float nk = 0.f, pk = 0.f, nq = 0.f, pq = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < KPW; ++kk) {
+                const int kb = KPW * wave + kk;
+                float kr[4];
+                if (kok) {
+                    raw4(key_raw(row), kb, kr);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        nk += kr[e] * kr[e];
+                        pk += kr[e] * aX[kk][cb][e];
+                    }
+                }
+                if (qok) {
+                    raw4(static_cast<const bf*>(a.q_raw) + ((size_t)bh * T_ + t0 + row) * D, kb, kr);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        nq += kr[e] * kr[e];
+                        pq += kr[e] * aQ[kk][cb][e];
+                    }
+                }
+            }
+            nk = row_sum(nk);
+            pk = row_sum(pk);
+            nq = row_sum(nq);
+            pq = row_sum(pq);
+            if (grp == 0) {
+                sm.part[wave][0][row] = nk;
+                sm.part[wave][1][row] = pk;
+                sm.part[wave][2][row] = nq;
+                sm.part[wave][3][row] = pq;
+            }
+        }
+        lds_barrier();
+        if (tid < CV) {
+            float nk = 0.f, pk = 0.f, nq = 0.f, pq = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                nk += sm.part[w][0][tid];
+                pk += sm.part[w][1][tid];
+                nq += sm.part[w][2][tid];
+                pq += sm.part[w][3][tid];
+            }
+            const float ik = nk > 0.f ? rsqrtf(nk) : 0.f, iq = nq > 0.f ? rsqrtf(nq) : 0.f;
+            sm.rowk[0][tid] = ik;
+            sm.rowk[1][tid] = pk * ik;  // phi . g
+            sm.rowq[0][tid] = iq;
+            sm.rowq[1][tid] = pq * iq;
+        }
+        lds_barrier();
+    }
+    auto phi_back = [&](float (&g)[4], const float (&kr)[4], float inv, float pd) __attribute__((always_inline)) {
+        if (a.phi == 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) g[e] = (g[e] - kr[e] * inv * pd) * inv;
+        } else if (a.phi == 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float sg = 1.f / (1.f + __expf(-kr[e]));
+                g[e] = g[e] * sg * (1.f + kr[e] * (1.f - sg));
+            }
+        }
+    };
+    auto pack4 = [&](const float (&g)[4]) __attribute__((always_inline)) {
+        Frag f;
+        f.x = (short)f2bf(g[0]);
+        f.y = (short)f2bf(g[1]);
+        f.z = (short)f2bf(g[2]);
+        f.w = (short)f2bf(g[3]);
+        return f;
+    };
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+        const int row = 16 * cb + lr, t = t0 + row, tau = t - lag;
+        if (key_ok(row)) {
+            bf* dst = tau >= 0 ? static_cast<bf*>(a.dk) + ((size_t)bh * T_ + tau) * D
+                               : static_cast<bf*>(a.dk_prev) + ((size_t)bh * W + W + tau) * D;
+            const bf* raw = key_raw(row);
+#pragma unroll
+            for (int kk = 0; kk < KPW; ++kk) {
+                const int kb = KPW * wave + kk;
+                float g[4] = {aX[kk][cb][0], aX[kk][cb][1], aX[kk][cb][2], aX[kk][cb][3]};
+                float kr[4] = {0.f, 0.f, 0.f, 0.f};
+                if (a.phi) raw4(raw, kb, kr);
+                phi_back(g, kr, a.phi == 1 ? sm.rowk[0][row] : 0.f, a.phi == 1 ? sm.rowk[1][row] : 0.f);
+                *reinterpret_cast<Frag*>(dst + 16 * kb + 4 * grp) = pack4(g);
+            }
+        }
+        if (t < T_) {
+            bf* dst = static_cast<bf*>(a.dq) + ((size_t)bh * T_ + t) * D;
+            const bf* raw = static_cast<const bf*>(a.q_raw) + ((size_t)bh * T_ + t) * D;
+#pragma unroll
+            for (int kk = 0; kk < KPW; ++kk) {
+                const int kb = KPW * wave + kk;
+                float g[4] = {aQ[kk][cb][0], aQ[kk][cb][1], aQ[kk][cb][2], aQ[kk][cb][3]};
+                float kr[4] = {0.f, 0.f, 0.f, 0.f};
+                if (a.phi) raw4(raw, kb, kr);
+                phi_back(g, kr, a.phi == 1 ? sm.rowq[0][row] : 0.f, a.phi == 1 ? sm.rowq[1][row] : 0.f);
+                *reinterpret_cast<Frag*>(dst + 16 * kb + 4 * grp) = pack4(g);
+            }
+        }
+    }
+    // keys no row of any tile reaches: k_{T-1} (prefix alignment, T a multiple
+    // of the tile) and the halo rows same-step pairs never read
+    if (t0 + CV == T_ && lag == 1) {
+        for (int c = tid; c < CPR; c += 256)
+            *reinterpret_cast<u32x4*>(static_cast<bf*>(a.dk) + ((size_t)bh * T_ + T_ - 1) * D + 8 * c) = zero_u4();
+    }
+    if (tile == 0 && a.dk_prev) {
+        for (int c = tid; c < W * CPR; c += 256) {
+            const int row = c / CPR;
+            if (lag == 0 || !a.kp_raw || row < W - 1)
+                *reinterpret_cast<u32x4*>(static_cast<bf*>(a.dk_prev) + ((size_t)bh * W + row) * D +
+                                          8 * (c % CPR)) = zero_u4();
+        }
+    }
+
     // ---- decay gradients: dlog alpha_s = sum over the tile's steps s' >= s of dg ----
     if (wave == 0) {
         float g = sm.dg[lane];
         if (lane == CV - 1) {
             float s3t = 0.f, sdt = 0.f;
 #pragma unroll
-            for (int w = 0; w < 8; ++w) {
+            for (int w = 0; w < 4; ++w) {
                 s3t += sm.red[w][0];
                 sdt += sm.red[w][1];
             }
@@ -725,7 +854,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.T > 0) {
-        hipLaunchKernelGGL((bwd_grad_kernel<D, CV, DELTA>), dim3(a.BH * a.ntiles), dim3(512), 0, stream, a);
+        hipLaunchKernelGGL((bwd_grad_kernel<D, CV, DELTA>), dim3(a.BH * a.ntiles), dim3(256), 0, stream, a);
         e = hipGetLastError();
     } else if (a.dk_prev) {
         const size_t n = (size_t)a.BH * a.W * D;
