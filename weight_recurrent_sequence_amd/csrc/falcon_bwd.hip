@@ -44,6 +44,9 @@ typedef uint16_t bf;
 
 __device__ __forceinline__ u32x4 zero_u4() { return u32x4{0u, 0u, 0u, 0u}; }
 
+// s_waitcnt vmcnt(0), leaving the other counters alone
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Key row of virtual row i of the tile starting at t0 (window 1): k_{t0+i-lag},
 // the halo before the sequence, zero outside.
 __device__ __forceinline__ u32x4 key_piece(const bf* kg, const bf* kp, int W, int T, int tau,
@@ -57,28 +60,37 @@ __device__ __forceinline__ u32x4 key_piece(const bf* kg, const bf* kp, int W, in
 
 // ---------------------------------------------------------------------------
 // Kernel 1: reverse scan over the tiles of one (batch*head, 64-wide value
-// slice); 4 waves, wave cw owns value columns v0 + 16 cw .. + 15.  The state
-// gradient slice lives in registers as accumulators of dS^T (lane (lr, grp),
-// block kb: dS[v = v0 + 16 cw + lr][k = 16 kb + 4 grp + r]), the operand
-// layout of X dS^T as it stands.  Per tile: checkpoint dS (the gradient at
-// the tile end), dDelta, the transposed blocked substitution, dv (= dR for a
-// window of one) through LDS as row stores, then dS at the tile start.  The
-// next tile's operands are loaded into registers while the current tile
-// computes.
+// slice), its 8 waves in two roles.
+//
+//   waves 0-3 (chain)  tile it: the state gradient slice lives in registers
+//                      as accumulators of dS^T (wave cw owns value columns
+//                      v0 + 16 cw .. + 15; lane (lr, grp), block kb holds
+//                      dS[v = v0 + 16 cw + lr][k = 16 kb + 4 grp + r]), the
+//                      operand layout of X dS^T as it stands.  Checkpoint of
+//                      dS (the gradient at the tile end, stored straight
+//                      from the registers), dDelta, the transposed blocked
+//                      substitution, dR to LDS, dS at the tile start.  No
+//                      loads: a wave that issues loads waits for its own
+//                      stores too (one counter), so the chain issues none.
+//   waves 4-7 (fill)   the LDS copies of tile it-1 (keys, queries, dO slice,
+//                      record), loaded through registers one iteration
+//                      ahead, and the row stores of dv for tile it+1 from the
+//                      chain's LDS dR.
+// Two LDS buffers by tile parity; one barrier per tile.
 // ---------------------------------------------------------------------------
 template <int D, int CV, bool DELTA>
 struct BScanSmem {
     using R = Rec<EBf16, CV, DELTA>;
     static constexpr int LDX = D + 8, LDY = 64 + 8;
-    bf X[CV][LDX];
-    bf Q[CV][LDX];
-    bf dO[CV][LDY];
-    bf dR[CV][LDY];
-    alignas(16) char rec[R::kBytes];
+    bf X[2][CV][LDX];
+    bf Q[2][CV][LDX];
+    bf dO[2][CV][LDY];
+    bf dR[2][CV][LDY];
+    alignas(16) char rec[2][R::kBytes];
 };
 
 template <int D, int CV, bool DELTA>
-__global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512) void bwd_scan_kernel(BwdArgs a) {
     using E = EBf16;
     using Frag = s16x4;
     using R = Rec<E, CV, DELTA>;
@@ -94,7 +106,9 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4,
               lr = lane & 15;
-    const int cw = wave;
+    const bool chain = wave < 4;
+    const int cw = wave & 3;
+    const int ftid = tid & 255;  // index within the fill role
     // slices of one sequence on one XCD (consecutive workgroups go round the 8)
     const int blk = blockIdx.x, xcd = blk & 7, jj = blk >> 3;
     const int bh = (jj / NVS) * 8 + xcd, vs = jj % NVS;
@@ -109,19 +123,13 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
     bf* dvg = static_cast<bf*>(a.dv) + (size_t)bh * T_ * D + v0;
     const int vcol = v0 + 16 * cw + lr;
 
-    f32x4 dS[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-        dS[kb] = a.dS_final ? *reinterpret_cast<const f32x4*>(a.dS_final + ((size_t)bh * D + vcol) * D +
-                                                              16 * kb + 4 * grp)
-                            : zero4();
-
+    // ---- fill: one tile through registers ----
     u32x4 px[NXL], pq[NXL], py[NYL], pr[NRL];
     auto load = [&](int tile) __attribute__((always_inline)) {
         const int t0 = tile * CV;
 #pragma unroll
         for (int it = 0; it < NXL; ++it) {
-            const int c = tid + 256 * it, i = c / CPR, col = (c % CPR) * 8;
+            const int c = ftid + 256 * it, i = c / CPR, col = (c % CPR) * 8;
             const bool ok = c < CV * CPR;
             px[it] = ok ? key_piece(kg, kp, W, T_, t0 + i - lag, col, D) : zero_u4();
             pq[it] = (ok && t0 + i < T_) ? *reinterpret_cast<const u32x4*>(qg + (size_t)(t0 + i) * D + col)
@@ -129,7 +137,7 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int it = 0; it < NYL; ++it) {
-            const int c = tid + 256 * it, i = c / 8, col = (c % 8) * 8;
+            const int c = ftid + 256 * it, i = c / 8, col = (c % 8) * 8;
             py[it] = (c < CV * 8 && t0 + i < T_)
                          ? *reinterpret_cast<const u32x4*>(dog + (size_t)(t0 + i) * D + col)
                          : zero_u4();
@@ -137,48 +145,90 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
         const char* rg = recg + (size_t)tile * R::kBytes;
 #pragma unroll
         for (int it = 0; it < NRL; ++it) {
-            const int c = tid + 256 * it;
+            const int c = ftid + 256 * it;
             pr[it] = c < RPC ? *reinterpret_cast<const u32x4*>(rg + 16 * (size_t)c) : zero_u4();
         }
     };
-    auto store = [&]() __attribute__((always_inline)) {
+    auto store = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
         for (int it = 0; it < NXL; ++it) {
-            const int c = tid + 256 * it, i = c / CPR, col = (c % CPR) * 8;
+            const int c = ftid + 256 * it, i = c / CPR, col = (c % CPR) * 8;
             if (c < CV * CPR) {
-                *reinterpret_cast<u32x4*>(&sm.X[i][col]) = px[it];
-                *reinterpret_cast<u32x4*>(&sm.Q[i][col]) = pq[it];
+                *reinterpret_cast<u32x4*>(&sm.X[b][i][col]) = px[it];
+                *reinterpret_cast<u32x4*>(&sm.Q[b][i][col]) = pq[it];
             }
         }
 #pragma unroll
         for (int it = 0; it < NYL; ++it) {
-            const int c = tid + 256 * it, i = c / 8, col = (c % 8) * 8;
-            if (c < CV * 8) *reinterpret_cast<u32x4*>(&sm.dO[i][col]) = py[it];
+            const int c = ftid + 256 * it, i = c / 8, col = (c % 8) * 8;
+            if (c < CV * 8) *reinterpret_cast<u32x4*>(&sm.dO[b][i][col]) = py[it];
         }
 #pragma unroll
         for (int it = 0; it < NRL; ++it) {
-            const int c = tid + 256 * it;
-            if (c < RPC) *reinterpret_cast<u32x4*>(sm.rec + 16 * c) = pr[it];
+            const int c = ftid + 256 * it;
+            if (c < RPC) *reinterpret_cast<u32x4*>(sm.rec[b] + 16 * c) = pr[it];
         }
     };
+    auto store_dv = [&](int tile) __attribute__((always_inline)) {
+        const int t0 = tile * CV, b = tile & 1;
+#pragma unroll
+        for (int q = 0; q < NYL; ++q) {
+            const int c = ftid + 256 * q, i = c / 8, col = (c % 8) * 8;
+            if (c < CV * 8 && t0 + i < T_)
+                *reinterpret_cast<u32x4*>(dvg + (size_t)(t0 + i) * D + col) =
+                    *reinterpret_cast<const u32x4*>(&sm.dR[b][i][col]);
+        }
+    };
+
     // column fragment of a row-major LDS tile: lane (lr, grp) gets
     // M[row0 + 4 grp + r][col0 + lr]
     auto colfrag = [&](const bf* m, int ld, int row0, int col0) __attribute__((always_inline)) {
         return E::load_tr(m + (size_t)(row0 + 4 * grp + (lr >> 2)) * ld + col0 + 4 * (lr & 3));
     };
+
+    if (!chain) {
+        // fill: tile ntl-1 into LDS, tile ntl-2 into registers, then per
+        // iteration it: tile it-1 into LDS, tile it-2 into registers, and
+        // dv of tile it+1 out of LDS
+        if (ntl > 0) {
+            load(ntl - 1);
+            store((ntl - 1) & 1);
+            if (ntl > 1) load(ntl - 2);
+        }
+        lds_barrier();
+        for (int it = ntl - 1; it >= 0; --it) {
+            if (it >= 1) store((it - 1) & 1);
+            if (it >= 2) load(it - 2);
+            if (it + 1 < ntl) store_dv(it + 1);
+            lds_barrier();
+        }
+        if (ntl > 0) store_dv(0);
+        return;
+    }
+
+    f32x4 dS[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+        dS[kb] = a.dS_final ? *reinterpret_cast<const f32x4*>(a.dS_final + ((size_t)bh * D + vcol) * D +
+                                                              16 * kb + 4 * grp)
+                            : zero4();
+    // the state gradient's initial loads are complete before the loop, so no
+    // wait inside it is owed to a load issued out here
+    wait_vm_all();
+    lds_barrier();
     // transposed record block (element offset `off`): lane (lr, grp) gets
     // M[4 grp + r][lr] of a block stored with M[lr][4 grp + r] at lane (lr, grp)
-    auto rec_tr = [&](size_t off) __attribute__((always_inline)) {
-        const bf* b = reinterpret_cast<const bf*>(sm.rec) + off;
-        return E::load_tr(b + (size_t)((lr & 3) * 16 + 4 * grp + (lr >> 2)) * 4);
-    };
-
-    if (ntl > 0) load(ntl - 1);
     for (int it = ntl - 1; it >= 0; --it) {
-        store();
-        lds_barrier();
-        if (it > 0) load(it - 1);
-        const float* gam = reinterpret_cast<const float*>(sm.rec + R::kScalBytes);
+        const int b = it & 1;
+        const char* recb = sm.rec[b];
+        auto rec_tr = [&](size_t off) __attribute__((always_inline)) {
+            const bf* blkp = reinterpret_cast<const bf*>(recb) + off;
+            return E::load_tr(blkp + (size_t)((lr & 3) * 16 + 4 * grp + (lr >> 2)) * 4);
+        };
+        const bf* Xb = &sm.X[b][0][0];
+        const bf* Qb = &sm.Q[b][0][0];
+        const bf* dOb = &sm.dO[b][0][0];
+        const float* gam = reinterpret_cast<const float*>(recb + R::kScalBytes);
         const float* hrow = gam + CV;
         const float* gq = gam + 2 * CV;
 
@@ -199,7 +249,7 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
         for (int m = 0; m < D / 32; ++m) {
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb) {
-                const bf* xr = &sm.X[16 * rb + lr][32 * m + 4 * grp];
+                const bf* xr = Xb + (size_t)(16 * rb + lr) * LDX + 32 * m + 4 * grp;
                 dd[rb] = E::mma32(E::load(xr), E::load(xr + 16), dSB[2 * m], dSB[2 * m + 1], dd[rb]);
             }
         }
@@ -211,7 +261,7 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
         }
         Frag dOc[NB];
 #pragma unroll
-        for (int tb = 0; tb < NB; ++tb) dOc[tb] = colfrag(&sm.dO[0][0], LDY, 16 * tb, 16 * cw);
+        for (int tb = 0; tb < NB; ++tb) dOc[tb] = colfrag(dOb, LDY, 16 * tb, 16 * cw);
         static_for<NB>([&](auto rbc) __attribute__((always_inline)) {
             constexpr int rb = decltype(rbc)::value;
             static_for<NB>([&](auto tbc) __attribute__((always_inline)) {
@@ -241,11 +291,11 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb) dr[rb] = dd[rb];
         }
-        // dv rows leave through LDS
+        // dv rows leave through LDS (the fill waves store them)
 #pragma unroll
         for (int rb = 0; rb < NB; ++rb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sm.dR[16 * rb + 4 * grp + r][16 * cw + lr] = f2bf(dr[rb][r]);
+            for (int r = 0; r < 4; ++r) sm.dR[b][16 * rb + 4 * grp + r][16 * cw + lr] = f2bf(dr[rb][r]);
 
         // dS at the tile start: exp(g_L) dS + (Q^T diag(gq) dO - X^T diag(gam) dR)^T
         const float gl = gq[CV - 1];
@@ -273,30 +323,19 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
             f32x4 acc = dS[kb] * gl;
 #pragma unroll
             for (int m = 0; m < NB / 2; ++m)
-                acc = E::mma32(colfrag(&sm.Q[0][0], LDX, 32 * m, 16 * kb),
-                               colfrag(&sm.Q[0][0], LDX, 32 * m + 16, 16 * kb), bq[2 * m], bq[2 * m + 1], acc);
+                acc = E::mma32(colfrag(Qb, LDX, 32 * m, 16 * kb), colfrag(Qb, LDX, 32 * m + 16, 16 * kb),
+                               bq[2 * m], bq[2 * m + 1], acc);
             // the residuals' S0 term (delta family only: the inner-product
             // family writes its targets, which do not depend on S0)
             if constexpr (DELTA) {
 #pragma unroll
                 for (int m = 0; m < NB / 2; ++m)
-                    acc = E::mma32(colfrag(&sm.X[0][0], LDX, 32 * m, 16 * kb),
-                                   colfrag(&sm.X[0][0], LDX, 32 * m + 16, 16 * kb), bx[2 * m], bx[2 * m + 1],
-                                   acc);
+                    acc = E::mma32(colfrag(Xb, LDX, 32 * m, 16 * kb), colfrag(Xb, LDX, 32 * m + 16, 16 * kb),
+                                   bx[2 * m], bx[2 * m + 1], acc);
             }
             dS[kb] = acc;
         }
         lds_barrier();
-        {
-            const int t0 = it * CV;
-#pragma unroll
-            for (int q = 0; q < NYL; ++q) {
-                const int c = tid + 256 * q, i = c / 8, col = (c % 8) * 8;
-                if (c < CV * 8 && t0 + i < T_)
-                    *reinterpret_cast<u32x4*>(dvg + (size_t)(t0 + i) * D + col) =
-                        *reinterpret_cast<const u32x4*>(&sm.dR[i][col]);
-            }
-        }
     }
     if (a.dS0) {
 #pragma unroll
@@ -850,7 +889,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     constexpr int CV = 64;
     const int nvs = D / 64;
     const int bh8 = (a.BH + 7) / 8 * 8;
-    hipLaunchKernelGGL((bwd_scan_kernel<D, CV, DELTA>), dim3(bh8 * nvs), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_scan_kernel<D, CV, DELTA>), dim3(bh8 * nvs), dim3(512), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.T > 0) {
