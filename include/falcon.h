@@ -188,17 +188,20 @@ int falcon_chunk_fwd_varlen(const void* q, const void* k, const void* v, const f
  *   dS0         [B,H,dv,dk] fp32 output, or NULL (not wanted)
  *   dk_prev     [B,H,W,dk]  dtype dt output, or NULL (not wanted); zero where
  *               no pair reads the halo key (or k_prev is NULL)
- *   dv_prev     unused (a window of one reads no value before the sequence)
+ *   dv_prev     [B,H,W-1,dv] dtype dt output, or NULL (not wanted); zero
+ *               where v_prev is NULL; unused for a window of one
  *   workspace   falcon_chunk_bwd_workspace(...) bytes: the forward's
  *               records, then the bf16 state at every tile start, the state
- *               gradient at every tile end and Delta of every
- *               tile, all bf16: about B*H*ceil(T/chunk)*dk*(4 dk + 2 chunk)
- *               bytes
+ *               gradient at every tile end and Delta of every tile (about
+ *               B*H*ntiles*dk*(4 dk + 2 chunk) bytes, ntiles =
+ *               ceil(T / (chunk / W))); with a window above one also the
+ *               per-row gradients of the targets and keys (2 B*H*ntiles*
+ *               chunk*dk*2 bytes), summed into dv / dk at the end
  * Outputs must not alias inputs or each other.
  *
- * Support matrix: dt bf16, dk = dv in {64, 128}, chunk 64, var F1 or F1A
- * (or F3 / F3A with window 1, the same rule), with FALCON_SAME_STEP and the
- * feature-map flags.  Other arguments that falcon_chunk_fwd accepts return
+ * Support matrix: dt bf16, dk = dv in {64, 128}, chunk 64, var F1, F1A,
+ * F3 or F3A (window 1..8), with FALCON_SAME_STEP and the feature-map
+ * flags.  Other arguments that falcon_chunk_fwd accepts return
  * FALCON_ERR_UNSUPPORTED; errors otherwise as for falcon_chunk_fwd.
  * falcon_chunk_bwd_workspace returns 0 for unsupported arguments and T = 0.
  */

@@ -14,9 +14,9 @@ from weight_recurrent_sequence_amd import inputs as I
 pytestmark = pytest.mark.gpu
 
 AX = {"dq": (2, 3), "dk": (2, 3), "dv": (2, 3), "dalpha": (2,), "deta": (2,), "dS0": (2, 3),
-      "dk_prev": (2, 3)}
+      "dk_prev": (2, 3), "dv_prev": (2, 3)}
 NAME = {"dq": "q", "dk": "k", "dv": "v", "dalpha": "alpha", "deta": "eta", "dS0": "S0",
-        "dk_prev": "k_prev"}
+        "dk_prev": "k_prev", "dv_prev": "v_prev"}
 
 
 @pytest.fixture(scope="module")
@@ -27,7 +27,7 @@ def dev():
     return torch.device("cuda:0")
 
 
-def run_bwd(dev, inp, variant, *, d_o, dS, align="prefix", phi="identity", sl=None):
+def run_bwd(dev, inp, variant, *, d_o, dS, align="prefix", phi="identity", sl=None, W=1):
     """GPU gradients and oracle gradients (optionally of one (b, h) slice)."""
     import torch
     import weight_recurrent_sequence_amd as fal
@@ -35,11 +35,11 @@ def run_bwd(dev, inp, variant, *, d_o, dS, align="prefix", phi="identity", sl=No
     B, H, T, D = inp.k.shape
     do_t = torch.from_numpy(np.ascontiguousarray(d_o)).view(torch.bfloat16).to(dev)
     dS_t = torch.from_numpy(dS).to(dev) if dS is not None else None
-    announce(f"chunk_bwd {variant} B{B} H{H} T{T} d{D} align={align} phi={phi} "
+    announce(f"chunk_bwd {variant} W{W} B{B} H{H} T{T} d{D} align={align} phi={phi} "
              f"S0={inp.S0 is not None} halo={inp.k_prev is not None} dS={dS is not None}")
     g = fal.chunk_bwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], do_t, variant, dS_final=dS_t,
-                      S0=t["S0"], k_prev=t["k_prev"], align=align, phi=phi,
-                      want_dk_prev=True)
+                      window=W, S0=t["S0"], k_prev=t["k_prev"], v_prev=t["v_prev"], align=align,
+                      phi=phi, want_dk_prev=True)
     torch.cuda.synchronize()
     d = inp.f64(sl)
     dof = inp.widen(d_o if sl is None else d_o[sl])
@@ -48,15 +48,15 @@ def run_bwd(dev, inp, variant, *, d_o, dS, align="prefix", phi="identity", sl=No
         d = {k: (None if v is None else v[None, None]) for k, v in d.items()}
         dof = dof[None, None]
         dSf = None if dSf is None else dSf[None, None]
-    ref = G.gradients(variant, d["q"], d["k"], d["v"], d["alpha"], d["eta"], dof, dSf,
-                      S0=d["S0"], k_prev=d["k_prev"], align=align, phi=phi)
+    ref = G.gradients(variant, d["q"], d["k"], d["v"], d["alpha"], d["eta"], dof, dSf, window=W,
+                      S0=d["S0"], k_prev=d["k_prev"], v_prev=d["v_prev"], align=align, phi=phi)
     got = {k: (None if v is None else to_np(v)) for k, v in g.items()}
     if sl is not None:
         got = {k: (None if v is None else v[sl][None, None]) for k, v in got.items()}
     return got, ref
 
 
-def check(got, ref, tol, keys=("dq", "dk", "dv", "dalpha", "deta", "dS0", "dk_prev")):
+def check(got, ref, tol, keys=("dq", "dk", "dv", "dalpha", "deta", "dS0", "dk_prev", "dv_prev")):
     """Per-slice errors at the bar.  The gate gradients of a step are dot
     products (dO_t . Delta, x_t . dOmega_t, ...) that can cancel, and the bf16
     forward forms Delta from a bf16 right-hand side: at a step whose dot
@@ -88,6 +88,42 @@ def test_bwd_grid(dev, variant, T, D):
     d_o, dS = I.make_cotangents(2, 3, T, D, D, seed=1300 + T + D)
     got, ref = run_bwd(dev, inp, variant, d_o=d_o, dS=dS)
     check(got, ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("W", [2, 3, 4, 8])
+@pytest.mark.parametrize("variant", ["F3", "F3A"])
+def test_bwd_window_grid(dev, variant, W, D):
+    """Windows above one: tiles of 64 // W steps, keys and values serving W
+    rows each (in up to two tiles), halos of W keys and W-1 values."""
+    T = 150
+    inp = I.make_chunk_inputs(2, 2, T, D, D, dtype="bf16", seed=1400 + 10 * W + D, window=W,
+                              halo=True, S0_sd=0.3)
+    d_o, dS = I.make_cotangents(2, 2, T, D, D, seed=1400 + 10 * W + D)
+    got, ref = run_bwd(dev, inp, variant, d_o=d_o, dS=dS, W=W)
+    check(got, ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("case", [("F3", 4, "same", "identity", 37), ("F3A", 3, "prefix", "l2", 64),
+                                  ("F3", 2, "prefix", "silu", 1), ("F3", 4, "prefix", "identity", 16),
+                                  ("F3A", 8, "same", "silu", 100)], ids=str)
+def test_bwd_window_options(dev, case):
+    variant, W, align, phi, T = case
+    inp = I.make_chunk_inputs(1, 3, T, 128, 128, dtype="bf16", seed=1450 + T + W, window=W,
+                              halo=True, S0_sd=0.3)
+    d_o, dS = I.make_cotangents(1, 3, T, 128, 128, seed=1450 + T + W)
+    got, ref = run_bwd(dev, inp, variant, d_o=d_o, dS=dS, W=W, align=align, phi=phi)
+    check(got, ref, TOL["bf16"])
+
+
+def test_bwd_window_without_halo(dev):
+    """No halos: the keys and values before the sequence are constant zeros,
+    and their gradients are reported as zeros."""
+    inp = I.make_chunk_inputs(1, 2, 90, 64, 64, dtype="bf16", seed=1460, window=4)
+    d_o, dS = I.make_cotangents(1, 2, 90, 64, 64, seed=1460)
+    got, ref = run_bwd(dev, inp, "F3", d_o=d_o, dS=dS, W=4)
+    check(got, ref, TOL["bf16"], keys=("dq", "dk", "dv", "dalpha", "deta", "dS0"))
+    assert not np.any(got["dk_prev"]) and not np.any(got["dv_prev"])
 
 
 @pytest.mark.parametrize("variant", ["F1", "F1A"])
@@ -140,7 +176,7 @@ def test_bwd_window_of_one_is_the_scalar_rule(dev, pair):
                       dS_final=dS_t, S0=t["S0"], k_prev=t["k_prev"])
     torch.cuda.synchronize()
     for k in a:
-        assert torch.equal(a[k], b[k]), k
+        assert (a[k] is None and b[k] is None) or torch.equal(a[k], b[k]), k
 
 
 def test_bwd_empty_sequence(dev):
@@ -172,7 +208,32 @@ def test_bwd_is_deterministic(dev):
                       S0=t["S0"], k_prev=t["k_prev"])
     torch.cuda.synchronize()
     for k in a:
-        assert torch.equal(a[k], b[k]), k
+        assert (a[k] is None and b[k] is None) or torch.equal(a[k], b[k]), k
+
+
+def test_bwd_window_large_sampled(dev):
+    """Falcon-3 with a window of four on the windowed workload's distributions
+    at B=2, H=16, d=128 and T=4096 (the fp64 oracle of one slice at the
+    workload's full T=32768 would take minutes); one (b, h) slice is checked."""
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    name = "falcon3_w4_bf16_B2H16T32768d128"
+    w = dict(I.WORKLOADS[name])
+    inp = I.workload_inputs(name, T=4096)
+    d_o, dS = I.make_cotangents(2, 16, 4096, 128, 128, seed=w["seed"])
+    t = inp.to_torch(dev)
+    do_t = torch.from_numpy(d_o).view(torch.bfloat16).to(dev)
+    announce("chunk_bwd F3 W4 B2 H16 T4096 d128")
+    g = fal.chunk_bwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], do_t, "F3", window=4,
+                      dS_final=torch.from_numpy(dS).to(dev))
+    torch.cuda.synchronize()
+    sl = (1, 9)
+    d = inp.f64(sl)
+    ref = G.gradients("F3", *(d[n][None, None] for n in ("q", "k", "v", "alpha", "eta")),
+                      inp.widen(d_o[sl])[None, None], np.asarray(dS[sl], np.float64)[None, None],
+                      window=4)
+    got = {k: (None if v is None else to_np(v[sl])[None, None]) for k, v in g.items()}
+    check(got, ref, TOL["bf16"], keys=("dq", "dk", "dv", "dalpha", "deta", "dS0"))
 
 
 @pytest.mark.parametrize("variant", ["F1", "F1A"])

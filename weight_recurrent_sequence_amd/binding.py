@@ -178,7 +178,8 @@ def chunk_bwd(q, k, v, alpha, eta, d_o, variant, *, dS_final=None, window=1, chu
     """Gradients of the chunk forward.  Inputs as for chunk_fwd, plus d_o
     [B,H,T,dv] (input dtype) and dS_final [B,H,dv,dk] fp32 or None.  Returns a
     dict with dq, dk, dv (input dtype), dalpha, deta (fp32), dS0 (fp32, or
-    None) and dk_prev (input dtype, when k_prev is given or want_dk_prev)."""
+    None), dk_prev (input dtype, when k_prev is given or want_dk_prev) and,
+    for a window above one, dv_prev (likewise)."""
     import torch
     var = _variant(variant, align, phi)
     B, H, T, dk = k.shape
@@ -204,6 +205,9 @@ def chunk_bwd(q, k, v, alpha, eta, d_o, variant, *, dS_final=None, window=1, chu
     if want_dk_prev is None:
         want_dk_prev = k_prev is not None
     g["dk_prev"] = torch.empty((B, H, window, dk), dtype=dt, device=dev) if want_dk_prev else None
+    # a window above one also reads W-1 values before the sequence
+    want_dv_prev = window > 1 and (v_prev is not None or want_dk_prev)
+    g["dv_prev"] = torch.empty((B, H, window - 1, dv), dtype=dt, device=dev) if want_dv_prev else None
     ws_n = int(lib().falcon_chunk_bwd_workspace(B, H, T, dk, dv, dtc, var, window, chunk))
     if workspace is not None:
         if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_n:
@@ -214,7 +218,7 @@ def chunk_bwd(q, k, v, alpha, eta, d_o, variant, *, dS_final=None, window=1, chu
     st = lib().falcon_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(S0),
                                 _ptr(k_prev), _ptr(v_prev), _ptr(d_o), _ptr(dS_final),
                                 _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dalpha"]),
-                                _ptr(g["deta"]), _ptr(g["dS0"]), _ptr(g["dk_prev"]), None,
+                                _ptr(g["deta"]), _ptr(g["dS0"]), _ptr(g["dk_prev"]), _ptr(g["dv_prev"]),
                                 B, H, T, dk, dv, dtc, var, window, chunk, float(eps), _ptr(ws),
                                 ws_n, _stream(stream))
     if st != 0:

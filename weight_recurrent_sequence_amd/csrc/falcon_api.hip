@@ -306,10 +306,13 @@ size_t falcon_chunk_bwd_workspace(int B, int H, int T, int dk, int dv, falcon_dt
     int base = 0, lag = 1, phi = 0;
     split_variant(var, &base, &lag, &phi);
     if (!falcon::chunk_bwd_supported((int)dt, dk, chunk, norm_of(base), window)) return 0;
-    const size_t ntiles = (size_t)((T + chunk - 1) / chunk);
+    const int Wv = norm_of(base) == falcon::kNormWindow ? window : 1;
+    const size_t ntiles = (size_t)((T + chunk / Wv - 1) / (chunk / Wv));
     const size_t ck = (size_t)B * H * ntiles * dk * dk * 2;
     const size_t cd = (size_t)B * H * ntiles * dk * chunk * 2;
-    return align256(fwd) + 2 * align256(ck) + align256(cd);
+    // windows above one: per-virtual-row gradients of targets and keys
+    const size_t cw = Wv > 1 ? 2 * align256(cd) : 0;
+    return align256(fwd) + 2 * align256(ck) + align256(cd) + cw;
 }
 
 int falcon_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
@@ -332,11 +335,10 @@ int falcon_chunk_bwd(const void* q, const void* k, const void* v, const float* a
         return FALCON_ERR_UNSUPPORTED;
     const size_t need = falcon_chunk_bwd_workspace(B, H, T, dk_, dv_, dt, var, window, chunk);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FALCON_ERR_WORKSPACE;
-    if (T == 0 && dS0 == nullptr && dk_prev == nullptr) return FALCON_OK;
-    (void)dv_prev;  // a window of one reads no value before the sequence
-
+    if (T == 0 && dS0 == nullptr && dk_prev == nullptr && dv_prev == nullptr) return FALCON_OK;
     const int BH = B * H;
-    const int ntiles = (T + chunk - 1) / chunk;
+    const int Wv = norm_of(base) == falcon::kNormWindow ? window : 1;
+    const int ntiles = (T + chunk / Wv - 1) / (chunk / Wv);
     const size_t fwd = falcon_chunk_fwd_workspace(B, H, T, dk_, dv_, dt, var, window, chunk);
     const size_t rec = align256(falcon::chunk_workspace_bytes(BH, T, (int)dt, chunk, window,
                                                               norm_of(base), is_delta(base)));
@@ -345,6 +347,9 @@ int falcon_chunk_bwd(const void* q, const void* k, const void* v, const float* a
     char* ck_s = ws + align256(fwd);
     char* ck_ds = ck_s + ck;
     char* ck_d = ck_ds + ck;
+    const size_t cdb = align256((size_t)BH * ntiles * dk_ * chunk * 2);
+    char* ck_r = Wv > 1 ? ck_d + cdb : nullptr;
+    char* ck_x = Wv > 1 ? ck_d + 2 * cdb : nullptr;
 
     falcon::ChunkArgs a;
     a.phi = phi;
@@ -402,6 +407,9 @@ int falcon_chunk_bwd(const void* q, const void* k, const void* v, const float* a
     b.ck_s = ck_s;
     b.ck_d = ck_d;
     b.ck_ds = ck_ds;
+    b.ck_r = ck_r;
+    b.ck_x = ck_x;
+    b.dv_prev = Wv > 1 ? dv_prev : nullptr;  // a window of one reads no value before the sequence
     b.BH = BH;
     b.T = T;
     b.ntiles = ntiles;

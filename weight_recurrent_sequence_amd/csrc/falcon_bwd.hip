@@ -89,7 +89,7 @@ struct BScanSmem {
     alignas(16) char rec[2][R::kBytes];
 };
 
-template <int D, int CV, bool DELTA>
+template <int D, int CV, bool DELTA, bool WIN>
 __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdArgs a) {
     using E = EBf16;
     using Frag = s16x4;
@@ -114,7 +114,9 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdArgs a) {
     const int bh = (jj / NVS) * 8 + xcd, vs = jj % NVS;
     if (bh >= a.BH) return;
     const int v0 = vs * 64;
-    const int T_ = a.T, ntiles = a.ntiles, ntl = tiles_of(T_, CV), W = a.W, lag = a.lag;
+    // a tile holds Ct steps of Wv virtual rows (step s, window slot w) each
+    const int W = a.W, Wv = WIN ? W : 1, Ct = CV / Wv, NVR = Ct * Wv, NBQ = (Ct + 15) / 16;
+    const int T_ = a.T, ntiles = a.ntiles, ntl = tiles_of(T_, Ct), lag = a.lag;
     const bf* kg = static_cast<const bf*>(a.k) + (size_t)bh * T_ * D;
     const bf* qg = static_cast<const bf*>(a.q) + (size_t)bh * T_ * D;
     const bf* dog = static_cast<const bf*>(a.d_o) + (size_t)bh * T_ * D + v0;
@@ -126,19 +128,22 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdArgs a) {
     // ---- fill: one tile through registers ----
     u32x4 px[NXL], pq[NXL], py[NYL], pr[NRL];
     auto load = [&](int tile) __attribute__((always_inline)) {
-        const int t0 = tile * CV;
+        const int t0 = tile * Ct;
 #pragma unroll
         for (int it = 0; it < NXL; ++it) {
             const int c = ftid + 256 * it, i = c / CPR, col = (c % CPR) * 8;
             const bool ok = c < CV * CPR;
-            px[it] = ok ? key_piece(kg, kp, W, T_, t0 + i - lag, col, D) : zero_u4();
-            pq[it] = (ok && t0 + i < T_) ? *reinterpret_cast<const u32x4*>(qg + (size_t)(t0 + i) * D + col)
-                                         : zero_u4();
+            // key of virtual row i = (step s, slot w): k_{t0 + s - w - lag}
+            const int sx = WIN ? i / Wv : i, wx = WIN ? i - sx * Wv : 0;
+            px[it] = (ok && i < NVR) ? key_piece(kg, kp, W, T_, t0 + sx - wx - lag, col, D) : zero_u4();
+            pq[it] = (ok && i < Ct && t0 + i < T_)
+                         ? *reinterpret_cast<const u32x4*>(qg + (size_t)(t0 + i) * D + col)
+                         : zero_u4();
         }
 #pragma unroll
         for (int it = 0; it < NYL; ++it) {
             const int c = ftid + 256 * it, i = c / 8, col = (c % 8) * 8;
-            py[it] = (c < CV * 8 && t0 + i < T_)
+            py[it] = (c < CV * 8 && i < Ct && t0 + i < T_)
                          ? *reinterpret_cast<const u32x4*>(dog + (size_t)(t0 + i) * D + col)
                          : zero_u4();
         }
@@ -169,14 +174,21 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdArgs a) {
             if (c < RPC) *reinterpret_cast<u32x4*>(sm.rec[b] + 16 * c) = pr[it];
         }
     };
+    // dR of `tile`: the rows of dv (a window of one), or the per-virtual-row
+    // gradients a gather sums into dv (windows above one)
     auto store_dv = [&](int tile) __attribute__((always_inline)) {
-        const int t0 = tile * CV, b = tile & 1;
+        const int t0 = tile * Ct, b = tile & 1;
 #pragma unroll
         for (int q = 0; q < NYL; ++q) {
             const int c = ftid + 256 * q, i = c / 8, col = (c % 8) * 8;
-            if (c < CV * 8 && t0 + i < T_)
-                *reinterpret_cast<u32x4*>(dvg + (size_t)(t0 + i) * D + col) =
-                    *reinterpret_cast<const u32x4*>(&sm.dR[b][i][col]);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.dR[b][i][col]);
+            if constexpr (WIN) {
+                if (c < CV * 8)
+                    *reinterpret_cast<u32x4*>(static_cast<bf*>(a.ck_r) +
+                                              (((size_t)bh * ntiles + tile) * CV + i) * D + v0 + col) = v;
+            } else {
+                if (c < CV * 8 && t0 + i < T_) *reinterpret_cast<u32x4*>(dvg + (size_t)(t0 + i) * D + col) = v;
+            }
         }
     };
 
@@ -266,8 +278,14 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdArgs a) {
             constexpr int rb = decltype(rbc)::value;
             static_for<NB>([&](auto tbc) __attribute__((always_inline)) {
                 constexpr int tb = decltype(tbc)::value;
-                if constexpr (tb >= rb)
+                if constexpr (WIN) {
+                    // the blocks the record holds: query block tb < NBQ that
+                    // reaches back to a row of block rb
+                    if (tb < NBQ && (16 * rb) / Wv <= 16 * tb + 15)
+                        dd[rb] = E::mma16(rec_tr(R::kP + (size_t)R::pblk(tb, rb, true) * 256), dOc[tb], dd[rb]);
+                } else if constexpr (tb >= rb) {
                     dd[rb] = E::mma16(rec_tr(R::kP + (size_t)R::pblk(tb, rb, false) * 256), dOc[tb], dd[rb]);
+                }
             });
         });
 
@@ -298,7 +316,7 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdArgs a) {
             for (int r = 0; r < 4; ++r) sm.dR[b][16 * rb + 4 * grp + r][16 * cw + lr] = f2bf(dr[rb][r]);
 
         // dS at the tile start: exp(g_L) dS + (Q^T diag(gq) dO - X^T diag(gam) dR)^T
-        const float gl = gq[CV - 1];
+        const float gl = gq[Ct - 1];
         Frag bq[NB], bx[NB];
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb) {
@@ -358,8 +376,8 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdArgs a) {
 template <int D, int CV>
 struct BGradSmem {
     static constexpr int LDX = D + 8, LDQ = 32 + 8, LDC = CV + 8;
-    bf X[CV][LDX];
-    bf Q[CV][LDX];
+    bf X[CV][LDX];   // keys of the virtual rows
+    bf Q[CV][LDX];   // queries of the steps
     struct Quarter {
         bf S0q[32][LDX];  // state at the tile start, 32 value rows ([v][k])
         bf dSq[32][LDX];  // state gradient at the tile end
@@ -378,22 +396,29 @@ struct BGradSmem {
         Mats m;
     } u;
     float part[4][4][CV];  // per-wave partial row sums
-    alignas(16) float gs[CV];  // log2(e) * g (tile-local cumulative log decay)
-    alignas(16) float rr[CV];  // write scale r_i
-    alignas(16) float nn[CV];  // ||x_i||^2 + eps
-    float al[CV], et[CV], dg[CV], cn[CV];
+    // per step s (tile-local): gates, log2(e) * g, the normalizer's
+    // denominator and step size, decay gradient, chain-rule factor
+    float al[CV], et[CV];
+    alignas(16) float gs[CV];
+    float den[CV], bst[CV], dg[CV], cn[CV];
+    // per virtual row i: its step, log2(e) * g of the step, write scale, ||x||^2,
+    // and the row sums x.dX, x.dOmega (q.dQ per step)
+    int st[CV];
+    alignas(16) float gv[CV];
+    alignas(16) float rr[CV];
+    float nrm[CV], sX[CV], sO[CV], sQ[CV];
     float rowk[2][CV], rowq[2][CV];  // feature map: 1/||raw||, phi . g
     float red[4][2];
 };
 
-template <int D, int CV, bool DELTA>
+template <int D, int CV, bool DELTA, bool WIN>
 __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
     using E = EBf16;
     using Frag = s16x4;
     using Smem = BGradSmem<D, CV>;
     constexpr int NB = CV / 16, KB = D / 16, CPR = D / 8, NQ = D / 32;
     constexpr int KPW = KB / 4;    // 16-row blocks of k per wave
-    constexpr int LDX = Smem::LDX, LDQ = Smem::LDQ, LDC = Smem::LDC;
+    constexpr int LDX = Smem::LDX, LDC = Smem::LDC;
     constexpr float kLog2e = 1.4426950408889634f;
     static_assert(NB == 4 && KB % 4 == 0, "one 64-row tile, d a multiple of 64");
     __shared__ Smem sm;
@@ -402,8 +427,10 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
               lr = lane & 15;
     const int ntiles = a.ntiles;
     const int bh = blockIdx.x / ntiles, tile = blockIdx.x - bh * ntiles;
-    const int T_ = a.T, W = a.W, lag = a.lag;
-    const int t0 = tile * CV;
+    // a tile holds Ct steps of Wv virtual rows (step s, window slot w) each
+    const int W = a.W, Wv = WIN ? W : 1, Ct = CV / Wv, NVR = Ct * Wv, NBQ = (Ct + 15) / 16;
+    const int T_ = a.T, lag = a.lag;
+    const int t0 = tile * Ct;
     if (bh >= a.BH || t0 >= T_) return;
     const size_t tix = (size_t)bh * ntiles + tile;
 
@@ -417,11 +444,13 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
         for (int it = 0; it < NXP; ++it) {
             const int c = tid + 256 * it, i = c / CPR, col = (c % CPR) * 8;
-            px[it] = key_piece(kg, kp, W, T_, t0 + i - lag, col, D);
-            pq[it] = t0 + i < T_ ? *reinterpret_cast<const u32x4*>(qg + (size_t)(t0 + i) * D + col) : zero_u4();
+            const int sx = WIN ? i / Wv : i, wx = WIN ? i - sx * Wv : 0;
+            px[it] = i < NVR ? key_piece(kg, kp, W, T_, t0 + sx - wx - lag, col, D) : zero_u4();
+            pq[it] = (i < Ct && t0 + i < T_) ? *reinterpret_cast<const u32x4*>(qg + (size_t)(t0 + i) * D + col)
+                                             : zero_u4();
         }
         if (tid < CV) {
-            const bool in = t0 + tid < T_;
+            const bool in = tid < Ct && t0 + tid < T_;
             sm.al[tid] = in ? a.alpha[(size_t)bh * T_ + t0 + tid] : 1.f;
             sm.et[tid] = in ? a.eta[(size_t)bh * T_ + t0 + tid] : 0.f;
         }
@@ -434,7 +463,7 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
     }
     lds_barrier();
     {
-        // norms and write scales (4 lanes per row), the log-decay scan (wave 0)
+        // norms (4 lanes per row)
         const int row = tid >> 2, part = tid & 3;
         constexpr int EP = D / 4;
         float n2 = 0.f;
@@ -444,20 +473,36 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
             n2 += x * x;
         }
         n2 = group_sum_dpp<4>(n2);
-        if (part == 0) {
-            const float den = n2 + a.eps;
-            sm.nn[row] = den;
-            sm.rr[row] = den > 0.f ? sm.et[row] / den : 0.f;
-        }
-        if (wave == 0) {
-            float lg = __logf(sm.al[lane]);
+        if (part == 0) sm.nrm[row] = n2;
+    }
+    lds_barrier();
+    if (tid < CV) {
+        // per step: the normalizer over the step's rows and the step size
+        const int s = tid;
+        float n2 = 0.f;
+        if (s < Ct)
+            for (int w = 0; w < Wv; ++w) n2 += sm.nrm[s * Wv + w];
+        const float dn = n2 + a.eps;
+        sm.den[s] = dn;
+        sm.bst[s] = (s < Ct && dn > 0.f) ? sm.et[s] / dn : 0.f;
+    }
+    if (wave == 0) {
+        // the log-decay scan over the steps (steps past the tile: alpha = 1)
+        float lg = __logf(sm.al[lane]);
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(lg, off, 64);
-                if (lane >= off) lg += y;
-            }
-            sm.gs[lane] = lg * kLog2e;
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(lg, off, 64);
+            if (lane >= off) lg += y;
         }
+        sm.gs[lane] = lg * kLog2e;
+    }
+    lds_barrier();
+    if (tid < CV) {
+        const int i = tid;
+        const int si = i < NVR ? i / Wv : (1 << 20);  // padding rows: after every step
+        sm.st[i] = si;
+        sm.gv[i] = sm.gs[i < NVR ? si : Ct - 1];
+        sm.rr[i] = i < NVR ? sm.bst[si] : 0.f;
     }
 
     auto colfrag = [&](const bf* m, int ld, int row0, int col0) __attribute__((always_inline)) {
@@ -479,7 +524,9 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
     const bf* cks = static_cast<const bf*>(a.ck_s) + tix * D * D;
     const bf* ckds = static_cast<const bf*>(a.ck_ds) + tix * D * D;
     const bf* ckd = static_cast<const bf*>(a.ck_d) + tix * D * CV;
-    const bf* dvg = static_cast<const bf*>(a.dv) + ((size_t)bh * T_ + t0) * D;
+    // dR rows: dv itself for a window of one, else the per-virtual-row copy
+    const bf* dRg = WIN ? static_cast<const bf*>(a.ck_r) + tix * CV * D
+                        : static_cast<const bf*>(a.dv) + ((size_t)bh * T_ + t0) * D;
     const bf* dog = static_cast<const bf*>(a.d_o) + ((size_t)bh * T_ + t0) * D;
     constexpr int NSP = 32 * CPR / 256, NDP = 32 * (CV / 8) / 256, NRP = CV * 4 / 256;
     // not unrolled: an unrolled loop would hoist every quarter's loads to the
@@ -501,9 +548,10 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
         for (int it = 0; it < NRP; ++it) {
             const int c = tid + 256 * it, i = c / 4, col = (c % 4) * 8;
-            const bool in = t0 + i < T_;
-            pR[it] = in ? *reinterpret_cast<const u32x4*>(dvg + (size_t)i * D + 32 * qv + col) : zero_u4();
-            pO[it] = in ? *reinterpret_cast<const u32x4*>(dog + (size_t)i * D + 32 * qv + col) : zero_u4();
+            const bool rin = WIN || t0 + i < T_;
+            const bool oin = i < Ct && t0 + i < T_;
+            pR[it] = rin ? *reinterpret_cast<const u32x4*>(dRg + (size_t)i * D + 32 * qv + col) : zero_u4();
+            pO[it] = oin ? *reinterpret_cast<const u32x4*>(dog + (size_t)i * D + 32 * qv + col) : zero_u4();
         }
         lds_barrier();  // the previous quarter's operands are consumed
 #pragma unroll
@@ -533,13 +581,15 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
             const Frag dj0 = colfrag(Dq, LDC, 0, 16 * jbw), dj1 = colfrag(Dq, LDC, 16, 16 * jbw);
 #pragma unroll
             for (int tb = 0; tb < NB; ++tb) {
-                if (tb >= jbw) {
+                // DP^T block (jbw, tb): query block tb reaching back to a row of block jbw
+                if (tb < NBQ && (16 * jbw) / Wv <= 16 * tb + 15) {
                     const bf* orow = &sm.u.q.dOq[16 * tb + lr][4 * grp];
                     aP[tb] = E::mma32(dj0, dj1, E::load(orow), E::load(orow + 16), aP[tb]);
-                    if constexpr (DELTA) {
-                        const bf* rrow = &sm.u.q.dRq[16 * tb + lr][4 * grp];
-                        aA[tb] = E::mma32(dj0, dj1, E::load(rrow), E::load(rrow + 16), aA[tb]);
-                    }
+                }
+                // DA^T block (jbw, tb): only rows of later steps, so tb >= jbw
+                if (DELTA && tb >= jbw) {
+                    const bf* rrow = &sm.u.q.dRq[16 * tb + lr][4 * grp];
+                    aA[tb] = E::mma32(dj0, dj1, E::load(rrow), E::load(rrow + 16), aA[tb]);
                 }
             }
         }
@@ -552,8 +602,10 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
             const Frag g1 = colfrag(&sm.u.q.dSq[0][0], LDX, 16, 16 * kb);
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb) {
-                const bf* orow = &sm.u.q.dOq[16 * cb + lr][4 * grp];
-                aQ[kk][cb] = E::mma32(s0, s1, E::load(orow), E::load(orow + 16), aQ[kk][cb]);
+                if (cb < NBQ) {
+                    const bf* orow = &sm.u.q.dOq[16 * cb + lr][4 * grp];
+                    aQ[kk][cb] = E::mma32(s0, s1, E::load(orow), E::load(orow + 16), aQ[kk][cb]);
+                }
                 if constexpr (DELTA) {
                     const bf* rrow = &sm.u.q.dRq[16 * cb + lr][4 * grp];
                     aX[kk][cb] = E::mma32(s0, s1, E::load(rrow), E::load(rrow + 16), aX[kk][cb]);
@@ -565,18 +617,19 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
     }
 
     // ---- decays; sum_j omega_j . dOmega3_j; DP and DA to LDS ----
-    const float gL = sm.gs[CV - 1];
+    const float gL = sm.gs[Ct - 1];
     float s3 = 0.f;
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
         const int col = 16 * cb + lr;
-        const float gc = sm.gs[col];
-        const float eq = exp2f(gc), ew = exp2f(gL - gc), rc = sm.rr[col];
+        const float eq = exp2f(sm.gs[col]);   // query column (step) col
+        const float gc = sm.gv[col];           // virtual row col
+        const float ex = exp2f(gc), ew = exp2f(gL - gc), rc = sm.rr[col];
 #pragma unroll
         for (int kk = 0; kk < KPW; ++kk) {
             const int kb = KPW * wave + kk;
             aQ[kk][cb] = aQ[kk][cb] * eq;
-            aX[kk][cb] = aX[kk][cb] * (-eq);
+            aX[kk][cb] = aX[kk][cb] * (-ex);
             aW[kk][cb] = aW[kk][cb] * ew;
             const Frag xk = E::load(&sm.X[col][16 * kb + 4 * grp]);
             float p = 0.f;
@@ -594,15 +647,16 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
     lds_barrier();  // the staging room is free for DP and DA
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb) {
-        const int t = 16 * tb + lr;
-        const float gt = sm.gs[t];
+        const int t = 16 * tb + lr;  // query step t (DP) or virtual row t (DA)
+        const float gt = sm.gs[t], gi = sm.gv[t];
+        const int si = sm.st[t];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int j = 16 * jbw + 4 * grp + r;
-            const float gj = sm.gs[j], rj = sm.rr[j];
-            const float dec = (j <= t) ? exp2f(gt - gj) : 0.f;
-            const float vp = aP[tb][r] * dec;
-            const float va = (DELTA && j < t) ? -aA[tb][r] * dec : 0.f;
+            const float gj = sm.gv[j], rj = sm.rr[j];
+            const int sj = sm.st[j];
+            const float vp = (sj <= t && t < Ct) ? aP[tb][r] * exp2f(gt - gj) : 0.f;
+            const float va = (DELTA && sj < si) ? -aA[tb][r] * exp2f(gi - gj) : 0.f;
             sm.u.m.DP[j][t] = f2bf(vp);
             sm.u.m.DPr[j][t] = f2bf(vp * rj);
             sm.u.m.DA[j][t] = f2bf(va);
@@ -628,24 +682,24 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
                 const Frag qj = colfrag(Qs, LDX, 16 * jb, 16 * kb);
 #pragma unroll
                 for (int cb = 0; cb < NB; ++cb) {
-                    if (jb <= cb) {
+                    // dQ^T (query block cb): rows of steps up to the block's last
+                    if (cb < NBQ && (16 * jb) / Wv <= 16 * cb + 15)
                         aQ[kk][cb] = E::mma16(xj, colfrag(DPr, LDC, 16 * jb, 16 * cb), aQ[kk][cb]);
-                        if constexpr (DELTA)
-                            aX[kk][cb] = E::mma16(xj, colfrag(DAr, LDC, 16 * jb, 16 * cb), aX[kk][cb]);
-                    }
-                    if (jb >= cb) {
+                    if (DELTA && jb <= cb)
+                        aX[kk][cb] = E::mma16(xj, colfrag(DAr, LDC, 16 * jb, 16 * cb), aX[kk][cb]);
+                    // dOmega^T (row block cb): queries of the steps from the block's first
+                    if (jb < NBQ && (16 * cb) / Wv <= 16 * jb + 15)
                         aW[kk][cb] = E::mma16(qj, E::load(DP + (size_t)(16 * cb + lr) * LDC + 16 * jb + 4 * grp),
                                               aW[kk][cb]);
-                        if constexpr (DELTA)
-                            aW[kk][cb] = E::mma16(xj, E::load(DA + (size_t)(16 * cb + lr) * LDC + 16 * jb + 4 * grp),
-                                                  aW[kk][cb]);
-                    }
+                    if (DELTA && jb >= cb)
+                        aW[kk][cb] = E::mma16(xj, E::load(DA + (size_t)(16 * cb + lr) * LDC + 16 * jb + 4 * grp),
+                                              aW[kk][cb]);
                 }
             }
         }
     }
 
-    // ---- row sums across the waves: x_j.dX_j, x_j.dOmega_j, q_t.dQ_t ----
+    // ---- row sums across the waves: x_i.dX_i, x_i.dOmega_i, q_t.dQ_t ----
     // lane (lr, grp) holds, for column block cb, row 16 cb + lr and entries
     // k = 16 kb + 4 grp + r of each of its k blocks
     auto row_sum = [&](float v) __attribute__((always_inline)) {
@@ -681,18 +735,36 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
     }
     lds_barrier();
     if (tid < CV) {
-        const int row = tid, t = t0 + row;
-        float sX = 0.f, sO = 0.f, sQ = 0.f;
+        float x = 0.f, o = 0.f, q = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            sX += sm.part[w][0][row];
-            sO += sm.part[w][1][row];
-            sQ += sm.part[w][2][row];
+            x += sm.part[w][0][tid];
+            o += sm.part[w][1][tid];
+            q += sm.part[w][2][tid];
         }
-        const float r = sm.rr[row], n = sm.nn[row];
-        sm.cn[row] = n > 0.f ? 2.f * r * sO / n : 0.f;
-        sm.dg[row] = sX - r * sO + sQ;
-        if (t < T_) a.deta[(size_t)bh * T_ + t] = n > 0.f ? sO / n : 0.f;
+        sm.sX[tid] = x;
+        sm.sO[tid] = o;
+        sm.sQ[tid] = q;
+    }
+    lds_barrier();
+    if (tid < CV) {
+        // per step s: x.dOmega of its rows gives deta and the normalizer's
+        // chain-rule factor; the decay gradient collects x.dX - omega.dOmega of
+        // its rows and q.dQ
+        const int s = tid;
+        float so = 0.f, sg = 0.f;
+        if (s < Ct) {
+            for (int w = 0; w < Wv; ++w) {
+                const int i = s * Wv + w;
+                so += sm.sO[i];
+                sg += sm.sX[i] - sm.rr[i] * sm.sO[i];
+            }
+            sg += sm.sQ[s];
+        }
+        const float dn = sm.den[s];
+        sm.cn[s] = (s < Ct && dn > 0.f) ? 2.f * sm.bst[s] * so / dn : 0.f;
+        sm.dg[s] = sg;
+        if (s < Ct && t0 + s < T_) a.deta[(size_t)bh * T_ + t0 + s] = dn > 0.f ? so / dn : 0.f;
     }
     lds_barrier();
 
@@ -700,7 +772,8 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
         const int row = 16 * cb + lr;
-        const float r = sm.rr[row], c = sm.cn[row];
+        const int si = sm.st[row];
+        const float r = sm.rr[row], c = si < Ct ? sm.cn[si] : 0.f;
 #pragma unroll
         for (int kk = 0; kk < KPW; ++kk) {
             const int kb = KPW * wave + kk;
@@ -710,12 +783,12 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
                 aX[kk][cb][e] = aX[kk][cb][e] + r * aW[kk][cb][e] - c * bf2f((bf)xk[e]);
         }
     }
-    // rows: key row tau = t - lag (its only use, window of one, is as x of step
-    // t; a padded step t >= T computes dx = 0, the gradient of the key no step
-    // reads), query row t
+    // rows: key row tau = t - lag (a window of one: its only use is as x of
+    // step t; a padded step t >= T computes dx = 0, the gradient of the key no
+    // step reads), query row t
     auto key_ok = [&](int row) __attribute__((always_inline)) {
         const int t = t0 + row, tau = t - lag;
-        return (t < T_ + lag) && tau < T_ && (tau >= 0 || (a.dk_prev && a.kp_raw));
+        return !WIN && (t < T_ + lag) && tau < T_ && (tau >= 0 || (a.dk_prev && a.kp_raw));
     };
     auto key_raw = [&](int row) __attribute__((always_inline)) {
         const int tau = t0 + row - lag;
@@ -732,7 +805,7 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) {
             const int row = 16 * cb + lr;
-            const bool kok = key_ok(row), qok = t0 + row < T_;
+            const bool kok = key_ok(row), qok = row < Ct && t0 + row < T_;
             float nk = 0.f, pk = 0.f, nq = 0.f, pq = 0.f;
 #pragma unroll
             for (int kk = 0; kk < KPW; ++kk) {
@@ -807,7 +880,17 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
         const int row = 16 * cb + lr, t = t0 + row, tau = t - lag;
-        if (key_ok(row)) {
+        if constexpr (WIN) {
+            // the key gradient of virtual row `row`, before the feature map: the
+            // gather sums a key's window rows and applies the map
+            bf* dst = static_cast<bf*>(a.ck_x) + (tix * CV + row) * D;
+#pragma unroll
+            for (int kk = 0; kk < KPW; ++kk) {
+                const int kb = KPW * wave + kk;
+                float g[4] = {aX[kk][cb][0], aX[kk][cb][1], aX[kk][cb][2], aX[kk][cb][3]};
+                *reinterpret_cast<Frag*>(dst + 16 * kb + 4 * grp) = pack4(g);
+            }
+        } else if (key_ok(row)) {
             bf* dst = tau >= 0 ? static_cast<bf*>(a.dk) + ((size_t)bh * T_ + tau) * D
                                : static_cast<bf*>(a.dk_prev) + ((size_t)bh * W + W + tau) * D;
             const bf* raw = key_raw(row);
@@ -821,7 +904,7 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
                 *reinterpret_cast<Frag*>(dst + 16 * kb + 4 * grp) = pack4(g);
             }
         }
-        if (t < T_) {
+        if (row < Ct && t < T_) {
             bf* dst = static_cast<bf*>(a.dq) + ((size_t)bh * T_ + t) * D;
             const bf* raw = static_cast<const bf*>(a.q_raw) + ((size_t)bh * T_ + t) * D;
 #pragma unroll
@@ -835,25 +918,28 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
             }
         }
     }
-    // keys no row of any tile reaches: k_{T-1} (prefix alignment, T a multiple
-    // of the tile) and the halo rows same-step pairs never read
-    if (t0 + CV == T_ && lag == 1) {
-        for (int c = tid; c < CPR; c += 256)
-            *reinterpret_cast<u32x4*>(static_cast<bf*>(a.dk) + ((size_t)bh * T_ + T_ - 1) * D + 8 * c) = zero_u4();
-    }
-    if (tile == 0 && a.dk_prev) {
-        for (int c = tid; c < W * CPR; c += 256) {
-            const int row = c / CPR;
-            if (lag == 0 || !a.kp_raw || row < W - 1)
-                *reinterpret_cast<u32x4*>(static_cast<bf*>(a.dk_prev) + ((size_t)bh * W + row) * D +
-                                          8 * (c % CPR)) = zero_u4();
+    if constexpr (!WIN) {
+        // keys no row of any tile reaches: k_{T-1} (prefix alignment, T a
+        // multiple of the tile) and the halo rows same-step pairs never read
+        if (t0 + CV == T_ && lag == 1) {
+            for (int c = tid; c < CPR; c += 256)
+                *reinterpret_cast<u32x4*>(static_cast<bf*>(a.dk) + ((size_t)bh * T_ + T_ - 1) * D + 8 * c) =
+                    zero_u4();
+        }
+        if (tile == 0 && a.dk_prev) {
+            for (int c = tid; c < W * CPR; c += 256) {
+                const int row = c / CPR;
+                if (lag == 0 || !a.kp_raw || row < W - 1)
+                    *reinterpret_cast<u32x4*>(static_cast<bf*>(a.dk_prev) + ((size_t)bh * W + row) * D +
+                                              8 * (c % CPR)) = zero_u4();
+            }
         }
     }
 
     // ---- decay gradients: dlog alpha_s = sum over the tile's steps s' >= s of dg ----
     if (wave == 0) {
-        float g = sm.dg[lane];
-        if (lane == CV - 1) {
+        float g = lane < Ct ? sm.dg[lane] : 0.f;
+        if (lane == Ct - 1) {
             float s3t = 0.f, sdt = 0.f;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
@@ -867,7 +953,101 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
             const float y = __shfl_down(g, off, 64);
             if (lane + off < 64) g += y;
         }
-        if (t0 + lane < T_) a.dalpha[(size_t)bh * T_ + t0 + lane] = g / sm.al[lane];
+        if (lane < Ct && t0 + lane < T_) a.dalpha[(size_t)bh * T_ + t0 + lane] = g / sm.al[lane];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 3 (windows above one): the gather.  Key tau serves the W rows
+// (step tau + lag + w, slot w) and value tau the rows (step tau + w, slot w),
+// w = 0..W-1, which can sit in two tiles: the per-virtual-row gradients are
+// summed here in fp32, the key sums go through the feature map's derivative,
+// and every key and value row (the halo rows included) is written once.
+// CPR lanes per row, 8 entries each.
+// ---------------------------------------------------------------------------
+template <int D, int CV>
+__global__ __launch_bounds__(256) void bwd_gather_kernel(BwdArgs a) {
+    constexpr int CPR = D / 8, RPB = 256 / CPR;
+    const int W = a.W, Ct = CV / W, T_ = a.T, lag = a.lag, ntiles = a.ntiles;
+    const int tid = threadIdx.x, part = tid % CPR;
+    const int nrows = T_ + W;  // rows tau = -W .. T-1
+    const int rid = blockIdx.x * RPB + tid / CPR;
+    const int bh = rid / nrows, tau = rid - bh * nrows - W;
+    if (bh >= a.BH) return;  // whole row groups: uniform within a DPP group
+    const int col = part * 8;
+    auto vrow = [&](int s, int w) {
+        return (((size_t)bh * ntiles + s / Ct) * CV + (s % Ct) * W + w) * D + col;
+    };
+    auto add8 = [&](float (&g)[8], const bf* p) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        const bf* e = reinterpret_cast<const bf*>(&v);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) g[u] += bf2f(e[u]);
+    };
+    auto put8 = [&](bf* dst, const float (&g)[8]) {
+        u32x4 o;
+        bf* e = reinterpret_cast<bf*>(&o);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) e[u] = f2bf(g[u]);
+        *reinterpret_cast<u32x4*>(dst + col) = o;
+    };
+    // keys: dk_tau = phi'(raw)^T sum_w dx(step tau + lag + w, slot w)
+    {
+        float g[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < W; ++w) {
+            const int s = tau + lag + w;
+            if (s >= 0 && s < T_) add8(g, static_cast<const bf*>(a.ck_x) + vrow(s, w));
+        }
+        const bf* raw = tau >= 0 ? static_cast<const bf*>(a.k_raw) + ((size_t)bh * T_ + tau) * D
+                                 : (a.kp_raw ? static_cast<const bf*>(a.kp_raw) + ((size_t)bh * W + W + tau) * D
+                                             : nullptr);
+        if (a.phi && raw) {
+            float kr[8];
+            const u32x4 v = *reinterpret_cast<const u32x4*>(raw + col);
+            const bf* e = reinterpret_cast<const bf*>(&v);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) kr[u] = bf2f(e[u]);
+            if (a.phi == 1) {
+                float n2 = 0.f, pk = 0.f;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    n2 += kr[u] * kr[u];
+                    pk += kr[u] * g[u];
+                }
+                if constexpr (CPR <= 16) {
+                    n2 = group_sum_dpp<CPR>(n2);
+                    pk = group_sum_dpp<CPR>(pk);
+                } else {
+                    n2 = group_sum<CPR>(n2);
+                    pk = group_sum<CPR>(pk);
+                }
+                const float inv = n2 > 0.f ? rsqrtf(n2) : 0.f, pd = pk * inv;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) g[u] = (g[u] - kr[u] * inv * pd) * inv;
+            } else {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float sg = 1.f / (1.f + __expf(-kr[u]));
+                    g[u] = g[u] * sg * (1.f + kr[u] * (1.f - sg));
+                }
+            }
+        }
+        if (!raw) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) g[u] = 0.f;  // no halo given: a constant zero key
+        }
+        if (tau >= 0) put8(static_cast<bf*>(a.dk) + ((size_t)bh * T_ + tau) * D, g);
+        else if (a.dk_prev) put8(static_cast<bf*>(a.dk_prev) + ((size_t)bh * W + W + tau) * D, g);
+    }
+    // values: dv_tau = sum_w dR(step tau + w, slot w), tau >= -(W - 1)
+    if (tau >= -(W - 1)) {
+        float g[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < W; ++w) {
+            const int s = tau + w;
+            if (s >= 0 && s < T_) add8(g, static_cast<const bf*>(a.ck_r) + vrow(s, w));
+        }
+        if (tau >= 0) put8(static_cast<bf*>(a.dv) + ((size_t)bh * T_ + tau) * D, g);
+        else if (a.dv_prev) put8(static_cast<bf*>(a.dv_prev) + ((size_t)bh * (W - 1) + W - 1 + tau) * D, g);
     }
 }
 
@@ -881,21 +1061,30 @@ __global__ void bwd_zero_kernel(bf* p, size_t n) {
 // ---------------------------------------------------------------------------
 bool chunk_bwd_supported(int dt, int D, int chunk, int norm, int window) {
     return dt == 1 && (D == 64 || D == 128) && chunk == 64 &&
-           (norm == kNormScalar || (norm == kNormWindow && window == 1));
+           (norm == kNormScalar || (norm == kNormWindow && window >= 1 && window <= 8));
 }
 
-template <int D, bool DELTA>
+template <int D, bool DELTA, bool WIN>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     constexpr int CV = 64;
     const int nvs = D / 64;
     const int bh8 = (a.BH + 7) / 8 * 8;
-    hipLaunchKernelGGL((bwd_scan_kernel<D, CV, DELTA>), dim3(bh8 * nvs), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((bwd_scan_kernel<D, CV, DELTA, WIN>), dim3(bh8 * nvs), dim3(512), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.T > 0) {
-        hipLaunchKernelGGL((bwd_grad_kernel<D, CV, DELTA>), dim3(a.BH * a.ntiles), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((bwd_grad_kernel<D, CV, DELTA, WIN>), dim3(a.BH * a.ntiles), dim3(256), 0, stream, a);
         e = hipGetLastError();
-    } else if (a.dk_prev) {
+        if (e != hipSuccess) return e;
+    }
+    if constexpr (WIN) {
+        // every key and value row, the halo rows included (also for T = 0)
+        constexpr int RPB = 256 / (D / 8);
+        const long long rows = (long long)a.BH * (a.T + a.W);
+        hipLaunchKernelGGL((bwd_gather_kernel<D, CV>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+                           stream, a);
+        e = hipGetLastError();
+    } else if (a.T == 0 && a.dk_prev) {
         const size_t n = (size_t)a.BH * a.W * D;
         hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
                            static_cast<bf*>(a.dk_prev), n);
@@ -904,10 +1093,17 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     return e;
 }
 
+template <int D>
+static hipError_t launch_bwd_dd(const BwdArgs& a, bool delta, bool win, hipStream_t stream) {
+    if (win) return delta ? launch_bwd_d<D, true, true>(a, stream) : launch_bwd_d<D, false, true>(a, stream);
+    return delta ? launch_bwd_d<D, true, false>(a, stream) : launch_bwd_d<D, false, false>(a, stream);
+}
+
 hipError_t launch_chunk_bwd(const BwdArgs& a, int D, int chunk, bool delta, hipStream_t stream) {
     if (chunk != 64) return hipErrorInvalidValue;
-    if (D == 64) return delta ? launch_bwd_d<64, true>(a, stream) : launch_bwd_d<64, false>(a, stream);
-    if (D == 128) return delta ? launch_bwd_d<128, true>(a, stream) : launch_bwd_d<128, false>(a, stream);
+    const bool win = a.W > 1;
+    if (D == 64) return launch_bwd_dd<64>(a, delta, win, stream);
+    if (D == 128) return launch_bwd_dd<128>(a, delta, win, stream);
     return hipErrorInvalidValue;
 }
 

@@ -128,6 +128,13 @@ struct BwdArgs {
     const void* ck_s;     // bf16 state at each tile start, [BH][ntiles][d][d]
     const void* ck_d;     // bf16 Delta of each tile, [BH][ntiles][d][CV]
     void* ck_ds;          // bf16 state gradient at each tile end, [BH][ntiles][d][d]
+    // windows above one: per-virtual-row gradients of the targets (ck_r) and
+    // keys (ck_x, before the feature map), bf16 [BH][ntiles][CV][d], summed
+    // into dv / dk by a gather (a key or value serves W rows, which can sit in
+    // two tiles)
+    void* ck_r;
+    void* ck_x;
+    void* dv_prev;        // [BH, W-1, d] or NULL (windows above one)
     int BH, T, ntiles, W, lag, phi;
     float eps;
 };
