@@ -199,8 +199,8 @@ int falcon_chunk_fwd_varlen(const void* q, const void* k, const void* v, const f
  *               chunk*dk*2 bytes), summed into dv / dk at the end
  * Outputs must not alias inputs or each other.
  *
- * Support matrix: dt bf16, dk = dv in {64, 128}, chunk 64, var F1, F1A,
- * F3 or F3A (window 1..8), with FALCON_SAME_STEP and the feature-map
+ * Support matrix: dt bf16, dk = dv in {64, 128}, chunk 64, every variant
+ * (window 1..8 for F3 / F3A), with FALCON_SAME_STEP and the feature-map
  * flags.  Other arguments that falcon_chunk_fwd accepts return
  * FALCON_ERR_UNSUPPORTED; errors otherwise as for falcon_chunk_fwd.
  * falcon_chunk_bwd_workspace returns 0 for unsupported arguments and T = 0.

@@ -229,8 +229,9 @@ def bwd(L, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(var=4), -3), (dict(dt=0), -3), (dict(chunk=32), -3), (dict(var=2), -3),
-    (dict(var=12), -3), (dict(var=3, window=9), -3), (dict(dk_=96, dv_=96), -3),
+    (dict(var=4), -3), (dict(dt=0), -3), (dict(chunk=32), -3), (dict(var=2, chunk=16), -3),
+    (dict(var=12, dt=0), -3), (dict(var=3, window=9), -3), (dict(dk_=96, dv_=96), -3),
+    (dict(var=2), -4), (dict(var=12 | 0x100), -4),
     (dict(var=3, window=2), -4), (dict(var=13, window=8), -4),
     (dict(B=0), -2), (dict(T=-1), -2), (dict(eps=-1.0), -2),
     (dict(q=None), -1), (dict(do=None), -1), (dict(dq=None), -1), (dict(dk=None), -1),
@@ -260,6 +261,6 @@ def test_bwd_workspace_sizes(L):
     nt = (T + 64 // W - 1) // (64 // W)
     want = al(fwd) + 2 * al(B * H * nt * d * d * 2) + 3 * al(B * H * nt * d * 64 * 2)
     assert L.falcon_chunk_bwd_workspace(B, H, T, d, d, 1, 3, W, 64) == want
-    assert L.falcon_chunk_bwd_workspace(2, 3, 1000, 128, 128, 1, 2, 1, 64) == 0   # unsupported
+    assert L.falcon_chunk_bwd_workspace(2, 3, 1000, 128, 128, 1, 2, 1, 32) == 0   # unsupported
     assert L.falcon_chunk_bwd_workspace(2, 3, 1000, 128, 128, 0, 1, 1, 32) == 0
     assert L.falcon_chunk_bwd_workspace(2, 3, 0, 128, 128, 1, 1, 1, 64) == 0

@@ -63,7 +63,13 @@ def check(got, ref, tol, keys=("dq", "dk", "dv", "dalpha", "deta", "dS0", "dk_pr
     cancels by a factor c the relative error is about c * 2^-9.  A slice of
     many steps is normalized by its largest gradient, which absorbs this; a
     slice of fewer than 16 steps has no scale of its own, so there the gate
-    gradients are normalized over all slices of the call."""
+    gradients are normalized over all slices of the call.
+
+    The halo rows are key (value) rows -W..-1 of the same sequence, so their
+    gradients are measured together with the sequence's own rows: the slice
+    of dk_prev is [k_prev; k] of its (batch, head).  (A halo of at most eight
+    rows has no scale of its own: for the per-column inner-product rule a key
+    row's gradient is sign(x) times one dot product that can cancel.)"""
     errs = {}
     for k in keys:
         r = ref.get(NAME[k])
@@ -71,9 +77,14 @@ def check(got, ref, tol, keys=("dq", "dk", "dv", "dalpha", "deta", "dS0", "dk_pr
             continue
         assert np.isfinite(got[k]).all(), k
         ax = AX[k]
+        g = got[k]
         if k in ("dalpha", "deta") and r.shape[2] < 16:
             ax = (0, 1, 2)
-        errs[k] = slice_rel_err(got[k], r, ax)
+        if k in ("dk_prev", "dv_prev") and got.get(k[:2]) is not None:
+            base = NAME[k[:2]]
+            g = np.concatenate([g, got[k[:2]]], axis=2)
+            r = np.concatenate([r, ref[base]], axis=2)
+        errs[k] = slice_rel_err(g, r, ax)
     bad = {k: e for k, e in errs.items() if e > tol}
     assert not bad, errs
     return errs
@@ -81,7 +92,7 @@ def check(got, ref, tol, keys=("dq", "dk", "dv", "dalpha", "deta", "dS0", "dk_pr
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("T", [150, 64, 1, 65, 128])
-@pytest.mark.parametrize("variant", ["F1", "F1A"])
+@pytest.mark.parametrize("variant", ["F1", "F1A", "F2", "F2A"])
 def test_bwd_grid(dev, variant, T, D):
     inp = I.make_chunk_inputs(2, 3, T, D, D, dtype="bf16", seed=1300 + T + D, halo=True,
                               S0_sd=0.3)
@@ -138,7 +149,7 @@ def test_bwd_without_optional_inputs(dev, variant):
 
 
 @pytest.mark.parametrize("T", [150, 64])
-@pytest.mark.parametrize("variant", ["F1", "F1A"])
+@pytest.mark.parametrize("variant", ["F1", "F1A", "F2", "F2A"])
 def test_bwd_same_step(dev, variant, T):
     inp = I.make_chunk_inputs(2, 2, T, 128, 128, dtype="bf16", seed=1330 + T, halo=True,
                               S0_sd=0.3)
@@ -149,7 +160,7 @@ def test_bwd_same_step(dev, variant, T):
 
 
 @pytest.mark.parametrize("phi", ["l2", "silu"])
-@pytest.mark.parametrize("variant", ["F1", "F1A"])
+@pytest.mark.parametrize("variant", ["F1", "F1A", "F2", "F2A"])
 def test_bwd_feature_maps(dev, variant, phi):
     inp = I.make_chunk_inputs(2, 2, 150, 128, 128, dtype="bf16", seed=1340, halo=True,
                               S0_sd=0.3)
@@ -232,6 +243,30 @@ def test_bwd_window_large_sampled(dev):
     ref = G.gradients("F3", *(d[n][None, None] for n in ("q", "k", "v", "alpha", "eta")),
                       inp.widen(d_o[sl])[None, None], np.asarray(dS[sl], np.float64)[None, None],
                       window=4)
+    got = {k: (None if v is None else to_np(v[sl])[None, None]) for k, v in g.items()}
+    check(got, ref, TOL["bf16"], keys=("dq", "dk", "dv", "dalpha", "deta", "dS0"))
+
+
+def test_bwd_falcon2_large_sampled(dev):
+    """Falcon-2 on the per-column workload's distributions (log-normal key
+    scales, a long high-retention span) at B=4, H=32, d=128, T=2048; one
+    (b, h) slice is checked."""
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    name = "falcon2_bf16_B4H32T8192d128"
+    w = dict(I.WORKLOADS[name])
+    inp = I.workload_inputs(name, T=2048, span=512)
+    d_o, dS = I.make_cotangents(4, 32, 2048, 128, 128, seed=w["seed"])
+    t = inp.to_torch(dev)
+    do_t = torch.from_numpy(d_o).view(torch.bfloat16).to(dev)
+    announce("chunk_bwd F2 B4 H32 T2048 d128")
+    g = fal.chunk_bwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], do_t, "F2",
+                      dS_final=torch.from_numpy(dS).to(dev))
+    torch.cuda.synchronize()
+    sl = (3, 17)
+    d = inp.f64(sl)
+    ref = G.gradients("F2", *(d[n][None, None] for n in ("q", "k", "v", "alpha", "eta")),
+                      inp.widen(d_o[sl])[None, None], np.asarray(dS[sl], np.float64)[None, None])
     got = {k: (None if v is None else to_np(v[sl])[None, None]) for k, v in g.items()}
     check(got, ref, TOL["bf16"], keys=("dq", "dk", "dv", "dalpha", "deta", "dS0"))
 

@@ -416,6 +416,7 @@ int falcon_chunk_bwd(const void* q, const void* k, const void* v, const float* a
     b.W = window;
     b.lag = lag;
     b.phi = phi;
+    b.norm = norm_of(base);
     b.eps = eps;
     hipError_t e = falcon::launch_chunk_bwd(b, dk_, chunk, is_delta(base), stream);
     return e == hipSuccess ? FALCON_OK : FALCON_ERR_HIP;

@@ -44,6 +44,20 @@ typedef uint16_t bf;
 
 __device__ __forceinline__ u32x4 zero_u4() { return u32x4{0u, 0u, 0u, 0u}; }
 
+// The per-column rule's write vector, u = eta x / (|x| l1 + eps) entry by
+// entry (l1 = ||x||_1 of the entry's row), for four bf16 entries whose rows
+// may differ (l1 and eta given per entry).
+__device__ __forceinline__ s16x4 col_write4(s16x4 x, f32x4 l1, f32x4 eta, float eps) {
+    f32x4 u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float v = bf2f((bf)x[r]);
+        const float den = fabsf(v) * l1[r] + eps;
+        u[r] = den > 0.f ? eta[r] * v / den : 0.f;
+    }
+    return EBf16::pack(u);
+}
+
 // s_waitcnt vmcnt(0), leaving the other counters alone
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -89,7 +103,7 @@ struct BScanSmem {
     alignas(16) char rec[2][R::kBytes];
 };
 
-template <int D, int CV, bool DELTA, bool WIN>
+template <int D, int CV, bool DELTA, bool WIN, bool COL>
 __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdArgs a) {
     using E = EBf16;
     using Frag = s16x4;
@@ -243,6 +257,16 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdArgs a) {
         const float* gam = reinterpret_cast<const float*>(recb + R::kScalBytes);
         const float* hrow = gam + CV;
         const float* gq = gam + 2 * CV;
+        // the per-column rule writes along u, not x: the A operand of
+        // U dS^T is formed from the key rows on the way
+        float l1r[NB], etr[NB];
+        if constexpr (COL) {
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) {
+                l1r[rb] = gam[3 * CV + 16 * rb + lr];
+                etr[rb] = gam[4 * CV + 16 * rb + lr];
+            }
+        }
 
         Frag dSB[KB];
 #pragma unroll
@@ -262,7 +286,14 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdArgs a) {
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb) {
                 const bf* xr = Xb + (size_t)(16 * rb + lr) * LDX + 32 * m + 4 * grp;
-                dd[rb] = E::mma32(E::load(xr), E::load(xr + 16), dSB[2 * m], dSB[2 * m + 1], dd[rb]);
+                Frag x0 = E::load(xr), x1 = E::load(xr + 16);
+                if constexpr (COL) {
+                    const f32x4 l = {l1r[rb], l1r[rb], l1r[rb], l1r[rb]};
+                    const f32x4 e = {etr[rb], etr[rb], etr[rb], etr[rb]};
+                    x0 = col_write4(x0, l, e, a.eps);
+                    x1 = col_write4(x1, l, e, a.eps);
+                }
+                dd[rb] = E::mma32(x0, x1, dSB[2 * m], dSB[2 * m + 1], dd[rb]);
             }
         }
 #pragma unroll
@@ -407,11 +438,13 @@ struct BGradSmem {
     alignas(16) float gv[CV];
     alignas(16) float rr[CV];
     float nrm[CV], sX[CV], sO[CV], sQ[CV];
+    alignas(16) float l1[CV];  // ||x_i||_1 (per-column rule)
+    float sC[CV];              // per-column rule: sum_k dOmega_k x_k |x_k| / den_k^2
     float rowk[2][CV], rowq[2][CV];  // feature map: 1/||raw||, phi . g
     float red[4][2];
 };
 
-template <int D, int CV, bool DELTA, bool WIN>
+template <int D, int CV, bool DELTA, bool WIN, bool COL>
 __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
     using E = EBf16;
     using Frag = s16x4;
@@ -466,14 +499,19 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
         // norms (4 lanes per row)
         const int row = tid >> 2, part = tid & 3;
         constexpr int EP = D / 4;
-        float n2 = 0.f;
+        float n2 = 0.f, n1 = 0.f;
 #pragma unroll
         for (int e = 0; e < EP; ++e) {
             const float x = bf2f(sm.X[row][part * EP + e]);
             n2 += x * x;
+            n1 += fabsf(x);
         }
         n2 = group_sum_dpp<4>(n2);
-        if (part == 0) sm.nrm[row] = n2;
+        n1 = group_sum_dpp<4>(n1);
+        if (part == 0) {
+            sm.nrm[row] = n2;
+            sm.l1[row] = n1;
+        }
     }
     lds_barrier();
     if (tid < CV) {
@@ -502,7 +540,9 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
         const int si = i < NVR ? i / Wv : (1 << 20);  // padding rows: after every step
         sm.st[i] = si;
         sm.gv[i] = sm.gs[i < NVR ? si : Ct - 1];
-        sm.rr[i] = i < NVR ? sm.bst[si] : 0.f;
+        // the per-column rule has no row scale: its write vectors are formed
+        // entry by entry (col_write4) where the products need them
+        sm.rr[i] = i < NVR ? (COL ? 1.f : sm.bst[si]) : 0.f;
     }
 
     auto colfrag = [&](const bf* m, int ld, int row0, int col0) __attribute__((always_inline)) {
@@ -631,7 +671,11 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
             aQ[kk][cb] = aQ[kk][cb] * eq;
             aX[kk][cb] = aX[kk][cb] * (-ex);
             aW[kk][cb] = aW[kk][cb] * ew;
-            const Frag xk = E::load(&sm.X[col][16 * kb + 4 * grp]);
+            Frag xk = E::load(&sm.X[col][16 * kb + 4 * grp]);
+            if constexpr (COL) {
+                const float l = sm.l1[col], e = sm.et[col];
+                xk = col_write4(xk, f32x4{l, l, l, l}, f32x4{e, e, e, e}, a.eps);
+            }
             float p = 0.f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) p += bf2f((bf)xk[r]) * aW[kk][cb][r];
@@ -680,13 +724,21 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
             for (int jb = 0; jb < NB; ++jb) {
                 const Frag xj = colfrag(Xs, LDX, 16 * jb, 16 * kb);
                 const Frag qj = colfrag(Qs, LDX, 16 * jb, 16 * kb);
+                // the write vectors omega_j: r_j x_j (the r_j sit in DPr, DAr), or
+                // the per-column rule's u_j, entries of rows 16 jb + 4 grp + r
+                Frag wj = xj;
+                if constexpr (COL) {
+                    const int j0 = 16 * jb + 4 * grp;
+                    wj = col_write4(xj, *reinterpret_cast<const f32x4*>(&sm.l1[j0]),
+                                    *reinterpret_cast<const f32x4*>(&sm.et[j0]), a.eps);
+                }
 #pragma unroll
                 for (int cb = 0; cb < NB; ++cb) {
                     // dQ^T (query block cb): rows of steps up to the block's last
                     if (cb < NBQ && (16 * jb) / Wv <= 16 * cb + 15)
-                        aQ[kk][cb] = E::mma16(xj, colfrag(DPr, LDC, 16 * jb, 16 * cb), aQ[kk][cb]);
+                        aQ[kk][cb] = E::mma16(wj, colfrag(DPr, LDC, 16 * jb, 16 * cb), aQ[kk][cb]);
                     if (DELTA && jb <= cb)
-                        aX[kk][cb] = E::mma16(xj, colfrag(DAr, LDC, 16 * jb, 16 * cb), aX[kk][cb]);
+                        aX[kk][cb] = E::mma16(wj, colfrag(DAr, LDC, 16 * jb, 16 * cb), aX[kk][cb]);
                     // dOmega^T (row block cb): queries of the steps from the block's first
                     if (jb < NBQ && (16 * cb) / Wv <= 16 * jb + 15)
                         aW[kk][cb] = E::mma16(qj, E::load(DP + (size_t)(16 * cb + lr) * LDC + 16 * jb + 4 * grp),
@@ -707,10 +759,13 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
         v += __shfl_xor(v, 32, 64);
         return v;
     };
+    // (per-column rule: x.dOmega is replaced by sum_k dOmega_k x_k / den_k,
+    // and sum_k dOmega_k x_k |x_k| / den_k^2 joins, den_k = |x_k| l1 + eps)
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
         const int row = 16 * cb + lr;
-        float pX = 0.f, pO = 0.f, pQ = 0.f;
+        const float l1r = COL ? sm.l1[row] : 0.f;
+        float pX = 0.f, pO = 0.f, pQ = 0.f, pC = 0.f;
 #pragma unroll
         for (int kk = 0; kk < KPW; ++kk) {
             const int kb = KPW * wave + kk;
@@ -720,31 +775,42 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
             for (int r = 0; r < 4; ++r) {
                 const float x = bf2f((bf)xk[r]);
                 pX += x * aX[kk][cb][r];
-                pO += x * aW[kk][cb][r];
                 pQ += bf2f((bf)qk[r]) * aQ[kk][cb][r];
+                if constexpr (COL) {
+                    const float den = fabsf(x) * l1r + a.eps;
+                    const float id = den > 0.f ? 1.f / den : 0.f;
+                    pO += aW[kk][cb][r] * x * id;
+                    pC += aW[kk][cb][r] * x * fabsf(x) * id * id;
+                } else {
+                    pO += x * aW[kk][cb][r];
+                }
             }
         }
         pX = row_sum(pX);
         pO = row_sum(pO);
         pQ = row_sum(pQ);
+        if constexpr (COL) pC = row_sum(pC);
         if (grp == 0) {
             sm.part[wave][0][row] = pX;
             sm.part[wave][1][row] = pO;
             sm.part[wave][2][row] = pQ;
+            if constexpr (COL) sm.part[wave][3][row] = pC;  // slot 3: free until the L2 map
         }
     }
     lds_barrier();
     if (tid < CV) {
-        float x = 0.f, o = 0.f, q = 0.f;
+        float x = 0.f, o = 0.f, q = 0.f, c = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             x += sm.part[w][0][tid];
             o += sm.part[w][1][tid];
             q += sm.part[w][2][tid];
+            if constexpr (COL) c += sm.part[w][3][tid];
         }
         sm.sX[tid] = x;
         sm.sO[tid] = o;
         sm.sQ[tid] = q;
+        if constexpr (COL) sm.sC[tid] = c;
     }
     lds_barrier();
     if (tid < CV) {
@@ -752,19 +818,28 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
         // chain-rule factor; the decay gradient collects x.dX - omega.dOmega of
         // its rows and q.dQ
         const int s = tid;
-        float so = 0.f, sg = 0.f;
-        if (s < Ct) {
-            for (int w = 0; w < Wv; ++w) {
-                const int i = s * Wv + w;
-                so += sm.sO[i];
-                sg += sm.sX[i] - sm.rr[i] * sm.sO[i];
+        if constexpr (COL) {
+            // u = eta x / den entrywise: deta = sum dOmega x / den,
+            // omega . dOmega = eta deta; cn carries eta sum dOmega x |x| / den^2
+            const float e = sm.et[s], de = sm.sO[s];
+            sm.dg[s] = s < Ct ? sm.sX[s] - e * de + sm.sQ[s] : 0.f;
+            sm.cn[s] = s < Ct ? e * sm.sC[s] : 0.f;
+            if (s < Ct && t0 + s < T_) a.deta[(size_t)bh * T_ + t0 + s] = de;
+        } else {
+            float so = 0.f, sg = 0.f;
+            if (s < Ct) {
+                for (int w = 0; w < Wv; ++w) {
+                    const int i = s * Wv + w;
+                    so += sm.sO[i];
+                    sg += sm.sX[i] - sm.rr[i] * sm.sO[i];
+                }
+                sg += sm.sQ[s];
             }
-            sg += sm.sQ[s];
+            const float dn = sm.den[s];
+            sm.cn[s] = (s < Ct && dn > 0.f) ? 2.f * sm.bst[s] * so / dn : 0.f;
+            sm.dg[s] = sg;
+            if (s < Ct && t0 + s < T_) a.deta[(size_t)bh * T_ + t0 + s] = dn > 0.f ? so / dn : 0.f;
         }
-        const float dn = sm.den[s];
-        sm.cn[s] = (s < Ct && dn > 0.f) ? 2.f * sm.bst[s] * so / dn : 0.f;
-        sm.dg[s] = sg;
-        if (s < Ct && t0 + s < T_) a.deta[(size_t)bh * T_ + t0 + s] = dn > 0.f ? so / dn : 0.f;
     }
     lds_barrier();
 
@@ -774,13 +849,24 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
         const int row = 16 * cb + lr;
         const int si = sm.st[row];
         const float r = sm.rr[row], c = si < Ct ? sm.cn[si] : 0.f;
+        const float l1r = COL ? sm.l1[row] : 0.f, er = COL ? sm.et[row] : 0.f;
 #pragma unroll
         for (int kk = 0; kk < KPW; ++kk) {
             const int kb = KPW * wave + kk;
             const Frag xk = E::load(&sm.X[row][16 * kb + 4 * grp]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                aX[kk][cb][e] = aX[kk][cb][e] + r * aW[kk][cb][e] - c * bf2f((bf)xk[e]);
+            for (int e = 0; e < 4; ++e) {
+                const float x = bf2f((bf)xk[e]);
+                if constexpr (COL) {
+                    // du_k/dx_k (l1 held) = eta eps / den^2; through l1: -sign(x) eta sum(...)
+                    const float den = fabsf(x) * l1r + a.eps;
+                    const float id = den > 0.f ? 1.f / den : 0.f;
+                    const float sg = x > 0.f ? 1.f : (x < 0.f ? -1.f : 0.f);
+                    aX[kk][cb][e] = aX[kk][cb][e] + aW[kk][cb][e] * er * a.eps * id * id - c * sg;
+                } else {
+                    aX[kk][cb][e] = aX[kk][cb][e] + r * aW[kk][cb][e] - c * x;
+                }
+            }
         }
     }
     // rows: key row tau = t - lag (a window of one: its only use is as x of
@@ -1061,19 +1147,20 @@ __global__ void bwd_zero_kernel(bf* p, size_t n) {
 // ---------------------------------------------------------------------------
 bool chunk_bwd_supported(int dt, int D, int chunk, int norm, int window) {
     return dt == 1 && (D == 64 || D == 128) && chunk == 64 &&
-           (norm == kNormScalar || (norm == kNormWindow && window >= 1 && window <= 8));
+           (norm == kNormScalar || norm == kNormColumn || (norm == kNormWindow && window >= 1 && window <= 8));
 }
 
-template <int D, bool DELTA, bool WIN>
+template <int D, bool DELTA, bool WIN, bool COL>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     constexpr int CV = 64;
     const int nvs = D / 64;
     const int bh8 = (a.BH + 7) / 8 * 8;
-    hipLaunchKernelGGL((bwd_scan_kernel<D, CV, DELTA, WIN>), dim3(bh8 * nvs), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((bwd_scan_kernel<D, CV, DELTA, WIN, COL>), dim3(bh8 * nvs), dim3(512), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.T > 0) {
-        hipLaunchKernelGGL((bwd_grad_kernel<D, CV, DELTA, WIN>), dim3(a.BH * a.ntiles), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((bwd_grad_kernel<D, CV, DELTA, WIN, COL>), dim3(a.BH * a.ntiles), dim3(256), 0,
+                           stream, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1094,16 +1181,19 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
 }
 
 template <int D>
-static hipError_t launch_bwd_dd(const BwdArgs& a, bool delta, bool win, hipStream_t stream) {
-    if (win) return delta ? launch_bwd_d<D, true, true>(a, stream) : launch_bwd_d<D, false, true>(a, stream);
-    return delta ? launch_bwd_d<D, true, false>(a, stream) : launch_bwd_d<D, false, false>(a, stream);
+static hipError_t launch_bwd_dd(const BwdArgs& a, bool delta, bool win, bool col, hipStream_t stream) {
+    if (win)
+        return delta ? launch_bwd_d<D, true, true, false>(a, stream) : launch_bwd_d<D, false, true, false>(a, stream);
+    if (col)
+        return delta ? launch_bwd_d<D, true, false, true>(a, stream) : launch_bwd_d<D, false, false, true>(a, stream);
+    return delta ? launch_bwd_d<D, true, false, false>(a, stream) : launch_bwd_d<D, false, false, false>(a, stream);
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs& a, int D, int chunk, bool delta, hipStream_t stream) {
     if (chunk != 64) return hipErrorInvalidValue;
-    const bool win = a.W > 1;
-    if (D == 64) return launch_bwd_dd<64>(a, delta, win, stream);
-    if (D == 128) return launch_bwd_dd<128>(a, delta, win, stream);
+    const bool win = a.W > 1, col = a.norm == kNormColumn;
+    if (D == 64) return launch_bwd_dd<64>(a, delta, win, col, stream);
+    if (D == 128) return launch_bwd_dd<128>(a, delta, win, col, stream);
     return hipErrorInvalidValue;
 }
 

@@ -136,6 +136,7 @@ struct BwdArgs {
     void* ck_x;
     void* dv_prev;        // [BH, W-1, d] or NULL (windows above one)
     int BH, T, ntiles, W, lag, phi;
+    int norm;             // NormKind
     float eps;
 };
 bool chunk_bwd_supported(int dt, int D, int chunk, int norm, int window);
