@@ -216,6 +216,28 @@ int falcon_chunk_bwd(const void* q, const void* k, const void* v, const float* a
                      size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Backward pass of falcon_chunk_fwd_varlen: the gradients for N packed
+ * sequences, in the layouts of that call (q, k, v, d_o and dq, dk, dv
+ * [H,total_T,d]; gates and their gradients [H,total_T]; S0, dS_final, dS0,
+ * the halos and their gradients per sequence).  Rows outside every sequence
+ * are not written.  The result equals one falcon_chunk_bwd call per
+ * sequence.  Support matrix and errors as for falcon_chunk_bwd; the
+ * workspace is falcon_chunk_bwd_varlen_workspace(...) bytes (0 for
+ * unsupported arguments).
+ */
+size_t falcon_chunk_bwd_varlen_workspace(int N, int H, int max_seqlen, int dk, int dv,
+                                         falcon_dtype dt, falcon_variant var, int window,
+                                         int chunk);
+int falcon_chunk_bwd_varlen(const void* q, const void* k, const void* v, const float* alpha,
+                            const float* eta, const float* S0, const void* k_prev,
+                            const void* v_prev, const void* d_o, const float* dS_final, void* dq,
+                            void* dk, void* dv, float* dalpha, float* deta, float* dS0,
+                            void* dk_prev, void* dv_prev, const int* cu_seqlens, int N, int H,
+                            int total_T, int max_seqlen, int dk_dim, int dv_dim, falcon_dtype dt,
+                            falcon_variant var, int window, int chunk, float eps, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/*
  * One decode step for N independent sequences x H heads (one token each):
  * x = k_cache (the previous key; with FALCON_SAME_STEP the new key k),
  * S' = alpha S, write as above, o = S q, then k_cache <- k.

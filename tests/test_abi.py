@@ -29,6 +29,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["falcon_chunk_fwd", "falcon_chunk_fwd_workspace",
                                            "falcon_chunk_bwd", "falcon_chunk_bwd_workspace",
+                                           "falcon_chunk_bwd_varlen",
+                                           "falcon_chunk_bwd_varlen_workspace",
                                            "falcon_chunk_fwd_varlen",
                                            "falcon_chunk_fwd_varlen_workspace",
                                            "falcon_decode_step", "falcon_decode_step_window",
@@ -264,3 +266,18 @@ def test_bwd_workspace_sizes(L):
     assert L.falcon_chunk_bwd_workspace(2, 3, 1000, 128, 128, 1, 2, 1, 32) == 0   # unsupported
     assert L.falcon_chunk_bwd_workspace(2, 3, 1000, 128, 128, 0, 1, 1, 32) == 0
     assert L.falcon_chunk_bwd_workspace(2, 3, 0, 128, 128, 1, 1, 1, 64) == 0
+
+
+def test_bwd_varlen_workspace(L):
+    """The packed forward's workspace, then the same checkpoint room as a
+    batched call of N sequences of max_seqlen steps."""
+    al = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    for var, W in ((1, 1), (13, 4), (2 | 0x200, 1)):
+        N, H, mx, d = 5, 3, 300, 128
+        fwd = L.falcon_chunk_fwd_varlen_workspace(N, H, mx, d, d, 1, var, W, 64)
+        nt = (mx + 64 // W - 1) // (64 // W)
+        want = al(fwd) + 2 * al(N * H * nt * d * d * 2) + al(N * H * nt * d * 64 * 2)
+        if W > 1:
+            want += 2 * al(N * H * nt * d * 64 * 2)
+        assert L.falcon_chunk_bwd_varlen_workspace(N, H, mx, d, d, 1, var, W, 64) == want
+    assert L.falcon_chunk_bwd_varlen_workspace(5, 3, 300, 128, 128, 0, 1, 1, 32) == 0

@@ -5,6 +5,7 @@ ABI of include/falcon.h); this package is its Python binding plus the seeded
 input generators used by tests and benchmarks.
 """
 from .binding import (BF16, F1, F1A, F2, F2A, F3, F3A, FP32, SAME_STEP, VARIANTS, FalconError,  # noqa: F401
-                      bwd_workspace_bytes, chunk_bwd, chunk_fwd, chunk_fwd_varlen, decode_step,
+                      bwd_varlen_workspace_bytes, bwd_workspace_bytes, chunk_bwd,
+                      chunk_bwd_varlen, chunk_fwd, chunk_fwd_varlen, decode_step,
                       decode_step_window, lib,
                       status_string, varlen_workspace_bytes, workspace_bytes)

@@ -59,6 +59,10 @@ def lib():
         L.falcon_chunk_bwd_workspace.argtypes = [ci] * 9
         L.falcon_chunk_bwd.restype = ci
         L.falcon_chunk_bwd.argtypes = [vp] * 18 + [ci] * 9 + [cf, vp, sz, vp]
+        L.falcon_chunk_bwd_varlen_workspace.restype = sz
+        L.falcon_chunk_bwd_varlen_workspace.argtypes = [ci] * 9
+        L.falcon_chunk_bwd_varlen.restype = ci
+        L.falcon_chunk_bwd_varlen.argtypes = [vp] * 19 + [ci] * 10 + [cf, vp, sz, vp]
         L.falcon_decode_step.restype = ci
         L.falcon_decode_step.argtypes = [vp] * 8 + [ci] * 7 + [cf, vp]
         L.falcon_decode_step_window.restype = ci
@@ -223,6 +227,74 @@ def chunk_bwd(q, k, v, alpha, eta, d_o, variant, *, dS_final=None, window=1, chu
                                 ws_n, _stream(stream))
     if st != 0:
         raise FalconError(st, "falcon_chunk_bwd")
+    return g
+
+
+def bwd_varlen_workspace_bytes(N, H, max_seqlen, dk, dv, dtype, variant, window=1, chunk=64,
+                               align="prefix", phi="identity") -> int:
+    return int(lib().falcon_chunk_bwd_varlen_workspace(N, H, max_seqlen, dk, dv, dtype,
+                                                       _variant(variant, align, phi), window,
+                                                       chunk))
+
+
+def chunk_bwd_varlen(q, k, v, alpha, eta, cu_seqlens, d_o, variant, *, max_seqlen=None,
+                     dS_final=None, window=1, chunk=64, eps=1e-6, S0=None, k_prev=None,
+                     v_prev=None, want_dS0=True, want_dk_prev=None, workspace=None, stream=None,
+                     align="prefix", phi="identity"):
+    """Gradients of chunk_fwd_varlen.  q, k, v, d_o [H,total_T,d]; alpha, eta
+    [H,total_T]; cu_seqlens int32 [N+1] on the device; S0, dS_final
+    [N,H,d,d]; k_prev [N,H,W,d], v_prev [N,H,W-1,d].  Returns a dict as
+    chunk_bwd does (dq, dk, dv, dalpha, deta in the packed layout; dS0 and the
+    halo gradients per sequence).  Rows outside every sequence are left as
+    allocated (torch.zeros here)."""
+    import torch
+    var = _variant(variant, align, phi)
+    H, Ttot, dk = k.shape
+    dv = v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    dev, dt = k.device, k.dtype
+    dtc = _dt(k)
+    if max_seqlen is None:
+        c = cu_seqlens.cpu()
+        max_seqlen = int((c[1:] - c[:-1]).max()) if N > 0 else 0
+    _check(q, "q", (H, Ttot, dk), dt, dev)
+    _check(v, "v", (H, Ttot, dv), dt, dev)
+    _check(d_o, "d_o", (H, Ttot, dv), dt, dev)
+    _check(alpha, "alpha", (H, Ttot), torch.float32, dev)
+    _check(eta, "eta", (H, Ttot), torch.float32, dev)
+    _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    _check(S0, "S0", (N, H, dv, dk), torch.float32, dev)
+    _check(dS_final, "dS_final", (N, H, dv, dk), torch.float32, dev)
+    _check(k_prev, "k_prev", (N, H, window, dk), dt, dev)
+    if window > 1:
+        _check(v_prev, "v_prev", (N, H, window - 1, dv), dt, dev)
+    else:
+        v_prev = None
+    g = dict(dq=torch.zeros_like(q), dk=torch.zeros_like(k), dv=torch.zeros_like(v),
+             dalpha=torch.zeros_like(alpha), deta=torch.zeros_like(eta),
+             dS0=torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev) if want_dS0 else None)
+    if want_dk_prev is None:
+        want_dk_prev = k_prev is not None
+    g["dk_prev"] = torch.empty((N, H, window, dk), dtype=dt, device=dev) if want_dk_prev else None
+    want_dv_prev = window > 1 and (v_prev is not None or want_dk_prev)
+    g["dv_prev"] = torch.empty((N, H, window - 1, dv), dtype=dt, device=dev) if want_dv_prev else None
+    ws_n = int(lib().falcon_chunk_bwd_varlen_workspace(N, H, max_seqlen, dk, dv, dtc, var, window,
+                                                       chunk))
+    if workspace is not None:
+        if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_n:
+            raise ValueError(f"workspace: need {ws_n} bytes on {dev}")
+        ws, ws_n = workspace, workspace.numel() * workspace.element_size()
+    else:
+        ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n > 0 else None
+    st = lib().falcon_chunk_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(S0),
+                                       _ptr(k_prev), _ptr(v_prev), _ptr(d_o), _ptr(dS_final),
+                                       _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+                                       _ptr(g["dalpha"]), _ptr(g["deta"]), _ptr(g["dS0"]),
+                                       _ptr(g["dk_prev"]), _ptr(g["dv_prev"]), _ptr(cu_seqlens),
+                                       N, H, Ttot, max_seqlen, dk, dv, dtc, var, window, chunk,
+                                       float(eps), _ptr(ws), ws_n, _stream(stream))
+    if st != 0:
+        raise FalconError(st, "falcon_chunk_bwd_varlen")
     return g
 
 

@@ -315,33 +315,37 @@ size_t falcon_chunk_bwd_workspace(int B, int H, int T, int dk, int dv, falcon_dt
     return align256(fwd) + 2 * align256(ck) + align256(cd) + cw;
 }
 
-int falcon_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
-                     const float* eta, const float* S0, const void* k_prev, const void* v_prev,
-                     const void* d_o, const float* dS_final, void* dq, void* dk, void* dv,
-                     float* dalpha, float* deta, float* dS0, void* dk_prev, void* dv_prev,
-                     int B, int H, int T, int dk_, int dv_, falcon_dtype dt, falcon_variant var,
-                     int window, int chunk, float eps, void* workspace, size_t workspace_bytes,
-                     hipStream_t stream) {
-    int st = check_chunk(q, k, v, alpha, eta, S0, k_prev, v_prev, d_o, dS_final, B, H, T, dk_,
-                         dv_, dt, var, window, chunk, eps);
-    if (st != FALCON_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// Checkpoint and gradient-row room of a backward call, after the forward's
+// workspace `fwd`: the state at every tile start and the state gradient at
+// every tile end (bf16, dk x dk), Delta (bf16, dk x chunk), and for a window
+// above one the per-row target and key gradients (bf16, chunk x dk each).
+size_t bwd_extra_bytes(int BH, int T, int dk, int chunk, int Wv) {
+    const size_t ntiles = (size_t)((T + chunk / Wv - 1) / (chunk / Wv));
+    const size_t ck = (size_t)BH * ntiles * dk * dk * 2;
+    const size_t cd = (size_t)BH * ntiles * dk * chunk * 2;
+    return 2 * align256(ck) + align256(cd) + (Wv > 1 ? 2 * align256(cd) : 0);
+}
+
+// The backward of falcon_chunk_fwd (cu == NULL: batched, BH = B * H rows of
+// T steps) or of falcon_chunk_fwd_varlen (cu: packed, T = max_seqlen),
+// arguments already checked.  `fwd` is the forward's workspace size, whose
+// layout (records, feature-map copies, packed schedule) the forward re-run
+// uses as it stands.
+int chunk_bwd_run(const void* q, const void* k, const void* v, const float* alpha,
+                  const float* eta, const float* S0, const void* k_prev, const void* v_prev,
+                  const void* d_o, const float* dS_final, void* dq, void* dk, void* dv,
+                  float* dalpha, float* deta, float* dS0, void* dk_prev, void* dv_prev,
+                  const int* cu, int BH, int H, int Ttot, int T, int dk_, int dt, int var,
+                  int window, int chunk, float eps, void* workspace, size_t fwd, size_t rec,
+                  size_t phi_rows, size_t order_off, hipStream_t stream) {
     int base = 0, lag = 1, phi = 0;
     split_variant(var, &base, &lag, &phi);
-    if (!falcon::chunk_bwd_supported((int)dt, dk_, chunk, norm_of(base), window))
-        return FALCON_ERR_UNSUPPORTED;
-    if (T > 0 && (!dq || !dk || !dv || !dalpha || !deta)) return FALCON_ERR_NULL;
-    if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dS0) ||
-        !aligned16(dk_prev) || !aligned16(dv_prev) || !aligned4(dalpha) || !aligned4(deta))
-        return FALCON_ERR_UNSUPPORTED;
-    const size_t need = falcon_chunk_bwd_workspace(B, H, T, dk_, dv_, dt, var, window, chunk);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FALCON_ERR_WORKSPACE;
-    if (T == 0 && dS0 == nullptr && dk_prev == nullptr && dv_prev == nullptr) return FALCON_OK;
-    const int BH = B * H;
     const int Wv = norm_of(base) == falcon::kNormWindow ? window : 1;
     const int ntiles = (T + chunk / Wv - 1) / (chunk / Wv);
-    const size_t fwd = falcon_chunk_fwd_workspace(B, H, T, dk_, dv_, dt, var, window, chunk);
-    const size_t rec = align256(falcon::chunk_workspace_bytes(BH, T, (int)dt, chunk, window,
-                                                              norm_of(base), is_delta(base)));
     char* ws = static_cast<char*>(workspace);
     const size_t ck = align256((size_t)BH * ntiles * dk_ * dk_ * 2);
     char* ck_s = ws + align256(fwd);
@@ -354,7 +358,7 @@ int falcon_chunk_bwd(const void* q, const void* k, const void* v, const float* a
     falcon::ChunkArgs a;
     a.phi = phi;
     a.kphi = a.qphi = a.kpphi = nullptr;
-    if (phi && T > 0) set_phi_buffers(a, workspace, (size_t)BH * T, BH, window, dk_, dt, rec);
+    if (phi && T > 0) set_phi_buffers(a, workspace, phi_rows, BH, window, dk_, dt, rec);
     a.q = q;
     a.k = k;
     a.v = v;
@@ -367,10 +371,10 @@ int falcon_chunk_bwd(const void* q, const void* k, const void* v, const float* a
     a.S_final = nullptr;
     a.BH = BH;
     a.T = T;
-    a.cu = nullptr;
+    a.cu = cu;
     a.H = H;
-    a.Ttot = T;
-    a.order_ws = nullptr;
+    a.Ttot = Ttot;
+    a.order_ws = (cu && T > 0) ? reinterpret_cast<int*>(ws + order_off) : nullptr;
     a.order = nullptr;
     a.toff = nullptr;
     a.jobs = nullptr;
@@ -381,7 +385,7 @@ int falcon_chunk_bwd(const void* q, const void* k, const void* v, const float* a
     a.ck_s = ck_s;
     a.ck_d = ck_d;
     if (T > 0) {
-        hipError_t e = falcon::launch_chunk(a, (int)dt, dk_, chunk, is_delta(base), workspace, stream);
+        hipError_t e = falcon::launch_chunk(a, dt, dk_, chunk, is_delta(base), workspace, stream);
         if (e != hipSuccess) return FALCON_ERR_HIP;
     }
 
@@ -418,8 +422,103 @@ int falcon_chunk_bwd(const void* q, const void* k, const void* v, const float* a
     b.phi = phi;
     b.norm = norm_of(base);
     b.eps = eps;
+    b.cu = cu;
+    b.H = H;
+    b.Ttot = Ttot;
     hipError_t e = falcon::launch_chunk_bwd(b, dk_, chunk, is_delta(base), stream);
     return e == hipSuccess ? FALCON_OK : FALCON_ERR_HIP;
+}
+
+int check_bwd_outputs(int dt, int dk_, int chunk, int var, int window, bool any_steps, void* dq,
+                      void* dk, void* dv, float* dalpha, float* deta, float* dS0, void* dk_prev,
+                      void* dv_prev) {
+    int base = 0, lag = 1, phi = 0;
+    split_variant(var, &base, &lag, &phi);
+    if (!falcon::chunk_bwd_supported(dt, dk_, chunk, norm_of(base), window)) return FALCON_ERR_UNSUPPORTED;
+    if (any_steps && (!dq || !dk || !dv || !dalpha || !deta)) return FALCON_ERR_NULL;
+    if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dS0) ||
+        !aligned16(dk_prev) || !aligned16(dv_prev) || !aligned4(dalpha) || !aligned4(deta))
+        return FALCON_ERR_UNSUPPORTED;
+    return FALCON_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int falcon_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
+                     const float* eta, const float* S0, const void* k_prev, const void* v_prev,
+                     const void* d_o, const float* dS_final, void* dq, void* dk, void* dv,
+                     float* dalpha, float* deta, float* dS0, void* dk_prev, void* dv_prev,
+                     int B, int H, int T, int dk_, int dv_, falcon_dtype dt, falcon_variant var,
+                     int window, int chunk, float eps, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+    int st = check_chunk(q, k, v, alpha, eta, S0, k_prev, v_prev, d_o, dS_final, B, H, T, dk_,
+                         dv_, dt, var, window, chunk, eps);
+    if (st != FALCON_OK) return st;
+    st = check_bwd_outputs((int)dt, dk_, chunk, var, window, T > 0, dq, dk, dv, dalpha, deta, dS0,
+                           dk_prev, dv_prev);
+    if (st != FALCON_OK) return st;
+    const size_t need = falcon_chunk_bwd_workspace(B, H, T, dk_, dv_, dt, var, window, chunk);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FALCON_ERR_WORKSPACE;
+    if (T == 0 && dS0 == nullptr && dk_prev == nullptr && dv_prev == nullptr) return FALCON_OK;
+    int base = 0, lag = 1, phi = 0;
+    split_variant(var, &base, &lag, &phi);
+    const int BH = B * H;
+    const size_t fwd = falcon_chunk_fwd_workspace(B, H, T, dk_, dv_, dt, var, window, chunk);
+    const size_t rec = align256(falcon::chunk_workspace_bytes(BH, T, (int)dt, chunk, window,
+                                                              norm_of(base), is_delta(base)));
+    return chunk_bwd_run(q, k, v, alpha, eta, S0, k_prev, v_prev, d_o, dS_final, dq, dk, dv, dalpha,
+                         deta, dS0, dk_prev, dv_prev, nullptr, BH, H, T, T, dk_, (int)dt, var, window,
+                         chunk, eps, workspace, fwd, rec, (size_t)BH * T, 0, stream);
+}
+
+size_t falcon_chunk_bwd_varlen_workspace(int N, int H, int max_seqlen, int dk, int dv,
+                                         falcon_dtype dt, falcon_variant var, int window,
+                                         int chunk) {
+    const size_t fwd = falcon_chunk_fwd_varlen_workspace(N, H, max_seqlen, dk, dv, dt, var, window, chunk);
+    if (fwd == 0) return 0;
+    int base = 0, lag = 1, phi = 0;
+    split_variant(var, &base, &lag, &phi);
+    if (!falcon::chunk_bwd_supported((int)dt, dk, chunk, norm_of(base), window)) return 0;
+    const int Wv = norm_of(base) == falcon::kNormWindow ? window : 1;
+    return align256(fwd) + bwd_extra_bytes(N * H, max_seqlen, dk, chunk, Wv);
+}
+
+int falcon_chunk_bwd_varlen(const void* q, const void* k, const void* v, const float* alpha,
+                            const float* eta, const float* S0, const void* k_prev,
+                            const void* v_prev, const void* d_o, const float* dS_final, void* dq,
+                            void* dk, void* dv, float* dalpha, float* deta, float* dS0,
+                            void* dk_prev, void* dv_prev, const int* cu_seqlens, int N, int H,
+                            int total_T, int max_seqlen, int dk_, int dv_, falcon_dtype dt,
+                            falcon_variant var, int window, int chunk, float eps, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    int st = check_chunk(q, k, v, alpha, eta, S0, k_prev, v_prev, d_o, dS_final, N, H, max_seqlen,
+                         dk_, dv_, dt, var, window, chunk, eps);
+    if (st != FALCON_OK) return st;
+    if (total_T < 0 || (long long)H * total_T > (1LL << 40) / (dk_ > 0 ? dk_ : 1))
+        return FALCON_ERR_SHAPE;
+    if (!cu_seqlens || !aligned4(cu_seqlens)) return cu_seqlens ? FALCON_ERR_UNSUPPORTED : FALCON_ERR_NULL;
+    const bool any = total_T > 0 && max_seqlen > 0;
+    if (any && (!q || !k || !v || !alpha || !eta || !d_o)) return FALCON_ERR_NULL;
+    st = check_bwd_outputs((int)dt, dk_, chunk, var, window, any, dq, dk, dv, dalpha, deta, dS0,
+                           dk_prev, dv_prev);
+    if (st != FALCON_OK) return st;
+    const size_t need = falcon_chunk_bwd_varlen_workspace(N, H, max_seqlen, dk_, dv_, dt, var,
+                                                          window, chunk);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FALCON_ERR_WORKSPACE;
+    if (!any && dS0 == nullptr && dk_prev == nullptr && dv_prev == nullptr) return FALCON_OK;
+    int base = 0, lag = 1, phi = 0;
+    split_variant(var, &base, &lag, &phi);
+    const int T = any ? max_seqlen : 0;
+    const size_t fwd = falcon_chunk_fwd_varlen_workspace(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk);
+    const size_t rec = align256(falcon::chunk_workspace_bytes(N * H, max_seqlen, (int)dt, chunk, window,
+                                                              norm_of(base), is_delta(base)));
+    return chunk_bwd_run(q, k, v, alpha, eta, S0, k_prev, v_prev, d_o, dS_final, dq, dk, dv, dalpha,
+                         deta, dS0, dk_prev, dv_prev, cu_seqlens, N * H, H, total_T, T, dk_, (int)dt,
+                         var, window, chunk, eps, workspace, fwd, rec, (size_t)N * H * max_seqlen,
+                         falcon_chunk_fwd_workspace(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk),
+                         stream);
 }
 
 const char* falcon_status_string(int status) {

@@ -44,6 +44,22 @@ typedef uint16_t bf;
 
 __device__ __forceinline__ u32x4 zero_u4() { return u32x4{0u, 0u, 0u, 0u}; }
 
+// Rows of sequence bh in the [rows, d] planes: [row0, row0 + T).  Batched
+// calls: row0 = bh * T.  Packed calls: the bounds come from cu, clamped to the
+// plane and to the longest sequence allowed (as the forward clamps them), so
+// offsets outside the contract cannot move any access out of the buffers.
+struct BSeq {
+    size_t row0;
+    int T;
+};
+__device__ __forceinline__ BSeq bwd_seq(const BwdArgs& a, int bh) {
+    if (!a.cu) return {(size_t)bh * a.T, a.T};
+    const int n = bh / a.H, h = bh - n * a.H;
+    const int s0 = min(max(a.cu[n], 0), a.Ttot);
+    const int s1 = min(min(max(a.cu[n + 1], s0), a.Ttot), s0 + a.T);
+    return {(size_t)h * a.Ttot + s0, s1 - s0};
+}
+
 // The per-column rule's write vector, u = eta x / (|x| l1 + eps) entry by
 // entry (l1 = ||x||_1 of the entry's row), for four bf16 entries whose rows
 // may differ (l1 and eta given per entry).
@@ -130,13 +146,14 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdArgs a) {
     const int v0 = vs * 64;
     // a tile holds Ct steps of Wv virtual rows (step s, window slot w) each
     const int W = a.W, Wv = WIN ? W : 1, Ct = CV / Wv, NVR = Ct * Wv, NBQ = (Ct + 15) / 16;
-    const int T_ = a.T, ntiles = a.ntiles, ntl = tiles_of(T_, Ct), lag = a.lag;
-    const bf* kg = static_cast<const bf*>(a.k) + (size_t)bh * T_ * D;
-    const bf* qg = static_cast<const bf*>(a.q) + (size_t)bh * T_ * D;
-    const bf* dog = static_cast<const bf*>(a.d_o) + (size_t)bh * T_ * D + v0;
+    const BSeq sq = bwd_seq(a, bh);
+    const int T_ = sq.T, ntiles = a.ntiles, ntl = tiles_of(T_, Ct), lag = a.lag;
+    const bf* kg = static_cast<const bf*>(a.k) + sq.row0 * D;
+    const bf* qg = static_cast<const bf*>(a.q) + sq.row0 * D;
+    const bf* dog = static_cast<const bf*>(a.d_o) + sq.row0 * D + v0;
     const bf* kp = a.k_prev ? static_cast<const bf*>(a.k_prev) + (size_t)bh * W * D : nullptr;
     const char* recg = static_cast<const char*>(a.rec) + (size_t)bh * ntiles * R::kBytes;
-    bf* dvg = static_cast<bf*>(a.dv) + (size_t)bh * T_ * D + v0;
+    bf* dvg = static_cast<bf*>(a.dv) + sq.row0 * D + v0;
     const int vcol = v0 + 16 * cw + lr;
 
     // ---- fill: one tile through registers ----
@@ -462,15 +479,18 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
     const int bh = blockIdx.x / ntiles, tile = blockIdx.x - bh * ntiles;
     // a tile holds Ct steps of Wv virtual rows (step s, window slot w) each
     const int W = a.W, Wv = WIN ? W : 1, Ct = CV / Wv, NVR = Ct * Wv, NBQ = (Ct + 15) / 16;
-    const int T_ = a.T, lag = a.lag;
+    if (bh >= a.BH) return;
+    const BSeq sq = bwd_seq(a, bh);
+    const int T_ = sq.T, lag = a.lag;
+    const size_t row0 = sq.row0;
     const int t0 = tile * Ct;
-    if (bh >= a.BH || t0 >= T_) return;
+    if (t0 >= T_) return;
     const size_t tix = (size_t)bh * ntiles + tile;
 
     // ---- keys, queries, gates ----
     {
-        const bf* kg = static_cast<const bf*>(a.k) + (size_t)bh * T_ * D;
-        const bf* qg = static_cast<const bf*>(a.q) + (size_t)bh * T_ * D;
+        const bf* kg = static_cast<const bf*>(a.k) + row0 * D;
+        const bf* qg = static_cast<const bf*>(a.q) + row0 * D;
         const bf* kp = a.k_prev ? static_cast<const bf*>(a.k_prev) + (size_t)bh * W * D : nullptr;
         constexpr int NXP = CV * CPR / 256;
         u32x4 px[NXP], pq[NXP];
@@ -484,8 +504,8 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
         }
         if (tid < CV) {
             const bool in = tid < Ct && t0 + tid < T_;
-            sm.al[tid] = in ? a.alpha[(size_t)bh * T_ + t0 + tid] : 1.f;
-            sm.et[tid] = in ? a.eta[(size_t)bh * T_ + t0 + tid] : 0.f;
+            sm.al[tid] = in ? a.alpha[row0 + t0 + tid] : 1.f;
+            sm.et[tid] = in ? a.eta[row0 + t0 + tid] : 0.f;
         }
 #pragma unroll
         for (int it = 0; it < NXP; ++it) {
@@ -566,8 +586,8 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
     const bf* ckd = static_cast<const bf*>(a.ck_d) + tix * D * CV;
     // dR rows: dv itself for a window of one, else the per-virtual-row copy
     const bf* dRg = WIN ? static_cast<const bf*>(a.ck_r) + tix * CV * D
-                        : static_cast<const bf*>(a.dv) + ((size_t)bh * T_ + t0) * D;
-    const bf* dog = static_cast<const bf*>(a.d_o) + ((size_t)bh * T_ + t0) * D;
+                        : static_cast<const bf*>(a.dv) + (row0 + t0) * D;
+    const bf* dog = static_cast<const bf*>(a.d_o) + (row0 + t0) * D;
     constexpr int NSP = 32 * CPR / 256, NDP = 32 * (CV / 8) / 256, NRP = CV * 4 / 256;
     // not unrolled: an unrolled loop would hoist every quarter's loads to the
     // top (the barriers order LDS only) and run out of registers
@@ -824,7 +844,7 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
             const float e = sm.et[s], de = sm.sO[s];
             sm.dg[s] = s < Ct ? sm.sX[s] - e * de + sm.sQ[s] : 0.f;
             sm.cn[s] = s < Ct ? e * sm.sC[s] : 0.f;
-            if (s < Ct && t0 + s < T_) a.deta[(size_t)bh * T_ + t0 + s] = de;
+            if (s < Ct && t0 + s < T_) a.deta[row0 + t0 + s] = de;
         } else {
             float so = 0.f, sg = 0.f;
             if (s < Ct) {
@@ -838,7 +858,7 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
             const float dn = sm.den[s];
             sm.cn[s] = (s < Ct && dn > 0.f) ? 2.f * sm.bst[s] * so / dn : 0.f;
             sm.dg[s] = sg;
-            if (s < Ct && t0 + s < T_) a.deta[(size_t)bh * T_ + t0 + s] = dn > 0.f ? so / dn : 0.f;
+            if (s < Ct && t0 + s < T_) a.deta[row0 + t0 + s] = dn > 0.f ? so / dn : 0.f;
         }
     }
     lds_barrier();
@@ -878,7 +898,7 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
     };
     auto key_raw = [&](int row) __attribute__((always_inline)) {
         const int tau = t0 + row - lag;
-        return tau >= 0 ? static_cast<const bf*>(a.k_raw) + ((size_t)bh * T_ + tau) * D
+        return tau >= 0 ? static_cast<const bf*>(a.k_raw) + (row0 + tau) * D
                         : static_cast<const bf*>(a.kp_raw) + ((size_t)bh * W + W + tau) * D;
     };
     auto raw4 = [&](const bf* raw, int kb, float (&kr)[4]) __attribute__((always_inline)) {
@@ -906,7 +926,7 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
                     }
                 }
                 if (qok) {
-                    raw4(static_cast<const bf*>(a.q_raw) + ((size_t)bh * T_ + t0 + row) * D, kb, kr);
+                    raw4(static_cast<const bf*>(a.q_raw) + (row0 + t0 + row) * D, kb, kr);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         nq += kr[e] * kr[e];
@@ -977,7 +997,7 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
                 *reinterpret_cast<Frag*>(dst + 16 * kb + 4 * grp) = pack4(g);
             }
         } else if (key_ok(row)) {
-            bf* dst = tau >= 0 ? static_cast<bf*>(a.dk) + ((size_t)bh * T_ + tau) * D
+            bf* dst = tau >= 0 ? static_cast<bf*>(a.dk) + (row0 + tau) * D
                                : static_cast<bf*>(a.dk_prev) + ((size_t)bh * W + W + tau) * D;
             const bf* raw = key_raw(row);
 #pragma unroll
@@ -991,8 +1011,8 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
             }
         }
         if (row < Ct && t < T_) {
-            bf* dst = static_cast<bf*>(a.dq) + ((size_t)bh * T_ + t) * D;
-            const bf* raw = static_cast<const bf*>(a.q_raw) + ((size_t)bh * T_ + t) * D;
+            bf* dst = static_cast<bf*>(a.dq) + (row0 + t) * D;
+            const bf* raw = static_cast<const bf*>(a.q_raw) + (row0 + t) * D;
 #pragma unroll
             for (int kk = 0; kk < KPW; ++kk) {
                 const int kb = KPW * wave + kk;
@@ -1009,8 +1029,7 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
         // multiple of the tile) and the halo rows same-step pairs never read
         if (t0 + CV == T_ && lag == 1) {
             for (int c = tid; c < CPR; c += 256)
-                *reinterpret_cast<u32x4*>(static_cast<bf*>(a.dk) + ((size_t)bh * T_ + T_ - 1) * D + 8 * c) =
-                    zero_u4();
+                *reinterpret_cast<u32x4*>(static_cast<bf*>(a.dk) + (row0 + T_ - 1) * D + 8 * c) = zero_u4();
         }
         if (tile == 0 && a.dk_prev) {
             for (int c = tid; c < W * CPR; c += 256) {
@@ -1039,7 +1058,7 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
             const float y = __shfl_down(g, off, 64);
             if (lane + off < 64) g += y;
         }
-        if (lane < Ct && t0 + lane < T_) a.dalpha[(size_t)bh * T_ + t0 + lane] = g / sm.al[lane];
+        if (lane < Ct && t0 + lane < T_) a.dalpha[row0 + t0 + lane] = g / sm.al[lane];
     }
 }
 
@@ -1054,12 +1073,16 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
 template <int D, int CV>
 __global__ __launch_bounds__(256) void bwd_gather_kernel(BwdArgs a) {
     constexpr int CPR = D / 8, RPB = 256 / CPR;
-    const int W = a.W, Ct = CV / W, T_ = a.T, lag = a.lag, ntiles = a.ntiles;
+    const int W = a.W, Ct = CV / W, lag = a.lag, ntiles = a.ntiles;
     const int tid = threadIdx.x, part = tid % CPR;
-    const int nrows = T_ + W;  // rows tau = -W .. T-1
+    const int nrows = a.T + W;  // rows tau = -W .. T-1 of the longest sequence allowed
     const int rid = blockIdx.x * RPB + tid / CPR;
     const int bh = rid / nrows, tau = rid - bh * nrows - W;
     if (bh >= a.BH) return;  // whole row groups: uniform within a DPP group
+    const BSeq sq = bwd_seq(a, bh);
+    const int T_ = sq.T;
+    const size_t row0 = sq.row0;
+    if (tau >= T_) return;
     const int col = part * 8;
     auto vrow = [&](int s, int w) {
         return (((size_t)bh * ntiles + s / Ct) * CV + (s % Ct) * W + w) * D + col;
@@ -1084,7 +1107,7 @@ __global__ __launch_bounds__(256) void bwd_gather_kernel(BwdArgs a) {
             const int s = tau + lag + w;
             if (s >= 0 && s < T_) add8(g, static_cast<const bf*>(a.ck_x) + vrow(s, w));
         }
-        const bf* raw = tau >= 0 ? static_cast<const bf*>(a.k_raw) + ((size_t)bh * T_ + tau) * D
+        const bf* raw = tau >= 0 ? static_cast<const bf*>(a.k_raw) + (row0 + tau) * D
                                  : (a.kp_raw ? static_cast<const bf*>(a.kp_raw) + ((size_t)bh * W + W + tau) * D
                                              : nullptr);
         if (a.phi && raw) {
@@ -1122,7 +1145,7 @@ __global__ __launch_bounds__(256) void bwd_gather_kernel(BwdArgs a) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) g[u] = 0.f;  // no halo given: a constant zero key
         }
-        if (tau >= 0) put8(static_cast<bf*>(a.dk) + ((size_t)bh * T_ + tau) * D, g);
+        if (tau >= 0) put8(static_cast<bf*>(a.dk) + (row0 + tau) * D, g);
         else if (a.dk_prev) put8(static_cast<bf*>(a.dk_prev) + ((size_t)bh * W + W + tau) * D, g);
     }
     // values: dv_tau = sum_w dR(step tau + w, slot w), tau >= -(W - 1)
@@ -1132,7 +1155,7 @@ __global__ __launch_bounds__(256) void bwd_gather_kernel(BwdArgs a) {
             const int s = tau + w;
             if (s >= 0 && s < T_) add8(g, static_cast<const bf*>(a.ck_r) + vrow(s, w));
         }
-        if (tau >= 0) put8(static_cast<bf*>(a.dv) + ((size_t)bh * T_ + tau) * D, g);
+        if (tau >= 0) put8(static_cast<bf*>(a.dv) + (row0 + tau) * D, g);
         else if (a.dv_prev) put8(static_cast<bf*>(a.dv_prev) + ((size_t)bh * (W - 1) + W - 1 + tau) * D, g);
     }
 }
@@ -1155,8 +1178,18 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     constexpr int CV = 64;
     const int nvs = D / 64;
     const int bh8 = (a.BH + 7) / 8 * 8;
+    hipError_t e;
+    if (!WIN && a.cu && a.dk_prev && a.T > 0) {
+        // packed: a sequence without steps has no tile whose workgroup would
+        // write its halo gradient, so the halo rows start at zero
+        const size_t n = (size_t)a.BH * a.W * D;
+        hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                           static_cast<bf*>(a.dk_prev), n);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((bwd_scan_kernel<D, CV, DELTA, WIN, COL>), dim3(bh8 * nvs), dim3(512), 0, stream, a);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.T > 0) {
         hipLaunchKernelGGL((bwd_grad_kernel<D, CV, DELTA, WIN, COL>), dim3(a.BH * a.ntiles), dim3(256), 0,

@@ -138,6 +138,12 @@ struct BwdArgs {
     int BH, T, ntiles, W, lag, phi;
     int norm;             // NormKind
     float eps;
+    // packed sequences (as ChunkArgs): rows cu[n] .. cu[n+1] of head h's
+    // plane are "batch row" n * H + h; T is the longest sequence allowed and
+    // ntiles its tile count.  NULL for the batched layout.
+    const int* cu;
+    int H;
+    int Ttot;
 };
 bool chunk_bwd_supported(int dt, int D, int chunk, int norm, int window);
 hipError_t launch_chunk_bwd(const BwdArgs& a, int D, int chunk, bool delta, hipStream_t stream);
