@@ -289,9 +289,10 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdArgs a) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) dSB[kb] = E::pack(dS[kb]);
         {
-            bf* cs = static_cast<bf*>(a.ck_ds) + (((size_t)bh * ntiles + it) * D + vcol) * D + 4 * grp;
+            // 16-column blocks ([kb][v][16]): one store writes 512 contiguous bytes
+            bf* cs = static_cast<bf*>(a.ck_ds) + ((size_t)bh * ntiles + it) * D * D + (size_t)vcol * 16 + 4 * grp;
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) *reinterpret_cast<Frag*>(cs + 16 * kb) = dSB[kb];
+            for (int kb = 0; kb < KB; ++kb) *reinterpret_cast<Frag*>(cs + (size_t)kb * D * 16) = dSB[kb];
         }
 
         // dDelta = diag(hrow) X dS^T + P^T dO   (rows j, columns v)
@@ -439,9 +440,14 @@ struct BGradSmem {
         bf DPr[CV][LDC];  // r_j DP^T
         bf DAr[CV][LDC];  // r_j DA^T
     };
+    struct Rows {
+        bf K[CV][LDX];    // key gradients (or per-row key gradients), staged for row stores
+        bf Qg[CV][LDX];   // query gradients
+    };
     union {
         Quarter q;
         Mats m;
+        Rows g;
     } u;
     float part[4][4][CV];  // per-wave partial row sums
     // per step s (tile-local): gates, log2(e) * g, the normalizer's
@@ -594,16 +600,20 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll 1
     for (int qv = 0; qv < NQ; ++qv) {
         u32x4 pS[NSP], pG[NSP], pD[NDP], pR[NRP], pO[NRP];
+        // the checkpoints are stored in 16-column blocks ([block][v][16]): piece c
+        // is half c % 2 of row c / 2 % 32 of the quarter in block c / 64, and
+        // consecutive pieces are consecutive 16 bytes
 #pragma unroll
         for (int it = 0; it < NSP; ++it) {
-            const int c = tid + 256 * it, v = c / CPR, col = (c % CPR) * 8;
-            pS[it] = *reinterpret_cast<const u32x4*>(cks + (size_t)(32 * qv + v) * D + col);
-            pG[it] = *reinterpret_cast<const u32x4*>(ckds + (size_t)(32 * qv + v) * D + col);
+            const int c = tid + 256 * it, kb = c >> 6, v = (c >> 1) & 31, h8 = (c & 1) * 8;
+            const size_t off = ((size_t)kb * D + 32 * qv + v) * 16 + h8;
+            pS[it] = *reinterpret_cast<const u32x4*>(cks + off);
+            pG[it] = *reinterpret_cast<const u32x4*>(ckds + off);
         }
 #pragma unroll
         for (int it = 0; it < NDP; ++it) {
-            const int c = tid + 256 * it, v = c / (CV / 8), col = (c % (CV / 8)) * 8;
-            pD[it] = *reinterpret_cast<const u32x4*>(ckd + (size_t)(32 * qv + v) * CV + col);
+            const int c = tid + 256 * it, cb = c >> 6, v = (c >> 1) & 31, h8 = (c & 1) * 8;
+            pD[it] = *reinterpret_cast<const u32x4*>(ckd + ((size_t)cb * D + 32 * qv + v) * 16 + h8);
         }
 #pragma unroll
         for (int it = 0; it < NRP; ++it) {
@@ -616,7 +626,7 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
         lds_barrier();  // the previous quarter's operands are consumed
 #pragma unroll
         for (int it = 0; it < NSP; ++it) {
-            const int c = tid + 256 * it, v = c / CPR, col = (c % CPR) * 8;
+            const int c = tid + 256 * it, v = (c >> 1) & 31, col = (c >> 6) * 16 + (c & 1) * 8;
             *reinterpret_cast<u32x4*>(&sm.u.q.S0q[v][col]) = pS[it];
             *reinterpret_cast<u32x4*>(&sm.u.q.dSq[v][col]) = pG[it];
             const bf* se = reinterpret_cast<const bf*>(&pS[it]);
@@ -626,7 +636,7 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int it = 0; it < NDP; ++it) {
-            const int c = tid + 256 * it, v = c / (CV / 8), col = (c % (CV / 8)) * 8;
+            const int c = tid + 256 * it, v = (c >> 1) & 31, col = (c >> 6) * 16 + (c & 1) * 8;
             *reinterpret_cast<u32x4*>(&sm.u.q.Dq[v][col]) = pD[it];
         }
 #pragma unroll
@@ -983,46 +993,56 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
         f.w = (short)f2bf(g[3]);
         return f;
     };
+    // the gradient rows go to LDS (the staging room is free since the second
+    // products), then leave as 16-byte row stores
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
-        const int row = 16 * cb + lr, t = t0 + row, tau = t - lag;
-        if constexpr (WIN) {
-            // the key gradient of virtual row `row`, before the feature map: the
-            // gather sums a key's window rows and applies the map
-            bf* dst = static_cast<bf*>(a.ck_x) + (tix * CV + row) * D;
+        const int row = 16 * cb + lr, t = t0 + row;
+        if (WIN || key_ok(row)) {
+            // the key gradient of the row; with a window before the feature map
+            // (the gather sums a key's window rows and applies the map)
+            const bf* raw = WIN ? nullptr : key_raw(row);
 #pragma unroll
             for (int kk = 0; kk < KPW; ++kk) {
                 const int kb = KPW * wave + kk;
                 float g[4] = {aX[kk][cb][0], aX[kk][cb][1], aX[kk][cb][2], aX[kk][cb][3]};
-                *reinterpret_cast<Frag*>(dst + 16 * kb + 4 * grp) = pack4(g);
-            }
-        } else if (key_ok(row)) {
-            bf* dst = tau >= 0 ? static_cast<bf*>(a.dk) + (row0 + tau) * D
-                               : static_cast<bf*>(a.dk_prev) + ((size_t)bh * W + W + tau) * D;
-            const bf* raw = key_raw(row);
-#pragma unroll
-            for (int kk = 0; kk < KPW; ++kk) {
-                const int kb = KPW * wave + kk;
-                float g[4] = {aX[kk][cb][0], aX[kk][cb][1], aX[kk][cb][2], aX[kk][cb][3]};
-                float kr[4] = {0.f, 0.f, 0.f, 0.f};
-                if (a.phi) raw4(raw, kb, kr);
-                phi_back(g, kr, a.phi == 1 ? sm.rowk[0][row] : 0.f, a.phi == 1 ? sm.rowk[1][row] : 0.f);
-                *reinterpret_cast<Frag*>(dst + 16 * kb + 4 * grp) = pack4(g);
+                if (!WIN && a.phi) {
+                    float kr[4];
+                    raw4(raw, kb, kr);
+                    phi_back(g, kr, a.phi == 1 ? sm.rowk[0][row] : 0.f, a.phi == 1 ? sm.rowk[1][row] : 0.f);
+                }
+                *reinterpret_cast<Frag*>(&sm.u.g.K[row][16 * kb + 4 * grp]) = pack4(g);
             }
         }
         if (row < Ct && t < T_) {
-            bf* dst = static_cast<bf*>(a.dq) + (row0 + t) * D;
             const bf* raw = static_cast<const bf*>(a.q_raw) + (row0 + t) * D;
 #pragma unroll
             for (int kk = 0; kk < KPW; ++kk) {
                 const int kb = KPW * wave + kk;
                 float g[4] = {aQ[kk][cb][0], aQ[kk][cb][1], aQ[kk][cb][2], aQ[kk][cb][3]};
-                float kr[4] = {0.f, 0.f, 0.f, 0.f};
-                if (a.phi) raw4(raw, kb, kr);
-                phi_back(g, kr, a.phi == 1 ? sm.rowq[0][row] : 0.f, a.phi == 1 ? sm.rowq[1][row] : 0.f);
-                *reinterpret_cast<Frag*>(dst + 16 * kb + 4 * grp) = pack4(g);
+                if (a.phi) {
+                    float kr[4];
+                    raw4(raw, kb, kr);
+                    phi_back(g, kr, a.phi == 1 ? sm.rowq[0][row] : 0.f, a.phi == 1 ? sm.rowq[1][row] : 0.f);
+                }
+                *reinterpret_cast<Frag*>(&sm.u.g.Qg[row][16 * kb + 4 * grp]) = pack4(g);
             }
         }
+    }
+    lds_barrier();
+    for (int c = tid; c < CV * CPR; c += 256) {
+        const int row = c / CPR, col = (c % CPR) * 8, t = t0 + row, tau = t - lag;
+        if constexpr (WIN) {
+            *reinterpret_cast<u32x4*>(static_cast<bf*>(a.ck_x) + (tix * CV + row) * D + col) =
+                *reinterpret_cast<const u32x4*>(&sm.u.g.K[row][col]);
+        } else if (key_ok(row)) {
+            bf* dst = tau >= 0 ? static_cast<bf*>(a.dk) + (row0 + tau) * D
+                               : static_cast<bf*>(a.dk_prev) + ((size_t)bh * W + W + tau) * D;
+            *reinterpret_cast<u32x4*>(dst + col) = *reinterpret_cast<const u32x4*>(&sm.u.g.K[row][col]);
+        }
+        if (row < Ct && t < T_)
+            *reinterpret_cast<u32x4*>(static_cast<bf*>(a.dq) + (row0 + t) * D + col) =
+                *reinterpret_cast<const u32x4*>(&sm.u.g.Qg[row][col]);
     }
     if constexpr (!WIN) {
         // keys no row of any tile reaches: k_{T-1} (prefix alignment, T a

@@ -1229,15 +1229,17 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) db[cb] = sm.DB[pb][cw][cb][lane];
         if (a.ck_s) {
-            // checkpoints for the backward pass: lane holds S[v][16 kb + 4 grp + r]
-            // and Delta[16 cb + 4 grp + r][v] of value row v = vcol
+            // checkpoints for the backward pass, in 16-column blocks ([block][v][16]):
+            // lane holds S[v][16 kb + 4 grp + r] and Delta[16 cb + 4 grp + r][v] of
+            // value row v = vcol, so each store instruction writes 512
+            // contiguous bytes
             const size_t tb = (size_t)bh * ntiles + p;
-            T* cs = static_cast<T*>(a.ck_s) + (tb * D + vcol) * D + 4 * grp;
-            T* cd = static_cast<T*>(a.ck_d) + (tb * D + vcol) * CV + 4 * grp;
+            T* cs = static_cast<T*>(a.ck_s) + tb * D * D + (size_t)vcol * 16 + 4 * grp;
+            T* cd = static_cast<T*>(a.ck_d) + tb * D * CV + (size_t)vcol * 16 + 4 * grp;
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) *reinterpret_cast<Frag*>(cs + 16 * kb) = sb[kb];
+            for (int kb = 0; kb < KB; ++kb) *reinterpret_cast<Frag*>(cs + (size_t)kb * D * 16) = sb[kb];
 #pragma unroll
-            for (int cb = 0; cb < NB; ++cb) *reinterpret_cast<Frag*>(cd + 16 * cb) = db[cb];
+            for (int cb = 0; cb < NB; ++cb) *reinterpret_cast<Frag*>(cd + (size_t)cb * D * 16) = db[cb];
         }
         static_for<NB>([&](auto tbc) __attribute__((always_inline)) {
             constexpr int tb = decltype(tbc)::value;

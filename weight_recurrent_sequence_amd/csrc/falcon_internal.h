@@ -56,12 +56,12 @@ struct ChunkArgs {
     void* kphi;
     void* qphi;
     void* kpphi;
-    // Checkpoints for the backward pass (bf16 state pass, batched layout):
-    // when ck_s is set, the state pass also writes, for every (row, tile), the
-    // state at the tile start rounded to bf16 ([d_v][d_k], row-major) to
-    // ck_s and the tile's Delta (the residuals at the decayed state; the
-    // targets for the inner-product family) as [d_v][CV] to ck_d.  o may then
-    // be NULL (not written).
+    // Checkpoints for the backward pass (bf16 state pass): when ck_s is set,
+    // the state pass also writes, for every (row, tile), the state at the tile
+    // start rounded to bf16 (d_v x d_k) to ck_s and the tile's Delta (the
+    // residuals at the decayed state; the targets for the inner-product
+    // family, d_v x CV) to ck_d, both in 16-column blocks: entry (v, c) at
+    // ((c / 16) * d_v + v) * 16 + c % 16.  o may then be NULL (not written).
     void* ck_s = nullptr;
     void* ck_d = nullptr;
 };
@@ -125,9 +125,10 @@ struct BwdArgs {
     float* dS0;           // or NULL
     void* dk_prev;        // or NULL
     const void* rec;      // records of the intra-chunk kernel
-    const void* ck_s;     // bf16 state at each tile start, [BH][ntiles][d][d]
-    const void* ck_d;     // bf16 Delta of each tile, [BH][ntiles][d][CV]
-    void* ck_ds;          // bf16 state gradient at each tile end, [BH][ntiles][d][d]
+    // checkpoints, per (row, tile), in 16-column blocks ([c/16][v][16]):
+    const void* ck_s;     // bf16 state at each tile start (d x d)
+    const void* ck_d;     // bf16 Delta of each tile (d x CV)
+    void* ck_ds;          // bf16 state gradient at each tile end (d x d)
     // windows above one: per-virtual-row gradients of the targets (ck_r) and
     // keys (ck_x, before the feature map), bf16 [BH][ntiles][CV][d], summed
     // into dv / dk by a gather (a key or value serves W rows, which can sit in
