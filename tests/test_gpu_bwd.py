@@ -293,3 +293,50 @@ def test_bwd_full_size_sampled(dev, variant):
                           inp.widen(d_o[sl])[None, None], np.asarray(dS[sl], np.float64)[None, None])
         got = {k: (None if v is None else to_np(v[sl])[None, None]) for k, v in g.items()}
         check(got, ref, TOL["bf16"], keys=("dq", "dk", "dv", "dalpha", "deta", "dS0"))
+
+
+@pytest.mark.parametrize("alpha", [0.5, 1 - 1e-4])
+@pytest.mark.parametrize("variant", ["F1", "F3"])
+def test_bwd_renormalization_stress(dev, variant, alpha):
+    """Constant decays over 20 tiles: strong (0.5, products down to 2^-1280
+    across the sequence) and weak (1 - 1e-4).  Every factor the kernels form
+    is exp(later - earlier) of a tile-local log sum, so the gradients stay
+    finite and equal the oracle's."""
+    W = 2 if variant == "F3" else 1
+    T = 1280 // W
+    inp = I.make_chunk_inputs(1, 2, T, 64, 64, dtype="bf16", seed=1600, window=W, halo=True,
+                              S0_sd=0.3)
+    inp.alpha[:] = np.float32(alpha)
+    d_o, dS = I.make_cotangents(1, 2, T, 64, 64, seed=1600)
+    got, ref = run_bwd(dev, inp, variant, d_o=d_o, dS=dS, W=W)
+    check(got, ref, TOL["bf16"])
+
+
+def test_bwd_decay_only(dev):
+    """eta = 0: nothing is written, so the targets get no gradient and the
+    state gradient only decays back to S0."""
+    inp = I.make_chunk_inputs(1, 2, 100, 64, 64, dtype="bf16", seed=1610, halo=True, S0_sd=0.3)
+    inp.eta[:] = 0
+    d_o, dS = I.make_cotangents(1, 2, 100, 64, 64, seed=1610)
+    got, ref = run_bwd(dev, inp, "F1", d_o=d_o, dS=dS)
+    assert not np.any(got["dv"])
+    check(got, ref, TOL["bf16"], keys=("dq", "dalpha", "deta", "dS0"))
+
+
+def test_bwd_eps_zero(dev):
+    """eps = 0 (the exact Kaczmarz step) on keys without zero rows."""
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    inp = I.make_chunk_inputs(1, 2, 90, 64, 64, dtype="bf16", seed=1620, halo=True, S0_sd=0.3)
+    d_o, dS = I.make_cotangents(1, 2, 90, 64, 64, seed=1620)
+    t = inp.to_torch(dev)
+    announce("chunk_bwd F1 eps=0")
+    g = fal.chunk_bwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"],
+                      torch.from_numpy(d_o).view(torch.bfloat16).to(dev), "F1", eps=0.0,
+                      dS_final=torch.from_numpy(dS).to(dev), S0=t["S0"], k_prev=t["k_prev"])
+    torch.cuda.synchronize()
+    d = inp.f64()
+    ref = G.gradients("F1", d["q"], d["k"], d["v"], d["alpha"], d["eta"], inp.widen(d_o),
+                      dS.astype(np.float64), eps=0.0, S0=d["S0"], k_prev=d["k_prev"])
+    got = {k: (None if v is None else to_np(v)) for k, v in g.items()}
+    check(got, ref, TOL["bf16"])
