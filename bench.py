@@ -10,8 +10,10 @@ blocked forward substitution, outputs, state update).  `value` is tokens
 (B*T) per second.  The same line reports Falcon-1A on the same batch,
 Falcon-1 with same-step pairs (k_t, v_t), Falcon-1 with L2-normalized keys
 and queries, Falcon-1 over 16 packed sequences
-of mixed lengths with the same token count, the decode step (256 sequences x
-32 heads, d=128, 1024 consecutive steps) and the
+of mixed lengths with the same token count, the backward of Falcon-1 and
+Falcon-1A on the same batch, Falcon-2 / Falcon-2A at B=4, H=32, T=8192 and
+Falcon-3 / Falcon-3A (window 4) at B=2, H=16, T=32768, the decode step (256
+sequences x 32 heads, d=128, 1024 consecutive steps) and the
 Falcon-3 decode step at the same shape with a window of four, each with its
 roofline, and the fp64 CPU oracle timed on this host over a bounded sample of
 the Falcon-1 workload.
@@ -280,6 +282,39 @@ def main():
     nbytes_b = bwd_bytes(B, H, T, D)
     del ws_b, d_o, dS_fin
 
+    # The other full-size chunk-forward workloads: Falcon-2 (per-column
+    # normalized step, lognormal key scales, long near-one decay spans) and
+    # Falcon-3 / Falcon-3A with a window of four prefix-aligned pairs.  A
+    # window of W turns each step into W virtual rows, so the chunk's 64 rows
+    # hold 64 / W steps and the contraction work scales with T * W.
+    extra = {}
+    for wname, variants in (("falcon2_bf16_B4H32T8192d128", ("F2", "F2A")),
+                            ("falcon3_w4_bf16_B2H16T32768d128", ("F3", "F3A"))):
+        wx = I.WORKLOADS[wname]
+        Bx, Hx, Tx, Dx, Wx = wx["B"], wx["H"], wx["T"], wx["d"], wx.get("window", 1)
+        tx = I.workload_inputs(wname).to_torch(dev)
+        ox = torch.empty_like(tx["v"])
+        Sx = torch.empty((Bx, Hx, Dx, Dx), dtype=torch.float32, device=dev)
+        wsx = torch.empty(max(fal.workspace_bytes(Bx, Hx, Tx, Dx, Dx, fal.BF16, v, Wx, C)
+                              for v in variants), dtype=torch.uint8, device=dev)
+        nb = chunk_bytes(Bx, Hx, Tx, Dx)
+        for v in variants:
+            def step_x(v=v):
+                fal.chunk_fwd(tx["q"], tx["k"], tx["v"], tx["alpha"], tx["eta"], v, chunk=C,
+                              window=Wx, o=ox, S_final=Sx, workspace=wsx)
+
+            print(f"[bench] {v} {wname}", file=sys.stderr, flush=True)
+            msx, _ = timed(step_x, args.steps, args.warmup)
+            fl = chunk_flops(Bx, Hx, Tx * Wx, Dx, C, delta=not v.endswith("A"))
+            gx = nb / (msx / 1e3) / 1e9
+            tfx = fl / (msx / 1e3) / 1e12
+            extra[v.lower().replace("f", "falcon")] = {
+                "workload": wname, "tokens_per_s": Bx * Tx / (msx / 1e3), "ms_per_step": msx,
+                "hbm_gbs": gx, "hbm_frac": gx / HBM_PEAK_GBS, "algorithmic_bytes_per_call": nb,
+                "mfma_tflops": tfx, "mfma_frac_bf16": tfx / BF16_PEAK_TFLOPS,
+                "algorithmic_flops_per_call": fl}
+        del tx, ox, Sx, wsx
+
     line = {
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -318,6 +353,7 @@ def main():
                            "batch": f"{len(lengths)} packed sequences, lengths {min(lengths)}.."
                                     f"{maxT}, {B * T} tokens per head, H={H}"},
     }
+    line.update(extra)
 
     if not args.no_decode:
         wd = I.WORKLOADS["decode_falcon1_N256H32d128_1024steps"]

@@ -961,7 +961,9 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
     u32x4 pxh[NXL], pyh[NYL];  // halo rows of the first tiles
     float pl1[COL ? NXL : 1], per[COL ? NXL : 1];
     u32x4 ppg[NPL];
-    Frag pQf[QG ? NB : 1][QG ? KB : 1];
+    // QG: the queries of one 16-row block (rows 16 (cw % NB) ..) as B fragments,
+    // pQa for the tile being output and pQb for the next one
+    Frag pQa[QG ? KB : 1], pQb[QG ? KB : 1];
 
     // keys, targets and the record of `tile` into registers
     auto load_xyr = [&](int tile) __attribute__((always_inline)) {
@@ -1011,18 +1013,16 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
             }
         }
     };
-    // queries of `tile`: staged through LDS, or (QG) as register fragments
+    // queries of `tile`: staged through LDS, or (QG) as register fragments of
+    // the wave's own row block into pQb
     auto load_q = [&](int tile) __attribute__((always_inline)) {
         const int t0 = tile * Ct;
         const rsrc_t rq = make_rsrc(qg + (size_t)t0 * D, (int64_t)(T_ - t0) * D * 2);
         if constexpr (QG) {
+            const int t = 16 * (cw % NB) + lr;
 #pragma unroll
-            for (int tb = 0; tb < NB; ++tb) {
-                const int t = 16 * tb + lr;
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-                    pQf[tb][kb] = buf_load8(rq, t < Ct ? (uint32_t)((t * D + 16 * kb + 4 * grp) * 2) : kOob);
-            }
+            for (int kb = 0; kb < KB; ++kb)
+                pQb[kb] = buf_load8(rq, t < Ct ? (uint32_t)((t * D + 16 * kb + 4 * grp) * 2) : kOob);
         } else {
 #pragma unroll
             for (int it = 0; it < NXL; ++it) pq[it] = buf_load16(rq, qvo[it]);
@@ -1076,7 +1076,8 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
                     for (int u = 0; u < 8; ++u) {
                         const float x = E::to_f(e[u]);
                         const float den = fabsf(x) * pl1[it] + eps;
-                        out[u] = E::from_f(den > 0.f ? per[it] * x / den : 0.f);
+                        // hardware reciprocal (1 ulp): u is rounded to bf16 next
+                        out[u] = E::from_f(den > 0.f ? per[it] * x * __builtin_amdgcn_rcpf(den) : 0.f);
                     }
                     *reinterpret_cast<u32x4*>(&sm.QU[b][i][col]) = outv;
                 }
@@ -1241,22 +1242,45 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb) *reinterpret_cast<Frag*>(cd + (size_t)cb * D * 16) = db[cb];
         }
+        if constexpr (QG) {
+            // Per-column rule: the queries come from global memory, so each
+            // wave takes one 16-row block tb (reading the queries once per
+            // workgroup) and forms its outputs for the value blocks
+            // c2 = cw / NB + k (4 / NB), from every chain wave's state and
+            // Delta fragments in LDS; stored at once.
+            const int tb = cw % NB;
+            const int t = 16 * tb + lr, t0 = p * Ct;
+            const float gs = gqt[t];
+            const bool st = t < Ct && t0 + t < T_ && a.o;
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                const int c2 = cw / NB + k * (4 / NB);
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int m = 0; m < D / 32; ++m)
+                    acc = E::mma32(sm.SB[pb][c2][2 * m][lane], sm.SB[pb][c2][2 * m + 1][lane],
+                                   pQa[2 * m], pQa[2 * m + 1], acc);
+                acc = acc * gs;
+#pragma unroll
+                for (int cb = 0; cb < NB; ++cb)
+                    if (cb <= tb)
+                        acc = E::mma16(sm.DB[pb][c2][cb][lane],
+                                       E::load(Pf + (size_t)R::pblk(tb, cb, false) * 256 + lane * 4),
+                                       acc);
+                if (st)
+                    *reinterpret_cast<Frag*>(og + (size_t)(t0 + t) * D + 16 * c2 + 4 * grp) =
+                        E::pack(acc);
+            }
+            return;
+        }
         static_for<NB>([&](auto tbc) __attribute__((always_inline)) {
             constexpr int tb = decltype(tbc)::value;
             if (tb < NBQ) {
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int m = 0; m < D / 32; ++m) {
-                    Frag q0, q1;
-                    if constexpr (QG) {
-                        q0 = pQf[tb][2 * m];
-                        q1 = pQf[tb][2 * m + 1];
-                    } else {
-                        const T* qr = &sm.QU[pb][16 * tb + lr][32 * m + 4 * grp];
-                        q0 = E::load(qr);
-                        q1 = E::load(qr + 16);
-                    }
-                    acc = E::mma32(sb[2 * m], sb[2 * m + 1], q0, q1, acc);
+                    const T* qr = &sm.QU[pb][16 * tb + lr][32 * m + 4 * grp];
+                    acc = E::mma32(sb[2 * m], sb[2 * m + 1], E::load(qr), E::load(qr + 16), acc);
                 }
                 acc = acc * gqt[16 * tb + lr];
                 static_for<NB>([&](auto cbc) __attribute__((always_inline)) {
@@ -1268,15 +1292,7 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
                                            acc);
                     }
                 });
-                if constexpr (COL) {
-                    // stored at once (the per-column pipeline does not defer)
-                    const int t = 16 * tb + lr, t0 = p * Ct;
-                    if (t < Ct && t0 + t < T_ && a.o)
-                        *reinterpret_cast<Frag*>(og + (size_t)(t0 + t) * D + 16 * cw + 4 * grp) =
-                            E::pack(acc);
-                } else {
-                    opk[tb] = E::pack(acc);
-                }
+                opk[tb] = E::pack(acc);
             }
         });
     };
@@ -1381,8 +1397,11 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
     // ---- pipeline: the chain works on tile it while the output half
     // finishes tile it-1 ----
     if constexpr (COL) {
-        // staged through registers (u is derived from x on the way)
+        // staged through registers (u is derived from x on the way); the
+        // queries of tile it+1 are loaded during iteration it, a full
+        // iteration before their use
         if (!chain && ntl > 0) {
+            load_q(0);
             load_xyr(0);
             load_pg(0);
             store_xyr(0);
@@ -1394,11 +1413,13 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
                 if (it < ntl) chain_tile(it);
             } else {
                 if (it >= 1) output_tile(it - 1);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) pQa[kb] = pQb[kb];
+                if (it + 1 < ntl) load_q(it + 1);
                 if (it + 1 < ntl) store_xyr(it + 1);
                 if (it < ntl) store_pg(it & 1);
                 if (it + 2 < ntl) load_xyr(it + 2);
                 if (it + 1 < ntl) load_pg(it + 1);
-                if (it < ntl) load_q(it);
             }
             lds_barrier();
         }
