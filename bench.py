@@ -308,9 +308,11 @@ def main():
             fl = chunk_flops(Bx, Hx, Tx * Wx, Dx, C, delta=not v.endswith("A"))
             gx = nb / (msx / 1e3) / 1e9
             tfx = fl / (msx / 1e3) / 1e12
+            tag = v + (f"W{Wx}" if Wx > 1 else "")
             extra[v.lower().replace("f", "falcon")] = {
                 "workload": wname, "tokens_per_s": Bx * Tx / (msx / 1e3), "ms_per_step": msx,
                 "hbm_gbs": gx, "hbm_frac": gx / HBM_PEAK_GBS, "algorithmic_bytes_per_call": nb,
+                "traffic": measured_traffic(f"chunk_fwd_{tag}_B{Bx}H{Hx}T{Tx}d{Dx}_bf16_c64"),
                 "mfma_tflops": tfx, "mfma_frac_bf16": tfx / BF16_PEAK_TFLOPS,
                 "algorithmic_flops_per_call": fl}
         del tx, ox, Sx, wsx
@@ -343,11 +345,13 @@ def main():
                         "hbm_gbs": nbytes_b / (ms_b / 1e3) / 1e9,
                         "hbm_frac": nbytes_b / (ms_b / 1e3) / 1e9 / HBM_PEAK_GBS,
                         "algorithmic_bytes_per_call": nbytes_b,
+                        "traffic": measured_traffic("chunk_bwd_F1_B8H16T4096d128_bf16_c64"),
                         "call": "falcon_chunk_bwd: dq, dk, dv, dalpha, deta, dS0 from d_o and "
                                 "dS_final (forward recomputed inside)"},
         "falcon1a_bwd": {"tokens_per_s": B * T / (ms_ba / 1e3), "ms_per_step": ms_ba,
                          "hbm_gbs": nbytes_b / (ms_ba / 1e3) / 1e9,
-                         "hbm_frac": nbytes_b / (ms_ba / 1e3) / 1e9 / HBM_PEAK_GBS},
+                         "hbm_frac": nbytes_b / (ms_ba / 1e3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("chunk_bwd_F1A_B8H16T4096d128_bf16_c64")},
         "falcon1_varlen": {"tokens_per_s": B * T / (ms_v / 1e3), "ms_per_step": ms_v,
                            "hbm_gbs": gbs_v, "hbm_frac": gbs_v / HBM_PEAK_GBS,
                            "batch": f"{len(lengths)} packed sequences, lengths {min(lengths)}.."
