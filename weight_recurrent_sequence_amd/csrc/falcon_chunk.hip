@@ -1297,6 +1297,70 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
         });
     };
 
+    // ---- output, row-block form (scalar and inner-product rules at 64-row
+    // tiles, windows of one): wave cw forms the outputs of query rows
+    // 16 cw .. 16 cw + 15 for all 64 value columns, from every recurrence
+    // wave's state and Delta fragments.  Its own query rows of the LDS
+    // buffer are then free (no other wave reads them, and the next fill of
+    // that buffer comes after the barrier), so the wave transposes its
+    // outputs through them and stores o as 16-byte row pieces: each store
+    // instruction writes 64 contiguous bytes of 16 rows instead of 32.
+    constexpr bool ROWS = !COL && !WIN && NB == 4;
+    auto output_rows = [&](int p) __attribute__((always_inline)) {
+        const int pb = p & 1, t0 = p * Ct, tb = cw;
+        const T* Pf = reinterpret_cast<const T*>(sm.pg[pb]);
+        const float* gqt = reinterpret_cast<const float*>(sm.pg[pb] + R::npblk(WIN) * 512);
+        if (a.ck_s) {
+            // checkpoints, as in output_tile (this wave's own value columns)
+            const size_t tt = (size_t)bh * ntiles + p;
+            T* cs = static_cast<T*>(a.ck_s) + tt * D * D + (size_t)vcol * 16 + 4 * grp;
+            T* cd = static_cast<T*>(a.ck_d) + tt * D * CV + (size_t)vcol * 16 + 4 * grp;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+                *reinterpret_cast<Frag*>(cs + (size_t)kb * D * 16) = sm.SB[pb][cw][kb][lane];
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb)
+                *reinterpret_cast<Frag*>(cd + (size_t)cb * D * 16) = sm.DB[pb][cw][cb][lane];
+        }
+        T* qrow = &sm.QU[pb][16 * tb][0];
+        Frag qf[KB];
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m) {
+            qf[2 * m] = E::load(qrow + lr * LDX + 32 * m + 4 * grp);
+            qf[2 * m + 1] = E::load(qrow + lr * LDX + 32 * m + 16 + 4 * grp);
+        }
+        const float gs = gqt[16 * tb + lr];
+        Frag of[4];
+#pragma unroll
+        for (int c2 = 0; c2 < 4; ++c2) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int m = 0; m < D / 32; ++m)
+                acc = E::mma32(sm.SB[pb][c2][2 * m][lane], sm.SB[pb][c2][2 * m + 1][lane], qf[2 * m],
+                               qf[2 * m + 1], acc);
+            acc = acc * gs;
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb)
+                if (cb <= tb)
+                    acc = E::mma16(sm.DB[pb][c2][cb][lane],
+                                   E::load(Pf + (size_t)R::pblk(tb, cb, false) * 256 + lane * 4), acc);
+            of[c2] = E::pack(acc);  // O[t = 16 tb + lr][v = 16 c2 + 4 grp + r]
+        }
+        // transpose through the wave's own query rows (read above, in order)
+#pragma unroll
+        for (int c2 = 0; c2 < 4; ++c2)
+            *reinterpret_cast<Frag*>(qrow + lr * LDX + 16 * c2 + 4 * grp) = of[c2];
+        const int rr = lane & 15, pc = lane >> 4;  // row, 16-byte piece (and piece + 4)
+        const u32x4 o0 = *reinterpret_cast<const u32x4*>(qrow + rr * LDX + 8 * pc);
+        const u32x4 o1 = *reinterpret_cast<const u32x4*>(qrow + rr * LDX + 8 * pc + 32);
+        const int t = 16 * tb + rr;
+        if (t < Ct && t0 + t < T_ && a.o) {
+            T* dst = og + (size_t)(t0 + t) * D + 8 * pc;
+            *reinterpret_cast<u32x4*>(dst) = o0;
+            *reinterpret_cast<u32x4*>(dst + 32) = o1;
+        }
+    };
+
     // ---- direct-to-LDS staging (all rules but the per-column one, whose
     // write vectors are derived while staging): every 16-byte slot of an LDS
     // tile is one lane of one buffer_load ... lds, issued by the output waves
@@ -1493,15 +1557,20 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
             }
         } else {
             for (int it = 0; it <= ntl; ++it) {
-                if (it >= 2) store_o(it - 2);
+                if (!ROWS && it >= 2) store_o(it - 2);
                 if (it + 1 < ntl && (it + 1) * Ct < W) {
                     load_xyr(it + 1);
                     store_xyr(it + 1);
                 }
-                if (it >= 1) output_tile(it - 1);
+                if (it >= 1) {
+                    if constexpr (ROWS)
+                        output_rows(it - 1);
+                    else
+                        output_tile(it - 1);
+                }
                 lds_barrier();
             }
-            if (ntl >= 1) store_o(ntl - 1);
+            if (!ROWS && ntl >= 1) store_o(ntl - 1);
         }
     }
 
