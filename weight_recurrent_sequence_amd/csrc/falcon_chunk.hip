@@ -1304,7 +1304,8 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
     // buffer are then free (no other wave reads them, and the next fill of
     // that buffer comes after the barrier), so the wave transposes its
     // outputs through them and stores o as 16-byte row pieces: each store
-    // instruction writes 64 contiguous bytes of 16 rows instead of 32.
+    // instruction writes 8 whole rows of its 64 value columns (128 bytes)
+    // instead of 32 bytes of 16 rows.
     constexpr bool ROWS = !COL && !WIN && NB == 4;
     auto output_rows = [&](int p) __attribute__((always_inline)) {
         const int pb = p & 1, t0 = p * Ct, tb = cw;
@@ -1350,14 +1351,14 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
 #pragma unroll
         for (int c2 = 0; c2 < 4; ++c2)
             *reinterpret_cast<Frag*>(qrow + lr * LDX + 16 * c2 + 4 * grp) = of[c2];
-        const int rr = lane & 15, pc = lane >> 4;  // row, 16-byte piece (and piece + 4)
+        const int rr = lane >> 3, pc = lane & 7;  // row (and row + 8), 16-byte piece
         const u32x4 o0 = *reinterpret_cast<const u32x4*>(qrow + rr * LDX + 8 * pc);
-        const u32x4 o1 = *reinterpret_cast<const u32x4*>(qrow + rr * LDX + 8 * pc + 32);
+        const u32x4 o1 = *reinterpret_cast<const u32x4*>(qrow + (rr + 8) * LDX + 8 * pc);
         const int t = 16 * tb + rr;
-        if (t < Ct && t0 + t < T_ && a.o) {
+        if (a.o) {
             T* dst = og + (size_t)(t0 + t) * D + 8 * pc;
-            *reinterpret_cast<u32x4*>(dst) = o0;
-            *reinterpret_cast<u32x4*>(dst + 32) = o1;
+            if (t < Ct && t0 + t < T_) *reinterpret_cast<u32x4*>(dst) = o0;
+            if (t + 8 < Ct && t0 + t + 8 < T_) *reinterpret_cast<u32x4*>(dst + 8 * D) = o1;
         }
     };
 
