@@ -784,16 +784,16 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs a, const void
 //                       residuals, forward substitution -> Delta (bf16 copy
 //                       in LDS), state update.  No global memory traffic.
 //   waves 4-7  (output) tile `it - 1`: O^T = diag(gq) (S0 Q^T) + Delta^T P^T
-//                       from the two LDS copies, stored straight from the
-//                       accumulators (each lane owns four adjacent columns of
-//                       one row).
+//                       from the two LDS copies; at 64-row tiles each wave
+//                       takes 16 rows for all 64 value columns and stores
+//                       them as whole rows (transposed through its own,
+//                       already read, query rows), otherwise each takes 16
+//                       value columns and stores from the accumulators.
 //   waves 8-11 (fill)   the fills of tile it+1's keys, targets and chain
-//                       record and tile it's queries and output record:
-//                       direct to LDS for the delta family, through registers
-//                       one iteration ahead for the A family.  A wave that
-//                       issues a tile's worth of fills stalls on a full
-//                       memory queue for thousands of cycles; here no
-//                       computing wave does.
+//                       record and tile it's queries and output record,
+//                       direct to LDS.  A wave that issues a tile's worth of
+//                       fills stalls on a full memory queue for thousands of
+//                       cycles; here no computing wave does.
 // The per-column rule stages through registers instead (its write vectors
 // are derived on the way) and runs without fill waves.  One barrier per
 // tile, fencing LDS only.  Loads use buffer descriptors: out-of-range rows
@@ -935,7 +935,7 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
     // rows outside the sequence read as zero (descriptor bounds), halo rows
     // come from a second load that is merged when the piece is stored.
     int xrel[NXL], yrel[NYL];
-    uint32_t xcb[NXL], ycb[NYL], qvo[NXL];
+    uint32_t xcb[NXL], ycb[NYL];
     bool xok[NXL], yok[NYL];
 #pragma unroll
     for (int it = 0; it < NXL; ++it) {
@@ -945,7 +945,6 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
         xok[it] = c < CV * CPR && i < NVR;
         xrel[it] = s - w - a.lag;
         xcb[it] = (uint32_t)col * 2;
-        qvo[it] = (c < CV * CPR && i < Ct) ? (uint32_t)((i * D + col) * 2) : kOob;
     }
 #pragma unroll
     for (int it = 0; it < NYL; ++it) {
@@ -957,7 +956,7 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
         ycb[it] = (uint32_t)col * 2;
     }
 
-    u32x4 px[NXL], pq[QG ? 1 : NXL], py[NYL], pr[NRL];
+    u32x4 px[NXL], py[NYL], pr[NRL];
     u32x4 pxh[NXL], pyh[NYL];  // halo rows of the first tiles
     float pl1[COL ? NXL : 1], per[COL ? NXL : 1];
     u32x4 ppg[NPL];
@@ -1013,19 +1012,16 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
             }
         }
     };
-    // queries of `tile`: staged through LDS, or (QG) as register fragments of
-    // the wave's own row block into pQb
+    // queries of `tile` (per-column rule) as register fragments of the
+    // wave's own row block into pQb
     auto load_q = [&](int tile) __attribute__((always_inline)) {
-        const int t0 = tile * Ct;
-        const rsrc_t rq = make_rsrc(qg + (size_t)t0 * D, (int64_t)(T_ - t0) * D * 2);
         if constexpr (QG) {
+            const int t0 = tile * Ct;
+            const rsrc_t rq = make_rsrc(qg + (size_t)t0 * D, (int64_t)(T_ - t0) * D * 2);
             const int t = 16 * (cw % NB) + lr;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
                 pQb[kb] = buf_load8(rq, t < Ct ? (uint32_t)((t * D + 16 * kb + 4 * grp) * 2) : kOob);
-        } else {
-#pragma unroll
-            for (int it = 0; it < NXL; ++it) pq[it] = buf_load16(rq, qvo[it]);
         }
     };
     // output-side record pieces of `tile` (P fragments, query decays)
@@ -1037,13 +1033,6 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
             ppg[it] = *reinterpret_cast<const u32x4*>(
                 rt + (pc < PFC ? R::kP * 2 + (size_t)pc * 16
                                : R::kScalBytes + 2 * CV * 4 + (size_t)(pc - PFC) * 16));
-        }
-    };
-    auto store_q = [&](int b) __attribute__((always_inline)) {
-#pragma unroll
-        for (int it = 0; it < NXL; ++it) {
-            const int c = otid + 256 * it;
-            if (c < CV * CPR) *reinterpret_cast<u32x4*>(&sm.QU[b][c / CPR][(c % CPR) * 8]) = pq[it];
         }
     };
     auto store_pg = [&](int b) __attribute__((always_inline)) {
@@ -1519,10 +1508,12 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
                 if (it < ntl) chain_tile(it);
                 lds_barrier();
             }
-        } else if (filler && DELTA) {
-            // Delta family: direct-to-LDS fills, issued after the barrier and
-            // waited for before the next one.  Its chain and output waves keep
-            // LDS busy, and these fills cost no LDS instruction of their own.
+        } else if (filler) {
+            // direct-to-LDS fills, issued after the barrier and waited for
+            // before the next one.  The chain and output waves keep LDS busy,
+            // and these fills cost no LDS instruction of their own.  (The
+            // inner-product rules once staged through registers one iteration
+            // ahead instead: Falcon-3A at window 4 ran 35% slower that way.)
             for (int it = 0; it <= ntl; ++it) {
                 if (it + 1 < ntl && (it + 1) * Ct >= W) {
                     dma_xr(it + 1);
@@ -1530,30 +1521,6 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
                 }
                 if (it < ntl) dma_qp(it);
                 wait_vm_all();
-                lds_barrier();
-            }
-        } else if (filler) {
-            // A family (lighter on LDS): loads run one iteration ahead of their
-            // LDS stores through registers, so each has a whole iteration to
-            // arrive: the registers hold tile it+1's keys, targets and chain
-            // record and tile it's queries and output record while iteration
-            // it-1 runs.
-            if (1 < ntl && Ct >= W) load_xyr(1);
-            if (ntl > 0) {
-                load_q(0);
-                load_pg(0);
-            }
-            for (int it = 0; it <= ntl; ++it) {
-                if (it + 1 < ntl && (it + 1) * Ct >= W) store_xyr(it + 1);
-                if (it < ntl) {
-                    store_q(it & 1);
-                    store_pg(it & 1);
-                }
-                if (it + 2 < ntl && (it + 2) * Ct >= W) load_xyr(it + 2);
-                if (it + 1 < ntl) {
-                    load_q(it + 1);
-                    load_pg(it + 1);
-                }
                 lds_barrier();
             }
         } else {
