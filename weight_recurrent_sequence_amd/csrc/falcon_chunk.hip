@@ -1231,6 +1231,7 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb) *reinterpret_cast<Frag*>(cd + (size_t)cb * D * 16) = db[cb];
         }
+        if (!a.o) return;  // checkpoint-only run (the backward pass's recompute)
         if constexpr (QG) {
             // Per-column rule: the queries come from global memory, so each
             // wave takes one 16-row block tb (reading the queries once per
@@ -1312,6 +1313,7 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
             for (int cb = 0; cb < NB; ++cb)
                 *reinterpret_cast<Frag*>(cd + (size_t)cb * D * 16) = sm.DB[pb][cw][cb][lane];
         }
+        if (!a.o) return;  // checkpoint-only run (the backward pass's recompute)
         T* qrow = &sm.QU[pb][16 * tb][0];
         Frag qf[KB];
 #pragma unroll
