@@ -11,7 +11,8 @@ blocked forward substitution, outputs, state update).  `value` is tokens
 Falcon-1 with same-step pairs (k_t, v_t), Falcon-1 with L2-normalized keys
 and queries, Falcon-1 over 16 packed sequences
 of mixed lengths with the same token count, the backward of Falcon-1 and
-Falcon-1A on the same batch, Falcon-2 / Falcon-2A at B=4, H=32, T=8192 and
+Falcon-1A on the same batch, a Falcon-1 training step (forward keeping the
+backward's checkpoints, backward from them), Falcon-2 / Falcon-2A at B=4, H=32, T=8192 and
 Falcon-3 / Falcon-3A (window 4) at B=2, H=16, T=32768, the decode step (256
 sequences x 32 heads, d=128, 1024 consecutive steps) and the
 Falcon-3 decode step at the same shape with a window of four, each with its
@@ -280,6 +281,19 @@ def main():
     print(f"[bench] F1A backward", file=sys.stderr, flush=True)
     ms_ba, _ = timed(step_bwd("F1A"), args.steps, args.warmup)
     nbytes_b = bwd_bytes(B, H, T, D)
+
+    # A training step without the backward's forward re-run: the forward
+    # keeps its records and checkpoints (falcon_chunk_fwd_save), the backward
+    # reads them (falcon_chunk_bwd_saved)
+    def step_train():
+        fal.chunk_fwd_save(t["q"], t["k"], t["v"], t["alpha"], t["eta"], "F1", chunk=C, o=o,
+                           S_final=S_fin, saved=ws_b)
+        fal.chunk_bwd_saved(t["q"], t["k"], t["v"], t["alpha"], t["eta"], d_o, "F1",
+                            dS_final=dS_fin, chunk=C, saved=ws_b)
+
+    print(f"[bench] F1 training step (forward with checkpoints + backward from them)",
+          file=sys.stderr, flush=True)
+    ms_t, _ = timed(step_train, args.steps, args.warmup)
     del ws_b, d_o, dS_fin
 
     # The other full-size chunk-forward workloads: Falcon-2 (per-column
@@ -348,6 +362,10 @@ def main():
                         "traffic": measured_traffic("chunk_bwd_F1_B8H16T4096d128_bf16_c64"),
                         "call": "falcon_chunk_bwd: dq, dk, dv, dalpha, deta, dS0 from d_o and "
                                 "dS_final (forward recomputed inside)"},
+        "falcon1_train_step": {"tokens_per_s": B * T / (ms_t / 1e3), "ms_per_step": ms_t,
+                               "fwd_plus_recomputing_bwd_ms": ms + ms_b,
+                               "call": "falcon_chunk_fwd_save (o, S_final and the backward's "
+                                       "checkpoints) + falcon_chunk_bwd_saved"},
         "falcon1a_bwd": {"tokens_per_s": B * T / (ms_ba / 1e3), "ms_per_step": ms_ba,
                          "hbm_gbs": nbytes_b / (ms_ba / 1e3) / 1e9,
                          "hbm_frac": nbytes_b / (ms_ba / 1e3) / 1e9 / HBM_PEAK_GBS,

@@ -238,6 +238,55 @@ int falcon_chunk_bwd_varlen(const void* q, const void* k, const void* v, const f
                             size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Training form of the pair above (the chunk form and its derivative; "Fast
+ * Weight Attention for Continual Learning", authors' abstract): the forward
+ * and the backward of one step without recomputing the forward.  Callers that can hold the checkpoints
+ * between the two calls (a training step) save the backward's forward
+ * re-run this way; the results are those of falcon_chunk_fwd and
+ * falcon_chunk_bwd (same kernels, same arithmetic).
+ *
+ * falcon_chunk_fwd_save: as falcon_chunk_fwd (same arguments and outputs),
+ *   and it also leaves in `saved` the records and checkpoints the backward
+ *   reads.  saved: falcon_chunk_bwd_workspace(...) bytes of device memory
+ *   owned by the caller.  Support matrix as for falcon_chunk_bwd.
+ * falcon_chunk_bwd_saved: as falcon_chunk_bwd (same arguments and outputs),
+ *   reading `saved` as a falcon_chunk_fwd_save call on the same inputs and
+ *   sizes left it instead of re-running the forward (it also writes its own
+ *   scratch regions there; the saved part stays intact, so it may be called
+ *   again with other cotangents).  A `saved` buffer from other inputs, or
+ *   not filled, gives meaningless results, not an error.
+ * The _varlen forms pair falcon_chunk_fwd_varlen and falcon_chunk_bwd_varlen
+ * in the same way, with falcon_chunk_bwd_varlen_workspace(...) bytes.
+ */
+int falcon_chunk_fwd_save(const void* q, const void* k, const void* v, const float* alpha,
+                          const float* eta, const float* S0, const void* k_prev, const void* v_prev,
+                          void* o, float* S_final, int B, int H, int T, int dk, int dv,
+                          falcon_dtype dt, falcon_variant var, int window, int chunk, float eps,
+                          void* saved, size_t saved_bytes, hipStream_t stream);
+int falcon_chunk_bwd_saved(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* eta, const float* S0, const void* k_prev,
+                           const void* v_prev, const void* d_o, const float* dS_final, void* dq,
+                           void* dk, void* dv, float* dalpha, float* deta, float* dS0,
+                           void* dk_prev, void* dv_prev, int B, int H, int T, int dk_dim,
+                           int dv_dim, falcon_dtype dt, falcon_variant var, int window, int chunk,
+                           float eps, void* saved, size_t saved_bytes, hipStream_t stream);
+int falcon_chunk_fwd_varlen_save(const void* q, const void* k, const void* v, const float* alpha,
+                                 const float* eta, const float* S0, const void* k_prev,
+                                 const void* v_prev, void* o, float* S_final,
+                                 const int* cu_seqlens, int N, int H, int total_T, int max_seqlen,
+                                 int dk, int dv, falcon_dtype dt, falcon_variant var, int window,
+                                 int chunk, float eps, void* saved, size_t saved_bytes,
+                                 hipStream_t stream);
+int falcon_chunk_bwd_varlen_saved(const void* q, const void* k, const void* v, const float* alpha,
+                                  const float* eta, const float* S0, const void* k_prev,
+                                  const void* v_prev, const void* d_o, const float* dS_final,
+                                  void* dq, void* dk, void* dv, float* dalpha, float* deta,
+                                  float* dS0, void* dk_prev, void* dv_prev, const int* cu_seqlens,
+                                  int N, int H, int total_T, int max_seqlen, int dk_dim, int dv_dim,
+                                  falcon_dtype dt, falcon_variant var, int window, int chunk,
+                                  float eps, void* saved, size_t saved_bytes, hipStream_t stream);
+
+/*
  * One decode step for N independent sequences x H heads (one token each):
  * x = k_cache (the previous key; with FALCON_SAME_STEP the new key k),
  * S' = alpha S, write as above, o = S q, then k_cache <- k.

@@ -33,6 +33,9 @@ def test_header_declares_the_entry_points():
                                            "falcon_chunk_bwd_varlen_workspace",
                                            "falcon_chunk_fwd_varlen",
                                            "falcon_chunk_fwd_varlen_workspace",
+                                           "falcon_chunk_fwd_save", "falcon_chunk_bwd_saved",
+                                           "falcon_chunk_fwd_varlen_save",
+                                           "falcon_chunk_bwd_varlen_saved",
                                            "falcon_decode_step", "falcon_decode_step_window",
                                            "falcon_status_string"])
 
@@ -218,12 +221,12 @@ def test_feature_map_workspace_holds_the_mapped_inputs(L):
         assert got == al(base) + 2 * al(B * H * T * d * es) + al(B * H * W * d * es)
 
 
-def bwd(L, **kw):
+def bwd(L, fn="falcon_chunk_bwd", **kw):
     a = dict(q=P, k=P, v=P, alpha=P, eta=P, S0=None, k_prev=None, v_prev=None, do=P, dS=None,
              dq=P, dk=P, dv=P, dal=P, det=P, dS0=None, dkp=None, dvp=None, B=2, H=4, T=100,
              dk_=128, dv_=128, dt=1, var=1, window=1, chunk=64, eps=1e-6, ws=None, wsn=0)
     a.update(kw)
-    return L.falcon_chunk_bwd(a["q"], a["k"], a["v"], a["alpha"], a["eta"], a["S0"], a["k_prev"],
+    return getattr(L, fn)(a["q"], a["k"], a["v"], a["alpha"], a["eta"], a["S0"], a["k_prev"],
                               a["v_prev"], a["do"], a["dS"], a["dq"], a["dk"], a["dv"], a["dal"],
                               a["det"], a["dS0"], a["dkp"], a["dvp"], a["B"], a["H"], a["T"],
                               a["dk_"], a["dv_"], a["dt"], a["var"], a["window"], a["chunk"],
@@ -244,6 +247,36 @@ def bwd(L, **kw):
 ])
 def test_bwd_rejects(L, kw, code):
     assert bwd(L, **kw) == code
+    # the backward from saved checkpoints checks its arguments the same way
+    assert bwd(L, fn="falcon_chunk_bwd_saved", **kw) == code
+
+
+def fwd_save(L, **kw):
+    a = dict(q=P, k=P, v=P, alpha=P, eta=P, S0=None, k_prev=None, v_prev=None, o=P, S=None,
+             B=2, H=4, T=100, dk_=128, dv_=128, dt=1, var=1, window=1, chunk=64, eps=1e-6,
+             ws=None, wsn=0)
+    a.update(kw)
+    return L.falcon_chunk_fwd_save(a["q"], a["k"], a["v"], a["alpha"], a["eta"], a["S0"],
+                                   a["k_prev"], a["v_prev"], a["o"], a["S"], a["B"], a["H"],
+                                   a["T"], a["dk_"], a["dv_"], a["dt"], a["var"], a["window"],
+                                   a["chunk"], ctypes.c_float(a["eps"]), a["ws"], a["wsn"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(var=4), -3), (dict(dt=0), -3), (dict(chunk=32), -3), (dict(dk_=96, dv_=96), -3),
+    (dict(var=3, window=9), -3), (dict(B=0), -2), (dict(eps=-1.0), -2),
+    (dict(q=None), -1), (dict(o=None), -1),
+    (dict(), -4), (dict(ws=P, wsn=1024), -4), (dict(var=13, window=4), -4),
+])
+def test_fwd_save_rejects(L, kw, code):
+    """The saving forward takes the forward's arguments, the backward's
+    support matrix and a buffer of the backward's workspace size."""
+    assert fwd_save(L, **kw) == code
+
+
+def test_fwd_save_with_nothing_to_do(L):
+    # no steps and no final state: nothing to write, no buffer needed
+    assert fwd_save(L, T=0) == 0
 
 
 def test_bwd_workspace_sizes(L):

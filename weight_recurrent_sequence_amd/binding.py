@@ -63,6 +63,11 @@ def lib():
         L.falcon_chunk_bwd_varlen_workspace.argtypes = [ci] * 9
         L.falcon_chunk_bwd_varlen.restype = ci
         L.falcon_chunk_bwd_varlen.argtypes = [vp] * 19 + [ci] * 10 + [cf, vp, sz, vp]
+        for name, nvp, nci in (("falcon_chunk_fwd_save", 10, 9), ("falcon_chunk_bwd_saved", 18, 9),
+                               ("falcon_chunk_fwd_varlen_save", 11, 10),
+                               ("falcon_chunk_bwd_varlen_saved", 19, 10)):
+            getattr(L, name).restype = ci
+            getattr(L, name).argtypes = [vp] * nvp + [ci] * nci + [cf, vp, sz, vp]
         L.falcon_decode_step.restype = ci
         L.falcon_decode_step.argtypes = [vp] * 8 + [ci] * 7 + [cf, vp]
         L.falcon_decode_step_window.restype = ci
@@ -124,7 +129,7 @@ def workspace_bytes(B, H, T, dk, dv, dtype, variant, window=1, chunk=64, phi="id
 
 def chunk_fwd(q, k, v, alpha, eta, variant, *, window=1, chunk=64, eps=1e-6, S0=None,
               k_prev=None, v_prev=None, o=None, S_final=None, return_state=True,
-              workspace=None, stream=None, align="prefix", phi="identity"):
+              workspace=None, stream=None, align="prefix", phi="identity", _save=False):
     """Chunk-parallel forward.  q,k [B,H,T,dk]; v [B,H,T,dv] (bf16 or fp32);
     alpha, eta [B,H,T] fp32; S0 [B,H,dv,dk] fp32 or None; k_prev [B,H,W,dk],
     v_prev [B,H,W-1,dv] or None.  `workspace` (uint8 device tensor of at
@@ -154,20 +159,29 @@ def chunk_fwd(q, k, v, alpha, eta, variant, *, window=1, chunk=64, eps=1e-6, S0=
     if S_final is None and return_state:
         S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     _check(S_final, "S_final", (B, H, dv, dk), torch.float32, dev)
-    ws_n = int(lib().falcon_chunk_fwd_workspace(B, H, T, dk, dv, dtc, var, window, chunk))
+    query = lib().falcon_chunk_bwd_workspace if _save else lib().falcon_chunk_fwd_workspace
+    ws_n = int(query(B, H, T, dk, dv, dtc, var, window, chunk))
     if workspace is not None:
         if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_n:
             raise ValueError(f"workspace: need {ws_n} bytes on {dev}")
         ws, ws_n = workspace, workspace.numel() * workspace.element_size()
     else:
         ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n > 0 else None
-    st = lib().falcon_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(S0),
-                                _ptr(k_prev), _ptr(v_prev), _ptr(o), _ptr(S_final), B, H, T, dk,
-                                dv, dtc, var, window, chunk, float(eps), _ptr(ws), ws_n,
-                                _stream(stream))
+    name = "falcon_chunk_fwd_save" if _save else "falcon_chunk_fwd"
+    st = getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(S0),
+                              _ptr(k_prev), _ptr(v_prev), _ptr(o), _ptr(S_final), B, H, T, dk,
+                              dv, dtc, var, window, chunk, float(eps), _ptr(ws), ws_n,
+                              _stream(stream))
     if st != 0:
-        raise FalconError(st, "falcon_chunk_fwd")
+        raise FalconError(st, name)
     return o, S_final
+
+
+def chunk_fwd_save(q, k, v, alpha, eta, variant, *, saved, **kw):
+    """chunk_fwd that also leaves the backward's records and checkpoints in
+    `saved` (uint8 device tensor of at least bwd_workspace_bytes(...) bytes),
+    for chunk_bwd_saved on the same inputs.  Returns (o, S_final)."""
+    return chunk_fwd(q, k, v, alpha, eta, variant, workspace=saved, _save=True, **kw)
 
 
 def bwd_workspace_bytes(B, H, T, dk, dv, dtype, variant, window=1, chunk=64, align="prefix",
@@ -178,7 +192,7 @@ def bwd_workspace_bytes(B, H, T, dk, dv, dtype, variant, window=1, chunk=64, ali
 
 def chunk_bwd(q, k, v, alpha, eta, d_o, variant, *, dS_final=None, window=1, chunk=64,
               eps=1e-6, S0=None, k_prev=None, v_prev=None, want_dS0=True, want_dk_prev=None,
-              workspace=None, stream=None, align="prefix", phi="identity"):
+              workspace=None, stream=None, align="prefix", phi="identity", _saved=False):
     """Gradients of the chunk forward.  Inputs as for chunk_fwd, plus d_o
     [B,H,T,dv] (input dtype) and dS_final [B,H,dv,dk] fp32 or None.  Returns a
     dict with dq, dk, dv (input dtype), dalpha, deta (fp32), dS0 (fp32, or
@@ -219,15 +233,24 @@ def chunk_bwd(q, k, v, alpha, eta, d_o, variant, *, dS_final=None, window=1, chu
         ws, ws_n = workspace, workspace.numel() * workspace.element_size()
     else:
         ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n > 0 else None
-    st = lib().falcon_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(S0),
-                                _ptr(k_prev), _ptr(v_prev), _ptr(d_o), _ptr(dS_final),
-                                _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dalpha"]),
-                                _ptr(g["deta"]), _ptr(g["dS0"]), _ptr(g["dk_prev"]), _ptr(g["dv_prev"]),
-                                B, H, T, dk, dv, dtc, var, window, chunk, float(eps), _ptr(ws),
-                                ws_n, _stream(stream))
+    if _saved and workspace is None and ws_n > 0:
+        raise ValueError("chunk_bwd_saved needs the buffer chunk_fwd_save filled")
+    name = "falcon_chunk_bwd_saved" if _saved else "falcon_chunk_bwd"
+    st = getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(S0),
+                              _ptr(k_prev), _ptr(v_prev), _ptr(d_o), _ptr(dS_final),
+                              _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dalpha"]),
+                              _ptr(g["deta"]), _ptr(g["dS0"]), _ptr(g["dk_prev"]), _ptr(g["dv_prev"]),
+                              B, H, T, dk, dv, dtc, var, window, chunk, float(eps), _ptr(ws),
+                              ws_n, _stream(stream))
     if st != 0:
-        raise FalconError(st, "falcon_chunk_bwd")
+        raise FalconError(st, name)
     return g
+
+
+def chunk_bwd_saved(q, k, v, alpha, eta, d_o, variant, *, saved, **kw):
+    """chunk_bwd from the buffer a chunk_fwd_save call on the same inputs
+    filled (the forward is not re-run).  Returns the dict chunk_bwd returns."""
+    return chunk_bwd(q, k, v, alpha, eta, d_o, variant, workspace=saved, _saved=True, **kw)
 
 
 def bwd_varlen_workspace_bytes(N, H, max_seqlen, dk, dv, dtype, variant, window=1, chunk=64,
@@ -240,7 +263,7 @@ def bwd_varlen_workspace_bytes(N, H, max_seqlen, dk, dv, dtype, variant, window=
 def chunk_bwd_varlen(q, k, v, alpha, eta, cu_seqlens, d_o, variant, *, max_seqlen=None,
                      dS_final=None, window=1, chunk=64, eps=1e-6, S0=None, k_prev=None,
                      v_prev=None, want_dS0=True, want_dk_prev=None, workspace=None, stream=None,
-                     align="prefix", phi="identity"):
+                     align="prefix", phi="identity", _saved=False):
     """Gradients of chunk_fwd_varlen.  q, k, v, d_o [H,total_T,d]; alpha, eta
     [H,total_T]; cu_seqlens int32 [N+1] on the device; S0, dS_final
     [N,H,d,d]; k_prev [N,H,W,d], v_prev [N,H,W-1,d].  Returns a dict as
@@ -286,16 +309,26 @@ def chunk_bwd_varlen(q, k, v, alpha, eta, cu_seqlens, d_o, variant, *, max_seqle
         ws, ws_n = workspace, workspace.numel() * workspace.element_size()
     else:
         ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n > 0 else None
-    st = lib().falcon_chunk_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(S0),
-                                       _ptr(k_prev), _ptr(v_prev), _ptr(d_o), _ptr(dS_final),
-                                       _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
-                                       _ptr(g["dalpha"]), _ptr(g["deta"]), _ptr(g["dS0"]),
-                                       _ptr(g["dk_prev"]), _ptr(g["dv_prev"]), _ptr(cu_seqlens),
-                                       N, H, Ttot, max_seqlen, dk, dv, dtc, var, window, chunk,
-                                       float(eps), _ptr(ws), ws_n, _stream(stream))
+    if _saved and workspace is None and ws_n > 0:
+        raise ValueError("chunk_bwd_varlen_saved needs the buffer chunk_fwd_varlen_save filled")
+    name = "falcon_chunk_bwd_varlen_saved" if _saved else "falcon_chunk_bwd_varlen"
+    st = getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(S0),
+                              _ptr(k_prev), _ptr(v_prev), _ptr(d_o), _ptr(dS_final),
+                              _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+                              _ptr(g["dalpha"]), _ptr(g["deta"]), _ptr(g["dS0"]),
+                              _ptr(g["dk_prev"]), _ptr(g["dv_prev"]), _ptr(cu_seqlens),
+                              N, H, Ttot, max_seqlen, dk, dv, dtc, var, window, chunk,
+                              float(eps), _ptr(ws), ws_n, _stream(stream))
     if st != 0:
-        raise FalconError(st, "falcon_chunk_bwd_varlen")
+        raise FalconError(st, name)
     return g
+
+
+def chunk_bwd_varlen_saved(q, k, v, alpha, eta, cu_seqlens, d_o, variant, *, saved, **kw):
+    """chunk_bwd_varlen from the buffer a chunk_fwd_varlen_save call on the
+    same inputs filled."""
+    return chunk_bwd_varlen(q, k, v, alpha, eta, cu_seqlens, d_o, variant, workspace=saved,
+                            _saved=True, **kw)
 
 
 def varlen_workspace_bytes(N, H, max_seqlen, dk, dv, dtype, variant, window=1, chunk=64,
@@ -307,7 +340,7 @@ def varlen_workspace_bytes(N, H, max_seqlen, dk, dv, dtype, variant, window=1, c
 def chunk_fwd_varlen(q, k, v, alpha, eta, cu_seqlens, variant, *, max_seqlen=None, window=1,
                      chunk=64, eps=1e-6, S0=None, k_prev=None, v_prev=None, o=None,
                      S_final=None, return_state=True, workspace=None, stream=None,
-                     align="prefix", phi="identity"):
+                     align="prefix", phi="identity", _save=False):
     """Chunk-parallel forward over N packed sequences.  q, k [H,total_T,dk];
     v [H,total_T,dv]; alpha, eta [H,total_T] fp32; cu_seqlens int32 [N+1] on
     the device (sequence n = rows cu_seqlens[n] .. cu_seqlens[n+1]-1 of every
@@ -345,22 +378,32 @@ def chunk_fwd_varlen(q, k, v, alpha, eta, cu_seqlens, variant, *, max_seqlen=Non
     if S_final is None and return_state:
         S_final = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
     _check(S_final, "S_final", (N, H, dv, dk), torch.float32, dev)
-    ws_n = int(lib().falcon_chunk_fwd_varlen_workspace(N, H, max_seqlen, dk, dv, dtc, var,
-                                                        window, chunk))
+    query = (lib().falcon_chunk_bwd_varlen_workspace if _save
+             else lib().falcon_chunk_fwd_varlen_workspace)
+    ws_n = int(query(N, H, max_seqlen, dk, dv, dtc, var, window, chunk))
     if workspace is not None:
         if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_n:
             raise ValueError(f"workspace: need {ws_n} bytes on {dev}")
         ws, ws_n = workspace, workspace.numel() * workspace.element_size()
     else:
         ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n > 0 else None
-    st = lib().falcon_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta),
-                                       _ptr(S0), _ptr(k_prev), _ptr(v_prev), _ptr(o),
-                                       _ptr(S_final), _ptr(cu_seqlens), N, H, Ttot, max_seqlen,
-                                       dk, dv, dtc, var, window, chunk, float(eps), _ptr(ws),
-                                       ws_n, _stream(stream))
+    name = "falcon_chunk_fwd_varlen_save" if _save else "falcon_chunk_fwd_varlen"
+    st = getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta),
+                              _ptr(S0), _ptr(k_prev), _ptr(v_prev), _ptr(o),
+                              _ptr(S_final), _ptr(cu_seqlens), N, H, Ttot, max_seqlen,
+                              dk, dv, dtc, var, window, chunk, float(eps), _ptr(ws),
+                              ws_n, _stream(stream))
     if st != 0:
-        raise FalconError(st, "falcon_chunk_fwd_varlen")
+        raise FalconError(st, name)
     return o, S_final
+
+
+def chunk_fwd_varlen_save(q, k, v, alpha, eta, cu_seqlens, variant, *, saved, **kw):
+    """chunk_fwd_varlen that also leaves the backward's records and
+    checkpoints in `saved` (at least bwd_varlen_workspace_bytes(...) bytes),
+    for chunk_bwd_varlen_saved on the same inputs."""
+    return chunk_fwd_varlen(q, k, v, alpha, eta, cu_seqlens, variant, workspace=saved, _save=True,
+                            **kw)
 
 
 def decode_step(S, k_cache, q, k, v, alpha, eta, variant, *, eps=1e-6, o=None, stream=None,

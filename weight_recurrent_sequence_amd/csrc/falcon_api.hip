@@ -334,14 +334,19 @@ size_t bwd_extra_bytes(int BH, int T, int dk, int chunk, int Wv) {
 // T steps) or of falcon_chunk_fwd_varlen (cu: packed, T = max_seqlen),
 // arguments already checked.  `fwd` is the forward's workspace size, whose
 // layout (records, feature-map copies, packed schedule) the forward re-run
-// uses as it stands.
+// uses as it stands.  mode 0: re-run the forward with checkpoints, then the
+// backward; mode 1: only the forward, with its outputs o / S_final and the
+// checkpoints kept in the workspace; mode 2: only the backward, from a
+// workspace that a mode-1 call on the same inputs filled.
+enum BwdMode { kRecompute = 0, kSaveOnly = 1, kFromSaved = 2 };
 int chunk_bwd_run(const void* q, const void* k, const void* v, const float* alpha,
                   const float* eta, const float* S0, const void* k_prev, const void* v_prev,
                   const void* d_o, const float* dS_final, void* dq, void* dk, void* dv,
                   float* dalpha, float* deta, float* dS0, void* dk_prev, void* dv_prev,
                   const int* cu, int BH, int H, int Ttot, int T, int dk_, int dt, int var,
                   int window, int chunk, float eps, void* workspace, size_t fwd, size_t rec,
-                  size_t phi_rows, size_t order_off, hipStream_t stream) {
+                  size_t phi_rows, size_t order_off, hipStream_t stream, int mode = kRecompute,
+                  void* o = nullptr, float* S_final = nullptr) {
     int base = 0, lag = 1, phi = 0;
     split_variant(var, &base, &lag, &phi);
     const int Wv = norm_of(base) == falcon::kNormWindow ? window : 1;
@@ -367,8 +372,8 @@ int chunk_bwd_run(const void* q, const void* k, const void* v, const float* alph
     a.S0 = S0;
     a.k_prev = k_prev;
     a.v_prev = v_prev;
-    a.o = nullptr;
-    a.S_final = nullptr;
+    a.o = o;
+    a.S_final = S_final;
     a.BH = BH;
     a.T = T;
     a.cu = cu;
@@ -384,10 +389,11 @@ int chunk_bwd_run(const void* q, const void* k, const void* v, const float* alph
     a.eps = eps;
     a.ck_s = ck_s;
     a.ck_d = ck_d;
-    if (T > 0) {
+    if (mode != kFromSaved && (T > 0 || S_final)) {
         hipError_t e = falcon::launch_chunk(a, dt, dk_, chunk, is_delta(base), workspace, stream);
         if (e != hipSuccess) return FALCON_ERR_HIP;
     }
+    if (mode == kSaveOnly) return FALCON_OK;
 
     falcon::BwdArgs b;
     b.q = phi ? a.qphi : q;
@@ -519,6 +525,129 @@ int falcon_chunk_bwd_varlen(const void* q, const void* k, const void* v, const f
                          var, window, chunk, eps, workspace, fwd, rec, (size_t)N * H * max_seqlen,
                          falcon_chunk_fwd_workspace(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk),
                          stream);
+}
+
+int falcon_chunk_fwd_save(const void* q, const void* k, const void* v, const float* alpha,
+                          const float* eta, const float* S0, const void* k_prev, const void* v_prev,
+                          void* o, float* S_final, int B, int H, int T, int dk_, int dv_,
+                          falcon_dtype dt, falcon_variant var, int window, int chunk, float eps,
+                          void* saved, size_t saved_bytes, hipStream_t stream) {
+    int st = check_chunk(q, k, v, alpha, eta, S0, k_prev, v_prev, o, S_final, B, H, T, dk_, dv_,
+                         dt, var, window, chunk, eps);
+    if (st != FALCON_OK) return st;
+    int base = 0, lag = 1, phi = 0;
+    split_variant(var, &base, &lag, &phi);
+    if (!falcon::chunk_bwd_supported((int)dt, dk_, chunk, norm_of(base), window))
+        return FALCON_ERR_UNSUPPORTED;
+    const size_t need = falcon_chunk_bwd_workspace(B, H, T, dk_, dv_, dt, var, window, chunk);
+    if (need > 0 && (saved == nullptr || saved_bytes < need)) return FALCON_ERR_WORKSPACE;
+    if (T == 0 && S_final == nullptr) return FALCON_OK;
+    const int BH = B * H;
+    const size_t fwd = falcon_chunk_fwd_workspace(B, H, T, dk_, dv_, dt, var, window, chunk);
+    const size_t rec = align256(falcon::chunk_workspace_bytes(BH, T, (int)dt, chunk, window,
+                                                              norm_of(base), is_delta(base)));
+    return chunk_bwd_run(q, k, v, alpha, eta, S0, k_prev, v_prev, nullptr, nullptr, nullptr, nullptr,
+                         nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, BH, H, T, T,
+                         dk_, (int)dt, var, window, chunk, eps, saved, fwd, rec, (size_t)BH * T, 0,
+                         stream, kSaveOnly, o, S_final);
+}
+
+int falcon_chunk_bwd_saved(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* eta, const float* S0, const void* k_prev,
+                           const void* v_prev, const void* d_o, const float* dS_final, void* dq,
+                           void* dk, void* dv, float* dalpha, float* deta, float* dS0,
+                           void* dk_prev, void* dv_prev, int B, int H, int T, int dk_, int dv_,
+                           falcon_dtype dt, falcon_variant var, int window, int chunk, float eps,
+                           void* saved, size_t saved_bytes, hipStream_t stream) {
+    int st = check_chunk(q, k, v, alpha, eta, S0, k_prev, v_prev, d_o, dS_final, B, H, T, dk_,
+                         dv_, dt, var, window, chunk, eps);
+    if (st != FALCON_OK) return st;
+    st = check_bwd_outputs((int)dt, dk_, chunk, var, window, T > 0, dq, dk, dv, dalpha, deta, dS0,
+                           dk_prev, dv_prev);
+    if (st != FALCON_OK) return st;
+    const size_t need = falcon_chunk_bwd_workspace(B, H, T, dk_, dv_, dt, var, window, chunk);
+    if (need > 0 && (saved == nullptr || saved_bytes < need)) return FALCON_ERR_WORKSPACE;
+    if (T == 0 && dS0 == nullptr && dk_prev == nullptr && dv_prev == nullptr) return FALCON_OK;
+    int base = 0, lag = 1, phi = 0;
+    split_variant(var, &base, &lag, &phi);
+    const int BH = B * H;
+    const size_t fwd = falcon_chunk_fwd_workspace(B, H, T, dk_, dv_, dt, var, window, chunk);
+    const size_t rec = align256(falcon::chunk_workspace_bytes(BH, T, (int)dt, chunk, window,
+                                                              norm_of(base), is_delta(base)));
+    return chunk_bwd_run(q, k, v, alpha, eta, S0, k_prev, v_prev, d_o, dS_final, dq, dk, dv, dalpha,
+                         deta, dS0, dk_prev, dv_prev, nullptr, BH, H, T, T, dk_, (int)dt, var, window,
+                         chunk, eps, saved, fwd, rec, (size_t)BH * T, 0, stream, kFromSaved);
+}
+
+int falcon_chunk_fwd_varlen_save(const void* q, const void* k, const void* v, const float* alpha,
+                                 const float* eta, const float* S0, const void* k_prev,
+                                 const void* v_prev, void* o, float* S_final,
+                                 const int* cu_seqlens, int N, int H, int total_T, int max_seqlen,
+                                 int dk_, int dv_, falcon_dtype dt, falcon_variant var, int window,
+                                 int chunk, float eps, void* saved, size_t saved_bytes,
+                                 hipStream_t stream) {
+    int st = check_chunk(q, k, v, alpha, eta, S0, k_prev, v_prev, o, S_final, N, H, max_seqlen,
+                         dk_, dv_, dt, var, window, chunk, eps);
+    if (st != FALCON_OK) return st;
+    if (total_T < 0 || (long long)H * total_T > (1LL << 40) / (dk_ > 0 ? dk_ : 1))
+        return FALCON_ERR_SHAPE;
+    if (!cu_seqlens || !aligned4(cu_seqlens)) return cu_seqlens ? FALCON_ERR_UNSUPPORTED : FALCON_ERR_NULL;
+    const bool any = total_T > 0 && max_seqlen > 0;
+    if (any && (!q || !k || !v || !alpha || !eta || !o)) return FALCON_ERR_NULL;
+    int base = 0, lag = 1, phi = 0;
+    split_variant(var, &base, &lag, &phi);
+    if (!falcon::chunk_bwd_supported((int)dt, dk_, chunk, norm_of(base), window))
+        return FALCON_ERR_UNSUPPORTED;
+    const size_t need = falcon_chunk_bwd_varlen_workspace(N, H, max_seqlen, dk_, dv_, dt, var,
+                                                          window, chunk);
+    if (need > 0 && (saved == nullptr || saved_bytes < need)) return FALCON_ERR_WORKSPACE;
+    if (!any && S_final == nullptr) return FALCON_OK;
+    const int T = any ? max_seqlen : 0;
+    const size_t fwd = falcon_chunk_fwd_varlen_workspace(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk);
+    const size_t rec = align256(falcon::chunk_workspace_bytes(N * H, max_seqlen, (int)dt, chunk, window,
+                                                              norm_of(base), is_delta(base)));
+    return chunk_bwd_run(q, k, v, alpha, eta, S0, k_prev, v_prev, nullptr, nullptr, nullptr, nullptr,
+                         nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, cu_seqlens, N * H, H,
+                         total_T, T, dk_, (int)dt, var, window, chunk, eps, saved, fwd, rec,
+                         (size_t)N * H * max_seqlen,
+                         falcon_chunk_fwd_workspace(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk),
+                         stream, kSaveOnly, o, S_final);
+}
+
+int falcon_chunk_bwd_varlen_saved(const void* q, const void* k, const void* v, const float* alpha,
+                                  const float* eta, const float* S0, const void* k_prev,
+                                  const void* v_prev, const void* d_o, const float* dS_final,
+                                  void* dq, void* dk, void* dv, float* dalpha, float* deta,
+                                  float* dS0, void* dk_prev, void* dv_prev, const int* cu_seqlens,
+                                  int N, int H, int total_T, int max_seqlen, int dk_, int dv_,
+                                  falcon_dtype dt, falcon_variant var, int window, int chunk,
+                                  float eps, void* saved, size_t saved_bytes, hipStream_t stream) {
+    int st = check_chunk(q, k, v, alpha, eta, S0, k_prev, v_prev, d_o, dS_final, N, H, max_seqlen,
+                         dk_, dv_, dt, var, window, chunk, eps);
+    if (st != FALCON_OK) return st;
+    if (total_T < 0 || (long long)H * total_T > (1LL << 40) / (dk_ > 0 ? dk_ : 1))
+        return FALCON_ERR_SHAPE;
+    if (!cu_seqlens || !aligned4(cu_seqlens)) return cu_seqlens ? FALCON_ERR_UNSUPPORTED : FALCON_ERR_NULL;
+    const bool any = total_T > 0 && max_seqlen > 0;
+    if (any && (!q || !k || !v || !alpha || !eta || !d_o)) return FALCON_ERR_NULL;
+    st = check_bwd_outputs((int)dt, dk_, chunk, var, window, any, dq, dk, dv, dalpha, deta, dS0,
+                           dk_prev, dv_prev);
+    if (st != FALCON_OK) return st;
+    const size_t need = falcon_chunk_bwd_varlen_workspace(N, H, max_seqlen, dk_, dv_, dt, var,
+                                                          window, chunk);
+    if (need > 0 && (saved == nullptr || saved_bytes < need)) return FALCON_ERR_WORKSPACE;
+    if (!any && dS0 == nullptr && dk_prev == nullptr && dv_prev == nullptr) return FALCON_OK;
+    int base = 0, lag = 1, phi = 0;
+    split_variant(var, &base, &lag, &phi);
+    const int T = any ? max_seqlen : 0;
+    const size_t fwd = falcon_chunk_fwd_varlen_workspace(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk);
+    const size_t rec = align256(falcon::chunk_workspace_bytes(N * H, max_seqlen, (int)dt, chunk, window,
+                                                              norm_of(base), is_delta(base)));
+    return chunk_bwd_run(q, k, v, alpha, eta, S0, k_prev, v_prev, d_o, dS_final, dq, dk, dv, dalpha,
+                         deta, dS0, dk_prev, dv_prev, cu_seqlens, N * H, H, total_T, T, dk_, (int)dt,
+                         var, window, chunk, eps, saved, fwd, rec, (size_t)N * H * max_seqlen,
+                         falcon_chunk_fwd_workspace(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk),
+                         stream, kFromSaved);
 }
 
 const char* falcon_status_string(int status) {
