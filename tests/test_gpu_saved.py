@@ -120,3 +120,39 @@ def test_saved_pair_varlen_equals_recompute(dev, case):
     torch.cuda.synchronize()
     for k in GRADS:
         same(g_s[k], g_r[k], k)
+
+
+@pytest.mark.parametrize("case", [("F1", 128, 1), ("F3A", 64, 4)], ids=lambda c: "-".join(map(str, c)))
+def test_saved_pair_no_steps(dev, case):
+    """T = 0: the saving forward only copies S0 to S_final (no buffer is
+    needed), and the backward from it gives dS0 = dS_final and zero halo
+    gradients, as the recompute path does."""
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    variant, D, W = case
+    B, H = 2, 3
+    inp = I.make_chunk_inputs(B, H, 0, D, D, dtype="bf16", seed=1800 + D, window=W, S0_sd=0.3,
+                              halo=True)
+    t = inp.to_torch(dev)
+    kw = dict(window=W, S0=t["S0"], k_prev=t["k_prev"], v_prev=t["v_prev"])
+    assert fal.bwd_workspace_bytes(B, H, 0, D, D, fal.BF16, variant, W, 64) == 0
+    saved = torch.empty(0, dtype=torch.uint8, device=dev)
+    announce(f"chunk_fwd_save {variant} d{D} W{W} T0")
+    o_s, S_s = fal.chunk_fwd_save(t["q"], t["k"], t["v"], t["alpha"], t["eta"], variant,
+                                  saved=saved, **kw)
+    o_r, S_r = fal.chunk_fwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], variant, **kw)
+    torch.cuda.synchronize()
+    same(S_s, S_r, "S_final")
+    assert torch.equal(S_s, t["S0"])
+    _, dS = I.make_cotangents(B, H, 0, D, D, seed=1810)
+    d_o = torch.empty((B, H, 0, D), dtype=torch.bfloat16, device=dev)
+    dS = to_dev(dS, dev)
+    announce(f"chunk_bwd_saved {variant} d{D} W{W} T0")
+    g_s = fal.chunk_bwd_saved(t["q"], t["k"], t["v"], t["alpha"], t["eta"], d_o, variant,
+                              saved=saved, dS_final=dS, want_dk_prev=True, **kw)
+    g_r = fal.chunk_bwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], d_o, variant, dS_final=dS,
+                        want_dk_prev=True, **kw)
+    torch.cuda.synchronize()
+    for k in GRADS:
+        same(g_s[k], g_r[k], k)
+    assert torch.equal(g_s["dS0"], dS)
