@@ -1467,28 +1467,55 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
         // staged through registers (u is derived from x on the way); the
         // queries of tile it+1 are loaded during iteration it, a full
         // iteration before their use
-        if (!chain && ntl > 0) {
-            load_q(0);
-            load_xyr(0);
-            load_pg(0);
-            store_xyr(0);
-            if (ntl > 1) load_xyr(1);
-        }
-        lds_barrier();
-        for (int it = 0; it <= ntl; ++it) {
-            if (chain) {
-                if (it < ntl) chain_tile(it);
-            } else {
-                if (it >= 1) output_tile(it - 1);
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) pQa[kb] = pQb[kb];
-                if (it + 1 < ntl) load_q(it + 1);
-                if (it + 1 < ntl) store_xyr(it + 1);
-                if (it < ntl) store_pg(it & 1);
-                if (it + 2 < ntl) load_xyr(it + 2);
-                if (it + 1 < ntl) load_pg(it + 1);
+        auto out_first = [&]() __attribute__((always_inline)) {
+            if (ntl > 0) {
+                load_q(0);
+                load_xyr(0);
+                load_pg(0);
+                store_xyr(0);
+                if (ntl > 1) load_xyr(1);
             }
+        };
+        auto out_iter = [&](int it) __attribute__((always_inline)) {
+            if (it >= 1) output_tile(it - 1);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) pQa[kb] = pQb[kb];
+            if (it + 1 < ntl) load_q(it + 1);
+            if (it + 1 < ntl) store_xyr(it + 1);
+            if (it < ntl) store_pg(it & 1);
+            if (it + 2 < ntl) load_xyr(it + 2);
+            if (it + 1 < ntl) load_pg(it + 1);
+        };
+        if constexpr (DELTA) {
+            // One loop per role (same barriers), so the output waves'
+            // prefetch registers are not live in the recurrence waves' code,
+            // whose substitution needs them (F2 716 vs 746 us); the
+            // inner-product rule runs better with one shared loop.
+            if (chain) {
+                lds_barrier();
+                for (int it = 0; it <= ntl; ++it) {
+                    if (it < ntl) chain_tile(it);
+                    lds_barrier();
+                }
+            } else {
+                out_first();
+                lds_barrier();
+                for (int it = 0; it <= ntl; ++it) {
+                    out_iter(it);
+                    lds_barrier();
+                }
+            }
+        } else {
+            if (!chain) out_first();
             lds_barrier();
+            for (int it = 0; it <= ntl; ++it) {
+                if (chain) {
+                    if (it < ntl) chain_tile(it);
+                } else {
+                    out_iter(it);
+                }
+                lds_barrier();
+            }
         }
     } else {
         // Iteration it.  Output half: store the outputs of tile it-2, start
