@@ -74,8 +74,6 @@ __device__ __forceinline__ s16x4 col_write4(s16x4 x, f32x4 l1, f32x4 eta, float 
     return EBf16::pack(u);
 }
 
-// s_waitcnt vmcnt(0), leaving the other counters alone
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Key row of virtual row i of the tile starting at t0 (window 1): k_{t0+i-lag},
 // the halo before the sequence, zero outside.
@@ -102,10 +100,11 @@ __device__ __forceinline__ u32x4 key_piece(const bf* kg, const bf* kp, int W, in
 //                      substitution, dR to LDS, dS at the tile start.  No
 //                      loads: a wave that issues loads waits for its own
 //                      stores too (one counter), so the chain issues none.
-//   waves 4-7 (fill)   the LDS copies of tile it-1 (keys, queries, dO slice,
-//                      record), loaded through registers one iteration
-//                      ahead, and the row stores of dv for tile it+1 from the
-//                      chain's LDS dR.
+//   waves 4-7 (fill)   the row stores of dv for tile it+1 from the chain's
+//                      LDS dR, and the LDS copies of tile it-1 (keys,
+//                      queries, dO slice, record) filled directly from
+//                      memory (through registers for the first tiles, whose
+//                      keys reach into the halo).
 // Two LDS buffers by tile parity; one barrier per tile.
 // ---------------------------------------------------------------------------
 template <int D, int CV, bool DELTA>
@@ -230,19 +229,84 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdArgs a) {
     };
 
     if (!chain) {
-        // fill: tile ntl-1 into LDS, tile ntl-2 into registers, then per
-        // iteration it: tile it-1 into LDS, tile it-2 into registers, and
-        // dv of tile it+1 out of LDS
-        if (ntl > 0) {
-            load(ntl - 1);
-            store((ntl - 1) & 1);
-            if (ntl > 1) load(ntl - 2);
+        // fill: tile ntl-1 before the loop, then per iteration it: dv of tile
+        // it+1 out of LDS and tile it-1 into LDS.  Tiles whose keys lie in
+        // the sequence go straight to LDS (buffer_load ... lds, a 16-byte
+        // slot per lane, the slots' source offsets fixed relative to the
+        // tile, padding and rows past the end reading as zero), waited for
+        // before the barrier; the first tiles, whose keys reach into the halo,
+        // go through registers.
+        constexpr int SPX = LDX / 8, SPY = LDY / 8;
+        constexpr int NSX = CV * SPX, NSY = CV * SPY;
+        constexpr int NIX = (NSX + 63) / 64, NIY = (NSY + 63) / 64, NIR = (RPC + 63) / 64;
+        constexpr int MIX = (NIX + 3) / 4, MIY = (NIY + 3) / 4, MIR = (NIR + 3) / 4;
+        const int ow = wave & 3;
+        uint32_t dx[MIX], dq[MIX], dy[MIY], dr[MIR];
+#pragma unroll
+        for (int m = 0; m < MIX; ++m) {
+            const int k = 64 * (ow + 4 * m) + lane;
+            const int row = k / SPX, wi = k - row * SPX;
+            const int s = WIN ? row / Wv : row, w = WIN ? row - s * Wv : 0;
+            const bool in = k < NSX && wi < D / 8;
+            dx[m] = (in && row < NVR) ? (uint32_t)(((s - w - lag + W) * D + wi * 8) * 2) : kOob;
+            dq[m] = (in && row < Ct) ? (uint32_t)((row * D + wi * 8) * 2) : kOob;
         }
+#pragma unroll
+        for (int m = 0; m < MIY; ++m) {
+            const int k = 64 * (ow + 4 * m) + lane;
+            const int row = k / SPY, wi = k - row * SPY;
+            dy[m] = (k < NSY && wi < 8 && row < Ct) ? (uint32_t)((row * D + wi * 8) * 2) : kOob;
+        }
+#pragma unroll
+        for (int m = 0; m < MIR; ++m) {
+            const int k = 64 * (ow + 4 * m) + lane;
+            dr[m] = k < RPC ? (uint32_t)(k * 16) : kOob;
+        }
+        const uint32_t sm_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) Smem*)&sm;
+        auto dma = [&](int tile) __attribute__((always_inline)) {
+            const int t0 = tile * Ct, b = tile & 1;
+            const u32x4 rx = make_desc(kg + (size_t)(t0 - W) * D, (int64_t)(T_ - t0 + W) * D * 2);
+            const u32x4 rq = make_desc(qg + (size_t)t0 * D, (int64_t)(T_ - t0) * D * 2);
+            const u32x4 ro = make_desc(dog + (size_t)t0 * D, (int64_t)(T_ - t0) * D * 2);
+            const u32x4 rr = make_desc(recg + (size_t)tile * R::kBytes, (int64_t)R::kBytes);
+            const uint32_t xb = sm_lds + (uint32_t)(offsetof(Smem, X) + sizeof(sm.X[0]) * b);
+            const uint32_t qb = sm_lds + (uint32_t)(offsetof(Smem, Q) + sizeof(sm.Q[0]) * b);
+            const uint32_t ob = sm_lds + (uint32_t)(offsetof(Smem, dO) + sizeof(sm.dO[0]) * b);
+            const uint32_t rb = sm_lds + (uint32_t)(offsetof(Smem, rec) + sizeof(sm.rec[0]) * b);
+#pragma unroll
+            for (int m = 0; m < MIX; ++m) {
+                const int i = ow + 4 * m;
+                if (i < NIX && 64 * i + lane < NSX) {
+                    buf_load16_lds(rx, xb + 1024 * i, dx[m]);
+                    buf_load16_lds(rq, qb + 1024 * i, dq[m]);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < MIY; ++m) {
+                const int i = ow + 4 * m;
+                if (i < NIY && 64 * i + lane < NSY) buf_load16_lds(ro, ob + 1024 * i, dy[m]);
+            }
+#pragma unroll
+            for (int m = 0; m < MIR; ++m) {
+                const int i = ow + 4 * m;
+                if (i < NIR && 64 * i + lane < RPC) buf_load16_lds(rr, rb + 1024 * i, dr[m]);
+            }
+        };
+        auto fill = [&](int tile) __attribute__((always_inline)) {
+            if (tile * Ct >= W) {
+                dma(tile);
+            } else {
+                load(tile);
+                store(tile & 1);
+            }
+        };
+        if (ntl > 0) fill(ntl - 1);
+        wait_vm_all();
         lds_barrier();
         for (int it = ntl - 1; it >= 0; --it) {
-            if (it >= 1) store((it - 1) & 1);
-            if (it >= 2) load(it - 2);
             if (it + 1 < ntl) store_dv(it + 1);
+            if (it >= 1) fill(it - 1);
+            wait_vm_all();
             lds_barrier();
         }
         if (ntl > 0) store_dv(0);

@@ -801,8 +801,6 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs a, const void
 // tile.
 // ---------------------------------------------------------------------------
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr int kRawBufferFlags = 0x00020000;  // descriptor word 3 of a raw gfx9 buffer
-constexpr uint32_t kOob = 0x80000000u;       // an offset beyond every record count used here
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
     const int n = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFF0 ? 0x7FFFFFF0 : (int)bytes);
@@ -815,38 +813,6 @@ __device__ __forceinline__ s16x4 buf_load8(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(s16x4, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
 }
 
-// Descriptor words of a raw buffer (base, stride 0, size in bytes, flags),
-// wave-uniform, for the direct-to-LDS fill below.
-__device__ __forceinline__ u32x4 make_desc(const void* base, int64_t bytes) {
-    const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0x7FFFFFF0 ? 0x7FFFFFF0u : (uint32_t)bytes);
-    const uint64_t p = reinterpret_cast<uint64_t>(base);
-    u32x4 d;
-    d[0] = __builtin_amdgcn_readfirstlane((uint32_t)p);
-    d[1] = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xFFFFu);
-    d[2] = __builtin_amdgcn_readfirstlane(n);
-    d[3] = (uint32_t)kRawBufferFlags;
-    return d;
-}
-// 16 bytes per lane from a buffer straight into LDS: lane l writes
-// lds + 16 l (lds is wave-uniform); lanes whose exec bit is off write nothing,
-// out-of-range offsets write zeros.  Completion is counted by vmcnt and the
-// caller waits for it (wait_vm_all) before the barrier that publishes the
-// tile.  The instruction is issued from inline assembly on purpose: the
-// compiler cannot tell which LDS bytes such a fill writes, and for the
-// builtin form it waits for every fill in flight before the wave's next LDS
-// read, which would serialize each fill's latency with the arithmetic it is
-// meant to overlap.  The asm has no outputs; the fills' targets are read only
-// after the explicit wait and a barrier.
-// `lds` is the wave's LDS byte address (it goes to M0).
-__device__ __forceinline__ void buf_load16_lds(u32x4 d, uint32_t lds, uint32_t off) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :
-                 : "v"(off), "s"(d), "{m0}"(m0)
-                 : "memory");
-}
-// s_waitcnt vmcnt(0), leaving the other counters alone
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // s_waitcnt vmcnt(2): all but the two most recent vector memory operations
 __device__ __forceinline__ void wait_vm_2() { __builtin_amdgcn_s_waitcnt(0x0F72); }
 // 4 bytes per lane from a buffer into LDS at lds + 4 l (as buf_load16_lds).
