@@ -116,6 +116,7 @@ struct BScanSmem {
     bf dO[2][CV][LDY];
     bf dR[2][CV][LDY];
     alignas(16) char rec[2][R::kBytes];
+    uint32_t pf[4][64];  // landing area of the fill waves' L2 warm-up loads (never read)
 };
 
 template <int D, int CV, bool DELTA, bool WIN, bool COL>
@@ -300,15 +301,52 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdArgs a) {
                 store(tile & 1);
             }
         };
+        // L2 warm-up of the tile after next (tile - 1, going down): two 4-byte
+        // LDS-DMA loads per lane, one lane per 128-byte line of its keys,
+        // queries, dO slice and record, landing in a scratch area nothing
+        // reads.  They are the wave's two most recent loads every iteration
+        // (offsets past the data read nothing), so the wait before the
+        // barrier (vmcnt(2)) covers the fills and lets these run on.
+        const uint32_t pfl = sm_lds + (uint32_t)(offsetof(Smem, pf) + 256 * ow);
+        auto warm = [&](int tile) __attribute__((always_inline)) {
+            const int t0 = tile * Ct;
+            const bool ok = tile >= 0 && t0 >= W;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                // 0-2: keys, 3-4: queries, 5: dO slice, 6-7: record (wave-uniform)
+                const int inst = 2 * __builtin_amdgcn_readfirstlane(ow) + j;
+                u32x4 d;
+                uint32_t off = kOob;
+                if (inst <= 2) {
+                    d = make_desc(kg + (size_t)(ok ? t0 - W : 0) * D, ok ? (int64_t)(T_ - t0 + W) * D * 2 : 0);
+                    const uint32_t o = (uint32_t)(inst * 64 + lane) * 128;
+                    if (ok && o < (uint32_t)((Ct + W) * D * 2)) off = o;
+                } else if (inst <= 4) {
+                    d = make_desc(qg + (size_t)(ok ? t0 : 0) * D, ok ? (int64_t)(T_ - t0) * D * 2 : 0);
+                    const uint32_t o = (uint32_t)((inst - 3) * 64 + lane) * 128;
+                    if (ok && o < (uint32_t)(Ct * D * 2)) off = o;
+                } else if (inst == 5) {
+                    d = make_desc(dog + (size_t)(ok ? t0 : 0) * D, ok ? (int64_t)(T_ - t0) * D * 2 : 0);
+                    if (ok && lane < Ct) off = (uint32_t)lane * D * 2;
+                } else {
+                    d = make_desc(recg + (size_t)(ok ? tile : 0) * R::kBytes, ok ? (int64_t)R::kBytes : 0);
+                    const uint32_t o = (uint32_t)((inst - 6) * 64 + lane) * 128;
+                    if (ok && o < (uint32_t)R::kBytes) off = o;
+                }
+                buf_load4_lds(d, pfl, off);
+            }
+        };
         if (ntl > 0) fill(ntl - 1);
         wait_vm_all();
         lds_barrier();
         for (int it = ntl - 1; it >= 0; --it) {
             if (it + 1 < ntl) store_dv(it + 1);
             if (it >= 1) fill(it - 1);
-            wait_vm_all();
+            warm(it - 2);
+            wait_vm_2();
             lds_barrier();
         }
+        wait_vm_all();
         if (ntl > 0) store_dv(0);
         return;
     }

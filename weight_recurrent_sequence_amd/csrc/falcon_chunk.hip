@@ -813,18 +813,6 @@ __device__ __forceinline__ s16x4 buf_load8(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(s16x4, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
 }
 
-// s_waitcnt vmcnt(2): all but the two most recent vector memory operations
-__device__ __forceinline__ void wait_vm_2() { __builtin_amdgcn_s_waitcnt(0x0F72); }
-// 4 bytes per lane from a buffer into LDS at lds + 4 l (as buf_load16_lds).
-__device__ __forceinline__ void buf_load4_lds(u32x4 d, uint32_t lds, uint32_t off) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
-    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
-                 :
-                 : "v"(off), "s"(d), "{m0}"(m0)
-                 : "memory");
-}
-
-
 template <int D, int CV, bool DELTA, bool COL, bool WIN>
 struct PassSmem {
     using R = Rec<EBf16, CV, DELTA>;

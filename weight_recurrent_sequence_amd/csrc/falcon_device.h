@@ -157,6 +157,17 @@ __device__ __forceinline__ void buf_load16_lds(u32x4 d, uint32_t lds, uint32_t o
 }
 // s_waitcnt vmcnt(0), leaving the other counters alone
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(2): all but the two most recent vector memory operations
+__device__ __forceinline__ void wait_vm_2() { __builtin_amdgcn_s_waitcnt(0x0F72); }
+// 4 bytes per lane from a buffer into LDS at lds + 4 l (as buf_load16_lds).
+__device__ __forceinline__ void buf_load4_lds(u32x4 d, uint32_t lds, uint32_t off) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :
+                 : "v"(off), "s"(d), "{m0}"(m0)
+                 : "memory");
+}
+
 // Compile-time loop: f(std::integral_constant<int, i>) for i = 0..N-1, so that
 // register arrays are only ever indexed by constants.
 template <int I, int N, class F>
