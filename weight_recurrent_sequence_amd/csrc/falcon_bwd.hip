@@ -699,9 +699,11 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
     constexpr int NSP = 32 * CPR / 256, NDP = 32 * (CV / 8) / 256, NRP = CV * 4 / 256;
     // not unrolled: an unrolled loop would hoist every quarter's loads to the
     // top (the barriers order LDS only) and run out of registers
-#pragma unroll 1
-    for (int qv = 0; qv < NQ; ++qv) {
-        u32x4 pS[NSP], pG[NSP], pD[NDP], pR[NRP], pO[NRP];
+    // Quarter qv's pieces are loaded while quarter qv-1 is computed: the
+    // registers that carried quarter qv-1 into LDS take quarter qv's loads
+    // right after.
+    u32x4 pS[NSP], pG[NSP], pD[NDP], pR[NRP], pO[NRP];
+    auto load_q = [&](int qv) __attribute__((always_inline)) {
         // the checkpoints are stored in 16-column blocks ([block][v][16]): piece c
         // is half c % 2 of row c / 2 % 32 of the quarter in block c / 64, and
         // consecutive pieces are consecutive 16 bytes
@@ -725,6 +727,10 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
             pR[it] = rin ? *reinterpret_cast<const u32x4*>(dRg + (size_t)i * D + 32 * qv + col) : zero_u4();
             pO[it] = oin ? *reinterpret_cast<const u32x4*>(dog + (size_t)i * D + 32 * qv + col) : zero_u4();
         }
+    };
+    load_q(0);
+#pragma unroll 1
+    for (int qv = 0; qv < NQ; ++qv) {
         lds_barrier();  // the previous quarter's operands are consumed
 #pragma unroll
         for (int it = 0; it < NSP; ++it) {
@@ -747,6 +753,7 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
             *reinterpret_cast<u32x4*>(&sm.u.q.dRq[i][col]) = pR[it];
             *reinterpret_cast<u32x4*>(&sm.u.q.dOq[i][col]) = pO[it];
         }
+        if (qv + 1 < NQ) load_q(qv + 1);
         lds_barrier();
         const bf* Dq = &sm.u.q.Dq[0][0];
         {
