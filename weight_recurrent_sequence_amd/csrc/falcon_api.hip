@@ -91,7 +91,7 @@ size_t falcon_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, falcon_dt
     int base = 0, lag = 1, phi = 0;
     split_variant(var, &base, &lag, &phi);
     const size_t rec = align256(falcon::chunk_workspace_bytes(B * H, T, (int)dt, chunk, window,
-                                                              norm_of(base), is_delta(base)));
+                                                              norm_of(base), is_delta(base), dk));
     if (rec == 0 || phi == 0) return rec;
     return rec + phi_bytes((size_t)B * H * T, (size_t)B * H, window, dk, dt);
 }
@@ -127,7 +127,7 @@ int falcon_chunk_fwd(const void* q, const void* k, const void* v, const float* a
     if (phi && need > 0)
         set_phi_buffers(a, workspace, (size_t)B * H * T, B * H, window, dk, dt,
                         align256(falcon::chunk_workspace_bytes(B * H, T, (int)dt, chunk, window,
-                                                               norm_of(base), is_delta(base))));
+                                                               norm_of(base), is_delta(base), dk)));
     a.q = q;
     a.k = k;
     a.v = v;
@@ -197,7 +197,7 @@ int falcon_chunk_fwd_varlen(const void* q, const void* k, const void* v, const f
         set_phi_buffers(a, workspace, (size_t)N * H * max_seqlen, N * H, window, dk, dt,
                         align256(falcon::chunk_workspace_bytes(N * H, max_seqlen, (int)dt, chunk,
                                                                window, norm_of(base),
-                                                               is_delta(base))));
+                                                               is_delta(base), dk)));
     a.q = q;
     a.k = k;
     a.v = v;
@@ -473,7 +473,7 @@ int falcon_chunk_bwd(const void* q, const void* k, const void* v, const float* a
     const int BH = B * H;
     const size_t fwd = falcon_chunk_fwd_workspace(B, H, T, dk_, dv_, dt, var, window, chunk);
     const size_t rec = align256(falcon::chunk_workspace_bytes(BH, T, (int)dt, chunk, window,
-                                                              norm_of(base), is_delta(base)));
+                                                              norm_of(base), is_delta(base), dk_));
     return chunk_bwd_run(q, k, v, alpha, eta, S0, k_prev, v_prev, d_o, dS_final, dq, dk, dv, dalpha,
                          deta, dS0, dk_prev, dv_prev, nullptr, BH, H, T, T, dk_, (int)dt, var, window,
                          chunk, eps, workspace, fwd, rec, (size_t)BH * T, 0, stream);
@@ -519,7 +519,7 @@ int falcon_chunk_bwd_varlen(const void* q, const void* k, const void* v, const f
     const int T = any ? max_seqlen : 0;
     const size_t fwd = falcon_chunk_fwd_varlen_workspace(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk);
     const size_t rec = align256(falcon::chunk_workspace_bytes(N * H, max_seqlen, (int)dt, chunk, window,
-                                                              norm_of(base), is_delta(base)));
+                                                              norm_of(base), is_delta(base), dk_));
     return chunk_bwd_run(q, k, v, alpha, eta, S0, k_prev, v_prev, d_o, dS_final, dq, dk, dv, dalpha,
                          deta, dS0, dk_prev, dv_prev, cu_seqlens, N * H, H, total_T, T, dk_, (int)dt,
                          var, window, chunk, eps, workspace, fwd, rec, (size_t)N * H * max_seqlen,
@@ -545,7 +545,7 @@ int falcon_chunk_fwd_save(const void* q, const void* k, const void* v, const flo
     const int BH = B * H;
     const size_t fwd = falcon_chunk_fwd_workspace(B, H, T, dk_, dv_, dt, var, window, chunk);
     const size_t rec = align256(falcon::chunk_workspace_bytes(BH, T, (int)dt, chunk, window,
-                                                              norm_of(base), is_delta(base)));
+                                                              norm_of(base), is_delta(base), dk_));
     return chunk_bwd_run(q, k, v, alpha, eta, S0, k_prev, v_prev, nullptr, nullptr, nullptr, nullptr,
                          nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, BH, H, T, T,
                          dk_, (int)dt, var, window, chunk, eps, saved, fwd, rec, (size_t)BH * T, 0,
@@ -573,7 +573,7 @@ int falcon_chunk_bwd_saved(const void* q, const void* k, const void* v, const fl
     const int BH = B * H;
     const size_t fwd = falcon_chunk_fwd_workspace(B, H, T, dk_, dv_, dt, var, window, chunk);
     const size_t rec = align256(falcon::chunk_workspace_bytes(BH, T, (int)dt, chunk, window,
-                                                              norm_of(base), is_delta(base)));
+                                                              norm_of(base), is_delta(base), dk_));
     return chunk_bwd_run(q, k, v, alpha, eta, S0, k_prev, v_prev, d_o, dS_final, dq, dk, dv, dalpha,
                          deta, dS0, dk_prev, dv_prev, nullptr, BH, H, T, T, dk_, (int)dt, var, window,
                          chunk, eps, saved, fwd, rec, (size_t)BH * T, 0, stream, kFromSaved);
@@ -605,7 +605,7 @@ int falcon_chunk_fwd_varlen_save(const void* q, const void* k, const void* v, co
     const int T = any ? max_seqlen : 0;
     const size_t fwd = falcon_chunk_fwd_varlen_workspace(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk);
     const size_t rec = align256(falcon::chunk_workspace_bytes(N * H, max_seqlen, (int)dt, chunk, window,
-                                                              norm_of(base), is_delta(base)));
+                                                              norm_of(base), is_delta(base), dk_));
     return chunk_bwd_run(q, k, v, alpha, eta, S0, k_prev, v_prev, nullptr, nullptr, nullptr, nullptr,
                          nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, cu_seqlens, N * H, H,
                          total_T, T, dk_, (int)dt, var, window, chunk, eps, saved, fwd, rec,
@@ -642,7 +642,7 @@ int falcon_chunk_bwd_varlen_saved(const void* q, const void* k, const void* v, c
     const int T = any ? max_seqlen : 0;
     const size_t fwd = falcon_chunk_fwd_varlen_workspace(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk);
     const size_t rec = align256(falcon::chunk_workspace_bytes(N * H, max_seqlen, (int)dt, chunk, window,
-                                                              norm_of(base), is_delta(base)));
+                                                              norm_of(base), is_delta(base), dk_));
     return chunk_bwd_run(q, k, v, alpha, eta, S0, k_prev, v_prev, d_o, dS_final, dq, dk, dv, dalpha,
                          deta, dS0, dk_prev, dv_prev, cu_seqlens, N * H, H, total_T, T, dk_, (int)dt,
                          var, window, chunk, eps, saved, fwd, rec, (size_t)N * H * max_seqlen,

@@ -833,7 +833,7 @@ struct PassSmem {
 };
 
 template <int D, int CV, bool DELTA, bool COL, bool WIN>
-__global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a, const void* ws,
+__global__ __launch_bounds__(768) void chunk_pass_kernel(ChunkArgs a, const void* ws,
                                                                      int ntiles) {
     using E = EBf16;
     using T = uint16_t;
@@ -847,14 +847,13 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
     constexpr int RCH = Smem::RECB / 16, RFC = Smem::RECF / 16;
     constexpr int NRL = (RCH + 255) / 256;
     constexpr int PCH = Smem::PGB / 16, PFC = R::npblk(WIN) * 32;
-    constexpr int NPL = (PCH + 255) / 256;
     constexpr bool QG = COL;  // queries as register fragments from global memory
     __shared__ Smem sm;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4,
               lr = lane & 15;
     const bool chain = wave < 4;
-    const bool filler = !COL && wave >= 8;
+    const bool filler = wave >= 8;
     const int cw = wave & 3;  // value-column block (16 columns) of this wave
     const int blk = blockIdx.x;
     const int xcd = blk & 7;
@@ -923,8 +922,6 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
 
     u32x4 px[NXL], py[NYL], pr[NRL];
     u32x4 pxh[NXL], pyh[NYL];  // halo rows of the first tiles
-    float pl1[COL ? NXL : 1], per[COL ? NXL : 1];
-    u32x4 ppg[NPL];
     // QG: the queries of one 16-row block (rows 16 (cw % NB) ..) as B fragments,
     // pQa for the tile being output and pQb for the next one
     Frag pQa[QG ? KB : 1], pQb[QG ? KB : 1];
@@ -967,15 +964,6 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
             pr[it] = *reinterpret_cast<const u32x4*>(
                 rt + (rc < RFC ? (size_t)rc * 16 : R::kScalBytes + (size_t)(rc - RFC) * 16));
         }
-        if constexpr (COL) {
-            const float* sc = reinterpret_cast<const float*>(rt + R::kScalBytes);
-#pragma unroll
-            for (int it = 0; it < NXL; ++it) {
-                const int i = min((otid + 256 * it) / CPR, CV - 1);
-                pl1[it] = sc[3 * CV + i];
-                per[it] = sc[4 * CV + i];
-            }
-        }
     };
     // queries of `tile` (per-column rule) as register fragments of the
     // wave's own row block into pQb
@@ -987,24 +975,6 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
                 pQb[kb] = buf_load8(rq, t < Ct ? (uint32_t)((t * D + 16 * kb + 4 * grp) * 2) : kOob);
-        }
-    };
-    // output-side record pieces of `tile` (P fragments, query decays)
-    auto load_pg = [&](int tile) __attribute__((always_inline)) {
-        const char* rt = recg + (size_t)tile * R::kBytes;
-#pragma unroll
-        for (int it = 0; it < NPL; ++it) {
-            const int pc = min(otid + 256 * it, PCH - 1);
-            ppg[it] = *reinterpret_cast<const u32x4*>(
-                rt + (pc < PFC ? R::kP * 2 + (size_t)pc * 16
-                               : R::kScalBytes + 2 * CV * 4 + (size_t)(pc - PFC) * 16));
-        }
-    };
-    auto store_pg = [&](int b) __attribute__((always_inline)) {
-#pragma unroll
-        for (int it = 0; it < NPL; ++it) {
-            const int pc = otid + 256 * it;
-            if (pc < PCH) reinterpret_cast<u32x4*>(sm.pg[b])[pc] = ppg[it];
         }
     };
     auto store_xyr = [&](int tile) __attribute__((always_inline)) {
@@ -1021,20 +991,6 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
             if (c < CV * CPR) {
                 const int i = c / CPR, col = (c % CPR) * 8;
                 *reinterpret_cast<u32x4*>(&sm.X[b][i][col]) = px[it];
-                if constexpr (COL) {
-                    // u = eta x / (|x| ||x||_1 + eps), elementwise
-                    const T* e = reinterpret_cast<const T*>(&px[it]);
-                    u32x4 outv;
-                    T* out = reinterpret_cast<T*>(&outv);
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        const float x = E::to_f(e[u]);
-                        const float den = fabsf(x) * pl1[it] + eps;
-                        // hardware reciprocal (1 ulp): u is rounded to bf16 next
-                        out[u] = E::from_f(den > 0.f ? per[it] * x * __builtin_amdgcn_rcpf(den) : 0.f);
-                    }
-                    *reinterpret_cast<u32x4*>(&sm.QU[b][i][col]) = outv;
-                }
             }
         }
 #pragma unroll
@@ -1331,7 +1287,7 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
     constexpr int MIX = (NIX + 3) / 4, MIY = (NIY + 3) / 4, MIR = (NIR + 3) / 4, MIP = (NIP + 3) / 4;
     uint32_t dx[MIX], dq[MIX], dy[MIY], dr[MIR], dp[MIP];
     const int ow = cw;  // index of this wave within its role
-    if constexpr (!COL) {
+    {
 #pragma unroll
         for (int m = 0; m < MIX; ++m) {
             const int k = 64 * (ow + 4 * m) + lane;
@@ -1370,6 +1326,20 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
     auto lds_of = [&](size_t field, size_t bytes_per_buffer, int b) __attribute__((always_inline)) {
         return sm_lds + (uint32_t)(field + bytes_per_buffer * b);
     };
+    // per-column rule: the tile's write vectors (rows as the query slots'
+    // rows, from the intra-chunk kernel's copy) into the query/u buffer
+    auto dma_u = [&](int tile) __attribute__((always_inline)) {
+        if constexpr (COL) {
+            const u32x4 ru = make_desc(static_cast<const T*>(a.uws) + ((size_t)bh * ntiles + tile) * CV * D,
+                                       (int64_t)CV * D * 2);
+            const uint32_t ub = lds_of(offsetof(Smem, QU), sizeof(sm.QU[0]), tile & 1);
+#pragma unroll
+            for (int m = 0; m < MIX; ++m) {
+                const int i = ow + 4 * m;
+                if (i < NIX && 64 * i + lane < NSX) buf_load16_lds(ru, ub + 1024 * i, dq[m]);
+            }
+        }
+    };
     auto dma_xr = [&](int tile) __attribute__((always_inline)) {
         const int t0 = tile * Ct, b = tile & 1;
         const u32x4 rx = make_desc(kg + (size_t)(t0 - W) * D, (int64_t)(T_ - t0 + W) * D * 2);
@@ -1381,6 +1351,7 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
             const int i = ow + 4 * m;
             if (i < NIX && 64 * i + lane < NSX) buf_load16_lds(rx, xb + 1024 * i, dx[m]);
         }
+        dma_u(tile);
 #pragma unroll
         for (int m = 0; m < MIR; ++m) {
             const int i = ow + 4 * m;
@@ -1403,10 +1374,12 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
         const u32x4 rr = make_desc(recg + (size_t)tile * R::kBytes, R::kBytes);
         const uint32_t qb = lds_of(offsetof(Smem, QU), sizeof(sm.QU[0]), b);
         const uint32_t pb = lds_of(offsetof(Smem, pg), sizeof(sm.pg[0]), b);
+        if constexpr (!COL) {  // the per-column rule's queries are register fragments
 #pragma unroll
-        for (int m = 0; m < MIX; ++m) {
-            const int i = ow + 4 * m;
-            if (i < NIX && 64 * i + lane < NSX) buf_load16_lds(rq, qb + 1024 * i, dq[m]);
+            for (int m = 0; m < MIX; ++m) {
+                const int i = ow + 4 * m;
+                if (i < NIX && 64 * i + lane < NSX) buf_load16_lds(rq, qb + 1024 * i, dq[m]);
+            }
         }
 #pragma unroll
         for (int m = 0; m < MIP; ++m) {
@@ -1417,61 +1390,7 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
 
     // ---- pipeline: the chain works on tile it while the output half
     // finishes tile it-1 ----
-    if constexpr (COL) {
-        // staged through registers (u is derived from x on the way); the
-        // queries of tile it+1 are loaded during iteration it, a full
-        // iteration before their use
-        auto out_first = [&]() __attribute__((always_inline)) {
-            if (ntl > 0) {
-                load_q(0);
-                load_xyr(0);
-                load_pg(0);
-                store_xyr(0);
-                if (ntl > 1) load_xyr(1);
-            }
-        };
-        auto out_iter = [&](int it) __attribute__((always_inline)) {
-            if (it >= 1) output_tile(it - 1);
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) pQa[kb] = pQb[kb];
-            if (it + 1 < ntl) load_q(it + 1);
-            if (it + 1 < ntl) store_xyr(it + 1);
-            if (it < ntl) store_pg(it & 1);
-            if (it + 2 < ntl) load_xyr(it + 2);
-            if (it + 1 < ntl) load_pg(it + 1);
-        };
-        if constexpr (DELTA) {
-            // One loop per role (same barriers), so the output waves'
-            // prefetch registers are not live in the recurrence waves' code,
-            // whose substitution needs them (F2 716 vs 746 us); the
-            // inner-product rule runs better with one shared loop.
-            if (chain) {
-                lds_barrier();
-                for (int it = 0; it <= ntl; ++it) {
-                    if (it < ntl) chain_tile(it);
-                    lds_barrier();
-                }
-            } else {
-                out_first();
-                lds_barrier();
-                for (int it = 0; it <= ntl; ++it) {
-                    out_iter(it);
-                    lds_barrier();
-                }
-            }
-        } else {
-            if (!chain) out_first();
-            lds_barrier();
-            for (int it = 0; it <= ntl; ++it) {
-                if (chain) {
-                    if (it < ntl) chain_tile(it);
-                } else {
-                    out_iter(it);
-                }
-                lds_barrier();
-            }
-        }
-    } else {
+    {
         // Iteration it.  Output half: store the outputs of tile it-2, start
         // the fills of tile it+1's keys and chain record, compute tile it-1.
         // Chain half: start the fills of tile it+1's targets and tile it's
@@ -1492,6 +1411,9 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
         if (out && ntl > 0) {
             load_xyr(0);
             store_xyr(0);
+            // per-column rule: tile 0's write vectors, and the first queries
+            dma_u(0);
+            load_q(0);
         }
         // the state's initial loads (chain) are complete before the loops, so
         // no wait inside them is owed to a load issued out here
@@ -1576,6 +1498,12 @@ __global__ __launch_bounds__(COL ? 512 : 768) void chunk_pass_kernel(ChunkArgs a
                         output_rows(it - 1);
                     else
                         output_tile(it - 1);
+                }
+                if constexpr (QG) {
+                    // the queries of tile it+1 load during iteration it
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) pQa[kb] = pQb[kb];
+                    if (it + 1 < ntl) load_q(it + 1);
                 }
                 lds_barrier();
             }
@@ -1878,6 +1806,9 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
                     out[u] = E::from_f(den > 0.f ? et * x / den : 0.f);
                 }
                 *reinterpret_cast<u32x4*>(&sm.Om[i][col]) = outv;
+                // and for the state pass (rows past the sequence hold zeros)
+                *reinterpret_cast<u32x4*>(static_cast<T*>(a.uws) +
+                                          (((size_t)bh * ntiles + tile) * CV + i) * D + col) = outv;
             }
         }
         lds_barrier();
@@ -2100,6 +2031,9 @@ static hipError_t launch_one(const ChunkArgs& a, void* ws, hipStream_t stream) {
     b.order = nullptr;
     b.toff = nullptr;
     b.jobs = nullptr;
+    // the per-column rule's write vectors follow the records
+    if constexpr (E::kBytes == 2 && COL)
+        b.uws = static_cast<char*>(ws) + (size_t)a.BH * ntiles * Rec<E, CV, DELTA>::kBytes;
     const int nbins = ntiles + 1;
     if (a.cu && a.order_ws && ntiles > 0 && nbins <= 8192) {
         // schedule layout: order [N], toff [N+1], then (256-byte aligned) the
@@ -2149,7 +2083,7 @@ static hipError_t launch_one(const ChunkArgs& a, void* ws, hipStream_t stream) {
     const int nvs = D / 64;
     const int bh8 = (b.BH + 7) / 8 * 8;
     if constexpr (E::kBytes == 2)
-        hipLaunchKernelGGL((chunk_pass_kernel<D, CV, DELTA, COL, WIN>), dim3(bh8 * nvs), dim3(COL ? 512 : 768),
+        hipLaunchKernelGGL((chunk_pass_kernel<D, CV, DELTA, COL, WIN>), dim3(bh8 * nvs), dim3(768),
                            0, stream, b, (const void*)ws, ntiles);
     else
         hipLaunchKernelGGL((chunk_scan_kernel<E, D, CV, DELTA, COL, WIN>), dim3(bh8 * nvs),
@@ -2210,7 +2144,8 @@ static size_t rec_bytes() {
     return Rec<E, CV, DELTA>::kBytes;
 }
 
-size_t chunk_workspace_bytes(int BH, int T, int dt, int chunk, int window, int norm, bool delta) {
+size_t chunk_workspace_bytes(int BH, int T, int dt, int chunk, int window, int norm, bool delta,
+                             int D) {
     const int Wv = (norm == kNormWindow) ? window : 1;
     const int ntiles = tiles_of(T, chunk / Wv);
     size_t rb = 0;
@@ -2223,6 +2158,8 @@ size_t chunk_workspace_bytes(int BH, int T, int dt, int chunk, int window, int n
         if (chunk == 32) rb = delta ? rec_bytes<EFp32, 32, true>() : rec_bytes<EFp32, 32, false>();
         if (chunk == 64) rb = delta ? rec_bytes<EFp32, 64, true>() : rec_bytes<EFp32, 64, false>();
     }
+    // bf16 per-column rule: the write vectors, chunk x D bf16 per tile
+    if (dt == 1 && norm == kNormColumn) rb += (size_t)chunk * D * 2;
     return (size_t)BH * ntiles * rb;
 }
 

@@ -64,6 +64,10 @@ struct ChunkArgs {
     // ((c / 16) * d_v + v) * 16 + c % 16.  o may then be NULL (not written).
     void* ck_s = nullptr;
     void* ck_d = nullptr;
+    // Per-column rule, bf16: the write vectors u of every (row, tile), CV x d
+    // bf16 rows, written by the intra-chunk kernel after the records and read
+    // by the state pass (set by the launcher).
+    void* uws = nullptr;
 };
 
 struct DecodeArgs {
@@ -152,8 +156,9 @@ hipError_t launch_chunk_bwd(const BwdArgs& a, int D, int chunk, bool delta, hipS
 // dt: 0 fp32, 1 bf16.  Return false when the combination is not built.
 bool chunk_supported(int dt, int D, int chunk);
 // Bytes of the per-tile records the intra-chunk kernel hands to the
-// state-passing kernel.
-size_t chunk_workspace_bytes(int BH, int T, int dt, int chunk, int window, int norm, bool delta);
+// state-passing kernel (bf16 per-column rule: then its write vectors).
+size_t chunk_workspace_bytes(int BH, int T, int dt, int chunk, int window, int norm, bool delta,
+                             int D);
 hipError_t launch_chunk(const ChunkArgs& a, int dt, int D, int chunk, bool delta, void* ws,
                         hipStream_t stream);
 bool decode_supported(int dt, int D);
