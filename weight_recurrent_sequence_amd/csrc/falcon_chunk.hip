@@ -1825,17 +1825,11 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
             constexpr int KM = D / 32;
             const int bA = wave, bP = DELTA ? NB - 1 - wave : wave;
             if (wave < NB) {
-                Frag xa[KM][2], qp[KM][2];
+                s16x8 xa[KM], qp[KM];
 #pragma unroll
                 for (int m = 0; m < KM; ++m) {
-                    const T* xr = &sm.X[16 * bA + lr][32 * m + 4 * grp];
-                    const T* qr = &sm.Q[16 * bP + lr][32 * m + 4 * grp];
-                    if constexpr (DELTA) {
-                        xa[m][0] = E::load(xr);
-                        xa[m][1] = E::load(xr + 16);
-                    }
-                    qp[m][0] = E::load(qr);
-                    qp[m][1] = E::load(qr + 16);
+                    if constexpr (DELTA) xa[m] = E::load8(&sm.X[16 * bA + lr][32 * m + 8 * grp]);
+                    qp[m] = E::load8(&sm.Q[16 * bP + lr][32 * m + 8 * grp]);
                 }
                 const int iA = 16 * bA + lr, iP = 16 * bP + lr;
                 const float giA = sm.gv[iA], giP = sm.gs[iP];
@@ -1843,13 +1837,13 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
                     constexpr int c = decltype(cc)::value;
                     const bool doA = DELTA && c <= bA, doP = c <= bP;
                     if (doA || doP) {
-                        const T* ar = omb + (size_t)(16 * c + lr) * LDX + 4 * grp;
+                        const T* ar = omb + (size_t)(16 * c + lr) * LDX + 8 * grp;
                         f32x4 accA = zero4(), accP = zero4();
 #pragma unroll
                         for (int m = 0; m < KM; ++m) {
-                            const Frag o0 = E::load(ar + 32 * m), o1 = E::load(ar + 32 * m + 16);
-                            if (doA) accA = E::mma32(o0, o1, xa[m][0], xa[m][1], accA);
-                            if (doP) accP = E::mma32(o0, o1, qp[m][0], qp[m][1], accP);
+                            const s16x8 om = E::load8(ar + 32 * m);
+                            if (doA) accA = E::mma32r(om, xa[m], accA);
+                            if (doP) accP = E::mma32r(om, qp[m], accP);
                         }
                         const int j0 = 16 * c + 4 * grp;
                         if (doA) {
@@ -1911,13 +1905,11 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
                     c = (q - NJA) - b * NB;
                     if (!(b < NBQ && (16 * c) / Wv <= 16 * b + 15)) continue;  // never read
                 }
-                const T* ar = omb + (size_t)(16 * c + lr) * LDX + 4 * grp;
-                const T* br = (isA ? &sm.X[16 * b + lr][0] : &sm.Q[16 * b + lr][0]) + 4 * grp;
+                const T* ar = omb + (size_t)(16 * c + lr) * LDX + 8 * grp;
+                const T* br = (isA ? &sm.X[16 * b + lr][0] : &sm.Q[16 * b + lr][0]) + 8 * grp;
                 f32x4 acc = zero4();
     #pragma unroll
-                for (int m = 0; m < D / 32; ++m)
-                    acc = E::mma32(E::load(ar + 32 * m), E::load(ar + 32 * m + 16), E::load(br + 32 * m),
-                                   E::load(br + 32 * m + 16), acc);
+                for (int m = 0; m < D / 32; ++m) acc = E::mma32r(E::load8(ar + 32 * m), E::load8(br + 32 * m), acc);
                 const int j0 = 16 * c + 4 * grp;
                 const int i = 16 * b + lr;
                 f32x4 val;

@@ -87,6 +87,19 @@ struct EBf16 {
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0,
                                                        0);
     }
+    // Row products A B^T with both operands read along their rows: a lane
+    // takes eight contiguous elements of the 32-wide contraction slice (one
+    // 16-byte LDS read; at a 272-byte row stride the 8-byte pairs of the
+    // split layout above hit each bank twice).  The contraction order only has
+    // to agree between the two operands.
+    static __device__ __forceinline__ s16x8 load8(const T* p) {
+        return *reinterpret_cast<const s16x8*>(p);
+    }
+    static __device__ __forceinline__ f32x4 mma32r(s16x8 a, s16x8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0,
+                                                       0);
+    }
 };
 
 struct EFp32 {
