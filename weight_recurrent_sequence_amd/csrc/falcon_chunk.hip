@@ -1741,13 +1741,9 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
         // ---- log-decay scan and row factors (wave 0) ----
         if (wave == 0) {
             const int j = lane;
-            float lg = (j < Ct) ? __logf(sm.al[j]) : 0.f;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(lg, off, 64);
-                if (j >= off) lg += y;
-            }
-            const float glast = __shfl(lg, Ct - 1, 64);
+            const float lg = wave_scan_dpp((j < Ct) ? __logf(sm.al[j]) : 0.f);
+            const float glast =
+                __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lg), Ct - 1));
             float bwin = 0.f;  // window normalizer of step j
             if (WIN && j < Ct) {
                 float tot = 0.f;
@@ -1756,9 +1752,10 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
                 bwin = den > 0.f ? sm.et[j] / den : 0.f;
             }
             const int sj = WIN ? min(j / Wv, Ct - 1) : min(j, Ct - 1);
-            const float gsj = __shfl(lg, sj, 64);
-            const float bsj = __shfl(bwin, sj, 64);
-            const float esj = __shfl(sm.et[j < CV ? j : 0], sj, 64);
+            // without a window a row is its own step (sj = j on the rows kept)
+            const float gsj = WIN ? __shfl(lg, sj, 64) : lg;
+            const float bsj = WIN ? __shfl(bwin, sj, 64) : 0.f;
+            const float esj = WIN ? __shfl(sm.et[j < CV ? j : 0], sj, 64) : sm.et[j < CV ? j : 0];
             if (j < CV) {
                 float r = 0.f;
                 if (j < NVR) {

@@ -213,6 +213,27 @@ __device__ __forceinline__ float group_sum_dpp(float x) {
     return x;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP (no LDS round
+// trips): shifts by 1, 2, 4 and 8 within each 16-lane row (lanes shifted in
+// from outside the row add zero), then the last lane of row 0 is added to
+// row 1 and that of row 2 to row 3, then lane 31 (rows 0-1 in total) to
+// rows 2 and 3.  Rows left out by the row mask add zero.
+__device__ __forceinline__ float wave_scan_dpp(float x) {
+    auto dpp = [](float v, auto ctrl, auto rows) {
+        return __builtin_bit_cast(
+            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), decltype(ctrl)::value,
+                                               decltype(rows)::value, 0xF, false));
+    };
+    using all = std::integral_constant<int, 0xF>;
+    x += dpp(x, std::integral_constant<int, 0x111>(), all());  // row_shr:1
+    x += dpp(x, std::integral_constant<int, 0x112>(), all());  // row_shr:2
+    x += dpp(x, std::integral_constant<int, 0x114>(), all());  // row_shr:4
+    x += dpp(x, std::integral_constant<int, 0x118>(), all());  // row_shr:8
+    x += dpp(x, std::integral_constant<int, 0x142>(), std::integral_constant<int, 0xA>());  // row_bcast:15
+    x += dpp(x, std::integral_constant<int, 0x143>(), std::integral_constant<int, 0xC>());  // row_bcast:31
+    return x;
+}
+
 // Sum over groups of `width` consecutive lanes (width a power of two <= 64).
 template <int width>
 __device__ __forceinline__ float group_sum(float x) {
