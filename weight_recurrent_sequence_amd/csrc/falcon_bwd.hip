@@ -654,12 +654,7 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
     }
     if (wave == 0) {
         // the log-decay scan over the steps (steps past the tile: alpha = 1)
-        float lg = __logf(sm.al[lane]);
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(lg, off, 64);
-            if (lane >= off) lg += y;
-        }
+        const float lg = wave_scan_dpp(__logf(sm.al[lane]));
         sm.gs[lane] = lg * kLog2e;
     }
     lds_barrier();
