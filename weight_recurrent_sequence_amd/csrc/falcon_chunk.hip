@@ -794,11 +794,12 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs a, const void
 //                       direct to LDS.  A wave that issues a tile's worth of
 //                       fills stalls on a full memory queue for thousands of
 //                       cycles; here no computing wave does.
-// The per-column rule stages through registers instead (its write vectors
-// are derived on the way) and runs without fill waves.  One barrier per
-// tile, fencing LDS only.  Loads use buffer descriptors: out-of-range rows
-// read as zero in hardware, and a lane's offsets stay fixed from tile to
-// tile.
+// For the per-column rule the fill waves also bring in the write vectors u
+// that the intra-chunk kernel stored (into the query buffer), and the output
+// waves take the queries as register fragments loaded one tile ahead.
+// One barrier per tile, fencing LDS only.  Loads use buffer descriptors:
+// out-of-range rows read as zero in hardware, and a lane's offsets stay
+// fixed from tile to tile.
 // ---------------------------------------------------------------------------
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
