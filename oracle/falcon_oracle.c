@@ -17,8 +17,9 @@
  *   - the state is a fixed-size fast-weight matrix updated once per token as
  *     one step of an online learner, and it is read after the write
  *     (authors' abstract: read-after-write autoregressive semantics);
- *   - the example revealed at step t is the prefix-aligned pair
- *     x_t = phi(k_{t-1}), y_t = v_t (authors' abstract; phi = identity here);
+ *   - step t learns from the key one step back paired with the current
+ *     value, x_t = phi(k_{t-1}), y_t = v_t ("Fast Weight Attention for
+ *     Continual Learning", authors' abstract; phi = identity here);
  *     the same-step pair x_t = k_t, y_t = v_t (the alignment of the KLA/GDN
  *     recurrences the pages contrast it with) is an option: `lag` = 1 is the
  *     prefix alignment, lag = 0 the same-step one;

@@ -65,3 +65,27 @@ def test_bwd_bytes(bench):
     B, H, T, d = 8, 16, 4096, 128
     want = B * H * T * (7 * d * 2 + 4 * 4) + 2 * B * H * d * d * 4
     assert bench.bwd_bytes(B, H, T, d) == want
+
+
+def test_window_flops(bench):
+    # Falcon-3 / Falcon-3A with W = 4 on chunks of C = 64 steps: E = C + W - 1
+    # = 67 distinct keys serve CW = 256 virtual examples.  Falcon-3: the
+    # extended key Gram (E^2 entries of d-long dot products), the query-key
+    # products (C x E), the CW x CW triangular solve, the transformed keys and
+    # targets (CW x CW times d_k + d_v), the residual product (CW x d_k x d_v),
+    # the state read by the queries (C x d_k x d_v), the intra-chunk outputs
+    # (C x CW x d_v) and the state update over the E keys (E x d_k x d_v),
+    # two flops per multiply-add.
+    C, W, d = 64, 4, 128
+    E, Cv = C + W - 1, C * W
+    per = (2 * E * E * d + 2 * C * E * d + 2 * Cv ** 3 / 3 + 2 * Cv * Cv * 2 * d
+           + 2 * Cv * d * d + 2 * C * d * d + 2 * C * Cv * d + 2 * E * d * d)
+    assert per == pytest.approx(63.86e6, rel=1e-3)
+    chunks = 2 * 16 * (32768 // C)
+    assert bench.window_flops(2, 16, 32768, d, C, W) == pytest.approx(chunks * per)
+    assert bench.window_flops(2, 16, 32768, d, C, W) == pytest.approx(1.046e12, rel=1e-3)
+    # Falcon-3A: the banded outputs over the E keys (C x E times d_k + d_v),
+    # the state read and the update
+    per_a = 2 * C * E * (d + d) + 2 * C * d * d + 2 * E * d * d
+    assert bench.window_flops(2, 16, 32768, d, C, W, delta=False) == pytest.approx(chunks * per_a)
+    assert bench.window_flops(2, 16, 32768, d, C, W, delta=False) == pytest.approx(106.3e9, rel=1e-2)

@@ -124,3 +124,58 @@ def test_varlen_full_size_sampled(dev):
         e_S = slice_rel_err(S_np[n:n + 1, heads], S_ref, (2, 3))
         announce(f"varlen full size seq {n} (T={b - a}): o {e_o:.2e} S {e_S:.2e}")
         assert e_o <= TOL["bf16"] and e_S <= TOL["bf16"]
+
+
+# A packed plane longer than its sequences (a fixed-capacity buffer): rows
+# after the last sequence belong to none.  With a feature map the intra-chunk
+# kernel writes mapped copies of the keys and queries into the workspace; the
+# plane is laid out so that head h's rows start at h * total_T, which for
+# H >= 2 reaches beyond N * H * max_seqlen rows, the room the workspace has
+# for them: the copies must be addressed per (sequence, head) instead.
+TAIL_CASE = dict(lengths=[40, 70], H=3, tail=600)
+
+
+def test_tail_shape_exceeds_plane_rows():
+    """CPU check that the case below is the one that needs per-(sequence,
+    head) rows: the last head's rows of the plane lie past the workspace's
+    N * H * max_seqlen mapped rows."""
+    L, H, tail = TAIL_CASE["lengths"], TAIL_CASE["H"], TAIL_CASE["tail"]
+    total_T, N, max_seqlen = sum(L) + tail, len(L), max(L)
+    assert (H - 1) * total_T + sum(L) > N * H * max_seqlen
+
+
+@pytest.mark.parametrize("phi", ["l2", "silu"])
+@pytest.mark.parametrize("case", [("F1", 1, 64), ("F3", 3, 32), ("F2A", 1, 64)],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_varlen_feature_map_long_tail(dev, case, phi):
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    variant, W, chunk = case
+    L, H, tail = TAIL_CASE["lengths"], TAIL_CASE["H"], TAIL_CASE["tail"]
+    vi = I.make_varlen_inputs(L, H, 128, 128, dtype="bf16", seed=990 + W, window=W,
+                              S0_sd=0.2, halo=True, tail=tail)
+    t = {n: to_dev(getattr(vi, n), "bf16", dev) for n in ("q", "k", "v", "k_prev", "v_prev")}
+    g = {n: to_dev(getattr(vi, n), "fp32", dev) for n in ("alpha", "eta", "S0")}
+    cu = torch.from_numpy(vi.cu).to(dev)
+    N, maxT = len(L), max(L)
+    need = fal.varlen_workspace_bytes(N, H, maxT, 128, 128, fal.BF16, variant, W, chunk, phi=phi)
+    guard = 1 << 20
+    ws = torch.full((need + guard,), 0x5A, dtype=torch.uint8, device=dev)
+    o = torch.full(t["v"].shape, 7.0, dtype=torch.bfloat16, device=dev)
+    announce(f"chunk_fwd_varlen {variant} W{W} phi={phi} lengths {L} tail {tail} H{H}")
+    o, S = fal.chunk_fwd_varlen(t["q"], t["k"], t["v"], g["alpha"], g["eta"], cu, variant,
+                                max_seqlen=maxT, window=W, chunk=chunk, S0=g["S0"],
+                                k_prev=t["k_prev"], v_prev=t["v_prev"], o=o, phi=phi,
+                                workspace=ws[:need])
+    torch.cuda.synchronize()
+    assert bool((ws[need:] == 0x5A).all()), "the call wrote past its workspace"
+    o_np, S_np = to_np(o), to_np(S)
+    assert np.all(o_np[:, sum(L):] == 7.0)
+    for n in range(N):
+        d = vi.sequence(n).f64()
+        o_ref, S_ref = oracle.recurrent(variant, d["q"], d["k"], d["v"], d["alpha"], d["eta"],
+                                        window=W, S0=d["S0"], k_prev=d["k_prev"],
+                                        v_prev=d["v_prev"], phi=phi)
+        a, b = vi.cu[n], vi.cu[n + 1]
+        assert slice_rel_err(o_np[None, :, a:b], o_ref, (2, 3)) <= TOL["bf16"], n
+        assert slice_rel_err(S_np[n:n + 1], S_ref, (2, 3)) <= TOL["bf16"], n

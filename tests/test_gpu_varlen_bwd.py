@@ -125,3 +125,48 @@ def test_varlen_bwd_leaves_other_rows(dev):
     for k in GRADS:
         assert torch.any(g[k][:, :40].float()), k
         assert not torch.any(g[k][:, 40:].float()), k
+
+
+@pytest.mark.parametrize("phi", ["l2", "silu"])
+@pytest.mark.parametrize("case", [("F1", 1), ("F3", 3)], ids=lambda c: "-".join(map(str, c)))
+def test_varlen_bwd_feature_map_long_tail(dev, case, phi):
+    """Packed planes longer than their sequences with a feature map: the
+    mapped key and query copies live at per-(sequence, head) rows of the
+    workspace, so a long tail (600 rows after two sequences of 40 and 70, H =
+    3: the last head's plane rows lie past N * H * max_seqlen) stays inside
+    it.  Gradients against the oracle per sequence; nothing past the
+    workspace is written; the tail rows of the gradients are not written."""
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    variant, W = case
+    L, H, tail = [40, 70], 3, 600
+    vi = I.make_varlen_inputs(L, H, 128, 128, dtype="bf16", seed=1560 + W, window=W,
+                              S0_sd=0.2, halo=True, tail=tail)
+    d_o, dS = packed_cotangents(vi, 1560 + W)
+    t = {n: to_dev(getattr(vi, n), dev) for n in ("q", "k", "v", "k_prev", "v_prev", "alpha",
+                                                   "eta", "S0")}
+    cu = torch.from_numpy(vi.cu).to(dev)
+    N, maxT = len(L), max(L)
+    need = fal.bwd_varlen_workspace_bytes(N, H, maxT, 128, 128, fal.BF16, variant, W, 64, phi=phi)
+    guard = 1 << 20
+    ws = torch.full((need + guard,), 0x5A, dtype=torch.uint8, device=dev)
+    announce(f"chunk_bwd_varlen {variant} W{W} phi={phi} lengths {L} tail {tail} H{H}")
+    g = fal.chunk_bwd_varlen(t["q"], t["k"], t["v"], t["alpha"], t["eta"], cu, to_dev(d_o, dev),
+                             variant, max_seqlen=maxT, dS_final=to_dev(dS, dev), window=W,
+                             S0=t["S0"], k_prev=t["k_prev"], v_prev=t["v_prev"], phi=phi,
+                             workspace=ws[:need])
+    torch.cuda.synchronize()
+    assert bool((ws[need:] == 0x5A).all()), "the call wrote past its workspace"
+    got = {k: (None if v is None else to_np(v)) for k, v in g.items()}
+    for k in GRADS:
+        assert not np.any(got[k][:, sum(L):]), k
+    for n in range(N):
+        a, b = int(vi.cu[n]), int(vi.cu[n + 1])
+        d = vi.sequence(n).f64()
+        ref = G.gradients(variant, d["q"], d["k"], d["v"], d["alpha"], d["eta"],
+                          vi.sequence(n).widen(d_o[None, :, a:b]), dS[n:n + 1].astype(np.float64),
+                          window=W, S0=d["S0"], k_prev=d["k_prev"], v_prev=d["v_prev"], phi=phi)
+        for k, name, ax in (("dq", "q", (2, 3)), ("dk", "k", (2, 3)), ("dv", "v", (2, 3)),
+                            ("dalpha", "alpha", (2,)), ("deta", "eta", (2,))):
+            e = slice_rel_err(got[k][None, :, a:b], ref[name], ax)
+            assert e <= TOL["bf16"], (n, k, e)

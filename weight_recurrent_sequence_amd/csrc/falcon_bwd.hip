@@ -148,8 +148,11 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdArgs a) {
     const int W = a.W, Wv = WIN ? W : 1, Ct = CV / Wv, NVR = Ct * Wv, NBQ = (Ct + 15) / 16;
     const BSeq sq = bwd_seq(a, bh);
     const int T_ = sq.T, ntiles = a.ntiles, ntl = tiles_of(T_, Ct), lag = a.lag;
-    const bf* kg = static_cast<const bf*>(a.k) + sq.row0 * D;
-    const bf* qg = static_cast<const bf*>(a.q) + sq.row0 * D;
+    // with a feature map, q and k are the mapped copies, at the sequence's own
+    // rows of the workspace (bh * T)
+    const size_t kq0 = a.phi ? (size_t)bh * a.T : sq.row0;
+    const bf* kg = static_cast<const bf*>(a.k) + kq0 * D;
+    const bf* qg = static_cast<const bf*>(a.q) + kq0 * D;
     const bf* dog = static_cast<const bf*>(a.d_o) + sq.row0 * D + v0;
     const bf* kp = a.k_prev ? static_cast<const bf*>(a.k_prev) + (size_t)bh * W * D : nullptr;
     const char* recg = static_cast<const char*>(a.rec) + (size_t)bh * ntiles * R::kBytes;
@@ -597,8 +600,9 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
 
     // ---- keys, queries, gates ----
     {
-        const bf* kg = static_cast<const bf*>(a.k) + row0 * D;
-        const bf* qg = static_cast<const bf*>(a.q) + row0 * D;
+        const size_t kq0 = a.phi ? (size_t)bh * a.T : row0;  // mapped copies: own rows
+        const bf* kg = static_cast<const bf*>(a.k) + kq0 * D;
+        const bf* qg = static_cast<const bf*>(a.q) + kq0 * D;
         const bf* kp = a.k_prev ? static_cast<const bf*>(a.k_prev) + (size_t)bh * W * D : nullptr;
         constexpr int NXP = CV * CPR / 256;
         u32x4 px[NXP], pq[NXP];

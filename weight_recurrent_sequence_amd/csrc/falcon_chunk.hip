@@ -69,6 +69,15 @@ __device__ __forceinline__ SeqRows seq_rows(const ChunkArgs& a, int bh) {
     return rows_of(a, bh - n * a.H, a.cu[n], a.cu[n + 1]);
 }
 
+// First row of sequence bh in the feature-mapped copies of the keys and
+// queries that the intra-chunk kernel writes to the workspace: each
+// (sequence, head) has its own T rows (packed calls: max_seqlen rows), so the
+// copies fit the workspace whatever the packed plane's length is.  Batched
+// calls: the same row as in the inputs.
+__device__ __forceinline__ size_t mapped_row0(const ChunkArgs& a, int bh) {
+    return (size_t)bh * a.T;
+}
+
 // The (batch*head) row of state-pass workgroup rank r: the natural order, or
 // for packed calls the sequences longest first (`order`), so the longest
 // sequences are dispatched first and none is left to run alone at the end.
@@ -242,8 +251,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a, void* ws, 
 
     // ---- stage keys (virtual rows) and queries, with the feature map; with a
     // map, also write the mapped keys, halo keys and queries for the state pass
-    T* kq = a.phi ? static_cast<T*>(a.kphi) + sr.row0 * D : nullptr;
-    T* qq = a.phi ? static_cast<T*>(a.qphi) + sr.row0 * D : nullptr;
+    T* kq = a.phi ? static_cast<T*>(a.kphi) + mapped_row0(a, bh) * D : nullptr;
+    T* qq = a.phi ? static_cast<T*>(a.qphi) + mapped_row0(a, bh) * D : nullptr;
     T* kpq = (a.phi && a.kpphi) ? static_cast<T*>(a.kpphi) + (size_t)bh * W * D : nullptr;
 #pragma unroll
     for (int it = 0; it < NXL; ++it) {
@@ -507,8 +516,10 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs a, const void
     const SeqRows sr = seq_rows(a, bh);
     const int T_ = sr.T;
     const float eps = a.eps;
-    const T* qg = static_cast<const T*>(a.q) + sr.row0 * D;
-    const T* kg = static_cast<const T*>(a.k) + sr.row0 * D;
+    // with a feature map, q and k are the mapped copies (their own rows)
+    const size_t kq0 = a.phi ? mapped_row0(a, bh) : sr.row0;
+    const T* qg = static_cast<const T*>(a.q) + kq0 * D;
+    const T* kg = static_cast<const T*>(a.k) + kq0 * D;
     const T* vg = static_cast<const T*>(a.v) + sr.row0 * D + v0;
     const T* kp = a.k_prev ? static_cast<const T*>(a.k_prev) + (size_t)bh * W * D : nullptr;
     const T* vp = (a.v_prev && W > 1)
@@ -871,8 +882,10 @@ __global__ __launch_bounds__(768) void chunk_pass_kernel(ChunkArgs a, const void
     const SeqRows sr = seq_rows(a, bh);
     const int T_ = sr.T;
     const float eps = a.eps;
-    const T* qg = static_cast<const T*>(a.q) + sr.row0 * D;
-    const T* kg = static_cast<const T*>(a.k) + sr.row0 * D;
+    // with a feature map, q and k are the mapped copies (their own rows)
+    const size_t kq0 = a.phi ? mapped_row0(a, bh) : sr.row0;
+    const T* qg = static_cast<const T*>(a.q) + kq0 * D;
+    const T* kg = static_cast<const T*>(a.k) + kq0 * D;
     const T* vg = static_cast<const T*>(a.v) + sr.row0 * D + v0;
     const T* kp = a.k_prev ? static_cast<const T*>(a.k_prev) + (size_t)bh * W * D : nullptr;
     const T* vp = (a.v_prev && W > 1)
@@ -1672,8 +1685,8 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
             // the state pass (a key appearing in several virtual rows is
             // written with the same value by each)
             const int t0 = tile * Ct;
-            T* kq = static_cast<T*>(a.kphi) + jb.sr.row0 * D;
-            T* qq = static_cast<T*>(a.qphi) + jb.sr.row0 * D;
+            T* kq = static_cast<T*>(a.kphi) + mapped_row0(a, bh) * D;
+            T* qq = static_cast<T*>(a.qphi) + mapped_row0(a, bh) * D;
             T* kpq = a.kpphi ? static_cast<T*>(a.kpphi) + (size_t)bh * W * D : nullptr;
 #pragma unroll
             for (int it = 0; it < NXL; ++it) {
