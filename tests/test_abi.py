@@ -88,7 +88,7 @@ def chunk(L, **kw):
     (dict(window=0), -2), (dict(window=2), -2),                 # window only for Falcon-3
     (dict(var=3, window=9), -3), (dict(chunk=48), -3), (dict(chunk=128), -3),
     (dict(dk=96, dv=96), -3), (dict(dk=64, dv=128), -3),
-    (dict(dt=0, chunk=64), -3),                                  # fp32 d128 chunk64: LDS
+    (dict(dt=0, chunk=64), -4),                                  # fp32 d128 chunk64: no workspace
     (dict(eps=-1.0), -2), (dict(eps=float("nan")), -2),
     (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(alpha=None), -1),
     (dict(eta=None), -1), (dict(o=None), -1),

@@ -25,10 +25,6 @@ def dev():
     return torch.device("cuda:0")
 
 
-def supported(dtype, D, chunk):
-    return not (dtype == "fp32" and D == 128 and chunk == 64)
-
-
 def gpu_run(dev, inp, variant, W, chunk, eps=1e-6, label="", align="prefix"):
     import torch
     import weight_recurrent_sequence_amd as fal
@@ -66,8 +62,6 @@ def check(dev, inp, variant, W, chunk, label="", align="prefix"):
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("variant", ALL)
 def test_grid(dev, variant, dtype, D, chunk):
-    if not supported(dtype, D, chunk):
-        pytest.skip("fp32 with d=128 supports chunk <= 32 (LDS)")
     W = 3 if variant in ("F3", "F3A") else 1
     inp = I.make_chunk_inputs(2, 3, 150, D, D, dtype=dtype, seed=100 + D + chunk, window=W,
                               halo=True, S0_sd=0.3)
@@ -102,8 +96,6 @@ def test_windows(dev, variant, W, chunk):
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("variant", ALL)
 def test_same_step_grid(dev, variant, dtype, D, chunk):
-    if not supported(dtype, D, chunk):
-        pytest.skip("fp32 with d=128 supports chunk <= 32 (LDS)")
     W = 3 if variant in ("F3", "F3A") else 1
     inp = I.make_chunk_inputs(2, 3, 150, D, D, dtype=dtype, seed=600 + D + chunk, window=W,
                               halo=True, S0_sd=0.3)
@@ -169,13 +161,14 @@ def test_deterministic_and_state_alias(dev):
     assert torch.equal(o3, runs[0][0]) and torch.equal(S_alias, runs[0][1])
 
 
-def test_fp32_large_chunk_rejected(dev):
-    import torch
-    import weight_recurrent_sequence_amd as fal
-    x = torch.zeros(1, 1, 8, 128, device=dev)
-    a = torch.ones(1, 1, 8, device=dev)
-    with pytest.raises(fal.FalconError):
-        fal.chunk_fwd(x, x, x, a, a, "F1", chunk=64)
+def test_fp32_d128_chunk64_full_tiles(dev):
+    """fp32 inputs at d = 128 with 64-row tiles (the support matrix's largest
+    fp32 tile): several full tiles and a ragged tail, every variant."""
+    for variant in ALL:
+        W = 4 if variant in ("F3", "F3A") else 1
+        inp = I.make_chunk_inputs(1, 2, 333, 128, 128, dtype="fp32", seed=530 + W, window=W,
+                                  halo=True, S0_sd=0.3)
+        check(dev, inp, variant, W, 64, label="fp32 d128 chunk64")
 
 
 # ---- the workloads at full size, in the launch configuration the benchmark

@@ -472,8 +472,10 @@ struct ScanSmem {
     T X[CV][LDX];               // keys x_i (virtual rows)
     T Q[CV][LDX];               // queries q_t
     T Om[COL ? CV : 1][LDX];    // per-column write vectors u_i
-    T Y[CV][64 + PADE];         // targets y_i, this workgroup's 64 value columns
-    T O[CV][64 + PADE];         // outputs on their way to HBM
+    // targets y_i of this workgroup's 64 value columns; each wave reads the 16
+    // columns it owns, then writes its outputs over them (staged there on
+    // their way to HBM), so at fp32, d = 128, chunk 64 the tiles fit LDS
+    T Y[CV][64 + PADE];
     alignas(16) char rec[R::kBytes];  // this tile's record
 };
 
@@ -734,8 +736,9 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs a, const void
                 acc = E::mma16(E::load(recT + R::kP + (size_t)R::pblk(tb, cb, WIN) * 256 + lane * 4),
                                DB[cb], acc);
             }
+            // the wave's own target columns, already read (program order)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sm.O[16 * tb + 4 * grp + r][16 * wave + lr] = E::from_f(acc[r]);
+            for (int r = 0; r < 4; ++r) sm.Y[16 * tb + 4 * grp + r][16 * wave + lr] = E::from_f(acc[r]);
         }
 
         // state update S^T = exp(g_last) S0^T + Omega^T diag(hrow) Delta; the A
@@ -775,8 +778,9 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs a, const void
             const int t = c / YCPR, col = (c % YCPR) * EPC;
             if (c < CV * YCPR && t < Ct && t0 + t < T_)
                 *reinterpret_cast<u32x4*>(og + (size_t)(t0 + t) * D + col) =
-                    *reinterpret_cast<const u32x4*>(&sm.O[t][col]);
+                    *reinterpret_cast<const u32x4*>(&sm.Y[t][col]);
         }
+        __syncthreads();  // the next tile's targets overwrite the staged outputs
     }
 
     if (a.S_final) {
@@ -2099,10 +2103,7 @@ static hipError_t launch_cv(const ChunkArgs& a, int chunk, void* ws, hipStream_t
     switch (chunk) {
         case 16: return launch_one<E, D, 16, DELTA, COL, WIN>(a, ws, stream);
         case 32: return launch_one<E, D, 32, DELTA, COL, WIN>(a, ws, stream);
-        case 64:
-            if constexpr (D == 64 || E::kBytes == 2)
-                return launch_one<E, D, 64, DELTA, COL, WIN>(a, ws, stream);
-            return hipErrorInvalidValue;
+        case 64: return launch_one<E, D, 64, DELTA, COL, WIN>(a, ws, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -2138,7 +2139,6 @@ static hipError_t launch_e(const ChunkArgs& a, int D, int chunk, bool delta, voi
 bool chunk_supported(int dt, int D, int chunk) {
     if (D != 64 && D != 128) return false;
     if (chunk != 16 && chunk != 32 && chunk != 64) return false;
-    if (chunk == 64 && dt == 0 && D == 128) return false;  // fp32 tiles of 64 x 128 exceed LDS
     return true;
 }
 

@@ -42,6 +42,14 @@ __device__ __forceinline__ void phi_row(int phi, float (&x)[16]) {
     }
 }
 
+// An empty asm statement that takes two values as register inputs: every
+// load whose data feeds them has returned that data (so it is complete)
+// before the statement, and the statement, being volatile, stays on its side
+// of a barrier that follows it.
+__device__ __forceinline__ void consumed(float a, float b) {
+    asm volatile("" ::"v"(a), "v"(b));
+}
+
 template <class E, int D>
 __global__ __launch_bounds__(256, 2) void decode_step_kernel(DecodeArgs a) {
     using T = typename E::T;
@@ -63,26 +71,23 @@ __global__ __launch_bounds__(256, 2) void decode_step_kernel(DecodeArgs a) {
     const float et = a.eta[head];
     // Everything this thread reads is requested up front (targets and the new
     // key too), so no wait further down has a load queued behind a store.
-    // Thread c < D is the only one that reads column c of the key cache from
-    // memory and the only one that writes it (program order on one address),
-    // so the cache needs no ordering between threads; the other threads get
-    // the pair's key through LDS.
-    __shared__ float xs[D];
-    const int col = tid < D ? tid : 0;
-    const T kold = kc[col];
-    const T knew = kh[col];
+    const T knew = kh[tid < D ? tid : 0];
     T vraw[RPT];  // converted where used, so the load stays in flight meanwhile
 #pragma unroll
     for (int p = 0; p < RPT; ++p) vraw[p] = vh[row0 + ROWS_PER_PASS * p];
 
     // columns of this lane: 4*seg + 4*LPR*j + e, j, e in 0..3
+    const T* xh = a.lag ? kc : kh;
     float x[16], qv[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int c = 4 * seg + 4 * LPR * j;
-        const typename E::Frag qf = E::load(qh + c);
+        const typename E::Frag xf = E::load(xh + c), qf = E::load(qh + c);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) qv[4 * j + e] = E::to_f((T)qf[e]);
+        for (int e = 0; e < 4; ++e) {
+            x[4 * j + e] = E::to_f((T)xf[e]);
+            qv[4 * j + e] = E::to_f((T)qf[e]);
+        }
     }
     f32x4 s[RPT][4];
 #pragma unroll
@@ -92,16 +97,6 @@ __global__ __launch_bounds__(256, 2) void decode_step_kernel(DecodeArgs a) {
         for (int j = 0; j < 4; ++j)
             s[p][j] = __builtin_nontemporal_load(
                 reinterpret_cast<const f32x4*>(S + (size_t)row * D + 4 * seg + 4 * LPR * j));
-    }
-    // x = k_{t-1} (the cache) or, for same-step pairs, the new key
-    if (tid < D) xs[tid] = E::to_f(a.lag ? kold : knew);
-    lds_barrier();  // orders LDS only: the state loads stay in flight
-    if (tid < D) kc[tid] = knew;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const f32x4 xf = *reinterpret_cast<const f32x4*>(&xs[4 * seg + 4 * LPR * j]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * j + e] = xf[e];
     }
     phi_row<LPR>(a.phi, x);
     phi_row<LPR>(a.phi, qv);
@@ -115,6 +110,16 @@ __global__ __launch_bounds__(256, 2) void decode_step_kernel(DecodeArgs a) {
     }
     n2 = group_sum_dpp<LPR>(n2);
     n1 = group_sum_dpp<LPR>(n1);
+    // Every lane has now consumed the previous key: its x values entered the
+    // norms, and the empty asm below takes n2 and n1 as register inputs, so
+    // the loads of the cached key have returned their data (they are
+    // complete) before this wave reaches the barrier; neither the asm nor the
+    // barrier can be moved across the other.  After the barrier k_cache may be
+    // overwritten.  The barrier orders no memory besides that, so it waits for
+    // no other load in flight (the state's).
+    consumed(n2, n1);
+    __builtin_amdgcn_s_barrier();
+    if (tid < D) kc[tid] = knew;
     float u[16];
     float uq = 0.f;
     if (a.norm == kNormScalar) {
@@ -193,10 +198,11 @@ namespace falcon {
 //     o  = S q = alpha S q + b sum_w r_w (x_w . q)
 // then both caches move one slot (the new key and value enter at slot 0).
 // One workgroup per head, as in the single-pair step: the state rows and the
-// W keys' column slices sit in registers, S is read and written once.
-// Thread c is the only one that reads column c of the caches from memory and
-// the only one that writes it (it shifts its own column); the keys reach the
-// other threads through LDS.
+// W keys' column slices sit in registers, S is read and written once.  Every
+// thread shifts only its own column of the caches, after a barrier that every
+// wave reaches only once its own reads of the caches have returned their
+// data, so no thread overwrites a cache element another thread still has to
+// read.
 // ---------------------------------------------------------------------------
 template <class E, int D, int W>
 __global__ __launch_bounds__(256, 2) void decode_window_kernel(DecodeWinArgs a) {
@@ -205,7 +211,6 @@ __global__ __launch_bounds__(256, 2) void decode_window_kernel(DecodeWinArgs a) 
     constexpr int ROWS_PER_PASS = 256 / LPR;
     constexpr int RPT = D / ROWS_PER_PASS;
     __shared__ float ys[W][D];  // targets y_w of every row
-    __shared__ float xs[W][D];  // keys x_w of the window
     const int tid = threadIdx.x;
     const int seg = tid % LPR;
     const int row0 = tid / LPR;
@@ -239,6 +244,13 @@ __global__ __launch_bounds__(256, 2) void decode_window_kernel(DecodeWinArgs a) 
         const typename E::Frag qf = E::load(qh + c);
 #pragma unroll
         for (int e = 0; e < 4; ++e) qv[4 * j + e] = E::to_f((T)qf[e]);
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const T* xw = (w + a.lag == 0) ? kh : kc + (size_t)(w + a.lag - 1) * D;
+            const typename E::Frag xf = E::load(xw + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[w][4 * j + e] = E::to_f((T)xf[e]);
+        }
     }
     f32x4 s[RPT][4];
 #pragma unroll
@@ -249,41 +261,16 @@ __global__ __launch_bounds__(256, 2) void decode_window_kernel(DecodeWinArgs a) 
             s[p][j] = __builtin_nontemporal_load(
                 reinterpret_cast<const f32x4*>(S + (size_t)row * D + 4 * seg + 4 * LPR * j));
     }
-    // The window's keys reach the other threads through LDS: thread c < D is
-    // the only one that reads column c of the caches from memory, and the
-    // only one that writes it, so the caches need no ordering between threads.
-    // Pair w's key is k_{t-w-lag}: the new key when w + lag = 0, else cache
-    // slot w + lag - 1.
-    if (tid < D) {
-#pragma unroll
-        for (int w = 0; w < W; ++w) {
-            xs[w][tid] = E::to_f(a.lag ? kcol[w] : (w == 0 ? knew : kcol[w > 0 ? w - 1 : 0]));
-            ys[w][tid] = E::to_f(vcol[w]);
-        }
-    }
-    lds_barrier();  // orders LDS only: the state loads stay in flight
-    if (tid < D) {
-#pragma unroll
-        for (int w = W - 1; w >= 1; --w) kc[(size_t)w * D + tid] = kcol[w - 1];
-        kc[tid] = knew;
-#pragma unroll
-        for (int w = W - 1; w >= 2; --w) vc[(size_t)(w - 1) * D + tid] = vcol[w - 1];
-        if (W > 1) vc[tid] = vcol[0];
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int w = 0; w < W; ++w) {
-            const f32x4 xf = *reinterpret_cast<const f32x4*>(&xs[w][4 * seg + 4 * LPR * j]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[w][4 * j + e] = xf[e];
-        }
-    }
+
     phi_row<LPR>(a.phi, qv);
 #pragma unroll
     for (int w = 0; w < W; ++w) phi_row<LPR>(a.phi, x[w]);
 
-    // ---- window norm and x_w . q ----
+    // ---- targets to LDS; window norm and x_w . q ----
+    if (tid < D) {
+#pragma unroll
+        for (int w = 0; w < W; ++w) ys[w][tid] = E::to_f(vcol[w]);
+    }
     float n2 = 0.f, xq[W];
 #pragma unroll
     for (int w = 0; w < W; ++w) {
@@ -298,6 +285,22 @@ __global__ __launch_bounds__(256, 2) void decode_window_kernel(DecodeWinArgs a) 
     n2 = group_sum_dpp<LPR>(n2);
     const float den = n2 + a.eps;
     const float bw = den > 0.f ? et / den : 0.f;
+    // Every lane has consumed its cache reads (they entered the sums above,
+    // and the empty asm takes the sums as register inputs, so those loads
+    // have returned their data before the wave reaches the barrier) and the
+    // targets are in LDS: the caches may now move.  The barrier orders LDS
+    // only, so no other load in flight (the state's) is waited for.
+    consumed(n2, xq[0]);
+    lds_barrier();
+    if (tid < D) {
+#pragma unroll
+        for (int w = W - 1; w >= 1; --w) kc[(size_t)w * D + tid] = kcol[w - 1];
+        kc[tid] = knew;
+#pragma unroll
+        for (int w = W - 1; w >= 2; --w) vc[(size_t)(w - 1) * D + tid] = vcol[w - 1];
+        if (W > 1) vc[tid] = vcol[0];
+    }
+
 #pragma unroll
     for (int p = 0; p < RPT; ++p) {
         const int row = row0 + ROWS_PER_PASS * p;
