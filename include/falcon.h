@@ -47,8 +47,10 @@
  * Conventions for every entry point
  *   - Pointers are device memory owned by the caller, except where noted.
  *     The library never allocates, frees or synchronizes, and keeps no
- *     global mutable state (re-entrant; concurrent calls on different
- *     streams are safe when their buffers do not overlap).
+ *     global mutable state besides the per-device address of the scratch
+ *     buffer built into it for falcon_chunk_fwd_noalloc (re-entrant;
+ *     concurrent calls on different streams are safe when their buffers do
+ *     not overlap, which for falcon_chunk_fwd_noalloc means: not on one GPU).
  *   - Work is enqueued on `stream` (NULL = the default stream); the call
  *     returns without waiting for it.
  *   - Arguments are validated on the host before anything is launched; an
@@ -77,8 +79,13 @@ typedef enum {
     FALCON_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
     FALCON_ERR_UNSUPPORTED = -3, /* valid, but not in the support matrix below */
     FALCON_ERR_WORKSPACE = -4,   /* workspace missing or too small */
-    FALCON_ERR_HIP = -5          /* HIP reported an error at launch */
+    FALCON_ERR_HIP = -5,         /* HIP reported an error at launch */
+    FALCON_ERR_SCRATCH = -6      /* falcon_chunk_fwd_noalloc: the call needs more scratch
+                                    than FALCON_NOALLOC_SCRATCH_BYTES */
 } falcon_status;
+
+/* Size of the built-in device scratch buffer of falcon_chunk_fwd_noalloc. */
+#define FALCON_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 
 typedef enum {
     FALCON_F1 = 1,
@@ -135,6 +142,33 @@ int falcon_chunk_fwd(const void* q, const void* k, const void* v, const float* a
                      void* o, float* S_final, int B, int H, int T, int dk, int dv,
                      falcon_dtype dt, falcon_variant var, int window, int chunk, float eps,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * falcon_chunk_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the workspace is a scratch buffer built
+ * into the library, FALCON_NOALLOC_SCRATCH_BYTES (128 MiB) of device memory
+ * per GPU, which each GPU the library runs on holds until the process ends.
+ * The call allocates nothing (no hipMalloc, no allocating library routine).
+ *
+ * Arguments, results and errors are those of falcon_chunk_fwd, plus
+ * FALCON_ERR_SCRATCH when falcon_chunk_fwd_workspace(...) for these
+ * arguments exceeds FALCON_NOALLOC_SCRATCH_BYTES (nothing is launched then).
+ * The result equals falcon_chunk_fwd's bit for bit.
+ *
+ * Every call on one GPU shares that GPU's scratch buffer: calls that overlap
+ * in time on one GPU (on different streams, or from different threads
+ * without ordering between their streams) race and give undefined results.
+ * Calls ordered on one stream are safe; the buffer keeps the last call's
+ * contents and no call depends on what it held before.  The first call on a
+ * device looks up that device's copy of the buffer (hipGetSymbolAddress)
+ * with the device current; later calls reuse the address.
+ */
+int falcon_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* alpha,
+                             const float* eta, const float* S0, const void* k_prev,
+                             const void* v_prev, void* o, float* S_final, int B, int H, int T,
+                             int dk, int dv, falcon_dtype dt, falcon_variant var, int window,
+                             int chunk, float eps, hipStream_t stream);
 
 /*
  * Chunk-parallel forward over N packed sequences of different lengths.  Each

@@ -34,6 +34,7 @@ def test_header_declares_the_entry_points():
                                            "falcon_chunk_fwd_varlen",
                                            "falcon_chunk_fwd_varlen_workspace",
                                            "falcon_chunk_fwd_save", "falcon_chunk_bwd_saved",
+                                           "falcon_chunk_fwd_noalloc",
                                            "falcon_chunk_fwd_varlen_save",
                                            "falcon_chunk_bwd_varlen_saved",
                                            "falcon_decode_step", "falcon_decode_step_window",
@@ -47,7 +48,7 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_status_strings(L):
     from weight_recurrent_sequence_amd import binding
-    for code in (0, -1, -2, -3, -4, -5, 42):
+    for code in (0, -1, -2, -3, -4, -5, -6, 42):
         s = binding.status_string(code)
         assert isinstance(s, str) and s
     assert binding.status_string(99) == "unknown status"

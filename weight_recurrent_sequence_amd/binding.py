@@ -22,7 +22,9 @@ PHI_L2, PHI_SILU = 0x200, 0x400  # flags: feature map on keys and queries
 PHI = {"identity": 0, "l2": PHI_L2, "silu": PHI_SILU}
 FP32, BF16 = 0, 1
 STATUS = {0: "FALCON_OK", -1: "FALCON_ERR_NULL", -2: "FALCON_ERR_SHAPE",
-          -3: "FALCON_ERR_UNSUPPORTED", -4: "FALCON_ERR_WORKSPACE", -5: "FALCON_ERR_HIP"}
+          -3: "FALCON_ERR_UNSUPPORTED", -4: "FALCON_ERR_WORKSPACE", -5: "FALCON_ERR_HIP",
+          -6: "FALCON_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 128 << 20  # FALCON_NOALLOC_SCRATCH_BYTES
 EXPORTS = ("falcon_chunk_fwd_workspace", "falcon_chunk_fwd", "falcon_chunk_fwd_varlen_workspace",
            "falcon_chunk_fwd_varlen", "falcon_decode_step",
            "falcon_decode_step_window", "falcon_status_string")
@@ -68,6 +70,8 @@ def lib():
                                ("falcon_chunk_bwd_varlen_saved", 19, 10)):
             getattr(L, name).restype = ci
             getattr(L, name).argtypes = [vp] * nvp + [ci] * nci + [cf, vp, sz, vp]
+        L.falcon_chunk_fwd_noalloc.restype = ci
+        L.falcon_chunk_fwd_noalloc.argtypes = [vp] * 10 + [ci] * 9 + [cf, vp]
         L.falcon_decode_step.restype = ci
         L.falcon_decode_step.argtypes = [vp] * 8 + [ci] * 7 + [cf, vp]
         L.falcon_decode_step_window.restype = ci
@@ -174,6 +178,46 @@ def chunk_fwd(q, k, v, alpha, eta, variant, *, window=1, chunk=64, eps=1e-6, S0=
                               _stream(stream))
     if st != 0:
         raise FalconError(st, name)
+    return o, S_final
+
+
+def chunk_fwd_noalloc(q, k, v, alpha, eta, variant, *, window=1, chunk=64, eps=1e-6, S0=None,
+                      k_prev=None, v_prev=None, o=None, S_final=None, stream=None,
+                      align="prefix", phi="identity"):
+    """chunk_fwd through falcon_chunk_fwd_noalloc: the library's built-in
+    scratch buffer replaces the workspace (no device allocation by the call;
+    o and S_final are allocated here when not given).  Raises FalconError
+    (FALCON_ERR_SCRATCH) when the call needs more than NOALLOC_SCRATCH_BYTES.
+    Returns (o, S_final)."""
+    import torch
+    var = _variant(variant, align, phi)
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    dev, dt = k.device, k.dtype
+    dtc = _dt(k)
+    _check(q, "q", (B, H, T, dk), dt, dev)
+    _check(k, "k", (B, H, T, dk), dt, dev)
+    _check(v, "v", (B, H, T, dv), dt, dev)
+    _check(alpha, "alpha", (B, H, T), torch.float32, dev)
+    _check(eta, "eta", (B, H, T), torch.float32, dev)
+    _check(S0, "S0", (B, H, dv, dk), torch.float32, dev)
+    _check(k_prev, "k_prev", (B, H, window, dk), dt, dev)
+    if window > 1:
+        _check(v_prev, "v_prev", (B, H, window - 1, dv), dt, dev)
+    else:
+        v_prev = None
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+    _check(o, "o", (B, H, T, dv), dt, dev)
+    if S_final is None:
+        S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    _check(S_final, "S_final", (B, H, dv, dk), torch.float32, dev)
+    st = lib().falcon_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta),
+                                        _ptr(S0), _ptr(k_prev), _ptr(v_prev), _ptr(o),
+                                        _ptr(S_final), B, H, T, dk, dv, dtc, var, window, chunk,
+                                        float(eps), _stream(stream))
+    if st != 0:
+        raise FalconError(st, "falcon_chunk_fwd_noalloc")
     return o, S_final
 
 

@@ -1,13 +1,45 @@
 // falcon_api.hip -- the C ABI declared in include/falcon.h: argument
 // validation on the host (before any HIP call), then dispatch to the
-// kernels on the caller's stream.  No allocation, no synchronization, no
-// global mutable state.
+// kernels on the caller's stream.  No allocation and no synchronization;
+// the only global state is the per-device address of the built-in scratch
+// buffer that falcon_chunk_fwd_noalloc uses.
 #include <stdint.h>
+
+#include <mutex>
 
 #include "../../include/falcon.h"
 #include "falcon_internal.h"
 
 namespace {
+
+// Scratch of falcon_chunk_fwd_noalloc: one buffer per device, a file-scope
+// device array (every GPU the library runs on holds its own copy for the
+// life of the process).  Host code never uses the array's name as an
+// address: the device address of each GPU's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// kept here.
+__device__ __align__(256) unsigned char scratch[FALCON_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The current device's copy of the scratch array (looked up on the first
+// call on that device).
+int device_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return FALCON_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return FALCON_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return FALCON_ERR_HIP;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return FALCON_OK;
+}
 
 bool is_variant(int v) {
     return v == FALCON_F1 || v == FALCON_F2 || v == FALCON_F3 || v == FALCON_F1A ||
@@ -650,6 +682,25 @@ int falcon_chunk_bwd_varlen_saved(const void* q, const void* k, const void* v, c
                          stream, kFromSaved);
 }
 
+int falcon_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* alpha,
+                             const float* eta, const float* S0, const void* k_prev,
+                             const void* v_prev, void* o, float* S_final, int B, int H, int T,
+                             int dk, int dv, falcon_dtype dt, falcon_variant var, int window,
+                             int chunk, float eps, hipStream_t stream) {
+    int st = check_chunk(q, k, v, alpha, eta, S0, k_prev, v_prev, o, S_final, B, H, T, dk, dv,
+                         dt, var, window, chunk, eps);
+    if (st != FALCON_OK) return st;
+    const size_t need = falcon_chunk_fwd_workspace(B, H, T, dk, dv, dt, var, window, chunk);
+    if (need > FALCON_NOALLOC_SCRATCH_BYTES) return FALCON_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (need > 0) {
+        st = device_scratch(&ws);
+        if (st != FALCON_OK) return st;
+    }
+    return falcon_chunk_fwd(q, k, v, alpha, eta, S0, k_prev, v_prev, o, S_final, B, H, T, dk, dv,
+                            dt, var, window, chunk, eps, ws, need, stream);
+}
+
 const char* falcon_status_string(int status) {
     switch (status) {
         case FALCON_OK: return "ok";
@@ -658,6 +709,9 @@ const char* falcon_status_string(int status) {
         case FALCON_ERR_UNSUPPORTED: return "arguments outside the supported set";
         case FALCON_ERR_WORKSPACE: return "workspace missing or too small";
         case FALCON_ERR_HIP: return "HIP reported an error at launch";
+        case FALCON_ERR_SCRATCH:
+            return "the call needs more scratch than the built-in buffer of "
+                   "FALCON_NOALLOC_SCRATCH_BYTES (128 MiB) holds";
         default: return "unknown status";
     }
 }
