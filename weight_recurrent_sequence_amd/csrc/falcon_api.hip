@@ -421,7 +421,19 @@ int chunk_bwd_run(const void* q, const void* k, const void* v, const float* alph
     a.eps = eps;
     a.ck_s = ck_s;
     a.ck_d = ck_d;
-    if (mode != kFromSaved && (T > 0 || S_final)) {
+    if (mode == kSaveOnly && (o || S_final) && dt == FALCON_BF16 &&
+        norm_of(base) == falcon::kNormWindow && window >= 2 && !phi) {
+        // the window rules' forward runs the collapsed form: o and S_final
+        // from it (so they equal falcon_chunk_fwd's bit for bit), then the
+        // checkpoints from a run of the virtual-row kernels without outputs
+        falcon::ChunkArgs f = a;
+        f.ck_s = f.ck_d = nullptr;
+        hipError_t e = falcon::launch_chunk(f, dt, dk_, chunk, is_delta(base), workspace, stream);
+        if (e != hipSuccess) return FALCON_ERR_HIP;
+        a.o = nullptr;
+        a.S_final = nullptr;
+    }
+    if (mode != kFromSaved && (T > 0 || a.S_final)) {
         hipError_t e = falcon::launch_chunk(a, dt, dk_, chunk, is_delta(base), workspace, stream);
         if (e != hipSuccess) return FALCON_ERR_HIP;
     }

@@ -436,9 +436,9 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdArgs a) {
                     // the blocks the record holds: query block tb < NBQ that
                     // reaches back to a row of block rb
                     if (tb < NBQ && (16 * rb) / Wv <= 16 * tb + 15)
-                        dd[rb] = E::mma16(rec_tr(R::kP + (size_t)R::pblk(tb, rb, true) * 256), dOc[tb], dd[rb]);
+                        dd[rb] = E::mma16n(rec_tr(R::kP + (size_t)R::pblk(tb, rb, true) * 256), dOc[tb], dd[rb]);
                 } else if constexpr (tb >= rb) {
-                    dd[rb] = E::mma16(rec_tr(R::kP + (size_t)R::pblk(tb, rb, false) * 256), dOc[tb], dd[rb]);
+                    dd[rb] = E::mma16n(rec_tr(R::kP + (size_t)R::pblk(tb, rb, false) * 256), dOc[tb], dd[rb]);
                 }
             });
         });
@@ -454,9 +454,9 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdArgs a) {
                 static_for<NB>([&](auto cbc) __attribute__((always_inline)) {
                     constexpr int cb = decltype(cbc)::value;
                     if constexpr (cb > rb)
-                        acc = E::mma16(rec_tr(R::kA + (size_t)R::ablk(cb, rb) * 256), drb[cb], acc);
+                        acc = E::mma16n(rec_tr(R::kA + (size_t)R::ablk(cb, rb) * 256), drb[cb], acc);
                 });
-                dr[rb] = E::mma16(rec_tr(R::kD + (size_t)rb * 256), E::pack(acc), zero4());
+                dr[rb] = E::mma16n(rec_tr(R::kD + (size_t)rb * 256), E::pack(acc), zero4());
                 drb[rb] = E::pack(dr[rb]);
             });
         } else {
@@ -874,15 +874,15 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
                 for (int cb = 0; cb < NB; ++cb) {
                     // dQ^T (query block cb): rows of steps up to the block's last
                     if (cb < NBQ && (16 * jb) / Wv <= 16 * cb + 15)
-                        aQ[kk][cb] = E::mma16(wj, colfrag(DPr, LDC, 16 * jb, 16 * cb), aQ[kk][cb]);
+                        aQ[kk][cb] = E::mma16n(wj, colfrag(DPr, LDC, 16 * jb, 16 * cb), aQ[kk][cb]);
                     if (DELTA && jb <= cb)
-                        aX[kk][cb] = E::mma16(wj, colfrag(DAr, LDC, 16 * jb, 16 * cb), aX[kk][cb]);
+                        aX[kk][cb] = E::mma16n(wj, colfrag(DAr, LDC, 16 * jb, 16 * cb), aX[kk][cb]);
                     // dOmega^T (row block cb): queries of the steps from the block's first
                     if (jb < NBQ && (16 * cb) / Wv <= 16 * jb + 15)
-                        aW[kk][cb] = E::mma16(qj, E::load(DP + (size_t)(16 * cb + lr) * LDC + 16 * jb + 4 * grp),
+                        aW[kk][cb] = E::mma16n(qj, E::load(DP + (size_t)(16 * cb + lr) * LDC + 16 * jb + 4 * grp),
                                               aW[kk][cb]);
                     if (DELTA && jb >= cb)
-                        aW[kk][cb] = E::mma16(xj, E::load(DA + (size_t)(16 * cb + lr) * LDC + 16 * jb + 4 * grp),
+                        aW[kk][cb] = E::mma16n(xj, E::load(DA + (size_t)(16 * cb + lr) * LDC + 16 * jb + 4 * grp),
                                               aW[kk][cb]);
                 }
             }

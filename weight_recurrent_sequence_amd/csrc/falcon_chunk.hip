@@ -46,46 +46,10 @@
 #include "falcon_device.h"
 #include "falcon_internal.h"
 #include "falcon_records.h"
+#include "falcon_rows.h"
 
 namespace falcon {
 
-
-// Rows of sequence bh in the [rows, d] planes: [row0, row0 + T).  Batched
-// calls: row0 = bh * T.  Packed calls: the bounds come from cu, clamped to the
-// plane and to the longest sequence allowed, so offsets outside the contract
-// cannot move any access out of the buffers.
-struct SeqRows {
-    size_t row0;
-    int T;
-};
-__device__ __forceinline__ SeqRows rows_of(const ChunkArgs& a, int h, int c0, int c1) {
-    const int s0 = min(max(c0, 0), a.Ttot);
-    const int s1 = min(min(max(c1, s0), a.Ttot), s0 + a.T);
-    return {(size_t)h * a.Ttot + s0, s1 - s0};
-}
-__device__ __forceinline__ SeqRows seq_rows(const ChunkArgs& a, int bh) {
-    if (!a.cu) return {(size_t)bh * a.T, a.T};
-    const int n = bh / a.H;
-    return rows_of(a, bh - n * a.H, a.cu[n], a.cu[n + 1]);
-}
-
-// First row of sequence bh in the feature-mapped copies of the keys and
-// queries that the intra-chunk kernel writes to the workspace: each
-// (sequence, head) has its own T rows (packed calls: max_seqlen rows), so the
-// copies fit the workspace whatever the packed plane's length is.  Batched
-// calls: the same row as in the inputs.
-__device__ __forceinline__ size_t mapped_row0(const ChunkArgs& a, int bh) {
-    return (size_t)bh * a.T;
-}
-
-// The (batch*head) row of state-pass workgroup rank r: the natural order, or
-// for packed calls the sequences longest first (`order`), so the longest
-// sequences are dispatched first and none is left to run alone at the end.
-__device__ __forceinline__ int pass_bh(const ChunkArgs& a, int r) {
-    if (!a.order) return r;
-    const int i = r / a.H;
-    return a.order[i] * a.H + (r - i * a.H);
-}
 
 constexpr int kCuLds = 4096;  // offsets the schedule kernel copies to LDS
 
@@ -173,26 +137,6 @@ __global__ __launch_bounds__(1024) void packed_schedule_kernel(ChunkArgs a, int 
         }
     }
 }
-
-// The (batch*head row, tile) of intra-chunk job j.  Batched calls: row-major
-// over (row, tile).  Packed calls: only existing tiles, j = h * G + g with G
-// the tile count of all sequences and g a tile index in sequence order (so
-// consecutive jobs walk one head's plane in address order), the sequence of
-// g found in toff by binary search.
-struct Job {
-    int bh, tile;
-    SeqRows sr;
-};
-__device__ __forceinline__ Job job_of(const ChunkArgs& a, int j, int ntiles) {
-    if (!a.jobs) {
-        const int bh = j / ntiles;
-        return {bh, j - bh * ntiles, seq_rows(a, bh)};
-    }
-    const int4 e = reinterpret_cast<const int4*>(a.jobs)[j];
-    const int h = e.x - (e.x / a.H) * a.H;
-    return {e.x, e.y, {(size_t)h * a.Ttot + e.z, e.w}};
-}
-
 
 __device__ __forceinline__ u32x4 sel16(bool ok, u32x4 v) {
     return ok ? v : u32x4{0u, 0u, 0u, 0u};
@@ -816,19 +760,6 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs a, const void
 // out-of-range rows read as zero in hardware, and a lane's offsets stay
 // fixed from tile to tile.
 // ---------------------------------------------------------------------------
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
-    const int n = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFF0 ? 0x7FFFFFF0 : (int)bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kRawBufferFlags);
-}
-__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
-}
-__device__ __forceinline__ s16x4 buf_load8(rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(s16x4, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
-}
-
 template <int D, int CV, bool DELTA, bool COL, bool WIN>
 struct PassSmem {
     using R = Rec<EBf16, CV, DELTA>;
@@ -2030,6 +1961,25 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+hipError_t launch_packed_schedule(const ChunkArgs& a, int Ct, int ntiles, ChunkArgs& b,
+                                  hipStream_t stream) {
+    const int nbins = ntiles + 1;
+    if (!(a.cu && a.order_ws && ntiles > 0 && nbins <= 8192)) return hipSuccess;
+    // schedule layout: order [N], toff [N+1], then (256-byte aligned) the job
+    // table, 4 ints for each of at most BH * ntiles jobs
+    const int N = a.BH / a.H;
+    int* jobs = a.order_ws + ((2 * (size_t)N + 1 + 63) / 64) * 64;
+    const int cul = N + 1 <= kCuLds ? N + 1 : 0;
+    hipLaunchKernelGGL(packed_schedule_kernel, dim3(1), dim3(1024), (nbins + 1025 + cul) * sizeof(int),
+                       stream, a, Ct, nbins, a.order_ws, a.order_ws + N, jobs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    b.order = a.order_ws;
+    b.toff = a.order_ws + N;
+    b.jobs = jobs;
+    return hipSuccess;
+}
+
 template <class E, int D, int CV, bool DELTA, bool COL, bool WIN>
 static hipError_t launch_one(const ChunkArgs& a, void* ws, hipStream_t stream) {
     const int Wv = WIN ? a.W : 1;
@@ -2041,21 +1991,9 @@ static hipError_t launch_one(const ChunkArgs& a, void* ws, hipStream_t stream) {
     // the per-column rule's write vectors follow the records
     if constexpr (E::kBytes == 2 && COL)
         b.uws = static_cast<char*>(ws) + (size_t)a.BH * ntiles * Rec<E, CV, DELTA>::kBytes;
-    const int nbins = ntiles + 1;
-    if (a.cu && a.order_ws && ntiles > 0 && nbins <= 8192) {
-        // schedule layout: order [N], toff [N+1], then (256-byte aligned) the
-        // job table, 4 ints for each of at most BH * ntiles jobs
-        const int N = a.BH / a.H;
-        int* jobs = a.order_ws + ((2 * (size_t)N + 1 + 63) / 64) * 64;
-        const int cul = N + 1 <= kCuLds ? N + 1 : 0;
-        hipLaunchKernelGGL(packed_schedule_kernel, dim3(1), dim3(1024),
-                           (nbins + 1025 + cul) * sizeof(int),
-                           stream, a, CV / Wv, nbins, a.order_ws, a.order_ws + N, jobs);
-        hipError_t e = hipGetLastError();
+    {
+        hipError_t e = launch_packed_schedule(a, CV / Wv, ntiles, b, stream);
         if (e != hipSuccess) return e;
-        b.order = a.order_ws;
-        b.toff = a.order_ws + N;
-        b.jobs = jobs;
     }
     if (ntiles > 0) {
         if constexpr (E::kBytes == 2) {
@@ -2163,11 +2101,23 @@ size_t chunk_workspace_bytes(int BH, int T, int dt, int chunk, int window, int n
     }
     // bf16 per-column rule: the write vectors, chunk x D bf16 per tile
     if (dt == 1 && norm == kNormColumn) rb += (size_t)chunk * D * 2;
-    return (size_t)BH * ntiles * rb;
+    const size_t bytes = (size_t)BH * ntiles * rb;
+    // bf16 windows: room for the records of either form (the collapsed one
+    // runs the forward, the virtual-row one the backward's checkpoint runs)
+    if (dt == 1 && norm == kNormWindow && window >= 2) {
+        const size_t wb = window_workspace_bytes(BH, T, delta);
+        return wb > bytes ? wb : bytes;
+    }
+    return bytes;
 }
 
 hipError_t launch_chunk(const ChunkArgs& a, int dt, int D, int chunk, bool delta, void* ws,
                         hipStream_t stream) {
+    // the window rules at bf16 run the collapsed form (tiles of kWinC steps);
+    // the backward pass's checkpoint runs and the feature maps keep the
+    // virtual-row kernels
+    if (dt == 1 && a.norm == kNormWindow && a.W >= 2 && !a.ck_s && !a.phi)
+        return launch_window(a, D, delta, ws, stream);
     if (dt == 1) return launch_e<EBf16>(a, D, chunk, delta, ws, stream);
     return launch_e<EFp32>(a, D, chunk, delta, ws, stream);
 }

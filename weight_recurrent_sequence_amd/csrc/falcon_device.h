@@ -77,7 +77,20 @@ struct EBf16 {
         return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4*)(p));
     }
+    // K = 16 on the K = 32 instruction with a zero upper half.  Every bf16
+    // product of the library then has one MFMA shape: a 16x16x16 bf16 MFMA
+    // that takes its accumulator straight from a 16x16x32 one issued just
+    // before it (no wait states in between, which the compiler allows for an
+    // exactly overlapping accumulator) was seen to return wrong rows on gfx950.
     static __device__ __forceinline__ f32x4 mma16(Frag a, Frag b, f32x4 c) {
+        const Frag z = {0, 0, 0, 0};
+        return mma32(a, z, b, z, c);
+    }
+    // The 16x16x16 instruction itself (half the K = 32 issue cost), for
+    // accumulation chains built from it alone; the assembly of every kernel is
+    // checked for a 16x16x32 result feeding it as accumulator within a few
+    // wait states.
+    static __device__ __forceinline__ f32x4 mma16n(Frag a, Frag b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
     }
     static __device__ __forceinline__ f32x4 mma32(Frag a0, Frag a1, Frag b0, Frag b1, f32x4 c) {

@@ -153,6 +153,17 @@ struct BwdArgs {
 bool chunk_bwd_supported(int dt, int D, int chunk, int norm, int window);
 hipError_t launch_chunk_bwd(const BwdArgs& a, int D, int chunk, bool delta, hipStream_t stream);
 
+// Packed calls: orders the sequences longest first and lists the tiles of Ct
+// steps that exist (b.order, b.toff, b.jobs); nothing for batched calls.
+hipError_t launch_packed_schedule(const ChunkArgs& a, int Ct, int ntiles, ChunkArgs& b,
+                                  hipStream_t stream);
+
+// The window rules (W >= 2) at bf16 in the collapsed form: tiles of kWinC
+// steps whose C + W - 1 distinct (key, value) pairs carry the state update.
+constexpr int kWinC = 32;
+size_t window_workspace_bytes(int BH, int T, bool delta);
+hipError_t launch_window(const ChunkArgs& a, int D, bool delta, void* ws, hipStream_t stream);
+
 // dt: 0 fp32, 1 bf16.  Return false when the combination is not built.
 bool chunk_supported(int dt, int D, int chunk);
 // Bytes of the per-tile records the intra-chunk kernel hands to the

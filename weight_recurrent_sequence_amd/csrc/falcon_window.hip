@@ -1,0 +1,791 @@
+// falcon_window.hip -- the window rules (Falcon-3 / Falcon-3A, W >= 2) at
+// bf16 in a collapsed chunk form ("Fast Weight Attention for Continual
+// Learning", authors' abstract: the sliding-window mini-batch update has a
+// chunk-parallel form with positive-decay renormalization).
+//
+// Per tile of C = 32 steps s (tile-local), the window of step s holds the W
+// pairs p = s .. s + W - 1 of the tile's E = C + W - 1 distinct pairs
+// (x_p, y_p) = (k_{t0 - W + 1 - lag + p}, v_{t0 - W + 1 + p}); the virtual
+// row r = s W + w (slot w) learns pair p(r) = s + W - 1 - w.  With g_s the
+// tile-local cumulative log decay, D(s, s') = exp(g_s - g_s'), b_s the
+// window step eta_s / (sum_{p in win(s)} ||x_p||^2 + eps) and the pair Gram
+// G = X X^T, the residuals R of the CW virtual rows solve
+//     (I + A) R = G_v Y - diag(gamma_v) G_v Z,   Z = X S0^T,
+//     A[r][r'] = [s' < s] D(s, s') b_s' G[p(r)][p(r')],
+// (G_v: the CW x E row gather of the pairs; the inner-product rule writes
+// R = G_v Y instead).  Every later use of R goes through the pairs:
+//     state    S_C = gamma_last S0 + delta^T X,   delta = H^T R,
+//              H[r][p] = [p(r) = p] exp(g_last - g_s(r)) b_s(r);
+//     outputs  O = diag(gamma) Q S0^T + P R,
+//              P[t][r'] = [s' <= t] D(t, s') b_s' (q_t . x_p(r')).
+// With M' = (I + A)^-1 G_v and M = (I + A)^-1 diag(gamma_v) G_v (CW x E) the
+// state-independent parts collapse to E x E and C x E matrices,
+//     N' = H^T M',  N = H^T M,  L' = P M',  L = P M,
+//     delta = N' Y - N Z,   O = diag(gamma) Q S0^T + L' Y - L Z,
+// which the intra-chunk kernel forms (bf16 MFMA blocked forward
+// substitution, diagonal-block inverses from fp32 MFMA products) and stores
+// per tile.  The state pass then walks C steps per tile with dense products
+// only: X S0^T, [N' | -N] [Y; Z], the state update X^T delta and the
+// outputs; no triangular solve is left on its sequential path.  The
+// inner-product rule needs no system: delta_p = c_p y_p with
+// c_p = sum_{s: p in win(s)} h_s, and L'[t][p] = (q_t . x_p) c'(t, p) with
+// c'(t, p) = sum_{s' <= t, p in win(s')} D(t, s') b_s'.
+//
+// Every decay factor is exp(later - earlier) <= 1 of a log sum that
+// restarts at each tile: nothing divides by a cumulative product.
+#include "falcon_device.h"
+#include "falcon_internal.h"
+#include "falcon_records.h"
+#include "falcon_rows.h"
+
+namespace falcon {
+
+namespace {
+
+constexpr int kC = kWinC;        // steps per tile
+constexpr int kEP = 48;          // pair slots: C + W - 1 <= 39 pairs, three 16-blocks
+constexpr int kNPB = kEP / 16;   // pair blocks
+constexpr int kNTB = kC / 16;    // step blocks
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Record of one (batch*head, tile), bf16 MFMA fragments (64 lanes x 4 values,
+// lane (lr, grp) holding M[lr][4 grp + r] of an A fragment, M[4 grp + r][lr]
+// of a B fragment):
+//   delta family: A fragments of [N' | -N] (pair block pb, K block kb < 6),
+//                 B fragments of [L'^T; -L^T] (K block kb < 6, step block tb);
+//   inner-product family: B fragments of L'^T (kb < 3);
+// then floats: gamma_t = exp(g_t) (32), gamma_last at [32] and, for the
+// inner-product family, c_p at [64 + p] (48).
+template <bool DELTA>
+struct WinRec {
+    static constexpr int NFA = DELTA ? kNPB * 2 * kNPB : 0;
+    static constexpr int NKB = DELTA ? 2 * kNPB : kNPB;
+    static constexpr int NFB = kNTB * NKB;
+    static constexpr size_t kA = 0;
+    static constexpr size_t kB = (size_t)NFA * 512;
+    static constexpr size_t kF = kB + (size_t)NFB * 512;
+    static constexpr int NF = 128;
+    static constexpr size_t kBytes = (kF + NF * 4 + 255) / 256 * 256;
+    static __host__ __device__ constexpr int fa(int pb, int kb) { return pb * 2 * kNPB + kb; }
+    static __host__ __device__ constexpr int fb(int tb, int kb) { return tb * NKB + kb; }
+};
+
+// Step and pair of virtual row r (row r = s W + w learns pair s + W - 1 - w).
+template <int W>
+__host__ __device__ constexpr int row_step(int r) { return r / W; }
+template <int W>
+__host__ __device__ constexpr int row_pair(int r) { return r / W + W - 1 - (r - (r / W) * W); }
+
+// Strictly lower blocks of A: index of block (rb, cb), cb < rb.
+__host__ __device__ constexpr int lblk(int rb, int cb) { return rb * (rb - 1) / 2 + cb; }
+
+// Steps spanned by row block rb and the most over all blocks: the diagonal
+// block N of A is nilpotent of that order (each factor lowers the step).
+template <int W>
+constexpr int max_block_steps() {
+    int m = 0;
+    for (int rb = 0; rb < kC * W / 16; ++rb) {
+        const int n = row_step<W>(16 * rb + 15) - row_step<W>(16 * rb) + 1;
+        m = n > m ? n : m;
+    }
+    return m;
+}
+// Factors (I + (-N)^(2^j)), j < J, of (I + N)^-1 for N^(2^J) = 0.
+template <int W>
+constexpr int inv_factors() {
+    int j = 0;
+    while ((1 << j) < max_block_steps<W>()) ++j;
+    return j < 1 ? 1 : j;
+}
+
+// ---------------------------------------------------------------------------
+// Intra-chunk kernel: persistent, 256 threads, one (batch*head, tile) job at a
+// time.
+// ---------------------------------------------------------------------------
+template <int D, int W, bool DELTA>
+struct WinPrepSmem {
+    static constexpr int LDX = D + 8;
+    static constexpr int CW = kC * W, RB = CW / 16;
+    static constexpr int NA = DELTA ? RB * (RB - 1) / 2 : 1;
+    uint16_t X[kEP][LDX];                  // pair keys x_p (rows >= E zero)
+    uint16_t Q[kC][LDX];                   // queries
+    float G[DELTA ? kEP : 1][kEP + 1];     // pair Gram x_p . x_p'
+    float QK[kC][kEP + 1];                 // q_t . x_p
+    float al[kC], et[kC];                  // gates (padding steps: 1, 0)
+    float nrm[kEP];                        // ||x_p||^2
+    float g2[kC];                          // log2(e) * g_s
+    float bs[kC];                          // window step b_s
+    float hs[kC];                          // exp(g_last - g_s) b_s
+    float gam[kC];                         // exp(g_s)
+    float cf[DELTA ? CW : 1];              // exp2(gref(block of row j) - g2_s(j)) b_s(j)
+    float gref[DELTA ? RB : 1];            // g2 at the step of a row block's last row
+    float e2[DELTA ? 1 : kC * W];          // exp2(g2_t - g2_{t-d}) b_{t-d}, d < W
+    float cpp[DELTA ? 1 : kEP];            // c'(p, p), p < C
+    s16x4 Af[NA][64];                      // -A, strictly lower blocks
+    s16x4 Tdf[DELTA ? RB : 1][64];         // (I + A_bb)^-1
+    s16x4 Pf[kNTB][DELTA ? RB : 1][64];    // P blocks
+};
+
+template <int D, int W, bool DELTA>
+__global__ __launch_bounds__(256) void win_prep_kernel(ChunkArgs a, void* ws, int ntiles,
+                                                       int njobs) {
+    using E = EBf16;
+    using T = uint16_t;
+    using Frag = s16x4;
+    using R = WinRec<DELTA>;
+    using Smem = WinPrepSmem<D, W, DELTA>;
+    constexpr int CPR = D / 8, CW = Smem::CW, RB = Smem::RB;
+    constexpr int NP = kC + W - 1;  // pairs of a tile
+    __shared__ Smem sm;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4,
+              lr = lane & 15;
+    const float eps = a.eps;
+    if (a.toff) njobs = a.H * a.toff[a.BH / a.H];  // packed: the tiles that exist
+
+    for (int job = blockIdx.x; job < njobs; job += gridDim.x) {
+        const Job jb = job_of(a, job, ntiles);
+        const int bh = jb.bh, tile = jb.tile, T_ = jb.sr.T;
+        if (tile >= tiles_of(T_, kC)) continue;  // (uniform over the workgroup)
+        const int t0 = tile * kC;
+        const T* kg = static_cast<const T*>(a.k) + jb.sr.row0 * D;
+        const T* qg = static_cast<const T*>(a.q) + jb.sr.row0 * D;
+        const T* kp = a.k_prev ? static_cast<const T*>(a.k_prev) + (size_t)bh * W * D : nullptr;
+        char* rec = static_cast<char*>(ws) + ((size_t)bh * ntiles + tile) * R::kBytes;
+
+        // ---- stage pair keys, queries and gates ----
+        {
+            constexpr int NXL = (kEP * CPR + 255) / 256, NQL = (kC * CPR + 255) / 256;
+            u32x4 px[NXL], pq[NQL];
+#pragma unroll
+            for (int it = 0; it < NXL; ++it) {
+                const int c = tid + 256 * it;
+                const int p = c / CPR, col = (c % CPR) * 8;
+                const int tau = t0 - (W - 1) - a.lag + p;  // key of pair p
+                const T* src = nullptr;
+                if (c < kEP * CPR && p < NP && tau < T_) {
+                    if (tau >= 0) src = kg + (size_t)tau * D + col;
+                    else if (kp) src = kp + (size_t)(W + tau) * D + col;
+                }
+                px[it] = src ? *reinterpret_cast<const u32x4*>(src) : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int it = 0; it < NQL; ++it) {
+                const int c = tid + 256 * it;
+                const int t = c / CPR, col = (c % CPR) * 8;
+                pq[it] = (c < kC * CPR && t0 + t < T_)
+                             ? *reinterpret_cast<const u32x4*>(qg + (size_t)(t0 + t) * D + col)
+                             : u32x4{0u, 0u, 0u, 0u};
+            }
+            float al = 1.f, et = 0.f;
+            if (tid < kC && t0 + tid < T_) {
+                al = a.alpha[jb.sr.row0 + t0 + tid];
+                et = a.eta[jb.sr.row0 + t0 + tid];
+            }
+#pragma unroll
+            for (int it = 0; it < NXL; ++it) {
+                const int c = tid + 256 * it;
+                if (c < kEP * CPR) *reinterpret_cast<u32x4*>(&sm.X[c / CPR][(c % CPR) * 8]) = px[it];
+            }
+#pragma unroll
+            for (int it = 0; it < NQL; ++it) {
+                const int c = tid + 256 * it;
+                if (c < kC * CPR) *reinterpret_cast<u32x4*>(&sm.Q[c / CPR][(c % CPR) * 8]) = pq[it];
+            }
+            if (tid < kC) {
+                sm.al[tid] = al;
+                sm.et[tid] = et;
+            }
+        }
+        __syncthreads();
+
+        // ---- pair norms: 4 threads per pair ----
+        {
+            const int p = tid >> 2, part = tid & 3;
+            float n2 = 0.f;
+            if (p < kEP) {
+#pragma unroll
+                for (int c = 0; c < D / 4; c += 8) {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.X[p][part * (D / 4) + c]);
+                    const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const float x = E::to_f(e[u]);
+                        n2 += x * x;
+                    }
+                }
+            }
+            n2 = group_sum_dpp<4>(n2);
+            if (p < kEP && part == 0) sm.nrm[p] = n2;
+        }
+        __syncthreads();
+
+        // ---- log-decay scan, window steps, per-step factors (wave 0) ----
+        if (wave == 0) {
+            const int s = lane;
+            const float lg = wave_scan_dpp(s < kC ? __logf(sm.al[s]) : 0.f);
+            const float glast = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lg), kC - 1));
+            if (s < kC) {
+                float tot = 0.f;
+#pragma unroll
+                for (int w = 0; w < W; ++w) tot += sm.nrm[s + w];  // the pairs of step s
+                const float den = tot + eps;
+                const float b = den > 0.f ? sm.et[s] / den : 0.f;
+                sm.g2[s] = lg * kLog2e;
+                sm.bs[s] = b;
+                sm.hs[s] = __expf(glast - lg) * b;
+                sm.gam[s] = __expf(lg);
+            }
+        }
+        __syncthreads();
+
+        // ---- decay factors of the blocks; the Gram blocks on MFMA ----
+        if constexpr (DELTA) {
+            // column factors split at the last row of the column's block:
+            // exp(g_ref - g_s(j)) <= 1, the row's factor exp(g_s(i) - g_ref) <= 1
+            for (int j = tid; j < CW; j += 256) {
+                const int s = row_step<W>(j), sref = row_step<W>(16 * (j / 16) + 15);
+                sm.cf[j] = exp2f(sm.g2[sref] - sm.g2[s]) * sm.bs[s];
+                if ((j & 15) == 15) sm.gref[j >> 4] = sm.g2[s];
+            }
+        } else {
+            for (int i = tid; i < kC * W; i += 256) {
+                const int t = i / W, d = i - t * W;
+                sm.e2[i] = (t - d >= 0) ? exp2f(sm.g2[t] - sm.g2[t - d]) * sm.bs[t - d] : 0.f;
+            }
+        }
+        {
+            // rows as eight contiguous contraction elements per lane; lane
+            // (lr, grp) ends with rowA(16 bi + 4 grp + r) . rowB(16 bj + lr)
+            constexpr int NG = DELTA ? kNPB * kNPB : 0;
+            constexpr int NQ = kNTB * kNPB;
+            for (int q = wave; q < NG + NQ; q += 4) {
+                const bool isG = q < NG;
+                const int qq = isG ? q : q - NG;
+                const int bi = qq / kNPB, bj = qq - bi * kNPB;
+                const T* ar = (isG ? &sm.X[16 * bi + lr][0] : &sm.Q[16 * bi + lr][0]) + 8 * grp;
+                const T* br = &sm.X[16 * bj + lr][0] + 8 * grp;
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int m = 0; m < D / 32; ++m)
+                    acc = E::mma32r(E::load8(ar + 32 * m), E::load8(br + 32 * m), acc);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if constexpr (DELTA) {
+                        if (isG) sm.G[16 * bi + 4 * grp + r][16 * bj + lr] = acc[r];
+                        else sm.QK[16 * bi + 4 * grp + r][16 * bj + lr] = acc[r];
+                    } else {
+                        sm.QK[16 * bi + 4 * grp + r][16 * bj + lr] = acc[r];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+
+        if constexpr (DELTA) {
+            // ---- -A (strictly lower blocks), the diagonal inverses and P,
+            // round-robin over the waves ----
+            constexpr int NL = RB * (RB - 1) / 2;
+            constexpr int NJ = NL + RB + kNTB * RB;
+            for (int q = wave; q < NJ; q += 4) {
+                if (q < NL) {
+                    int rb = 1;
+                    while (lblk(rb + 1, 0) <= q) ++rb;
+                    const int cb = q - lblk(rb, 0);
+                    const int i = 16 * rb + lr, si = row_step<W>(i), pi = row_pair<W>(i);
+                    const float rf = exp2f(sm.g2[si] - sm.gref[cb]);
+                    f32x4 v;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = 16 * cb + 4 * grp + r;
+                        v[r] = (row_step<W>(j) < si) ? -(rf * sm.cf[j] * sm.G[pi][row_pair<W>(j)]) : 0.f;
+                    }
+                    sm.Af[q][lane] = E::pack(v);
+                } else if (q < NL + RB) {
+                    // (I + N)^-1, N the diagonal block (nilpotent: every nonzero
+                    // entry lowers the step), as the product of the factors
+                    // I + (-N)^(2^j) in fp32 MFMA.  Fragments: a(X) holds
+                    // X[lr][4 grp + r], b(X) holds X[4 grp + r][lr]; a product's
+                    // accumulator is b(XY), and a(X) = b(X^T).  The chain builds
+                    // c(F_{J-1}^T .. F_0^T) = c(Td^T) = a(Td).
+                    const int rb = q - NL;
+                    auto nval = [&](int i, int j) __attribute__((always_inline)) {
+                        const int si = row_step<W>(i), sj = row_step<W>(j);
+                        return sj < si ? exp2f(sm.g2[si] - sm.g2[sj]) * sm.bs[sj] *
+                                             sm.G[row_pair<W>(i)][row_pair<W>(j)]
+                                       : 0.f;
+                    };
+                    f32x4 aN, bN, aI;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        aN[r] = nval(16 * rb + lr, 16 * rb + 4 * grp + r);
+                        bN[r] = nval(16 * rb + 4 * grp + r, 16 * rb + lr);
+                        aI[r] = (lr == 4 * grp + r) ? 1.f : 0.f;
+                    }
+                    f32x4 Y = aI - aN;  // b(F_0^T) = a(I - N)
+                    f32x4 aP = aN, bP = bN;
+                    constexpr int J = inv_factors<W>();
+#pragma unroll
+                    for (int j = 1; j < J; ++j) {
+                        const f32x4 bP2 = EFp32::mma16(aP, bP, zero4());  // b(P^2)
+                        if (j + 1 < J) aP = EFp32::mma16(bP, aP, zero4());  // a(P^2) = c(P^T P^T)
+                        bP = bP2;
+                        Y = EFp32::mma16(aI + bP, Y, zero4());  // F_j^T Y, a(F_j^T) = b(F_j)
+                    }
+                    sm.Tdf[rb][lane] = E::pack(Y);
+                } else {
+                    const int qq = q - NL - RB;
+                    const int tb = qq / RB, rb = qq - tb * RB;
+                    const int t = 16 * tb + lr;
+                    // fully causal block: every row's step <= every t of the block
+                    const bool full = row_step<W>(16 * rb + 15) <= 16 * tb;
+                    const float rf = full ? exp2f(sm.g2[t] - sm.gref[rb]) : 0.f;
+                    f32x4 v;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = 16 * rb + 4 * grp + r, sj = row_step<W>(j);
+                        const float qk = sm.QK[t][row_pair<W>(j)];
+                        v[r] = full ? rf * sm.cf[j] * qk
+                                    : (sj <= t ? exp2f(sm.g2[t] - sm.g2[sj]) * sm.bs[sj] * qk : 0.f);
+                    }
+                    sm.Pf[tb][rb][lane] = E::pack(v);
+                }
+            }
+            __syncthreads();
+
+            // ---- blocked forward substitution (waves 0-2, pair block q each):
+            // M'_rb = Td_rb (G_v,rb - sum_{c<rb} A_rb,c M'_c) and the same for M
+            // with the gamma-scaled right-hand side; as each block of rows is
+            // done it enters N^T = M^T H and L^T = M^T P^T ----
+            if (wave < kNPB) {
+                const int q = wave;
+                Frag Mp[RB], Mg[RB];
+                f32x4 nP[kNPB], nG[kNPB], lP[kNTB], lG[kNTB];
+#pragma unroll
+                for (int i = 0; i < kNPB; ++i) nP[i] = nG[i] = zero4();
+#pragma unroll
+                for (int i = 0; i < kNTB; ++i) lP[i] = lG[i] = zero4();
+                static_for<RB>([&](auto rbc) __attribute__((always_inline)) {
+                    constexpr int rb = decltype(rbc)::value;
+                    f32x4 acc1, acc2;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 16 * rb + 4 * grp + r;
+                        const float one = (row_pair<W>(i) == 16 * q + lr) ? 1.f : 0.f;
+                        acc1[r] = one;
+                        acc2[r] = one * sm.gam[row_step<W>(i)];
+                    }
+                    static_for<rb>([&](auto cc) __attribute__((always_inline)) {
+                        constexpr int c = decltype(cc)::value;
+                        const Frag af = sm.Af[lblk(rb, c)][lane];
+                        acc1 = E::mma16(af, Mp[c], acc1);
+                        acc2 = E::mma16(af, Mg[c], acc2);
+                    });
+                    const Frag td = sm.Tdf[rb][lane];
+                    Mp[rb] = E::pack(E::mma16(td, E::pack(acc1), zero4()));
+                    Mg[rb] = E::pack(E::mma16(td, E::pack(acc2), zero4()));
+                    constexpr int plo = row_step<W>(16 * rb), phi_ = row_step<W>(16 * rb + 15) + W - 1;
+                    static_for<kNPB>([&](auto pbc) __attribute__((always_inline)) {
+                        constexpr int pb = decltype(pbc)::value;
+                        if constexpr (16 * pb <= phi_ && 16 * pb + 15 >= plo) {
+                            f32x4 h;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const int j = 16 * rb + 4 * grp + r;
+                                h[r] = (row_pair<W>(j) == 16 * pb + lr) ? sm.hs[row_step<W>(j)] : 0.f;
+                            }
+                            const Frag hb = E::pack(h);
+                            nP[pb] = E::mma16(Mp[rb], hb, nP[pb]);
+                            nG[pb] = E::mma16(Mg[rb], hb, nG[pb]);
+                        }
+                    });
+                    static_for<kNTB>([&](auto tbc) __attribute__((always_inline)) {
+                        constexpr int tb = decltype(tbc)::value;
+                        if constexpr (row_step<W>(16 * rb) <= 16 * tb + 15) {
+                            const Frag pf = sm.Pf[tb][rb][lane];
+                            lP[tb] = E::mma16(Mp[rb], pf, lP[tb]);
+                            lG[tb] = E::mma16(Mg[rb], pf, lG[tb]);
+                        }
+                    });
+                });
+                // the accumulator of N^T block (q, pb) is the A fragment of N
+                // block (pb, q); that of L^T block (q, tb) the B fragment of L^T
+                // block (q, tb)
+                Frag* fa = reinterpret_cast<Frag*>(rec + R::kA);
+                Frag* fb = reinterpret_cast<Frag*>(rec + R::kB);
+#pragma unroll
+                for (int pb = 0; pb < kNPB; ++pb) {
+                    fa[R::fa(pb, q) * 64 + lane] = E::pack(nP[pb]);
+                    fa[R::fa(pb, kNPB + q) * 64 + lane] = E::pack(-nG[pb]);
+                }
+#pragma unroll
+                for (int tb = 0; tb < kNTB; ++tb) {
+                    fb[R::fb(tb, q) * 64 + lane] = E::pack(lP[tb]);
+                    fb[R::fb(tb, kNPB + q) * 64 + lane] = E::pack(-lG[tb]);
+                }
+            } else {
+                float* fl = reinterpret_cast<float*>(rec + R::kF);
+                if (lane < kC) fl[lane] = sm.gam[lane];
+                if (lane == 0) fl[kC] = sm.gam[kC - 1];
+            }
+        } else {
+            // ---- inner-product family: c'(p, p) and c_p, then L'^T ----
+            if (tid < kEP) {
+                const int p = tid;
+                float cq = 0.f, c = 0.f;
+                if (p < kC) {
+#pragma unroll
+                    for (int d = 0; d < W; ++d)
+                        if (d <= p) cq += sm.e2[p * W + d];
+                }
+#pragma unroll
+                for (int d = 0; d < W; ++d) {
+                    const int s = p - d;  // steps whose window holds pair p
+                    if (p < NP && s >= 0 && s < kC) c += sm.hs[s];
+                }
+                sm.cpp[p] = cq;
+                float* fl = reinterpret_cast<float*>(rec + R::kF);
+                fl[64 + p] = c;
+                if (p < kC) fl[p] = sm.gam[p];
+                if (p == 0) fl[kC] = sm.gam[kC - 1];
+            }
+            __syncthreads();
+            Frag* fb = reinterpret_cast<Frag*>(rec + R::kB);
+            for (int q = wave; q < kNTB * kNPB; q += 4) {
+                const int tb = q / kNPB, kb = q - tb * kNPB;
+                const int t = 16 * tb + lr;
+                f32x4 v;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int p = 16 * kb + 4 * grp + r;
+                    float cp = 0.f;
+                    if (p <= t) {
+                        cp = exp2f(sm.g2[t] - sm.g2[p]) * sm.cpp[p];
+                    } else {
+                        // steps s' in [p - W + 1, t]: d = t - s'
+#pragma unroll
+                        for (int d = 0; d < W; ++d)
+                            if (t - d >= p - W + 1 && t - d >= 0) cp += sm.e2[t * W + d];
+                    }
+                    v[r] = sm.QK[t][p] * cp;
+                }
+                fb[R::fb(tb, kb) * 64 + lane] = E::pack(v);
+            }
+        }
+        __syncthreads();  // the next job's staging overwrites the tiles
+    }
+}
+
+// ---------------------------------------------------------------------------
+// State pass: one 512-thread workgroup per (batch*head, 64-wide value slice),
+// walking the tiles in order.  Waves 0-3 (16 value columns each) carry the
+// state slice as MFMA accumulators of S^T and form the tile's products and
+// outputs; waves 4-7 bring the next tile's pair keys, pair values, queries
+// and record into the other LDS buffer.  One barrier per tile.
+// ---------------------------------------------------------------------------
+template <int D, bool DELTA>
+struct WinPassSmem {
+    using R = WinRec<DELTA>;
+    static constexpr int LDX = D + 8, LDV = 64 + 8;
+    uint16_t X[2][kEP][LDX];   // pair keys
+    uint16_t Q[2][kC][LDX];    // queries
+    uint16_t V[2][kEP][LDV];   // pair values, this slice's 64 columns
+    alignas(16) char rec[2][R::kBytes];
+};
+
+template <int D, bool DELTA>
+__global__ __launch_bounds__(512) void win_pass_kernel(ChunkArgs a, const void* ws, int ntiles) {
+    using E = EBf16;
+    using T = uint16_t;
+    using Frag = s16x4;
+    using R = WinRec<DELTA>;
+    using Smem = WinPassSmem<D, DELTA>;
+    constexpr int LDX = Smem::LDX, LDV = Smem::LDV, KB = D / 16, NVS = D / 64, CPR = D / 8;
+    constexpr int RCH = (int)(R::kBytes / 16);
+    // 16-byte pieces per fill thread: pair keys, pair values, queries, record
+    constexpr int NXL = (kEP * CPR + 255) / 256, NVL = (kEP * 8 + 255) / 256;
+    constexpr int NQL = (kC * CPR + 255) / 256, NRL = (RCH + 255) / 256;
+    __shared__ Smem sm;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4,
+              lr = lane & 15;
+    const bool chain = wave < 4;
+    const int cw = wave & 3;
+    // slices of one sequence on one XCD (workgroup i runs on XCD i mod 8)
+    const int blk = blockIdx.x, xcd = blk & 7, jj = blk >> 3;
+    const int rr = (jj / NVS) * 8 + xcd, vs = jj % NVS;
+    if (rr >= a.BH) return;
+    const int bh = pass_bh(a, rr);
+    const int v0 = vs * 64;
+    const int W = a.W;
+    const int NP = kC + W - 1;
+    const SeqRows sr = seq_rows(a, bh);
+    const int T_ = sr.T;
+    const int ntl = tiles_of(T_, kC);
+    const T* qg = static_cast<const T*>(a.q) + sr.row0 * D;
+    const T* kg = static_cast<const T*>(a.k) + sr.row0 * D;
+    const T* vg = static_cast<const T*>(a.v) + sr.row0 * D + v0;
+    const T* kp = a.k_prev ? static_cast<const T*>(a.k_prev) + (size_t)bh * W * D : nullptr;
+    const T* vp = (a.v_prev && W > 1)
+                      ? static_cast<const T*>(a.v_prev) + (size_t)bh * (W - 1) * D + v0
+                      : nullptr;
+    const char* recg = static_cast<const char*>(ws) + (size_t)bh * ntiles * R::kBytes;
+    T* og = a.o ? static_cast<T*>(a.o) + sr.row0 * D + v0 : nullptr;
+
+    // state slice: Sacc[kb][r] = S[v][k], v = v0 + 16 cw + lr, k = 16 kb + 4 grp + r
+    const int vcol = v0 + 16 * cw + lr;
+    f32x4 Sacc[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+        Sacc[kb] = (chain && a.S0) ? *reinterpret_cast<const f32x4*>(
+                                         a.S0 + ((size_t)bh * D + vcol) * D + 16 * kb + 4 * grp)
+                                   : zero4();
+
+    // ---- fill waves: tile `tile` into buffer tile & 1, through registers ----
+    const int ft = tid - 256;
+    auto fill = [&](int tile) __attribute__((always_inline)) {
+        const int b = tile & 1, t0 = tile * kC;
+        u32x4 px[NXL], pv[NVL], pq[NQL], pr[NRL];
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int it = 0; it < NXL; ++it) {
+            const int c = ft + 256 * it;
+            const int p = c / CPR, col = (c % CPR) * 8;
+            const int tau = t0 - (W - 1) - a.lag + p;
+            const T* src = nullptr;
+            if (c < kEP * CPR && p < NP && tau < T_) {
+                if (tau >= 0) src = kg + (size_t)tau * D + col;
+                else if (kp) src = kp + (size_t)(W + tau) * D + col;
+            }
+            px[it] = src ? *reinterpret_cast<const u32x4*>(src) : z;
+        }
+#pragma unroll
+        for (int it = 0; it < NVL; ++it) {
+            const int c = ft + 256 * it;
+            const int p = c / 8, col = (c % 8) * 8;
+            const int tv = t0 - (W - 1) + p;  // value of pair p
+            const T* src = nullptr;
+            if (c < kEP * 8 && p < NP && tv < T_) {
+                if (tv >= 0) src = vg + (size_t)tv * D + col;
+                else if (vp) src = vp + (size_t)(W - 1 + tv) * D + col;
+            }
+            pv[it] = src ? *reinterpret_cast<const u32x4*>(src) : z;
+        }
+#pragma unroll
+        for (int it = 0; it < NQL; ++it) {
+            const int c = ft + 256 * it;
+            const int t = c / CPR, col = (c % CPR) * 8;
+            pq[it] = (c < kC * CPR && t0 + t < T_)
+                         ? *reinterpret_cast<const u32x4*>(qg + (size_t)(t0 + t) * D + col)
+                         : z;
+        }
+        const u32x4* rg = reinterpret_cast<const u32x4*>(recg + (size_t)tile * R::kBytes);
+#pragma unroll
+        for (int it = 0; it < NRL; ++it) {
+            const int c = ft + 256 * it;
+            pr[it] = c < RCH ? rg[c] : z;
+        }
+#pragma unroll
+        for (int it = 0; it < NXL; ++it) {
+            const int c = ft + 256 * it;
+            if (c < kEP * CPR) *reinterpret_cast<u32x4*>(&sm.X[b][c / CPR][(c % CPR) * 8]) = px[it];
+        }
+#pragma unroll
+        for (int it = 0; it < NVL; ++it) {
+            const int c = ft + 256 * it;
+            if (c < kEP * 8) *reinterpret_cast<u32x4*>(&sm.V[b][c / 8][(c % 8) * 8]) = pv[it];
+        }
+#pragma unroll
+        for (int it = 0; it < NQL; ++it) {
+            const int c = ft + 256 * it;
+            if (c < kC * CPR) *reinterpret_cast<u32x4*>(&sm.Q[b][c / CPR][(c % CPR) * 8]) = pq[it];
+        }
+#pragma unroll
+        for (int it = 0; it < NRL; ++it) {
+            const int c = ft + 256 * it;
+            if (c < RCH) reinterpret_cast<u32x4*>(sm.rec[b])[c] = pr[it];
+        }
+    };
+
+    // column fragment of a row-major LDS tile: lane (lr, grp) gets
+    // M[row0 + 4 grp + r][col0 + lr], r = 0..3
+    auto colfrag = [&](const T* m, int ld, int row0, int col0) __attribute__((always_inline)) {
+        return E::load_tr(m + (size_t)(row0 + 4 * grp + (lr >> 2)) * ld + col0 + 4 * (lr & 3));
+    };
+
+    // ---- chain waves: one tile ----
+    auto chain_tile = [&](int it) __attribute__((always_inline)) {
+        const int b = it & 1, t0 = it * kC;
+        const T* Xb = &sm.X[b][0][0];
+        const T* Qb = &sm.Q[b][0][0];
+        const T* Vb = &sm.V[b][0][0];
+        const Frag* FA = reinterpret_cast<const Frag*>(sm.rec[b] + R::kA);
+        const Frag* FB = reinterpret_cast<const Frag*>(sm.rec[b] + R::kB);
+        const float* FL = reinterpret_cast<const float*>(sm.rec[b] + R::kF);
+        Frag SB[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) SB[kb] = E::pack(Sacc[kb]);
+        // pair values of the wave's columns: b(Y block kb) = a(Y^T block kb)
+        Frag Vf[kNPB];
+#pragma unroll
+        for (int kb = 0; kb < kNPB; ++kb) Vf[kb] = colfrag(Vb, LDV, 16 * kb, 16 * cw);
+        Frag Zb[kNPB], Db[kNPB];
+        if constexpr (DELTA) {
+            // Z = X S0^T (pairs x the wave's value columns)
+            f32x4 Z[kNPB];
+#pragma unroll
+            for (int pb = 0; pb < kNPB; ++pb) Z[pb] = zero4();
+#pragma unroll
+            for (int m = 0; m < D / 32; ++m) {
+#pragma unroll
+                for (int pb = 0; pb < kNPB; ++pb) {
+                    const T* xr = Xb + (size_t)(16 * pb + lr) * LDX + 32 * m + 4 * grp;
+                    Z[pb] = E::mma32(E::load(xr), E::load(xr + 16), SB[2 * m], SB[2 * m + 1], Z[pb]);
+                }
+            }
+#pragma unroll
+            for (int pb = 0; pb < kNPB; ++pb) Zb[pb] = E::pack(Z[pb]);
+            // delta = [N' | -N] [Y; Z]
+#pragma unroll
+            for (int pb = 0; pb < kNPB; ++pb) {
+                f32x4 acc = zero4();
+                acc = E::mma32(FA[R::fa(pb, 0) * 64 + lane], FA[R::fa(pb, 1) * 64 + lane], Vf[0], Vf[1],
+                               acc);
+                acc = E::mma32(FA[R::fa(pb, 2) * 64 + lane], FA[R::fa(pb, 3) * 64 + lane], Vf[2], Zb[0],
+                               acc);
+                acc = E::mma32(FA[R::fa(pb, 4) * 64 + lane], FA[R::fa(pb, 5) * 64 + lane], Zb[1], Zb[2],
+                               acc);
+                Db[pb] = E::pack(acc);
+            }
+        } else {
+            // delta_p = c_p y_p
+#pragma unroll
+            for (int pb = 0; pb < kNPB; ++pb) {
+                const f32x4 c4 = *reinterpret_cast<const f32x4*>(FL + 64 + 16 * pb + 4 * grp);
+                f32x4 d;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) d[r] = c4[r] * E::to_f((T)Vf[pb][r]);
+                Db[pb] = E::pack(d);
+            }
+        }
+        // S^T = gamma_last S0^T + X^T delta
+        const float glast = FL[kC];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            f32x4 acc = Sacc[kb] * glast;
+            acc = E::mma32(colfrag(Xb, LDX, 0, 16 * kb), colfrag(Xb, LDX, 16, 16 * kb), Db[0], Db[1], acc);
+            acc = E::mma16(colfrag(Xb, LDX, 32, 16 * kb), Db[2], acc);
+            Sacc[kb] = acc;
+        }
+        // O^T = (S0 Q^T) diag(gamma) + Y^T L'^T - Z^T L^T; lane ends with
+        // O[t = 16 tb + lr][v = 16 cw + 4 grp + r]
+#pragma unroll
+        for (int tb = 0; tb < kNTB; ++tb) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int m = 0; m < D / 32; ++m) {
+                const T* qr = Qb + (size_t)(16 * tb + lr) * LDX + 32 * m + 4 * grp;
+                acc = E::mma32(SB[2 * m], SB[2 * m + 1], E::load(qr), E::load(qr + 16), acc);
+            }
+            acc = acc * FL[16 * tb + lr];
+            if constexpr (DELTA) {
+                acc = E::mma32(Vf[0], Vf[1], FB[R::fb(tb, 0) * 64 + lane], FB[R::fb(tb, 1) * 64 + lane],
+                               acc);
+                acc = E::mma32(Vf[2], Zb[0], FB[R::fb(tb, 2) * 64 + lane], FB[R::fb(tb, 3) * 64 + lane],
+                               acc);
+                acc = E::mma32(Zb[1], Zb[2], FB[R::fb(tb, 4) * 64 + lane], FB[R::fb(tb, 5) * 64 + lane],
+                               acc);
+            } else {
+                acc = E::mma32(Vf[0], Vf[1], FB[R::fb(tb, 0) * 64 + lane], FB[R::fb(tb, 1) * 64 + lane],
+                               acc);
+                acc = E::mma16(Vf[2], FB[R::fb(tb, 2) * 64 + lane], acc);
+            }
+            const int t = 16 * tb + lr;
+            if (og && t0 + t < T_)
+                *reinterpret_cast<Frag*>(og + (size_t)(t0 + t) * D + 16 * cw + 4 * grp) = E::pack(acc);
+        }
+    };
+
+    if (!chain && ntl > 0) fill(0);
+    __syncthreads();
+    for (int it = 0; it < ntl; ++it) {
+        if (chain) chain_tile(it);
+        else if (it + 1 < ntl) fill(it + 1);
+        __syncthreads();
+    }
+
+    if (chain && a.S_final) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            *reinterpret_cast<f32x4*>(a.S_final + ((size_t)bh * D + vcol) * D + 16 * kb + 4 * grp) =
+                Sacc[kb];
+    }
+}
+
+template <int D, int W, bool DELTA>
+hipError_t launch_prep(const ChunkArgs& b, void* ws, int ntiles, hipStream_t stream) {
+    using Smem = WinPrepSmem<D, W, DELTA>;
+    constexpr int per_cu_lds = (int)(163840 / sizeof(Smem));
+    constexpr int per_cu = per_cu_lds < 1 ? 1 : (per_cu_lds > 2 ? 2 : per_cu_lds);
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        cus = 256;
+    const int njobs = b.BH * ntiles;
+    const int grid = njobs < cus * per_cu ? njobs : cus * per_cu;
+    hipLaunchKernelGGL((win_prep_kernel<D, W, DELTA>), dim3(grid), dim3(256), 0, stream, b, ws,
+                       ntiles, njobs);
+    return hipGetLastError();
+}
+
+template <int D, bool DELTA>
+hipError_t launch_prep_w(const ChunkArgs& b, void* ws, int ntiles, hipStream_t stream) {
+    switch (b.W) {
+        case 2: return launch_prep<D, 2, DELTA>(b, ws, ntiles, stream);
+        case 3: return launch_prep<D, 3, DELTA>(b, ws, ntiles, stream);
+        case 4: return launch_prep<D, 4, DELTA>(b, ws, ntiles, stream);
+        case 5: return launch_prep<D, 5, DELTA>(b, ws, ntiles, stream);
+        case 6: return launch_prep<D, 6, DELTA>(b, ws, ntiles, stream);
+        case 7: return launch_prep<D, 7, DELTA>(b, ws, ntiles, stream);
+        case 8: return launch_prep<D, 8, DELTA>(b, ws, ntiles, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int D, bool DELTA>
+hipError_t launch_d(const ChunkArgs& a, void* ws, hipStream_t stream) {
+    const int ntiles = tiles_of(a.T, kC);
+    ChunkArgs b = a;
+    b.order = nullptr;
+    b.toff = nullptr;
+    b.jobs = nullptr;
+    hipError_t e = launch_packed_schedule(a, kC, ntiles, b, stream);
+    if (e != hipSuccess) return e;
+    if (ntiles > 0) {
+        e = launch_prep_w<D, DELTA>(b, ws, ntiles, stream);
+        if (e != hipSuccess) return e;
+    }
+    const int nvs = D / 64;
+    const int bh8 = (b.BH + 7) / 8 * 8;
+    hipLaunchKernelGGL((win_pass_kernel<D, DELTA>), dim3(bh8 * nvs), dim3(512), 0, stream, b,
+                       (const void*)ws, ntiles);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t window_workspace_bytes(int BH, int T, bool delta) {
+    const size_t nt = (size_t)tiles_of(T, kC);
+    return (size_t)BH * nt * (delta ? WinRec<true>::kBytes : WinRec<false>::kBytes);
+}
+
+hipError_t launch_window(const ChunkArgs& a, int D, bool delta, void* ws, hipStream_t stream) {
+    if (a.W < 2 || a.W > 8) return hipErrorInvalidValue;
+    if (D == 64) return delta ? launch_d<64, true>(a, ws, stream) : launch_d<64, false>(a, ws, stream);
+    if (D == 128) return delta ? launch_d<128, true>(a, ws, stream) : launch_d<128, false>(a, ws, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace falcon
