@@ -478,46 +478,62 @@ __global__ __launch_bounds__(256) void win_prep_kernel(ChunkArgs a, void* ws, in
 }
 
 // ---------------------------------------------------------------------------
-// State pass: one 512-thread workgroup per (batch*head, 64-wide value slice),
-// walking the tiles in order.  Waves 0-3 (16 value columns each) carry the
-// state slice as MFMA accumulators of S^T and form the tile's products and
-// outputs; waves 4-7 bring the next tile's pair keys, pair values, queries
-// and record into the other LDS buffer.  One barrier per tile.
+// State pass: one workgroup per (batch*head, 16-wide value slice), walking the
+// tiles in order.  Wave 0 carries the slice's state as MFMA accumulators of
+// S^T and forms the products the next state needs (X S0^T, delta, the update);
+// wave 1 forms the tile's outputs from the state at the tile's start, which
+// wave 0 hands over through LDS; waves 2 .. 2 + NF - 1 bring the tiles into
+// LDS, wave f the tiles it = f (mod NF), whose loads it issues NF tiles ahead.
+// One LDS-only barrier per tile.
+//
+// Key and query tiles hold rows of D elements with no padding; the 16-byte
+// chunk j of row r sits at chunk j ^ swz(r), which spreads both the row reads
+// (16 rows, one chunk) and the transposing column reads (four rows, two
+// chunks) of a wave over distinct banks.
 // ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    // D = 128: a row spans the 64 banks; D = 64: two rows do (the row's
+    // parity picks the half)
+    return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+}
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int c) {
+    return r * D + ((((c >> 3) ^ swz<D>(r)) << 3) | (c & 7));
+}
+
 template <int D, bool DELTA>
 struct WinPassSmem {
     using R = WinRec<DELTA>;
-    static constexpr int LDX = D + 8, LDV = 64 + 8;
-    uint16_t X[2][kEP][LDX];   // pair keys
-    uint16_t Q[2][kC][LDX];    // queries
-    uint16_t V[2][kEP][LDV];   // pair values, this slice's 64 columns
+    uint16_t X[2][kEP * D];    // pair keys (swizzled rows)
+    uint16_t Q[2][kC * D];     // queries (swizzled rows)
+    uint16_t V[2][kEP * 16];   // pair values of the slice's 16 columns
     alignas(16) char rec[2][R::kBytes];
+    s16x4 SB[2][D / 16][64];   // the state at a tile's start, B fragments of S^T
 };
 
+constexpr int kPassFill = 4;  // fill waves = tiles in flight
+
 template <int D, bool DELTA>
-__global__ __launch_bounds__(512) void win_pass_kernel(ChunkArgs a, const void* ws, int ntiles) {
+__global__ __launch_bounds__(64 * (2 + kPassFill)) void win_pass_kernel(ChunkArgs a, const void* ws,
+                                                                        int ntiles) {
     using E = EBf16;
     using T = uint16_t;
     using Frag = s16x4;
     using R = WinRec<DELTA>;
     using Smem = WinPassSmem<D, DELTA>;
-    constexpr int LDX = Smem::LDX, LDV = Smem::LDV, KB = D / 16, NVS = D / 64, CPR = D / 8;
-    constexpr int RCH = (int)(R::kBytes / 16);
-    // 16-byte pieces per fill thread: pair keys, pair values, queries, record
-    constexpr int NXL = (kEP * CPR + 255) / 256, NVL = (kEP * 8 + 255) / 256;
-    constexpr int NQL = (kC * CPR + 255) / 256, NRL = (RCH + 255) / 256;
+    constexpr int KB = D / 16, NVS = D / 16, CPR = D / 8, NF = kPassFill;
+    constexpr int RCH = (int)(R::kBytes / 16);  // 16-byte pieces of a record
     __shared__ Smem sm;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4,
               lr = lane & 15;
-    const bool chain = wave < 4;
-    const int cw = wave & 3;
     // slices of one sequence on one XCD (workgroup i runs on XCD i mod 8)
     const int blk = blockIdx.x, xcd = blk & 7, jj = blk >> 3;
     const int rr = (jj / NVS) * 8 + xcd, vs = jj % NVS;
     if (rr >= a.BH) return;
     const int bh = pass_bh(a, rr);
-    const int v0 = vs * 64;
+    const int v0 = vs * 16;
     const int W = a.W;
     const int NP = kC + W - 1;
     const SeqRows sr = seq_rows(a, bh);
@@ -531,195 +547,298 @@ __global__ __launch_bounds__(512) void win_pass_kernel(ChunkArgs a, const void* 
                       ? static_cast<const T*>(a.v_prev) + (size_t)bh * (W - 1) * D + v0
                       : nullptr;
     const char* recg = static_cast<const char*>(ws) + (size_t)bh * ntiles * R::kBytes;
-    T* og = a.o ? static_cast<T*>(a.o) + sr.row0 * D + v0 : nullptr;
 
-    // state slice: Sacc[kb][r] = S[v][k], v = v0 + 16 cw + lr, k = 16 kb + 4 grp + r
-    const int vcol = v0 + 16 * cw + lr;
-    f32x4 Sacc[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-        Sacc[kb] = (chain && a.S0) ? *reinterpret_cast<const f32x4*>(
-                                         a.S0 + ((size_t)bh * D + vcol) * D + 16 * kb + 4 * grp)
-                                   : zero4();
-
-    // ---- fill waves: tile `tile` into buffer tile & 1, through registers ----
-    const int ft = tid - 256;
-    auto fill = [&](int tile) __attribute__((always_inline)) {
-        const int b = tile & 1, t0 = tile * kC;
-        u32x4 px[NXL], pv[NVL], pq[NQL], pr[NRL];
-        const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int it = 0; it < NXL; ++it) {
-            const int c = ft + 256 * it;
-            const int p = c / CPR, col = (c % CPR) * 8;
-            const int tau = t0 - (W - 1) - a.lag + p;
-            const T* src = nullptr;
-            if (c < kEP * CPR && p < NP && tau < T_) {
-                if (tau >= 0) src = kg + (size_t)tau * D + col;
-                else if (kp) src = kp + (size_t)(W + tau) * D + col;
-            }
-            px[it] = src ? *reinterpret_cast<const u32x4*>(src) : z;
-        }
-#pragma unroll
-        for (int it = 0; it < NVL; ++it) {
-            const int c = ft + 256 * it;
-            const int p = c / 8, col = (c % 8) * 8;
-            const int tv = t0 - (W - 1) + p;  // value of pair p
-            const T* src = nullptr;
-            if (c < kEP * 8 && p < NP && tv < T_) {
-                if (tv >= 0) src = vg + (size_t)tv * D + col;
-                else if (vp) src = vp + (size_t)(W - 1 + tv) * D + col;
-            }
-            pv[it] = src ? *reinterpret_cast<const u32x4*>(src) : z;
-        }
-#pragma unroll
-        for (int it = 0; it < NQL; ++it) {
-            const int c = ft + 256 * it;
-            const int t = c / CPR, col = (c % CPR) * 8;
-            pq[it] = (c < kC * CPR && t0 + t < T_)
-                         ? *reinterpret_cast<const u32x4*>(qg + (size_t)(t0 + t) * D + col)
-                         : z;
-        }
-        const u32x4* rg = reinterpret_cast<const u32x4*>(recg + (size_t)tile * R::kBytes);
-#pragma unroll
-        for (int it = 0; it < NRL; ++it) {
-            const int c = ft + 256 * it;
-            pr[it] = c < RCH ? rg[c] : z;
-        }
-#pragma unroll
-        for (int it = 0; it < NXL; ++it) {
-            const int c = ft + 256 * it;
-            if (c < kEP * CPR) *reinterpret_cast<u32x4*>(&sm.X[b][c / CPR][(c % CPR) * 8]) = px[it];
-        }
-#pragma unroll
-        for (int it = 0; it < NVL; ++it) {
-            const int c = ft + 256 * it;
-            if (c < kEP * 8) *reinterpret_cast<u32x4*>(&sm.V[b][c / 8][(c % 8) * 8]) = pv[it];
-        }
-#pragma unroll
-        for (int it = 0; it < NQL; ++it) {
-            const int c = ft + 256 * it;
-            if (c < kC * CPR) *reinterpret_cast<u32x4*>(&sm.Q[b][c / CPR][(c % CPR) * 8]) = pq[it];
-        }
-#pragma unroll
-        for (int it = 0; it < NRL; ++it) {
-            const int c = ft + 256 * it;
-            if (c < RCH) reinterpret_cast<u32x4*>(sm.rec[b])[c] = pr[it];
-        }
+    // row fragment (8 bytes) of a swizzled tile: row r, columns c .. c + 3
+    auto rowld = [&](const T* m, int r, int c) __attribute__((always_inline)) {
+        return E::load(m + tile_off<D>(r, c));
     };
-
-    // column fragment of a row-major LDS tile: lane (lr, grp) gets
+    // column fragment of a swizzled tile: lane (lr, grp) gets
     // M[row0 + 4 grp + r][col0 + lr], r = 0..3
-    auto colfrag = [&](const T* m, int ld, int row0, int col0) __attribute__((always_inline)) {
-        return E::load_tr(m + (size_t)(row0 + 4 * grp + (lr >> 2)) * ld + col0 + 4 * (lr & 3));
+    auto colfrag = [&](const T* m, int row0, int col0) __attribute__((always_inline)) {
+        return E::load_tr(m + tile_off<D>(row0 + 4 * grp + (lr >> 2), col0 + 4 * (lr & 3)));
+    };
+    // the pair values: b(Y block kb) = a(Y^T block kb), rows of 16 elements
+    auto vfrag = [&](const T* vb, int kb) __attribute__((always_inline)) {
+        return E::load_tr(vb + (16 * kb + 4 * grp + (lr >> 2)) * 16 + 4 * (lr & 3));
     };
 
-    // ---- chain waves: one tile ----
-    auto chain_tile = [&](int it) __attribute__((always_inline)) {
-        const int b = it & 1, t0 = it * kC;
-        const T* Xb = &sm.X[b][0][0];
-        const T* Qb = &sm.Q[b][0][0];
-        const T* Vb = &sm.V[b][0][0];
-        const Frag* FA = reinterpret_cast<const Frag*>(sm.rec[b] + R::kA);
-        const Frag* FB = reinterpret_cast<const Frag*>(sm.rec[b] + R::kB);
-        const float* FL = reinterpret_cast<const float*>(sm.rec[b] + R::kF);
+    if (wave == 0) {
+        // ---- the state chain ----
+        // Sacc[kb][r] = S[v][k], v = v0 + lr, k = 16 kb + 4 grp + r
+        f32x4 Sacc[KB];
         Frag SB[KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) SB[kb] = E::pack(Sacc[kb]);
-        // pair values of the wave's columns: b(Y block kb) = a(Y^T block kb)
-        Frag Vf[kNPB];
+        for (int kb = 0; kb < KB; ++kb) {
+            Sacc[kb] = a.S0 ? *reinterpret_cast<const f32x4*>(
+                                  a.S0 + ((size_t)bh * D + v0 + lr) * D + 16 * kb + 4 * grp)
+                            : zero4();
+            SB[kb] = E::pack(Sacc[kb]);
+            sm.SB[0][kb][lane] = SB[kb];
+        }
+        lds_barrier();
+        for (int it = 0; it < ntl; ++it) {
+            const int b = it & 1;
+            const T* Xb = sm.X[b];
+            const char* rec = sm.rec[b];
+            const Frag* FA = reinterpret_cast<const Frag*>(rec + R::kA);
+            const float* FL = reinterpret_cast<const float*>(rec + R::kF);
+            Frag Vf[kNPB], Db[kNPB];
 #pragma unroll
-        for (int kb = 0; kb < kNPB; ++kb) Vf[kb] = colfrag(Vb, LDV, 16 * kb, 16 * cw);
-        Frag Zb[kNPB], Db[kNPB];
-        if constexpr (DELTA) {
-            // Z = X S0^T (pairs x the wave's value columns)
-            f32x4 Z[kNPB];
+            for (int kb = 0; kb < kNPB; ++kb) Vf[kb] = vfrag(sm.V[b], kb);
+            if constexpr (DELTA) {
+                // Z = X S0^T (pairs x the slice's columns)
+                f32x4 Z[kNPB];
 #pragma unroll
-            for (int pb = 0; pb < kNPB; ++pb) Z[pb] = zero4();
+                for (int pb = 0; pb < kNPB; ++pb) Z[pb] = zero4();
 #pragma unroll
-            for (int m = 0; m < D / 32; ++m) {
+                for (int m = 0; m < D / 32; ++m) {
+#pragma unroll
+                    for (int pb = 0; pb < kNPB; ++pb)
+                        Z[pb] = E::mma32(rowld(Xb, 16 * pb + lr, 32 * m + 4 * grp),
+                                         rowld(Xb, 16 * pb + lr, 32 * m + 16 + 4 * grp), SB[2 * m],
+                                         SB[2 * m + 1], Z[pb]);
+                }
+                Frag Zb[kNPB];
+#pragma unroll
+                for (int pb = 0; pb < kNPB; ++pb) Zb[pb] = E::pack(Z[pb]);
+                // delta = [N' | -N] [Y; Z]
 #pragma unroll
                 for (int pb = 0; pb < kNPB; ++pb) {
-                    const T* xr = Xb + (size_t)(16 * pb + lr) * LDX + 32 * m + 4 * grp;
-                    Z[pb] = E::mma32(E::load(xr), E::load(xr + 16), SB[2 * m], SB[2 * m + 1], Z[pb]);
+                    f32x4 acc = E::mma32(FA[R::fa(pb, 0) * 64 + lane], FA[R::fa(pb, 1) * 64 + lane],
+                                         Vf[0], Vf[1], zero4());
+                    acc = E::mma32(FA[R::fa(pb, 2) * 64 + lane], FA[R::fa(pb, 3) * 64 + lane], Vf[2],
+                                   Zb[0], acc);
+                    acc = E::mma32(FA[R::fa(pb, 4) * 64 + lane], FA[R::fa(pb, 5) * 64 + lane], Zb[1],
+                                   Zb[2], acc);
+                    Db[pb] = E::pack(acc);
+                }
+            } else {
+                // delta_p = c_p y_p
+#pragma unroll
+                for (int pb = 0; pb < kNPB; ++pb) {
+                    const f32x4 c4 = *reinterpret_cast<const f32x4*>(FL + 64 + 16 * pb + 4 * grp);
+                    f32x4 d;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) d[r] = c4[r] * E::to_f((T)Vf[pb][r]);
+                    Db[pb] = E::pack(d);
                 }
             }
+            // S^T = gamma_last S0^T + X^T delta, handed to the output wave
+            const float glast = FL[kC];
+            const Frag z = {0, 0, 0, 0};
 #pragma unroll
-            for (int pb = 0; pb < kNPB; ++pb) Zb[pb] = E::pack(Z[pb]);
-            // delta = [N' | -N] [Y; Z]
-#pragma unroll
-            for (int pb = 0; pb < kNPB; ++pb) {
-                f32x4 acc = zero4();
-                acc = E::mma32(FA[R::fa(pb, 0) * 64 + lane], FA[R::fa(pb, 1) * 64 + lane], Vf[0], Vf[1],
-                               acc);
-                acc = E::mma32(FA[R::fa(pb, 2) * 64 + lane], FA[R::fa(pb, 3) * 64 + lane], Vf[2], Zb[0],
-                               acc);
-                acc = E::mma32(FA[R::fa(pb, 4) * 64 + lane], FA[R::fa(pb, 5) * 64 + lane], Zb[1], Zb[2],
-                               acc);
-                Db[pb] = E::pack(acc);
+            for (int kb = 0; kb < KB; ++kb) {
+                f32x4 acc = Sacc[kb] * glast;
+                acc = E::mma32(colfrag(Xb, 0, 16 * kb), colfrag(Xb, 16, 16 * kb), Db[0], Db[1], acc);
+                acc = E::mma32(colfrag(Xb, 32, 16 * kb), z, Db[2], z, acc);
+                Sacc[kb] = acc;
+                SB[kb] = E::pack(acc);
+                sm.SB[b ^ 1][kb][lane] = SB[kb];
             }
-        } else {
-            // delta_p = c_p y_p
-#pragma unroll
-            for (int pb = 0; pb < kNPB; ++pb) {
-                const f32x4 c4 = *reinterpret_cast<const f32x4*>(FL + 64 + 16 * pb + 4 * grp);
-                f32x4 d;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) d[r] = c4[r] * E::to_f((T)Vf[pb][r]);
-                Db[pb] = E::pack(d);
-            }
+            lds_barrier();
         }
-        // S^T = gamma_last S0^T + X^T delta
-        const float glast = FL[kC];
+        if (a.S_final) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            f32x4 acc = Sacc[kb] * glast;
-            acc = E::mma32(colfrag(Xb, LDX, 0, 16 * kb), colfrag(Xb, LDX, 16, 16 * kb), Db[0], Db[1], acc);
-            acc = E::mma16(colfrag(Xb, LDX, 32, 16 * kb), Db[2], acc);
-            Sacc[kb] = acc;
+            for (int kb = 0; kb < KB; ++kb)
+                *reinterpret_cast<f32x4*>(a.S_final + ((size_t)bh * D + v0 + lr) * D + 16 * kb +
+                                          4 * grp) = Sacc[kb];
         }
-        // O^T = (S0 Q^T) diag(gamma) + Y^T L'^T - Z^T L^T; lane ends with
-        // O[t = 16 tb + lr][v = 16 cw + 4 grp + r]
+    } else if (wave == 1) {
+        // ---- the outputs: O^T = (S0 Q^T) diag(gamma) + Y^T L'^T - Z^T L^T;
+        // lane ends with O[t = 16 tb + lr][v = v0 + 4 grp + r] ----
+        T* og = a.o ? static_cast<T*>(a.o) + sr.row0 * D + v0 : nullptr;
+        lds_barrier();
+        for (int it = 0; it < ntl; ++it) {
+            const int b = it & 1, t0 = it * kC;
+            const T* Xb = sm.X[b];
+            const T* Qb = sm.Q[b];
+            const char* rec = sm.rec[b];
+            const Frag* FB = reinterpret_cast<const Frag*>(rec + R::kB);
+            const float* FL = reinterpret_cast<const float*>(rec + R::kF);
+            Frag SB[KB], Vf[kNPB];
 #pragma unroll
-        for (int tb = 0; tb < kNTB; ++tb) {
-            f32x4 acc = zero4();
+            for (int kb = 0; kb < KB; ++kb) SB[kb] = sm.SB[b][kb][lane];
 #pragma unroll
-            for (int m = 0; m < D / 32; ++m) {
-                const T* qr = Qb + (size_t)(16 * tb + lr) * LDX + 32 * m + 4 * grp;
-                acc = E::mma32(SB[2 * m], SB[2 * m + 1], E::load(qr), E::load(qr + 16), acc);
-            }
-            acc = acc * FL[16 * tb + lr];
+            for (int kb = 0; kb < kNPB; ++kb) Vf[kb] = vfrag(sm.V[b], kb);
+            Frag Zb[kNPB];
             if constexpr (DELTA) {
-                acc = E::mma32(Vf[0], Vf[1], FB[R::fb(tb, 0) * 64 + lane], FB[R::fb(tb, 1) * 64 + lane],
-                               acc);
-                acc = E::mma32(Vf[2], Zb[0], FB[R::fb(tb, 2) * 64 + lane], FB[R::fb(tb, 3) * 64 + lane],
-                               acc);
-                acc = E::mma32(Zb[1], Zb[2], FB[R::fb(tb, 4) * 64 + lane], FB[R::fb(tb, 5) * 64 + lane],
-                               acc);
-            } else {
-                acc = E::mma32(Vf[0], Vf[1], FB[R::fb(tb, 0) * 64 + lane], FB[R::fb(tb, 1) * 64 + lane],
-                               acc);
-                acc = E::mma16(Vf[2], FB[R::fb(tb, 2) * 64 + lane], acc);
-            }
-            const int t = 16 * tb + lr;
-            if (og && t0 + t < T_)
-                *reinterpret_cast<Frag*>(og + (size_t)(t0 + t) * D + 16 * cw + 4 * grp) = E::pack(acc);
-        }
-    };
-
-    if (!chain && ntl > 0) fill(0);
-    __syncthreads();
-    for (int it = 0; it < ntl; ++it) {
-        if (chain) chain_tile(it);
-        else if (it + 1 < ntl) fill(it + 1);
-        __syncthreads();
-    }
-
-    if (chain && a.S_final) {
+                f32x4 Z[kNPB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-            *reinterpret_cast<f32x4*>(a.S_final + ((size_t)bh * D + vcol) * D + 16 * kb + 4 * grp) =
-                Sacc[kb];
+                for (int pb = 0; pb < kNPB; ++pb) Z[pb] = zero4();
+#pragma unroll
+                for (int m = 0; m < D / 32; ++m) {
+#pragma unroll
+                    for (int pb = 0; pb < kNPB; ++pb)
+                        Z[pb] = E::mma32(rowld(Xb, 16 * pb + lr, 32 * m + 4 * grp),
+                                         rowld(Xb, 16 * pb + lr, 32 * m + 16 + 4 * grp), SB[2 * m],
+                                         SB[2 * m + 1], Z[pb]);
+                }
+#pragma unroll
+                for (int pb = 0; pb < kNPB; ++pb) Zb[pb] = E::pack(Z[pb]);
+            }
+            const Frag z = {0, 0, 0, 0};
+#pragma unroll
+            for (int tb = 0; tb < kNTB; ++tb) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int m = 0; m < D / 32; ++m)
+                    acc = E::mma32(SB[2 * m], SB[2 * m + 1], rowld(Qb, 16 * tb + lr, 32 * m + 4 * grp),
+                                   rowld(Qb, 16 * tb + lr, 32 * m + 16 + 4 * grp), acc);
+                acc = acc * FL[16 * tb + lr];
+                if constexpr (DELTA) {
+                    acc = E::mma32(Vf[0], Vf[1], FB[R::fb(tb, 0) * 64 + lane],
+                                   FB[R::fb(tb, 1) * 64 + lane], acc);
+                    acc = E::mma32(Vf[2], Zb[0], FB[R::fb(tb, 2) * 64 + lane],
+                                   FB[R::fb(tb, 3) * 64 + lane], acc);
+                    acc = E::mma32(Zb[1], Zb[2], FB[R::fb(tb, 4) * 64 + lane],
+                                   FB[R::fb(tb, 5) * 64 + lane], acc);
+                } else {
+                    acc = E::mma32(Vf[0], Vf[1], FB[R::fb(tb, 0) * 64 + lane],
+                                   FB[R::fb(tb, 1) * 64 + lane], acc);
+                    acc = E::mma32(Vf[2], z, FB[R::fb(tb, 2) * 64 + lane], z, acc);
+                }
+                const int t = 16 * tb + lr;
+                if (og && t0 + t < T_)
+                    *reinterpret_cast<Frag*>(og + (size_t)(t0 + t) * D + 4 * grp) = E::pack(acc);
+            }
+            lds_barrier();
+        }
+    } else {
+        // ---- fill waves: every tile is split over the NF waves (lane l of
+        // wave f takes the 16-byte pieces (64 f + l) + 256 i); each lane keeps
+        // the pieces of the next NF tiles in registers, slot = tile mod NF ----
+        const int fl = 64 * (wave - 2) + lane;
+        constexpr int NXC = kEP * CPR, NQC = kC * CPR, NVC = kEP * 2;
+        constexpr int NXL = (NXC + 255) / 256, NQL = (NQC + 255) / 256, NVL = (NVC + 255) / 256,
+                      NRL = (RCH + 255) / 256;
+        u32x4 px[NF][NXL], pq[NF][NQL], pv[NF][NVL], pr[NF][NRL];
+        const rsrc_t kr = make_rsrc(kg, (int64_t)T_ * D * 2);
+        const rsrc_t qr = make_rsrc(qg, (int64_t)T_ * D * 2);
+        const rsrc_t vr = make_rsrc(vg, (int64_t)T_ * D * 2 - (int64_t)v0 * 2);
+        const rsrc_t rr_ = make_rsrc(recg, (int64_t)ntiles * R::kBytes);
+        // tile 0 may reach into the halo rows before the sequence
+        auto issue0 = [&](auto& x, auto& q, auto& v, auto& r) __attribute__((always_inline)) {
+            const u32x4 zz = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int i = 0; i < NXL; ++i) {
+                const int c = fl + 256 * i;
+                const int p = c / CPR, col = (c % CPR) * 8;
+                const int tau = p - (W - 1) - a.lag;  // key of pair p
+                const T* src = nullptr;
+                if (c < NXC && p < NP && tau < T_) {
+                    if (tau >= 0) src = kg + (size_t)tau * D + col;
+                    else if (kp) src = kp + (size_t)(W + tau) * D + col;
+                }
+                x[i] = src ? *reinterpret_cast<const u32x4*>(src) : zz;
+            }
+#pragma unroll
+            for (int i = 0; i < NVL; ++i) {
+                const int c = fl + 256 * i;
+                const int p = c / 2, col = (c % 2) * 8;
+                const int tv = p - (W - 1);  // value of pair p
+                const T* src = nullptr;
+                if (c < NVC && p < NP && tv < T_) {
+                    if (tv >= 0) src = vg + (size_t)tv * D + col;
+                    else if (vp) src = vp + (size_t)(W - 1 + tv) * D + col;
+                }
+                v[i] = src ? *reinterpret_cast<const u32x4*>(src) : zz;
+            }
+#pragma unroll
+            for (int i = 0; i < NQL; ++i) {
+                const int c = fl + 256 * i;
+                q[i] = buf_load16(qr, c < NQC ? (uint32_t)(c * 16) : kOob);
+            }
+#pragma unroll
+            for (int i = 0; i < NRL; ++i) {
+                const int c = fl + 256 * i;
+                r[i] = buf_load16(rr_, c < RCH ? (uint32_t)(c * 16) : kOob);
+            }
+        };
+        // tiles >= 1 read rows of the sequence only (tile * C - (W - 1) - lag
+        // >= 0 for W <= 8); rows at or past the end read as zeros
+        auto issue = [&](int tile, auto& x, auto& q, auto& v, auto& r) __attribute__((always_inline)) {
+            const int t0 = tile * kC;
+#pragma unroll
+            for (int i = 0; i < NXL; ++i) {
+                const int c = fl + 256 * i;
+                const int p = c / CPR, col = (c % CPR) * 8;
+                const int tau = t0 - (W - 1) - a.lag + p;
+                x[i] = buf_load16(kr, (c < NXC && p < NP) ? (uint32_t)((tau * D + col) * 2) : kOob);
+            }
+#pragma unroll
+            for (int i = 0; i < NVL; ++i) {
+                const int c = fl + 256 * i;
+                const int p = c / 2, col = (c % 2) * 8;
+                const int tv = t0 - (W - 1) + p;
+                v[i] = buf_load16(vr, (c < NVC && p < NP && tv < T_) ? (uint32_t)((tv * D + col) * 2)
+                                                                    : kOob);
+            }
+#pragma unroll
+            for (int i = 0; i < NQL; ++i) {
+                const int c = fl + 256 * i;
+                q[i] = buf_load16(qr, c < NQC ? (uint32_t)((t0 * D + c * 8) * 2) : kOob);
+            }
+#pragma unroll
+            for (int i = 0; i < NRL; ++i) {
+                const int c = fl + 256 * i;
+                r[i] = buf_load16(rr_, c < RCH ? (uint32_t)(tile * R::kBytes + c * 16) : kOob);
+            }
+        };
+        auto store = [&](int tile, const auto& x, const auto& q, const auto& v, const auto& r)
+            __attribute__((always_inline)) {
+            const int b = tile & 1;
+#pragma unroll
+            for (int i = 0; i < NXL; ++i) {
+                const int c = fl + 256 * i;
+                if (c < NXC)
+                    *reinterpret_cast<u32x4*>(&sm.X[b][tile_off<D>(c / CPR, (c % CPR) * 8)]) = x[i];
+            }
+#pragma unroll
+            for (int i = 0; i < NVL; ++i) {
+                const int c = fl + 256 * i;
+                if (c < NVC) *reinterpret_cast<u32x4*>(&sm.V[b][c * 8]) = v[i];
+            }
+#pragma unroll
+            for (int i = 0; i < NQL; ++i) {
+                const int c = fl + 256 * i;
+                if (c < NQC)
+                    *reinterpret_cast<u32x4*>(&sm.Q[b][tile_off<D>(c / CPR, (c % CPR) * 8)]) = q[i];
+            }
+#pragma unroll
+            for (int i = 0; i < NRL; ++i) {
+                const int c = fl + 256 * i;
+                if (c < RCH) reinterpret_cast<u32x4*>(sm.rec[b])[c] = r[i];
+            }
+        };
+        // tiles 0 .. NF - 1 in flight; tile 0 is published before the first
+        // barrier and tile NF takes its slot.  At step it tile it + 1 moves
+        // from slot (it + 1) mod NF into LDS and tile it + 1 + NF is issued
+        // into the slot.  The barriers order LDS only, so the loads stay in
+        // flight across them.
+        if (ntl > 0) issue0(px[0], pq[0], pv[0], pr[0]);
+        static_for<NF - 1>([&](auto jc) __attribute__((always_inline)) {
+            constexpr int j = decltype(jc)::value + 1;
+            if (j < ntl) issue(j, px[j], pq[j], pv[j], pr[j]);
+        });
+        if (ntl > 0) {
+            store(0, px[0], pq[0], pv[0], pr[0]);
+            if (NF < ntl) issue(NF, px[0], pq[0], pv[0], pr[0]);
+        }
+        lds_barrier();
+        for (int base = 0; base < ntl; base += NF) {
+            static_for<NF>([&](auto jc) __attribute__((always_inline)) {
+                constexpr int j = decltype(jc)::value, slot = (j + 1) % NF;
+                const int it = base + j;
+                if (it < ntl) {
+                    const int nt = it + 1;
+                    if (nt < ntl) {
+                        store(nt, px[slot], pq[slot], pv[slot], pr[slot]);
+                        if (nt + NF < ntl) issue(nt + NF, px[slot], pq[slot], pv[slot], pr[slot]);
+                    }
+                    lds_barrier();
+                }
+            });
+        }
     }
 }
 
@@ -767,10 +886,10 @@ hipError_t launch_d(const ChunkArgs& a, void* ws, hipStream_t stream) {
         e = launch_prep_w<D, DELTA>(b, ws, ntiles, stream);
         if (e != hipSuccess) return e;
     }
-    const int nvs = D / 64;
+    const int nvs = D / 16;
     const int bh8 = (b.BH + 7) / 8 * 8;
-    hipLaunchKernelGGL((win_pass_kernel<D, DELTA>), dim3(bh8 * nvs), dim3(512), 0, stream, b,
-                       (const void*)ws, ntiles);
+    hipLaunchKernelGGL((win_pass_kernel<D, DELTA>), dim3(bh8 * nvs), dim3(64 * (2 + kPassFill)), 0,
+                       stream, b, (const void*)ws, ntiles);
     return hipGetLastError();
 }
 
