@@ -14,8 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfalcon.so")
-SOURCES = ["falcon_api.hip", "falcon_chunk.hip", "falcon_window.hip", "falcon_decode.hip",
-           "falcon_bwd.hip"]
+SOURCES = ["falcon_api.hip", "falcon_chunk.hip", "falcon_window.hip", "falcon_fused.hip",
+           "falcon_decode.hip", "falcon_bwd.hip"]
 ARCH = "gfx950"
 
 

@@ -421,11 +421,11 @@ int chunk_bwd_run(const void* q, const void* k, const void* v, const float* alph
     a.eps = eps;
     a.ck_s = ck_s;
     a.ck_d = ck_d;
-    if (mode == kSaveOnly && (o || S_final) && dt == FALCON_BF16 &&
-        norm_of(base) == falcon::kNormWindow && window >= 2 && !phi) {
-        // the window rules' forward runs the collapsed form: o and S_final
-        // from it (so they equal falcon_chunk_fwd's bit for bit), then the
-        // checkpoints from a run of the virtual-row kernels without outputs
+    if (mode == kSaveOnly && (o || S_final) && falcon::forward_kernel_differs(a, dt, dk_, chunk, is_delta(base))) {
+        // the forward runs other kernels (the window rules' collapsed form,
+        // the fused scalar-rule kernel): o and S_final from them (so they
+        // equal falcon_chunk_fwd's bit for bit), then the checkpoints from a
+        // run of the split kernels without outputs
         falcon::ChunkArgs f = a;
         f.ck_s = f.ck_d = nullptr;
         hipError_t e = falcon::launch_chunk(f, dt, dk_, chunk, is_delta(base), workspace, stream);

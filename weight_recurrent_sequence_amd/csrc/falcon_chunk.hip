@@ -2111,6 +2111,13 @@ size_t chunk_workspace_bytes(int BH, int T, int dt, int chunk, int window, int n
     return bytes;
 }
 
+bool forward_kernel_differs(const ChunkArgs& a, int dt, int D, int chunk, bool delta) {
+    ChunkArgs f = a;
+    f.ck_s = f.ck_d = nullptr;
+    return (dt == 1 && a.norm == kNormWindow && a.W >= 2 && !a.phi) ||
+           fused_supported(f, dt, D, chunk, delta);
+}
+
 hipError_t launch_chunk(const ChunkArgs& a, int dt, int D, int chunk, bool delta, void* ws,
                         hipStream_t stream) {
     // the window rules at bf16 run the collapsed form (tiles of kWinC steps);
@@ -2118,6 +2125,7 @@ hipError_t launch_chunk(const ChunkArgs& a, int dt, int D, int chunk, bool delta
     // virtual-row kernels
     if (dt == 1 && a.norm == kNormWindow && a.W >= 2 && !a.ck_s && !a.phi)
         return launch_window(a, D, delta, ws, stream);
+    if (fused_supported(a, dt, D, chunk, delta)) return launch_fused(a, D, delta, stream);
     if (dt == 1) return launch_e<EBf16>(a, D, chunk, delta, ws, stream);
     return launch_e<EFp32>(a, D, chunk, delta, ws, stream);
 }

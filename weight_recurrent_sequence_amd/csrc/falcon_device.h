@@ -140,6 +140,23 @@ struct EFp32 {
     }
 };
 
+// Unpadded LDS tiles of bf16 rows of N elements (N = 64 or 128): the 16-byte
+// chunk j of row r sits at chunk j ^ swz_row<N>(r).  A wave's row reads (16
+// rows, one 8- or 16-byte piece each) and its transposing column reads (four
+// rows, two adjacent chunks per 16 lanes) then fall on distinct banks; for
+// N = 64 two rows share a 256-byte bank line and the row's parity picks the
+// half.
+template <int N>
+__device__ __forceinline__ int swz_row(int r) {
+    static_assert(N == 64 || N == 128, "row length");
+    return N == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+}
+// element offset of (row r, column c) in such a tile
+template <int N>
+__device__ __forceinline__ int swz_off(int r, int c) {
+    return r * N + ((((c >> 3) ^ swz_row<N>(r)) << 3) | (c & 7));
+}
+
 // Workgroup barrier that orders LDS only: global loads and stores in flight
 // are not waited for.
 __device__ __forceinline__ void lds_barrier() {

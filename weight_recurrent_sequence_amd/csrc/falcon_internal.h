@@ -164,6 +164,18 @@ constexpr int kWinC = 32;
 size_t window_workspace_bytes(int BH, int T, bool delta);
 hipError_t launch_window(const ChunkArgs& a, int D, bool delta, void* ws, hipStream_t stream);
 
+// The scalar inner-product rule (kNormScalar, or kNormWindow with W = 1) at
+// bf16, 64-step tiles, no feature map and no checkpoints: intra-chunk work and
+// state pass in one kernel (needs no workspace beyond a packed call's
+// schedule).
+bool fused_supported(const ChunkArgs& a, int dt, int D, int chunk, bool delta);
+hipError_t launch_fused(const ChunkArgs& a, int D, bool delta, hipStream_t stream);
+
+// True when launch_chunk runs a call without checkpoints (ck_s == NULL) on
+// other kernels than the same call with them, so that a forward that keeps
+// checkpoints takes its outputs from a separate run.
+bool forward_kernel_differs(const ChunkArgs& a, int dt, int D, int chunk, bool delta);
+
 // dt: 0 fp32, 1 bf16.  Return false when the combination is not built.
 bool chunk_supported(int dt, int D, int chunk);
 // Bytes of the per-tile records the intra-chunk kernel hands to the

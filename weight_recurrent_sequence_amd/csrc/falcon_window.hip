@@ -482,26 +482,13 @@ __global__ __launch_bounds__(256) void win_prep_kernel(ChunkArgs a, void* ws, in
 // tiles in order.  Wave 0 carries the slice's state as MFMA accumulators of
 // S^T and forms the products the next state needs (X S0^T, delta, the update);
 // wave 1 forms the tile's outputs from the state at the tile's start, which
-// wave 0 hands over through LDS; waves 2 .. 2 + NF - 1 bring the tiles into
-// LDS, wave f the tiles it = f (mod NF), whose loads it issues NF tiles ahead.
-// One LDS-only barrier per tile.
+// wave 0 hands over through LDS; waves 2 .. 2 + NF - 1 share the fill of
+// every tile and issue its loads NF tiles ahead.  One LDS-only barrier per
+// tile.
 //
-// Key and query tiles hold rows of D elements with no padding; the 16-byte
-// chunk j of row r sits at chunk j ^ swz(r), which spreads both the row reads
-// (16 rows, one chunk) and the transposing column reads (four rows, two
-// chunks) of a wave over distinct banks.
+// Key and query tiles hold rows of D elements with no padding, chunks
+// swizzled per row (swz_off).
 // ---------------------------------------------------------------------------
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-    // D = 128: a row spans the 64 banks; D = 64: two rows do (the row's
-    // parity picks the half)
-    return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
-}
-template <int D>
-__device__ __forceinline__ int tile_off(int r, int c) {
-    return r * D + ((((c >> 3) ^ swz<D>(r)) << 3) | (c & 7));
-}
-
 template <int D, bool DELTA>
 struct WinPassSmem {
     using R = WinRec<DELTA>;
@@ -550,12 +537,12 @@ __global__ __launch_bounds__(64 * (2 + kPassFill)) void win_pass_kernel(ChunkArg
 
     // row fragment (8 bytes) of a swizzled tile: row r, columns c .. c + 3
     auto rowld = [&](const T* m, int r, int c) __attribute__((always_inline)) {
-        return E::load(m + tile_off<D>(r, c));
+        return E::load(m + swz_off<D>(r, c));
     };
     // column fragment of a swizzled tile: lane (lr, grp) gets
     // M[row0 + 4 grp + r][col0 + lr], r = 0..3
     auto colfrag = [&](const T* m, int row0, int col0) __attribute__((always_inline)) {
-        return E::load_tr(m + tile_off<D>(row0 + 4 * grp + (lr >> 2), col0 + 4 * (lr & 3)));
+        return E::load_tr(m + swz_off<D>(row0 + 4 * grp + (lr >> 2), col0 + 4 * (lr & 3)));
     };
     // the pair values: b(Y block kb) = a(Y^T block kb), rows of 16 elements
     auto vfrag = [&](const T* vb, int kb) __attribute__((always_inline)) {
@@ -791,7 +778,7 @@ __global__ __launch_bounds__(64 * (2 + kPassFill)) void win_pass_kernel(ChunkArg
             for (int i = 0; i < NXL; ++i) {
                 const int c = fl + 256 * i;
                 if (c < NXC)
-                    *reinterpret_cast<u32x4*>(&sm.X[b][tile_off<D>(c / CPR, (c % CPR) * 8)]) = x[i];
+                    *reinterpret_cast<u32x4*>(&sm.X[b][swz_off<D>(c / CPR, (c % CPR) * 8)]) = x[i];
             }
 #pragma unroll
             for (int i = 0; i < NVL; ++i) {
@@ -802,7 +789,7 @@ __global__ __launch_bounds__(64 * (2 + kPassFill)) void win_pass_kernel(ChunkArg
             for (int i = 0; i < NQL; ++i) {
                 const int c = fl + 256 * i;
                 if (c < NQC)
-                    *reinterpret_cast<u32x4*>(&sm.Q[b][tile_off<D>(c / CPR, (c % CPR) * 8)]) = q[i];
+                    *reinterpret_cast<u32x4*>(&sm.Q[b][swz_off<D>(c / CPR, (c % CPR) * 8)]) = q[i];
             }
 #pragma unroll
             for (int i = 0; i < NRL; ++i) {
