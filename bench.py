@@ -344,7 +344,8 @@ def main():
         tm = timed(fwd("F1A", workspace=ws), args.steps, args.warmup)
         fl = chunk_flops(B, H, T, D, C, delta=False)
         r = rate(tm, nbytes, B * T)
-        r.update({"traffic": measured_traffic("chunk_fwd_F1A_B8H16T4096d128_bf16_c64"),
+        r.update({"kernels": "fused_kernel<128> (one falcon_chunk_fwd call)",
+                  "traffic": measured_traffic("chunk_fwd_F1A_B8H16T4096d128_bf16_c64"),
                   "algorithmic_flops_per_call": fl,
                   "mfma_frac_bf16": fl / (tm["mean"] / 1e3) / 1e12 / BF16_PEAK_TFLOPS})
         if errors:
@@ -479,6 +480,8 @@ def main():
             tag = v + (f"W{Wx}" if Wx > 1 else "")
             r = rate(tm, nb, Bx * Tx)
             r.update({"workload": wname, "algorithmic_bytes_per_call": nb,
+                      "kernels": ("win_prep_kernel + win_pass_kernel" if Wx > 1
+                                  else "chunk_prep2_kernel + chunk_pass_kernel"),
                       "traffic": measured_traffic(f"chunk_fwd_{tag}_B{Bx}H{Hx}T{Tx}d{Dx}_bf16_c64"),
                       "mfma_tflops": tfx, "mfma_frac_bf16": tfx / BF16_PEAK_TFLOPS,
                       "algorithmic_flops_per_call": fl})
