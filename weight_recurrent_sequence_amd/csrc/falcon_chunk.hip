@@ -970,16 +970,36 @@ __global__ __launch_bounds__(768) void chunk_pass_kernel(ChunkArgs a, const void
         const float* hrow = gam + CV;
         const float* gq = gam + 2 * CV;
 
-        // reads that do not depend on the state go out first, so their latency
-        // overlaps X S0^T
+        // Reads that do not depend on the state go out first, so their latency
+        // overlaps the state's packing and X S0^T: at 64-row tiles of the
+        // scalar rule every key fragment of X S0^T, the targets and the
+        // system's blocks are all requested before the first product (a
+        // scheduling fence keeps the compiler from interleaving them with
+        // the products, which would expose one LDS round trip per product).
+        constexpr bool XPRE = DELTA && !COL && !WIN && NB == 4;
         Frag yf[NB], Af[R::NBA > 0 ? R::NBA : 1], Tf[NB];
+        Frag xq[XPRE ? D / 32 : 1][NB][2];
         f32x4 gm[NB], hv[NB];
+        if constexpr (XPRE) {
 #pragma unroll
-        for (int rb = 0; rb < NB; ++rb) {
-            yf[rb] = colfrag(Yb, LDY, 16 * rb, 16 * cw);
-            hv[rb] = *reinterpret_cast<const f32x4*>(hrow + 16 * rb + 4 * grp);
-            if constexpr (DELTA) gm[rb] = *reinterpret_cast<const f32x4*>(gam + 16 * rb + 4 * grp);
+            for (int m = 0; m < D / 32; ++m)
+#pragma unroll
+                for (int rb = 0; rb < NB; ++rb) {
+                    const T* xr = Xb + (16 * rb + lr) * LDX + 32 * m + 4 * grp;
+                    xq[m][rb][0] = E::load(xr);
+                    xq[m][rb][1] = E::load(xr + 16);
+                }
         }
+        auto load_gates = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) {
+                hv[rb] = *reinterpret_cast<const f32x4*>(hrow + 16 * rb + 4 * grp);
+                if constexpr (DELTA) gm[rb] = *reinterpret_cast<const f32x4*>(gam + 16 * rb + 4 * grp);
+            }
+        };
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) yf[rb] = colfrag(Yb, LDY, 16 * rb, 16 * cw);
+        if constexpr (!XPRE) load_gates();
         // the system's blocks too, unless registers are short (per-column rule)
         auto load_sys = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -988,6 +1008,7 @@ __global__ __launch_bounds__(768) void chunk_pass_kernel(ChunkArgs a, const void
             for (int q = 0; q < R::NBA; ++q) Af[q] = E::load(recT + R::kA + (size_t)q * 256 + lane * 4);
         };
         if constexpr (DELTA && !COL) load_sys();
+        if constexpr (XPRE) __builtin_amdgcn_sched_barrier(0);
         const float glq = gq[Ct - 1];
 
         Frag SB[KB];
@@ -1009,14 +1030,20 @@ __global__ __launch_bounds__(768) void chunk_pass_kernel(ChunkArgs a, const void
                 Frag xf0[NB], xf1[NB];
 #pragma unroll
                 for (int rb = 0; rb < NB; ++rb) {
-                    const T* xr = Xb + (16 * rb + lr) * LDX + 32 * m + 4 * grp;
-                    xf0[rb] = E::load(xr);
-                    xf1[rb] = E::load(xr + 16);
+                    if constexpr (XPRE) {
+                        xf0[rb] = xq[m][rb][0];
+                        xf1[rb] = xq[m][rb][1];
+                    } else {
+                        const T* xr = Xb + (16 * rb + lr) * LDX + 32 * m + 4 * grp;
+                        xf0[rb] = E::load(xr);
+                        xf1[rb] = E::load(xr + 16);
+                    }
                 }
 #pragma unroll
                 for (int rb = 0; rb < NB; ++rb)
                     Z[rb] = E::mma32(xf0[rb], xf1[rb], SB[2 * m], SB[2 * m + 1], Z[rb]);
             }
+            if constexpr (XPRE) load_gates();
             // residuals R = Y - diag(gam) Z, then the blocked forward substitution
             // Delta_b = Td_b (R_b - sum_{c<b} A_bc Delta_c)
             if constexpr (COL) load_sys();
@@ -1184,43 +1211,57 @@ __global__ __launch_bounds__(768) void chunk_pass_kernel(ChunkArgs a, const void
                 *reinterpret_cast<Frag*>(cd + (size_t)cb * D * 16) = sm.DB[pb][cw][cb][lane];
         }
         if (!a.o) return;  // checkpoint-only run (the backward pass's recompute)
-        T* qrow = &sm.QU[pb][16 * tb][0];
-        Frag qf[KB];
+        // the row block is a compile-time constant of each copy, so the causal
+        // block tests below leave no branches between the products, and the
+        // four value blocks' products accumulate side by side
+        with_const4(tb, [&](auto tbc) __attribute__((always_inline)) {
+            constexpr int TB = decltype(tbc)::value;
+            T* qrow = &sm.QU[pb][16 * TB][0];
+            const Frag zf = {0, 0, 0, 0};
+            Frag qf[KB], pf[NB];
 #pragma unroll
-        for (int m = 0; m < D / 32; ++m) {
-            qf[2 * m] = E::load(qrow + lr * LDX + 32 * m + 4 * grp);
-            qf[2 * m + 1] = E::load(qrow + lr * LDX + 32 * m + 16 + 4 * grp);
-        }
-        const float gs = gqt[16 * tb + lr];
-        Frag of[4];
-#pragma unroll
-        for (int c2 = 0; c2 < 4; ++c2) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int m = 0; m < D / 32; ++m)
-                acc = E::mma32(sm.SB[pb][c2][2 * m][lane], sm.SB[pb][c2][2 * m + 1][lane], qf[2 * m],
-                               qf[2 * m + 1], acc);
-            acc = acc * gs;
+            for (int m = 0; m < D / 32; ++m) {
+                qf[2 * m] = E::load(qrow + lr * LDX + 32 * m + 4 * grp);
+                qf[2 * m + 1] = E::load(qrow + lr * LDX + 32 * m + 16 + 4 * grp);
+            }
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb)
-                if (cb <= tb)
-                    acc = E::mma16(sm.DB[pb][c2][cb][lane],
-                                   E::load(Pf + (size_t)R::pblk(tb, cb, false) * 256 + lane * 4), acc);
-            of[c2] = E::pack(acc);  // O[t = 16 tb + lr][v = 16 c2 + 4 grp + r]
-        }
-        // transpose through the wave's own query rows (read above, in order)
+                pf[cb] = cb <= TB ? E::load(Pf + (size_t)R::pblk(TB, cb, false) * 256 + lane * 4) : zf;
+            const float gs = gqt[16 * TB + lr];
+            f32x4 acc[4];
 #pragma unroll
-        for (int c2 = 0; c2 < 4; ++c2)
-            *reinterpret_cast<Frag*>(qrow + lr * LDX + 16 * c2 + 4 * grp) = of[c2];
-        const int rr = lane >> 3, pc = lane & 7;  // row (and row + 8), 16-byte piece
-        const u32x4 o0 = *reinterpret_cast<const u32x4*>(qrow + rr * LDX + 8 * pc);
-        const u32x4 o1 = *reinterpret_cast<const u32x4*>(qrow + (rr + 8) * LDX + 8 * pc);
-        const int t = 16 * tb + rr;
-        if (a.o) {
-            T* dst = og + (size_t)(t0 + t) * D + 8 * pc;
-            if (t < Ct && t0 + t < T_) *reinterpret_cast<u32x4*>(dst) = o0;
-            if (t + 8 < Ct && t0 + t + 8 < T_) *reinterpret_cast<u32x4*>(dst + 8 * D) = o1;
-        }
+            for (int c2 = 0; c2 < 4; ++c2) acc[c2] = zero4();
+#pragma unroll
+            for (int m = 0; m < D / 32; ++m)
+#pragma unroll
+                for (int c2 = 0; c2 < 4; ++c2)
+                    acc[c2] = E::mma32(sm.SB[pb][c2][2 * m][lane], sm.SB[pb][c2][2 * m + 1][lane],
+                                       qf[2 * m], qf[2 * m + 1], acc[c2]);
+            // Delta^T P^T over the causal blocks cb <= TB, two per product
+            Frag of[4];
+#pragma unroll
+            for (int c2 = 0; c2 < 4; ++c2) {
+                acc[c2] = acc[c2] * gs;
+                acc[c2] = E::mma32(sm.DB[pb][c2][0][lane], TB >= 1 ? sm.DB[pb][c2][1][lane] : zf,
+                                   pf[0], pf[1], acc[c2]);
+                if constexpr (TB >= 2)
+                    acc[c2] = E::mma32(sm.DB[pb][c2][2][lane], TB >= 3 ? sm.DB[pb][c2][3][lane] : zf,
+                                       pf[2], pf[3], acc[c2]);
+                of[c2] = E::pack(acc[c2]);  // O[t = 16 TB + lr][v = 16 c2 + 4 grp + r]
+            }
+            // transpose through the wave's own query rows (read above, in order)
+#pragma unroll
+            for (int c2 = 0; c2 < 4; ++c2)
+                *reinterpret_cast<Frag*>(qrow + lr * LDX + 16 * c2 + 4 * grp) = of[c2];
+            const int rr = lane >> 3, pc = lane & 7;  // row (and row + 8), 16-byte piece
+            const u32x4 o0 = *reinterpret_cast<const u32x4*>(qrow + rr * LDX + 8 * pc);
+            const u32x4 o1 = *reinterpret_cast<const u32x4*>(qrow + (rr + 8) * LDX + 8 * pc);
+            // rows past the tile or the sequence: an out-of-range offset, no branch
+            const int nrow = min(Ct, T_ - t0), t = 16 * TB + rr;
+            const rsrc_t ro = make_rsrc(og + (size_t)t0 * D, (int64_t)nrow * D * 2);
+            buf_store16(ro, t < nrow ? (uint32_t)((t * D + 8 * pc) * 2) : kOob, o0);
+            buf_store16(ro, t + 8 < nrow ? (uint32_t)(((t + 8) * D + 8 * pc) * 2) : kOob, o1);
+        });
     };
 
     // ---- direct-to-LDS staging (all rules but the per-column one, whose

@@ -224,6 +224,18 @@ template <int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
     static_for_impl<0, N>(f);
 }
+// f(std::integral_constant<int, w>()) for a wave-uniform w in 0..3: one
+// specialized copy of f per value, so that conditions on w are resolved at
+// compile time and do not split the copy's instruction stream into branches.
+template <class F>
+__device__ __forceinline__ void with_const4(int w, F&& f) {
+    switch (__builtin_amdgcn_readfirstlane(w)) {
+        case 0: f(std::integral_constant<int, 0>()); break;
+        case 1: f(std::integral_constant<int, 1>()); break;
+        case 2: f(std::integral_constant<int, 2>()); break;
+        default: f(std::integral_constant<int, 3>()); break;
+    }
+}
 
 // Sum over aligned groups of `width` consecutive lanes, width in {2,4,8,16},
 // with DPP lane permutations (VALU only, no LDS round trip): quad_perm swaps

@@ -275,15 +275,19 @@ __global__ __launch_bounds__(768) void fused_kernel(ChunkArgs a) {
         s16x8 qq[D / 32];
 #pragma unroll
         for (int m = 0; m < D / 32; ++m) qq[m] = xrow8(Qb, 16 * w + lr, 32 * m + 8 * grp);
+        with_const4(w, [&](auto wc) __attribute__((always_inline)) {
+            constexpr int W = decltype(wc)::value;
+            // the blocks cb <= W interleaved, m outer, so that consecutive
+            // products accumulate into different blocks
 #pragma unroll
-        for (int cb = 0; cb < NB; ++cb) {
-            acc[cb] = zero4();
-            if (cb <= w) {
+            for (int cb = 0; cb < NB; ++cb) acc[cb] = zero4();
 #pragma unroll
-                for (int m = 0; m < D / 32; ++m)
+            for (int m = 0; m < D / 32; ++m)
+                static_for<W + 1>([&](auto cbc) __attribute__((always_inline)) {
+                    constexpr int cb = decltype(cbc)::value;
                     acc[cb] = E::mma32r(xrow8(Xb, 16 * cb + lr, 32 * m + 8 * grp), qq[m], acc[cb]);
-            }
-        }
+                });
+        });
     };
     auto prow2 = [&](int tt, const f32x4 (&acc)[NB]) __attribute__((always_inline)) {
         const int pb = tt & 1;
@@ -292,12 +296,13 @@ __global__ __launch_bounds__(768) void fused_kernel(ChunkArgs a) {
         const float* cf = sm.fac[pb][kCf];
         const int t = 16 * w + lr;
         const float g2t = g2[t];
-#pragma unroll
-        for (int cb = 0; cb < NB; ++cb) {
-            if (cb <= w) {
+        with_const4(w, [&](auto wc) __attribute__((always_inline)) {
+            constexpr int W = decltype(wc)::value;
+            static_for<W + 1>([&](auto cbc) __attribute__((always_inline)) {
+                constexpr int cb = decltype(cbc)::value;
                 const int j0 = 16 * cb + 4 * grp;
                 f32x4 v;
-                if (cb < w) {
+                if constexpr (cb < W) {
                     const float rf = exp2f(g2t - sm.gref[pb][cb]);
                     const f32x4 cfv = *reinterpret_cast<const f32x4*>(cf + j0);
 #pragma unroll
@@ -310,44 +315,54 @@ __global__ __launch_bounds__(768) void fused_kernel(ChunkArgs a) {
                         v[r] = (j0 + r <= t) ? exp2f(g2t - gj[r]) * rj[r] * acc[cb][r] : 0.f;
                 }
                 sm.Pf[pb][w][cb][lane] = E::pack(v);
-            }
-        }
+            });
+        });
     };
 
     // the outputs of the wave's 16 columns, O^T = (S0 Q^T) diag(gamma)
-    // + Delta^T P^T; lane ends with O[t = 16 tb + lr][v = v0 + 16 cw + 4 grp + r]
+    // + Delta^T P^T; lane ends with O[t = 16 tb + lr][v = v0 + 16 cw + 4 grp + r].
+    // The four row blocks accumulate side by side (consecutive products go to
+    // different blocks) and are stored at the end, rows past the sequence
+    // masked by an out-of-range offset rather than a branch.
     auto outputs = [&](int it, const Frag (&SB)[KB], const Frag (&DB)[NB])
         __attribute__((always_inline)) {
         const int b2 = it & 1, t0 = it * kF;
         const T* Qb = sm.Q[it % 3];
         const float* gam = sm.fac[b2][kGam];
         const Frag zf = {0, 0, 0, 0};
+        f32x4 acc[NB];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) acc[tb] = zero4();
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m) {
+#pragma unroll
+            for (int tb = 0; tb < NB; ++tb)
+                acc[tb] = E::mma32(SB[2 * m], SB[2 * m + 1], xrow(Qb, 16 * tb + lr, 32 * m + 4 * grp),
+                                   xrow(Qb, 16 * tb + lr, 32 * m + 16 + 4 * grp), acc[tb]);
+        }
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) acc[tb] = acc[tb] * gam[16 * tb + lr];
+        // the causal blocks cb <= tb, two per product
         static_for<NB>([&](auto tbc) __attribute__((always_inline)) {
             constexpr int tb = decltype(tbc)::value;
-            Frag qf[KB];
-#pragma unroll
-            for (int m = 0; m < D / 32; ++m) {
-                qf[2 * m] = xrow(Qb, 16 * tb + lr, 32 * m + 4 * grp);
-                qf[2 * m + 1] = xrow(Qb, 16 * tb + lr, 32 * m + 16 + 4 * grp);
-            }
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int m = 0; m < D / 32; ++m)
-                acc = E::mma32(SB[2 * m], SB[2 * m + 1], qf[2 * m], qf[2 * m + 1], acc);
-            acc = acc * gam[16 * tb + lr];
-            // the causal blocks cb <= tb, two per product
             const Frag p0 = sm.Pf[b2][tb][0][lane];
             const Frag p1 = tb >= 1 ? sm.Pf[b2][tb][1][lane] : zf;
-            acc = E::mma32(DB[0], DB[1], p0, p1, acc);
+            acc[tb] = E::mma32(DB[0], DB[1], p0, p1, acc[tb]);
             if constexpr (tb >= 2) {
                 const Frag p2 = sm.Pf[b2][tb][2][lane];
                 const Frag p3 = tb >= 3 ? sm.Pf[b2][tb][3][lane] : zf;
-                acc = E::mma32(DB[2], DB[3], p2, p3, acc);
+                acc[tb] = E::mma32(DB[2], DB[3], p2, p3, acc[tb]);
             }
-            const int t = 16 * tb + lr;
-            if (og && t0 + t < T_)
-                *reinterpret_cast<Frag*>(og + (size_t)(t0 + t) * D + 16 * cw + 4 * grp) = E::pack(acc);
         });
+        if (og) {
+            const int nrow = T_ - t0;
+            const rsrc_t ro = make_rsrc(og + (size_t)t0 * D, (int64_t)nrow * D * 2);
+#pragma unroll
+            for (int tb = 0; tb < NB; ++tb) {
+                const int t = 16 * tb + lr;
+                buf_store8(ro, t < nrow ? (uint32_t)((t * D + 16 * cw + 4 * grp) * 2) : kOob, E::pack(acc[tb]));
+            }
+        }
     };
 
     // ---- chain wave: tile it; the state slice Sacc[kb][r] = S[v][k],
@@ -359,27 +374,21 @@ __global__ __launch_bounds__(768) void fused_kernel(ChunkArgs a) {
         const T* Yb = sm.Y[b2];
         const float* hrow = sm.fac[b2][kHrow];
         Frag SB[KB], DB[NB];
-        f32x4 Dl[NB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) SB[kb] = E::pack(Sacc[kb]);
-        // Delta = Y: the targets themselves
+        // Delta = Y: the targets themselves; and the update's right-hand
+        // side diag(hrow) Delta
 #pragma unroll
         for (int rb = 0; rb < NB; ++rb) {
             const Frag yf = ycol(Yb, 16 * rb, 16 * cw);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Dl[rb][r] = E::to_f((T)yf[r]);
-            DB[rb] = yf;
-        }
-        outputs(it, SB, DB);
-        // the update's right-hand side diag(hrow) Delta
-#pragma unroll
-        for (int cb = 0; cb < NB; ++cb) {
-            const f32x4 hv = *reinterpret_cast<const f32x4*>(hrow + 16 * cb + 4 * grp);
+            const f32x4 hv = *reinterpret_cast<const f32x4*>(hrow + 16 * rb + 4 * grp);
             f32x4 h;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) h[r] = hv[r] * Dl[cb][r];
-            HB[cb] = E::pack(h);
+            for (int r = 0; r < 4; ++r) h[r] = hv[r] * E::to_f((T)yf[r]);
+            DB[rb] = yf;
+            HB[rb] = E::pack(h);
         }
+        outputs(it, SB, DB);
     };
     // part 2: S^T = exp(g_last) S0^T + X^T diag(hrow) Delta
     auto chain2 = [&](int it, f32x4 (&Sacc)[KB], const Frag (&HB)[NB])

@@ -81,5 +81,14 @@ __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ s16x4 buf_load8(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(s16x4, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
 }
+// 16 (8) bytes per lane to a buffer; an offset past the buffer's size (kOob)
+// writes nothing, so a lane's store is masked without a branch.
+__device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, s16x4 v) {
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
 
 }  // namespace falcon
