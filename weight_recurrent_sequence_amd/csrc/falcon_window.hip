@@ -109,8 +109,7 @@ struct WinPrepSmem {
     static constexpr int NA = DELTA ? RB * (RB - 1) / 2 : 1;
     uint16_t X[kEP][LDX];                  // pair keys x_p (rows >= E zero)
     uint16_t Q[kC][LDX];                   // queries
-    float G[DELTA ? kEP : 1][kEP + 1];     // pair Gram x_p . x_p'
-    float QK[kC][kEP + 1];                 // q_t . x_p
+    float QK[DELTA ? 1 : kC][kEP + 1];     // q_t . x_p (inner-product rule)
     float al[kC], et[kC];                  // gates (padding steps: 1, 0)
     float nrm[kEP];                        // ||x_p||^2
     float g2[kC];                          // log2(e) * g_s
@@ -143,61 +142,76 @@ __global__ __launch_bounds__(256) void win_prep_kernel(ChunkArgs a, void* ws, in
     const float eps = a.eps;
     if (a.toff) njobs = a.H * a.toff[a.BH / a.H];  // packed: the tiles that exist
 
-    for (int job = blockIdx.x; job < njobs; job += gridDim.x) {
-        const Job jb = job_of(a, job, ntiles);
-        const int bh = jb.bh, tile = jb.tile, T_ = jb.sr.T;
-        if (tile >= tiles_of(T_, kC)) continue;  // (uniform over the workgroup)
-        const int t0 = tile * kC;
+    // The next job's keys, queries and gates are loaded into registers while
+    // the current job computes, so their latency is hidden; a job's staging
+    // then only moves them into LDS.
+    constexpr int NXL = (kEP * CPR + 255) / 256, NQL = (kC * CPR + 255) / 256;
+    u32x4 px[NXL], pq[NQL];
+    float gal = 1.f, get = 0.f;
+    auto valid = [&](int j) __attribute__((always_inline)) {
+        const Job jb = job_of(a, j, ntiles);
+        return jb.tile < tiles_of(jb.sr.T, kC);  // (uniform over the workgroup)
+    };
+    auto load_job = [&](int j) __attribute__((always_inline)) {
+        const Job jb = job_of(a, j, ntiles);
+        const int bh = jb.bh, T_ = jb.sr.T, t0 = jb.tile * kC;
         const T* kg = static_cast<const T*>(a.k) + jb.sr.row0 * D;
         const T* qg = static_cast<const T*>(a.q) + jb.sr.row0 * D;
         const T* kp = a.k_prev ? static_cast<const T*>(a.k_prev) + (size_t)bh * W * D : nullptr;
+#pragma unroll
+        for (int it = 0; it < NXL; ++it) {
+            const int c = tid + 256 * it;
+            const int p = c / CPR, col = (c % CPR) * 8;
+            const int tau = t0 - (W - 1) - a.lag + p;  // key of pair p
+            const T* src = nullptr;
+            if (c < kEP * CPR && p < NP && tau < T_) {
+                if (tau >= 0) src = kg + (size_t)tau * D + col;
+                else if (kp) src = kp + (size_t)(W + tau) * D + col;
+            }
+            px[it] = src ? *reinterpret_cast<const u32x4*>(src) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int it = 0; it < NQL; ++it) {
+            const int c = tid + 256 * it;
+            const int t = c / CPR, col = (c % CPR) * 8;
+            pq[it] = (c < kC * CPR && t0 + t < T_)
+                         ? *reinterpret_cast<const u32x4*>(qg + (size_t)(t0 + t) * D + col)
+                         : u32x4{0u, 0u, 0u, 0u};
+        }
+        gal = 1.f;
+        get = 0.f;
+        if (tid < kC && t0 + tid < T_) {
+            gal = a.alpha[jb.sr.row0 + t0 + tid];
+            get = a.eta[jb.sr.row0 + t0 + tid];
+        }
+    };
+    int job = blockIdx.x;
+    while (job < njobs && !valid(job)) job += gridDim.x;
+    if (job < njobs) load_job(job);
+    while (job < njobs) {
+        const Job jb = job_of(a, job, ntiles);
+        const int bh = jb.bh, tile = jb.tile;
         char* rec = static_cast<char*>(ws) + ((size_t)bh * ntiles + tile) * R::kBytes;
 
         // ---- stage pair keys, queries and gates ----
-        {
-            constexpr int NXL = (kEP * CPR + 255) / 256, NQL = (kC * CPR + 255) / 256;
-            u32x4 px[NXL], pq[NQL];
 #pragma unroll
-            for (int it = 0; it < NXL; ++it) {
-                const int c = tid + 256 * it;
-                const int p = c / CPR, col = (c % CPR) * 8;
-                const int tau = t0 - (W - 1) - a.lag + p;  // key of pair p
-                const T* src = nullptr;
-                if (c < kEP * CPR && p < NP && tau < T_) {
-                    if (tau >= 0) src = kg + (size_t)tau * D + col;
-                    else if (kp) src = kp + (size_t)(W + tau) * D + col;
-                }
-                px[it] = src ? *reinterpret_cast<const u32x4*>(src) : u32x4{0u, 0u, 0u, 0u};
-            }
-#pragma unroll
-            for (int it = 0; it < NQL; ++it) {
-                const int c = tid + 256 * it;
-                const int t = c / CPR, col = (c % CPR) * 8;
-                pq[it] = (c < kC * CPR && t0 + t < T_)
-                             ? *reinterpret_cast<const u32x4*>(qg + (size_t)(t0 + t) * D + col)
-                             : u32x4{0u, 0u, 0u, 0u};
-            }
-            float al = 1.f, et = 0.f;
-            if (tid < kC && t0 + tid < T_) {
-                al = a.alpha[jb.sr.row0 + t0 + tid];
-                et = a.eta[jb.sr.row0 + t0 + tid];
-            }
-#pragma unroll
-            for (int it = 0; it < NXL; ++it) {
-                const int c = tid + 256 * it;
-                if (c < kEP * CPR) *reinterpret_cast<u32x4*>(&sm.X[c / CPR][(c % CPR) * 8]) = px[it];
-            }
-#pragma unroll
-            for (int it = 0; it < NQL; ++it) {
-                const int c = tid + 256 * it;
-                if (c < kC * CPR) *reinterpret_cast<u32x4*>(&sm.Q[c / CPR][(c % CPR) * 8]) = pq[it];
-            }
-            if (tid < kC) {
-                sm.al[tid] = al;
-                sm.et[tid] = et;
-            }
+        for (int it = 0; it < NXL; ++it) {
+            const int c = tid + 256 * it;
+            if (c < kEP * CPR) *reinterpret_cast<u32x4*>(&sm.X[c / CPR][(c % CPR) * 8]) = px[it];
         }
-        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < NQL; ++it) {
+            const int c = tid + 256 * it;
+            if (c < kC * CPR) *reinterpret_cast<u32x4*>(&sm.Q[c / CPR][(c % CPR) * 8]) = pq[it];
+        }
+        if (tid < kC) {
+            sm.al[tid] = gal;
+            sm.et[tid] = get;
+        }
+        int nxt = job + gridDim.x;
+        while (nxt < njobs && !valid(nxt)) nxt += gridDim.x;
+        lds_barrier();
+        if (nxt < njobs) load_job(nxt);
 
         // ---- pair norms: 4 threads per pair ----
         {
@@ -218,7 +232,7 @@ __global__ __launch_bounds__(256) void win_prep_kernel(ChunkArgs a, void* ws, in
             n2 = group_sum_dpp<4>(n2);
             if (p < kEP && part == 0) sm.nrm[p] = n2;
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- log-decay scan, window steps, per-step factors (wave 0) ----
         if (wave == 0) {
@@ -238,7 +252,7 @@ __global__ __launch_bounds__(256) void win_prep_kernel(ChunkArgs a, void* ws, in
                 sm.gam[s] = __expf(lg);
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- decay factors of the blocks; the Gram blocks on MFMA ----
         if constexpr (DELTA) {
@@ -255,33 +269,27 @@ __global__ __launch_bounds__(256) void win_prep_kernel(ChunkArgs a, void* ws, in
                 sm.e2[i] = (t - d >= 0) ? exp2f(sm.g2[t] - sm.g2[t - d]) * sm.bs[t - d] : 0.f;
             }
         }
-        {
-            // rows as eight contiguous contraction elements per lane; lane
-            // (lr, grp) ends with rowA(16 bi + 4 grp + r) . rowB(16 bj + lr)
-            constexpr int NG = DELTA ? kNPB * kNPB : 0;
-            constexpr int NQ = kNTB * kNPB;
-            for (int q = wave; q < NG + NQ; q += 4) {
-                const bool isG = q < NG;
-                const int qq = isG ? q : q - NG;
-                const int bi = qq / kNPB, bj = qq - bi * kNPB;
-                const T* ar = (isG ? &sm.X[16 * bi + lr][0] : &sm.Q[16 * bi + lr][0]) + 8 * grp;
-                const T* br = &sm.X[16 * bj + lr][0] + 8 * grp;
-                f32x4 acc = zero4();
+        // Gram block of two groups of 16 rows, rows as eight contiguous
+        // contraction elements per lane: with lane l of each operand pointing
+        // at its row's first element (plus 8 grp), lane (lr, grp) ends with
+        // rowA(4 grp + r) . rowB(lr).  Rows are gathered by the addresses.
+        auto gram = [&](const T* ar, const T* br) __attribute__((always_inline)) {
+            f32x4 acc = zero4();
 #pragma unroll
-                for (int m = 0; m < D / 32; ++m)
-                    acc = E::mma32r(E::load8(ar + 32 * m), E::load8(br + 32 * m), acc);
+            for (int m = 0; m < D / 32; ++m)
+                acc = E::mma32r(E::load8(ar + 32 * m), E::load8(br + 32 * m), acc);
+            return acc;
+        };
+        if constexpr (!DELTA) {
+            // q_t . x_p for the inner-product rule's L'
+            for (int q = wave; q < kNTB * kNPB; q += 4) {
+                const int bi = q / kNPB, bj = q - bi * kNPB;
+                const f32x4 acc = gram(&sm.Q[16 * bi + lr][8 * grp], &sm.X[16 * bj + lr][8 * grp]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if constexpr (DELTA) {
-                        if (isG) sm.G[16 * bi + 4 * grp + r][16 * bj + lr] = acc[r];
-                        else sm.QK[16 * bi + 4 * grp + r][16 * bj + lr] = acc[r];
-                    } else {
-                        sm.QK[16 * bi + 4 * grp + r][16 * bj + lr] = acc[r];
-                    }
-                }
+                for (int r = 0; r < 4; ++r) sm.QK[16 * bi + 4 * grp + r][16 * bj + lr] = acc[r];
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         if constexpr (DELTA) {
             // ---- -A (strictly lower blocks), the diagonal inverses and P,
@@ -293,13 +301,16 @@ __global__ __launch_bounds__(256) void win_prep_kernel(ChunkArgs a, void* ws, in
                     int rb = 1;
                     while (lblk(rb + 1, 0) <= q) ++rb;
                     const int cb = q - lblk(rb, 0);
-                    const int i = 16 * rb + lr, si = row_step<W>(i), pi = row_pair<W>(i);
+                    const int i = 16 * rb + lr, si = row_step<W>(i);
+                    // x_p(j) . x_p(i), j = 16 cb + 4 grp + r, on the matrix cores
+                    const f32x4 gv = gram(&sm.X[row_pair<W>(16 * cb + lr)][8 * grp],
+                                          &sm.X[row_pair<W>(i)][8 * grp]);
                     const float rf = exp2f(sm.g2[si] - sm.gref[cb]);
                     f32x4 v;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int j = 16 * cb + 4 * grp + r;
-                        v[r] = (row_step<W>(j) < si) ? -(rf * sm.cf[j] * sm.G[pi][row_pair<W>(j)]) : 0.f;
+                        v[r] = (row_step<W>(j) < si) ? -(rf * sm.cf[j] * gv[r]) : 0.f;
                     }
                     sm.Af[q][lane] = E::pack(v);
                 } else if (q < NL + RB) {
@@ -310,17 +321,19 @@ __global__ __launch_bounds__(256) void win_prep_kernel(ChunkArgs a, void* ws, in
                     // accumulator is b(XY), and a(X) = b(X^T).  The chain builds
                     // c(F_{J-1}^T .. F_0^T) = c(Td^T) = a(Td).
                     const int rb = q - NL;
-                    auto nval = [&](int i, int j) __attribute__((always_inline)) {
+                    // the block's Gram x_p(16 rb + 4 grp + r) . x_p(16 rb + lr),
+                    // symmetric, so it serves both fragment layouts of N
+                    const T* xr = &sm.X[row_pair<W>(16 * rb + lr)][8 * grp];
+                    const f32x4 gv = gram(xr, xr);
+                    auto nfac = [&](int i, int j) __attribute__((always_inline)) {
                         const int si = row_step<W>(i), sj = row_step<W>(j);
-                        return sj < si ? exp2f(sm.g2[si] - sm.g2[sj]) * sm.bs[sj] *
-                                             sm.G[row_pair<W>(i)][row_pair<W>(j)]
-                                       : 0.f;
+                        return sj < si ? exp2f(sm.g2[si] - sm.g2[sj]) * sm.bs[sj] : 0.f;
                     };
                     f32x4 aN, bN, aI;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        aN[r] = nval(16 * rb + lr, 16 * rb + 4 * grp + r);
-                        bN[r] = nval(16 * rb + 4 * grp + r, 16 * rb + lr);
+                        aN[r] = nfac(16 * rb + lr, 16 * rb + 4 * grp + r) * gv[r];
+                        bN[r] = nfac(16 * rb + 4 * grp + r, 16 * rb + lr) * gv[r];
                         aI[r] = (lr == 4 * grp + r) ? 1.f : 0.f;
                     }
                     f32x4 Y = aI - aN;  // b(F_0^T) = a(I - N)
@@ -341,18 +354,20 @@ __global__ __launch_bounds__(256) void win_prep_kernel(ChunkArgs a, void* ws, in
                     // fully causal block: every row's step <= every t of the block
                     const bool full = row_step<W>(16 * rb + 15) <= 16 * tb;
                     const float rf = full ? exp2f(sm.g2[t] - sm.gref[rb]) : 0.f;
+                    // x_p(j) . q_t, j = 16 rb + 4 grp + r
+                    const f32x4 gv = gram(&sm.X[row_pair<W>(16 * rb + lr)][8 * grp], &sm.Q[t][8 * grp]);
                     f32x4 v;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int j = 16 * rb + 4 * grp + r, sj = row_step<W>(j);
-                        const float qk = sm.QK[t][row_pair<W>(j)];
+                        const float qk = gv[r];
                         v[r] = full ? rf * sm.cf[j] * qk
                                     : (sj <= t ? exp2f(sm.g2[t] - sm.g2[sj]) * sm.bs[sj] * qk : 0.f);
                     }
                     sm.Pf[tb][rb][lane] = E::pack(v);
                 }
             }
-            __syncthreads();
+            lds_barrier();
 
             // ---- blocked forward substitution (waves 0-2, pair block q each):
             // M'_rb = Td_rb (G_v,rb - sum_{c<rb} A_rb,c M'_c) and the same for M
@@ -376,38 +391,52 @@ __global__ __launch_bounds__(256) void win_prep_kernel(ChunkArgs a, void* ws, in
                         acc1[r] = one;
                         acc2[r] = one * sm.gam[row_step<W>(i)];
                     }
-                    static_for<rb>([&](auto cc) __attribute__((always_inline)) {
-                        constexpr int c = decltype(cc)::value;
+                    // two blocks c, c + 1 per product
+                    static_for<(rb + 1) / 2>([&](auto cc) __attribute__((always_inline)) {
+                        constexpr int c = 2 * decltype(cc)::value;
                         const Frag af = sm.Af[lblk(rb, c)][lane];
-                        acc1 = E::mma16(af, Mp[c], acc1);
-                        acc2 = E::mma16(af, Mg[c], acc2);
+                        if constexpr (c + 1 < rb) {
+                            const Frag af1 = sm.Af[lblk(rb, c + 1)][lane];
+                            acc1 = E::mma32(af, af1, Mp[c], Mp[c + 1], acc1);
+                            acc2 = E::mma32(af, af1, Mg[c], Mg[c + 1], acc2);
+                        } else {
+                            acc1 = E::mma16(af, Mp[c], acc1);
+                            acc2 = E::mma16(af, Mg[c], acc2);
+                        }
                     });
                     const Frag td = sm.Tdf[rb][lane];
                     Mp[rb] = E::pack(E::mma16(td, E::pack(acc1), zero4()));
                     Mg[rb] = E::pack(E::mma16(td, E::pack(acc2), zero4()));
-                    constexpr int plo = row_step<W>(16 * rb), phi_ = row_step<W>(16 * rb + 15) + W - 1;
-                    static_for<kNPB>([&](auto pbc) __attribute__((always_inline)) {
-                        constexpr int pb = decltype(pbc)::value;
-                        if constexpr (16 * pb <= phi_ && 16 * pb + 15 >= plo) {
-                            f32x4 h;
+                    // N and L from row blocks rb - 1 and rb together (RB = 2 W is
+                    // even); a block whose rows miss pair block pb contributes
+                    // zeros of h, one whose steps all follow step block tb zeros of P
+                    if constexpr (rb % 2 == 1) {
+                        constexpr int r0 = rb - 1;
+                        constexpr int plo = row_step<W>(16 * r0), phi_ = row_step<W>(16 * rb + 15) + W - 1;
+                        static_for<kNPB>([&](auto pbc) __attribute__((always_inline)) {
+                            constexpr int pb = decltype(pbc)::value;
+                            if constexpr (16 * pb <= phi_ && 16 * pb + 15 >= plo) {
+                                f32x4 h0, h1;
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const int j = 16 * rb + 4 * grp + r;
-                                h[r] = (row_pair<W>(j) == 16 * pb + lr) ? sm.hs[row_step<W>(j)] : 0.f;
+                                for (int r = 0; r < 4; ++r) {
+                                    const int j0 = 16 * r0 + 4 * grp + r, j1 = j0 + 16;
+                                    h0[r] = (row_pair<W>(j0) == 16 * pb + lr) ? sm.hs[row_step<W>(j0)] : 0.f;
+                                    h1[r] = (row_pair<W>(j1) == 16 * pb + lr) ? sm.hs[row_step<W>(j1)] : 0.f;
+                                }
+                                const Frag hb0 = E::pack(h0), hb1 = E::pack(h1);
+                                nP[pb] = E::mma32(Mp[r0], Mp[rb], hb0, hb1, nP[pb]);
+                                nG[pb] = E::mma32(Mg[r0], Mg[rb], hb0, hb1, nG[pb]);
                             }
-                            const Frag hb = E::pack(h);
-                            nP[pb] = E::mma16(Mp[rb], hb, nP[pb]);
-                            nG[pb] = E::mma16(Mg[rb], hb, nG[pb]);
-                        }
-                    });
-                    static_for<kNTB>([&](auto tbc) __attribute__((always_inline)) {
-                        constexpr int tb = decltype(tbc)::value;
-                        if constexpr (row_step<W>(16 * rb) <= 16 * tb + 15) {
-                            const Frag pf = sm.Pf[tb][rb][lane];
-                            lP[tb] = E::mma16(Mp[rb], pf, lP[tb]);
-                            lG[tb] = E::mma16(Mg[rb], pf, lG[tb]);
-                        }
-                    });
+                        });
+                        static_for<kNTB>([&](auto tbc) __attribute__((always_inline)) {
+                            constexpr int tb = decltype(tbc)::value;
+                            if constexpr (row_step<W>(16 * r0) <= 16 * tb + 15) {
+                                const Frag pf0 = sm.Pf[tb][r0][lane], pf1 = sm.Pf[tb][rb][lane];
+                                lP[tb] = E::mma32(Mp[r0], Mp[rb], pf0, pf1, lP[tb]);
+                                lG[tb] = E::mma32(Mg[r0], Mg[rb], pf0, pf1, lG[tb]);
+                            }
+                        });
+                    }
                 });
                 // the accumulator of N^T block (q, pb) is the A fragment of N
                 // block (pb, q); that of L^T block (q, tb) the B fragment of L^T
@@ -450,7 +479,7 @@ __global__ __launch_bounds__(256) void win_prep_kernel(ChunkArgs a, void* ws, in
                 if (p < kC) fl[p] = sm.gam[p];
                 if (p == 0) fl[kC] = sm.gam[kC - 1];
             }
-            __syncthreads();
+            lds_barrier();
             Frag* fb = reinterpret_cast<Frag*>(rec + R::kB);
             for (int q = wave; q < kNTB * kNPB; q += 4) {
                 const int tb = q / kNPB, kb = q - tb * kNPB;
@@ -473,7 +502,8 @@ __global__ __launch_bounds__(256) void win_prep_kernel(ChunkArgs a, void* ws, in
                 fb[R::fb(tb, kb) * 64 + lane] = E::pack(v);
             }
         }
-        __syncthreads();  // the next job's staging overwrites the tiles
+        lds_barrier();  // the next job's staging overwrites the tiles
+        job = nxt;
     }
 }
 
