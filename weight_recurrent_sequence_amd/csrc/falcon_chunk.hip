@@ -772,8 +772,10 @@ struct PassSmem {
     uint16_t X[2][CV][LDX];     // keys x_i
     uint16_t Y[2][CV][LDY];     // targets y_i of this slice's 64 value columns
     uint16_t QU[2][CV][LDX];    // queries q_t; write vectors u_i for the per-column rule
-    s16x4 SB[2][4][KB][64];     // bf16 state at the tile start, fragment order per chain wave
-    s16x4 DB[2][4][NB][64];     // bf16 Delta, fragment order per chain wave
+    // bf16 state at the tile start and bf16 Delta, fragment order per chain
+    // wave, fragments 2j and 2j + 1 of a lane side by side (one 16-byte read)
+    s16x4 SB[2][4][KB / 2][64][2];
+    s16x4 DB[2][4][(NB + 1) / 2][64][2];
     alignas(16) char rec[2][RECB];
     alignas(16) char pg[2][PGB];  // the output half's record pieces, staged one tile later
     uint32_t pf[WIN && !COL ? 4 : 1][64];  // landing area of the fill waves' L2 warm-up loads (never read)
@@ -960,6 +962,18 @@ __global__ __launch_bounds__(768) void chunk_pass_kernel(ChunkArgs a, const void
         return E::load_tr(m + (size_t)(row0 + 4 * grp + (lr >> 2)) * ld + col0 + 4 * (lr & 3));
     };
 
+    // the state and Delta fragments in LDS: one, or a pair read at once
+    auto sbf = [&](int b, int c, int kb) __attribute__((always_inline)) { return sm.SB[b][c][kb >> 1][lane][kb & 1]; };
+    auto dbf = [&](int b, int c, int cb) __attribute__((always_inline)) { return sm.DB[b][c][cb >> 1][lane][cb & 1]; };
+    auto pair_lo = [](s16x8 v) __attribute__((always_inline)) { return Frag{v[0], v[1], v[2], v[3]}; };
+    auto pair_hi = [](s16x8 v) __attribute__((always_inline)) { return Frag{v[4], v[5], v[6], v[7]}; };
+    auto sbp = [&](int b, int c, int m) __attribute__((always_inline)) {
+        return *reinterpret_cast<const s16x8*>(&sm.SB[b][c][m][lane][0]);
+    };
+    auto dbp = [&](int b, int c, int j) __attribute__((always_inline)) {
+        return *reinterpret_cast<const s16x8*>(&sm.DB[b][c][j][lane][0]);
+    };
+
     // ---- chain: one tile ----
     auto chain_tile = [&](int it) __attribute__((always_inline)) {
         const int b = it & 1;
@@ -1013,10 +1027,12 @@ __global__ __launch_bounds__(768) void chunk_pass_kernel(ChunkArgs a, const void
 
         Frag SB[KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            SB[kb] = E::pack(Sacc[kb]);
-            sm.SB[b][cw][kb][lane] = SB[kb];
-        }
+        for (int kb = 0; kb < KB; ++kb) SB[kb] = E::pack(Sacc[kb]);
+#pragma unroll
+        for (int m = 0; m < KB / 2; ++m)
+            *reinterpret_cast<s16x8*>(&sm.SB[b][cw][m][lane][0]) =
+                s16x8{SB[2 * m][0], SB[2 * m][1], SB[2 * m][2], SB[2 * m][3],
+                      SB[2 * m + 1][0], SB[2 * m + 1][1], SB[2 * m + 1][2], SB[2 * m + 1][3]};
 
         f32x4 Dl[NB];
         Frag DB[NB];
@@ -1066,7 +1082,11 @@ __global__ __launch_bounds__(768) void chunk_pass_kernel(ChunkArgs a, const void
             }
         }
 #pragma unroll
-        for (int rb = 0; rb < NB; ++rb) sm.DB[b][cw][rb][lane] = DB[rb];
+        for (int j = 0; j < NB / 2; ++j)
+            *reinterpret_cast<s16x8*>(&sm.DB[b][cw][j][lane][0]) =
+                s16x8{DB[2 * j][0], DB[2 * j][1], DB[2 * j][2], DB[2 * j][3],
+                      DB[2 * j + 1][0], DB[2 * j + 1][1], DB[2 * j + 1][2], DB[2 * j + 1][3]};
+        if constexpr (NB % 2 == 1) sm.DB[b][cw][NB / 2][lane][0] = DB[NB - 1];
 
         // S^T = exp(g_last) S0^T + Omega^T diag(hrow) Delta
         Frag HB[NB];
@@ -1112,9 +1132,9 @@ __global__ __launch_bounds__(768) void chunk_pass_kernel(ChunkArgs a, const void
         const float* gqt = reinterpret_cast<const float*>(sm.pg[pb] + R::npblk(WIN) * 512);
         Frag sb[KB], db[NB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) sb[kb] = sm.SB[pb][cw][kb][lane];
+        for (int kb = 0; kb < KB; ++kb) sb[kb] = sbf(pb, cw, kb);
 #pragma unroll
-        for (int cb = 0; cb < NB; ++cb) db[cb] = sm.DB[pb][cw][cb][lane];
+        for (int cb = 0; cb < NB; ++cb) db[cb] = dbf(pb, cw, cb);
         if (a.ck_s) {
             // checkpoints for the backward pass, in 16-column blocks ([block][v][16]):
             // lane holds S[v][16 kb + 4 grp + r] and Delta[16 cb + 4 grp + r][v] of
@@ -1145,13 +1165,15 @@ __global__ __launch_bounds__(768) void chunk_pass_kernel(ChunkArgs a, const void
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int m = 0; m < D / 32; ++m)
-                    acc = E::mma32(sm.SB[pb][c2][2 * m][lane], sm.SB[pb][c2][2 * m + 1][lane],
-                                   pQa[2 * m], pQa[2 * m + 1], acc);
+                {
+                    const s16x8 sp = sbp(pb, c2, m);
+                    acc = E::mma32(pair_lo(sp), pair_hi(sp), pQa[2 * m], pQa[2 * m + 1], acc);
+                }
                 acc = acc * gs;
 #pragma unroll
                 for (int cb = 0; cb < NB; ++cb)
                     if (cb <= tb)
-                        acc = E::mma16(sm.DB[pb][c2][cb][lane],
+                        acc = E::mma16(dbf(pb, c2, cb),
                                        E::load(Pf + (size_t)R::pblk(tb, cb, false) * 256 + lane * 4),
                                        acc);
                 if (st)
@@ -1205,10 +1227,10 @@ __global__ __launch_bounds__(768) void chunk_pass_kernel(ChunkArgs a, const void
             T* cd = static_cast<T*>(a.ck_d) + tt * D * CV + (size_t)vcol * 16 + 4 * grp;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
-                *reinterpret_cast<Frag*>(cs + (size_t)kb * D * 16) = sm.SB[pb][cw][kb][lane];
+                *reinterpret_cast<Frag*>(cs + (size_t)kb * D * 16) = sbf(pb, cw, kb);
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb)
-                *reinterpret_cast<Frag*>(cd + (size_t)cb * D * 16) = sm.DB[pb][cw][cb][lane];
+                *reinterpret_cast<Frag*>(cd + (size_t)cb * D * 16) = dbf(pb, cw, cb);
         }
         if (!a.o) return;  // checkpoint-only run (the backward pass's recompute)
         // the row block is a compile-time constant of each copy, so the causal
@@ -1235,18 +1257,27 @@ __global__ __launch_bounds__(768) void chunk_pass_kernel(ChunkArgs a, const void
             for (int m = 0; m < D / 32; ++m)
 #pragma unroll
                 for (int c2 = 0; c2 < 4; ++c2)
-                    acc[c2] = E::mma32(sm.SB[pb][c2][2 * m][lane], sm.SB[pb][c2][2 * m + 1][lane],
-                                       qf[2 * m], qf[2 * m + 1], acc[c2]);
+                {
+                    const s16x8 sp = sbp(pb, c2, m);
+                    acc[c2] = E::mma32(pair_lo(sp), pair_hi(sp), qf[2 * m], qf[2 * m + 1], acc[c2]);
+                }
             // Delta^T P^T over the causal blocks cb <= TB, two per product
             Frag of[4];
 #pragma unroll
             for (int c2 = 0; c2 < 4; ++c2) {
                 acc[c2] = acc[c2] * gs;
-                acc[c2] = E::mma32(sm.DB[pb][c2][0][lane], TB >= 1 ? sm.DB[pb][c2][1][lane] : zf,
-                                   pf[0], pf[1], acc[c2]);
-                if constexpr (TB >= 2)
-                    acc[c2] = E::mma32(sm.DB[pb][c2][2][lane], TB >= 3 ? sm.DB[pb][c2][3][lane] : zf,
-                                       pf[2], pf[3], acc[c2]);
+                if constexpr (TB >= 1) {
+                    const s16x8 dp = dbp(pb, c2, 0);
+                    acc[c2] = E::mma32(pair_lo(dp), pair_hi(dp), pf[0], pf[1], acc[c2]);
+                } else {
+                    acc[c2] = E::mma32(dbf(pb, c2, 0), zf, pf[0], zf, acc[c2]);
+                }
+                if constexpr (TB >= 3) {
+                    const s16x8 dp = dbp(pb, c2, 1);
+                    acc[c2] = E::mma32(pair_lo(dp), pair_hi(dp), pf[2], pf[3], acc[c2]);
+                } else if constexpr (TB == 2) {
+                    acc[c2] = E::mma32(dbf(pb, c2, 2), zf, pf[2], zf, acc[c2]);
+                }
                 of[c2] = E::pack(acc[c2]);  // O[t = 16 TB + lr][v = 16 c2 + 4 grp + r]
             }
             // transpose through the wave's own query rows (read above, in order)
