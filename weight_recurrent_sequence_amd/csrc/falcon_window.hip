@@ -126,7 +126,7 @@ struct WinPrepSmem {
 };
 
 template <int D, int W, bool DELTA>
-__global__ __launch_bounds__(256) void win_prep_kernel(ChunkArgs a, void* ws, int ntiles,
+__global__ __launch_bounds__(256, W <= 6 ? 2 : 1) void win_prep_kernel(ChunkArgs a, void* ws, int ntiles,
                                                        int njobs) {
     using E = EBf16;
     using T = uint16_t;
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256) void win_prep_kernel(ChunkArgs a, void* ws, in
             // round-robin over the waves ----
             constexpr int NL = RB * (RB - 1) / 2;
             constexpr int NJ = NL + RB + kNTB * RB;
-            for (int q = wave; q < NJ; q += 4) {
+            auto run_job = [&](const int q) __attribute__((always_inline)) {
                 if (q < NL) {
                     int rb = 1;
                     while (lblk(rb + 1, 0) <= q) ++rb;
@@ -366,6 +366,19 @@ __global__ __launch_bounds__(256) void win_prep_kernel(ChunkArgs a, void* ws, in
                     }
                     sm.Pf[tb][rb][lane] = E::pack(v);
                 }
+            };
+            if constexpr (NJ <= 64) {
+                // each wave's jobs q = wave + 4 i unrolled with constant q (the
+                // tests on q fold away), so one job's loads and products
+                // overlap the previous job's factor arithmetic
+                with_const4(wave, [&](auto wc) __attribute__((always_inline)) {
+                    constexpr int WV = decltype(wc)::value;
+                    static_for<(NJ - WV + 3) / 4>([&](auto ic) __attribute__((always_inline)) {
+                        run_job(WV + 4 * decltype(ic)::value);
+                    });
+                });
+            } else {
+                for (int q = wave; q < NJ; q += 4) run_job(q);
             }
             lds_barrier();
 
@@ -863,7 +876,13 @@ template <int D, int W, bool DELTA>
 hipError_t launch_prep(const ChunkArgs& b, void* ws, int ntiles, hipStream_t stream) {
     using Smem = WinPrepSmem<D, W, DELTA>;
     constexpr int per_cu_lds = (int)(163840 / sizeof(Smem));
-    constexpr int per_cu = per_cu_lds < 1 ? 1 : (per_cu_lds > 2 ? 2 : per_cu_lds);
+    int per_cu = per_cu_lds < 1 ? 1 : (per_cu_lds > 2 ? 2 : per_cu_lds);
+    // a persistent grid must be resident at once: no more workgroups per CU
+    // than the kernel's registers allow (the larger windows fit one)
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, win_prep_kernel<D, W, DELTA>, 256, 0) == hipSuccess &&
+        occ >= 1 && occ < per_cu)
+        per_cu = occ;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
