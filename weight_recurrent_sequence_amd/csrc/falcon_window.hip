@@ -306,11 +306,15 @@ __global__ __launch_bounds__(256, W <= 6 ? 2 : 1) void win_prep_kernel(ChunkArgs
                     const f32x4 gv = gram(&sm.X[row_pair<W>(16 * cb + lr)][8 * grp],
                                           &sm.X[row_pair<W>(i)][8 * grp]);
                     const float rf = exp2f(sm.g2[si] - sm.gref[cb]);
+                    // factors loaded for every lane, then selected: a load
+                    // under a lane condition would become a branch
+                    const f32x4 cfv = *reinterpret_cast<const f32x4*>(&sm.cf[16 * cb + 4 * grp]);
                     f32x4 v;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int j = 16 * cb + 4 * grp + r;
-                        v[r] = (row_step<W>(j) < si) ? -(rf * sm.cf[j] * gv[r]) : 0.f;
+                        const float e = -(rf * cfv[r] * gv[r]);
+                        v[r] = (row_step<W>(j) < si) ? e : 0.f;
                     }
                     sm.Af[q][lane] = E::pack(v);
                 } else if (q < NL + RB) {
@@ -327,7 +331,10 @@ __global__ __launch_bounds__(256, W <= 6 ? 2 : 1) void win_prep_kernel(ChunkArgs
                     const f32x4 gv = gram(xr, xr);
                     auto nfac = [&](int i, int j) __attribute__((always_inline)) {
                         const int si = row_step<W>(i), sj = row_step<W>(j);
-                        return sj < si ? exp2f(sm.g2[si] - sm.g2[sj]) * sm.bs[sj] : 0.f;
+                        // evaluated for every lane and selected (no branch);
+                        // the discarded values may be large but are never used
+                        const float e = exp2f(sm.g2[si] - sm.g2[sj]) * sm.bs[sj];
+                        return sj < si ? e : 0.f;
                     };
                     f32x4 aN, bN, aI;
 #pragma unroll
@@ -361,8 +368,12 @@ __global__ __launch_bounds__(256, W <= 6 ? 2 : 1) void win_prep_kernel(ChunkArgs
                     for (int r = 0; r < 4; ++r) {
                         const int j = 16 * rb + 4 * grp + r, sj = row_step<W>(j);
                         const float qk = gv[r];
-                        v[r] = full ? rf * sm.cf[j] * qk
-                                    : (sj <= t ? exp2f(sm.g2[t] - sm.g2[sj]) * sm.bs[sj] * qk : 0.f);
+                        if (full) {
+                            v[r] = rf * sm.cf[j] * qk;
+                        } else {
+                            const float e = exp2f(sm.g2[t] - sm.g2[sj]) * sm.bs[sj] * qk;
+                            v[r] = sj <= t ? e : 0.f;
+                        }
                     }
                     sm.Pf[tb][rb][lane] = E::pack(v);
                 }
@@ -426,6 +437,14 @@ __global__ __launch_bounds__(256, W <= 6 ? 2 : 1) void win_prep_kernel(ChunkArgs
                     if constexpr (rb % 2 == 1) {
                         constexpr int r0 = rb - 1;
                         constexpr int plo = row_step<W>(16 * r0), phi_ = row_step<W>(16 * rb + 15) + W - 1;
+                        // h of the two blocks' rows, read for every lane and
+                        // selected per pair block below
+                        f32x4 hs0, hs1;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            hs0[r] = sm.hs[row_step<W>(16 * r0 + 4 * grp + r)];
+                            hs1[r] = sm.hs[row_step<W>(16 * rb + 4 * grp + r)];
+                        }
                         static_for<kNPB>([&](auto pbc) __attribute__((always_inline)) {
                             constexpr int pb = decltype(pbc)::value;
                             if constexpr (16 * pb <= phi_ && 16 * pb + 15 >= plo) {
@@ -433,8 +452,8 @@ __global__ __launch_bounds__(256, W <= 6 ? 2 : 1) void win_prep_kernel(ChunkArgs
 #pragma unroll
                                 for (int r = 0; r < 4; ++r) {
                                     const int j0 = 16 * r0 + 4 * grp + r, j1 = j0 + 16;
-                                    h0[r] = (row_pair<W>(j0) == 16 * pb + lr) ? sm.hs[row_step<W>(j0)] : 0.f;
-                                    h1[r] = (row_pair<W>(j1) == 16 * pb + lr) ? sm.hs[row_step<W>(j1)] : 0.f;
+                                    h0[r] = (row_pair<W>(j0) == 16 * pb + lr) ? hs0[r] : 0.f;
+                                    h1[r] = (row_pair<W>(j1) == 16 * pb + lr) ? hs1[r] : 0.f;
                                 }
                                 const Frag hb0 = E::pack(h0), hb1 = E::pack(h1);
                                 nP[pb] = E::mma32(Mp[r0], Mp[rb], hb0, hb1, nP[pb]);
