@@ -1841,8 +1841,12 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
             // column block's omega rows serve both products as two independent
             // accumulation chains.
             constexpr int KM = D / 32;
-            const int bA = wave, bP = DELTA ? NB - 1 - wave : wave;
-            if (wave < NB) {
+            // the wave's row blocks are compile-time constants of each copy, so
+            // the causal tests on the column block leave no branches
+            with_const4(wave, [&](auto wc) __attribute__((always_inline)) {
+            constexpr int WV = decltype(wc)::value;
+            constexpr int bA = WV, bP = DELTA ? NB - 1 - WV : WV;
+            if constexpr (WV < NB) {
                 s16x8 xa[KM], qp[KM];
 #pragma unroll
                 for (int m = 0; m < KM; ++m) {
@@ -1853,20 +1857,20 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
                 const float giA = sm.gv[iA], giP = sm.gs[iP];
                 static_for<NB>([&](auto cc) __attribute__((always_inline)) {
                     constexpr int c = decltype(cc)::value;
-                    const bool doA = DELTA && c <= bA, doP = c <= bP;
-                    if (doA || doP) {
+                    constexpr bool doA = DELTA && c <= bA, doP = c <= bP;
+                    if constexpr (doA || doP) {
                         const T* ar = omb + (size_t)(16 * c + lr) * LDX + 8 * grp;
                         f32x4 accA = zero4(), accP = zero4();
 #pragma unroll
                         for (int m = 0; m < KM; ++m) {
                             const s16x8 om = E::load8(ar + 32 * m);
-                            if (doA) accA = E::mma32r(om, xa[m], accA);
-                            if (doP) accP = E::mma32r(om, qp[m], accP);
+                            if constexpr (doA) accA = E::mma32r(om, xa[m], accA);
+                            if constexpr (doP) accP = E::mma32r(om, qp[m], accP);
                         }
                         const int j0 = 16 * c + 4 * grp;
-                        if (doA) {
+                        if constexpr (doA) {
                             f32x4 val;
-                            if (c < bA) {
+                            if constexpr (c < bA) {
                                 // fully unmasked: row factor times column factor
                                 const f32x4 cfj = *reinterpret_cast<const f32x4*>(&sm.cf[j0]);
                                 const float rf = exp2f(giA - sm.gref[c]);
@@ -1880,14 +1884,16 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
 #pragma unroll
                                 for (int r = 0; r < 4; ++r) {
                                     const int j = j0 + r;
-                                    val[r] = (j < iA) ? exp2f(giA - gj[r]) * accA[r] * rj[r] : 0.f;
+                                    // every lane evaluates, the mask selects (no branch)
+                                    const float e = exp2f(giA - gj[r]) * accA[r] * rj[r];
+                                    val[r] = (j < iA) ? e : 0.f;
                                     sm.Adg[bA][lr][4 * grp + r] = val[r];
                                 }
                             }
                         }
-                        if (doP) {
+                        if constexpr (doP) {
                             f32x4 val;
-                            if (c < bP) {
+                            if constexpr (c < bP) {
                                 const f32x4 cfj = *reinterpret_cast<const f32x4*>(&sm.cf[j0]);
                                 const float rf = exp2f(giP - sm.gref[c]);
 #pragma unroll
@@ -1898,8 +1904,8 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
 #pragma unroll
                                 for (int r = 0; r < 4; ++r) {
                                     const int j = j0 + r;
-                                    val[r] = (j <= iP && iP < Ct) ? exp2f(giP - gj[r]) * accP[r] * rj[r]
-                                                                  : 0.f;
+                                    const float e = exp2f(giP - gj[r]) * accP[r] * rj[r];
+                                    val[r] = (j <= iP && iP < Ct) ? e : 0.f;
                                 }
                             }
                             *reinterpret_cast<Frag*>(recT + R::kP + (size_t)R::pblk(bP, c, WIN) * 256 +
@@ -1908,6 +1914,7 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
                     }
                 });
             }
+            });
         } else {
             // window: round-robin over the waves
             for (int q = wave; q < NJA + NJP; q += 4) {
