@@ -109,7 +109,6 @@ struct WinPrepSmem {
     static constexpr int NA = DELTA ? RB * (RB - 1) / 2 : 1;
     uint16_t X[kEP][LDX];                  // pair keys x_p (rows >= E zero)
     uint16_t Q[kC][LDX];                   // queries
-    float QK[DELTA ? 1 : kC][kEP + 1];     // q_t . x_p (inner-product rule)
     float al[kC], et[kC];                  // gates (padding steps: 1, 0)
     float nrm[kEP];                        // ||x_p||^2
     float g2[kC];                          // log2(e) * g_s
@@ -280,15 +279,6 @@ __global__ __launch_bounds__(256, W <= 6 ? 2 : 1) void win_prep_kernel(ChunkArgs
                 acc = E::mma32r(E::load8(ar + 32 * m), E::load8(br + 32 * m), acc);
             return acc;
         };
-        if constexpr (!DELTA) {
-            // q_t . x_p for the inner-product rule's L'
-            for (int q = wave; q < kNTB * kNPB; q += 4) {
-                const int bi = q / kNPB, bj = q - bi * kNPB;
-                const f32x4 acc = gram(&sm.Q[16 * bi + lr][8 * grp], &sm.X[16 * bj + lr][8 * grp]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sm.QK[16 * bi + 4 * grp + r][16 * bj + lr] = acc[r];
-            }
-        }
         lds_barrier();
 
         if constexpr (DELTA) {
@@ -516,20 +506,24 @@ __global__ __launch_bounds__(256, W <= 6 ? 2 : 1) void win_prep_kernel(ChunkArgs
             for (int q = wave; q < kNTB * kNPB; q += 4) {
                 const int tb = q / kNPB, kb = q - tb * kNPB;
                 const int t = 16 * tb + lr;
+                // q_t . x_p, p = 16 kb + 4 grp + r, on the matrix cores
+                const f32x4 qk = gram(&sm.X[16 * kb + lr][8 * grp], &sm.Q[t][8 * grp]);
+                // both cases evaluated for every lane and selected (a load or
+                // transcendental under a lane condition would become a branch)
+                float e2v[W];
+#pragma unroll
+                for (int d = 0; d < W; ++d) e2v[d] = sm.e2[t * W + d];
+                const float g2t = sm.g2[t];
                 f32x4 v;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int p = 16 * kb + 4 * grp + r;
-                    float cp = 0.f;
-                    if (p <= t) {
-                        cp = exp2f(sm.g2[t] - sm.g2[p]) * sm.cpp[p];
-                    } else {
-                        // steps s' in [p - W + 1, t]: d = t - s'
+                    const float near = exp2f(g2t - sm.g2[min(p, kC - 1)]) * sm.cpp[p];
+                    // steps s' in [p - W + 1, t]: d = t - s'
+                    float far = 0.f;
 #pragma unroll
-                        for (int d = 0; d < W; ++d)
-                            if (t - d >= p - W + 1 && t - d >= 0) cp += sm.e2[t * W + d];
-                    }
-                    v[r] = sm.QK[t][p] * cp;
+                    for (int d = 0; d < W; ++d) far += (t - d >= p - W + 1 && t - d >= 0) ? e2v[d] : 0.f;
+                    v[r] = qk[r] * (p <= t ? near : far);
                 }
                 fb[R::fb(tb, kb) * 64 + lane] = E::pack(v);
             }
@@ -895,7 +889,7 @@ template <int D, int W, bool DELTA>
 hipError_t launch_prep(const ChunkArgs& b, void* ws, int ntiles, hipStream_t stream) {
     using Smem = WinPrepSmem<D, W, DELTA>;
     constexpr int per_cu_lds = (int)(163840 / sizeof(Smem));
-    int per_cu = per_cu_lds < 1 ? 1 : (per_cu_lds > 2 ? 2 : per_cu_lds);
+    int per_cu = per_cu_lds < 1 ? 1 : (per_cu_lds > 4 ? 4 : per_cu_lds);
     // a persistent grid must be resident at once: no more workgroups per CU
     // than the kernel's registers allow (the larger windows fit one)
     int occ = 0;
