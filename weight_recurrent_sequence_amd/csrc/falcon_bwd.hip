@@ -755,22 +755,25 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
         if (qv + 1 < NQ) load_q(qv + 1);
         lds_barrier();
         const bf* Dq = &sm.u.q.Dq[0][0];
-        {
-            const Frag dj0 = colfrag(Dq, LDC, 0, 16 * jbw), dj1 = colfrag(Dq, LDC, 16, 16 * jbw);
+        // the wave's block jbw is a compile-time constant of each copy, so
+        // the causal tests leave no branches between the products
+        with_const4(jbw, [&](auto jc) __attribute__((always_inline)) {
+            constexpr int JB = decltype(jc)::value;
+            const Frag dj0 = colfrag(Dq, LDC, 0, 16 * JB), dj1 = colfrag(Dq, LDC, 16, 16 * JB);
 #pragma unroll
             for (int tb = 0; tb < NB; ++tb) {
                 // DP^T block (jbw, tb): query block tb reaching back to a row of block jbw
-                if (tb < NBQ && (16 * jbw) / Wv <= 16 * tb + 15) {
+                if (tb < NBQ && (16 * JB) / Wv <= 16 * tb + 15) {
                     const bf* orow = &sm.u.q.dOq[16 * tb + lr][4 * grp];
                     aP[tb] = E::mma32(dj0, dj1, E::load(orow), E::load(orow + 16), aP[tb]);
                 }
                 // DA^T block (jbw, tb): only rows of later steps, so tb >= jbw
-                if (DELTA && tb >= jbw) {
+                if (DELTA && tb >= JB) {
                     const bf* rrow = &sm.u.q.dRq[16 * tb + lr][4 * grp];
                     aA[tb] = E::mma32(dj0, dj1, E::load(rrow), E::load(rrow + 16), aA[tb]);
                 }
             }
-        }
+        });
 #pragma unroll
         for (int kk = 0; kk < KPW; ++kk) {
             const int kb = KPW * wave + kk;
@@ -837,8 +840,14 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a) {
             const int j = 16 * jbw + 4 * grp + r;
             const float gj = sm.gv[j], rj = sm.rr[j];
             const int sj = sm.st[j];
-            const float vp = (sj <= t && t < Ct) ? aP[tb][r] * exp2f(gt - gj) : 0.f;
-            const float va = (DELTA && sj < si) ? -aA[tb][r] * exp2f(gi - gj) : 0.f;
+            // evaluated for every lane and selected (no branch around exp2)
+            const float ep = aP[tb][r] * exp2f(gt - gj);
+            const float vp = (sj <= t && t < Ct) ? ep : 0.f;
+            float va = 0.f;
+            if constexpr (DELTA) {
+                const float ea = -aA[tb][r] * exp2f(gi - gj);
+                va = sj < si ? ea : 0.f;
+            }
             sm.u.m.DP[j][t] = f2bf(vp);
             sm.u.m.DPr[j][t] = f2bf(vp * rj);
             sm.u.m.DA[j][t] = f2bf(va);
