@@ -60,17 +60,12 @@ __device__ __forceinline__ BSeq bwd_seq(const BwdArgs& a, int bh) {
     return {(size_t)h * a.Ttot + s0, s1 - s0};
 }
 
-// The per-column rule's write vector, u = eta x / (|x| l1 + eps) entry by
-// entry (l1 = ||x||_1 of the entry's row), for four bf16 entries whose rows
-// may differ (l1 and eta given per entry).
+// The per-column rule's write vector (col_write) for four bf16 entries whose
+// rows may differ (l1 and eta given per entry).
 __device__ __forceinline__ s16x4 col_write4(s16x4 x, f32x4 l1, f32x4 eta, float eps) {
     f32x4 u;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const float v = bf2f((bf)x[r]);
-        const float den = fabsf(v) * l1[r] + eps;
-        u[r] = den > 0.f ? eta[r] * v / den : 0.f;
-    }
+    for (int r = 0; r < 4; ++r) u[r] = col_write(bf2f((bf)x[r]), l1[r], eta[r], eps);
     return EBf16::pack(u);
 }
 

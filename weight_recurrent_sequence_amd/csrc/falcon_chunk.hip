@@ -1510,7 +1510,8 @@ __global__ __launch_bounds__(768) void chunk_pass_kernel(ChunkArgs a, const void
         } else {
             for (int it = 0; it <= ntl; ++it) {
                 if (!ROWS && it >= 2) store_o(it - 2);
-                if (it + 1 < ntl && (it + 1) * Ct < W) {
+                // (without a window W = 1, so only tile 0, in the prologue)
+                if (WIN && it + 1 < ntl && (it + 1) * Ct < W) {
                     load_xyr(it + 1);
                     store_xyr(it + 1);
                 }
@@ -1813,16 +1814,7 @@ __global__ __launch_bounds__(256, kPrepPerCu<DELTA>) void chunk_prep2_kernel(Chu
                 const int i = c / CPR, col = (c % CPR) * 8;
                 const int s = WIN ? min(i / Wv, Ct - 1) : min(i, Ct - 1);
                 const float et = (i < NVR) ? sm.et[s] : 0.f, l1 = sm.l1[i];
-                const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.X[i][col]);
-                const T* e = reinterpret_cast<const T*>(&v);
-                u32x4 outv;
-                T* out = reinterpret_cast<T*>(&outv);
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const float x = E::to_f(e[u]);
-                    const float den = fabsf(x) * l1 + eps;
-                    out[u] = E::from_f(den > 0.f ? et * x / den : 0.f);
-                }
+                const u32x4 outv = col_write8(*reinterpret_cast<const u32x4*>(&sm.X[i][col]), l1, et, eps);
                 *reinterpret_cast<u32x4*>(&sm.Om[i][col]) = outv;
                 // and for the state pass (rows past the sequence hold zeros)
                 *reinterpret_cast<u32x4*>(static_cast<T*>(a.uws) +

@@ -39,6 +39,25 @@ __device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(ui
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// One entry of the per-column rule's write vector, u = eta x / (|x| l1 + eps)
+// with l1 = ||x||_1 of the entry's row, through the hardware reciprocal
+// (about 1 ulp; every caller rounds u to bf16 next).  The bf16 kernels that
+// form u (intra-chunk products, state update, backward) all use this one
+// expression, so they see the same bits.
+__device__ __forceinline__ float col_write(float x, float l1, float eta, float eps) {
+    const float den = __builtin_fmaf(fabsf(x), l1, eps);
+    return den > 0.f ? (eta * x) * __builtin_amdgcn_rcpf(den) : 0.f;
+}
+// Eight bf16 entries of one row (16 bytes) to their write-vector entries.
+__device__ __forceinline__ u32x4 col_write8(u32x4 v, float l1, float eta, float eps) {
+    const uint16_t* e = reinterpret_cast<const uint16_t*>(&v);
+    u32x4 o;
+    uint16_t* out = reinterpret_cast<uint16_t*>(&o);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) out[u] = f2bf(col_write(bf2f(e[u]), l1, eta, eps));
+    return o;
+}
+
 struct EBf16 {
     using T = uint16_t;   // storage element in HBM and LDS
     using Frag = s16x4;   // four operand values
