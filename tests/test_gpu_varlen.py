@@ -95,6 +95,26 @@ def test_varlen_equals_one_call_per_sequence(dev, case):
         assert torch.equal(S[n], Sn[0]), n
 
 
+def test_varlen_window_inner_product_two_segments(dev):
+    """Falcon-3A packed calls whose longest sequence has 64 tiles or more run
+    every sequence's chain as two segments: long ones split, a one-tile and an
+    empty sequence leave the second segment empty."""
+    lengths = [2100, 0, 33, 4100, 700]
+    vi = I.make_varlen_inputs(lengths, 2, 128, 128, dtype="bf16", seed=990, window=4, S0_sd=0.3,
+                              halo=True)
+    o, S = run_varlen(dev, vi, "F3A", 64)
+    o_np, S_np = to_np(o), to_np(S)
+    for n in range(len(lengths)):
+        d = vi.sequence(n).f64()
+        o_ref, S_ref = oracle.recurrent("F3A", d["q"], d["k"], d["v"], d["alpha"], d["eta"],
+                                        window=4, S0=d["S0"], k_prev=d["k_prev"],
+                                        v_prev=d["v_prev"])
+        a, b = vi.cu[n], vi.cu[n + 1]
+        if b > a:
+            assert slice_rel_err(o_np[None, :, a:b], o_ref, (2, 3)) <= TOL["bf16"], n
+        assert slice_rel_err(S_np[n:n + 1], S_ref, (2, 3)) <= TOL["bf16"], n
+
+
 def test_varlen_leaves_rows_outside_sequences(dev):
     """Rows after the last sequence belong to none and are not written."""
     vi = I.make_varlen_inputs([40, 70], 2, 64, 64, dtype="bf16", seed=970, tail=33)

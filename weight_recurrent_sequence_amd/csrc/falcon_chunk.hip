@@ -2176,7 +2176,7 @@ size_t chunk_workspace_bytes(int BH, int T, int dt, int chunk, int window, int n
     // bf16 windows: room for the records of either form (the collapsed one
     // runs the forward, the virtual-row one the backward's checkpoint runs)
     if (dt == 1 && norm == kNormWindow && window >= 2) {
-        const size_t wb = window_workspace_bytes(BH, T, delta);
+        const size_t wb = window_workspace_bytes(BH, T, delta, D);
         return wb > bytes ? wb : bytes;
     }
     return bytes;

@@ -161,7 +161,7 @@ hipError_t launch_packed_schedule(const ChunkArgs& a, int Ct, int ntiles, ChunkA
 // The window rules (W >= 2) at bf16 in the collapsed form: tiles of kWinC
 // steps whose C + W - 1 distinct (key, value) pairs carry the state update.
 constexpr int kWinC = 32;
-size_t window_workspace_bytes(int BH, int T, bool delta);
+size_t window_workspace_bytes(int BH, int T, bool delta, int D);
 hipError_t launch_window(const ChunkArgs& a, int D, bool delta, void* ws, hipStream_t stream);
 
 // The scalar inner-product rule (kNormScalar, or kNormWindow with W = 1) at

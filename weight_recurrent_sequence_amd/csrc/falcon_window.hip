@@ -70,6 +70,11 @@ struct WinRec {
     static __host__ __device__ constexpr int fb(int tb, int kb) { return tb * NKB + kb; }
 };
 
+// Bytes of the records of BH sequences of nt tiles (256-byte multiples).
+__host__ __device__ constexpr size_t window_records_bytes(int BH, int nt, bool delta) {
+    return (size_t)BH * nt * (delta ? WinRec<true>::kBytes : WinRec<false>::kBytes);
+}
+
 // Step and pair of virtual row r (row r = s W + w learns pair s + W - 1 - w).
 template <int W>
 __host__ __device__ constexpr int row_step(int r) { return r / W; }
@@ -534,54 +539,212 @@ __global__ __launch_bounds__(256, W <= 6 ? 2 : 1) void win_prep_kernel(ChunkArgs
 }
 
 // ---------------------------------------------------------------------------
-// State pass: one workgroup per (batch*head, 16-wide value slice), walking the
-// tiles in order.  Wave 0 carries the slice's state as MFMA accumulators of
-// S^T and forms the products the next state needs (X S0^T, delta, the update);
-// wave 1 forms the tile's outputs from the state at the tile's start, which
-// wave 0 hands over through LDS; waves 2 .. 2 + NF - 1 share the fill of
+// Two-segment state pass of the inner-product rule.  Its state increments do
+// not depend on the state, so after a run of tiles that starts from a state S
+// the state is (the product of the run's gamma_last) S plus the state the
+// same run reaches from zero.  The state pass therefore splits each chain of
+// ntl tiles at seg_split(ntl) and runs both segments at once (two workgroups
+// per compute unit fit); the second segment starts from the state at the
+// split, which win_seg_kernel forms beforehand: the first segment's tiles in
+// groups of kSegTiles, each group's state from zero (part) and the product of
+// its gamma_last (gprod), combined group by group when the second segment
+// starts.  Chains shorter than kSegMinTiles tiles (the longest of the call)
+// keep one segment.
+// ---------------------------------------------------------------------------
+constexpr int kSegTiles = 32;
+constexpr int kSegMinTiles = 64;
+__host__ __device__ constexpr int seg_split(int ntl) { return (ntl + 1) / 2; }
+__host__ __device__ constexpr int seg_groups(int ntiles) {
+    return (seg_split(ntiles) + kSegTiles - 1) / kSegTiles;
+}
+
+// One workgroup of D / 16 waves per (group g, batch*head): wave w carries
+// value columns 16 w .. 16 w + 15 of the group's state from zero, with the
+// state pass's per-tile update S^T = gamma_last S^T + X^T delta,
+// delta_p = c_p y_p; every key tile is loaded once for all columns.  Keys and
+// values are staged through registers one tile ahead (tile 0 reads the halo
+// rows, as the state pass does).
+// part: [BH][gmax][D][D] fp32 (S layout, [v][k]), then gprod [BH][gmax].
+template <int D>
+__global__ __launch_bounds__(4 * D) void win_seg_kernel(ChunkArgs a, const void* ws, int ntiles, int gmax,
+                                                        float* part) {
+    using E = EBf16;
+    using T = uint16_t;
+    using Frag = s16x4;
+    using R = WinRec<false>;
+    constexpr int KB = D / 16, CPR = D / 8, NT = 4 * D;
+    constexpr int NXC = kEP * CPR;  // 16-byte pieces of a key (and of a value) tile
+    constexpr int NXL = (NXC + NT - 1) / NT;
+    __shared__ alignas(16) uint16_t X[kEP * D];  // pair keys, swizzled rows as in the state pass
+    __shared__ alignas(16) uint16_t V[kEP * D];  // pair values
+    __shared__ alignas(16) float cf[kEP + 16];   // c_p, then gamma_last at [kEP]
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, lr = lane & 15;
+    const int g = blockIdx.x / a.BH, bh = blockIdx.x - g * a.BH;
+    const int W = a.W, NP = kC + W - 1;
+    const SeqRows sr = seq_rows(a, bh);
+    const int T_ = sr.T, ntl = tiles_of(T_, kC), Lt = seg_split(ntl);
+    const int j0 = g * kSegTiles, j1 = min(j0 + kSegTiles, Lt);
+    if (j0 >= j1) return;  // a group the state pass does not read
+    const T* kg = static_cast<const T*>(a.k) + sr.row0 * D;
+    const T* vg = static_cast<const T*>(a.v) + sr.row0 * D;
+    const T* kp = a.k_prev ? static_cast<const T*>(a.k_prev) + (size_t)bh * W * D : nullptr;
+    const T* vp = a.v_prev ? static_cast<const T*>(a.v_prev) + (size_t)bh * (W - 1) * D : nullptr;
+    const float* recf = reinterpret_cast<const float*>(static_cast<const char*>(ws) +
+                                                       (size_t)bh * ntiles * R::kBytes + R::kF);
+    constexpr size_t RF = R::kBytes / 4;  // record stride in floats
+
+    u32x4 px[NXL], pv[NXL];
+    float pc = 0.f;
+    auto load = [&](int j) __attribute__((always_inline)) {
+        const int t0 = j * kC;
+        const u32x4 zz = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < NXL; ++i) {
+            const int c = tid + NT * i;
+            const int p = c / CPR, col = (c % CPR) * 8;
+            const int tau = t0 - (W - 1) - a.lag + p;  // key of pair p
+            const T* src = nullptr;
+            if (c < NXC && p < NP && tau < T_) {
+                if (tau >= 0) src = kg + (size_t)tau * D + col;
+                else if (kp) src = kp + (size_t)(W + tau) * D + col;
+            }
+            px[i] = src ? *reinterpret_cast<const u32x4*>(src) : zz;
+        }
+#pragma unroll
+        for (int i = 0; i < NXL; ++i) {
+            const int c = tid + NT * i;
+            const int p = c / CPR, col = (c % CPR) * 8;
+            const int tv = t0 - (W - 1) + p;  // value of pair p
+            const T* src = nullptr;
+            if (c < NXC && p < NP && tv < T_) {
+                if (tv >= 0) src = vg + (size_t)tv * D + col;
+                else if (vp) src = vp + (size_t)(W - 1 + tv) * D + col;
+            }
+            pv[i] = src ? *reinterpret_cast<const u32x4*>(src) : zz;
+        }
+        // c_p of the tile's pair slots and its gamma_last
+        if (tid <= kEP) pc = recf[(size_t)j * RF + (tid < kEP ? 64 + tid : kC)];
+    };
+    auto colfrag = [&](int row0, int col0) __attribute__((always_inline)) {
+        return E::load_tr(X + swz_off<D>(row0 + 4 * grp + (lr >> 2), col0 + 4 * (lr & 3)));
+    };
+
+    // Sacc[kb][r] = S[v][k], v = 16 wave + lr, k = 16 kb + 4 grp + r
+    f32x4 Sacc[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) Sacc[kb] = zero4();
+    float gp = 1.f;
+    const Frag z = {0, 0, 0, 0};
+    load(j0);
+    for (int j = j0; j < j1; ++j) {
+#pragma unroll
+        for (int i = 0; i < NXL; ++i) {
+            const int c = tid + NT * i;
+            if (c < NXC) {
+                *reinterpret_cast<u32x4*>(&X[swz_off<D>(c / CPR, (c % CPR) * 8)]) = px[i];
+                *reinterpret_cast<u32x4*>(&V[c * 8]) = pv[i];
+            }
+        }
+        if (tid <= kEP) cf[tid] = pc;
+        lds_barrier();
+        if (j + 1 < j1) load(j + 1);
+        // delta of the wave's 16 columns: B fragments over the pair blocks
+        Frag Db[kNPB];
+#pragma unroll
+        for (int pb = 0; pb < kNPB; ++pb) {
+            const Frag vf = E::load_tr(V + (16 * pb + 4 * grp + (lr >> 2)) * D + 16 * wave + 4 * (lr & 3));
+            const f32x4 c4 = *reinterpret_cast<const f32x4*>(&cf[16 * pb + 4 * grp]);
+            f32x4 d;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) d[r] = c4[r] * E::to_f((T)vf[r]);
+            Db[pb] = E::pack(d);
+        }
+        const float glast = cf[kEP];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            f32x4 acc = Sacc[kb] * glast;
+            acc = E::mma32(colfrag(0, 16 * kb), colfrag(16, 16 * kb), Db[0], Db[1], acc);
+            acc = E::mma32(colfrag(32, 16 * kb), z, Db[2], z, acc);
+            Sacc[kb] = acc;
+        }
+        gp *= glast;
+        lds_barrier();  // the next tile's staging overwrites the tiles
+    }
+    float* pg = part + ((size_t)bh * gmax + g) * D * D + (size_t)(16 * wave + lr) * D + 4 * grp;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) *reinterpret_cast<f32x4*>(pg + 16 * kb) = Sacc[kb];
+    if (tid == 0) part[(size_t)a.BH * gmax * D * D + (size_t)bh * gmax + g] = gp;
+}
+
+// ---------------------------------------------------------------------------
+// State pass: one workgroup per (segment, batch*head, SW-wide value slice),
+// walking its tiles in order.  Chain wave c (c < SW / 16) carries 16 columns
+// of the slice's state as MFMA accumulators of S^T and forms the products the
+// next state needs (X S0^T, delta, the update); output wave c forms those
+// columns' outputs of the tile from the state at the tile's start, which its
+// chain wave hands over through LDS; the NF fill waves share the fill of
 // every tile and issue its loads NF tiles ahead.  One LDS-only barrier per
-// tile.
+// tile.  The delta rule runs one segment of 16-column slices; the
+// inner-product rule with long chains two segments of 32-column slices.
 //
 // Key and query tiles hold rows of D elements with no padding, chunks
 // swizzled per row (swz_off).
 // ---------------------------------------------------------------------------
-template <int D, bool DELTA>
+template <int D, bool DELTA, int SW>
 struct WinPassSmem {
     using R = WinRec<DELTA>;
     uint16_t X[2][kEP * D];    // pair keys (swizzled rows)
     uint16_t Q[2][kC * D];     // queries (swizzled rows)
-    uint16_t V[2][kEP * 16];   // pair values of the slice's 16 columns
+    uint16_t V[2][kEP * SW];   // pair values of the slice's SW columns
     alignas(16) char rec[2][R::kBytes];
-    s16x4 SB[2][D / 16][64];   // the state at a tile's start, B fragments of S^T
+    s16x4 SB[2][SW / 16][D / 16][64];  // the state at a tile's start, B fragments of S^T, per chain wave
 };
 
 constexpr int kPassFill = 4;  // fill waves = tiles in flight
 
-template <int D, bool DELTA>
-__global__ __launch_bounds__(64 * (2 + kPassFill)) void win_pass_kernel(ChunkArgs a, const void* ws,
-                                                                        int ntiles) {
+// SW value columns per workgroup (16 or 32): SW / 16 chain waves and as
+// many output waves, each owning 16 columns, then the fill waves.  Wider
+// slices share each key and query tile among more columns, so a compute unit
+// moves fewer bytes per unit of work.
+template <int D, bool DELTA, int SW>
+__global__ __launch_bounds__(64 * (2 * (SW / 16) + kPassFill)) void win_pass_kernel(
+    ChunkArgs a, const void* ws, int ntiles, int nseg, int gmax, const float* part) {
     using E = EBf16;
     using T = uint16_t;
     using Frag = s16x4;
     using R = WinRec<DELTA>;
-    using Smem = WinPassSmem<D, DELTA>;
-    constexpr int KB = D / 16, NVS = D / 16, CPR = D / 8, NF = kPassFill;
+    using Smem = WinPassSmem<D, DELTA, SW>;
+    constexpr int KB = D / 16, NVS = D / SW, CPR = D / 8, NF = kPassFill, NCW = SW / 16;
     constexpr int RCH = (int)(R::kBytes / 16);  // 16-byte pieces of a record
     __shared__ Smem sm;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4,
               lr = lane & 15;
+    // the segment (inner-product rule: nseg = 2 splits each chain in two)
+    const int per = (int)gridDim.x / nseg;
+    const int seg = (int)blockIdx.x / per;
     // slices of one sequence on one XCD (workgroup i runs on XCD i mod 8)
-    const int blk = blockIdx.x, xcd = blk & 7, jj = blk >> 3;
+    const int blk = (int)blockIdx.x - seg * per, xcd = blk & 7, jj = blk >> 3;
     const int rr = (jj / NVS) * 8 + xcd, vs = jj % NVS;
     if (rr >= a.BH) return;
     const int bh = pass_bh(a, rr);
-    const int v0 = vs * 16;
+    const int v0 = vs * SW;
+    // a chain or output wave's 16 columns start at vc
+    const int cw = NCW == 1 ? 0 : (wave < NCW ? wave : wave - NCW);
+    const int vc = v0 + 16 * cw;
     const int W = a.W;
     const int NP = kC + W - 1;
     const SeqRows sr = seq_rows(a, bh);
     const int T_ = sr.T;
     const int ntl = tiles_of(T_, kC);
+    // this workgroup's tiles [tb0, tb1); the one that ends the chain writes
+    // S_final (the delta rule always runs one segment)
+    const bool first = DELTA || seg == 0;
+    const int Lt = (!DELTA && nseg > 1) ? seg_split(ntl) : ntl;
+    const int tb0 = first ? 0 : Lt, tb1 = first ? Lt : ntl;
+    if (!first && tb0 >= tb1) return;  // an empty second segment
+    const bool ends = first ? Lt == ntl : true;
     const T* qg = static_cast<const T*>(a.q) + sr.row0 * D;
     const T* kg = static_cast<const T*>(a.k) + sr.row0 * D;
     const T* vg = static_cast<const T*>(a.v) + sr.row0 * D + v0;
@@ -602,25 +765,42 @@ __global__ __launch_bounds__(64 * (2 + kPassFill)) void win_pass_kernel(ChunkArg
     };
     // the pair values: b(Y block kb) = a(Y^T block kb), rows of 16 elements
     auto vfrag = [&](const T* vb, int kb) __attribute__((always_inline)) {
-        return E::load_tr(vb + (16 * kb + 4 * grp + (lr >> 2)) * 16 + 4 * (lr & 3));
+        return E::load_tr(vb + (16 * kb + 4 * grp + (lr >> 2)) * SW + 16 * cw + 4 * (lr & 3));
     };
 
-    if (wave == 0) {
+    if (wave < NCW) {
         // ---- the state chain ----
-        // Sacc[kb][r] = S[v][k], v = v0 + lr, k = 16 kb + 4 grp + r
+        // Sacc[kb][r] = S[v][k], v = vc + lr, k = 16 kb + 4 grp + r
         f32x4 Sacc[KB];
         Frag SB[KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int kb = 0; kb < KB; ++kb)
             Sacc[kb] = a.S0 ? *reinterpret_cast<const f32x4*>(
-                                  a.S0 + ((size_t)bh * D + v0 + lr) * D + 16 * kb + 4 * grp)
+                                  a.S0 + ((size_t)bh * D + vc + lr) * D + 16 * kb + 4 * grp)
                             : zero4();
+        if constexpr (!DELTA) {
+            if (seg > 0) {
+                // the state at the split: S0 carried through the first
+                // segment's groups in order, S = gprod_g S + part_g
+                const int G = (Lt + kSegTiles - 1) / kSegTiles;
+                const float* pp = part + (size_t)bh * gmax * D * D + (size_t)(vc + lr) * D + 4 * grp;
+                const float* gpr = part + (size_t)a.BH * gmax * D * D + (size_t)bh * gmax;
+                for (int gg = 0; gg < G; ++gg) {
+                    const float f = gpr[gg];
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb)
+                        Sacc[kb] = Sacc[kb] * f + *reinterpret_cast<const f32x4*>(pp + (size_t)gg * D * D + 16 * kb);
+                }
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
             SB[kb] = E::pack(Sacc[kb]);
-            sm.SB[0][kb][lane] = SB[kb];
+            sm.SB[0][cw][kb][lane] = SB[kb];
         }
         lds_barrier();
-        for (int it = 0; it < ntl; ++it) {
-            const int b = it & 1;
+        for (int it = tb0; it < tb1; ++it) {
+            const int b = (it - tb0) & 1;
             const T* Xb = sm.X[b];
             const char* rec = sm.rec[b];
             const Frag* FA = reinterpret_cast<const Frag*>(rec + R::kA);
@@ -676,23 +856,23 @@ __global__ __launch_bounds__(64 * (2 + kPassFill)) void win_pass_kernel(ChunkArg
                 acc = E::mma32(colfrag(Xb, 32, 16 * kb), z, Db[2], z, acc);
                 Sacc[kb] = acc;
                 SB[kb] = E::pack(acc);
-                sm.SB[b ^ 1][kb][lane] = SB[kb];
+                sm.SB[b ^ 1][cw][kb][lane] = SB[kb];
             }
             lds_barrier();
         }
-        if (a.S_final) {
+        if (a.S_final && ends) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
-                *reinterpret_cast<f32x4*>(a.S_final + ((size_t)bh * D + v0 + lr) * D + 16 * kb +
+                *reinterpret_cast<f32x4*>(a.S_final + ((size_t)bh * D + vc + lr) * D + 16 * kb +
                                           4 * grp) = Sacc[kb];
         }
-    } else if (wave == 1) {
+    } else if (wave < 2 * NCW) {
         // ---- the outputs: O^T = (S0 Q^T) diag(gamma) + Y^T L'^T - Z^T L^T;
-        // lane ends with O[t = 16 tb + lr][v = v0 + 4 grp + r] ----
-        T* og = a.o ? static_cast<T*>(a.o) + sr.row0 * D + v0 : nullptr;
+        // lane ends with O[t = 16 tb + lr][v = vc + 4 grp + r] ----
+        T* og = a.o ? static_cast<T*>(a.o) + sr.row0 * D + vc : nullptr;
         lds_barrier();
-        for (int it = 0; it < ntl; ++it) {
-            const int b = it & 1, t0 = it * kC;
+        for (int it = tb0; it < tb1; ++it) {
+            const int b = (it - tb0) & 1, t0 = it * kC;
             const T* Xb = sm.X[b];
             const T* Qb = sm.Q[b];
             const char* rec = sm.rec[b];
@@ -700,7 +880,7 @@ __global__ __launch_bounds__(64 * (2 + kPassFill)) void win_pass_kernel(ChunkArg
             const float* FL = reinterpret_cast<const float*>(rec + R::kF);
             Frag SB[KB], Vf[kNPB];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) SB[kb] = sm.SB[b][kb][lane];
+            for (int kb = 0; kb < KB; ++kb) SB[kb] = sm.SB[b][cw][kb][lane];
 #pragma unroll
             for (int kb = 0; kb < kNPB; ++kb) Vf[kb] = vfrag(sm.V[b], kb);
             Frag Zb[kNPB];
@@ -750,8 +930,9 @@ __global__ __launch_bounds__(64 * (2 + kPassFill)) void win_pass_kernel(ChunkArg
         // ---- fill waves: every tile is split over the NF waves (lane l of
         // wave f takes the 16-byte pieces (64 f + l) + 256 i); each lane keeps
         // the pieces of the next NF tiles in registers, slot = tile mod NF ----
-        const int fl = 64 * (wave - 2) + lane;
-        constexpr int NXC = kEP * CPR, NQC = kC * CPR, NVC = kEP * 2;
+        const int fl = 64 * (wave - 2 * NCW) + lane;
+        constexpr int VPR = SW / 8;  // 16-byte pieces of a pair value row
+        constexpr int NXC = kEP * CPR, NQC = kC * CPR, NVC = kEP * VPR;
         constexpr int NXL = (NXC + 255) / 256, NQL = (NQC + 255) / 256, NVL = (NVC + 255) / 256,
                       NRL = (RCH + 255) / 256;
         u32x4 px[NF][NXL], pq[NF][NQL], pv[NF][NVL], pr[NF][NRL];
@@ -777,7 +958,7 @@ __global__ __launch_bounds__(64 * (2 + kPassFill)) void win_pass_kernel(ChunkArg
 #pragma unroll
             for (int i = 0; i < NVL; ++i) {
                 const int c = fl + 256 * i;
-                const int p = c / 2, col = (c % 2) * 8;
+                const int p = c / VPR, col = (c % VPR) * 8;
                 const int tv = p - (W - 1);  // value of pair p
                 const T* src = nullptr;
                 if (c < NVC && p < NP && tv < T_) {
@@ -811,7 +992,7 @@ __global__ __launch_bounds__(64 * (2 + kPassFill)) void win_pass_kernel(ChunkArg
 #pragma unroll
             for (int i = 0; i < NVL; ++i) {
                 const int c = fl + 256 * i;
-                const int p = c / 2, col = (c % 2) * 8;
+                const int p = c / VPR, col = (c % VPR) * 8;
                 const int tv = t0 - (W - 1) + p;
                 v[i] = buf_load16(vr, (c < NVC && p < NP && tv < T_) ? (uint32_t)((tv * D + col) * 2)
                                                                     : kOob);
@@ -827,9 +1008,9 @@ __global__ __launch_bounds__(64 * (2 + kPassFill)) void win_pass_kernel(ChunkArg
                 r[i] = buf_load16(rr_, c < RCH ? (uint32_t)(tile * R::kBytes + c * 16) : kOob);
             }
         };
-        auto store = [&](int tile, const auto& x, const auto& q, const auto& v, const auto& r)
+        auto store = [&](int rel, const auto& x, const auto& q, const auto& v, const auto& r)
             __attribute__((always_inline)) {
-            const int b = tile & 1;
+            const int b = rel & 1;
 #pragma unroll
             for (int i = 0; i < NXL; ++i) {
                 const int c = fl + 256 * i;
@@ -853,30 +1034,35 @@ __global__ __launch_bounds__(64 * (2 + kPassFill)) void win_pass_kernel(ChunkArg
                 if (c < RCH) reinterpret_cast<u32x4*>(sm.rec[b])[c] = r[i];
             }
         };
-        // tiles 0 .. NF - 1 in flight; tile 0 is published before the first
-        // barrier and tile NF takes its slot.  At step it tile it + 1 moves
-        // from slot (it + 1) mod NF into LDS and tile it + 1 + NF is issued
-        // into the slot.  The barriers order LDS only, so the loads stay in
-        // flight across them.
-        if (ntl > 0) issue0(px[0], pq[0], pv[0], pr[0]);
+        // The segment's tiles by index i relative to tb0 (n of them): tiles
+        // 0 .. NF - 1 in flight; tile 0 is published before the first barrier
+        // and tile NF takes its slot.  At step i tile i + 1 moves from slot
+        // (i + 1) mod NF into LDS and tile i + 1 + NF is issued into the slot.
+        // The barriers order LDS only, so the loads stay in flight across
+        // them.  Only the chain's first tile (tb0 = 0) reaches the halo.
+        const int n = tb1 - tb0;
+        if (n > 0) {
+            if (tb0 == 0) issue0(px[0], pq[0], pv[0], pr[0]);
+            else issue(tb0, px[0], pq[0], pv[0], pr[0]);
+        }
         static_for<NF - 1>([&](auto jc) __attribute__((always_inline)) {
             constexpr int j = decltype(jc)::value + 1;
-            if (j < ntl) issue(j, px[j], pq[j], pv[j], pr[j]);
+            if (j < n) issue(tb0 + j, px[j], pq[j], pv[j], pr[j]);
         });
-        if (ntl > 0) {
+        if (n > 0) {
             store(0, px[0], pq[0], pv[0], pr[0]);
-            if (NF < ntl) issue(NF, px[0], pq[0], pv[0], pr[0]);
+            if (NF < n) issue(tb0 + NF, px[0], pq[0], pv[0], pr[0]);
         }
         lds_barrier();
-        for (int base = 0; base < ntl; base += NF) {
+        for (int base = 0; base < n; base += NF) {
             static_for<NF>([&](auto jc) __attribute__((always_inline)) {
                 constexpr int j = decltype(jc)::value, slot = (j + 1) % NF;
-                const int it = base + j;
-                if (it < ntl) {
-                    const int nt = it + 1;
-                    if (nt < ntl) {
-                        store(nt, px[slot], pq[slot], pv[slot], pr[slot]);
-                        if (nt + NF < ntl) issue(nt + NF, px[slot], pq[slot], pv[slot], pr[slot]);
+                const int i = base + j;
+                if (i < n) {
+                    const int ni = i + 1;
+                    if (ni < n) {
+                        store(ni, px[slot], pq[slot], pv[slot], pr[slot]);
+                        if (ni + NF < n) issue(tb0 + ni + NF, px[slot], pq[slot], pv[slot], pr[slot]);
                     }
                     lds_barrier();
                 }
@@ -935,18 +1121,45 @@ hipError_t launch_d(const ChunkArgs& a, void* ws, hipStream_t stream) {
         e = launch_prep_w<D, DELTA>(b, ws, ntiles, stream);
         if (e != hipSuccess) return e;
     }
-    const int nvs = D / 16;
+    // inner-product rule, long chains: the first segment's group states
+    const int nseg = (!DELTA && ntiles >= kSegMinTiles) ? 2 : 1;
+    const int gmax = nseg > 1 ? seg_groups(ntiles) : 0;
+    float* part = nullptr;
+    if (nseg > 1) {
+        part = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                        window_records_bytes(b.BH, ntiles, DELTA));
+        hipLaunchKernelGGL((win_seg_kernel<D>), dim3(gmax * b.BH), dim3(4 * D), 0, stream, b,
+                           (const void*)ws, ntiles, gmax, part);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const int bh8 = (b.BH + 7) / 8 * 8;
-    hipLaunchKernelGGL((win_pass_kernel<D, DELTA>), dim3(bh8 * nvs), dim3(64 * (2 + kPassFill)), 0,
-                       stream, b, (const void*)ws, ntiles);
+    if (nseg > 1) {
+        // two segments, 32-column slices: one workgroup per compute unit at
+        // 16-column slices' grid size
+        if constexpr (!DELTA)
+            hipLaunchKernelGGL((win_pass_kernel<D, DELTA, 32>), dim3(nseg * bh8 * (D / 32)),
+                               dim3(64 * (2 * 2 + kPassFill)), 0, stream, b, (const void*)ws, ntiles, nseg,
+                               gmax, (const float*)part);
+    } else {
+        hipLaunchKernelGGL((win_pass_kernel<D, DELTA, 16>), dim3(bh8 * (D / 16)),
+                           dim3(64 * (2 + kPassFill)), 0, stream, b, (const void*)ws, ntiles, 1, 0,
+                           (const float*)nullptr);
+    }
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t window_workspace_bytes(int BH, int T, bool delta) {
-    const size_t nt = (size_t)tiles_of(T, kC);
-    return (size_t)BH * nt * (delta ? WinRec<true>::kBytes : WinRec<false>::kBytes);
+size_t window_workspace_bytes(int BH, int T, bool delta, int D) {
+    const int nt = tiles_of(T, kC);
+    size_t bytes = window_records_bytes(BH, nt, delta);
+    // the two-segment pass's group states: [BH][gmax][D][D] fp32, then [BH][gmax] fp32
+    if (!delta && nt >= kSegMinTiles) {
+        const size_t ng = (size_t)BH * seg_groups(nt);
+        bytes += (ng * D * D + ng) * 4;
+    }
+    return bytes;
 }
 
 hipError_t launch_window(const ChunkArgs& a, int D, bool delta, void* ws, hipStream_t stream) {
