@@ -209,24 +209,26 @@ def test_full_workloads_every_head(dev, name, variant):
     assert e_o <= tol and e_S <= tol, (e_o, e_S)
 
 
-@pytest.mark.parametrize("case", [(2048, 128, 4), (2049, 64, 2), (3000, 128, 3), (4100, 128, 8)],
+@pytest.mark.parametrize("case", [(2048, 128, 4), (2049, 64, 2), (3000, 128, 3), (4100, 128, 8),
+                                  (12805, 64, 4)],
                          ids=lambda c: "-".join(map(str, c)))
-def test_window_inner_product_two_segments(dev, case):
-    """Falcon-3A chains of 64 tiles (2048 steps) or more run as two segments
-    at once, the second starting from the state at the split, which is formed
-    from the first segment's groups of 32 tiles (one full group at T = 2048,
-    a ragged last group at 3000 and 4100 steps).  S0 and halos are set."""
+def test_window_inner_product_segments(dev, case):
+    """Falcon-3A chains of 64 tiles (2048 steps) or more run as up to four
+    segments at once, each starting from the state at its first tile, formed
+    from groups of 32 tiles before it: two segments at T = 2048 and 2049,
+    three at 3000 and 4100 (a ragged last segment), four at 12805.  S0 and
+    halos are set."""
     T, D, W = case
     inp = I.make_chunk_inputs(1, 2, T, D, D, dtype="bf16", seed=5100 + T + W, window=W, halo=True,
                               S0_sd=0.3)
-    check(dev, inp, "F3A", W, 64, label="two segments")
+    check(dev, inp, "F3A", W, 64, label="segments")
 
 
-def test_window_inner_product_two_segments_deterministic(dev):
-    """The split chains give the same bits on every call."""
+def test_window_inner_product_segments_deterministic(dev):
+    """The segmented chains give the same bits on every call."""
     import torch
     inp = I.make_chunk_inputs(2, 2, 4100, 128, 128, dtype="bf16", seed=5190, window=4, halo=True,
                               S0_sd=0.3)
-    o1, S1 = gpu_run(dev, inp, "F3A", 4, 64, label="two segments, call 1")
-    o2, S2 = gpu_run(dev, inp, "F3A", 4, 64, label="two segments, call 2")
+    o1, S1 = gpu_run(dev, inp, "F3A", 4, 64, label="segments, call 1")
+    o2, S2 = gpu_run(dev, inp, "F3A", 4, 64, label="segments, call 2")
     assert torch.equal(o1, o2) and torch.equal(S1, S2)

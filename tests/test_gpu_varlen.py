@@ -95,10 +95,10 @@ def test_varlen_equals_one_call_per_sequence(dev, case):
         assert torch.equal(S[n], Sn[0]), n
 
 
-def test_varlen_window_inner_product_two_segments(dev):
+def test_varlen_window_inner_product_segments(dev):
     """Falcon-3A packed calls whose longest sequence has 64 tiles or more run
-    every sequence's chain as two segments: long ones split, a one-tile and an
-    empty sequence leave the second segment empty."""
+    every sequence's chain in segments: long ones split, a one-tile and an
+    empty sequence leave the later segments empty."""
     lengths = [2100, 0, 33, 4100, 700]
     vi = I.make_varlen_inputs(lengths, 2, 128, 128, dtype="bf16", seed=990, window=4, S0_sd=0.3,
                               halo=True)

@@ -539,23 +539,30 @@ __global__ __launch_bounds__(256, W <= 6 ? 2 : 1) void win_prep_kernel(ChunkArgs
 }
 
 // ---------------------------------------------------------------------------
-// Two-segment state pass of the inner-product rule.  Its state increments do
+// Segmented state pass of the inner-product rule.  Its state increments do
 // not depend on the state, so after a run of tiles that starts from a state S
 // the state is (the product of the run's gamma_last) S plus the state the
-// same run reaches from zero.  The state pass therefore splits each chain of
-// ntl tiles at seg_split(ntl) and runs both segments at once (two workgroups
-// per compute unit fit); the second segment starts from the state at the
-// split, which win_seg_kernel forms beforehand: the first segment's tiles in
-// groups of kSegTiles, each group's state from zero (part) and the product of
-// its gamma_last (gprod), combined group by group when the second segment
-// starts.  Chains shorter than kSegMinTiles tiles (the longest of the call)
-// keep one segment.
+// same run reaches from zero.  The state pass therefore cuts each chain of
+// ntl tiles into kSegs segments of seg_len(ntl) tiles (a multiple of
+// kSegTiles) and runs them all at once; segment s starts from the state after
+// s seg_len tiles, which win_seg_kernel forms beforehand: the tiles before
+// the last segment in groups of kSegTiles, each group's state from zero
+// (part) and the product of its gamma_last (gprod), combined group by group
+// when a segment starts.  Calls whose longest chain has fewer than
+// kSegMinTiles tiles keep one segment.
 // ---------------------------------------------------------------------------
 constexpr int kSegTiles = 32;
 constexpr int kSegMinTiles = 64;
-__host__ __device__ constexpr int seg_split(int ntl) { return (ntl + 1) / 2; }
+constexpr int kSegs = 4;
+__host__ __device__ constexpr int seg_len(int ntl) {
+    return ((ntl + kSegs - 1) / kSegs + kSegTiles - 1) / kSegTiles * kSegTiles;
+}
+// tiles whose group states a chain of ntl tiles needs: those before its last segment
+__host__ __device__ constexpr int seg_prefix(int ntl) {
+    return (kSegs - 1) * seg_len(ntl) < ntl ? (kSegs - 1) * seg_len(ntl) : ntl;
+}
 __host__ __device__ constexpr int seg_groups(int ntiles) {
-    return (seg_split(ntiles) + kSegTiles - 1) / kSegTiles;
+    return (seg_prefix(ntiles) + kSegTiles - 1) / kSegTiles;
 }
 
 // One workgroup of D / 16 waves per (group g, batch*head): wave w carries
@@ -583,7 +590,7 @@ __global__ __launch_bounds__(4 * D) void win_seg_kernel(ChunkArgs a, const void*
     const int g = blockIdx.x / a.BH, bh = blockIdx.x - g * a.BH;
     const int W = a.W, NP = kC + W - 1;
     const SeqRows sr = seq_rows(a, bh);
-    const int T_ = sr.T, ntl = tiles_of(T_, kC), Lt = seg_split(ntl);
+    const int T_ = sr.T, ntl = tiles_of(T_, kC), Lt = seg_prefix(ntl);
     const int j0 = g * kSegTiles, j1 = min(j0 + kSegTiles, Lt);
     if (j0 >= j1) return;  // a group the state pass does not read
     const T* kg = static_cast<const T*>(a.k) + sr.row0 * D;
@@ -686,7 +693,7 @@ __global__ __launch_bounds__(4 * D) void win_seg_kernel(ChunkArgs a, const void*
 // chain wave hands over through LDS; the NF fill waves share the fill of
 // every tile and issue its loads NF tiles ahead.  One LDS-only barrier per
 // tile.  The delta rule runs one segment of 16-column slices; the
-// inner-product rule with long chains two segments of 32-column slices.
+// inner-product rule with long chains kSegs segments of 64-column slices.
 //
 // Key and query tiles hold rows of D elements with no padding, chunks
 // swizzled per row (swz_off).
@@ -741,10 +748,10 @@ __global__ __launch_bounds__(64 * (2 * (SW / 16) + kPassFill)) void win_pass_ker
     // this workgroup's tiles [tb0, tb1); the one that ends the chain writes
     // S_final (the delta rule always runs one segment)
     const bool first = DELTA || seg == 0;
-    const int Lt = (!DELTA && nseg > 1) ? seg_split(ntl) : ntl;
-    const int tb0 = first ? 0 : Lt, tb1 = first ? Lt : ntl;
-    if (!first && tb0 >= tb1) return;  // an empty second segment
-    const bool ends = first ? Lt == ntl : true;
+    const int L = (!DELTA && nseg > 1) ? seg_len(ntl) : ntl;
+    const int tb0 = first ? 0 : min(seg * L, ntl), tb1 = min(first ? L : seg * L + L, ntl);
+    if (!first && tb0 >= tb1) return;  // an empty segment after the chain's end
+    const bool ends = tb1 >= ntl;
     const T* qg = static_cast<const T*>(a.q) + sr.row0 * D;
     const T* kg = static_cast<const T*>(a.k) + sr.row0 * D;
     const T* vg = static_cast<const T*>(a.v) + sr.row0 * D + v0;
@@ -780,9 +787,9 @@ __global__ __launch_bounds__(64 * (2 * (SW / 16) + kPassFill)) void win_pass_ker
                             : zero4();
         if constexpr (!DELTA) {
             if (seg > 0) {
-                // the state at the split: S0 carried through the first
-                // segment's groups in order, S = gprod_g S + part_g
-                const int G = (Lt + kSegTiles - 1) / kSegTiles;
+                // the state at the segment's start: S0 carried through the
+                // groups before it in order, S = gprod_g S + part_g
+                const int G = tb0 / kSegTiles;
                 const float* pp = part + (size_t)bh * gmax * D * D + (size_t)(vc + lr) * D + 4 * grp;
                 const float* gpr = part + (size_t)a.BH * gmax * D * D + (size_t)bh * gmax;
                 for (int gg = 0; gg < G; ++gg) {
@@ -1121,8 +1128,8 @@ hipError_t launch_d(const ChunkArgs& a, void* ws, hipStream_t stream) {
         e = launch_prep_w<D, DELTA>(b, ws, ntiles, stream);
         if (e != hipSuccess) return e;
     }
-    // inner-product rule, long chains: the first segment's group states
-    const int nseg = (!DELTA && ntiles >= kSegMinTiles) ? 2 : 1;
+    // inner-product rule, long chains: the group states before the last segment
+    const int nseg = (!DELTA && ntiles >= kSegMinTiles) ? kSegs : 1;
     const int gmax = nseg > 1 ? seg_groups(ntiles) : 0;
     float* part = nullptr;
     if (nseg > 1) {
@@ -1135,11 +1142,11 @@ hipError_t launch_d(const ChunkArgs& a, void* ws, hipStream_t stream) {
     }
     const int bh8 = (b.BH + 7) / 8 * 8;
     if (nseg > 1) {
-        // two segments, 32-column slices: one workgroup per compute unit at
-        // 16-column slices' grid size
+        // kSegs segments of 64-column slices: as many workgroups as 16-column
+        // slices of one segment would be
         if constexpr (!DELTA)
-            hipLaunchKernelGGL((win_pass_kernel<D, DELTA, 32>), dim3(nseg * bh8 * (D / 32)),
-                               dim3(64 * (2 * 2 + kPassFill)), 0, stream, b, (const void*)ws, ntiles, nseg,
+            hipLaunchKernelGGL((win_pass_kernel<D, DELTA, 64>), dim3(nseg * bh8 * (D / 64)),
+                               dim3(64 * (2 * 4 + kPassFill)), 0, stream, b, (const void*)ws, ntiles, nseg,
                                gmax, (const float*)part);
     } else {
         hipLaunchKernelGGL((win_pass_kernel<D, DELTA, 16>), dim3(bh8 * (D / 16)),
