@@ -232,3 +232,21 @@ def test_window_inner_product_segments_deterministic(dev):
     o1, S1 = gpu_run(dev, inp, "F3A", 4, 64, label="segments, call 1")
     o2, S2 = gpu_run(dev, inp, "F3A", 4, 64, label="segments, call 2")
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_window_inner_product_segments_state_alias(dev):
+    """S_final may alias S0: the segmented pass's workgroups read S0 only
+    through the copy the group kernel makes before them, so an aliased call
+    gives the same bits as a separate one."""
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    inp = I.make_chunk_inputs(2, 2, 4100, 128, 128, dtype="bf16", seed=5195, window=4, halo=True,
+                              S0_sd=0.3)
+    o1, S1 = gpu_run(dev, inp, "F3A", 4, 64, label="segments, S_final separate")
+    t = inp.to_torch(dev)
+    S_alias = t["S0"].clone()
+    announce("chunk_fwd F3A bf16 B2 H2 T4100 d128 W4 chunk64 segments, S_final = S0")
+    o2, _ = fal.chunk_fwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], "F3A", window=4, chunk=64,
+                          S0=S_alias, k_prev=t["k_prev"], v_prev=t["v_prev"], S_final=S_alias)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S_alias)

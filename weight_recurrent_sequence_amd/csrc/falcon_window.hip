@@ -547,9 +547,11 @@ __global__ __launch_bounds__(256, W <= 6 ? 2 : 1) void win_prep_kernel(ChunkArgs
 // kSegTiles) and runs them all at once; segment s starts from the state after
 // s seg_len tiles, which win_seg_kernel forms beforehand: the tiles before
 // the last segment in groups of kSegTiles, each group's state from zero
-// (part) and the product of its gamma_last (gprod), combined group by group
-// when a segment starts.  Calls whose longest chain has fewer than
-// kSegMinTiles tiles keep one segment.
+// (part; group 0 from S0) and the product of its gamma_last (gprod),
+// combined group by group when a segment starts.  That kernel also keeps a
+// copy of S0 for the first segment, so the state pass never reads the
+// caller's S0, which S_final may alias.  Calls whose longest chain has fewer
+// than kSegMinTiles tiles keep one segment.
 // ---------------------------------------------------------------------------
 constexpr int kSegTiles = 32;
 constexpr int kSegMinTiles = 64;
@@ -564,6 +566,11 @@ __host__ __device__ constexpr int seg_prefix(int ntl) {
 __host__ __device__ constexpr int seg_groups(int ntiles) {
     return (seg_prefix(ntiles) + kSegTiles - 1) / kSegTiles;
 }
+// Float offset of the copy of S0 in the segment buffer: after the group
+// states and the gates' products (padded to 256 bytes).
+__host__ __device__ constexpr size_t seg_s0_offset(int BH, int gmax, int D) {
+    return (size_t)BH * gmax * D * D + ((size_t)BH * gmax + 63) / 64 * 64;
+}
 
 // One workgroup of D / 16 waves per (group g, batch*head): wave w carries
 // value columns 16 w .. 16 w + 15 of the group's state from zero, with the
@@ -571,7 +578,8 @@ __host__ __device__ constexpr int seg_groups(int ntiles) {
 // delta_p = c_p y_p; every key tile is loaded once for all columns.  Keys and
 // values are staged through registers one tile ahead (tile 0 reads the halo
 // rows, as the state pass does).
-// part: [BH][gmax][D][D] fp32 (S layout, [v][k]), then gprod [BH][gmax].
+// part: [BH][gmax][D][D] fp32 (S layout, [v][k]), then gprod [BH][gmax],
+// then the copy of S0 [BH][D][D] (group 0's workgroups write it).
 template <int D>
 __global__ __launch_bounds__(4 * D) void win_seg_kernel(ChunkArgs a, const void* ws, int ntiles, int gmax,
                                                         float* part) {
@@ -592,6 +600,13 @@ __global__ __launch_bounds__(4 * D) void win_seg_kernel(ChunkArgs a, const void*
     const SeqRows sr = seq_rows(a, bh);
     const int T_ = sr.T, ntl = tiles_of(T_, kC), Lt = seg_prefix(ntl);
     const int j0 = g * kSegTiles, j1 = min(j0 + kSegTiles, Lt);
+    const float* s0 = a.S0 ? a.S0 + (size_t)bh * D * D : nullptr;
+    if (g == 0 && s0) {
+        // the first segment's copy of S0
+        float* c = part + seg_s0_offset(a.BH, gmax, D) + (size_t)bh * D * D;
+        for (int i = tid; i < D * D / 4; i += NT)
+            reinterpret_cast<f32x4*>(c)[i] = reinterpret_cast<const f32x4*>(s0)[i];
+    }
     if (j0 >= j1) return;  // a group the state pass does not read
     const T* kg = static_cast<const T*>(a.k) + sr.row0 * D;
     const T* vg = static_cast<const T*>(a.v) + sr.row0 * D;
@@ -637,10 +652,14 @@ __global__ __launch_bounds__(4 * D) void win_seg_kernel(ChunkArgs a, const void*
         return E::load_tr(X + swz_off<D>(row0 + 4 * grp + (lr >> 2), col0 + 4 * (lr & 3)));
     };
 
-    // Sacc[kb][r] = S[v][k], v = 16 wave + lr, k = 16 kb + 4 grp + r
+    // Sacc[kb][r] = S[v][k], v = 16 wave + lr, k = 16 kb + 4 grp + r; group 0
+    // starts from S0, the others from zero
     f32x4 Sacc[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) Sacc[kb] = zero4();
+    for (int kb = 0; kb < KB; ++kb)
+        Sacc[kb] = (g == 0 && s0) ? *reinterpret_cast<const f32x4*>(s0 + (size_t)(16 * wave + lr) * D +
+                                                                     16 * kb + 4 * grp)
+                                  : zero4();
     float gp = 1.f;
     const Frag z = {0, 0, 0, 0};
     load(j0);
@@ -780,19 +799,26 @@ __global__ __launch_bounds__(64 * (2 * (SW / 16) + kPassFill)) void win_pass_ker
         // Sacc[kb][r] = S[v][k], v = vc + lr, k = 16 kb + 4 grp + r
         f32x4 Sacc[KB];
         Frag SB[KB];
+        // the state at the tile start: S0, or with segments (whose
+        // workgroups must not read S0, which S_final may alias) the copy of
+        // S0 for the first segment and, for a later one, the state after
+        // group 0 (from S0) carried through the groups before the segment in
+        // order, S = gprod_g S + part_g
+        const float* s0 = a.S0 ? a.S0 + (size_t)bh * D * D : nullptr;
+        if (!DELTA && nseg > 1 && s0)
+            s0 = part + seg_s0_offset(a.BH, gmax, D) + (size_t)bh * D * D;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-            Sacc[kb] = a.S0 ? *reinterpret_cast<const f32x4*>(
-                                  a.S0 + ((size_t)bh * D + vc + lr) * D + 16 * kb + 4 * grp)
-                            : zero4();
+            Sacc[kb] = s0 ? *reinterpret_cast<const f32x4*>(s0 + (size_t)(vc + lr) * D + 16 * kb + 4 * grp)
+                          : zero4();
         if constexpr (!DELTA) {
             if (seg > 0) {
-                // the state at the segment's start: S0 carried through the
-                // groups before it in order, S = gprod_g S + part_g
                 const int G = tb0 / kSegTiles;
                 const float* pp = part + (size_t)bh * gmax * D * D + (size_t)(vc + lr) * D + 4 * grp;
                 const float* gpr = part + (size_t)a.BH * gmax * D * D + (size_t)bh * gmax;
-                for (int gg = 0; gg < G; ++gg) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) Sacc[kb] = *reinterpret_cast<const f32x4*>(pp + 16 * kb);
+                for (int gg = 1; gg < G; ++gg) {
                     const float f = gpr[gg];
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb)
@@ -1161,10 +1187,10 @@ hipError_t launch_d(const ChunkArgs& a, void* ws, hipStream_t stream) {
 size_t window_workspace_bytes(int BH, int T, bool delta, int D) {
     const int nt = tiles_of(T, kC);
     size_t bytes = window_records_bytes(BH, nt, delta);
-    // the two-segment pass's group states: [BH][gmax][D][D] fp32, then [BH][gmax] fp32
+    // the segmented pass's group states [BH][gmax][D][D] fp32, the products
+    // of their gates [BH][gmax] fp32 and the copy of S0 [BH][D][D] fp32
     if (!delta && nt >= kSegMinTiles) {
-        const size_t ng = (size_t)BH * seg_groups(nt);
-        bytes += (ng * D * D + ng) * 4;
+        bytes += (seg_s0_offset(BH, seg_groups(nt), D) + (size_t)BH * D * D) * 4;
     }
     return bytes;
 }
