@@ -140,6 +140,24 @@ def test_poisoned_workspace(dev, case, T):
     assert torch.equal(o0, oN) and torch.equal(S0, SN)
 
 
+@pytest.mark.parametrize("with_s0", [True, False])
+def test_poisoned_workspace_segments(dev, with_s0):
+    """Falcon-3A chains of 64 tiles or more run in segments whose group
+    states and copy of S0 live in the workspace: every byte read there is
+    written first by the same call."""
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    inp = I.make_chunk_inputs(2, 2, 2100, 128, 128, dtype="bf16", seed=5390 + with_s0, window=4,
+                              halo=True, S0_sd=0.2 if with_s0 else 0.0)
+    t = inp.to_torch(dev)
+    announce(f"poisoned workspace: chunk_fwd F3A W4 bf16 d128 chunk64 T2100 segments S0={with_s0}")
+    o0, S0 = _ws_run(fal, t, "F3A", 4, 64, 0)
+    oN, SN = _ws_run(fal, t, "F3A", 4, 64, 0xFF)
+    torch.cuda.synchronize()
+    assert torch.isfinite(oN.float()).all() and torch.isfinite(SN).all()
+    assert torch.equal(o0, oN) and torch.equal(S0, SN)
+
+
 @pytest.mark.parametrize("phi", ["l2", "silu"])
 @pytest.mark.parametrize("align", ["prefix", "same"])
 def test_poisoned_workspace_feature_map(dev, phi, align):
