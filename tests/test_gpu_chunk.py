@@ -224,6 +224,16 @@ def test_window_inner_product_segments(dev, case):
     check(dev, inp, "F3A", W, 64, label="segments")
 
 
+@pytest.mark.parametrize("case", [(4100, 128, 4), (2049, 64, 3)], ids=lambda c: "-".join(map(str, c)))
+def test_window_inner_product_segments_same_step(dev, case):
+    """Same-step pairs (k_t, v_t) through the segmented pass: the group
+    kernel and the segments read each pair's key at the same lag."""
+    T, D, W = case
+    inp = I.make_chunk_inputs(1, 2, T, D, D, dtype="bf16", seed=5150 + T + W, window=W, halo=True,
+                              S0_sd=0.3)
+    check(dev, inp, "F3A", W, 64, label="segments", align="same")
+
+
 def test_window_inner_product_segments_deterministic(dev):
     """The segmented chains give the same bits on every call."""
     import torch
