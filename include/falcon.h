@@ -282,7 +282,11 @@ int falcon_chunk_bwd_varlen(const void* q, const void* k, const void* v, const f
  * falcon_chunk_fwd_save: as falcon_chunk_fwd (same arguments and outputs),
  *   and it also leaves in `saved` the records and checkpoints the backward
  *   reads.  saved: falcon_chunk_bwd_workspace(...) bytes of device memory
- *   owned by the caller.  Support matrix as for falcon_chunk_bwd.
+ *   owned by the caller.  Support matrix as for falcon_chunk_bwd.  When
+ *   S_final aliases S0 and falcon_chunk_fwd would run other kernels than the
+ *   checkpoint run (window rules with W >= 2, Falcon-1A), S_final comes from
+ *   the checkpoint run's kernels: the same recurrence, equal up to rounding
+ *   (o is still falcon_chunk_fwd's, bit for bit).
  * falcon_chunk_bwd_saved: as falcon_chunk_bwd (same arguments and outputs),
  *   reading `saved` as a falcon_chunk_fwd_save call on the same inputs and
  *   sizes left it instead of re-running the forward (it also writes its own

@@ -156,3 +156,42 @@ def test_saved_pair_no_steps(dev, case):
     for k in GRADS:
         same(g_s[k], g_r[k], k)
     assert torch.equal(g_s["dS0"], dS)
+
+
+@pytest.mark.parametrize("case", [("F1A", 128, 1), ("F3A", 128, 4), ("F3", 64, 3), ("F1", 128, 1)],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_saved_pair_with_aliased_state(dev, case):
+    """S_final aliasing S0 in the saving forward: o is still falcon_chunk_fwd's,
+    the checkpoints come from the unmodified S0 (the backward from them equals
+    the recomputing backward bitwise), and S_final is the recurrence's final
+    state (for the rules whose forward runs other kernels, from the
+    checkpoint run's split kernels: equal up to rounding)."""
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    variant, D, W = case
+    B, H, T = 2, 3, 150
+    inp = I.make_chunk_inputs(B, H, T, D, D, dtype="bf16", seed=1780 + D + W, window=W, S0_sd=0.3,
+                              halo=True)
+    t = inp.to_torch(dev)
+    kw = dict(window=W, k_prev=t["k_prev"], v_prev=t["v_prev"])
+    n = fal.bwd_workspace_bytes(B, H, T, D, D, fal.BF16, variant, W, 64)
+    saved = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    S_alias = t["S0"].clone()
+    announce(f"chunk_fwd_save {variant} d{D} W{W} T{T} S_final = S0")
+    o_s, _ = fal.chunk_fwd_save(t["q"], t["k"], t["v"], t["alpha"], t["eta"], variant, saved=saved,
+                                S0=S_alias, S_final=S_alias, **kw)
+    o_r, S_r = fal.chunk_fwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], variant, S0=t["S0"], **kw)
+    torch.cuda.synchronize()
+    same(o_s, o_r, "o")
+    err = ((S_alias - S_r).abs().amax(dim=(2, 3)) / S_r.abs().amax(dim=(2, 3))).max().item()
+    assert err <= 1e-2, err
+    d_o, dS = I.make_cotangents(B, H, T, D, D, seed=1790)
+    d_o, dS = to_dev(d_o, dev), to_dev(dS, dev)
+    announce(f"chunk_bwd_saved {variant} d{D} W{W} T{T} after an aliased save")
+    g_s = fal.chunk_bwd_saved(t["q"], t["k"], t["v"], t["alpha"], t["eta"], d_o, variant, saved=saved,
+                              S0=t["S0"], dS_final=dS, want_dk_prev=True, **kw)
+    g_r = fal.chunk_bwd(t["q"], t["k"], t["v"], t["alpha"], t["eta"], d_o, variant, S0=t["S0"],
+                        dS_final=dS, want_dk_prev=True, **kw)
+    torch.cuda.synchronize()
+    for k in GRADS:
+        same(g_s.get(k), g_r.get(k), k)

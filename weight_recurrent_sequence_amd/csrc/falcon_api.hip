@@ -426,12 +426,17 @@ int chunk_bwd_run(const void* q, const void* k, const void* v, const float* alph
         // the fused scalar-rule kernel): o and S_final from them (so they
         // equal falcon_chunk_fwd's bit for bit), then the checkpoints from a
         // run of the split kernels without outputs
+        // With S_final aliasing S0 that first run must leave S0 alone: the
+        // checkpoint run still reads it, and writes S_final itself (each of
+        // its workgroups reads its slice of S0 before writing it).
         falcon::ChunkArgs f = a;
         f.ck_s = f.ck_d = nullptr;
+        const bool alias = S_final && static_cast<const void*>(S_final) == static_cast<const void*>(S0);
+        if (alias) f.S_final = nullptr;
         hipError_t e = falcon::launch_chunk(f, dt, dk_, chunk, is_delta(base), workspace, stream);
         if (e != hipSuccess) return FALCON_ERR_HIP;
         a.o = nullptr;
-        a.S_final = nullptr;
+        if (!alias) a.S_final = nullptr;
     }
     if (mode != kFromSaved && (T > 0 || a.S_final)) {
         hipError_t e = falcon::launch_chunk(a, dt, dk_, chunk, is_delta(base), workspace, stream);
