@@ -103,7 +103,10 @@ typedef enum { FALCON_FP32 = 0, FALCON_BF16 = 1 } falcon_dtype;
 
 /*
  * Workspace bytes falcon_chunk_fwd needs for these arguments (0 when none).
- * Returns 0 as well for arguments falcon_chunk_fwd would reject.
+ * Returns 0 as well for arguments falcon_chunk_fwd would reject.  The size
+ * follows the kernels the forward runs (for the window rules at bf16 without
+ * a feature map, the collapsed form's records); the backward and the saving
+ * forward have their own queries.
  */
 size_t falcon_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, falcon_dtype dt,
                                   falcon_variant var, int window, int chunk);

@@ -212,14 +212,37 @@ def test_varlen_workspace_matches_batched_layout(L):
 
 def test_feature_map_workspace_holds_the_mapped_inputs(L):
     """With a feature map the workspace also holds the mapped keys and queries
-    (B*H*T*dk entries each, 256-byte aligned) and the mapped halo keys."""
-    B, H, T, d, W = 2, 3, 1000, 128, 4
-    base = L.falcon_chunk_fwd_workspace(B, H, T, d, d, 1, 3, W, 64)
+    (B*H*T*dk entries each, 256-byte aligned) and the mapped halo keys.  The
+    scalar rule's records are the same with and without a map; the window
+    rules with a map run the split kernels, whose records are at least the
+    collapsed form's that the call without a map sizes."""
+    B, H, T, d = 2, 3, 1000, 128
     es = 2
     al = lambda n: (n + 255) // 256 * 256  # noqa: E731
-    for flag in (0x200, 0x400, 0x200 | 0x100):
-        got = L.falcon_chunk_fwd_workspace(B, H, T, d, d, 1, 3 | flag, W, 64)
-        assert got == al(base) + 2 * al(B * H * T * d * es) + al(B * H * W * d * es)
+    for var, W in ((1, 1), (3, 4), (13, 3)):
+        base = L.falcon_chunk_fwd_workspace(B, H, T, d, d, 1, var, W, 64)
+        sizes = set()
+        for flag in (0x200, 0x400, 0x200 | 0x100):
+            got = L.falcon_chunk_fwd_workspace(B, H, T, d, d, 1, var | flag, W, 64)
+            rec = got - 2 * al(B * H * T * d * es) - al(B * H * W * d * es)
+            assert rec % 256 == 0 and rec >= base, (var, flag)
+            if W == 1:
+                assert rec == al(base)
+            sizes.add(got)
+        assert len(sizes) == 1  # the map and the alignment do not change the size
+
+
+def test_window_forward_workspace_is_the_collapsed_forms(L):
+    """The window rules at bf16 without a feature map size the forward's
+    workspace by the collapsed form's records (and the segmented pass's group
+    states), not by the split kernels' records that the backward's checkpoint
+    runs need (its workspace query includes those)."""
+    for var in (3, 13):
+        fwd = L.falcon_chunk_fwd_workspace(2, 16, 32768, 128, 128, 1, var, 4, 64)
+        fp32 = L.falcon_chunk_fwd_workspace(2, 16, 32768, 128, 128, 0, var, 4, 64)
+        mapped = L.falcon_chunk_fwd_workspace(2, 16, 32768, 128, 128, 1, var | 0x200, 4, 64)
+        bwd = L.falcon_chunk_bwd_workspace(2, 16, 32768, 128, 128, 1, var, 4, 64)
+        assert 0 < fwd < fp32 and fwd < mapped and fwd < bwd, var
 
 
 def bwd(L, fn="falcon_chunk_bwd", **kw):
@@ -291,9 +314,14 @@ def test_bwd_workspace_sizes(L):
         nt = (T + 63) // 64
         want = al(fwd) + 2 * al(B * H * nt * d * d * 2) + al(B * H * nt * d * 64 * 2)
         assert L.falcon_chunk_bwd_workspace(B, H, T, d, d, 1, var, 1, 64) == want
-    # windows: tiles of 64 // W steps, and room for the per-row target and key gradients
+    # windows: tiles of 64 // W steps, and room for the per-row target and key
+    # gradients; the forward part is the split kernels' records (those of a
+    # call with a feature map, less the mapped inputs), which the checkpoint
+    # runs use, not the collapsed form's that the forward alone sizes
     B, H, T, d, W = 2, 3, 1000, 128, 4
-    fwd = L.falcon_chunk_fwd_workspace(B, H, T, d, d, 1, 3, W, 64)
+    fwd = (L.falcon_chunk_fwd_workspace(B, H, T, d, d, 1, 3 | 0x200, W, 64)
+           - 2 * al(B * H * T * d * 2) - al(B * H * W * d * 2))
+    assert fwd > L.falcon_chunk_fwd_workspace(B, H, T, d, d, 1, 3, W, 64)
     nt = (T + 64 // W - 1) // (64 // W)
     want = al(fwd) + 2 * al(B * H * nt * d * d * 2) + 3 * al(B * H * nt * d * 64 * 2)
     assert L.falcon_chunk_bwd_workspace(B, H, T, d, d, 1, 3, W, 64) == want
@@ -309,6 +337,10 @@ def test_bwd_varlen_workspace(L):
     for var, W in ((1, 1), (13, 4), (2 | 0x200, 1)):
         N, H, mx, d = 5, 3, 300, 128
         fwd = L.falcon_chunk_fwd_varlen_workspace(N, H, mx, d, d, 1, var, W, 64)
+        if W > 1:
+            # the split kernels' records, as in test_bwd_workspace_sizes
+            fwd = (L.falcon_chunk_fwd_varlen_workspace(N, H, mx, d, d, 1, var | 0x200, W, 64)
+                   - 2 * al(N * H * mx * d * 2) - al(N * H * W * d * 2))
         nt = (mx + 64 // W - 1) // (64 // W)
         want = al(fwd) + 2 * al(N * H * nt * d * d * 2) + al(N * H * nt * d * 64 * 2)
         if W > 1:

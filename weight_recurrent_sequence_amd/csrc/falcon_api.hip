@@ -109,12 +109,12 @@ int check_chunk(const void* q, const void* k, const void* v, const float* alpha,
     return FALCON_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t falcon_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, falcon_dtype dt,
-                                  falcon_variant var, int window, int chunk) {
+// Workspace of a forward call.  full: room for the split kernels' records as
+// well (the backward's checkpoint runs and the saving forward run them for
+// every rule); otherwise the window rules at bf16 without a feature map get
+// their collapsed form's bytes only, the kernels falcon_chunk_fwd runs.
+size_t fwd_ws(int B, int H, int T, int dk, int dv, falcon_dtype dt, falcon_variant var, int window,
+              int chunk, bool full) {
     // Sizes only: pointers are not needed to size the workspace.
     const void* p = reinterpret_cast<const void*>(uintptr_t(256));
     if (check_chunk(p, p, p, (const float*)p, (const float*)p, nullptr, nullptr, nullptr, p,
@@ -122,10 +122,37 @@ size_t falcon_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, falcon_dt
         return 0;
     int base = 0, lag = 1, phi = 0;
     split_variant(var, &base, &lag, &phi);
-    const size_t rec = align256(falcon::chunk_workspace_bytes(B * H, T, (int)dt, chunk, window,
-                                                              norm_of(base), is_delta(base), dk));
+    // the window rules at bf16 without a feature map run their collapsed
+    // form: its records (and group states) only; everything else the split
+    // kernels' records
+    const bool collapsed = !full && dt == FALCON_BF16 && norm_of(base) == falcon::kNormWindow && window >= 2 && phi == 0;
+    const size_t rec = align256(collapsed ? falcon::window_workspace_bytes(B * H, T, is_delta(base), dk)
+                                          : falcon::chunk_workspace_bytes(B * H, T, (int)dt, chunk, window,
+                                                                          norm_of(base), is_delta(base), dk));
     if (rec == 0 || phi == 0) return rec;
     return rec + phi_bytes((size_t)B * H * T, (size_t)B * H, window, dk, dt);
+}
+
+size_t fwd_varlen_ws(int N, int H, int max_seqlen, int dk, int dv, falcon_dtype dt,
+                     falcon_variant var, int window, int chunk, bool full) {
+    // the records, laid out per (sequence, head) with the longest sequence's
+    // tile count, then the schedule: 2N+1 ints (the sequences' order, the
+    // prefix sums of their tile counts) and, 256-byte aligned, a job table of
+    // 4 ints per record slot
+    const size_t rec = fwd_ws(N, H, max_seqlen, dk, dv, dt, var, window, chunk, full);
+    if (rec == 0) return 0;
+    const int Wv = (var & 0xFF) == FALCON_F3 || (var & 0xFF) == FALCON_F3A ? window : 1;
+    const size_t slots = (size_t)N * H * ((max_seqlen + chunk / Wv - 1) / (chunk / Wv));
+    return rec + ((2 * (size_t)N + 1) * sizeof(int) + 255) / 256 * 256 + slots * 4 * sizeof(int);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t falcon_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, falcon_dtype dt,
+                                  falcon_variant var, int window, int chunk) {
+    return fwd_ws(B, H, T, dk, dv, dt, var, window, chunk, false);
 }
 
 // Where the mapped keys, queries and halo keys go (after the records).
@@ -190,15 +217,7 @@ int falcon_chunk_fwd(const void* q, const void* k, const void* v, const float* a
 size_t falcon_chunk_fwd_varlen_workspace(int N, int H, int max_seqlen, int dk, int dv,
                                          falcon_dtype dt, falcon_variant var, int window,
                                          int chunk) {
-    // the records, laid out per (sequence, head) with the longest sequence's
-    // tile count, then the schedule: 2N+1 ints (the sequences' order, the
-    // prefix sums of their tile counts) and, 256-byte aligned, a job table of
-    // 4 ints per record slot
-    const size_t rec = falcon_chunk_fwd_workspace(N, H, max_seqlen, dk, dv, dt, var, window, chunk);
-    if (rec == 0) return 0;
-    const int Wv = (var & 0xFF) == FALCON_F3 || (var & 0xFF) == FALCON_F3A ? window : 1;
-    const size_t slots = (size_t)N * H * ((max_seqlen + chunk / Wv - 1) / (chunk / Wv));
-    return rec + ((2 * (size_t)N + 1) * sizeof(int) + 255) / 256 * 256 + slots * 4 * sizeof(int);
+    return fwd_varlen_ws(N, H, max_seqlen, dk, dv, dt, var, window, chunk, false);
 }
 
 int falcon_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* alpha,
@@ -333,7 +352,7 @@ int falcon_decode_step_window(float* S, void* k_cache, void* v_cache, const void
 
 size_t falcon_chunk_bwd_workspace(int B, int H, int T, int dk, int dv, falcon_dtype dt,
                                   falcon_variant var, int window, int chunk) {
-    const size_t fwd = falcon_chunk_fwd_workspace(B, H, T, dk, dv, dt, var, window, chunk);
+    const size_t fwd = fwd_ws(B, H, T, dk, dv, dt, var, window, chunk, true);
     if (fwd == 0) return 0;
     int base = 0, lag = 1, phi = 0;
     split_variant(var, &base, &lag, &phi);
@@ -520,7 +539,7 @@ int falcon_chunk_bwd(const void* q, const void* k, const void* v, const float* a
     int base = 0, lag = 1, phi = 0;
     split_variant(var, &base, &lag, &phi);
     const int BH = B * H;
-    const size_t fwd = falcon_chunk_fwd_workspace(B, H, T, dk_, dv_, dt, var, window, chunk);
+    const size_t fwd = fwd_ws(B, H, T, dk_, dv_, dt, var, window, chunk, true);
     const size_t rec = align256(falcon::chunk_workspace_bytes(BH, T, (int)dt, chunk, window,
                                                               norm_of(base), is_delta(base), dk_));
     return chunk_bwd_run(q, k, v, alpha, eta, S0, k_prev, v_prev, d_o, dS_final, dq, dk, dv, dalpha,
@@ -531,7 +550,7 @@ int falcon_chunk_bwd(const void* q, const void* k, const void* v, const float* a
 size_t falcon_chunk_bwd_varlen_workspace(int N, int H, int max_seqlen, int dk, int dv,
                                          falcon_dtype dt, falcon_variant var, int window,
                                          int chunk) {
-    const size_t fwd = falcon_chunk_fwd_varlen_workspace(N, H, max_seqlen, dk, dv, dt, var, window, chunk);
+    const size_t fwd = fwd_varlen_ws(N, H, max_seqlen, dk, dv, dt, var, window, chunk, true);
     if (fwd == 0) return 0;
     int base = 0, lag = 1, phi = 0;
     split_variant(var, &base, &lag, &phi);
@@ -566,13 +585,13 @@ int falcon_chunk_bwd_varlen(const void* q, const void* k, const void* v, const f
     int base = 0, lag = 1, phi = 0;
     split_variant(var, &base, &lag, &phi);
     const int T = any ? max_seqlen : 0;
-    const size_t fwd = falcon_chunk_fwd_varlen_workspace(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk);
+    const size_t fwd = fwd_varlen_ws(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk, true);
     const size_t rec = align256(falcon::chunk_workspace_bytes(N * H, max_seqlen, (int)dt, chunk, window,
                                                               norm_of(base), is_delta(base), dk_));
     return chunk_bwd_run(q, k, v, alpha, eta, S0, k_prev, v_prev, d_o, dS_final, dq, dk, dv, dalpha,
                          deta, dS0, dk_prev, dv_prev, cu_seqlens, N * H, H, total_T, T, dk_, (int)dt,
                          var, window, chunk, eps, workspace, fwd, rec, (size_t)N * H * max_seqlen,
-                         falcon_chunk_fwd_workspace(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk),
+                         fwd_ws(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk, true),
                          stream);
 }
 
@@ -592,7 +611,7 @@ int falcon_chunk_fwd_save(const void* q, const void* k, const void* v, const flo
     if (need > 0 && (saved == nullptr || saved_bytes < need)) return FALCON_ERR_WORKSPACE;
     if (T == 0 && S_final == nullptr) return FALCON_OK;
     const int BH = B * H;
-    const size_t fwd = falcon_chunk_fwd_workspace(B, H, T, dk_, dv_, dt, var, window, chunk);
+    const size_t fwd = fwd_ws(B, H, T, dk_, dv_, dt, var, window, chunk, true);
     const size_t rec = align256(falcon::chunk_workspace_bytes(BH, T, (int)dt, chunk, window,
                                                               norm_of(base), is_delta(base), dk_));
     return chunk_bwd_run(q, k, v, alpha, eta, S0, k_prev, v_prev, nullptr, nullptr, nullptr, nullptr,
@@ -620,7 +639,7 @@ int falcon_chunk_bwd_saved(const void* q, const void* k, const void* v, const fl
     int base = 0, lag = 1, phi = 0;
     split_variant(var, &base, &lag, &phi);
     const int BH = B * H;
-    const size_t fwd = falcon_chunk_fwd_workspace(B, H, T, dk_, dv_, dt, var, window, chunk);
+    const size_t fwd = fwd_ws(B, H, T, dk_, dv_, dt, var, window, chunk, true);
     const size_t rec = align256(falcon::chunk_workspace_bytes(BH, T, (int)dt, chunk, window,
                                                               norm_of(base), is_delta(base), dk_));
     return chunk_bwd_run(q, k, v, alpha, eta, S0, k_prev, v_prev, d_o, dS_final, dq, dk, dv, dalpha,
@@ -652,14 +671,14 @@ int falcon_chunk_fwd_varlen_save(const void* q, const void* k, const void* v, co
     if (need > 0 && (saved == nullptr || saved_bytes < need)) return FALCON_ERR_WORKSPACE;
     if (!any && S_final == nullptr) return FALCON_OK;
     const int T = any ? max_seqlen : 0;
-    const size_t fwd = falcon_chunk_fwd_varlen_workspace(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk);
+    const size_t fwd = fwd_varlen_ws(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk, true);
     const size_t rec = align256(falcon::chunk_workspace_bytes(N * H, max_seqlen, (int)dt, chunk, window,
                                                               norm_of(base), is_delta(base), dk_));
     return chunk_bwd_run(q, k, v, alpha, eta, S0, k_prev, v_prev, nullptr, nullptr, nullptr, nullptr,
                          nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, cu_seqlens, N * H, H,
                          total_T, T, dk_, (int)dt, var, window, chunk, eps, saved, fwd, rec,
                          (size_t)N * H * max_seqlen,
-                         falcon_chunk_fwd_workspace(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk),
+                         fwd_ws(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk, true),
                          stream, kSaveOnly, o, S_final);
 }
 
@@ -689,13 +708,13 @@ int falcon_chunk_bwd_varlen_saved(const void* q, const void* k, const void* v, c
     int base = 0, lag = 1, phi = 0;
     split_variant(var, &base, &lag, &phi);
     const int T = any ? max_seqlen : 0;
-    const size_t fwd = falcon_chunk_fwd_varlen_workspace(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk);
+    const size_t fwd = fwd_varlen_ws(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk, true);
     const size_t rec = align256(falcon::chunk_workspace_bytes(N * H, max_seqlen, (int)dt, chunk, window,
                                                               norm_of(base), is_delta(base), dk_));
     return chunk_bwd_run(q, k, v, alpha, eta, S0, k_prev, v_prev, d_o, dS_final, dq, dk, dv, dalpha,
                          deta, dS0, dk_prev, dv_prev, cu_seqlens, N * H, H, total_T, T, dk_, (int)dt,
                          var, window, chunk, eps, saved, fwd, rec, (size_t)N * H * max_seqlen,
-                         falcon_chunk_fwd_workspace(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk),
+                         fwd_ws(N, H, max_seqlen, dk_, dv_, dt, var, window, chunk, true),
                          stream, kFromSaved);
 }
 
