@@ -29,7 +29,10 @@ steps (ms_per_step, which `value` uses) and the median and minimum per call.
 Before the first timed region, untimed Falcon-1 calls run for 0.3 s so the
 device's clocks reach their sustained state (a fresh process otherwise times
 its first ~100 calls up to 10% slow); every region then does its own
---warmup steps.
+--warmup steps.  The decode lines time the 1024 steps captured once as a HIP
+graph (one launch per replay, as a serving loop would run them), after
+checking that a replay leaves the eager steps' state bit for bit, and give
+the eager loop's time (one launch per step) beside it.
 
 roofline.achieved is the algorithmic HBM bytes of one call (q, k, v, o once,
 alpha, eta, final state) over the call's mean HIP-event time; roofline.traffic
@@ -524,22 +527,63 @@ def main():
                 fal.decode_step(S, kc, x["q"][s], x["k"][s], x["v"][s], x["alpha"][s],
                                 x["eta"][s], variant, o=od)
 
-        log(f"decode {variant} window {Wd}, {steps} steps")
-        reps = []
-        for rep in range(3):
+        def reset():
             S.copy_(x["S0"])
             kc.copy_(x["k_cache0"])
             if vc is not None:
                 vc.copy_(x["v_cache0"])
             counter[0] = 0
             torch.cuda.synchronize()
-            reps.append(timed(dec, steps, 0)["mean"])
+
+        log(f"decode {variant} window {Wd}, {steps} steps")
+        eager = []
+        for rep in range(3):
+            reset()
+            eager.append(timed(dec, steps, 0)["mean"])
+        eager.sort()
+        S_eager = S.clone()
+        # The same steps captured once as a HIP graph (a serving loop would
+        # launch them so): one launch per replay instead of one per step.
+        # Each replay starts from the initial state; the first must leave
+        # the state the eager run left, bit for bit, or the eager times stand.
+        reps, graph_ok = [], False
+        try:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                reset()
+                for _ in range(2):
+                    dec()
+            torch.cuda.current_stream().wait_stream(side)
+            reset()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(steps):
+                    dec()
+            for rep in range(3):
+                reset()
+                st = torch.cuda.current_stream()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                g.replay()
+                e1.record(st)
+                torch.cuda.synchronize()
+                reps.append(e0.elapsed_time(e1) / steps)
+                if rep == 0:
+                    graph_ok = bool(torch.equal(S, S_eager))
+            del g
+        except RuntimeError as ex:  # capture not available: keep the eager times
+            log(f"decode graph capture failed: {ex}")
+        if not graph_ok:
+            reps = eager
         reps.sort()
         db = decode_window_bytes(N, Hd, Dd, Wd) if Wd > 1 else decode_bytes(N, Hd, Dd)
         med, best = reps[1], reps[0]
         dgbs = db / (med / 1e3) / 1e9
         r = {"workload": wn, "tokens_per_s": N / (med / 1e3), "ms_per_step": med,
              "ms_per_step_min": best, "repeats_ms_per_step": reps,
+             "timing": "hip graph of the steps" if graph_ok else "one launch per step",
+             "ms_per_step_eager": eager[1], "repeats_ms_per_step_eager": eager,
              "steps": steps, "roofline": {
                  "bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                  "frac": dgbs / HBM_PEAK_GBS,

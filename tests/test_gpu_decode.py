@@ -247,3 +247,66 @@ def test_same_step_decode_window(dev, variant, W, D):
     np.testing.assert_array_equal(to_np(kc), kc_o)
     if W > 1:
         np.testing.assert_array_equal(to_np(vc), vc_o)
+
+
+@pytest.mark.parametrize("W", [1, 4])
+def test_decode_steps_replayed_from_a_graph(dev, W):
+    """The decode steps captured once as a HIP graph (as bench.py times them):
+    three replays, each from the initial state with eager steps run between
+    them, leave the state, caches and last output the eager steps leave, bit
+    for bit."""
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    N, H, D, steps = 4, 3, 128, 16
+    variant = "F3" if W > 1 else "F1"
+    x = I.make_decode_inputs_torch(N, H, D, D, steps, device=dev, seed=690 + W, window=W)
+    S = x["S0"].clone()
+    kc = x["k_cache0"].clone()
+    vc = x["v_cache0"].clone() if W > 1 else None
+    o = torch.empty((N, H, D), dtype=torch.bfloat16, device=dev)
+
+    def step(s):
+        if W > 1:
+            fal.decode_step_window(S, kc, vc, x["q"][s], x["k"][s], x["v"][s], x["alpha"][s],
+                                   x["eta"][s], variant, o=o)
+        else:
+            fal.decode_step(S, kc, x["q"][s], x["k"][s], x["v"][s], x["alpha"][s], x["eta"][s],
+                            variant, o=o)
+
+    def reset():
+        S.copy_(x["S0"])
+        kc.copy_(x["k_cache0"])
+        if vc is not None:
+            vc.copy_(x["v_cache0"])
+        torch.cuda.synchronize()
+
+    announce(f"decode {variant} W{W} N{N} H{H} d{D}: {steps} eager steps")
+    reset()
+    for s in range(steps):
+        step(s)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (S, kc, o) + ((vc,) if vc is not None else ())]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        reset()
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    reset()
+    announce(f"decode {variant} W{W}: capturing {steps} steps")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for s in range(steps):
+            step(s)
+    for rep in range(3):
+        reset()
+        announce(f"decode {variant} W{W}: graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in (S, kc, o) + ((vc,) if vc is not None else ())]
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), rep
+        # eager work between the replays
+        reset()
+        step(0)
+        torch.cuda.synchronize()
