@@ -53,6 +53,22 @@ def test_noalloc_equals_workspace_call_twice(dev, case):
         assert torch.equal(o_n, o_w) and torch.equal(S_n, S_w), (T, B, H)
 
 
+def test_noalloc_segmented_window_pass(dev):
+    """Falcon-3A chains of 64 tiles or more run in segments whose group states
+    and copy of S0 live in the scratch buffer: two such calls in a row, the
+    second smaller, equal the workspace calls bit for bit."""
+    import torch
+    import weight_recurrent_sequence_amd as fal
+    for T, B, H in ((2100, 2, 3), (2050, 1, 2)):
+        inp = I.make_chunk_inputs(B, H, T, 128, 128, dtype="bf16", seed=7750 + T, window=4,
+                                  halo=True, S0_sd=0.2)
+        t = inp.to_torch(dev)
+        announce(f"chunk_fwd_noalloc F3A W4 bf16 d128 chunk64 B{B} H{H} T{T} (segments)")
+        (o_n, S_n), (o_w, S_w) = both(fal, t, "F3A", 4, 64)
+        assert torch.isfinite(o_n.float()).all()
+        assert torch.equal(o_n, o_w) and torch.equal(S_n, S_w), (T, B, H)
+
+
 def test_noalloc_feature_map_and_same_step(dev):
     import torch
     import weight_recurrent_sequence_amd as fal
