@@ -572,7 +572,7 @@ def main():
                 if rep == 0:
                     graph_ok = bool(torch.equal(S, S_eager))
             del g
-        except RuntimeError as ex:  # capture not available: keep the eager times
+        except Exception as ex:  # capture not available: keep the eager times
             log(f"decode graph capture failed: {ex}")
         if not graph_ok:
             reps = eager
