@@ -26,10 +26,12 @@ the Falcon-1 workload.
 Timing: each timed region records a HIP event on the launch stream before
 the first step and after every step, so the line gives the mean over the K
 steps (ms_per_step, which `value` uses) and the median and minimum per call.
-Before the first timed region, untimed Falcon-1 calls run for 0.3 s so the
-device's clocks reach their sustained state (a fresh process otherwise times
-its first ~100 calls up to 10% slow); every region then does its own
---warmup steps.  The decode lines time the 1024 steps captured once as a HIP
+Every timed region starts with untimed calls of its own step, back to back
+for at least 0.3 s and at least --warmup of them, so the device's clocks are
+at their sustained state when the timed steps begin: a fresh process times
+its first ~100 calls up to 10% slow, and after the host has checked the
+previous region's errors (the device idle for a second or more) a region
+with only a few warm-up calls ran up to 20% slow.  The decode lines time the 1024 steps captured once as a HIP
 graph (one launch per replay, as a serving loop would run them), after
 checking that a replay leaves the eager steps' state bit for bit, and give
 the eager loop's time (one launch per step) beside it.
@@ -58,7 +60,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "Falcon-1 chunk fwd tokens/s (B8 H16 T4096 d128) + decode tok/s; % roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
-SETTLE_S = 0.3               # untimed calls before the first timed region
+SETTLE_S = 0.3               # untimed back-to-back calls before every timed region
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 SECTIONS = ("f1", "f1a", "f1_same", "f1_l2", "f1_varlen", "bwd", "f2", "f3", "decode", "decode3")
 
@@ -140,14 +142,31 @@ def measured_traffic(entry):
         return None
 
 
-def timed(fn, steps, warmup):
+def settle(fn, seconds, min_calls=0):
+    """Untimed calls of fn, back to back, for at least `seconds` and at least
+    `min_calls` calls; returns their number.  The device lowers its clocks
+    while it idles (the host checking a region's errors against the oracle,
+    for one) and takes a few hundred milliseconds under load to bring them
+    back, so a few warm-up calls alone leave the next region's timed calls
+    up to 20% slow.  Synchronizes every four calls, so the queue stays short."""
+    import torch
+    t_end = time.perf_counter() + seconds
+    n = 0
+    while n < min_calls or time.perf_counter() < t_end:
+        for _ in range(4):
+            fn()
+        n += 4
+        torch.cuda.synchronize()
+    return n
+
+
+def timed(fn, steps, warmup, settle_s=SETTLE_S):
     """Mean, median and minimum milliseconds per call of `steps` calls, from
     HIP events on the current stream (one before the first call, one after
-    each); synchronized before and after."""
+    each); synchronized before and after.  Before them, untimed calls for at
+    least `settle_s` seconds and at least `warmup` calls."""
     import torch
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
+    settle(fn, settle_s, warmup)
     st = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
@@ -292,17 +311,11 @@ def main():
                                      chunk=C, o=o, S_final=S_fin, **kw)
 
     # Clocks settle: in a fresh process the first ~100 calls run up to 10%
-    # slower while the device ramps to its sustained state, so untimed calls
-    # run for at least SETTLE_S before the first warm-up of the first timed
-    # region (each region then does its own `--warmup` steps).
+    # slower while the device ramps to its sustained state, and after an
+    # idle gap it ramps again, so every timed region starts with untimed
+    # calls of its own for at least SETTLE_S (and at least `--warmup`).
     step_f1 = fwd("F1", workspace=ws)
-    t_end = time.perf_counter() + SETTLE_S
-    n_settle = 0
-    while time.perf_counter() < t_end or n_settle < 20:
-        for _ in range(10):
-            step_f1()
-        torch.cuda.synchronize()
-        n_settle += 10
+    n_settle = settle(step_f1, SETTLE_S, 20)
     log(f"settle {n_settle} Falcon-1 calls, warmup {args.warmup}, steps {args.steps}")
 
     def rate(tm, nb, tokens):
@@ -536,10 +549,11 @@ def main():
             torch.cuda.synchronize()
 
         log(f"decode {variant} window {Wd}, {steps} steps")
+        settle(dec, SETTLE_S)
         eager = []
         for rep in range(3):
             reset()
-            eager.append(timed(dec, steps, 0)["mean"])
+            eager.append(timed(dec, steps, 0, settle_s=0.0)["mean"])
         eager.sort()
         S_eager = S.clone()
         # The same steps captured once as a HIP graph (a serving loop would
