@@ -498,7 +498,8 @@ def main():
             r.update({"workload": wname, "algorithmic_bytes_per_call": nb,
                       "kernels": (("win_prep_kernel + win_pass_kernel" if delta else
                                    "win_prep_kernel + win_seg_kernel + win_pass_kernel (4 segments)")
-                                  if Wx > 1 else "chunk_prep2_kernel + chunk_pass_kernel"),
+                                  if Wx > 1 else ("chunk_prep2_kernel + chunk_pass_kernel" if delta
+                                                  else "fused_kernel<128, per-column write vectors>")),
                       "traffic": measured_traffic(f"chunk_fwd_{tag}_B{Bx}H{Hx}T{Tx}d{Dx}_bf16_c64"),
                       "mfma_tflops": tfx, "mfma_frac_bf16": tfx / BF16_PEAK_TFLOPS,
                       "algorithmic_flops_per_call": fl})

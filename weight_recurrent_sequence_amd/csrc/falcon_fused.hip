@@ -1,13 +1,15 @@
-// falcon_fused.hip -- the scalar inner-product rule (Falcon-1A) at bf16 with
-// 64-step tiles, intra-chunk work and state pass in one kernel: keys and
-// queries come from HBM once, and no per-tile record makes a round trip
-// through it.
+// falcon_fused.hip -- the inner-product rules (Falcon-1A, and Falcon-2A with
+// its per-column write vectors) at bf16 with 64-step tiles, intra-chunk work
+// and state pass in one kernel: keys and queries come from HBM once, and no
+// per-tile record or write vector makes a round trip through it.
 //
 // Method ("Fast Weight Attention for Continual Learning", authors' abstract;
 // decay-then-write order and the normalized step from the KLA abstract on the
 // same listing): per (batch, head) the state S (d_v x d_k) is decayed by
 // alpha_t, receives the write y_t u_t^T with x_t = k_{t-lag} and
-// u_t = eta_t x_t / (||x_t||^2 + eps), and is read after the write,
+// u_t = eta_t x_t / (||x_t||^2 + eps) (Falcon-2A: u_tj = eta_t x_tj /
+// (|x_tj| ||x_t||_1 + eps), the per-column normalization read as a diagonal
+// normalizer), and is read after the write,
 // o_t = S_t q_t.  Per 64-step tile, with S0 the state at the tile start, g the
 // tile-local cumulative log decay and D(t, s) = exp(g_t - g_s):
 //   P[t][j] = [j <= t] D(t, j) (q_t . u_j),
@@ -35,7 +37,12 @@
 // iteration's intra-chunk work overlaps the state chain of the one before.
 // Keys and queries of a tile are used in three iterations (in flight, the
 // intra-chunk work, the chain), so they have three LDS buffers; targets,
-// gates and the intra-chunk results two.  Every decay factor is
+// gates and the intra-chunk results two.  The per-column rule keeps the keys
+// one stage longer (four; fills three tiles ahead): in the half-iteration
+// after barrier 1, where the scalar rule's intra-chunk waves are idle, they
+// turn tile it+2's keys into x / (|x| ||x||_1 + eps) in place (tiles 0 and 1
+// at the prologue's fill, in registers), so the P waves and the chain read
+// write vectors, and eta_t becomes the row scale.  Every decay factor is
 // exp(later - earlier) <= 1 of a log sum that restarts at each tile.  LDS
 // tiles are unpadded with swizzled chunks (swz_off), filled by lanes whose
 // source offsets apply the swizzle.
@@ -57,9 +64,12 @@ constexpr float kL2e = 1.4426950408889634f;
 // per-row factors of a tile
 enum : int { kGam = 0, kHrow = 1, kG2 = 2, kRs = 3, kCf = 4, kNFac = 5 };
 
-template <int D>
+template <int D, bool COL>
 struct FusedSmem {
-    uint16_t X[3][kF * D];             // keys x_i = k_{t0+i-lag}
+    // key stages: the per-column rule fills keys one tile further ahead, so
+    // that a tile's keys become its write vectors before the P waves read them
+    static constexpr int kXS = COL ? 4 : 3;
+    uint16_t X[kXS][kF * D];           // keys x_i = k_{t0+i-lag}; per-column rule: x_i / (|x_i| ||x_i||_1 + eps)
     uint16_t Q[3][kF * D];             // queries
     uint16_t Y[2][kF * 64];            // targets, this slice's 64 value columns
     s16x4 Pf[2][kFB][kFB][64];         // P blocks (tb, cb <= tb), B fragments of P^T
@@ -71,12 +81,14 @@ struct FusedSmem {
     float pe[kFB][kF];                 // and the gates eta, steps past the end 0
 };
 
-template <int D>
+template <int D, bool COL>
 __global__ __launch_bounds__(768) void fused_kernel(ChunkArgs a) {
     using E = EBf16;
     using T = uint16_t;
     using Frag = s16x4;
-    using Smem = FusedSmem<D>;
+    using Smem = FusedSmem<D, COL>;
+    constexpr int XS = Smem::kXS;       // key stages
+    constexpr int XD = XS - 1;          // tiles ahead the key fills run
     constexpr int NB = kFB, KB = D / 16, CPR = D / 8, NVS = D / 64;
     // direct-to-LDS fills: 1 KB per instruction, RPI rows of a D-wide tile
     constexpr int RPI = 1024 / (2 * D), NIX = kF / RPI, MIX = NIX / 4, MIY = 2;
@@ -139,6 +151,20 @@ __global__ __launch_bounds__(768) void fused_kernel(ChunkArgs a) {
             }
             px[it] = src ? *reinterpret_cast<const u32x4*>(src) : z;
         }
+        if constexpr (COL) {
+            // per-column rule: the write vectors without their step size,
+            // u_i / eta_i = x_i / (|x_i| ||x_i||_1 + eps); the CPR lanes of a
+            // row are consecutive and aligned, so the norm is a group sum
+#pragma unroll
+            for (int it = 0; it < NXP; ++it) {
+                const uint16_t* h = reinterpret_cast<const uint16_t*>(&px[it]);
+                float s1 = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s1 += fabsf(bf2f(h[e]));
+                s1 = group_sum_dpp<CPR>(s1);
+                px[it] = col_write8(px[it], s1, 1.f, eps);
+            }
+        }
 #pragma unroll
         for (int it = 0; it < NQP; ++it) {
             const int c = ft + 256 * it;
@@ -181,14 +207,18 @@ __global__ __launch_bounds__(768) void fused_kernel(ChunkArgs a) {
     const int c = cw;
     auto prep1 = [&](int tt) __attribute__((always_inline)) {
         const int t0 = tt * kF, pb = tt & 1;
-        const T* xt = sm.X[tt % 3];
-        // diagonal Gram block: dg[r] = x_{16c+4grp+r} . x_{16c+lr}
-        s16x8 xc[D / 32];
-#pragma unroll
-        for (int m = 0; m < D / 32; ++m) xc[m] = xrow8(xt, 16 * c + lr, 32 * m + 8 * grp);
+        const T* xt = sm.X[tt % XS];
+        // diagonal Gram block: dg[r] = x_{16c+4grp+r} . x_{16c+lr} (the
+        // scalar rule's norms; the per-column rule's keys are already its
+        // write vectors)
         f32x4 dg = zero4();
+        if constexpr (!COL) {
+            s16x8 xc[D / 32];
 #pragma unroll
-        for (int m = 0; m < D / 32; ++m) dg = E::mma32r(xc[m], xc[m], dg);
+            for (int m = 0; m < D / 32; ++m) xc[m] = xrow8(xt, 16 * c + lr, 32 * m + 8 * grp);
+#pragma unroll
+            for (int m = 0; m < D / 32; ++m) dg = E::mma32r(xc[m], xc[m], dg);
+        }
         const bool valid = t0 + lane < T_;
         const float al = valid ? sm.gates[pb][0][lane] : 1.f;  // steps past the end: identity
         const float et = valid ? sm.gates[pb][1][lane] : 0.f;
@@ -207,7 +237,9 @@ __global__ __launch_bounds__(768) void fused_kernel(ChunkArgs a) {
         const float n2r = sm.nrm[c][lr];
         const float gref = sm.pl[c][16 * c + 15] * kL2e;
         const float denr = n2r + eps;
-        const float rsc = denr > 0.f ? etr / denr : 0.f;  // eta 0 past the end
+        // row scale of the write vector: eta / (||x||^2 + eps), or eta for the
+        // per-column rule (eta 0 past the end)
+        const float rsc = COL ? etr : (denr > 0.f ? etr / denr : 0.f);
         const float g2r = lgr * kL2e;
         if (lane < 16) {
             sm.fac[pb][kGam][16 * c + lr] = __expf(lgr);
@@ -217,6 +249,27 @@ __global__ __launch_bounds__(768) void fused_kernel(ChunkArgs a) {
             sm.fac[pb][kCf][16 * c + lr] = exp2f(gref - g2r) * rsc;
         }
         if (lane == 0) sm.gref[pb][c] = gref;
+    };
+    // per-column rule: the keys of tile tt become x_i / (|x_i| ||x_i||_1 +
+    // eps) in place; wave c takes rows 16 c .. 16 c + 15, four lanes a row
+    auto to_write = [&](int tt) __attribute__((always_inline)) {
+        T* xt = sm.X[tt % XS];
+        constexpr int NCH = D / 32;  // 8-column chunks per lane
+        const int row = 16 * c + (lane >> 2), q4 = lane & 3;
+        u32x4 v[NCH];
+        float s1 = 0.f;
+#pragma unroll
+        for (int m = 0; m < NCH; ++m) {
+            v[m] = *reinterpret_cast<const u32x4*>(xt + swz_off<D>(row, 8 * (q4 * NCH + m)));
+            const uint16_t* h = reinterpret_cast<const uint16_t*>(&v[m]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s1 += fabsf(bf2f(h[e]));
+        }
+        s1 = group_sum_dpp<4>(s1);
+#pragma unroll
+        for (int m = 0; m < NCH; ++m)
+            *reinterpret_cast<u32x4*>(xt + swz_off<D>(row, 8 * (q4 * NCH + m))) =
+                col_write8(v[m], s1, 1.f, eps);
     };
 
     // ---- direct-to-LDS fills of the main loop (P waves).  Lane l of fill
@@ -237,16 +290,19 @@ __global__ __launch_bounds__(768) void fused_kernel(ChunkArgs a) {
         dyo[m] = (uint32_t)((row * D + 8 * (jp ^ swz_row<64>(row))) * 2);
     }
     const uint32_t sm_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) Smem*)&sm;
-    // keys, queries and gates of tile tt (t0 >= 2 * 64: no halo) into
-    // X[tt % 3], Q[tt % 3], gates[tt & 1]; rows past the sequence read as zeros
-    auto dma_xq = [&](int tt) __attribute__((always_inline)) {
+    // keys of tile tt (t0 >= 2 * 64: no halo) into X[tt % XS]; queries and
+    // gates into Q[tt % 3], gates[tt & 1]; rows past the sequence read as zeros
+    auto dma_x = [&](int tt) __attribute__((always_inline)) {
         const int t0 = tt * kF;
         const u32x4 rx = make_desc(kg + (size_t)(t0 - lag) * D, (int64_t)(T_ - t0 + lag) * D * 2);
-        const u32x4 rq = make_desc(qg + (size_t)t0 * D, (int64_t)(T_ - t0) * D * 2);
-        const uint32_t xb = sm_lds + (uint32_t)(offsetof(Smem, X) + sizeof(sm.X[0]) * (tt % 3));
-        const uint32_t qb = sm_lds + (uint32_t)(offsetof(Smem, Q) + sizeof(sm.Q[0]) * (tt % 3));
+        const uint32_t xb = sm_lds + (uint32_t)(offsetof(Smem, X) + sizeof(sm.X[0]) * (tt % XS));
 #pragma unroll
         for (int m = 0; m < MIX; ++m) buf_load16_lds(rx, xb + 1024 * (cw + 4 * m), dxo[m]);
+    };
+    auto dma_qg = [&](int tt) __attribute__((always_inline)) {
+        const int t0 = tt * kF;
+        const u32x4 rq = make_desc(qg + (size_t)t0 * D, (int64_t)(T_ - t0) * D * 2);
+        const uint32_t qb = sm_lds + (uint32_t)(offsetof(Smem, Q) + sizeof(sm.Q[0]) * (tt % 3));
 #pragma unroll
         for (int m = 0; m < MIX; ++m) buf_load16_lds(rq, qb + 1024 * (cw + 4 * m), dxo[m]);
         if (cw < 2) {
@@ -270,7 +326,7 @@ __global__ __launch_bounds__(768) void fused_kernel(ChunkArgs a) {
     // 4 grp + r], the B fragment of block (cb, w) of P^T ----
     const int w = cw;
     auto prow1 = [&](int tt, f32x4 (&acc)[NB]) __attribute__((always_inline)) {
-        const T* Xb = sm.X[tt % 3];
+        const T* Xb = sm.X[tt % XS];
         const T* Qb = sm.Q[tt % 3];
         s16x8 qq[D / 32];
 #pragma unroll
@@ -393,7 +449,7 @@ __global__ __launch_bounds__(768) void fused_kernel(ChunkArgs a) {
     // part 2: S^T = exp(g_last) S0^T + X^T diag(hrow) Delta
     auto chain2 = [&](int it, f32x4 (&Sacc)[KB], const Frag (&HB)[NB])
         __attribute__((always_inline)) {
-        const T* Xb = sm.X[it % 3];
+        const T* Xb = sm.X[it % XS];
         const float glq = sm.fac[it & 1][kGam][kF - 1];
         // the key column fragments: the first half of the state's blocks
         // requested before the first product, the rest while they run
@@ -451,6 +507,10 @@ __global__ __launch_bounds__(768) void fused_kernel(ChunkArgs a) {
         for (int it = 0; it < ntl; ++it) {
             if (it + 1 < ntl) prep1(it + 1);
             lds_barrier();
+            // the per-column rule: tile it+2's keys (filled during iteration
+            // it-1, tiles 0-1 converted at the prologue's fill) become write
+            // vectors before iteration it+1's P waves read them
+            if (COL && it + 2 < ntl) to_write(it + 2);
             lds_barrier();
         }
     } else {
@@ -459,9 +519,15 @@ __global__ __launch_bounds__(768) void fused_kernel(ChunkArgs a) {
         if (ntl > 0) prow1(0, pacc);
         __syncthreads();
         if (ntl > 0) prow2(0, pacc);
+        if (COL && ntl > 2) {
+            // the per-column rule's third key tile, converted during iteration 0
+            dma_x(2);
+            wait_vm_all();
+        }
         __syncthreads();
         for (int it = 0; it < ntl; ++it) {
-            if (it + 2 < ntl) dma_xq(it + 2);
+            if (it + XD < ntl) dma_x(it + XD);
+            if (it + 2 < ntl) dma_qg(it + 2);
             if (it + 1 < ntl) {
                 dma_y(it + 1);
                 prow1(it + 1, pacc);
@@ -481,7 +547,7 @@ bool fused_supported(const ChunkArgs& a, int dt, int D, int chunk, bool delta) {
     // solve and its state chain contended for LDS bandwidth and ran slower
     // than the split kernels
     return !delta && dt == 1 && (D == 64 || D == 128) && chunk == 64 && !a.phi && !a.ck_s &&
-           (a.norm == kNormScalar || (a.norm == kNormWindow && a.W == 1));
+           (a.norm == kNormScalar || a.norm == kNormColumn || (a.norm == kNormWindow && a.W == 1));
 }
 
 hipError_t launch_fused(const ChunkArgs& a, int D, bool delta, hipStream_t stream) {
@@ -496,8 +562,14 @@ hipError_t launch_fused(const ChunkArgs& a, int D, bool delta, hipStream_t strea
     const int nvs = D / 64;
     const int bh8 = (b.BH + 7) / 8 * 8;
     if (delta) return hipErrorInvalidValue;
-    if (D == 128) hipLaunchKernelGGL((fused_kernel<128>), dim3(bh8 * nvs), dim3(768), 0, stream, b);
-    else hipLaunchKernelGGL((fused_kernel<64>), dim3(bh8 * nvs), dim3(768), 0, stream, b);
+    const bool col = a.norm == kNormColumn;
+    if (D == 128) {
+        if (col) hipLaunchKernelGGL((fused_kernel<128, true>), dim3(bh8 * nvs), dim3(768), 0, stream, b);
+        else hipLaunchKernelGGL((fused_kernel<128, false>), dim3(bh8 * nvs), dim3(768), 0, stream, b);
+    } else {
+        if (col) hipLaunchKernelGGL((fused_kernel<64, true>), dim3(bh8 * nvs), dim3(768), 0, stream, b);
+        else hipLaunchKernelGGL((fused_kernel<64, false>), dim3(bh8 * nvs), dim3(768), 0, stream, b);
+    }
     return hipGetLastError();
 }
 
