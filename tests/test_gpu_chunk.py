@@ -68,6 +68,20 @@ def test_grid(dev, variant, dtype, D, chunk):
     check(dev, inp, variant, W, chunk)
 
 
+@pytest.mark.parametrize("T", [192, 193, 450, 777])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("variant", ["F1A", "F2A"])
+def test_fused_steady_state(dev, variant, D, T):
+    """The fused inner-product kernel past its prologue: 3 to 13 tiles, so
+    the key fills of the main loop (and, for the per-column rule, the keys
+    turned into write vectors in LDS from tile 2 on) are exercised, with a
+    start state, a halo key and LogNormal key scales for Falcon-2A."""
+    inp = I.make_chunk_inputs(2, 2, T, D, D, dtype="bf16", seed=300 + T + D, halo=True,
+                              S0_sd=0.3, key_lognormal=variant == "F2A")
+    check(dev, inp, variant, 1, 64, label="fused steady state")
+    check(dev, inp, variant, 1, 64, label="fused steady state, same-step", align="same")
+
+
 @pytest.mark.parametrize("T", [0, 1, 2, 15, 16, 17, 63, 64, 65, 129])
 @pytest.mark.parametrize("case", [("F1", "bf16", 128, 64, 1), ("F3", "bf16", 128, 64, 4),
                                   ("F2", "fp32", 64, 32, 1), ("F1A", "bf16", 64, 16, 1)])
